@@ -1,0 +1,202 @@
+// MXFP8 block quantisation of bf16 tensors ([news] "MXFP8 reduces compute and memory costs":
+// 8-bit floats with a separate scale per small block of values).  Three layouts, each with one
+// E8M0 scale per 32 elements along a GEMM's contraction dimension:
+//   rows     blocks along the contiguous dim, output in the input's layout;
+//   cols     blocks along the strided dim, output transposed (each block contiguous again);
+//   grouped  token-axis blocks restarting at each expert group (padded to 32 rows), output
+//            transposed to [C, padded tokens]: the weight-gradient operands.
+// All are HBM-bound: 2 bytes read, 1 + 1/32 bytes written per element.
+#include "mx_common.h"
+
+namespace moe {
+namespace {
+
+// ---- rows: 4 lanes per 32-element block, 8 elements (16 bytes) per lane
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ in, long long total,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+  const long long g = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long e0 = g * 8;
+  const bool live = e0 < total;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (live) v = *reinterpret_cast<const uint4*>(in + e0);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+    amax = lo > amax ? lo : amax;
+    amax = hi > amax ? hi : amax;
+  }
+  // reduce over the 4 lanes of the block (lanes 4m..4m+3 of the wave)
+  amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1, 64)));
+  amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, 64)));
+  if (!live) return;
+  const int sh = mx_shared_exp(amax);
+  uint32_t o0 = 0, o1 = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    o0 |= mx_encode(w[i] & 0xffffu, sh) << (16 * i);
+    o0 |= mx_encode(w[i] >> 16, sh) << (16 * i + 8);
+    o1 |= mx_encode(w[i + 2] & 0xffffu, sh) << (16 * i);
+    o1 |= mx_encode(w[i + 2] >> 16, sh) << (16 * i + 8);
+  }
+  *reinterpret_cast<uint2*>(q + e0) = make_uint2(o0, o1);
+  if ((threadIdx.x & 3) == 0) scale[e0 / 32] = static_cast<uint8_t>(sh + 127);
+}
+
+// ---- transposed layouts: a tile of 128 (strided-dim) positions x 64 columns staged in LDS.
+constexpr int kTP = 128;       // positions per tile (4 blocks of 32)
+constexpr int kTC = 64;        // columns per tile
+constexpr int kPitch = kTC + 2;  // LDS row pitch in bf16 (33 words: column reads hit distinct banks)
+
+// Each of the 256 threads quantises one (column, 32-position block) of the staged tile and
+// writes 32 bytes of q and one scale byte.  Lanes 4c..4c+3 take the 4 blocks of column c, so
+// they write 128 contiguous bytes.
+__device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch], int ncols, long long pos0,
+                                                   long long out_pitch, uint8_t* __restrict__ q,
+                                                   uint8_t* __restrict__ scale) {
+  const int c = threadIdx.x >> 2;
+  const int blk = threadIdx.x & 3;
+  if (c >= ncols) return;
+  uint32_t vals[32];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    vals[i] = tile[blk * 32 + i][c];
+    const uint32_t m = vals[i] & 0x7fffu;
+    amax = m > amax ? m : amax;
+  }
+  const int sh = mx_shared_exp(amax);
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    o[i] = mx_encode(vals[4 * i], sh) | (mx_encode(vals[4 * i + 1], sh) << 8) |
+           (mx_encode(vals[4 * i + 2], sh) << 16) | (mx_encode(vals[4 * i + 3], sh) << 24);
+  }
+  uint8_t* dst = q + c * out_pitch + pos0 + blk * 32;
+  reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  scale[c * (out_pitch / 32) + (pos0 / 32) + blk] = static_cast<uint8_t>(sh + 127);
+}
+
+// in [batch][rows][cols] -> q [batch][cols][rows], scale [batch][cols][rows/32]
+// grid: (ceil(rows/128), ceil(cols/64), batch); rows % 32 == 0, cols % 64 == 0.
+__global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ in, int rows, int cols,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+  __shared__ uint16_t tile[kTP][kPitch];
+  const long long b = blockIdx.z;
+  const int r0 = blockIdx.x * kTP;
+  const int c0 = blockIdx.y * kTC;
+  const uint16_t* src = in + b * rows * static_cast<long long>(cols);
+  // load 128 x 64 bf16: thread t takes column chunk t%8 of rows t/8 + 32i
+  const int cc = threadIdx.x & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (threadIdx.x >> 3) + 32 * i;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < rows) v = *reinterpret_cast<const uint4*>(src + static_cast<long long>(r0 + r) * cols + c0 + 8 * cc);
+    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[r][8 * cc]);
+    t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
+  }
+  __syncthreads();
+  // positions beyond `rows` in the last tile form whole 32-blocks (rows % 32 == 0): skip them
+  const int blk = threadIdx.x & 3;
+  if (r0 + blk * 32 >= rows) return;
+  quant_tile_columns(tile, kTC, r0, rows, q + b * cols * static_cast<long long>(rows) + static_cast<long long>(c0) * rows,
+                     scale + b * cols * static_cast<long long>(rows / 32) + static_cast<long long>(c0) * (rows / 32));
+}
+
+// Grouped token-axis blocks.  Padded position p in [offsets_pad[e], offsets_pad[e+1]) holds
+// grouped row r = offsets[e] + (p - offsets_pad[e]) if r < offsets[e+1], else zero; positions
+// from offsets_pad[E] to n_pad_cap hold zeros.  Row r's data is in[row_token ? row_token[r] : r].
+// grid: (n_pad_cap/128, C/64).
+__global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __restrict__ in,
+                                                            const int32_t* __restrict__ row_token,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ offsets_pad, int E, int C,
+                                                            long long n_pad_cap, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ scale) {
+  __shared__ uint16_t tile[kTP][kPitch];
+  __shared__ int s_off[257];
+  __shared__ int s_offp[257];
+  __shared__ long long s_src[kTP];
+  for (int i = threadIdx.x; i <= E; i += 256) {
+    s_off[i] = offsets[i];
+    s_offp[i] = offsets_pad[i];
+  }
+  __syncthreads();
+  const long long p0 = static_cast<long long>(blockIdx.x) * kTP;
+  const int c0 = blockIdx.y * kTC;
+  if (threadIdx.x < kTP) {
+    const long long p = p0 + threadIdx.x;
+    long long src = -1;
+    if (p < s_offp[E]) {
+      int lo = 0, hi = E - 1;                 // last e with offsets_pad[e] <= p
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_offp[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      const long long r = s_off[lo] + (p - s_offp[lo]);
+      if (r < s_off[lo + 1]) src = row_token ? row_token[r] : r;
+    }
+    s_src[threadIdx.x] = src;
+  }
+  __syncthreads();
+  const int cc = threadIdx.x & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (threadIdx.x >> 3) + 32 * i;
+    const long long src = s_src[r];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (src >= 0) v = *reinterpret_cast<const uint4*>(in + src * C + c0 + 8 * cc);
+    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[r][8 * cc]);
+    t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
+  }
+  __syncthreads();
+  quant_tile_columns(tile, kTC, p0, n_pad_cap, q + static_cast<long long>(c0) * n_pad_cap,
+                     scale + static_cast<long long>(c0) * (n_pad_cap / 32));
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_mx_pad_cap(int n, int E) {
+  const long long cap = (static_cast<long long>(n) + 32LL * E + 127) / 128 * 128;
+  return cap < (1LL << 31) ? static_cast<int>(cap) : -1;
+}
+
+extern "C" int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, uint8_t* q,
+                              uint8_t* scale, void* stream) {
+  MOE_CHECK_PTR(in); MOE_CHECK_PTR(q); MOE_CHECK_PTR(scale);
+  MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(q);
+  MOE_REQUIRE(batch >= 1 && rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG, "sizes must be positive");
+  hipStream_t s = as_stream(stream);
+  if (axis == 0) {
+    MOE_REQUIRE(cols % 32 == 0, MOE_ERR_UNSUPPORTED, "axis 0 needs cols %% 32 == 0");
+    const long long total = static_cast<long long>(batch) * rows * cols;
+    quant_rows_kernel<<<static_cast<unsigned>((total / 8 + 255) / 256), 256, 0, s>>>(in, total, q, scale);
+    return check_launch("mxfp8_quantize rows");
+  }
+  MOE_REQUIRE(axis == 1, MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
+  MOE_REQUIRE(rows % 32 == 0 && cols % 64 == 0, MOE_ERR_UNSUPPORTED, "axis 1 needs rows %% 32 == 0, cols %% 64 == 0");
+  MOE_REQUIRE(batch <= 65535, MOE_ERR_UNSUPPORTED, "batch too large");
+  dim3 grid((rows + kTP - 1) / kTP, cols / kTC, batch);
+  quant_cols_kernel<<<grid, 256, 0, s>>>(in, rows, cols, q, scale);
+  return check_launch("mxfp8_quantize cols");
+}
+
+extern "C" int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_token, const int32_t* offsets,
+                                      const int32_t* offsets_pad, int E, int n, int C, uint8_t* qT, uint8_t* scaleT,
+                                      void* stream) {
+  MOE_CHECK_PTR(in); MOE_CHECK_PTR(offsets); MOE_CHECK_PTR(offsets_pad); MOE_CHECK_PTR(qT); MOE_CHECK_PTR(scaleT);
+  MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(qT);
+  MOE_REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "E must be in [1, 256]");
+  MOE_REQUIRE(n >= 1 && C >= 64 && C % 64 == 0, MOE_ERR_UNSUPPORTED, "need n >= 1 and C a multiple of 64");
+  const int cap = moe_mx_pad_cap(n, E);
+  MOE_REQUIRE(cap > 0, MOE_ERR_UNSUPPORTED, "padded token axis too long");
+  dim3 grid(cap / kTP, C / kTC);
+  quant_grouped_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, row_token, offsets, offsets_pad, E, C, cap, qT, scaleT);
+  return check_launch("mxfp8_quantize_grouped");
+}

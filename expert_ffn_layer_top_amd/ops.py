@@ -1,0 +1,298 @@
+"""Torch-facing wrappers of the C ABI: argument marshalling only.
+
+Each function checks device, dtype, contiguity and shape, allocates the outputs (and any
+workspace) with torch on the input's device, and passes raw pointers plus the current HIP
+stream to the library.  All arithmetic happens in the library's kernels; nothing here computes.
+
+Tensor conventions: bf16 tensors are torch.bfloat16; E4M3 elements and E8M0 scales are
+torch.uint8 bytes; indices are torch.int32; gates and logits are torch.float32.
+"""
+
+import torch
+
+from ._lib import call, lib
+
+BF16, MXFP8 = 0, 1
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(t, dtype, name, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {t.dim()}")
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------- router
+
+def router_project(x, w_r):
+    """logits [T,E] fp32 = x [T,d] bf16 @ w_r [d,E] fp32."""
+    _check(x, torch.bfloat16, "x", 2)
+    _check(w_r, torch.float32, "w_r", 2)
+    T, d = x.shape
+    E = w_r.shape[1]
+    assert w_r.shape[0] == d
+    logits = _empty((T, E), torch.float32, x)
+    call("moe_router_project", _ptr(x), _ptr(w_r), T, d, E, _ptr(logits), _stream(x))
+    return logits
+
+
+def router_project_bwd(x, w_r, d_logits, want_dx=True, want_dw=True):
+    """(dx_router [T,d] fp32 or None, dw_r [d,E] fp32 or None)."""
+    _check(x, torch.bfloat16, "x", 2)
+    _check(w_r, torch.float32, "w_r", 2)
+    _check(d_logits, torch.float32, "d_logits", 2)
+    T, d = x.shape
+    E = w_r.shape[1]
+    dx = _empty((T, d), torch.float32, x) if want_dx else None
+    dw = _empty((d, E), torch.float32, x) if want_dw else None
+    nbytes = lib.moe_router_bwd_workspace_bytes(T, d, E) if want_dw else 0
+    ws = _empty((max(nbytes, 1),), torch.uint8, x)
+    call("moe_router_project_bwd", _ptr(x), _ptr(w_r), _ptr(d_logits), T, d, E, _ptr(dx), _ptr(dw),
+         _ptr(ws), nbytes, _stream(x))
+    return dx, dw
+
+
+def route_topk(logits, k, want_probs=False, pad=None, want_row_token=True):
+    """Router top-k + routing metadata.  Returns a dict with topk_idx, topk_gate, probs (or None),
+    counts, offsets, offsets_pad (or None), dest, row_token (or None)."""
+    _check(logits, torch.float32, "logits", 2)
+    T, E = logits.shape
+    out = dict(
+        topk_idx=_empty((T, k), torch.int32, logits),
+        topk_gate=_empty((T, k), torch.float32, logits),
+        probs=_empty((T, E), torch.float32, logits) if want_probs else None,
+        counts=_empty((E,), torch.int32, logits),
+        offsets=_empty((E + 1,), torch.int32, logits),
+        offsets_pad=_empty((E + 1,), torch.int32, logits) if pad else None,
+        dest=_empty((T, k), torch.int32, logits),
+        row_token=_empty((T * k,), torch.int32, logits) if want_row_token else None,
+    )
+    nbytes = lib.moe_route_workspace_bytes(T, E, k)
+    ws = _empty((max(nbytes, 1),), torch.uint8, logits)
+    call("moe_route_topk", _ptr(logits), T, E, k, _ptr(out["topk_idx"]), _ptr(out["topk_gate"]),
+         _ptr(out["probs"]), _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["offsets_pad"]),
+         int(pad or 0), _ptr(out["dest"]), _ptr(out["row_token"]), _ptr(ws), nbytes, _stream(logits))
+    return out
+
+
+def route_topk_bwd(topk_gate, topk_idx, d_gate, E):
+    """d_logits [T,E] fp32."""
+    _check(topk_gate, torch.float32, "topk_gate", 2)
+    _check(topk_idx, torch.int32, "topk_idx", 2)
+    _check(d_gate, torch.float32, "d_gate", 2)
+    T, k = topk_idx.shape
+    dl = _empty((T, E), torch.float32, topk_gate)
+    call("moe_route_topk_bwd", _ptr(topk_gate), _ptr(topk_idx), _ptr(d_gate), T, E, k, _ptr(dl),
+         _stream(topk_gate))
+    return dl
+
+
+# ---------------------------------------------------------------- rows
+
+def permute(x, dest, x_scale=None):
+    """xp [n,d] (bf16, or E4M3 bytes + xp_scale when x_scale is given)."""
+    _check(dest, torch.int32, "dest", 2)
+    T, k = dest.shape
+    if x_scale is None:
+        _check(x, torch.bfloat16, "x", 2)
+        xp = _empty((T * k, x.shape[1]), torch.bfloat16, x)
+        call("moe_permute", BF16, _ptr(x), None, _ptr(dest), T, x.shape[1], k, _ptr(xp), None, _stream(x))
+        return xp
+    _check(x, torch.uint8, "x", 2)
+    _check(x_scale, torch.uint8, "x_scale", 2)
+    d = x.shape[1]
+    xp = _empty((T * k, d), torch.uint8, x)
+    xps = _empty((T * k, d // 32), torch.uint8, x)
+    call("moe_permute", MXFP8, _ptr(x), _ptr(x_scale), _ptr(dest), T, d, k, _ptr(xp), _ptr(xps), _stream(x))
+    return xp, xps
+
+
+def unpermute_combine(yexp, topk_gate, dest):
+    _check(yexp, torch.bfloat16, "yexp", 2)
+    _check(topk_gate, torch.float32, "topk_gate", 2)
+    _check(dest, torch.int32, "dest", 2)
+    T, k = dest.shape
+    d = yexp.shape[1]
+    y = _empty((T, d), torch.bfloat16, yexp)
+    call("moe_unpermute_combine", _ptr(yexp), _ptr(topk_gate), _ptr(dest), T, d, k, _ptr(y), _stream(yexp))
+    return y
+
+
+def unpermute_combine_bwd(dy, yexp, topk_gate, dest):
+    """(dyexp [n,d] bf16, d_gate [T,k] fp32)."""
+    _check(dy, torch.bfloat16, "dy", 2)
+    _check(yexp, torch.bfloat16, "yexp", 2)
+    _check(topk_gate, torch.float32, "topk_gate", 2)
+    _check(dest, torch.int32, "dest", 2)
+    T, k = dest.shape
+    d = dy.shape[1]
+    dyexp = _empty((T * k, d), torch.bfloat16, dy)
+    dgate = _empty((T, k), torch.float32, dy)
+    call("moe_unpermute_combine_bwd", _ptr(dy), _ptr(yexp), _ptr(topk_gate), _ptr(dest), T, d, k,
+         _ptr(dyexp), _ptr(dgate), _stream(dy))
+    return dyexp, dgate
+
+
+def permute_bwd(dxp, dest, addend=None):
+    _check(dxp, torch.bfloat16, "dxp", 2)
+    _check(dest, torch.int32, "dest", 2)
+    if addend is not None:
+        _check(addend, torch.float32, "addend", 2)
+    T, k = dest.shape
+    d = dxp.shape[1]
+    dx = _empty((T, d), torch.bfloat16, dxp)
+    call("moe_permute_bwd", _ptr(dxp), _ptr(dest), T, d, k, _ptr(addend), _ptr(dx), _stream(dxp))
+    return dx
+
+
+# ---------------------------------------------------------------- MXFP8
+
+def mxfp8_quantize(x, axis):
+    """x [..., R, C] bf16 (2-D or 3-D).  axis 0: blocks along C, outputs in x's layout;
+    axis 1: blocks along R, outputs transposed to [..., C, R]."""
+    _check(x, torch.bfloat16, "x")
+    if x.dim() == 2:
+        batch, (R, C) = 1, x.shape
+    elif x.dim() == 3:
+        batch, R, C = x.shape
+    else:
+        raise ValueError("x must be 2-D or 3-D")
+    lead = x.shape[:-2]
+    if axis == 0:
+        q = _empty((*lead, R, C), torch.uint8, x)
+        s = _empty((*lead, R, C // 32), torch.uint8, x)
+    else:
+        q = _empty((*lead, C, R), torch.uint8, x)
+        s = _empty((*lead, C, R // 32), torch.uint8, x)
+    call("mxfp8_quantize", _ptr(x), batch, R, C, axis, _ptr(q), _ptr(s), _stream(x))
+    return q, s
+
+
+def mx_pad_cap(n, E):
+    return lib.moe_mx_pad_cap(n, E)
+
+
+def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None):
+    """Token-axis blocks per expert group: (qT [C, P], sT [C, P/32]), P = mx_pad_cap(n, E)."""
+    _check(x, torch.bfloat16, "x", 2)
+    _check(offsets, torch.int32, "offsets", 1)
+    _check(offsets_pad, torch.int32, "offsets_pad", 1)
+    E = offsets.shape[0] - 1
+    C = x.shape[1]
+    P = mx_pad_cap(n, E)
+    q = _empty((C, P), torch.uint8, x)
+    s = _empty((C, P // 32), torch.uint8, x)
+    call("mxfp8_quantize_grouped", _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(offsets_pad), E, n, C,
+         _ptr(q), _ptr(s), _stream(x))
+    return q, s
+
+
+# ---------------------------------------------------------------- grouped GEMMs
+
+def gg_workspace(dtype, E, n, d, f, like):
+    nbytes = lib.moe_gg_workspace_bytes(dtype, E, n, d, f)
+    return _empty((max(nbytes, 1),), torch.uint8, like), nbytes
+
+
+def grouped_gemm_swiglu(xp, offsets, w_gate, w_up, w_down, scales=None, ws=None):
+    """(g, u, a [n,f], yexp [n,d]) bf16.  bf16: xp, w_* bf16 and scales None.  MXFP8: xp and w_*
+    are E4M3 bytes and scales = (xp_scale, w_gate_scale, w_up_scale, w_down_scale)."""
+    _check(offsets, torch.int32, "offsets", 1)
+    E, f, d = w_gate.shape
+    n = xp.shape[0]
+    dtype = BF16 if scales is None else MXFP8
+    wdt = torch.bfloat16 if dtype == BF16 else torch.uint8
+    for t, name in ((xp, "xp"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _check(t, wdt, name)
+    g = _empty((n, f), torch.bfloat16, xp)
+    u = _empty((n, f), torch.bfloat16, xp)
+    a = _empty((n, f), torch.bfloat16, xp)
+    yexp = _empty((n, d), torch.bfloat16, xp)
+    sc = (None,) * 4 if scales is None else scales
+    if ws is None:
+        ws, nbytes = gg_workspace(dtype, E, n, d, f, xp)
+    else:
+        nbytes = ws.numel()
+    call("moe_grouped_gemm_swiglu", dtype, E, n, d, f, _ptr(offsets), _ptr(xp), _ptr(sc[0]), _ptr(w_gate),
+         _ptr(sc[1]), _ptr(w_up), _ptr(sc[2]), _ptr(w_down), _ptr(sc[3]), _ptr(g), _ptr(u), _ptr(a), _ptr(yexp),
+         _ptr(ws), nbytes, _stream(xp))
+    return g, u, a, yexp
+
+
+def grouped_gemm_gate_up(xp, offsets, w_gate, w_up, scales=None):
+    """(g, u, a [n,f]) bf16: the first grouped product with the SwiGLU epilogue.  MXFP8: xp and
+    w_* are E4M3 bytes and scales = (xp_scale, w_gate_scale, w_up_scale)."""
+    _check(offsets, torch.int32, "offsets", 1)
+    E, f, d = w_gate.shape
+    n = xp.shape[0]
+    dtype = BF16 if scales is None else MXFP8
+    wdt = torch.bfloat16 if dtype == BF16 else torch.uint8
+    for t, name in ((xp, "xp"), (w_gate, "w_gate"), (w_up, "w_up")):
+        _check(t, wdt, name)
+    g = _empty((n, f), torch.bfloat16, xp)
+    u = _empty((n, f), torch.bfloat16, xp)
+    a = _empty((n, f), torch.bfloat16, xp)
+    sc = (None,) * 3 if scales is None else scales
+    call("moe_grouped_gemm_gate_up", dtype, E, n, d, f, _ptr(offsets), _ptr(xp), _ptr(sc[0]), _ptr(w_gate),
+         _ptr(sc[1]), _ptr(w_up), _ptr(sc[2]), _ptr(g), _ptr(u), _ptr(a), _stream(xp))
+    return g, u, a
+
+
+def grouped_gemm_down(a, offsets, w_down, w_down_scale=None, ws=None):
+    """yexp [n,d] bf16 = a W_down[e]^T per expert (MXFP8 when w_down_scale is given)."""
+    _check(a, torch.bfloat16, "a", 2)
+    _check(offsets, torch.int32, "offsets", 1)
+    E, d, f = w_down.shape
+    n = a.shape[0]
+    dtype = BF16 if w_down_scale is None else MXFP8
+    _check(w_down, torch.bfloat16 if dtype == BF16 else torch.uint8, "w_down")
+    yexp = _empty((n, d), torch.bfloat16, a)
+    if ws is None:
+        ws, nbytes = gg_workspace(dtype, E, n, d, f, a)
+    else:
+        nbytes = ws.numel()
+    call("moe_grouped_gemm_down", dtype, E, n, d, f, _ptr(offsets), _ptr(a), _ptr(w_down), _ptr(w_down_scale),
+         _ptr(yexp), _ptr(ws), nbytes, _stream(a))
+    return yexp
+
+
+def grouped_gemm_swiglu_bwd(x_rows, g, u, a, dyexp, offsets, w_gate, w_up, w_down, scales=None,
+                            offsets_pad=None, row_token=None, ws=None):
+    """dict(dg, du, dxp, dw_gate, dw_up, dw_down), all bf16.
+    bf16: x_rows = xp [n,d]; w_* the forward weights.
+    MXFP8: x_rows = x [T,d] (read through row_token); w_gate, w_up [E,d,f] and w_down [E,f,d] are
+    the dgrad-direction E4M3 weights with scales = (w_gate_scale, w_up_scale, w_down_scale)."""
+    _check(offsets, torch.int32, "offsets", 1)
+    n, f = g.shape
+    E = offsets.shape[0] - 1
+    d = dyexp.shape[1]
+    dtype = BF16 if scales is None else MXFP8
+    out = dict(dg=_empty((n, f), torch.bfloat16, g), du=_empty((n, f), torch.bfloat16, g),
+               dxp=_empty((n, d), torch.bfloat16, g), dw_gate=_empty((E, f, d), torch.bfloat16, g),
+               dw_up=_empty((E, f, d), torch.bfloat16, g), dw_down=_empty((E, d, f), torch.bfloat16, g))
+    sc = (None,) * 3 if scales is None else scales
+    if ws is None:
+        ws, nbytes = gg_workspace(dtype, E, n, d, f, g)
+    else:
+        nbytes = ws.numel()
+    call("moe_grouped_gemm_swiglu_bwd", dtype, E, n, d, f, _ptr(offsets), _ptr(offsets_pad), _ptr(row_token),
+         _ptr(x_rows), _ptr(g), _ptr(u), _ptr(a), _ptr(dyexp), _ptr(w_gate), _ptr(sc[0]), _ptr(w_up),
+         _ptr(sc[1]), _ptr(w_down), _ptr(sc[2]), _ptr(out["dg"]), _ptr(out["du"]), _ptr(out["dxp"]),
+         _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(ws), nbytes, _stream(g))
+    return out

@@ -1,0 +1,239 @@
+/*
+ * moe_mi355x.h - C ABI of the MoE expert-FFN layer hot path for MI355X (gfx950).
+ *
+ * One GPU's share of an expert-parallel mixture-of-experts layer: router top-k, routing
+ * metadata computed on the device, a rowwise permute into contiguous expert buffers, a
+ * device-scheduled grouped GEMM running the SwiGLU expert FFN (bf16 or MXFP8), a weighted
+ * unpermute-combine, and the matching backward.
+ *
+ * The method is the MoE layer of the Olmo-core 3 training stack:
+ *   [news] "Ai2 rebuilds Olmo's training stack for trillion-parameter MoEs"
+ *          - lead paragraphs: a router sends each token to a small selection of FFN experts;
+ *          - "Routing work stays on the GPU": rows are written straight into expert input
+ *            buffers, routing metadata stays on the device so the CPU never waits for a copy
+ *            back, and a grouped GEMM runs the many small expert products together;
+ *          - "MXFP8 reduces compute and memory costs": 8-bit floats with one scale per small
+ *            block of values.
+ *   [card] "Supercharging Olmo-core for Efficient and Scalable MoE Training", "Summary":
+ *          rowwise EP, GPU-resident routing metadata, device-scheduled grouped GEMMs, MXFP8.
+ * The pages give no arithmetic; this library computes: softmax over all E experts, top-k
+ * (descending logit, ties to the lower expert id), gates renormalised over the k chosen;
+ * SwiGLU experts  A = silu(X W_gate^T) * (X W_up^T),  Yexp = A W_down^T  (no biases);
+ * y[t] = sum_j gate[t,j] * Yexp[dest[t,j]]; MXFP8 = E4M3 elements + one E8M0 scale per 32
+ * consecutive elements along each GEMM's contraction dimension.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major, contiguous,
+ *     16-byte aligned.  They must stay valid until the enqueued work has completed.
+ *   - bf16 tensors are passed as uint16_t bit patterns; E4M3 elements and E8M0 scales as
+ *     uint8_t.  Indices are int32_t.  Floating-point accumulation is fp32; bf16 results are
+ *     rounded to nearest-even once, when stored.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work on
+ *     it: no allocation, no synchronisation, no device-to-host copy.
+ *   - Outputs are written, never accumulated into.  Results are deterministic: the same
+ *     inputs give bit-identical outputs (no floating-point atomics anywhere).
+ *   - Errors: a nonzero moe_status_t.  Every check on host-visible arguments happens before
+ *     anything is enqueued.  Device-side contents are trusted (e.g. `dest` must come from
+ *     moe_route_topk with the same T, k).  A failed kernel launch returns MOE_ERR_HIP; its
+ *     text is in moe_last_error_string() (per calling thread).  Asynchronous faults surface
+ *     at the caller's next synchronisation.
+ *   - Shapes: 1 <= E <= 256, 1 <= k <= min(E, 16), T >= 1, T*k < 2^31, d and f multiples of
+ *     64 (of 32 for the MXFP8 scale layout, implied).  Anything else: MOE_ERR_UNSUPPORTED.
+ *
+ * Layouts (n = T*k routed rows):
+ *   x [T,d] bf16; router weight w_r [d,E] fp32; logits [T,E] fp32;
+ *   w_gate, w_up [E,f,d] bf16; w_down [E,d,f] bf16 (output features first);
+ *   xp, yexp, dyexp, dxp [n,d] bf16; g, u, a, dg, du [n,f] bf16;
+ *   topk_idx, dest [T,k] int32; topk_gate, d_gate [T,k] fp32; counts [E]; offsets [E+1].
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MI355X_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, negative size, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2,  /* a shape or mode outside the supported set */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes value */
+  MOE_ERR_HIP = 4           /* a HIP launch failed; see moe_last_error_string() */
+} moe_status_t;
+
+enum { MOE_BF16 = 0, MOE_MXFP8 = 1 };
+
+/* Version of this ABI (MOE_MI355X_ABI_VERSION of the built library). */
+int moe_abi_version(void);
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+/* Text of the last MOE_ERR_* returned on the calling thread ("" if none). */
+const char* moe_last_error_string(void);
+
+/* ---------------------------------------------------------------- router */
+
+/* logits[T,E] = x[T,d] (bf16) @ w_r[d,E] (fp32), fp32 accumulation.
+ * The router's projection that scores every expert for every token ([news] lead paragraphs).
+ * Used where the router weight is part of the layer (the router-driven workloads); callers that
+ * already hold logits skip it. */
+int moe_router_project(const uint16_t* x, const float* w_r, int T, int d, int E, float* logits,
+                       void* stream);
+
+/* Workspace for moe_router_project_bwd (the split-K partial sums of dw_r). */
+size_t moe_router_bwd_workspace_bytes(int T, int d, int E);
+
+/* Backward of moe_router_project:  dx_router[T,d] = d_logits @ w_r^T (fp32),
+ * dw_r[d,E] = x^T @ d_logits (fp32; summed over token chunks in a fixed order).  Either output
+ * may be NULL to skip it; ws (>= moe_router_bwd_workspace_bytes) is needed only for dw_r. */
+int moe_router_project_bwd(const uint16_t* x, const float* w_r, const float* d_logits, int T, int d,
+                           int E, float* dx_router_or_null, float* dw_r_or_null, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace for moe_route_topk, from host scalars only. */
+size_t moe_route_workspace_bytes(int T, int E, int k);
+
+/* Router top-k and the device-resident routing metadata ([news] "Routing work stays on the GPU";
+ * [card] "Summary": GPU-resident routing metadata).
+ *   in   logits [T,E] fp32
+ *   out  topk_idx [T,k]: the k largest logits per token, descending, ties to the lower expert id;
+ *        topk_gate [T,k]: softmax over the chosen logits (= full softmax renormalised over them);
+ *        probs [T,E] (optional): full softmax;
+ *        counts [E]: rows per expert; offsets [E+1]: exclusive prefix sum (offsets[E] = T*k);
+ *        offsets_pad [E+1] (optional): prefix sum of counts rounded up to `pad` (pad >= 1; the
+ *        MXFP8 token-block layout uses 32);
+ *        dest [T,k]: row of (t, j) in the expert-major buffer, rows ordered by expert, then token;
+ *        row_token [T*k] (optional): the token of each row.
+ *   ws   at least moe_route_workspace_bytes(T,E,k) bytes of device memory (contents ignored). */
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_gate,
+                   float* probs_or_null, int32_t* counts, int32_t* offsets,
+                   int32_t* offsets_pad_or_null, int pad, int32_t* dest, int32_t* row_token_or_null,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the renormalised gates with the selection held fixed:
+ * d_logits[t, idx[t,j]] = g_j * (dg_j - sum_i g_i dg_i), 0 for experts not chosen.  [T,E] fp32. */
+int moe_route_topk_bwd(const float* topk_gate, const int32_t* topk_idx, const float* d_gate, int T,
+                       int E, int k, float* d_logits, void* stream);
+
+/* ---------------------------------------------------------------- rows */
+
+/* Rowwise permute: xp[dest[t,j], :] = x[t, :] for every slot j, a bit copy
+ * ([news] "Routing work stays on the GPU": routed rows go straight into expert input buffers).
+ *   dtype MOE_BF16:  x [T,d] bf16 -> xp [n,d] bf16; the scale pointers must be NULL.
+ *   dtype MOE_MXFP8: x [T,d] E4M3 + x_scale [T,d/32] E8M0 -> xp [n,d] + xp_scale [n,d/32]. */
+int moe_permute(int dtype, const void* x, const uint8_t* x_scale_or_null, const int32_t* dest,
+                int T, int d, int k, void* xp, uint8_t* xp_scale_or_null, void* stream);
+
+/* Weighted unpermute-combine: y[t] = sum_j topk_gate[t,j] * yexp[dest[t,j]], fp32 in slot order,
+ * bf16 out. */
+int moe_unpermute_combine(const uint16_t* yexp, const float* topk_gate, const int32_t* dest, int T,
+                          int d, int k, uint16_t* y, void* stream);
+
+/* Backward of the combine: dyexp[dest[t,j]] = bf16(gate[t,j] * dy[t]);
+ * d_gate[t,j] = <dy[t], yexp[dest[t,j]]> (fp32). */
+int moe_unpermute_combine_bwd(const uint16_t* dy, const uint16_t* yexp, const float* topk_gate,
+                              const int32_t* dest, int T, int d, int k, uint16_t* dyexp,
+                              float* d_gate, void* stream);
+
+/* Backward of the permute: dx[t] = sum_j dxp[dest[t,j]] (+ dx_addend[t] if given, the fp32
+ * router-path term), fp32 accumulation, bf16 out. */
+int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int k,
+                    const float* dx_addend_or_null, uint16_t* dx, void* stream);
+
+/* ---------------------------------------------------------------- MXFP8 quantisation */
+
+/* MXFP8 block quantisation of a bf16 tensor in[batch][rows][cols]
+ * ([news] "MXFP8 reduces compute and memory costs").  Per block of 32 bf16 values:
+ * amax = max|v|; scale byte s = clamp(floor(log2 amax) - 8, -127, 127) + 127 (s = 0 when
+ * amax = 0); q = E4M3(v / 2^(s-127)) with round-to-nearest-even, magnitudes above 448 saturate
+ * to 448, signs (and -0) kept.
+ *   axis 0: blocks along cols (the contiguous dim): q [batch][rows][cols], scale [batch][rows][cols/32]
+ *           (cols % 32 == 0)
+ *   axis 1: blocks along rows (the strided dim), output transposed:
+ *           q [batch][cols][rows], scale [batch][cols][rows/32]   (rows % 32 == 0) */
+int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, uint8_t* q,
+                   uint8_t* scale, void* stream);
+
+/* Token-axis MXFP8 blocks restarting at each expert group (the weight-gradient operands).
+ * Row r of the grouped tensor is in[r] (row_token NULL; in is [n,C]) or in[row_token[r]]
+ * (in is the token-major source [T,C]).  Expert e's rows [offsets[e], offsets[e+1]) go to
+ * positions [offsets_pad[e], offsets_pad[e] + count_e) of a padded token axis; padding
+ * positions up to offsets_pad[e+1] hold zeros, and so does everything from offsets_pad[E] to
+ * n_pad_cap.  offsets_pad must be the 32-padded prefix sum from moe_route_topk (pad = 32).
+ *   out qT [C, n_pad_cap] E4M3, scaleT [C, n_pad_cap/32] E8M0, n_pad_cap = n + 32*E rounded
+ *   up to a multiple of 128 (moe_mx_pad_cap). */
+int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_token_or_null,
+                           const int32_t* offsets, const int32_t* offsets_pad, int E, int n, int C,
+                           uint8_t* qT, uint8_t* scaleT, void* stream);
+
+/* Length of the padded token axis used by mxfp8_quantize_grouped and the MXFP8 backward. */
+int moe_mx_pad_cap(int n, int E);
+
+/* ---------------------------------------------------------------- grouped GEMMs */
+
+/* Workspace for moe_grouped_gemm_swiglu / _bwd, from host scalars only. */
+size_t moe_gg_workspace_bytes(int dtype, int E, int n, int d, int f);
+
+/* Expert SwiGLU FFN as device-scheduled grouped GEMMs over the expert-major rows
+ * ([news] "Routing work stays on the GPU": grouped GEMM; [card] "Summary": device-scheduled).
+ * The per-expert row ranges are read from `offsets` on the device; the host never sees them.
+ * For expert e, rows r in [offsets[e], offsets[e+1]):
+ *   g = xp W_gate[e]^T, u = xp W_up[e]^T, a = silu(g) * u  (stored bf16; a from fp32 g, u),
+ *   yexp = a W_down[e]^T.
+ * dtype MOE_BF16:  xp, w_* bf16; all *_scale NULL.
+ * dtype MOE_MXFP8: xp [n,d] E4M3 + xp_scale [n,d/32]; w_gate, w_up [E,f,d] E4M3 + scales
+ *   [E,f,d/32]; w_down [E,d,f] E4M3 + scale [E,d,f/32] (all blocks along the contraction dim).
+ *   a is quantised (rows, blocks along f) into the workspace before the second product.
+ * Outputs g, u, a [n,f], yexp [n,d] bf16. */
+int moe_grouped_gemm_swiglu(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                            const void* xp, const uint8_t* xp_scale, const void* w_gate,
+                            const uint8_t* w_gate_scale, const void* w_up,
+                            const uint8_t* w_up_scale, const void* w_down,
+                            const uint8_t* w_down_scale, uint16_t* g, uint16_t* u, uint16_t* a,
+                            uint16_t* yexp, void* ws, size_t ws_bytes, void* stream);
+
+/* The two products of moe_grouped_gemm_swiglu as separate calls (same arguments, same results):
+ * gate_up runs the first grouped product with the SwiGLU epilogue (g, u, a); down runs the second
+ * (yexp) from a bf16 `a` (for MOE_MXFP8 it first quantises a along f into the workspace, so it
+ * needs moe_gg_workspace_bytes; gate_up needs none).  One kernel each for bf16. */
+int moe_grouped_gemm_gate_up(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                             const void* xp, const uint8_t* xp_scale, const void* w_gate,
+                             const uint8_t* w_gate_scale, const void* w_up,
+                             const uint8_t* w_up_scale, uint16_t* g, uint16_t* u, uint16_t* a,
+                             void* stream);
+int moe_grouped_gemm_down(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                          const uint16_t* a, const void* w_down, const uint8_t* w_down_scale,
+                          uint16_t* yexp, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of moe_grouped_gemm_swiglu (dgrad and wgrad grouped GEMMs).
+ *   da = dyexp W_down[e];  dg = da * u * s * (1 + g (1 - s)),  du = da * g * s,  s = sigmoid(g)
+ *   dxp = dg W_gate[e] + du W_up[e]
+ *   dw_down[e] = dyexp_e^T a_e,  dw_gate[e] = dg_e^T xp_e,  dw_up[e] = du_e^T xp_e
+ * Weight gradients of experts with no rows are written as zeros.
+ * dtype MOE_BF16: x_rows = xp [n,d] bf16 (row_token NULL); w_* are the forward weights (bf16).
+ * dtype MOE_MXFP8: x_rows = x [T,d] bf16 read through row_token (the token of each row);
+ *   w_gate_t, w_up_t [E,d,f] and w_down_t [E,f,d] are the weights quantised along the dgrad
+ *   contraction (mxfp8_quantize axis 1 per expert), with scales [E,d,f/32], [E,f,d/32];
+ *   dyexp, dg|du are quantised along rows, and xp, a, dyexp, dg, du along grouped tokens
+ *   (offsets_pad, pad 32), into the workspace.
+ * Outputs dg, du [n,f], dxp [n,d], dw_gate, dw_up [E,f,d], dw_down [E,d,f], all bf16. */
+int moe_grouped_gemm_swiglu_bwd(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                                const int32_t* offsets_pad_or_null,
+                                const int32_t* row_token_or_null, const uint16_t* x_rows,
+                                const uint16_t* g, const uint16_t* u, const uint16_t* a,
+                                const uint16_t* dyexp, const void* w_gate,
+                                const uint8_t* w_gate_scale, const void* w_up,
+                                const uint8_t* w_up_scale, const void* w_down,
+                                const uint8_t* w_down_scale, uint16_t* dg, uint16_t* du,
+                                uint16_t* dxp, uint16_t* dw_gate, uint16_t* dw_up,
+                                uint16_t* dw_down, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

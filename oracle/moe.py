@@ -126,6 +126,32 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
+def _segments(offsets):
+    off = np.asarray(offsets, dtype=np.int64)
+    return [(e, off[e], off[e + 1]) for e in range(off.shape[0] - 1) if off[e + 1] > off[e]]
+
+
+def expert_gate_up(xp, offsets, w_gate, w_up):
+    """First grouped product with the SwiGLU activation: for expert e's rows,
+    G = X W_gate[e]^T,  U = X W_up[e]^T,  A = silu(G) * U.  Returns float64 (G, U, A)."""
+    X = _as_f64(xp)
+    f = w_gate.shape[1]
+    G = np.zeros((X.shape[0], f)); U = np.zeros_like(G)
+    for e, r0, r1 in _segments(offsets):
+        G[r0:r1] = X[r0:r1] @ _as_f64(w_gate[e]).T
+        U[r0:r1] = X[r0:r1] @ _as_f64(w_up[e]).T
+    return G, U, silu(G) * U
+
+
+def expert_down(a, offsets, w_down):
+    """Second grouped product: Yexp = A W_down[e]^T for expert e's rows (float64)."""
+    A = _as_f64(a)
+    Y = np.zeros((A.shape[0], w_down.shape[1]))
+    for e, r0, r1 in _segments(offsets):
+        Y[r0:r1] = A[r0:r1] @ _as_f64(w_down[e]).T
+    return Y
+
+
 def expert_ffn(xp, offsets, w_gate, w_up, w_down):
     """SwiGLU expert FFN on each expert's contiguous rows.
 
@@ -135,23 +161,8 @@ def expert_ffn(xp, offsets, w_gate, w_up, w_down):
     stays on the GPU": the per-expert products are one grouped operation.)
     Returns float64 (G, U, A, Yexp).
     """
-    X = _as_f64(xp)
-    n = X.shape[0]
-    off = np.asarray(offsets, dtype=np.int64)
-    E = off.shape[0] - 1
-    f = w_gate.shape[1]
-    d = w_down.shape[1]
-    G = np.zeros((n, f)); U = np.zeros((n, f)); A = np.zeros((n, f)); Y = np.zeros((n, d))
-    for e in range(E):
-        r0, r1 = off[e], off[e + 1]
-        if r1 == r0:
-            continue
-        Wg = _as_f64(w_gate[e]); Wu = _as_f64(w_up[e]); Wd = _as_f64(w_down[e])
-        G[r0:r1] = X[r0:r1] @ Wg.T
-        U[r0:r1] = X[r0:r1] @ Wu.T
-        A[r0:r1] = silu(G[r0:r1]) * U[r0:r1]
-        Y[r0:r1] = A[r0:r1] @ Wd.T
-    return G, U, A, Y
+    G, U, A = expert_gate_up(xp, offsets, w_gate, w_up)
+    return G, U, A, expert_down(A, offsets, w_down)
 
 
 # ------------------------------------------------------------------ backward
@@ -180,6 +191,32 @@ def swiglu_bwd(dA, G, U):
     return dG, dU
 
 
+def expert_down_bwd(dyexp, a, offsets, w_down, E):
+    """Backward of expert_down: dA = dYexp W_down[e]; dW_down[e] = dYexp_e^T A_e (zeros for
+    experts with no rows).  Returns float64 (dA [n,f], dW_down [E,d,f])."""
+    dY = _as_f64(dyexp); A = _as_f64(a)
+    d, f = w_down.shape[1], w_down.shape[2]
+    dA = np.zeros((dY.shape[0], f)); dW = np.zeros((E, d, f))
+    for e, r0, r1 in _segments(offsets):
+        dA[r0:r1] = dY[r0:r1] @ _as_f64(w_down[e])
+        dW[e] = dY[r0:r1].T @ A[r0:r1]
+    return dA, dW
+
+
+def expert_gate_up_bwd(xp, dG, dU, offsets, w_gate, w_up, E):
+    """Backward of the first product given dG, dU: dXp = dG W_gate[e] + dU W_up[e];
+    dW_gate[e] = dG_e^T X_e, dW_up[e] = dU_e^T X_e (zeros for experts with no rows).
+    Returns float64 (dXp [n,d], dW_gate [E,f,d], dW_up [E,f,d])."""
+    X = _as_f64(xp); dGf = _as_f64(dG); dUf = _as_f64(dU)
+    f, d = w_gate.shape[1], w_gate.shape[2]
+    dX = np.zeros((dGf.shape[0], d)); dWg = np.zeros((E, f, d)); dWu = np.zeros((E, f, d))
+    for e, r0, r1 in _segments(offsets):
+        dX[r0:r1] = dGf[r0:r1] @ _as_f64(w_gate[e]) + dUf[r0:r1] @ _as_f64(w_up[e])
+        dWg[e] = dGf[r0:r1].T @ X[r0:r1]
+        dWu[e] = dUf[r0:r1].T @ X[r0:r1]
+    return dX, dWg, dWu
+
+
 def expert_ffn_bwd(xp, G, U, A, dyexp, offsets, w_gate, w_up, w_down):
     """Backward of expert_ffn for each expert's rows (top-k choices held constant).
 
@@ -189,28 +226,11 @@ def expert_ffn_bwd(xp, G, U, A, dyexp, offsets, w_gate, w_up, w_down):
     Weight gradients of experts with no rows are exact zeros.
     Returns float64 dict with dA, dG, dU, dxp, dw_gate, dw_up, dw_down.
     """
-    X = _as_f64(xp); Gf = _as_f64(G); Uf = _as_f64(U); Af = _as_f64(A); dY = _as_f64(dyexp)
-    off = np.asarray(offsets, dtype=np.int64)
-    E = off.shape[0] - 1
-    f, d = w_gate.shape[1], w_gate.shape[2]
-    n = X.shape[0]
-    out = dict(dA=np.zeros((n, f)), dG=np.zeros((n, f)), dU=np.zeros((n, f)), dxp=np.zeros((n, d)),
-               dw_gate=np.zeros((E, f, d)), dw_up=np.zeros((E, f, d)), dw_down=np.zeros((E, d, f)))
-    for e in range(E):
-        r0, r1 = off[e], off[e + 1]
-        if r1 == r0:
-            continue
-        Wg = _as_f64(w_gate[e]); Wu = _as_f64(w_up[e]); Wd = _as_f64(w_down[e])
-        dA = dY[r0:r1] @ Wd
-        dG, dU = swiglu_bwd(dA, Gf[r0:r1], Uf[r0:r1])
-        out["dA"][r0:r1] = dA
-        out["dG"][r0:r1] = dG
-        out["dU"][r0:r1] = dU
-        out["dxp"][r0:r1] = dG @ Wg + dU @ Wu
-        out["dw_down"][e] = dY[r0:r1].T @ Af[r0:r1]
-        out["dw_gate"][e] = dG.T @ X[r0:r1]
-        out["dw_up"][e] = dU.T @ X[r0:r1]
-    return out
+    E = w_gate.shape[0]
+    dA, dWd = expert_down_bwd(dyexp, A, offsets, w_down, E)
+    dG, dU = swiglu_bwd(dA, _as_f64(G), _as_f64(U))
+    dX, dWg, dWu = expert_gate_up_bwd(xp, dG, dU, offsets, w_gate, w_up, E)
+    return dict(dA=dA, dG=dG, dU=dU, dxp=dX, dw_gate=dWg, dw_up=dWu, dw_down=dWd)
 
 
 def permute_bwd(dxp, dest, addend=None):

@@ -26,6 +26,8 @@ Logit constructions:
                most rows, some take none
 """
 
+import concurrent.futures
+import os
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -114,15 +116,20 @@ def gen_logits(cfg):
 
 def gen_expert_weights(cfg, experts=None):
     """(w_gate [E,f,d], w_up [E,f,d], w_down [E,d,f]) as bf16 bits; `experts` limits the
-    draw to a subset (the other experts' slices are left zero and must not be used)."""
+    draw to a subset (the other experts' slices are left zero and must not be used).  Experts
+    are drawn on a thread pool (each has its own streams, so the result does not depend on it)."""
     E, d, f = cfg.E, cfg.d, cfg.f
     wg = np.zeros((E, f, d), dtype=np.uint16)
     wu = np.zeros((E, f, d), dtype=np.uint16)
     wd = np.zeros((E, d, f), dtype=np.uint16)
-    for e in (range(E) if experts is None else experts):
+
+    def one(e):
         wg[e] = to_bf16_bits(_normal([cfg.seed, E, 2, e], (f, d), W_STD))
         wu[e] = to_bf16_bits(_normal([cfg.seed, E, 3, e], (f, d), W_STD))
         wd[e] = to_bf16_bits(_normal([cfg.seed, E, 4, e], (d, f), W_STD))
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, range(E) if experts is None else experts))
     return wg, wu, wd
 
 
@@ -136,4 +143,16 @@ def make_inputs(cfg, with_dy=True):
     out["w_gate"], out["w_up"], out["w_down"] = gen_expert_weights(cfg)
     if with_dy:
         out["dy"] = gen_dy(cfg)
+    return out
+
+
+def to_torch(inputs, device):
+    """Moves a make_inputs() dict to `device`: bf16 bit arrays become torch.bfloat16 tensors,
+    fp32 arrays torch.float32 (a layout change only)."""
+    out = {}
+    for key, a in inputs.items():
+        if a.dtype == np.uint16:
+            out[key] = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+        else:
+            out[key] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return out

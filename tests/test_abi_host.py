@@ -1,0 +1,93 @@
+"""Host-side checks of the C ABI (no GPU needed): the built library loads, exports every function
+declared in include/*.h with the binding's signature, and rejects bad host-visible arguments with
+the documented status before anything is enqueued (every call below fails argument checks, so
+no kernel is launched)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+try:
+    from expert_ffn_layer_top_amd import _lib
+except ImportError as exc:      # library not built: the build step is part of the check
+    pytest.fail(f"libmoe_mi355x.so not importable: {exc}", pytrace=False)
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b([a-z_][a-z0-9_]*)\s*\(", text):
+            name = m.group(1)
+            if name.startswith(("moe_", "mxfp8_")):
+                names.add(name)
+    return names
+
+
+def test_every_declared_function_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 21
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+        assert n in _lib.SIGNATURES, f"{n} exported but has no binding signature"
+    assert set(_lib.SIGNATURES) == names
+
+
+def test_version_and_status_strings():
+    assert _lib.lib.moe_abi_version() == 1
+    assert _lib.lib.moe_status_string(0) == b"ok"
+    assert b"workspace" in _lib.lib.moe_status_string(3)
+    assert _lib.lib.moe_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes_from_host_scalars():
+    L = _lib.lib
+    assert L.moe_route_workspace_bytes(8192, 64, 4) == 32 * 64 * 4
+    assert L.moe_route_workspace_bytes(1, 1, 1) == 4
+    assert L.moe_gg_workspace_bytes(0, 64, 32768, 2048, 1024) == 0          # bf16 needs none
+    mx = L.moe_gg_workspace_bytes(1, 64, 131072, 7168, 2048)
+    assert mx > 131072 * (7168 + 2 * 2048)                                    # monotone, covers the row operands
+    assert L.moe_gg_workspace_bytes(1, 64, 131072, 7168, 2048) <= L.moe_gg_workspace_bytes(1, 64, 131072 * 2, 7168, 2048)
+    assert L.moe_mx_pad_cap(512, 8) == 768 and L.moe_mx_pad_cap(100, 1) == 256
+    assert L.moe_router_bwd_workspace_bytes(32768, 7168, 64) == 32 * 7168 * 64 * 4
+
+
+def test_argument_checks_return_status_without_launching():
+    L = _lib.lib
+    fake = ctypes.c_void_p(0x1000)           # never dereferenced: every call fails its checks first
+    # route: T = 0, E too large, k > E, null pointer
+    assert L.moe_route_topk(fake, 0, 8, 2, *[fake] * 6, 0, fake, None, fake, 1 << 20, None) == UNSUPPORTED
+    assert L.moe_route_topk(fake, 16, 300, 2, *[fake] * 6, 0, fake, None, fake, 1 << 20, None) == UNSUPPORTED
+    assert L.moe_route_topk(fake, 16, 4, 5, *[fake] * 6, 0, fake, None, fake, 1 << 20, None) == UNSUPPORTED
+    assert L.moe_route_topk(None, 16, 8, 2, *[fake] * 6, 0, fake, None, fake, 1 << 20, None) == INVALID
+    # route: workspace too small
+    assert L.moe_route_topk(fake, 1000, 8, 2, *[fake] * 6, 32, fake, None, fake, 4, None) == WORKSPACE
+    assert L.moe_route_topk(fake, 1000, 8, 2, *[fake] * 6, 0, fake, None, fake, 1 << 20, None) == INVALID  # pad 0
+    # misaligned pointer
+    assert L.moe_unpermute_combine(ctypes.c_void_p(0x1002), fake, fake, 16, 64, 2, fake, None) == INVALID
+    # d not a multiple of 64
+    assert L.moe_permute(0, fake, None, fake, 16, 100, 2, fake, None, None) == UNSUPPORTED
+    # bf16 permute must not get scales; unknown dtype
+    assert L.moe_permute(0, fake, fake, fake, 16, 128, 2, fake, fake, None) == INVALID
+    assert L.moe_permute(7, fake, None, fake, 16, 128, 2, fake, None, None) == UNSUPPORTED
+    # quantiser: bad axis, cols not a multiple of 32
+    assert L.mxfp8_quantize(fake, 1, 64, 64, 2, fake, fake, None) == INVALID
+    assert L.mxfp8_quantize(fake, 1, 64, 48, 0, fake, fake, None) == UNSUPPORTED
+    # grouped GEMM: MXFP8 needs d, f multiples of 128 and a workspace
+    args = [fake] * 14
+    assert L.moe_grouped_gemm_swiglu(1, 8, 256, 192, 256, *args, 0, None) == UNSUPPORTED
+    assert L.moe_grouped_gemm_swiglu(1, 8, 256, 256, 256, *args, 0, None) == WORKSPACE
+    assert L.moe_grouped_gemm_swiglu(0, 8, 256, 128, 256, fake, fake, fake, *[fake] * 11, 0, None) == INVALID
+    # router backward: dw_r requested without workspace
+    assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, fake, None, 0, None) == WORKSPACE
+    msg = L.moe_last_error_string().decode()
+    assert "workspace" in msg

@@ -1,0 +1,146 @@
+"""GPU parity of the whole layer step (forward + backward) through expert_ffn_layer_top_amd.layer.
+
+  tiny      (256 tokens, d 128, 8 experts, top-2, d_ff 256, router weight): the float64 oracle
+            runs the whole layer independently, router included.
+  balanced  (8192 tokens, d 2048, 64 experts, top-4, d_ff 1024, round-robin logits): the
+            benchmarked workload, at full size, in the same launch configuration the benchmark
+            times.  Integer outputs are checked in full; float outputs on sampled rows, tokens
+            and experts the oracle recomputes one by one, each on the GPU's own inputs to that
+            step (chained), plus independent per-token checks of y.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codecs, moe, sampled
+from tests.gpu_util import BF16_TOL, assert_close, bits, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_layer(cfg, inputs):
+    import torch
+    from expert_ffn_layer_top_amd import layer
+    t = synth.to_torch(inputs, torch.device("cuda:0"))
+    w = layer.Weights(t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"))
+    ctx = layer.forward(t["x"], w, cfg.k, logits=t.get("logits"), mxfp8=cfg.mxfp8)
+    out = layer.backward(ctx, w, t["dy"])
+    torch.cuda.synchronize()
+    return ctx, out
+
+
+def test_tiny_layer_end_to_end_independent():
+    cfg = synth.CONFIGS["tiny"]
+    inputs = synth.make_inputs(cfg)
+    note("layer tiny fwd+bwd")
+    ctx, out = _run_layer(cfg, inputs)
+    x, w_r, wg, wu, wd, dy = (inputs[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "dy"))
+    logits = moe.router_project(x, w_r)
+    assert_close(host(ctx["logits"]), logits, 1e-5, "logits")
+    # routing: bit-exact on the GPU's own fp32 logits, and equal to the independent routing
+    # unless a k-th / (k+1)-th gap is below the fp32 noise of the logits
+    idx_c, gate_c, _ = moe.route_topk(host(ctx["logits"]), cfg.k)
+    assert np.array_equal(host(ctx["topk_idx"]), idx_c)
+    srt = np.sort(logits, axis=1)[:, ::-1]
+    gap = srt[:, cfg.k - 1] - srt[:, cfg.k]
+    near = gap < 1e-5 * np.max(np.abs(logits))
+    idx_i, _, _ = moe.route_topk(logits, cfg.k)
+    assert np.array_equal(host(ctx["topk_idx"])[~near], idx_i[~near])
+    assert not near.any(), "near-tie tokens: compare those in chained mode only"
+
+    fwd = moe.layer_forward(x, logits, cfg.k, wg, wu, wd)
+    assert np.array_equal(host(ctx["dest"]), fwd["dest"])
+    assert_close(codecs.bf16_to_f64(bits(ctx["y"])), fwd["y"], BF16_TOL, "y")
+    bwd = moe.layer_backward(fwd, dy, wg, wu, wd)
+    add, dwr = moe.router_project_bwd(x, w_r, bwd["d_logits"])
+    dx = moe.permute_bwd(bwd["dxp"], fwd["dest"], addend=add)
+    assert_close(codecs.bf16_to_f64(bits(out["dx"])), dx, BF16_TOL, "dx")
+    assert_close(host(out["d_logits"]), bwd["d_logits"], BF16_TOL, "d_logits")
+    assert_close(host(out["dw_r"]), dwr, BF16_TOL, "dw_r")
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        assert_close(codecs.bf16_to_f64(bits(out[key])), bwd[key], BF16_TOL, key)
+
+
+@pytest.fixture(scope="module")
+def balanced_run():
+    cfg = synth.CONFIGS["balanced"]
+    inputs = synth.make_inputs(cfg)
+    note(f"layer balanced fwd+bwd T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f}")
+    ctx, out = _run_layer(cfg, inputs)
+    return cfg, inputs, ctx, out
+
+
+def test_balanced_full_size_routing_and_permute(balanced_run):
+    cfg, inputs, ctx, _ = balanced_run
+    idx, gate, _ = moe.route_topk(inputs["logits"], cfg.k)
+    counts, off, dest, row_token, _ = moe.route_metadata(idx, cfg.E)
+    assert np.all(counts == 512)
+    assert np.array_equal(host(ctx["topk_idx"]), idx) and np.array_equal(host(ctx["dest"]), dest)
+    assert np.array_equal(host(ctx["offsets"]), off) and np.array_equal(host(ctx["row_token"]), row_token)
+    assert np.max(np.abs(host(ctx["topk_gate"]) - gate)) < 1e-5
+    assert np.array_equal(bits(ctx["xp"]), moe.permute(inputs["x"], dest))
+
+
+def test_balanced_full_size_forward_samples(balanced_run):
+    cfg, inputs, ctx, _ = balanced_run
+    rng = np.random.default_rng(0)
+    off = host(ctx["offsets"])
+    rows = np.sort(rng.choice(cfg.n, size=96, replace=False))
+    rows = np.concatenate([rows, [0, 511, 512, cfg.n - 1]])              # tile edges
+    experts = np.searchsorted(off, rows, side="right") - 1
+    xp = bits(ctx["xp"])
+    W = (inputs["w_gate"], inputs["w_up"], inputs["w_down"])
+    G, U, A, Y = sampled.ffn_forward_rows(xp[rows], experts, *W)
+    assert_close(codecs.bf16_to_f64(bits(ctx["g"])[rows]), G, BF16_TOL, "G rows")
+    assert_close(codecs.bf16_to_f64(bits(ctx["u"])[rows]), U, BF16_TOL, "U rows")
+    assert_close(codecs.bf16_to_f64(bits(ctx["a"])[rows]), A, BF16_TOL, "A rows")
+    assert_close(codecs.bf16_to_f64(bits(ctx["yexp"])[rows]), Y, BF16_TOL, "Yexp rows")
+    # y for sampled tokens, independently: sum_j g_j FFN_{e_j}(x_t)
+    toks = np.sort(rng.choice(cfg.T, size=24, replace=False))
+    dest = host(ctx["dest"])
+    gate = moe.route_topk(inputs["logits"][toks], cfg.k)[1]
+    trow = dest[toks].ravel()
+    texp = np.searchsorted(off, trow, side="right") - 1
+    _, _, _, Yt = sampled.ffn_forward_rows(xp[trow], texp, *W)
+    y_ref = np.einsum("tj,tjd->td", gate, Yt.reshape(len(toks), cfg.k, -1))
+    assert_close(codecs.bf16_to_f64(bits(ctx["y"])[toks]), y_ref, BF16_TOL, "y tokens")
+
+
+def test_balanced_full_size_backward_samples(balanced_run):
+    cfg, inputs, ctx, out = balanced_run
+    rng = np.random.default_rng(1)
+    off = host(ctx["offsets"])
+    dest = host(ctx["dest"])
+    gate = host(ctx["topk_gate"])
+    yexp = bits(ctx["yexp"])
+    # combine backward: full tensors, on the GPU's own yexp and gates
+    rdy, rdg = moe.combine_bwd(inputs["dy"], yexp, gate, dest)
+    assert_close(codecs.bf16_to_f64(bits(out["dyexp"])), rdy, BF16_TOL, "dyexp")
+    assert_close(host(out["d_gate"]), rdg, 1e-4, "d_gate")
+    assert_close(host(out["d_logits"]), moe.route_topk_bwd(gate, host(ctx["topk_idx"]), host(out["d_gate"]), cfg.E),
+                 1e-5, "d_logits")
+    W = (inputs["w_gate"], inputs["w_up"], inputs["w_down"])
+    rows = np.sort(rng.choice(cfg.n, size=96, replace=False))
+    experts = np.searchsorted(off, rows, side="right") - 1
+    dyexp = bits(out["dyexp"])
+    r = sampled.ffn_dgrad_rows(dyexp[rows], codecs.bf16_to_f64(bits(ctx["g"])[rows]),
+                               codecs.bf16_to_f64(bits(ctx["u"])[rows]), experts, *W)
+    assert_close(codecs.bf16_to_f64(bits(out["dg"])[rows]), r["dG"], BF16_TOL, "dG rows")
+    assert_close(codecs.bf16_to_f64(bits(out["du"])[rows]), r["dU"], BF16_TOL, "dU rows")
+    dg, du = bits(out["dg"]), bits(out["du"])
+    dxp_ref = sampled.ffn_dxp_rows(dg[rows], du[rows], experts, inputs["w_gate"], inputs["w_up"])
+    assert_close(codecs.bf16_to_f64(bits(out["dxp"])[rows]), dxp_ref, BF16_TOL, "dXp rows")
+    # weight gradients of sampled experts, on the GPU's own xp, A, dG, dU, dYexp
+    xp, a = bits(ctx["xp"]), bits(ctx["a"])
+    for e in (0, 37, cfg.E - 1):
+        r0, r1 = off[e], off[e + 1]
+        dwg, dwu, dwd = sampled.wgrad_expert(xp[r0:r1], a[r0:r1], dg[r0:r1], du[r0:r1], dyexp[r0:r1])
+        assert_close(codecs.bf16_to_f64(bits(out["dw_gate"])[e]), dwg, BF16_TOL, f"dW_gate[{e}]")
+        assert_close(codecs.bf16_to_f64(bits(out["dw_up"])[e]), dwu, BF16_TOL, f"dW_up[{e}]")
+        assert_close(codecs.bf16_to_f64(bits(out["dw_down"])[e]), dwd, BF16_TOL, f"dW_down[{e}]")
+    # dx for sampled tokens, on the GPU's own dXp
+    toks = np.sort(rng.choice(cfg.T, size=64, replace=False))
+    dxp = bits(out["dxp"])
+    dx_ref = moe.permute_bwd(dxp, dest[toks])
+    assert_close(codecs.bf16_to_f64(bits(out["dx"])[toks]), dx_ref, BF16_TOL, "dx tokens")
