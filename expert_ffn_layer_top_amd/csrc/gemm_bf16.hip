@@ -16,17 +16,30 @@
 //   WGRAD_DOWN  dW_down[e] = dYexp_e^T A_e                                         (K = rows of e)
 //   WGRAD_GU    dW_gate[e] = dG_e^T Xp_e,  dW_up[e] = dU_e^T Xp_e                   (K = rows of e)
 //
-// Tiling: 256 x 256 output tile per 256-thread workgroup, K step 64, four waves in a 2 x 2
-// grid, each wave owning 128 x 128 outputs as 8 x 8 MFMA 16x16 tiles (256 fp32 accumulators
-// per lane).  Operands are staged in LDS as [row][64 k] bf16 with a 16-byte-chunk XOR swizzle
-// (chunk ^ ((row ^ row >> 3) & 7)) so that both the MFMA fragment reads (16 consecutive rows,
-// one chunk) and the transposed writes (rows 8 apart) spread over all banks; two LDS stages
-// (128 KiB) double-buffer the K loop.  Operands stored K-contiguous are copied with 16-byte
-// loads; operands stored K-strided (the weights in the dgrad products, the token-major
-// activations in the wgrad products) are read as 8 rows x 16 bytes per lane and transposed
-// 8 x 8 in registers before the LDS store.  The MFMA computes the transposed tile
-// (weights / N side as the first operand), so each lane ends with 4 consecutive output
-// columns of one row and stores 8 bytes.
+// Tiling: 256 x 256 outputs per 256-thread workgroup, four waves in a 2 x 2 grid, each wave
+// owning 128 x 128 outputs as 8 x 8 MFMA 16x16 tiles (256 fp32 accumulators per lane).  K steps
+// of 32 run through a four-deep ring of LDS stages (4 x 32 KiB).
+//
+// Operand staging.  Every operand tile goes from HBM/L2 to LDS by the LDS-DMA form of the
+// buffer load (16 bytes per lane, written to a wave-contiguous 1 KiB LDS span), so no operand
+// passes through VGPRs and no wave spends VALU time on copies.  Two LDS layouts:
+//   KC  operand stored K-contiguous (rows x K): LDS [256 rows][32 k] (64 B rows); MFMA fragments
+//       are one ds_read_b128 per lane.
+//   KS  operand stored K-strided (K x columns: the weights in the dgrad products, the
+//       token-major activations in the wgrad products): LDS [32 k][256 columns] (512 B rows),
+//       kept in the source layout; fragments come from two ds_read_b64_tr_b16 per lane, which
+//       transpose 4 x 4 blocks of 16-bit elements across each group of 16 lanes.
+// Both layouts XOR-swizzle 16-byte chunks within a row (the DMA source address of each lane is
+// permuted to match), so fragment reads spread over all LDS banks.  Buffer descriptors bound
+// every operand to its valid extent: rows past an expert's last row (wgrad K tails) and past
+// the tensor end read as zeros.
+//
+// Pipeline.  Three K steps are in flight in a four-stage ring.  In the middle of step kt (after
+// its fourth MFMA row) every wave waits for its own DMA of tile kt+1 and joins a barrier; past it,
+// all of tile kt+1 is in LDS and every wave has finished reading tile kt-1, so the DMA of tile
+// kt+3 goes into that stage.  Fragment reads run one MFMA row ahead of their use.  The MFMA
+// computes the transposed tile (weights / N side as the first operand), so each lane ends with 4
+// consecutive output columns of one row.
 #include <type_traits>
 
 #include "common.h"
@@ -35,16 +48,46 @@ namespace moe {
 namespace gg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;
+constexpr int BK = 32;
 constexpr int NTH = 256;
-constexpr int ROW_BYTES = BK * 2;                 // 128 bytes per LDS row
-constexpr int TILE_BYTES = BM * ROW_BYTES;        // 32 KiB per operand per stage
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;        // 128 KiB
+constexpr int OP_BYTES = BM * BK * 2;             // 16 KiB per operand per stage
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;      // raw buffer, 32-bit data format (gfx9 family)
+
+// Four stages of each operand as eight distinct LDS objects: the compiler tracks outstanding
+// LDS-DMA per object, so a fragment read of one stage never waits for the DMA into another.  The
+// A stages fill the first 64 KiB and the B stages the next, so every fragment address is one
+// per-lane base plus a 16-bit immediate.
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a0[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a1[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a2[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a3[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b0[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b1[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b2[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b3[OP_BYTES];
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage_a() {
+  if constexpr (S == 0) return lds_a0;
+  else if constexpr (S == 1) return lds_a1;
+  else if constexpr (S == 2) return lds_a2;
+  else return lds_a3;
+}
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage_b() {
+  if constexpr (S == 0) return lds_b0;
+  else if constexpr (S == 1) return lds_b1;
+  else if constexpr (S == 2) return lds_b2;
+  else return lds_b3;
+}
 
 enum Mode { FWD1 = 0, FWD2 = 1, DGRAD1 = 2, DGRAD2 = 3, WGRAD_DOWN = 4, WGRAD_GU = 5 };
 
@@ -63,8 +106,7 @@ struct Params {
 };
 
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I = B .. E-1, so that indices into
-// the accumulator array stay static (a dynamically indexed accumulator array would be demoted
-// to scratch memory).
+// the accumulator and fragment arrays stay static (dynamic indexing would demote them to scratch).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (B < E) {
@@ -73,36 +115,43 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int chunk) { return r * ROW_BYTES + ((chunk ^ swz(r)) << 4); }
-
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// 8 x 8 transpose of bf16: in[i] holds k = i, columns 0..7; out[j] holds column j, k = 0..7.
-__device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint4& lo = in[2 * p];
-      const uint4& hi = in[2 * p + 1];
-      const uint32_t a = (j >> 1) == 0 ? lo.x : (j >> 1) == 1 ? lo.y : (j >> 1) == 2 ? lo.z : lo.w;
-      const uint32_t b = (j >> 1) == 0 ? hi.x : (j >> 1) == 1 ? hi.y : (j >> 1) == 2 ? hi.z : hi.w;
-      w[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    out[j] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 template <int MODE>
 struct Traits {
-  static constexpr bool A_KCONTIG = (MODE <= DGRAD2);
-  static constexpr bool B_KCONTIG = (MODE <= FWD2);
+  static constexpr bool A_KC = (MODE <= DGRAD2);   // M side K-contiguous
+  static constexpr bool B_KC = (MODE <= FWD2);     // N side K-contiguous
   static constexpr bool WGRAD = (MODE >= WGRAD_DOWN);
 };
 
-// Tile -> work mapping (computed per workgroup from device-resident offsets).
+// ---------------------------------------------------------------- LDS layouts
+
+// KC: row r (64 bytes = 4 chunks), chunk c stored at chunk position c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// KS: row k (512 bytes = 32 chunks), chunk c stored at chunk position c ^ ks_swz(k); the XOR
+// value is even, so the two chunks of an aligned 32-byte pair stay adjacent.
+__device__ __forceinline__ int ks_swz(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
+__device__ __forceinline__ int ks_off(int k, int c) { return k * 512 + ((c ^ ks_swz(k)) << 4); }
+
+// ---------------------------------------------------------------- buffer descriptors / DMA
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  const int nrec = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nrec, RSRC_WORD3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds), 16, voff, soff, 0, 0);
+}
+
+// Waits for this wave's LDS reads and all but the newest N of its vector-memory operations,
+// then joins the workgroup barrier.  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------- tile -> work
+
 struct Tile {
   int e;
   int m0;          // FWD/DGRAD: first row (absolute); WGRAD: first output row of dW
@@ -121,6 +170,9 @@ __device__ __forceinline__ int n_total(const Params& p) {
 }
 
 template <int MODE>
+__device__ __forceinline__ int m_total_wgrad(const Params& p) { return MODE == WGRAD_DOWN ? p.d : p.f; }
+
+template <int MODE>
 __device__ __forceinline__ int n_tile_width() { return MODE == FWD1 ? BN / 2 : BN; }
 
 template <int MODE>
@@ -131,109 +183,196 @@ __device__ __forceinline__ int k_total(const Params& p) {
   return 0;
 }
 
-// ---------------------------------------------------------------- operand loaders
+// Per-lane DMA offsets of one operand (4 instructions per lane per stage) and the descriptors.
+struct OpLoad {
+  __amdgpu_buffer_rsrc_t r0, r1;   // r1: second tensor (FWD1 B: W_up; DGRAD2: dU / W_up)
+  int vo[4];
+  int step;                        // bytes to advance per K step (KC: 64; KS: 32 rows)
+};
 
-// A side (rows of the output; the second MFMA operand).
-template <int MODE>
-__device__ __forceinline__ void load_a(const Params& p, const Tile& t, int kt, uint4 (&reg)[8]) {
-  const int tid = threadIdx.x;
-  if constexpr (Traits<MODE>::A_KCONTIG) {
-    const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
-    int k0 = kt * BK;
-    const uint16_t* base = p.a0;
-    if (MODE == DGRAD2 && k0 >= p.f) { base = p.a1; k0 -= p.f; }
+// KC operand, rows [row0, row0 + 256) of a row-major tensor with `ldb` bytes per row.
+// Wave w fills LDS rows 64w .. 64w + 63 with 4 instructions of 16 rows each.
+__device__ __forceinline__ void kc_offsets(int ldb, int (&vo)[4]) {
+  const int L = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = (L & 3) ^ ((L >> 4) & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = t.m0 + (tid >> 3) + 32 * i;
-      r = r < p.n ? r : p.n - 1;                       // rows past n: clamped, never stored
-      reg[i] = ld16(base + static_cast<long long>(r) * K + k0 + 8 * (tid & 7));
-    }
-  } else {
-    // WGRAD: M side is a token-major activation [n][Mtot], read K(token)-strided
-    const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
-    const uint16_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
-    const int m = t.m0 + 8 * (tid & 31);
-    const int kk = kt * BK + 8 * (tid >> 5);
+  for (int i = 0; i < 4; ++i) vo[i] = (64 * w + 16 * i + (L >> 2)) * ldb + 16 * c;
+}
+
+// KS operand, 32 K-rows x 256 columns; wave w fills LDS rows 8w .. 8w + 7, 2 rows per instruction.
+__device__ __forceinline__ void ks_offsets(int ldb, int (&vo)[4]) {
+  const int L = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = kk + i;
-      if (m < Mtot && k < t.k_len)
-        reg[i] = ld16(base + static_cast<long long>(t.k_begin + k) * Mtot + m);
-      else
-        reg[i] = make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int kr = 8 * w + 2 * i + (L >> 5);
+    vo[i] = kr * ldb + 16 * ((L & 31) ^ ks_swz(kr));
   }
 }
 
-// B side (columns of the output; the first MFMA operand).
-template <int MODE>
-__device__ __forceinline__ void load_b(const Params& p, const Tile& t, int kt, uint4 (&reg)[8]) {
-  const int tid = threadIdx.x;
-  if constexpr (MODE == FWD1) {
-    // LDS rows 0..127: W_gate[e] rows n0 + r; rows 128..255: W_up[e] rows n0 + r - 128
-    const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const uint16_t* base = (r < 128) ? p.b0 : p.b1;
-      int c = t.n0 + (r & 127);
-      c = c < p.f ? c : p.f - 1;
-      reg[i] = ld16(base + eoff + static_cast<long long>(c) * p.d + kt * BK + 8 * (tid & 7));
+// Issues the DMA of K step kt into stage S.  Steps past the last one (kt >= nk) read through an
+// empty descriptor, so the stage fills with zeros and its MFMAs add nothing.
+template <int MODE, int S>
+__device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& la, const OpLoad& lb, int kt, int nk) {
+  const int w = threadIdx.x >> 6;
+  const bool valid = kt < nk;
+  uint8_t* da = stage_a<S>() + w * 4096;
+  uint8_t* db = stage_b<S>() + w * 4096;
+  // ---- A (M side)
+  {
+    __amdgpu_buffer_rsrc_t r = la.r0;
+    int soff = kt * la.step;
+    if constexpr (MODE == DGRAD2) {
+      const int kf = p.f / BK;   // K steps per half
+      if (kt >= kf) { r = la.r1; soff = (kt - kf) * la.step; }
     }
-  } else if constexpr (MODE == FWD2) {
-    const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
+    if (!valid) { r = make_rsrc(p.a0, 0); soff = 0; }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int c = t.n0 + (tid >> 3) + 32 * i;
-      c = c < p.d ? c : p.d - 1;
-      reg[i] = ld16(p.b0 + eoff + static_cast<long long>(c) * p.f + kt * BK + 8 * (tid & 7));
-    }
-  } else {
-    // K-strided: element (k, n) at base + k * ld + n, 8 k-rows x 8 n per lane
-    const int n = t.n0 + 8 * (tid & 31);
-    const int kk = kt * BK + 8 * (tid >> 5);
-    if constexpr (MODE == DGRAD1) {
-      const uint16_t* base = p.b0 + static_cast<long long>(t.e) * p.d * p.f;   // W_down[e] [d][f]
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        reg[i] = (n < p.f) ? ld16(base + static_cast<long long>(kk + i) * p.f + n) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16(r, da + i * 1024, la.vo[i], soff);
+  }
+  // ---- B (N side)
+  {
+    __amdgpu_buffer_rsrc_t r = lb.r0;
+    int soff = kt * lb.step;
+    if constexpr (MODE == FWD1) {
+      if (w >= 2) r = lb.r1;
     } else if constexpr (MODE == DGRAD2) {
-      // k < f: W_gate[e] [f][d] row k; k >= f: W_up[e] row k - f (a 64-block never straddles)
-      const bool up = kk >= p.f;
-      const uint16_t* base = (up ? p.b1 : p.b0) + static_cast<long long>(t.e) * p.f * p.d;
-      const int k0 = up ? kk - p.f : kk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        reg[i] = (n < p.d) ? ld16(base + static_cast<long long>(k0 + i) * p.d + n) : make_uint4(0, 0, 0, 0);
-    } else {
-      // WGRAD: N side is a token-major activation [n][Ntot]
-      const int Ntot = n_total<MODE>(p);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = kk + i;
-        if (n < Ntot && k < t.k_len)
-          reg[i] = ld16(p.b0 + static_cast<long long>(t.k_begin + k) * Ntot + n);
-        else
-          reg[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int kf = p.f / BK;
+      if (kt >= kf) { r = lb.r1; soff = (kt - kf) * lb.step; }
     }
+    if (!valid) { r = make_rsrc(p.b0, 0); soff = 0; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(r, db + i * 1024, lb.vo[i], soff);
   }
 }
 
-template <bool KCONTIG>
-__device__ __forceinline__ void store_tile(uint8_t* lds, const uint4 (&reg)[8]) {
-  const int tid = threadIdx.x;
-  if constexpr (KCONTIG) {
+// ---------------------------------------------------------------- fragments
+
+// Per-lane fragment addresses, computed once.
+//   KC: fragment q (rows 16q .. 16q + 15 of the stage) of lane l sits at kc + 1024 q: the chunk
+//       swizzle (r >> 2) & 3 of row r = 16q + l % 16 does not depend on q.
+//   KS: fragment q (columns 16q .. 16q + 15) of lane l, half h (K = 8 (l / 16) + 4h .. + 3), is
+//       read at ks[h] ^ (q << 5): row k = 8 (l / 16) + 4h + (l % 16) / 4 and columns
+//       16q + 4 (l % 4) .. + 3; the row's swizzle only flips bits 5..7 of the byte address, the
+//       same bits q selects.
+struct FragAddr {
+  int a_kc, b_kc;
+  int a_ks[2], b_ks[2];
+};
+
+__device__ __forceinline__ int kc_lane() {
+  const int l = threadIdx.x & 63;
+  return kc_off(l & 15, l >> 4);
+}
+
+__device__ __forceinline__ int ks_lane(int h) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> 4, i = l & 15;
+  const int k = 8 * g + 4 * h + (i >> 2);
+  const int col = 4 * (i & 3);                   // fragment 0
+  return ks_off(k, col >> 3) + ((col & 7) << 1);
+}
+
+template <int MODE>
+__device__ __forceinline__ FragAddr frag_addr() {
+  FragAddr fa;
+  fa.a_kc = fa.b_kc = kc_lane();
+  fa.a_ks[0] = fa.b_ks[0] = ks_lane(0);
+  fa.a_ks[1] = fa.b_ks[1] = ks_lane(1);
+  return fa;
+}
+
+__device__ __forceinline__ bf16x8 read_kc(const uint8_t* stage, int lane_off, int q) {
+  return *reinterpret_cast<const bf16x8*>(stage + lane_off + 1024 * q);
+}
+
+__device__ __forceinline__ bf16x8 read_ks(const uint8_t* stage, const int (&ks)[2], int q) {
+  bf16x4 h[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(lds + lds_off((tid >> 3) + 32 * i, tid & 7)) = reg[i];
-  } else {
-    uint4 tr[8];
-    transpose8(reg, tr);
-    const int rb = tid & 31, kb = tid >> 5;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(lds + lds_off(8 * rb + j, kb)) = tr[j];
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint8_t* pa = stage + (ks[hh] ^ (q << 5));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pa));
+    h[hh] = __builtin_bit_cast(bf16x4, v);
   }
+  return bf16x8{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+}
+
+// Fragment q of the LDS B tile for MFMA tile i (FWD1 pairs gate rows with up rows), in units of
+// 16 rows (KC) or 16 columns (KS).
+template <int MODE>
+__device__ __forceinline__ int bfrag(int wn, int i) {
+  if constexpr (MODE == FWD1) return (i < 4) ? (4 * wn + i) : (8 + 4 * wn + (i - 4));
+  return 8 * wn + i;
+}
+
+// The transposing read takes no immediate offset, so every (stage, fragment, half) address is a
+// VGPR.  The KS bases are laundered once per K step so the compiler forms those addresses next to
+// their reads instead of keeping all of them live across the loop.
+// acc += x * y on the matrix core, accumulating in place in AGPRs.  Written as inline asm so the
+// accumulator is tied to one register quad for the whole loop: the builtin's untied form made the
+// register allocator rotate all 256 accumulators through copies every K step.  Callers cover the
+// hazards the compiler cannot see: wait states between the accumulator initialisation and the
+// first MFMA, and between the last MFMA and any VALU read of the accumulators.
+__device__ __forceinline__ void mfma_acc(f32x4& c, const bf16x8& x, const bf16x8& y) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+}
+
+// Orders the (zero) initialisation of one accumulator row before later volatile asm.
+__device__ __forceinline__ void pin_acc_row(f32x4 (&r)[8]) {
+  asm volatile("" : "+a"(r[0]), "+a"(r[1]), "+a"(r[2]), "+a"(r[3]), "+a"(r[4]), "+a"(r[5]), "+a"(r[6]),
+               "+a"(r[7]));
+}
+
+template <int MODE, int S>
+__device__ __forceinline__ bf16x8 read_a(const FragAddr& fa, int q) {
+  if constexpr (Traits<MODE>::A_KC) return read_kc(stage_a<S>(), fa.a_kc, q);
+  else return read_ks(stage_a<S>(), fa.a_ks, q);
+}
+
+template <int MODE, int S>
+__device__ __forceinline__ bf16x8 read_b(const FragAddr& fa, int q) {
+  if constexpr (Traits<MODE>::B_KC) return read_kc(stage_b<S>(), fa.b_kc, q);
+  else return read_ks(stage_b<S>(), fa.b_ks, q);
+}
+
+// One K step of tile kt (stage S), as 8 rows of 8 MFMAs; row i multiplies B fragment i by the
+// 8 A fragments.  Fragment reads run one row ahead of their use, from two small register sets:
+//   a[8]      A fragments of tile kt (read during the previous step), an[8] those of tile kt+1;
+//   b[2]      ping-pong: B fragment i+1 is read while row i runs.
+// The barrier before row 4 opens tile kt+1: each wave first waits for its own DMA of that tile
+// (one newer tile, 8 DMA instructions, stays in flight), and past the barrier every wave has
+// also finished reading tile kt-1, whose stage then receives the DMA of tile kt+3.  Rows 4..7
+// read the A fragments of tile kt+1 (two per row) and row 7 its first B fragment.
+template <int MODE, int S>
+__device__ __forceinline__ void k_step(const Params& p, const OpLoad& la, const OpLoad& lb, const FragAddr& fa_in,
+                                       int kt, int nk, bf16x8 (&a)[8], bf16x8 (&an)[8], bf16x8 (&b)[2],
+                                       f32x4 (&acc)[8][8]) {
+  constexpr int SN = (S + 1) & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qa = 8 * (wave >> 1), wn = wave & 1;
+  FragAddr fa = fa_in;
+  if constexpr (!Traits<MODE>::A_KC) asm volatile("" : "+v"(fa.a_ks[0]), "+v"(fa.a_ks[1]));
+  if constexpr (!Traits<MODE>::B_KC) asm volatile("" : "+v"(fa.b_ks[0]), "+v"(fa.b_ks[1]));
+  constexpr int RB = Traits<MODE>::B_KC ? 1 : 2;   // LDS reads per B fragment
+  constexpr int RA = Traits<MODE>::A_KC ? 1 : 2;
+  static_for<0, 8>([&](auto i) {
+    if constexpr (i == 4) {
+      wait_barrier<8>();
+      issue_stage<MODE, (S + 3) & 3>(p, la, lb, kt + 3, nk);
+    }
+    if constexpr (i < 7) b[(i + 1) & 1] = read_b<MODE, S>(fa, bfrag<MODE>(wn, i + 1));
+    else b[0] = read_b<MODE, SN>(fa, bfrag<MODE>(wn, 0));
+    if constexpr (i >= 4) {
+      an[2 * (i - 4)] = read_a<MODE, SN>(fa, qa + 2 * (i - 4));
+      an[2 * (i - 4) + 1] = read_a<MODE, SN>(fa, qa + 2 * (i - 4) + 1);
+    }
+    static_for<0, 8>([&](auto j) {
+      mfma_acc(acc[i][j], b[i & 1], a[j]);
+    });
+    // keep this row's reads ahead of its MFMAs (the DMA of row 4 goes first)
+    if constexpr (i == 4) __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RB + (i >= 4 ? 2 * RA : 0), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  });
 }
 
 // ---------------------------------------------------------------- epilogue helpers
@@ -248,7 +387,6 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 
 template <int MODE>
 __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int s_pre[257];     // FWD/DGRAD: prefix of m-tiles per expert
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -271,8 +409,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     __syncthreads();
     total_tiles = s_pre[p.E] * ntiles_n;
   } else {
-    const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
-    const int mt = (Mtot + BM - 1) / BM;
+    const int mt = (m_total_wgrad<MODE>(p) + BM - 1) / BM;
     total_tiles = p.E * mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
   }
   const int tot8 = (total_tiles + 7) & ~7;
@@ -282,7 +419,6 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   if (lid >= total_tiles) return;
 
   Tile t;
-  int nk;
   if constexpr (!Traits<MODE>::WGRAD) {
     const int mt_glob = lid / ntiles_n;
     const int nt = lid - mt_glob * ntiles_n;
@@ -298,9 +434,8 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     t.half = 0;
     t.k_begin = 0;
     t.k_len = k_total<MODE>(p);
-    nk = t.k_len / BK;
   } else {
-    const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
+    const int Mtot = m_total_wgrad<MODE>(p);
     const int mt = (Mtot + BM - 1) / BM;
     const int mtt = mt * (MODE == WGRAD_GU ? 2 : 1);
     const int per_e = mtt * ntiles_n;
@@ -314,7 +449,76 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     t.n0 = nt * BN;
     t.k_begin = p.offsets[t.e];
     t.k_len = p.offsets[t.e + 1] - t.k_begin;
-    nk = (t.k_len + BK - 1) / BK;
+  }
+  const int nk = (t.k_len + BK - 1) / BK;
+
+  // ---- operand descriptors, bounded to each operand's valid extent
+  OpLoad la, lb;
+  if constexpr (MODE == FWD1 || MODE == FWD2 || MODE == DGRAD1) {
+    const int K = k_total<MODE>(p);
+    const long long rem_rows = static_cast<long long>(p.n) - t.m0;
+    la.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K * 2);
+    la.r1 = la.r0;
+    la.step = BK * 2;
+    kc_offsets(K * 2, la.vo);
+  } else if constexpr (MODE == DGRAD2) {
+    const long long rem_rows = static_cast<long long>(p.n) - t.m0;
+    la.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
+    la.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
+    la.step = BK * 2;
+    kc_offsets(p.f * 2, la.vo);
+  } else {
+    // WGRAD: M side is a token-major activation [n][Mtot], rows k_begin .. k_begin + k_len
+    const int Mtot = m_total_wgrad<MODE>(p);
+    const uint16_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
+    la.r0 = make_rsrc(base + static_cast<long long>(t.k_begin) * Mtot + t.m0,
+                      static_cast<long long>(t.k_len) * Mtot * 2 - t.m0 * 2);
+    la.r1 = la.r0;
+    la.step = BK * Mtot * 2;
+    ks_offsets(Mtot * 2, la.vo);
+  }
+  if constexpr (MODE == FWD1) {
+    // rows 0..127 of the B tile: W_gate[e] rows n0 ..; rows 128..255: W_up[e] rows n0 ..
+    const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
+    const long long bytes = static_cast<long long>(p.f - t.n0) * p.d * 2;
+    lb.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
+    lb.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
+    lb.step = BK * 2;
+    // wave w fills rows 64w..: waves 2, 3 start again at row 0 of W_up
+    const int L = tid & 63;
+    const int c = (L & 3) ^ ((L >> 4) & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lb.vo[i] = (64 * (wave & 1) + 16 * i + (L >> 2)) * p.d * 2 + 16 * c;
+  } else if constexpr (MODE == FWD2) {
+    // W_down[e] [d][f], rows n0 .. (K = f contiguous)
+    const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
+    lb.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.f, static_cast<long long>(p.d - t.n0) * p.f * 2);
+    lb.r1 = lb.r0;
+    lb.step = BK * 2;
+    kc_offsets(p.f * 2, lb.vo);
+  } else if constexpr (MODE == DGRAD1) {
+    // W_down[e] [d][f]: element (k = d index, n = f index), rows k, columns n0 ..
+    const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
+    lb.r0 = make_rsrc(p.b0 + eoff + t.n0, static_cast<long long>(p.d) * p.f * 2 - t.n0 * 2);
+    lb.r1 = lb.r0;
+    lb.step = BK * p.f * 2;
+    ks_offsets(p.f * 2, lb.vo);
+  } else if constexpr (MODE == DGRAD2) {
+    // W_gate[e] / W_up[e] [f][d]: element (k = f index, n = d index)
+    const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
+    const long long bytes = static_cast<long long>(p.f) * p.d * 2 - t.n0 * 2;
+    lb.r0 = make_rsrc(p.b0 + eoff + t.n0, bytes);
+    lb.r1 = make_rsrc(p.b1 + eoff + t.n0, bytes);
+    lb.step = BK * p.d * 2;
+    ks_offsets(p.d * 2, lb.vo);
+  } else {
+    // WGRAD: N side is a token-major activation [n][Ntot]
+    const int Ntot = n_total<MODE>(p);
+    lb.r0 = make_rsrc(p.b0 + static_cast<long long>(t.k_begin) * Ntot + t.n0,
+                      static_cast<long long>(t.k_len) * Ntot * 2 - t.n0 * 2);
+    lb.r1 = lb.r0;
+    lb.step = BK * Ntot * 2;
+    ks_offsets(Ntot * 2, lb.vo);
   }
 
   f32x4 acc[8][8];
@@ -323,52 +527,31 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // LDS B rows owned by this wave for MFMA tile i (FWD1 pairs gate rows with up rows)
-  auto brow = [&](int i) -> int {
-    if constexpr (MODE == FWD1) return (i < 4) ? (64 * wn + 16 * i) : (128 + 64 * wn + 16 * (i - 4));
-    return 128 * wn + 16 * i;
-  };
-
-  uint4 ra[8], rb[8];
   if (nk > 0) {
-    load_a<MODE>(p, t, 0, ra);
-    load_b<MODE>(p, t, 0, rb);
-    store_tile<Traits<MODE>::A_KCONTIG>(lds, ra);
-    store_tile<Traits<MODE>::B_KCONTIG>(lds + TILE_BYTES, rb);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = lds + (kt & 1) * STAGE_BYTES;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_a<MODE>(p, t, kt + 1, ra);
-      load_b<MODE>(p, t, kt + 1, rb);
+    // ---- prologue: tiles 0..2 in flight, fragments of tile 0 read
+    // accumulator initialisation -> first MFMA: pin the zeroed registers ahead of the wait states
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
+    asm volatile("s_nop 7" ::: "memory");
+    issue_stage<MODE, 0>(p, la, lb, 0, nk);
+    issue_stage<MODE, 1>(p, la, lb, 1, nk);
+    issue_stage<MODE, 2>(p, la, lb, 2, nk);
+    const FragAddr fa = frag_addr<MODE>();
+    wait_barrier<16>();
+    const int qa = 8 * (wave >> 1);
+    bf16x8 fa0[8], fa1[8], fb[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fa0[j] = read_a<MODE, 0>(fa, qa + j);
+    fb[0] = read_b<MODE, 0>(fa, bfrag<MODE>(wn, 0));
+    for (int kt = 0; kt < nk; kt += 4) {
+      k_step<MODE, 0>(p, la, lb, fa, kt, nk, fa0, fa1, fb, acc);
+      k_step<MODE, 1>(p, la, lb, fa, kt + 1, nk, fa1, fa0, fb, acc);
+      k_step<MODE, 2>(p, la, lb, fa, kt + 2, nk, fa0, fa1, fb, acc);
+      k_step<MODE, 3>(p, la, lb, fa, kt + 3, nk, fa1, fa0, fb, acc);
     }
-    const uint8_t* sa = cur;
-    const uint8_t* sb = cur + TILE_BYTES;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int chunk = 4 * s + (lane >> 4);
-      bf16x8 fa[8], fb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        fa[j] = *reinterpret_cast<const bf16x8*>(sa + lds_off(128 * wm + 16 * j + (lane & 15), chunk));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        fb[i] = *reinterpret_cast<const bf16x8*>(sb + lds_off(brow(i) + (lane & 15), chunk));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], fa[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint8_t* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-      store_tile<Traits<MODE>::A_KCONTIG>(nxt, ra);
-      store_tile<Traits<MODE>::B_KCONTIG>(nxt + TILE_BYTES, rb);
-    }
-    __syncthreads();
+    // no LDS-DMA may still be writing when the workgroup ends; the last MFMA results settle
+    // before the epilogue's VALU reads them
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
   }
 
   // ---- epilogue: lane holds, for MFMA tile (i, j), output row 16j + lane%16 of the wave's
@@ -421,7 +604,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     const int Ntot = n_total<MODE>(p);
     uint16_t* out = p.o0;
     if constexpr (Traits<MODE>::WGRAD) {
-      const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
+      const int Mtot = m_total_wgrad<MODE>(p);
       out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
     }
     static_for<0, 8>([&](auto j) {
@@ -451,18 +634,13 @@ inline long long grid_upper(int mode, int E, int n, int d, int f) {
 
 template <int MODE>
 int launch(const Params& p, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    // Raises the dynamic-LDS limit for this kernel.  Advisory: where the runtime does not take the
-    // attribute, the launch below reports any real problem, so its status is cleared, not returned.
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<MODE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    (void)hipGetLastError();
-    attr_set = true;
-  }
   const long long g = (grid_upper(MODE, p.E, p.n, p.d, p.f) + 7) / 8 * 8;
   MOE_REQUIRE(g < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many tiles");
-  grouped_gemm_kernel<MODE><<<static_cast<unsigned>(g), NTH, LDS_BYTES, s>>>(p);
+  // every buffer offset the kernel forms stays below 2^31 bytes
+  MOE_REQUIRE(static_cast<long long>(p.n) * (p.d > p.f ? p.d : p.f) * 2 < 0x7fffffffLL &&
+                  static_cast<long long>(p.d) * p.f * 2 < 0x7fffffffLL,
+              MOE_ERR_UNSUPPORTED, "bf16 grouped GEMM: an operand exceeds 2 GiB");
+  grouped_gemm_kernel<MODE><<<static_cast<unsigned>(g), NTH, 0, s>>>(p);
   return check_launch("grouped_gemm_bf16");
 }
 
