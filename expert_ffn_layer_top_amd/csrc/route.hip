@@ -5,14 +5,16 @@
 // (routing metadata stays on the device, so the host never waits for a copy back).
 //
 // Three kernels, all sized from host scalars (no host sync):
-//   route_topk_local   one wave per token: k rounds of a wave-wide arg-max over packed
-//                      (order-preserving logit bits, inverted expert id) keys, gates, probs;
-//                      then, per block of 256 tokens, a stable rank of every (token, slot)
-//                      among the block's rows of the same expert (ballot-based match on the
-//                      expert-id bits + popcount under the lane mask) and the block's
-//                      per-expert histogram.
-//   route_scan         one block: per-expert exclusive scan over blocks (in place), counts,
-//                      offsets, padded offsets.
+//   route_topk_local   16 lanes per token, 64 tokens per 1024-thread block: k rounds of a
+//                      16-lane arg-max over packed (order-preserving
+//                      logit bits, inverted expert id) keys, the gates and the optional probs.
+//                      Each (token, slot) then sets its token's bit in a per-expert 64-bit LDS
+//                      mask (atomic OR, order-free), so the stable rank of a row among the
+//                      block's rows of the same expert is a popcount of the lower bits, and
+//                      the block's per-expert count is the mask's popcount.
+//   route_scan         one block: per-expert exclusive scan over blocks (in place; 1024 / E'
+//                      partial chains per expert, E' = E rounded up to a power of two),
+//                      counts, offsets, padded offsets.
 //   route_finalize     dest = offsets[e] + rows of e in earlier blocks + rank in block;
 //                      row_token[dest] = token.
 #include <cmath>
@@ -22,8 +24,10 @@
 namespace moe {
 namespace {
 
-constexpr int kRouteBlock = 256;   // tokens (and threads) per block
+constexpr int kRouteBlock = 64;    // tokens per block (one bit each in a 64-bit mask)
+constexpr int kGroup = 16;         // lanes per token
 constexpr int kMaxK = 16;
+constexpr int kMaxE = 256;
 
 // Order-preserving map of a float to uint32 (larger float -> larger key); -0 is folded to +0
 // so that equal logits compare equal.
@@ -38,161 +42,172 @@ __device__ __forceinline__ float key_float(uint32_t key) {
   return __uint_as_float(u);
 }
 
-__global__ __launch_bounds__(kRouteBlock) void route_topk_local(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate, float* __restrict__ probs, int32_t* __restrict__ local_rank,
-    int32_t* __restrict__ hist) {
-  __shared__ int s_idx[kRouteBlock][kMaxK];
-  __shared__ int s_cnt[kRouteBlock / 64][256];
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const long long t0 = static_cast<long long>(blockIdx.x) * kRouteBlock;
-
-  for (int i = tid; i < (kRouteBlock / 64) * 256; i += kRouteBlock) (&s_cnt[0][0])[i] = 0;
-
-  // ---- phase 1: top-k per token, one wave per token
-  for (int i = 0; i < 64; ++i) {
-    const int tl = w * 64 + i;
-    const long long t = t0 + tl;
-    if (t >= T) break;
-    const float* row = logits + t * E;
-    float v[4];
-    unsigned long long key[4];
+template <class T>
+__device__ __forceinline__ T group_max(T v) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = (e < E) ? row[e] : 0.f;
-      key[q] = (e < E) ? ((static_cast<unsigned long long>(float_key(v[q])) << 32) | (255u - e)) : 0ull;
-    }
-    int my_e = 0;
-    float my_l = 0.f;
-    float l0 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      unsigned long long best = key[0];
-#pragma unroll
-      for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
-      best = wave_max_u64(best);
-      const int e = 255 - static_cast<int>(best & 0xffu);
-      const float lv = key_float(static_cast<uint32_t>(best >> 32));
-      if (j == 0) l0 = lv;
-      if (lane == j) { my_e = e; my_l = lv; }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lane + 64 * q == e) key[q] = 0ull;
-    }
-    // gates: softmax over the chosen logits (the full-softmax denominator cancels)
-    const float ex = (lane < k) ? expf(my_l - l0) : 0.f;
-    const float den = wave_sum(ex);
-    if (lane < k) {
-      topk_idx[t * k + lane] = my_e;
-      topk_gate[t * k + lane] = ex / den;
-      s_idx[tl][lane] = my_e;
-    }
-    if (probs != nullptr) {
-      float p[4];
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        p[q] = (lane + 64 * q < E) ? expf(v[q] - l0) : 0.f;
-        s += p[q];
-      }
-      s = wave_sum(s);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lane + 64 * q < E) probs[t * E + lane + 64 * q] = p[q] / s;
-    }
+  for (int o = kGroup / 2; o > 0; o >>= 1) {
+    const T w = __shfl_xor(v, o, kGroup);
+    v = w > v ? w : v;
   }
-  __syncthreads();
+  return v;
+}
 
-  // ---- phase 2: stable rank within each 64-token group (wave), per expert
-  const int tl = tid;
-  const bool valid = (t0 + tl) < T;
-  int my_exp[kMaxK], rank[kMaxK], total[kMaxK];
+__device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    my_exp[j] = (j < k && valid) ? s_idx[tl][j] : 256;
-    rank[j] = 0;
-    total[j] = 0;
-  }
-  const unsigned long long lt = __lanemask_lt();
-#pragma unroll
-  for (int jp = 0; jp < kMaxK; ++jp) {
-    if (jp < k) {
-    const int ej = my_exp[jp];
-    unsigned long long b[9];
-#pragma unroll
-    for (int bit = 0; bit < 9; ++bit) b[bit] = __ballot((ej >> bit) & 1);
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      unsigned long long m = ~0ull;
-#pragma unroll
-      for (int bit = 0; bit < 9; ++bit) m &= ((my_exp[j] >> bit) & 1) ? b[bit] : ~b[bit];
-      rank[j] += __popcll(m & lt);
-      total[j] += __popcll(m);
-    }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j < k && valid && rank[j] == total[j] - 1) s_cnt[w][my_exp[j]] = total[j];
-  __syncthreads();
+  for (int o = kGroup / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kGroup);
+  return v;
+}
 
-  // ---- phase 3: rank within the block, and the block's histogram
-  if (valid) {
+// 16 lanes per token; lane g of a token holds experts g, g + 16, ... (NQ = ceil(E / 16) slots).
+template <int NQ>
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int g, int& my_e,
+                                           float& my_gate, float* __restrict__ prow) {
+  float v[NQ];
+  unsigned long long key[NQ];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= k) continue;
-      int base = 0;
-      for (int wp = 0; wp < w; ++wp) base += s_cnt[wp][my_exp[j]];
-      local_rank[(t0 + tl) * k + j] = base + rank[j];
-    }
+  for (int q = 0; q < NQ; ++q) {
+    const int e = g + kGroup * q;
+    v[q] = (e < E) ? row[e] : 0.f;
+    key[q] = (e < E) ? ((static_cast<unsigned long long>(float_key(v[q])) << 32) | (255u - e)) : 0ull;
   }
-  for (int e = tid; e < E; e += kRouteBlock) {
-    int s = 0;
+  my_e = 0;
+  float my_l = 0.f, l0 = 0.f;
+  for (int j = 0; j < k; ++j) {
+    unsigned long long best = key[0];
 #pragma unroll
-    for (int wp = 0; wp < kRouteBlock / 64; ++wp) s += s_cnt[wp][e];
-    hist[static_cast<long long>(blockIdx.x) * E + e] = s;
+    for (int q = 1; q < NQ; ++q) best = key[q] > best ? key[q] : best;
+    best = group_max(best);
+    const int e = 255 - static_cast<int>(best & 0xffu);
+    const float lv = key_float(static_cast<uint32_t>(best >> 32));
+    if (j == 0) l0 = lv;
+    if (g == j) { my_e = e; my_l = lv; }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (g + kGroup * q == e) key[q] = 0ull;
+  }
+  // gates: softmax over the chosen logits (the full-softmax denominator cancels)
+  const float ex = (g < k) ? expf(my_l - l0) : 0.f;
+  const float den = group_sum(ex);
+  my_gate = ex / den;
+  if (prow != nullptr) {
+    float pe[NQ];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      pe[q] = (g + kGroup * q < E) ? expf(v[q] - l0) : 0.f;
+      s += pe[q];
+    }
+    s = group_sum(s);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (g + kGroup * q < E) prow[g + kGroup * q] = pe[q] / s;
   }
 }
 
-// Single block.  hist[b][e] becomes the exclusive prefix over blocks b' < b for expert e.
-__global__ __launch_bounds__(256) void route_scan(int32_t* __restrict__ hist, int nb, int E,
-                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ offsets_pad, int pad) {
-  __shared__ int s_a[256];
-  __shared__ int s_b[256];
-  const int e = threadIdx.x;
-  int run = 0;
+template <int NQ>
+__global__ __launch_bounds__(1024) void route_topk_local(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_gate, float* __restrict__ probs, int32_t* __restrict__ local_rank,
+    int32_t* __restrict__ hist) {
+  __shared__ unsigned long long s_mask[kMaxE];
+  __shared__ int s_e[kRouteBlock][kMaxK];
+  const int tid = threadIdx.x;
+  const int g = tid & (kGroup - 1);
+  const long long t0 = static_cast<long long>(blockIdx.x) * kRouteBlock;
+  for (int e = tid; e < E; e += 1024) s_mask[e] = 0ull;
+  __syncthreads();
+
+  // ---- top-k, one token per 16 lanes
+  {
+    const int tl = tid >> 4;
+    const long long t = t0 + tl;
+    if (t < T) {   // uniform across the token's 16 lanes
+      int my_e;
+      float my_gate;
+      topk_token<NQ>(logits + t * E, E, k, g, my_e, my_gate, probs != nullptr ? probs + t * E : nullptr);
+      if (g < k) {
+        topk_idx[t * k + g] = my_e;
+        topk_gate[t * k + g] = my_gate;
+        s_e[tl][g] = my_e;
+        atomicOr(&s_mask[my_e], 1ull << tl);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- stable rank within the block: rows of the same expert from earlier tokens
+  for (int i = tid; i < kRouteBlock * k; i += 1024) {
+    const int tl = i / k, j = i - tl * k;
+    const long long t = t0 + tl;
+    if (t < T) {
+      const int e = s_e[tl][j];
+      local_rank[t * k + j] = __popcll(s_mask[e] & ((1ull << tl) - 1ull));
+    }
+  }
+  for (int e = tid; e < E; e += 1024) hist[static_cast<long long>(blockIdx.x) * E + e] = __popcll(s_mask[e]);
+}
+
+// Single block of 1024 threads.  hist[b][e] becomes the exclusive prefix over blocks b' < b for
+// expert e.  Thread (part, e) owns a contiguous run of blocks; the runs' sums are scanned
+// through LDS, then every run rewrites its entries as prefixes.
+__global__ __launch_bounds__(1024) void route_scan(int32_t* __restrict__ hist, int nb, int E, int ep_log2,
+                                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ offsets_pad, int pad) {
+  __shared__ int s_part[1024];
+  __shared__ int s_a[kMaxE];
+  __shared__ int s_b[kMaxE];
+  const int ep = 1 << ep_log2;                 // E rounded up to a power of two
+  const int e = threadIdx.x & (ep - 1);
+  const int part = threadIdx.x >> ep_log2;
+  const int nparts = 1024 >> ep_log2;
+  const int per = (nb + nparts - 1) / nparts;
+  const int b0 = min(nb, part * per);
+  const int b1 = min(nb, b0 + per);
+  int sum = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int v = hist[static_cast<long long>(b) * E + e];
-      hist[static_cast<long long>(b) * E + e] = run;
+    for (int b = b0; b < b1; ++b) sum += hist[static_cast<long long>(b) * E + e];
+  }
+  s_part[threadIdx.x] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int q = 0; q < part; ++q) run += s_part[(q << ep_log2) + e];
+  if (e < E) {
+    for (int b = b0; b < b1; ++b) {
+      const long long o = static_cast<long long>(b) * E + e;
+      const int v = hist[o];
+      hist[o] = run;
       run += v;
     }
-    counts[e] = run;
   }
-  const int padded = (e < E) ? (run + pad - 1) / pad * pad : 0;
-  s_a[e] = (e < E) ? run : 0;
-  s_b[e] = padded;
+  if (threadIdx.x < kMaxE) {
+    const int ee = threadIdx.x;
+    int total = 0;
+    if (ee < E)
+      for (int q = 0; q < nparts; ++q) total += s_part[(q << ep_log2) + ee];
+    if (ee < E) counts[ee] = total;
+    s_a[ee] = (ee < E) ? total : 0;
+    s_b[ee] = (ee < E) ? (total + pad - 1) / pad * pad : 0;
+  }
   __syncthreads();
-  // inclusive Hillis-Steele scan over 256 entries (two arrays at once)
-  for (int o = 1; o < 256; o <<= 1) {
-    const int a = (e >= o) ? s_a[e - o] : 0;
-    const int b = (e >= o) ? s_b[e - o] : 0;
+  // inclusive Hillis-Steele scan over 256 entries (two arrays at once) by the first 256 threads
+  const bool lead = threadIdx.x < kMaxE;
+  const int ee = threadIdx.x;
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    int a = 0, b = 0;
+    if (lead && ee >= o) { a = s_a[ee - o]; b = s_b[ee - o]; }
     __syncthreads();
-    s_a[e] += a;
-    s_b[e] += b;
+    if (lead) { s_a[ee] += a; s_b[ee] += b; }
     __syncthreads();
   }
-  if (e < E) {
-    offsets[e + 1] = s_a[e];
-    if (offsets_pad != nullptr) offsets_pad[e + 1] = s_b[e];
-  }
-  if (e == 0) {
-    offsets[0] = 0;
-    if (offsets_pad != nullptr) offsets_pad[0] = 0;
+  if (lead) {
+    if (ee < E) {
+      offsets[ee + 1] = s_a[ee];
+      if (offsets_pad != nullptr) offsets_pad[ee + 1] = s_b[ee];
+    }
+    if (ee == 0) {
+      offsets[0] = 0;
+      if (offsets_pad != nullptr) offsets_pad[0] = 0;
+    }
   }
 }
 
@@ -270,9 +285,16 @@ extern "C" int moe_route_topk(const float* logits, int T, int E, int k, int32_t*
   hipStream_t s = as_stream(stream);
   const int nb = (T + kRouteBlock - 1) / kRouteBlock;
   int32_t* hist = static_cast<int32_t*>(ws);
-  route_topk_local<<<nb, kRouteBlock, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
+  const int nq = (E + kGroup - 1) / kGroup;
+  if (nq <= 1) route_topk_local<1><<<nb, 1024, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
+  else if (nq <= 2) route_topk_local<2><<<nb, 1024, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
+  else if (nq <= 4) route_topk_local<4><<<nb, 1024, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
+  else if (nq <= 8) route_topk_local<8><<<nb, 1024, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
+  else route_topk_local<16><<<nb, 1024, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
   if (int st = check_launch("route_topk_local")) return st;
-  route_scan<<<1, 256, 0, s>>>(hist, nb, E, counts, offsets, offsets_pad, offsets_pad ? pad : 1);
+  int ep_log2 = 0;
+  while ((1 << ep_log2) < E) ++ep_log2;
+  route_scan<<<1, 1024, 0, s>>>(hist, nb, E, ep_log2, counts, offsets, offsets_pad, offsets_pad ? pad : 1);
   if (int st = check_launch("route_scan")) return st;
   const long long n = static_cast<long long>(T) * k;
   route_finalize<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(topk_idx, dest, hist, offsets, T, k, E, row_token);

@@ -24,19 +24,11 @@ __device__ __forceinline__ void load_dest(const int32_t* __restrict__ dest, long
   for (int j = 0; j < kMaxK; ++j) rows[j] = __shfl(mine, j, 64);
 }
 
-// Copies `chunks` 16-byte chunks of row t of `src` to the k rows `rows[j]` of `dst`
-// (row pitch `pitch` bytes for both).
-__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                         long long t, const long long (&rows)[kMaxK], int k, long long pitch,
-                                         int chunks, int lane) {
-  const uint4* s = reinterpret_cast<const uint4*>(src + t * pitch);
-  for (int c = lane; c < chunks; c += 64) {
-    const uint4 v = s[c];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) reinterpret_cast<uint4*>(dst + rows[j] * pitch)[c] = v;
-  }
-}
+// Chunks per lane per batch: every lane issues all loads of a batch before using any, so each
+// wave keeps several 1 KiB transactions per row in flight.  The two backward kernels gain from
+// it; permute and combine keep one chunk per batch, where the higher occupancy serves better.
+constexpr int kUFwd = 1;
+constexpr int kUBwd = 4;
 
 __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
                                                       const int32_t* __restrict__ dest, int T, int k,
@@ -47,12 +39,28 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict_
   if (t >= T) return;
   long long rows[kMaxK];
   load_dest(dest, t, k, lane, rows);
-  copy_row(x, xp, t, rows, k, pitch, static_cast<int>(pitch / 16), lane);
+  const int chunks = static_cast<int>(pitch / 16);
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * pitch);
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kUFwd) {
+    uint4 v[kUFwd];
+#pragma unroll
+    for (int u = 0; u < kUFwd; ++u)
+      if (c0 + 64 * u < chunks) v[u] = src[c0 + 64 * u];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        uint4* dst = reinterpret_cast<uint4*>(xp + rows[j] * pitch);
+#pragma unroll
+        for (int u = 0; u < kUFwd; ++u)
+          if (c0 + 64 * u < chunks) dst[c0 + 64 * u] = v[u];
+      }
+    }
+  }
   if (xs != nullptr) {
     // scale rows: d/32 bytes, an even count; copied in 2-byte units
-    const uint16_t* s = reinterpret_cast<const uint16_t*>(xs + t * spitch);
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(xs + t * spitch);
     for (int c = lane; c < spitch / 2; c += 64) {
-      const uint16_t v = s[c];
+      const uint16_t v = sc[c];
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j)
         if (j < k) reinterpret_cast<uint16_t*>(xps + rows[j] * spitch)[c] = v;
@@ -70,7 +78,7 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
                     pack_bf16x2(f[6], f[7]));
 }
 
-// y[t] = sum_j gate[t,j] * yexp[dest[t,j]]   (bf16 rows of d elements)
+// y[t] = sum_j gate[t,j] * yexp[dest[t,j]]   (bf16 rows of d elements), fp32 in slot order
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ yexp, const float* __restrict__ gate,
                                                       const int32_t* __restrict__ dest, int T, int d, int k,
                                                       uint16_t* __restrict__ y) {
@@ -84,19 +92,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) g[j] = __shfl(gmine, j, 64);
   const int chunks = d / 8;
-  for (int c = lane; c < chunks; c += 64) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kUFwd) {
+    float acc[kUFwd][8];
+#pragma unroll
+    for (int u = 0; u < kUFwd; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < k) {
-        const uint4 v = reinterpret_cast<const uint4*>(yexp + rows[j] * d)[c];
-        float f[8];
-        unpack8(v, f);
+        const uint4* row = reinterpret_cast<const uint4*>(yexp + rows[j] * d);
+        uint4 v[kUFwd];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
+        for (int u = 0; u < kUFwd; ++u)
+          if (c0 + 64 * u < chunks) v[u] = row[c0 + 64 * u];
+#pragma unroll
+        for (int u = 0; u < kUFwd; ++u) {
+          if (c0 + 64 * u < chunks) {
+            float f[8];
+            unpack8(v[u], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g[j], f[i], acc[u][i]);
+          }
+        }
       }
     }
-    reinterpret_cast<uint4*>(y + t * d)[c] = pack8(acc);
+    uint4* out = reinterpret_cast<uint4*>(y + t * d);
+#pragma unroll
+    for (int u = 0; u < kUFwd; ++u)
+      if (c0 + 64 * u < chunks) out[c0 + 64 * u] = pack8(acc[u]);
   }
 }
 
@@ -118,20 +142,35 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
     dot[j] = 0.f;
   }
   const int chunks = d / 8;
-  for (int c = lane; c < chunks; c += 64) {
-    float fdy[8];
-    unpack8(reinterpret_cast<const uint4*>(dy + t * d)[c], fdy);
+  const uint4* dyrow = reinterpret_cast<const uint4*>(dy + t * d);
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kUBwd) {
+    uint4 vdy[kUBwd];
+#pragma unroll
+    for (int u = 0; u < kUBwd; ++u)
+      if (c0 + 64 * u < chunks) vdy[u] = dyrow[c0 + 64 * u];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < k) {
-        float fy[8], o[8];
-        unpack8(reinterpret_cast<const uint4*>(yexp + rows[j] * d)[c], fy);
+        const uint4* yrow = reinterpret_cast<const uint4*>(yexp + rows[j] * d);
+        uint4* orow = reinterpret_cast<uint4*>(dyexp + rows[j] * d);
+        uint4 vy[kUBwd];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dot[j] = fmaf(fdy[i], fy[i], dot[j]);
-          o[i] = g[j] * fdy[i];
+        for (int u = 0; u < kUBwd; ++u)
+          if (c0 + 64 * u < chunks) vy[u] = yrow[c0 + 64 * u];
+#pragma unroll
+        for (int u = 0; u < kUBwd; ++u) {
+          if (c0 + 64 * u < chunks) {
+            float fdy[8], fy[8], o[8];
+            unpack8(vdy[u], fdy);
+            unpack8(vy[u], fy);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              dot[j] = fmaf(fdy[i], fy[i], dot[j]);
+              o[i] = g[j] * fdy[i];
+            }
+            orow[c0 + 64 * u] = pack8(o);
+          }
         }
-        reinterpret_cast<uint4*>(dyexp + rows[j] * d)[c] = pack8(o);
       }
     }
   }
@@ -154,24 +193,42 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const uint16_t* __rest
   long long rows[kMaxK];
   load_dest(dest, t, k, lane, rows);
   const int chunks = d / 8;
-  for (int c = lane; c < chunks; c += 64) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (addend != nullptr) {
-      const float4* a = reinterpret_cast<const float4*>(addend + t * d + 8 * c);
-      const float4 a0 = a[0], a1 = a[1];
-      acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
-      acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kUBwd) {
+    float acc[kUBwd][8];
+#pragma unroll
+    for (int u = 0; u < kUBwd; ++u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+      if (addend != nullptr && c0 + 64 * u < chunks) {
+        const float4* a = reinterpret_cast<const float4*>(addend + t * d + 8 * (c0 + 64 * u));
+        const float4 a0 = a[0], a1 = a[1];
+        acc[u][0] = a0.x; acc[u][1] = a0.y; acc[u][2] = a0.z; acc[u][3] = a0.w;
+        acc[u][4] = a1.x; acc[u][5] = a1.y; acc[u][6] = a1.z; acc[u][7] = a1.w;
+      }
     }
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < k) {
-        float f[8];
-        unpack8(reinterpret_cast<const uint4*>(dxp + rows[j] * d)[c], f);
+        const uint4* row = reinterpret_cast<const uint4*>(dxp + rows[j] * d);
+        uint4 v[kUBwd];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += f[i];
+        for (int u = 0; u < kUBwd; ++u)
+          if (c0 + 64 * u < chunks) v[u] = row[c0 + 64 * u];
+#pragma unroll
+        for (int u = 0; u < kUBwd; ++u) {
+          if (c0 + 64 * u < chunks) {
+            float f[8];
+            unpack8(v[u], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] += f[i];
+          }
+        }
       }
     }
-    reinterpret_cast<uint4*>(dx + t * d)[c] = pack8(acc);
+    uint4* out = reinterpret_cast<uint4*>(dx + t * d);
+#pragma unroll
+    for (int u = 0; u < kUBwd; ++u)
+      if (c0 + 64 * u < chunks) out[c0 + 64 * u] = pack8(acc[u]);
   }
 }
 
