@@ -17,8 +17,8 @@
 //   WGRAD_GU    dW_gate[e] = dG_e^T Xp_e,  dW_up[e] = dU_e^T Xp_e                   (K = rows of e)
 //
 // Tiling: 256 x 256 outputs per 256-thread workgroup, four waves in a 2 x 2 grid, each wave
-// owning 128 x 128 outputs as 8 x 8 MFMA 16x16 tiles (256 fp32 accumulators per lane).  K steps
-// of 32 run through a four-deep ring of LDS stages (4 x 32 KiB).
+// owning 128 x 128 outputs as 8 x 8 MFMA 16x16 tiles (256 fp32 accumulators per lane, AGPRs).  K
+// steps of 32 run through a five-deep ring of LDS stages (5 x 32 KiB = the whole 160 KiB LDS).
 //
 // Operand staging.  Every operand tile goes from HBM/L2 to LDS by the LDS-DMA form of the
 // buffer load (16 bytes per lane, written to a wave-contiguous 1 KiB LDS span), so no operand
@@ -32,14 +32,17 @@
 // Both layouts XOR-swizzle 16-byte chunks within a row (the DMA source address of each lane is
 // permuted to match), so fragment reads spread over all LDS banks.  Buffer descriptors bound
 // every operand to its valid extent: rows past an expert's last row (wgrad K tails) and past
-// the tensor end read as zeros.
+// the tensor end read as zeros, and so do K steps past the last one.
 //
-// Pipeline.  Three K steps are in flight in a four-stage ring.  In the middle of step kt (after
-// its fourth MFMA row) every wave waits for its own DMA of tile kt+1 and joins a barrier; past it,
-// all of tile kt+1 is in LDS and every wave has finished reading tile kt-1, so the DMA of tile
-// kt+3 goes into that stage.  Fragment reads run one MFMA row ahead of their use.  The MFMA
-// computes the transposed tile (weights / N side as the first operand), so each lane ends with 4
-// consecutive output columns of one row.
+// Pipeline.  Three K steps are in flight.  In the middle of step kt (after its fourth MFMA row)
+// every wave waits for its own DMA of tile kt+1 and joins a barrier; past it, all of tile kt+1
+// is in LDS and every wave has finished reading tile kt-1, so the DMA of tile kt+4 goes into
+// that stage.  Fragment reads run one MFMA row ahead of their use.  They are inline asm with
+// explicit lgkmcnt waits: the stage is a runtime index (the loop is unrolled by two, not by the
+// ring length), and the compiler, which cannot tell which stage a read touches, would otherwise
+// wait for every outstanding DMA before each read.  The MFMA computes the transposed tile
+// (weights / N side as the first operand), so each lane ends with 4 consecutive output columns
+// of one row.
 #include <type_traits>
 
 #include "common.h"
@@ -58,35 +61,21 @@ constexpr int BN = 256;
 constexpr int BK = 32;
 constexpr int NTH = 256;
 constexpr int OP_BYTES = BM * BK * 2;             // 16 KiB per operand per stage
+// Stage counts of the two operand rings (A = M side, B = N side), 160 KiB in all.  The N side
+// (the weights in the forward and dgrad products) mostly misses L2, so its ring is deeper.
+constexpr int NA = 4;
+constexpr int NB = 6;
+constexpr int A_RING = 0;
+constexpr int B_RING = NA * OP_BYTES;
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;      // raw buffer, 32-bit data format (gfx9 family)
 
-// Four stages of each operand as eight distinct LDS objects: the compiler tracks outstanding
-// LDS-DMA per object, so a fragment read of one stage never waits for the DMA into another.  The
-// A stages fill the first 64 KiB and the B stages the next, so every fragment address is one
-// per-lane base plus a 16-bit immediate.
-__shared__ __attribute__((aligned(1024))) uint8_t lds_a0[OP_BYTES];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_a1[OP_BYTES];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_a2[OP_BYTES];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_a3[OP_BYTES];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_b0[OP_BYTES];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_b1[OP_BYTES];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_b2[OP_BYTES];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_b3[OP_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_ring[(NA + NB) * OP_BYTES];
 
-template <int S>
-__device__ __forceinline__ uint8_t* stage_a() {
-  if constexpr (S == 0) return lds_a0;
-  else if constexpr (S == 1) return lds_a1;
-  else if constexpr (S == 2) return lds_a2;
-  else return lds_a3;
-}
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-template <int S>
-__device__ __forceinline__ uint8_t* stage_b() {
-  if constexpr (S == 0) return lds_b0;
-  else if constexpr (S == 1) return lds_b1;
-  else if constexpr (S == 2) return lds_b2;
-  else return lds_b3;
+// LDS byte address of a generic pointer into lds_ring.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(p)));
 }
 
 enum Mode { FWD1 = 0, FWD2 = 1, DGRAD1 = 2, DGRAD2 = 3, WGRAD_DOWN = 4, WGRAD_GU = 5 };
@@ -183,71 +172,59 @@ __device__ __forceinline__ int k_total(const Params& p) {
   return 0;
 }
 
-// Per-lane DMA offsets of one operand (4 instructions per lane per stage) and the descriptors.
+// DMA roles: waves 0 and 1 stream the N-side operand (B), waves 2 and 3 the M-side operand (A);
+// each wave fills one half of its operand's stage (8 instructions of 1 KiB).  Splitting by
+// operand gives each ring its own depth: a wave's vmcnt counts only its own loads, and vector
+// loads complete in order, so one deep ring shared with a shallow one would wait at the
+// shallow one's pace.
 struct OpLoad {
-  __amdgpu_buffer_rsrc_t r0, r1;   // r1: second tensor (FWD1 B: W_up; DGRAD2: dU / W_up)
-  int vo[4];
+  __amdgpu_buffer_rsrc_t r0, r1;   // r1: second tensor (FWD1 B half 1: W_up; DGRAD2 K >= f)
+  int vo[8];
   int step;                        // bytes to advance per K step (KC: 64; KS: 32 rows)
 };
 
-// KC operand, rows [row0, row0 + 256) of a row-major tensor with `ldb` bytes per row.
-// Wave w fills LDS rows 64w .. 64w + 63 with 4 instructions of 16 rows each.
-__device__ __forceinline__ void kc_offsets(int ldb, int (&vo)[4]) {
-  const int L = threadIdx.x & 63, w = threadIdx.x >> 6;
+// KC operand: LDS rows 128h .. 128h + 127 of a [256 rows][32 k] stage; `row0` is the first tensor
+// row of this half (relative to the descriptor base), `ldb` the tensor's bytes per row.
+__device__ __forceinline__ void kc_offsets(int row0, int ldb, int (&vo)[8]) {
+  const int L = threadIdx.x & 63;
   const int c = (L & 3) ^ ((L >> 4) & 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vo[i] = (64 * w + 16 * i + (L >> 2)) * ldb + 16 * c;
+  for (int i = 0; i < 8; ++i) vo[i] = (row0 + 16 * i + (L >> 2)) * ldb + 16 * c;
 }
 
-// KS operand, 32 K-rows x 256 columns; wave w fills LDS rows 8w .. 8w + 7, 2 rows per instruction.
-__device__ __forceinline__ void ks_offsets(int ldb, int (&vo)[4]) {
-  const int L = threadIdx.x & 63, w = threadIdx.x >> 6;
+// KS operand: K-rows 16h .. 16h + 15 of a [32 k][256 columns] stage, 2 rows per instruction.
+__device__ __forceinline__ void ks_offsets(int h, int ldb, int (&vo)[8]) {
+  const int L = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kr = 8 * w + 2 * i + (L >> 5);
+  for (int i = 0; i < 8; ++i) {
+    const int kr = 16 * h + 2 * i + (L >> 5);
     vo[i] = kr * ldb + 16 * ((L & 31) ^ ks_swz(kr));
   }
 }
 
-// Issues the DMA of K step kt into stage S.  Steps past the last one (kt >= nk) read through an
-// empty descriptor, so the stage fills with zeros and its MFMAs add nothing.
-template <int MODE, int S>
-__device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& la, const OpLoad& lb, int kt, int nk) {
-  const int w = threadIdx.x >> 6;
-  const bool valid = kt < nk;
-  uint8_t* da = stage_a<S>() + w * 4096;
-  uint8_t* db = stage_b<S>() + w * 4096;
-  // ---- A (M side)
-  {
-    __amdgpu_buffer_rsrc_t r = la.r0;
-    int soff = kt * la.step;
-    if constexpr (MODE == DGRAD2) {
-      const int kf = p.f / BK;   // K steps per half
-      if (kt >= kf) { r = la.r1; soff = (kt - kf) * la.step; }
-    }
-    if (!valid) { r = make_rsrc(p.a0, 0); soff = 0; }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(r, da + i * 1024, la.vo[i], soff);
+// Issues this wave's DMA of K step kt into stage `st` of its operand's ring.  Steps past the
+// last one (kt >= nk) read through an empty descriptor, so the stage fills with zeros and its
+// MFMAs add nothing.
+template <int MODE>
+__device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& ld, bool role_b, int h, int kt, int nk,
+                                            int st) {
+  __amdgpu_buffer_rsrc_t r = ld.r0;
+  int soff = kt * ld.step;
+  if constexpr (MODE == FWD1) {
+    if (role_b && h) r = ld.r1;
+  } else if constexpr (MODE == DGRAD2) {
+    const int kf = p.f / BK;   // K steps per half
+    if (kt >= kf) { r = ld.r1; soff = (kt - kf) * ld.step; }
   }
-  // ---- B (N side)
-  {
-    __amdgpu_buffer_rsrc_t r = lb.r0;
-    int soff = kt * lb.step;
-    if constexpr (MODE == FWD1) {
-      if (w >= 2) r = lb.r1;
-    } else if constexpr (MODE == DGRAD2) {
-      const int kf = p.f / BK;
-      if (kt >= kf) { r = lb.r1; soff = (kt - kf) * lb.step; }
-    }
-    if (!valid) { r = make_rsrc(p.b0, 0); soff = 0; }
+  if (kt >= nk) { r = make_rsrc(p.a0, 0); soff = 0; }
+  uint8_t* dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * 8192;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(r, db + i * 1024, lb.vo[i], soff);
-  }
+  for (int i = 0; i < 8; ++i) dma16(r, dst + i * 1024, ld.vo[i], soff);
 }
 
 // ---------------------------------------------------------------- fragments
 
-// Per-lane fragment addresses, computed once.
+// Per-lane fragment addresses within a stage, computed once.
 //   KC: fragment q (rows 16q .. 16q + 15 of the stage) of lane l sits at kc + 1024 q: the chunk
 //       swizzle (r >> 2) & 3 of row r = 16q + l % 16 does not depend on q.
 //   KS: fragment q (columns 16q .. 16q + 15) of lane l, half h (K = 8 (l / 16) + 4h .. + 3), is
@@ -255,58 +232,60 @@ __device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& la, c
 //       16q + 4 (l % 4) .. + 3; the row's swizzle only flips bits 5..7 of the byte address, the
 //       same bits q selects.
 struct FragAddr {
-  int a_kc, b_kc;
-  int a_ks[2], b_ks[2];
+  uint32_t kc;
+  uint32_t ks[2];
 };
 
-__device__ __forceinline__ int kc_lane() {
-  const int l = threadIdx.x & 63;
-  return kc_off(l & 15, l >> 4);
-}
-
-__device__ __forceinline__ int ks_lane(int h) {
-  const int l = threadIdx.x & 63;
-  const int g = l >> 4, i = l & 15;
-  const int k = 8 * g + 4 * h + (i >> 2);
-  const int col = 4 * (i & 3);                   // fragment 0
-  return ks_off(k, col >> 3) + ((col & 7) << 1);
-}
-
-template <int MODE>
 __device__ __forceinline__ FragAddr frag_addr() {
+  const int l = threadIdx.x & 63;
   FragAddr fa;
-  fa.a_kc = fa.b_kc = kc_lane();
-  fa.a_ks[0] = fa.b_ks[0] = ks_lane(0);
-  fa.a_ks[1] = fa.b_ks[1] = ks_lane(1);
+  fa.kc = kc_off(l & 15, l >> 4);
+  const int g = l >> 4, i = l & 15;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = 8 * g + 4 * h + (i >> 2);
+    const int col = 4 * (i & 3);                 // fragment 0
+    fa.ks[h] = ks_off(k, col >> 3) + ((col & 7) << 1);
+  }
   return fa;
 }
 
-__device__ __forceinline__ bf16x8 read_kc(const uint8_t* stage, int lane_off, int q) {
-  return *reinterpret_cast<const bf16x8*>(stage + lane_off + 1024 * q);
+// LDS reads as asm: the compiler neither reorders them across the barrier asm nor inserts DMA
+// waits before them; callers wait with lgkm_wait before using the results.
+template <int OFF>
+__device__ __forceinline__ void ds_b128(bf16x8& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
 
-__device__ __forceinline__ bf16x8 read_ks(const uint8_t* stage, const int (&ks)[2], int q) {
-  bf16x4 h[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const uint8_t* pa = stage + (ks[hh] ^ (q << 5));
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pa));
-    h[hh] = __builtin_bit_cast(bf16x4, v);
+__device__ __forceinline__ void ds_tr(s16x4& v, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+}
+
+// Fragment q of the operand whose stage starts at LDS address `base` (KC or KS layout).
+template <bool KC, int Q>
+__device__ __forceinline__ void read_frag(bf16x8& v, uint32_t base, const FragAddr& fa, int qoff) {
+  if constexpr (KC) {
+    ds_b128<1024 * Q>(v, base + fa.kc + 1024 * qoff);
+  } else {
+    s16x4 h0, h1;
+    const uint32_t q = static_cast<uint32_t>(Q + qoff) << 5;
+    ds_tr(h0, base + (fa.ks[0] ^ q));
+    ds_tr(h1, base + (fa.ks[1] ^ q));
+    v = __builtin_shufflevector(__builtin_bit_cast(bf16x4, h0), __builtin_bit_cast(bf16x4, h1), 0, 1, 2, 3, 4, 5,
+                                6, 7);
   }
-  return bf16x8{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
 }
 
-// Fragment q of the LDS B tile for MFMA tile i (FWD1 pairs gate rows with up rows), in units of
-// 16 rows (KC) or 16 columns (KS).
-template <int MODE>
-__device__ __forceinline__ int bfrag(int wn, int i) {
-  if constexpr (MODE == FWD1) return (i < 4) ? (4 * wn + i) : (8 + 4 * wn + (i - 4));
-  return 8 * wn + i;
+// Waits until at most N LDS reads are outstanding; ties the fragments the next MFMAs use, so
+// those MFMAs cannot be scheduled above the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(bf16x8& b, bf16x8 (&a)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%9)"
+               : "+v"(b), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                 "+v"(a[7])
+               : "n"(N));
 }
 
-// The transposing read takes no immediate offset, so every (stage, fragment, half) address is a
-// VGPR.  The KS bases are laundered once per K step so the compiler forms those addresses next to
-// their reads instead of keeping all of them live across the loop.
 // acc += x * y on the matrix core, accumulating in place in AGPRs.  Written as inline asm so the
 // accumulator is tied to one register quad for the whole loop: the builtin's untied form made the
 // register allocator rotate all 256 accumulators through copies every K step.  Callers cover the
@@ -322,56 +301,57 @@ __device__ __forceinline__ void pin_acc_row(f32x4 (&r)[8]) {
                "+a"(r[7]));
 }
 
-template <int MODE, int S>
-__device__ __forceinline__ bf16x8 read_a(const FragAddr& fa, int q) {
-  if constexpr (Traits<MODE>::A_KC) return read_kc(stage_a<S>(), fa.a_kc, q);
-  else return read_ks(stage_a<S>(), fa.a_ks, q);
+// Fragment index (units of 16 rows/columns) of B fragment i for wave column wn (FWD1 pairs gate
+// rows with up rows).
+template <int MODE, int I>
+__device__ __forceinline__ constexpr int bfrag_c() {
+  if constexpr (MODE == FWD1) return (I < 4) ? I : 8 + (I - 4);
+  return I;
 }
 
-template <int MODE, int S>
-__device__ __forceinline__ bf16x8 read_b(const FragAddr& fa, int q) {
-  if constexpr (Traits<MODE>::B_KC) return read_kc(stage_b<S>(), fa.b_kc, q);
-  else return read_ks(stage_b<S>(), fa.b_ks, q);
+template <int MODE>
+__device__ __forceinline__ int bfrag_base(int wn) {
+  return MODE == FWD1 ? 4 * wn : 8 * wn;
 }
 
-// One K step of tile kt (stage S), as 8 rows of 8 MFMAs; row i multiplies B fragment i by the
-// 8 A fragments.  Fragment reads run one row ahead of their use, from two small register sets:
+// One K step of tile kt (in stage st), as 8 rows of 8 MFMAs; row i multiplies B fragment i by
+// the 8 A fragments.  Fragment reads run one row ahead of their use, from small register sets:
 //   a[8]      A fragments of tile kt (read during the previous step), an[8] those of tile kt+1;
 //   b[2]      ping-pong: B fragment i+1 is read while row i runs.
-// The barrier before row 4 opens tile kt+1: each wave first waits for its own DMA of that tile
-// (one newer tile, 8 DMA instructions, stays in flight), and past the barrier every wave has
-// also finished reading tile kt-1, whose stage then receives the DMA of tile kt+3.  Rows 4..7
-// read the A fragments of tile kt+1 (two per row) and row 7 its first B fragment.
-template <int MODE, int S>
-__device__ __forceinline__ void k_step(const Params& p, const OpLoad& la, const OpLoad& lb, const FragAddr& fa_in,
-                                       int kt, int nk, bf16x8 (&a)[8], bf16x8 (&an)[8], bf16x8 (&b)[2],
-                                       f32x4 (&acc)[8][8]) {
-  constexpr int SN = (S + 1) & 3;
+// The barrier before row 4 opens tile kt+1: each wave first waits for its own DMA of that tile,
+// and past the barrier every wave has also finished reading tile kt-1, whose stages then
+// receive the DMA of tiles kt+NA-1 (A waves) and kt+NB-1 (B waves).  Rows 4..7 read the A
+// fragments of tile kt+1 (two per row) and row 7 its first B fragment.
+template <int MODE>
+__device__ __forceinline__ void k_step(const Params& p, const OpLoad& ld, bool role_b, int h, const FragAddr& fa,
+                                       int kt, int nk, int sa, int sb, bf16x8 (&a)[8], bf16x8 (&an)[8],
+                                       bf16x8 (&b)[2], f32x4 (&acc)[8][8]) {
+  constexpr bool AKC = Traits<MODE>::A_KC, BKC = Traits<MODE>::B_KC;
+  constexpr int RA = AKC ? 1 : 2;   // LDS reads per A fragment
+  constexpr int RB = BKC ? 1 : 2;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qa = 8 * (wave >> 1), wn = wave & 1;
-  FragAddr fa = fa_in;
-  if constexpr (!Traits<MODE>::A_KC) asm volatile("" : "+v"(fa.a_ks[0]), "+v"(fa.a_ks[1]));
-  if constexpr (!Traits<MODE>::B_KC) asm volatile("" : "+v"(fa.b_ks[0]), "+v"(fa.b_ks[1]));
-  constexpr int RB = Traits<MODE>::B_KC ? 1 : 2;   // LDS reads per B fragment
-  constexpr int RA = Traits<MODE>::A_KC ? 1 : 2;
+  const int qa = 8 * (wave >> 1);
+  const int qb = bfrag_base<MODE>(wave & 1);
+  const int san = sa + 1 == NA ? 0 : sa + 1, sap = sa == 0 ? NA - 1 : sa - 1;
+  const int sbn = sb + 1 == NB ? 0 : sb + 1, sbp = sb == 0 ? NB - 1 : sb - 1;
+  const uint32_t ring = lds_addr(lds_ring);
+  const uint32_t b_cur = ring + B_RING + sb * OP_BYTES, b_nxt = ring + B_RING + sbn * OP_BYTES;
+  const uint32_t a_nxt = ring + A_RING + san * OP_BYTES;
   static_for<0, 8>([&](auto i) {
     if constexpr (i == 4) {
-      wait_barrier<8>();
-      issue_stage<MODE, (S + 3) & 3>(p, la, lb, kt + 3, nk);
+      // own DMA of tile kt+1 done (B waves keep NB-3 newer tiles in flight, A waves NA-3)
+      if (role_b) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NB - 3)) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NA - 3)) : "memory");
+      issue_stage<MODE>(p, ld, role_b, h, kt + (role_b ? NB : NA) - 1, nk, role_b ? sbp : sap);
     }
-    if constexpr (i < 7) b[(i + 1) & 1] = read_b<MODE, S>(fa, bfrag<MODE>(wn, i + 1));
-    else b[0] = read_b<MODE, SN>(fa, bfrag<MODE>(wn, 0));
+    if constexpr (i < 7) read_frag<BKC, bfrag_c<MODE, i + 1>()>(b[(i + 1) & 1], b_cur, fa, qb);
+    else read_frag<BKC, bfrag_c<MODE, 0>()>(b[0], b_nxt, fa, qb);
     if constexpr (i >= 4) {
-      an[2 * (i - 4)] = read_a<MODE, SN>(fa, qa + 2 * (i - 4));
-      an[2 * (i - 4) + 1] = read_a<MODE, SN>(fa, qa + 2 * (i - 4) + 1);
+      read_frag<AKC, 2 * (i - 4)>(an[2 * (i - 4)], a_nxt, fa, qa);
+      read_frag<AKC, 2 * (i - 4) + 1>(an[2 * (i - 4) + 1], a_nxt, fa, qa);
     }
-    static_for<0, 8>([&](auto j) {
-      mfma_acc(acc[i][j], b[i & 1], a[j]);
-    });
-    // keep this row's reads ahead of its MFMAs (the DMA of row 4 goes first)
-    if constexpr (i == 4) __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, RB + (i >= 4 ? 2 * RA : 0), 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    lgkm_wait<RB + (i >= 4 ? 2 * RA : 0)>(b[i & 1], a);
+    static_for<0, 8>([&](auto j) { mfma_acc(acc[i][j], b[i & 1], a[j]); });
   });
 }
 
@@ -385,51 +365,83 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 
 // ---------------------------------------------------------------- the kernel
 
+// m-tile prefix over experts, computed by every wave from one round of loads (no LDS: the whole
+// LDS is the operand rings).  Lane l holds experts l, l + 64, l + 128, l + 192.
+struct MTiles {
+  int tiles[4], excl[4];
+  int total;
+};
+
+__device__ __forceinline__ MTiles mtile_scan(const int32_t* __restrict__ offsets, int E) {
+  const int lane = threadIdx.x & 63;
+  MTiles m;
+  int lo[4], hi[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ex = 64 * r + lane;
+    lo[r] = ex < E ? offsets[ex] : 0;
+    hi[r] = ex < E ? offsets[ex + 1] : 0;
+  }
+  int carry = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tiles = (hi[r] - lo[r] + BM - 1) / BM;
+    int incl = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    m.tiles[r] = tiles;
+    m.excl[r] = carry + incl - tiles;
+    carry += __shfl(incl, 63, 64);
+  }
+  m.total = __builtin_amdgcn_readfirstlane(carry);
+  return m;
+}
+
+// The expert owning global m-tile mt (< total) and that expert's first m-tile.
+__device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int& first) {
+  const int lane = threadIdx.x & 63;
+  e = 0;
+  first = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const unsigned long long hit = __ballot(m.tiles[r] > 0 && m.excl[r] <= mt && mt < m.excl[r] + m.tiles[r]);
+    if (hit) {
+      const int src = __ffsll(static_cast<long long>(hit)) - 1;
+      e = 64 * r + src;
+      first = __shfl(m.excl[r], src, 64);
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
-  __shared__ int s_pre[257];     // FWD/DGRAD: prefix of m-tiles per expert
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- device-side schedule: count tiles, remap the block id XCD-major, find the tile
   const int NTW = n_tile_width<MODE>();
   const int ntiles_n = (n_total<MODE>(p) + NTW - 1) / NTW;
-  int total_tiles;
-  if constexpr (!Traits<MODE>::WGRAD) {
-    if (tid == 0) s_pre[0] = 0;
-    for (int e = tid; e < p.E; e += NTH) {
-      const int cnt = p.offsets[e + 1] - p.offsets[e];
-      s_pre[e + 1] = (cnt + BM - 1) / BM;
-    }
-    __syncthreads();
-    if (tid == 0)
-      for (int e = 0; e < p.E; ++e) s_pre[e + 1] += s_pre[e];
-    __syncthreads();
-    total_tiles = s_pre[p.E] * ntiles_n;
-  } else {
-    const int mt = (m_total_wgrad<MODE>(p) + BM - 1) / BM;
-    total_tiles = p.E * mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
-  }
-  const int tot8 = (total_tiles + 7) & ~7;
   const int bid = blockIdx.x;
-  if (bid >= tot8) return;
-  const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
-  if (lid >= total_tiles) return;
-
   Tile t;
   if constexpr (!Traits<MODE>::WGRAD) {
+    const MTiles mts = mtile_scan(p.offsets, p.E);
+    const int total_tiles = mts.total * ntiles_n;
+    const int tot8 = (total_tiles + 7) & ~7;
+    if (bid >= tot8) return;
+    const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
+    if (lid >= total_tiles) return;
     const int mt_glob = lid / ntiles_n;
     const int nt = lid - mt_glob * ntiles_n;
-    int lo = 0, hi = p.E - 1;                     // last e with s_pre[e] <= mt_glob
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[mid] <= mt_glob) lo = mid; else hi = mid - 1;
-    }
-    t.e = lo;
-    t.m0 = p.offsets[lo] + (mt_glob - s_pre[lo]) * BM;
-    t.m_end = p.offsets[lo + 1];
+    int e, first;
+    mtile_find(mts, mt_glob, e, first);
+    t.e = e;
+    t.m0 = p.offsets[e] + (mt_glob - first) * BM;
+    t.m_end = p.offsets[e + 1];
     t.n0 = nt * NTW;
     t.half = 0;
     t.k_begin = 0;
@@ -438,6 +450,11 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     const int Mtot = m_total_wgrad<MODE>(p);
     const int mt = (Mtot + BM - 1) / BM;
     const int mtt = mt * (MODE == WGRAD_GU ? 2 : 1);
+    const int total_tiles = p.E * mtt * ntiles_n;
+    const int tot8 = (total_tiles + 7) & ~7;
+    if (bid >= tot8) return;
+    const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
+    if (lid >= total_tiles) return;
     const int per_e = mtt * ntiles_n;
     t.e = lid / per_e;
     const int rem = lid - t.e * per_e;
@@ -450,75 +467,87 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     t.k_begin = p.offsets[t.e];
     t.k_len = p.offsets[t.e + 1] - t.k_begin;
   }
+  // The tile is uniform across the workgroup, but it was derived through shuffles and loads the
+  // compiler treats as per-lane; without this, every buffer descriptor built from it would be
+  // "divergent" and each DMA instruction wrapped in a readfirstlane waterfall loop.
+  t.e = __builtin_amdgcn_readfirstlane(t.e);
+  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+  t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);
+  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  t.half = __builtin_amdgcn_readfirstlane(t.half);
+  t.k_begin = __builtin_amdgcn_readfirstlane(t.k_begin);
+  t.k_len = __builtin_amdgcn_readfirstlane(t.k_len);
   const int nk = (t.k_len + BK - 1) / BK;
 
-  // ---- operand descriptors, bounded to each operand's valid extent
-  OpLoad la, lb;
-  if constexpr (MODE == FWD1 || MODE == FWD2 || MODE == DGRAD1) {
-    const int K = k_total<MODE>(p);
-    const long long rem_rows = static_cast<long long>(p.n) - t.m0;
-    la.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K * 2);
-    la.r1 = la.r0;
-    la.step = BK * 2;
-    kc_offsets(K * 2, la.vo);
-  } else if constexpr (MODE == DGRAD2) {
-    const long long rem_rows = static_cast<long long>(p.n) - t.m0;
-    la.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
-    la.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
-    la.step = BK * 2;
-    kc_offsets(p.f * 2, la.vo);
+  // ---- this wave's DMA operand, bounded to its valid extent (role: waves 0, 1 -> B; 2, 3 -> A)
+  const bool role_b = wave < 2;
+  const int h = wave & 1;
+  OpLoad ld;
+  if (!role_b) {
+    if constexpr (MODE == FWD1 || MODE == FWD2 || MODE == DGRAD1) {
+      const int K = k_total<MODE>(p);
+      const long long rem_rows = static_cast<long long>(p.n) - t.m0;
+      ld.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K * 2);
+      ld.r1 = ld.r0;
+      ld.step = BK * 2;
+      kc_offsets(128 * h, K * 2, ld.vo);
+    } else if constexpr (MODE == DGRAD2) {
+      const long long rem_rows = static_cast<long long>(p.n) - t.m0;
+      ld.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
+      ld.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
+      ld.step = BK * 2;
+      kc_offsets(128 * h, p.f * 2, ld.vo);
+    } else {
+      // WGRAD: M side is a token-major activation [n][Mtot], rows k_begin .. k_begin + k_len
+      const int Mtot = m_total_wgrad<MODE>(p);
+      const uint16_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
+      ld.r0 = make_rsrc(base + static_cast<long long>(t.k_begin) * Mtot + t.m0,
+                        static_cast<long long>(t.k_len) * Mtot * 2 - t.m0 * 2);
+      ld.r1 = ld.r0;
+      ld.step = BK * Mtot * 2;
+      ks_offsets(h, Mtot * 2, ld.vo);
+    }
   } else {
-    // WGRAD: M side is a token-major activation [n][Mtot], rows k_begin .. k_begin + k_len
-    const int Mtot = m_total_wgrad<MODE>(p);
-    const uint16_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
-    la.r0 = make_rsrc(base + static_cast<long long>(t.k_begin) * Mtot + t.m0,
-                      static_cast<long long>(t.k_len) * Mtot * 2 - t.m0 * 2);
-    la.r1 = la.r0;
-    la.step = BK * Mtot * 2;
-    ks_offsets(Mtot * 2, la.vo);
-  }
-  if constexpr (MODE == FWD1) {
-    // rows 0..127 of the B tile: W_gate[e] rows n0 ..; rows 128..255: W_up[e] rows n0 ..
-    const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
-    const long long bytes = static_cast<long long>(p.f - t.n0) * p.d * 2;
-    lb.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
-    lb.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
-    lb.step = BK * 2;
-    // wave w fills rows 64w..: waves 2, 3 start again at row 0 of W_up
-    const int L = tid & 63;
-    const int c = (L & 3) ^ ((L >> 4) & 3);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lb.vo[i] = (64 * (wave & 1) + 16 * i + (L >> 2)) * p.d * 2 + 16 * c;
-  } else if constexpr (MODE == FWD2) {
-    // W_down[e] [d][f], rows n0 .. (K = f contiguous)
-    const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
-    lb.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.f, static_cast<long long>(p.d - t.n0) * p.f * 2);
-    lb.r1 = lb.r0;
-    lb.step = BK * 2;
-    kc_offsets(p.f * 2, lb.vo);
-  } else if constexpr (MODE == DGRAD1) {
-    // W_down[e] [d][f]: element (k = d index, n = f index), rows k, columns n0 ..
-    const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
-    lb.r0 = make_rsrc(p.b0 + eoff + t.n0, static_cast<long long>(p.d) * p.f * 2 - t.n0 * 2);
-    lb.r1 = lb.r0;
-    lb.step = BK * p.f * 2;
-    ks_offsets(p.f * 2, lb.vo);
-  } else if constexpr (MODE == DGRAD2) {
-    // W_gate[e] / W_up[e] [f][d]: element (k = f index, n = d index)
-    const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
-    const long long bytes = static_cast<long long>(p.f) * p.d * 2 - t.n0 * 2;
-    lb.r0 = make_rsrc(p.b0 + eoff + t.n0, bytes);
-    lb.r1 = make_rsrc(p.b1 + eoff + t.n0, bytes);
-    lb.step = BK * p.d * 2;
-    ks_offsets(p.d * 2, lb.vo);
-  } else {
-    // WGRAD: N side is a token-major activation [n][Ntot]
-    const int Ntot = n_total<MODE>(p);
-    lb.r0 = make_rsrc(p.b0 + static_cast<long long>(t.k_begin) * Ntot + t.n0,
-                      static_cast<long long>(t.k_len) * Ntot * 2 - t.n0 * 2);
-    lb.r1 = lb.r0;
-    lb.step = BK * Ntot * 2;
-    ks_offsets(Ntot * 2, lb.vo);
+    if constexpr (MODE == FWD1) {
+      // B half 0: W_gate[e] rows n0 .. n0 + 127; half 1: W_up[e] rows n0 .. n0 + 127
+      const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
+      const long long bytes = static_cast<long long>(p.f - t.n0) * p.d * 2;
+      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
+      ld.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
+      ld.step = BK * 2;
+      kc_offsets(0, p.d * 2, ld.vo);
+    } else if constexpr (MODE == FWD2) {
+      // W_down[e] [d][f], rows n0 .. (K = f contiguous)
+      const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
+      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.f,
+                        static_cast<long long>(p.d - t.n0) * p.f * 2);
+      ld.r1 = ld.r0;
+      ld.step = BK * 2;
+      kc_offsets(128 * h, p.f * 2, ld.vo);
+    } else if constexpr (MODE == DGRAD1) {
+      // W_down[e] [d][f]: element (k = d index, n = f index), rows k, columns n0 ..
+      const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
+      ld.r0 = make_rsrc(p.b0 + eoff + t.n0, static_cast<long long>(p.d) * p.f * 2 - t.n0 * 2);
+      ld.r1 = ld.r0;
+      ld.step = BK * p.f * 2;
+      ks_offsets(h, p.f * 2, ld.vo);
+    } else if constexpr (MODE == DGRAD2) {
+      // W_gate[e] / W_up[e] [f][d]: element (k = f index, n = d index)
+      const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
+      const long long bytes = static_cast<long long>(p.f) * p.d * 2 - t.n0 * 2;
+      ld.r0 = make_rsrc(p.b0 + eoff + t.n0, bytes);
+      ld.r1 = make_rsrc(p.b1 + eoff + t.n0, bytes);
+      ld.step = BK * p.d * 2;
+      ks_offsets(h, p.d * 2, ld.vo);
+    } else {
+      // WGRAD: N side is a token-major activation [n][Ntot]
+      const int Ntot = n_total<MODE>(p);
+      ld.r0 = make_rsrc(p.b0 + static_cast<long long>(t.k_begin) * Ntot + t.n0,
+                        static_cast<long long>(t.k_len) * Ntot * 2 - t.n0 * 2);
+      ld.r1 = ld.r0;
+      ld.step = BK * Ntot * 2;
+      ks_offsets(h, Ntot * 2, ld.vo);
+    }
   }
 
   f32x4 acc[8][8];
@@ -528,30 +557,39 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nk > 0) {
-    // ---- prologue: tiles 0..2 in flight, fragments of tile 0 read
     // accumulator initialisation -> first MFMA: pin the zeroed registers ahead of the wait states
 #pragma unroll
     for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
     asm volatile("s_nop 7" ::: "memory");
-    issue_stage<MODE, 0>(p, la, lb, 0, nk);
-    issue_stage<MODE, 1>(p, la, lb, 1, nk);
-    issue_stage<MODE, 2>(p, la, lb, 2, nk);
-    const FragAddr fa = frag_addr<MODE>();
-    wait_barrier<16>();
-    const int qa = 8 * (wave >> 1);
-    bf16x8 fa0[8], fa1[8], fb[2];
+    // ---- prologue: tiles 0 .. N-2 of this wave's ring in flight, then tile 0 everywhere
+    if (role_b) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fa0[j] = read_a<MODE, 0>(fa, qa + j);
-    fb[0] = read_b<MODE, 0>(fa, bfrag<MODE>(wn, 0));
-    for (int kt = 0; kt < nk; kt += 4) {
-      k_step<MODE, 0>(p, la, lb, fa, kt, nk, fa0, fa1, fb, acc);
-      k_step<MODE, 1>(p, la, lb, fa, kt + 1, nk, fa1, fa0, fb, acc);
-      k_step<MODE, 2>(p, la, lb, fa, kt + 2, nk, fa0, fa1, fb, acc);
-      k_step<MODE, 3>(p, la, lb, fa, kt + 3, nk, fa1, fa0, fb, acc);
+      for (int st = 0; st < NB - 1; ++st) issue_stage<MODE>(p, ld, true, h, st, nk, st);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NB - 2)) : "memory");
+    } else {
+#pragma unroll
+      for (int st = 0; st < NA - 1; ++st) issue_stage<MODE>(p, ld, false, h, st, nk, st);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NA - 2)) : "memory");
+    }
+    const FragAddr fa = frag_addr();
+    const uint32_t a0 = lds_addr(lds_ring) + A_RING, b0 = lds_addr(lds_ring) + B_RING;
+    const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
+    bf16x8 fa0[8], fa1[8], fb[2];
+    static_for<0, 8>([&](auto j) { read_frag<Traits<MODE>::A_KC, j>(fa0[j], a0, fa, qa); });
+    read_frag<Traits<MODE>::B_KC, bfrag_c<MODE, 0>()>(fb[0], b0, fa, qb);
+    // the K loop runs an even number of steps; steps past nk multiply zeros
+    int sa = 0, sb = 0;
+    for (int kt = 0; kt < nk; kt += 2) {
+      k_step<MODE>(p, ld, role_b, h, fa, kt, nk, sa, sb, fa0, fa1, fb, acc);
+      sa = sa + 1 == NA ? 0 : sa + 1;
+      sb = sb + 1 == NB ? 0 : sb + 1;
+      k_step<MODE>(p, ld, role_b, h, fa, kt + 1, nk, sa, sb, fa1, fa0, fb, acc);
+      sa = sa + 1 == NA ? 0 : sa + 1;
+      sb = sb + 1 == NB ? 0 : sb + 1;
     }
     // no LDS-DMA may still be writing when the workgroup ends; the last MFMA results settle
     // before the epilogue's VALU reads them
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
   }
 
   // ---- epilogue: lane holds, for MFMA tile (i, j), output row 16j + lane%16 of the wave's
