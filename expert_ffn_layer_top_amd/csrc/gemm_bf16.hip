@@ -58,13 +58,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 32;
+constexpr int BK = 64;                            // K per stage (two 32-deep MFMA sub-steps)
 constexpr int NTH = 256;
-constexpr int OP_BYTES = BM * BK * 2;             // 16 KiB per operand per stage
+constexpr int OP_BYTES = BM * BK * 2;             // 32 KiB per operand per stage
 // Stage counts of the two operand rings (A = M side, B = N side), 160 KiB in all.  The N side
 // (the weights in the forward and dgrad products) mostly misses L2, so its ring is deeper.
-constexpr int NA = 4;
-constexpr int NB = 6;
+constexpr int NA = 2;
+constexpr int NB = 3;
 constexpr int A_RING = 0;
 constexpr int B_RING = NA * OP_BYTES;
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;      // raw buffer, 32-bit data format (gfx9 family)
@@ -113,8 +113,9 @@ struct Traits {
 
 // ---------------------------------------------------------------- LDS layouts
 
-// KC: row r (64 bytes = 4 chunks), chunk c stored at chunk position c ^ ((r >> 2) & 3).
-__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// KC: row r (128 bytes = 8 chunks), chunk c stored at chunk position c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 128 + ((c ^ kc_swz(r)) << 4); }
 // KS: row k (512 bytes = 32 chunks), chunk c stored at chunk position c ^ ks_swz(k); the XOR
 // value is even, so the two chunks of an aligned 32-byte pair stay adjacent.
 __device__ __forceinline__ int ks_swz(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
@@ -179,25 +180,28 @@ __device__ __forceinline__ int k_total(const Params& p) {
 // shallow one's pace.
 struct OpLoad {
   __amdgpu_buffer_rsrc_t r0, r1;   // r1: second tensor (FWD1 B half 1: W_up; DGRAD2 K >= f)
-  int vo[8];
-  int step;                        // bytes to advance per K step (KC: 64; KS: 32 rows)
+  int vo[16];
+  int step;                        // bytes to advance per K step (KC: 128; KS: 64 rows)
 };
 
-// KC operand: LDS rows 128h .. 128h + 127 of a [256 rows][32 k] stage; `row0` is the first tensor
-// row of this half (relative to the descriptor base), `ldb` the tensor's bytes per row.
-__device__ __forceinline__ void kc_offsets(int row0, int ldb, int (&vo)[8]) {
+// KC operand: LDS rows 128h .. 128h + 127 of a [256 rows][64 k] stage, 8 rows per instruction;
+// `row0` is the first tensor row of this half (relative to the descriptor base), `ldb` the
+// tensor's bytes per row.  Each row is one whole 128-byte line.
+__device__ __forceinline__ void kc_offsets(int row0, int ldb, int (&vo)[16]) {
   const int L = threadIdx.x & 63;
-  const int c = (L & 3) ^ ((L >> 4) & 3);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) vo[i] = (row0 + 16 * i + (L >> 2)) * ldb + 16 * c;
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * i + (L >> 3);              // LDS row within the half (128h is a multiple of 16)
+    vo[i] = (row0 + r) * ldb + 16 * ((L & 7) ^ kc_swz(r));
+  }
 }
 
-// KS operand: K-rows 16h .. 16h + 15 of a [32 k][256 columns] stage, 2 rows per instruction.
-__device__ __forceinline__ void ks_offsets(int h, int ldb, int (&vo)[8]) {
+// KS operand: K-rows 32h .. 32h + 31 of a [64 k][256 columns] stage, 2 rows per instruction.
+__device__ __forceinline__ void ks_offsets(int h, int ldb, int (&vo)[16]) {
   const int L = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kr = 16 * h + 2 * i + (L >> 5);
+  for (int i = 0; i < 16; ++i) {
+    const int kr = 32 * h + 2 * i + (L >> 5);
     vo[i] = kr * ldb + 16 * ((L & 31) ^ ks_swz(kr));
   }
 }
@@ -217,29 +221,31 @@ __device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& ld, b
     if (kt >= kf) { r = ld.r1; soff = (kt - kf) * ld.step; }
   }
   if (kt >= nk) { r = make_rsrc(p.a0, 0); soff = 0; }
-  uint8_t* dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * 8192;
+  uint8_t* dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * (OP_BYTES / 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma16(r, dst + i * 1024, ld.vo[i], soff);
+  for (int i = 0; i < 16; ++i) dma16(r, dst + i * 1024, ld.vo[i], soff);
 }
 
 // ---------------------------------------------------------------- fragments
 
 // Per-lane fragment addresses within a stage, computed once.
-//   KC: fragment q (rows 16q .. 16q + 15 of the stage) of lane l sits at kc + 1024 q: the chunk
-//       swizzle (r >> 2) & 3 of row r = 16q + l % 16 does not depend on q.
-//   KS: fragment q (columns 16q .. 16q + 15) of lane l, half h (K = 8 (l / 16) + 4h .. + 3), is
-//       read at ks[h] ^ (q << 5): row k = 8 (l / 16) + 4h + (l % 16) / 4 and columns
-//       16q + 4 (l % 4) .. + 3; the row's swizzle only flips bits 5..7 of the byte address, the
-//       same bits q selects.
+//   KC: fragment q (rows 16q .. 16q + 15 of the stage) of lane l, sub-step s, sits at
+//       kc[s] + 2048 q: the chunk swizzle (r >> 1) & 7 of row r = 16q + l % 16 does not depend
+//       on q.
+//   KS: fragment q (columns 16q .. 16q + 15) of lane l, half h (K = 32s + 8 (l / 16) + 4h .. + 3),
+//       is read at (ks[h] ^ (q << 5)) + 16384 s: row k = 32s + 8 (l / 16) + 4h + (l % 16) / 4 and
+//       columns 16q + 4 (l % 4) .. + 3; the row's swizzle only flips bits 5..7 of the byte
+//       address, the same bits q selects, and does not depend on s.
 struct FragAddr {
-  uint32_t kc;
-  uint32_t ks[2];
+  uint32_t kc[2];     // per 32-deep sub-step
+  uint32_t ks[2];     // per half; sub-step 1 is 32 rows (16 KiB) further
 };
 
 __device__ __forceinline__ FragAddr frag_addr() {
   const int l = threadIdx.x & 63;
   FragAddr fa;
-  fa.kc = kc_off(l & 15, l >> 4);
+  fa.kc[0] = kc_off(l & 15, l >> 4);
+  fa.kc[1] = kc_off(l & 15, 4 + (l >> 4));
   const int g = l >> 4, i = l & 15;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -257,20 +263,21 @@ __device__ __forceinline__ void ds_b128(bf16x8& v, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
 
+template <int OFF>
 __device__ __forceinline__ void ds_tr(s16x4& v, uint32_t addr) {
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
 
-// Fragment q of the operand whose stage starts at LDS address `base` (KC or KS layout).
-template <bool KC, int Q>
+// Fragment q of sub-step S of the operand whose stage starts at LDS address `base`.
+template <bool KC, int S, int Q>
 __device__ __forceinline__ void read_frag(bf16x8& v, uint32_t base, const FragAddr& fa, int qoff) {
   if constexpr (KC) {
-    ds_b128<1024 * Q>(v, base + fa.kc + 1024 * qoff);
+    ds_b128<2048 * Q>(v, base + fa.kc[S] + 2048 * qoff);
   } else {
     s16x4 h0, h1;
     const uint32_t q = static_cast<uint32_t>(Q + qoff) << 5;
-    ds_tr(h0, base + (fa.ks[0] ^ q));
-    ds_tr(h1, base + (fa.ks[1] ^ q));
+    ds_tr<16384 * S>(h0, base + (fa.ks[0] ^ q));
+    ds_tr<16384 * S>(h1, base + (fa.ks[1] ^ q));
     v = __builtin_shufflevector(__builtin_bit_cast(bf16x4, h0), __builtin_bit_cast(bf16x4, h1), 0, 1, 2, 3, 4, 5,
                                 6, 7);
   }
@@ -314,41 +321,43 @@ __device__ __forceinline__ int bfrag_base(int wn) {
   return MODE == FWD1 ? 4 * wn : 8 * wn;
 }
 
-// One K step of tile kt (in stage st), as 8 rows of 8 MFMAs; row i multiplies B fragment i by
+// One 32-deep sub-step S of K tile kt, as 8 rows of 8 MFMAs; row i multiplies B fragment i by
 // the 8 A fragments.  Fragment reads run one row ahead of their use, from small register sets:
-//   a[8]      A fragments of tile kt (read during the previous step), an[8] those of tile kt+1;
+//   a[8]      A fragments of this sub-step (read during the previous one), an[8] the next's;
 //   b[2]      ping-pong: B fragment i+1 is read while row i runs.
-// The barrier before row 4 opens tile kt+1: each wave first waits for its own DMA of that tile,
-// and past the barrier every wave has also finished reading tile kt-1, whose stages then
-// receive the DMA of tiles kt+NA-1 (A waves) and kt+NB-1 (B waves).  Rows 4..7 read the A
-// fragments of tile kt+1 (two per row) and row 7 its first B fragment.
-template <int MODE>
-__device__ __forceinline__ void k_step(const Params& p, const OpLoad& ld, bool role_b, int h, const FragAddr& fa,
-                                       int kt, int nk, int sa, int sb, bf16x8 (&a)[8], bf16x8 (&an)[8],
-                                       bf16x8 (&b)[2], f32x4 (&acc)[8][8]) {
+// Sub-step 0 prefetches sub-step 1 from the same stages.  Sub-step 1 opens tile kt+1 before its
+// row 4: each wave waits for its own DMA of that tile and joins a barrier; past it every wave
+// has finished reading A of tile kt (consumed by the end of sub-step 0) and B of tile kt-1, so
+// the DMA of tile kt+2 goes into those stages.  Rows 4..7 then read tile kt+1's first A
+// fragments, and row 7 its first B fragment.
+template <int MODE, int S>
+__device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool role_b, int h, const FragAddr& fa,
+                                         int kt, int nk, int sa, int sb, bf16x8 (&a)[8], bf16x8 (&an)[8],
+                                         bf16x8 (&b)[2], f32x4 (&acc)[8][8]) {
   constexpr bool AKC = Traits<MODE>::A_KC, BKC = Traits<MODE>::B_KC;
   constexpr int RA = AKC ? 1 : 2;   // LDS reads per A fragment
   constexpr int RB = BKC ? 1 : 2;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qa = 8 * (wave >> 1);
   const int qb = bfrag_base<MODE>(wave & 1);
-  const int san = sa + 1 == NA ? 0 : sa + 1, sap = sa == 0 ? NA - 1 : sa - 1;
+  const int san = sa + 1 == NA ? 0 : sa + 1;
   const int sbn = sb + 1 == NB ? 0 : sb + 1, sbp = sb == 0 ? NB - 1 : sb - 1;
   const uint32_t ring = lds_addr(lds_ring);
+  const uint32_t a_cur = ring + A_RING + sa * OP_BYTES, a_nxt = ring + A_RING + san * OP_BYTES;
   const uint32_t b_cur = ring + B_RING + sb * OP_BYTES, b_nxt = ring + B_RING + sbn * OP_BYTES;
-  const uint32_t a_nxt = ring + A_RING + san * OP_BYTES;
   static_for<0, 8>([&](auto i) {
-    if constexpr (i == 4) {
-      // own DMA of tile kt+1 done (B waves keep NB-3 newer tiles in flight, A waves NA-3)
-      if (role_b) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NB - 3)) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NA - 3)) : "memory");
-      issue_stage<MODE>(p, ld, role_b, h, kt + (role_b ? NB : NA) - 1, nk, role_b ? sbp : sap);
+    if constexpr (S == 1 && i == 4) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      issue_stage<MODE>(p, ld, role_b, h, kt + 2, nk, role_b ? sbp : sa);
     }
-    if constexpr (i < 7) read_frag<BKC, bfrag_c<MODE, i + 1>()>(b[(i + 1) & 1], b_cur, fa, qb);
-    else read_frag<BKC, bfrag_c<MODE, 0>()>(b[0], b_nxt, fa, qb);
+    if constexpr (i < 7) read_frag<BKC, S, bfrag_c<MODE, i + 1>()>(b[(i + 1) & 1], b_cur, fa, qb);
+    else if constexpr (S == 0) read_frag<BKC, 1, bfrag_c<MODE, 0>()>(b[0], b_cur, fa, qb);
+    else read_frag<BKC, 0, bfrag_c<MODE, 0>()>(b[0], b_nxt, fa, qb);
     if constexpr (i >= 4) {
-      read_frag<AKC, 2 * (i - 4)>(an[2 * (i - 4)], a_nxt, fa, qa);
-      read_frag<AKC, 2 * (i - 4) + 1>(an[2 * (i - 4) + 1], a_nxt, fa, qa);
+      constexpr int SN = S ^ 1;
+      const uint32_t src = S == 0 ? a_cur : a_nxt;
+      read_frag<AKC, SN, 2 * (i - 4)>(an[2 * (i - 4)], src, fa, qa);
+      read_frag<AKC, SN, 2 * (i - 4) + 1>(an[2 * (i - 4) + 1], src, fa, qa);
     }
     lgkm_wait<RB + (i >= 4 ? 2 * RA : 0)>(b[i & 1], a);
     static_for<0, 8>([&](auto j) { mfma_acc(acc[i][j], b[i & 1], a[j]); });
@@ -561,29 +570,20 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
     asm volatile("s_nop 7" ::: "memory");
-    // ---- prologue: tiles 0 .. N-2 of this wave's ring in flight, then tile 0 everywhere
-    if (role_b) {
-#pragma unroll
-      for (int st = 0; st < NB - 1; ++st) issue_stage<MODE>(p, ld, true, h, st, nk, st);
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NB - 2)) : "memory");
-    } else {
-#pragma unroll
-      for (int st = 0; st < NA - 1; ++st) issue_stage<MODE>(p, ld, false, h, st, nk, st);
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (NA - 2)) : "memory");
-    }
+    // ---- prologue: tiles 0 and 1 in flight, then tile 0 everywhere
+    issue_stage<MODE>(p, ld, role_b, h, 0, nk, 0);
+    issue_stage<MODE>(p, ld, role_b, h, 1, nk, 1);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
     const FragAddr fa = frag_addr();
     const uint32_t a0 = lds_addr(lds_ring) + A_RING, b0 = lds_addr(lds_ring) + B_RING;
     const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
     bf16x8 fa0[8], fa1[8], fb[2];
-    static_for<0, 8>([&](auto j) { read_frag<Traits<MODE>::A_KC, j>(fa0[j], a0, fa, qa); });
-    read_frag<Traits<MODE>::B_KC, bfrag_c<MODE, 0>()>(fb[0], b0, fa, qb);
-    // the K loop runs an even number of steps; steps past nk multiply zeros
+    static_for<0, 8>([&](auto j) { read_frag<Traits<MODE>::A_KC, 0, j>(fa0[j], a0, fa, qa); });
+    read_frag<Traits<MODE>::B_KC, 0, bfrag_c<MODE, 0>()>(fb[0], b0, fa, qb);
     int sa = 0, sb = 0;
-    for (int kt = 0; kt < nk; kt += 2) {
-      k_step<MODE>(p, ld, role_b, h, fa, kt, nk, sa, sb, fa0, fa1, fb, acc);
-      sa = sa + 1 == NA ? 0 : sa + 1;
-      sb = sb + 1 == NB ? 0 : sb + 1;
-      k_step<MODE>(p, ld, role_b, h, fa, kt + 1, nk, sa, sb, fa1, fa0, fb, acc);
+    for (int kt = 0; kt < nk; ++kt) {
+      sub_step<MODE, 0>(p, ld, role_b, h, fa, kt, nk, sa, sb, fa0, fa1, fb, acc);
+      sub_step<MODE, 1>(p, ld, role_b, h, fa, kt, nk, sa, sb, fa1, fa0, fb, acc);
       sa = sa + 1 == NA ? 0 : sa + 1;
       sb = sb + 1 == NB ? 0 : sb + 1;
     }
