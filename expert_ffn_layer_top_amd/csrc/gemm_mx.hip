@@ -16,11 +16,20 @@
 //   WGRAD_GU    dg^T_q | du^T_q [f][P]  x  xp^T_q [d][P]              -> dW_gate[e], dW_up[e]
 // where P is the padded token axis: expert e owns positions [offsets_pad[e], offsets_pad[e+1]).
 //
-// Tile geometry matches the bf16 kernels: 256 x 256 outputs per workgroup, four waves of
-// 128 x 128, K step 128 elements = one 128-byte LDS row per operand row (same XOR swizzle), two
-// stages.  Each K step also stages 4 scale bytes per row (one 32-bit word) in LDS.  The MFMA
-// lane layout (checked on the device): lane l holds row l % 16, K bytes 16*(l/16) .. +15 and
-// 64 + 16*(l/16) .. +15 of the 128-wide step, and supplies the scale of row l % 16, K block l/16.
+// Tile geometry and staging follow the bf16 kernels: 256 x 256 outputs per workgroup, four
+// waves of 128 x 128 (256 fp32 accumulators per lane in AGPRs), K stages of 128 elements = one
+// 128-byte row per operand row, XOR-swizzled 16-byte chunks, LDS-DMA buffer loads.  Waves 0-1
+// stream the N-side operand and waves 2-3 the M-side one, two stages each; each stage also
+// carries the 4 scale bytes of every row.  The barrier opening tile
+// kt sits at the start of step kt: past it every wave has finished tile kt-1, so the DMA of tile
+// kt+1 goes into its stages while tile kt is consumed.  The MFMA lane layout (checked on the
+// device): lane l holds row l % 16, K bytes 16*(l/16) .. +15 and 64 + 16*(l/16) .. +15 of the
+// 128-wide step, and supplies the scale of row l % 16, K block l/16.
+//
+// Weight-gradient K tails: an expert's padded token range is a multiple of 32, not of 128, so a
+// stage can run into the next expert's positions.  Those K blocks get scale byte 0 on both
+// operands (2^-127 each): their products fall below the smallest fp32 subnormal and add exactly
+// zero.
 #include <type_traits>
 
 #include "common.h"
@@ -29,17 +38,30 @@ namespace moe {
 namespace gmx {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 128;                           // fp8 elements (bytes) per K step
 constexpr int NTH = 256;
-constexpr int ROW_BYTES = BK;
-constexpr int TILE_BYTES = BM * ROW_BYTES;        // 32 KiB
-constexpr int SCALE_BYTES = BM * 4;               // 1 KiB per operand per stage
-constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * SCALE_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;        // 130 KiB
+constexpr int OP_BYTES = BM * BK;                 // 32 KiB per operand per stage
+constexpr int SC_BYTES = BM * 4 * 4;              // scales: one dword slot per (row, K block)
+constexpr int NSTG = 2;                           // stages per operand ring
+constexpr int A_RING = 0;
+constexpr int B_RING = NSTG * OP_BYTES;
+constexpr int SA_RING = 2 * NSTG * OP_BYTES;
+constexpr int SB_RING = SA_RING + NSTG * SC_BYTES;
+constexpr int LDS_TOTAL = SB_RING + NSTG * SC_BYTES;   // 144 KiB
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;      // raw buffer, 32-bit data format (gfx9 family)
+
+__shared__ __attribute__((aligned(1024))) uint8_t lds_ring[LDS_TOTAL];
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(p)));
+}
 
 enum Mode { FWD1 = 0, FWD2 = 1, DGRAD1 = 2, DGRAD2 = 3, WGRAD_DOWN = 4, WGRAD_GU = 5 };
 
@@ -67,14 +89,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int chunk) { return r * ROW_BYTES + ((chunk ^ swz(r)) << 4); }
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
 template <int MODE>
 struct Traits {
   static constexpr bool WGRAD = (MODE >= WGRAD_DOWN);
 };
+
+// row r (128 bytes = 8 chunks), chunk c stored at chunk position c ^ ((r >> 1) & 7)
+__device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 128 + ((c ^ kc_swz(r)) << 4); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  const int nrec = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nrec, RSRC_WORD3);
+}
 
 struct Tile {
   int e, m0, m_end, n0, half;
@@ -97,118 +124,153 @@ __device__ __forceinline__ int k_total(const Params& p) {
   return 0;
 }
 
-// Loads one K step of the A side (M rows) into registers: 8 data chunks + 1 scale word.
-template <int MODE>
-__device__ __forceinline__ void load_a(const Params& p, const Tile& t, int kt, uint4 (&reg)[8], uint32_t& sreg) {
-  const int tid = threadIdx.x;
-  const int ch = tid & 7;
-  if constexpr (!Traits<MODE>::WGRAD) {
-    const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
-    int k0 = kt * BK;
-    const uint8_t* base = p.a0;
-    const uint8_t* sbase = p.a0s;
-    if (MODE == DGRAD2 && k0 >= p.f) { base = p.a1; sbase = p.a1s; k0 -= p.f; }
+// m-tile prefix over experts from one round of loads (lane l holds experts l + 64 r).
+struct MTiles {
+  int tiles[4], excl[4];
+  int total;
+};
+
+__device__ __forceinline__ MTiles mtile_scan(const int32_t* __restrict__ offsets, int E) {
+  const int lane = threadIdx.x & 63;
+  MTiles m;
+  int lo[4], hi[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = t.m0 + (tid >> 3) + 32 * i;
-      r = r < p.n ? r : p.n - 1;
-      reg[i] = ld16(base + static_cast<long long>(r) * K + k0 + 16 * ch);
+  for (int r = 0; r < 4; ++r) {
+    const int ex = 64 * r + lane;
+    lo[r] = ex < E ? offsets[ex] : 0;
+    hi[r] = ex < E ? offsets[ex + 1] : 0;
+  }
+  int carry = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tiles = (hi[r] - lo[r] + BM - 1) / BM;
+    int incl = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
     }
-    int r = t.m0 + tid;
-    r = r < p.n ? r : p.n - 1;
-    sreg = *reinterpret_cast<const uint32_t*>(sbase + static_cast<long long>(r) * (K / 32) + k0 / 32);
-  } else {
-    const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
-    const uint8_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
-    const uint8_t* sbase = (MODE == WGRAD_GU && t.half) ? p.a1s : p.a0s;
-    const int k0 = kt * BK;
+    m.tiles[r] = tiles;
+    m.excl[r] = carry + incl - tiles;
+    carry += __shfl(incl, 63, 64);
+  }
+  m.total = __builtin_amdgcn_readfirstlane(carry);
+  return m;
+}
+
+__device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int& first) {
+  const int lane = threadIdx.x & 63;
+  e = 0;
+  first = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int m = t.m0 + (tid >> 3) + 32 * i;
-      m = m < Mtot ? m : Mtot - 1;
-      const int k = k0 + 16 * ch;
-      reg[i] = (k < t.k_len) ? ld16(base + static_cast<long long>(m) * p.P + t.k_begin + k) : make_uint4(0, 0, 0, 0);
+  for (int r = 0; r < 4; ++r) {
+    const unsigned long long hit = __ballot(m.tiles[r] > 0 && m.excl[r] <= mt && mt < m.excl[r] + m.tiles[r]);
+    if (hit) {
+      const int src = __ffsll(static_cast<long long>(hit)) - 1;
+      e = 64 * r + src;
+      first = __shfl(m.excl[r], src, 64);
     }
-    int m = t.m0 + tid;
-    m = m < Mtot ? m : Mtot - 1;
-    const uint8_t* sp = sbase + static_cast<long long>(m) * (p.P / 32) + (t.k_begin + k0) / 32;
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (k0 + 32 * b < t.k_len) w |= static_cast<uint32_t>(sp[b]) << (8 * b);
-    sreg = w;
   }
 }
 
-// Loads one K step of the B side (N rows).
+// One wave's share of an operand stage: 128 rows x 128 bytes of data (16 DMA instructions) and
+// the rows' 4-byte scale words (2 dword DMA instructions).
+struct OpLoad {
+  __amdgpu_buffer_rsrc_t r0, r1, s0, s1;   // data / scale descriptors (r1, s1: second tensor)
+  int vo[16];
+  int so[8];
+  int step, sstep;                         // bytes per K step (data, scales)
+};
+
+// Rows row0 .. row0 + 127 of a row-major byte tensor with `ldb` bytes per row, and their scale
+// bytes (`lds_` bytes per row).  The byte form of the LDS-DMA load puts each lane's byte in a
+// dword slot of its own (checked on the device), so a stage keeps one dword per (row, K block):
+// 8 instructions of 16 rows x 4 blocks.  Bytes also serve the weight-gradient operands, whose
+// scales start at an expert's padded position / 32 and need not be 4-byte aligned.
+__device__ __forceinline__ void op_offsets(int row0, int ldb, int lds_, OpLoad& ld) {
+  const int L = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * i + (L >> 3);
+    ld.vo[i] = (row0 + r) * ldb + 16 * ((L & 7) ^ kc_swz(r));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ld.so[i] = (row0 + 16 * i + (L >> 2)) * lds_ + (L & 3);
+}
+
 template <int MODE>
-__device__ __forceinline__ void load_b(const Params& p, const Tile& t, int kt, uint4 (&reg)[8], uint32_t& sreg) {
-  const int tid = threadIdx.x;
-  const int ch = tid & 7;
-  const int k0 = kt * BK;
+__device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& ld, bool role_b, int h, int kt, int nk,
+                                            int st) {
+  __amdgpu_buffer_rsrc_t r = ld.r0, rs = ld.s0;
+  int soff = kt * ld.step, ssoff = kt * ld.sstep;
   if constexpr (MODE == FWD1) {
-    // LDS rows 0..127: W_gate_q[e] rows n0 + r; rows 128..255: W_up_q[e] rows n0 + r - 128
-    const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
-    const long long esoff = static_cast<long long>(t.e) * p.f * (p.d / 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      int c = t.n0 + (r & 127);
-      c = c < p.f ? c : p.f - 1;
-      reg[i] = ld16(((r < 128) ? p.b0 : p.b1) + eoff + static_cast<long long>(c) * p.d + k0 + 16 * ch);
-    }
-    int c = t.n0 + (tid & 127);
-    c = c < p.f ? c : p.f - 1;
-    sreg = *reinterpret_cast<const uint32_t*>(((tid < 128) ? p.b0s : p.b1s) + esoff +
-                                              static_cast<long long>(c) * (p.d / 32) + k0 / 32);
-  } else if constexpr (!Traits<MODE>::WGRAD) {
-    // weights [E][Ntot][K'] quantised along K' (K' = K, or f per half for DGRAD2)
-    const int Ntot = n_total<MODE>(p);
-    int K = k_total<MODE>(p);
-    int kk = k0;
-    const uint8_t* base = p.b0;
-    const uint8_t* sbase = p.b0s;
-    if constexpr (MODE == DGRAD2) {
-      K = p.f;
-      if (kk >= p.f) { base = p.b1; sbase = p.b1s; kk -= p.f; }
-    }
-    const long long eoff = static_cast<long long>(t.e) * Ntot * K;
-    const long long esoff = static_cast<long long>(t.e) * Ntot * (K / 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int c = t.n0 + (tid >> 3) + 32 * i;
-      c = c < Ntot ? c : Ntot - 1;
-      reg[i] = ld16(base + eoff + static_cast<long long>(c) * K + kk + 16 * ch);
-    }
-    int c = t.n0 + tid;
-    c = c < Ntot ? c : Ntot - 1;
-    sreg = *reinterpret_cast<const uint32_t*>(sbase + esoff + static_cast<long long>(c) * (K / 32) + kk / 32);
-  } else {
-    const int Ntot = n_total<MODE>(p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int c = t.n0 + (tid >> 3) + 32 * i;
-      c = c < Ntot ? c : Ntot - 1;
-      const int k = k0 + 16 * ch;
-      reg[i] = (k < t.k_len) ? ld16(p.b0 + static_cast<long long>(c) * p.P + t.k_begin + k) : make_uint4(0, 0, 0, 0);
-    }
-    int c = t.n0 + tid;
-    c = c < Ntot ? c : Ntot - 1;
-    const uint8_t* sp = p.b0s + static_cast<long long>(c) * (p.P / 32) + (t.k_begin + k0) / 32;
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (k0 + 32 * b < t.k_len) w |= static_cast<uint32_t>(sp[b]) << (8 * b);
-    sreg = w;
+    if (role_b && h) { r = ld.r1; rs = ld.s1; }
+  } else if constexpr (MODE == DGRAD2) {
+    const int kf = p.f / BK;
+    if (kt >= kf) { r = ld.r1; rs = ld.s1; soff = (kt - kf) * ld.step; ssoff = (kt - kf) * ld.sstep; }
   }
-}
-
-__device__ __forceinline__ void store_stage(uint8_t* tile, uint32_t* scales, const uint4 (&reg)[8], uint32_t sreg) {
-  const int tid = threadIdx.x;
+  if (kt >= nk) { r = make_rsrc(p.a0, 0); rs = r; soff = 0; ssoff = 0; }
+  uint8_t* dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * (OP_BYTES / 2);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, ld.vo[i], soff, 0, 0);
+  uint8_t* sdst = lds_ring + (role_b ? SB_RING : SA_RING) + st * SC_BYTES + h * (SC_BYTES / 2);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint4*>(tile + lds_off((tid >> 3) + 32 * i, tid & 7)) = reg[i];
-  scales[tid] = sreg;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sdst + i * 256), 1, ld.so[i], ssoff, 0, 0);
+}
+
+// acc += x * y (scaled fp8), accumulating in place in AGPRs (tied inline asm; callers cover the
+// accumulator-initialisation and epilogue wait states).
+__device__ __forceinline__ void mfma_acc(f32x4& c, const i32x8& x, const i32x8& y, int sx, int sy) {
+  asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+      : "+a"(c)
+      : "v"(x), "v"(y), "v"(sx), "v"(sy));
+}
+
+__device__ __forceinline__ void pin_acc_row(f32x4 (&r)[8]) {
+  asm volatile("" : "+a"(r[0]), "+a"(r[1]), "+a"(r[2]), "+a"(r[3]), "+a"(r[4]), "+a"(r[5]), "+a"(r[6]),
+               "+a"(r[7]));
+}
+
+// Fragment q (16 rows) of a stage: lane l reads row 16q + l % 16, chunks l/16 and 4 + l/16, and
+// the scale slot of that row and K block l/16.
+template <int OFF>
+__device__ __forceinline__ void ds_b128(i32x4& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_b32(int& v, uint32_t addr) {
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+
+template <int Q>
+__device__ __forceinline__ void read_frag(i32x8& v, int& sw, uint32_t base, uint32_t sbase, uint32_t kc0,
+                                          uint32_t kc1, uint32_t srow, int qoff) {
+  i32x4 lo, hi;
+  ds_b128<2048 * Q>(lo, base + kc0 + 2048 * qoff);
+  ds_b128<2048 * Q>(hi, base + kc1 + 2048 * qoff);
+  ds_b32<256 * Q>(sw, sbase + srow + 256 * qoff);
+  v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait(i32x8& b, int& sb, i32x8 (&a)[8], int (&sa)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%18)"
+               : "+v"(b), "+v"(sb), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                 "+v"(a[6]), "+v"(a[7]), "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sa[4]),
+                 "+v"(sa[5]), "+v"(sa[6]), "+v"(sa[7])
+               : "n"(N));
+}
+
+template <int MODE, int I>
+__device__ __forceinline__ constexpr int bfrag_c() {
+  if constexpr (MODE == FWD1) return (I < 4) ? I : 8 + (I - 4);
+  return I;
+}
+template <int MODE>
+__device__ __forceinline__ int bfrag_base(int wn) {
+  return MODE == FWD1 ? 4 * wn : 8 * wn;
 }
 
 __device__ __forceinline__ void st4(uint16_t* p, float a, float b, float c, float d) {
@@ -218,46 +280,30 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 
 template <int MODE>
 __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int s_pre[257];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
+  // ---- device-side schedule (as in the bf16 kernels)
   const int NTW = n_tile_width<MODE>();
   const int ntiles_n = (n_total<MODE>(p) + NTW - 1) / NTW;
-  int total_tiles;
-  if constexpr (!Traits<MODE>::WGRAD) {
-    if (tid == 0) s_pre[0] = 0;
-    for (int e = tid; e < p.E; e += NTH) s_pre[e + 1] = (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
-    __syncthreads();
-    if (tid == 0)
-      for (int e = 0; e < p.E; ++e) s_pre[e + 1] += s_pre[e];
-    __syncthreads();
-    total_tiles = s_pre[p.E] * ntiles_n;
-  } else {
-    const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
-    total_tiles = p.E * ((Mtot + BM - 1) / BM) * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
-  }
-  const int tot8 = (total_tiles + 7) & ~7;
   const int bid = blockIdx.x;
-  if (bid >= tot8) return;
-  const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
-  if (lid >= total_tiles) return;
-
   Tile t;
   if constexpr (!Traits<MODE>::WGRAD) {
+    const MTiles mts = mtile_scan(p.offsets, p.E);
+    const int total_tiles = mts.total * ntiles_n;
+    const int tot8 = (total_tiles + 7) & ~7;
+    if (bid >= tot8) return;
+    const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
+    if (lid >= total_tiles) return;
     const int mt_glob = lid / ntiles_n;
     const int nt = lid - mt_glob * ntiles_n;
-    int lo = 0, hi = p.E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[mid] <= mt_glob) lo = mid; else hi = mid - 1;
-    }
-    t.e = lo;
-    t.m0 = p.offsets[lo] + (mt_glob - s_pre[lo]) * BM;
-    t.m_end = p.offsets[lo + 1];
+    int e, first;
+    mtile_find(mts, mt_glob, e, first);
+    t.e = e;
+    t.m0 = p.offsets[e] + (mt_glob - first) * BM;
+    t.m_end = p.offsets[e + 1];
     t.n0 = nt * NTW;
     t.half = 0;
     t.k_begin = 0;
@@ -265,7 +311,13 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
   } else {
     const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
     const int mt = (Mtot + BM - 1) / BM;
-    const int per_e = mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
+    const int mtt = mt * (MODE == WGRAD_GU ? 2 : 1);
+    const int total_tiles = p.E * mtt * ntiles_n;
+    const int tot8 = (total_tiles + 7) & ~7;
+    if (bid >= tot8) return;
+    const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
+    if (lid >= total_tiles) return;
+    const int per_e = mtt * ntiles_n;
     t.e = lid / per_e;
     const int rem = lid - t.e * per_e;
     const int mi = rem / ntiles_n;
@@ -277,7 +329,93 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
     t.k_begin = p.offsets_pad[t.e];
     t.k_len = p.offsets_pad[t.e + 1] - t.k_begin;
   }
+  // the tile is uniform; without this the descriptors below would look divergent
+  t.e = __builtin_amdgcn_readfirstlane(t.e);
+  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+  t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);
+  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  t.half = __builtin_amdgcn_readfirstlane(t.half);
+  t.k_begin = __builtin_amdgcn_readfirstlane(t.k_begin);
+  t.k_len = __builtin_amdgcn_readfirstlane(t.k_len);
   const int nk = (t.k_len + BK - 1) / BK;
+
+  // ---- this wave's DMA operand (waves 0, 1 -> B; 2, 3 -> A), bounded to its valid extent
+  const bool role_b = wave < 2;
+  const int h = wave & 1;
+  OpLoad ld;
+  if (!role_b) {
+    if constexpr (!Traits<MODE>::WGRAD) {
+      const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
+      const long long rem_rows = static_cast<long long>(p.n) - t.m0;
+      ld.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K);
+      ld.s0 = make_rsrc(p.a0s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
+      ld.r1 = ld.r0;
+      ld.s1 = ld.s0;
+      if constexpr (MODE == DGRAD2) {
+        ld.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * K, rem_rows * K);
+        ld.s1 = make_rsrc(p.a1s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
+      }
+      ld.step = BK;
+      ld.sstep = BK / 32;
+      op_offsets(128 * h, K, K / 32, ld);
+    } else {
+      // [Mtot][P]: rows m0 .., columns from the expert's first padded position
+      const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
+      const uint8_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
+      const uint8_t* sbase = (MODE == WGRAD_GU && t.half) ? p.a1s : p.a0s;
+      const long long rem_rows = static_cast<long long>(Mtot) - t.m0;
+      ld.r0 = make_rsrc(base + static_cast<long long>(t.m0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
+      ld.s0 = make_rsrc(sbase + static_cast<long long>(t.m0) * (p.P / 32) + t.k_begin / 32,
+                        rem_rows * (p.P / 32) - t.k_begin / 32);
+      ld.r1 = ld.r0;
+      ld.s1 = ld.s0;
+      ld.step = BK;
+      ld.sstep = BK / 32;
+      op_offsets(128 * h, p.P, p.P / 32, ld);
+    }
+  } else {
+    if constexpr (MODE == FWD1) {
+      const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
+      const long long esoff = static_cast<long long>(t.e) * p.f * (p.d / 32);
+      const long long rows = p.f - t.n0;
+      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
+      ld.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
+      ld.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
+      ld.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
+      ld.step = BK;
+      ld.sstep = BK / 32;
+      op_offsets(0, p.d, p.d / 32, ld);
+    } else if constexpr (!Traits<MODE>::WGRAD) {
+      // weights [E][Ntot][K'] quantised along K' (K' = K, or f per half for DGRAD2)
+      const int Ntot = n_total<MODE>(p);
+      const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
+      const long long eoff = static_cast<long long>(t.e) * Ntot * K;
+      const long long esoff = static_cast<long long>(t.e) * Ntot * (K / 32);
+      const long long rows = Ntot - t.n0;
+      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * K, rows * K);
+      ld.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
+      ld.r1 = ld.r0;
+      ld.s1 = ld.s0;
+      if constexpr (MODE == DGRAD2) {
+        ld.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * K, rows * K);
+        ld.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
+      }
+      ld.step = BK;
+      ld.sstep = BK / 32;
+      op_offsets(128 * h, K, K / 32, ld);
+    } else {
+      const int Ntot = n_total<MODE>(p);
+      const long long rem_rows = static_cast<long long>(Ntot) - t.n0;
+      ld.r0 = make_rsrc(p.b0 + static_cast<long long>(t.n0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
+      ld.s0 = make_rsrc(p.b0s + static_cast<long long>(t.n0) * (p.P / 32) + t.k_begin / 32,
+                        rem_rows * (p.P / 32) - t.k_begin / 32);
+      ld.r1 = ld.r0;
+      ld.s1 = ld.s0;
+      ld.step = BK;
+      ld.sstep = BK / 32;
+      op_offsets(128 * h, p.P, p.P / 32, ld);
+    }
+  }
 
   f32x4 acc[8][8];
 #pragma unroll
@@ -285,71 +423,38 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto brow = [&](int i) -> int {
-    if constexpr (MODE == FWD1) return (i < 4) ? (64 * wn + 16 * i) : (128 + 64 * wn + 16 * (i - 4));
-    return 128 * wn + 16 * i;
-  };
-
-  uint4 ra[8], rb[8];
-  uint32_t sa_reg = 0, sb_reg = 0;
-  auto stage_ptrs = [&](int st, uint8_t*& ta, uint8_t*& tb, uint32_t*& sa, uint32_t*& sb) {
-    uint8_t* base = lds + st * STAGE_BYTES;
-    ta = base;
-    tb = base + TILE_BYTES;
-    sa = reinterpret_cast<uint32_t*>(base + 2 * TILE_BYTES);
-    sb = reinterpret_cast<uint32_t*>(base + 2 * TILE_BYTES + SCALE_BYTES);
-  };
   if (nk > 0) {
-    load_a<MODE>(p, t, 0, ra, sa_reg);
-    load_b<MODE>(p, t, 0, rb, sb_reg);
-    uint8_t *ta, *tb;
-    uint32_t *sa, *sb;
-    stage_ptrs(0, ta, tb, sa, sb);
-    store_stage(ta, sa, ra, sa_reg);
-    store_stage(tb, sb, rb, sb_reg);
-  }
-  __syncthreads();
-
-  const int sel = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_a<MODE>(p, t, kt + 1, ra, sa_reg);
-      load_b<MODE>(p, t, kt + 1, rb, sb_reg);
-    }
-    uint8_t *ta, *tb;
-    uint32_t *sa, *sb;
-    stage_ptrs(kt & 1, ta, tb, sa, sb);
-    i32x8 fa[8], fb[8];
-    int xa[8], xb[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 128 * wm + 16 * j + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(ta + lds_off(r, sel));
-      const uint4 hi = *reinterpret_cast<const uint4*>(ta + lds_off(r, 4 + sel));
-      fa[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      xa[j] = (sa[r] >> (8 * sel)) & 0xff;
+    for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
+    asm volatile("s_nop 7" ::: "memory");
+    // per-lane fragment addresses: row l % 16 of each 16-row fragment, chunks l/16 and 4 + l/16
+    const uint32_t kc0 = kc_off(lane & 15, lane >> 4), kc1 = kc_off(lane & 15, 4 + (lane >> 4));
+    const uint32_t srow = 16 * (lane & 15) + 4 * (lane >> 4);   // dword slot (row, K block l/16)
+    const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
+    const uint32_t ring = lds_addr(lds_ring);
+    issue_stage<MODE>(p, ld, role_b, h, 0, nk, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      // tile kt in LDS everywhere; every wave is done with tile kt-1, whose stages take tile kt+1
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      issue_stage<MODE>(p, ld, role_b, h, kt + 1, nk, st ^ 1);
+      const uint32_t a_base = ring + A_RING + st * OP_BYTES, b_base = ring + B_RING + st * OP_BYTES;
+      const uint32_t sa_base = ring + SA_RING + st * SC_BYTES, sb_base = ring + SB_RING + st * SC_BYTES;
+      i32x8 fa[8], fb[2];
+      int xa[8], xb[2];
+      static_for<0, 8>([&](auto j) { read_frag<j>(fa[j], xa[j], a_base, sa_base, kc0, kc1, srow, qa); });
+      read_frag<bfrag_c<MODE, 0>()>(fb[0], xb[0], b_base, sb_base, kc0, kc1, srow, qb);
+      // K blocks past the expert's padded range (wgrad only): scale 0 on both sides -> exact zero
+      int live = 0xff;
+      if constexpr (Traits<MODE>::WGRAD) live = (kt * BK + 32 * (lane >> 4) < t.k_len) ? 0xff : 0;
+      static_for<0, 8>([&](auto i) {
+        if constexpr (i < 7) read_frag<bfrag_c<MODE, i + 1>()>(fb[(i + 1) & 1], xb[(i + 1) & 1], b_base, sb_base, kc0, kc1, srow, qb);
+        lgkm_wait<i < 7 ? 3 : 0>(fb[i & 1], xb[i & 1], fa, xa);
+        const int sbv = xb[i & 1] & live;
+        static_for<0, 8>([&](auto j) { mfma_acc(acc[i][j], fb[i & 1], fa[j], sbv, xa[j] & live); });
+      });
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = brow(i) + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(tb + lds_off(r, sel));
-      const uint4 hi = *reinterpret_cast<const uint4*>(tb + lds_off(r, 4 + sel));
-      fb[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      xb[i] = (sb[r] >> (8 * sel)) & 0xff;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[i], fa[j], acc[i][j], 0, 0, 0, xb[i], 0,
-                                                                     xa[j]);
-    if (more) {
-      stage_ptrs((kt + 1) & 1, ta, tb, sa, sb);
-      store_stage(ta, sa, ra, sa_reg);
-      store_stage(tb, sb, rb, sb_reg);
-    }
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
   }
 
   const int rl = lane & 15;
@@ -428,18 +533,15 @@ inline long long grid_upper(int mode, int E, int n, int d, int f) {
 
 template <int MODE>
 int launch(const Params& p, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    // Raises the dynamic-LDS limit for this kernel.  Advisory: where the runtime does not take the
-    // attribute, the launch below reports any real problem, so its status is cleared, not returned.
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&mx_grouped_gemm_kernel<MODE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    (void)hipGetLastError();
-    attr_set = true;
-  }
   const long long g = (grid_upper(MODE, p.E, p.n, p.d, p.f) + 7) / 8 * 8;
   MOE_REQUIRE(g < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many tiles");
-  mx_grouped_gemm_kernel<MODE><<<static_cast<unsigned>(g), NTH, LDS_BYTES, s>>>(p);
+  // every buffer offset the kernel forms stays below 2^31 bytes
+  const long long big = static_cast<long long>(p.n) * (p.d > p.f ? p.d : p.f);
+  const long long wbig = static_cast<long long>(p.d) * p.f;
+  const long long pbig = static_cast<long long>(p.P) * (p.d > p.f ? p.d : p.f);
+  MOE_REQUIRE(big < 0x7fffffffLL && wbig < 0x7fffffffLL && pbig < 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
+              "MXFP8 grouped GEMM: an operand exceeds 2 GiB");
+  mx_grouped_gemm_kernel<MODE><<<static_cast<unsigned>(g), NTH, 0, s>>>(p);
   return check_launch("grouped_gemm_mxfp8");
 }
 
