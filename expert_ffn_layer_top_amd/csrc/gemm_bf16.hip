@@ -409,6 +409,25 @@ __device__ __forceinline__ MTiles mtile_scan(const int32_t* __restrict__ offsets
   return m;
 }
 
+// True when some expert's row count exceeds twice the mean (n / E, rounded up).
+__device__ __forceinline__ bool wgrad_skewed(const int32_t* __restrict__ offsets, int E, int n) {
+  const int lane = threadIdx.x & 63;
+  int cmax = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ex = 64 * r + lane;
+    const int c = ex < E ? offsets[ex + 1] - offsets[ex] : 0;
+    cmax = c > cmax ? c : cmax;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int v = __shfl_xor(cmax, o, 64);
+    cmax = v > cmax ? v : cmax;
+  }
+  cmax = __builtin_amdgcn_readfirstlane(cmax);
+  return cmax > 2 * ((n + E - 1) / E);
+}
+
 // The expert owning global m-tile mt (< total) and that expert's first m-tile.
 __device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int& first) {
   const int lane = threadIdx.x & 63;
@@ -462,7 +481,11 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     const int total_tiles = p.E * mtt * ntiles_n;
     const int tot8 = (total_tiles + 7) & ~7;
     if (bid >= tot8) return;
-    const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
+    // Weight-gradient tiles cost in proportion to their expert's rows.  With balanced experts,
+    // keep each XCD on a contiguous run of tiles (experts' operand rows shared in its L2); when
+    // one expert holds more than twice the mean, deal tiles round-robin over the XCDs instead
+    // (block ids go to XCDs round-robin), so a hot expert's tiles run on every XCD at once.
+    const int lid = wgrad_skewed(p.offsets, p.E, p.n) ? bid : (bid & 7) * (tot8 >> 3) + (bid >> 3);
     if (lid >= total_tiles) return;
     const int per_e = mtt * ntiles_n;
     t.e = lid / per_e;
