@@ -8,9 +8,16 @@ backward grouped GEMMs, route backward and permute backward.  Inputs are residen
 the timed region.  The default workload is the balanced-routing layer (8192 tokens, d 2048,
 64 experts, top-4, SwiGLU d_ff 1024, bf16, round-robin logits), fwd+bwd.
 
-Prints one JSON line with the throughput (tokens/s), the roofline of the dominant kernel (the
-gate/up grouped GEMM, timed with HIP events on the stream it runs on, during the timed steps)
-and the oracle's throughput on the host cores over a bounded token sample (a baseline only).
+Prints one JSON line with the throughput (tokens/s), the roofline of the dominant kernel and the
+oracle's throughput on the host cores over a bounded token sample (a baseline only).  Every
+grouped-GEMM call of the step is one kernel and is bracketed with HIP events on the stream it
+runs on, during the timed steps; the dominant kernel is the one with the largest average
+duration (under MXFP8 the forward down call, which also quantises A, is not a candidate).  Its
+`traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary kept
+in profiles/, and is null when that summary is missing or was taken on other kernel sources.
+
+--copy-probe N runs torch's elementwise negation over an fp32 buffer of N bytes three times
+before the warm-up: the plain copy kernel that calibrates the HBM byte counters.
 """
 
 import argparse
@@ -38,6 +45,7 @@ def parse():
     ap.add_argument("--experts", type=int, default=None, help="expert count for the sweep workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     return ap.parse_args()
 
 
@@ -57,38 +65,85 @@ def describe(cfg):
             f"SwiGLU d_ff={cfg.f}, {prec}, fp32 accumulate, seed {cfg.seed}")
 
 
-def run_gpu(cfg, steps, warmup):
+def gemm_flops(cfg):
+    """Algorithmic flop of each grouped-GEMM call over the routed rows (n = T k)."""
+    ndf = float(cfg.n) * cfg.d * cfg.f
+    return {"gate_up": 4 * ndf, "down": 2 * ndf, "dgrad_down": 2 * ndf, "wgrad_down": 2 * ndf,
+            "dgrad_gate_up": 4 * ndf, "wgrad_gate_up": 4 * ndf}
+
+
+def copy_probe(nbytes):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def run_gpu(cfg, steps, warmup, probe_bytes=0):
     import torch
 
     import synth
     from expert_ffn_layer_top_amd import layer
 
     dev = torch.device("cuda:0")
+    if probe_bytes:
+        copy_probe(probe_bytes)
     inputs = synth.to_torch(synth.make_inputs(cfg), dev)
     w = layer.Weights(inputs["w_gate"], inputs["w_up"], inputs["w_down"], w_r=inputs.get("w_r"))
     if cfg.mxfp8:
         w.quantize_mx()
     x, dy, logits = inputs["x"], inputs["dy"], inputs.get("logits")
+    calls = layer.GEMM_CALLS if not cfg.forward_only else ("gate_up", "down")
 
     def step(events=None):
         if cfg.mxfp8:
             w.quantize_mx()                  # weights are re-quantised every step (both directions)
-        ctx = layer.forward(x, w, cfg.k, logits=logits, mxfp8=cfg.mxfp8, gate_up_events=events)
+        ctx = layer.forward(x, w, cfg.k, logits=logits, mxfp8=cfg.mxfp8, events=events)
         if not cfg.forward_only:
-            layer.backward(ctx, w, dy)
+            layer.backward(ctx, w, dy, events=events)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [{c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in calls}
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gate_up_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-    return elapsed, gate_up_ms
+    gemm_ms = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / steps for c in calls}
+    return elapsed, gemm_ms
+
+
+def traffic_of(cfg, call):
+    """HBM bytes per launch of `call` from its counter summary, if it matches the current sources."""
+    from expert_ffn_layer_top_amd import profsum
+    dtype = "mxfp8" if cfg.mxfp8 else "bf16"
+    tag = cfg.name if cfg.name != "sweep" else f"sweep_E{cfg.E}"
+    path = os.path.join(ROOT, "profiles", f"{call}_{dtype}_{tag}_traffic.txt")
+    t = profsum.read_traffic(path)
+    if (t is None or t.get("source_sha256") != profsum.source_sha256(dtype)
+            or t.get("kernel") != profsum.kernel_name(call, dtype)):
+        return None
+    return float(t["traffic_bytes"])
+
+
+def gemm_bytes(cfg, call):
+    """Algorithmic HBM bytes of one grouped-GEMM call: each operand read once, each output written
+    once (bf16 2 B; MXFP8 operands 1 B + 1/32 B of scale)."""
+    n, d, f, E = float(cfg.n), cfg.d, cfg.f, cfg.E
+    ob = 1 + 1 / 32 if cfg.mxfp8 else 2
+    return {"gate_up": ob * (n * d + 2 * E * f * d) + 2 * 3 * n * f,
+            "down": ob * (n * f + E * d * f) + 2 * n * d,
+            "dgrad_down": ob * (n * d + E * d * f) + 2 * 2 * n * f + 2 * 2 * n * f,
+            "wgrad_down": ob * (n * d + n * f) + 2 * E * d * f,
+            "dgrad_gate_up": ob * (2 * n * f + 2 * E * f * d) + 2 * n * d,
+            "wgrad_gate_up": ob * (2 * n * f + n * d) + 2 * 2 * E * f * d}[call]
 
 
 def cpu_baseline(cfg, sample_tokens):
@@ -126,12 +181,16 @@ def main():
               file=sys.stderr)
         return 2
     cfg = workload_config(args)
-    elapsed, gate_up_ms = run_gpu(cfg, args.steps, args.warmup)
+    elapsed, gemm_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
-    flops = 4.0 * cfg.n * cfg.d * cfg.f                      # gate + up products of every routed row
-    achieved = flops / (gate_up_ms * 1e-3) / 1e12
+    flops = gemm_flops(cfg)
+    cand = [c for c in gemm_ms if not (cfg.mxfp8 and c == "down")]
+    dom = max(cand, key=lambda c: gemm_ms[c])
+    achieved = flops[dom] / (gemm_ms[dom] * 1e-3) / 1e12
     peak = PEAK_MXFP8_TFLOPS if cfg.mxfp8 else PEAK_BF16_TFLOPS
+    from expert_ffn_layer_top_amd import profsum
+    dtype = "mxfp8" if cfg.mxfp8 else "bf16"
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -143,14 +202,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8" if cfg.mxfp8 else "bf16",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": describe(cfg), "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
                    "top_k": cfg.k, "d_ff": cfg.f, "fwd_bwd": not cfg.forward_only},
-        "roofline": {"bound": "mfma", "kernel": "grouped GEMM gate/up + SwiGLU epilogue",
-                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
-                     "avg_ms": round(gate_up_ms, 4), "flop_per_launch": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic_of(cfg, dom),
+                     "kernel": f"{profsum.kernel_name(dom, dtype)} ({dom})",
+                     "avg_ms": round(gemm_ms[dom], 4), "flop_per_launch": flops[dom],
+                     "algorithmic_bytes": round(gemm_bytes(cfg, dom))},
+        "gemm_ms": {c: round(v, 4) for c, v in gemm_ms.items()},
+        "gemm_tflops": {c: round(flops[c] / (v * 1e-3) / 1e12, 1) for c, v in gemm_ms.items()},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)

@@ -39,6 +39,12 @@ SIGNATURES = {
     "moe_grouped_gemm_swiglu_bwd": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p,
                                          _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                          _sz, _p]),
+    "moe_grouped_gemm_dgrad_down": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_gemm_wgrad_down": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_gemm_dgrad_gate_up": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                            _p, _p]),
+    "moe_grouped_gemm_wgrad_gate_up": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                            _p, _p]),
 }
 
 

@@ -723,30 +723,49 @@ int gg_bf16_down(int E, int n, int d, int f, const int32_t* offsets, const uint1
   return gg::launch<gg::FWD2>(q, s);
 }
 
-int gg_bf16_backward(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* xp, const uint16_t* g,
-                     const uint16_t* u, const uint16_t* a, const uint16_t* dyexp, const uint16_t* wg,
-                     const uint16_t* wu, const uint16_t* wd, uint16_t* dg, uint16_t* du, uint16_t* dxp,
-                     uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, hipStream_t s) {
+int gg_bf16_dgrad_down(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* dyexp,
+                       const uint16_t* wd, const uint16_t* g, const uint16_t* u, uint16_t* dg, uint16_t* du,
+                       hipStream_t s) {
+  // dgrad through W_down with the SwiGLU backward epilogue
   gg::Params p{};
   p.offsets = offsets; p.E = E; p.n = n; p.d = d; p.f = f;
-  // dgrad through W_down with the SwiGLU backward epilogue
   p.a0 = dyexp; p.b0 = wd; p.g = g; p.u = u; p.o0 = dg; p.o1 = du;
-  if (int st = gg::launch<gg::DGRAD1>(p, s)) return st;
-  // wgrad of W_down
+  return gg::launch<gg::DGRAD1>(p, s);
+}
+
+int gg_bf16_wgrad_down(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* dyexp,
+                       const uint16_t* a, uint16_t* dwd, hipStream_t s) {
   gg::Params w{};
   w.offsets = offsets; w.E = E; w.n = n; w.d = d; w.f = f;
   w.a0 = dyexp; w.b0 = a; w.o0 = dwd;
-  if (int st = gg::launch<gg::WGRAD_DOWN>(w, s)) return st;
-  // dgrad through W_gate and W_up
+  return gg::launch<gg::WGRAD_DOWN>(w, s);
+}
+
+int gg_bf16_dgrad_gate_up(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* dg,
+                          const uint16_t* du, const uint16_t* wg, const uint16_t* wu, uint16_t* dxp,
+                          hipStream_t s) {
   gg::Params q{};
   q.offsets = offsets; q.E = E; q.n = n; q.d = d; q.f = f;
   q.a0 = dg; q.a1 = du; q.b0 = wg; q.b1 = wu; q.o0 = dxp;
-  if (int st = gg::launch<gg::DGRAD2>(q, s)) return st;
-  // wgrad of W_gate and W_up
+  return gg::launch<gg::DGRAD2>(q, s);
+}
+
+int gg_bf16_wgrad_gate_up(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* dg,
+                          const uint16_t* du, const uint16_t* xp, uint16_t* dwg, uint16_t* dwu, hipStream_t s) {
   gg::Params r{};
   r.offsets = offsets; r.E = E; r.n = n; r.d = d; r.f = f;
   r.a0 = dg; r.a1 = du; r.b0 = xp; r.o0 = dwg; r.o1 = dwu;
   return gg::launch<gg::WGRAD_GU>(r, s);
+}
+
+int gg_bf16_backward(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* xp, const uint16_t* g,
+                     const uint16_t* u, const uint16_t* a, const uint16_t* dyexp, const uint16_t* wg,
+                     const uint16_t* wu, const uint16_t* wd, uint16_t* dg, uint16_t* du, uint16_t* dxp,
+                     uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, hipStream_t s) {
+  if (int st = gg_bf16_dgrad_down(E, n, d, f, offsets, dyexp, wd, g, u, dg, du, s)) return st;
+  if (int st = gg_bf16_wgrad_down(E, n, d, f, offsets, dyexp, a, dwd, s)) return st;
+  if (int st = gg_bf16_dgrad_gate_up(E, n, d, f, offsets, dg, du, wg, wu, dxp, s)) return st;
+  return gg_bf16_wgrad_gate_up(E, n, d, f, offsets, dg, du, xp, dwg, dwu, s);
 }
 
 }  // namespace moe

@@ -620,6 +620,46 @@ struct MxBwdLayout {
 
 size_t gg_mx_backward_ws(int E, int n, int d, int f) { return MxBwdLayout(E, n, d, f).total; }
 
+int gg_mx_dgrad_down(int E, int n, int d, int f, const int32_t* offsets, const uint8_t* dyq, const uint8_t* dys,
+                     const uint8_t* wdtq, const uint8_t* wdts, const uint16_t* g, const uint16_t* u, uint16_t* dg,
+                     uint16_t* du, hipStream_t s) {
+  gmx::Params p{};
+  p.offsets = offsets; p.E = E; p.n = n; p.d = d; p.f = f;
+  p.a0 = dyq; p.a0s = dys; p.b0 = wdtq; p.b0s = wdts; p.g = g; p.u = u; p.o0 = dg; p.o1 = du;
+  return gmx::launch<gmx::DGRAD1>(p, s);
+}
+
+int gg_mx_wgrad_down(int E, int n, int d, int f, const int32_t* offsets, const int32_t* offsets_pad,
+                     const uint8_t* dyT, const uint8_t* dyTs, const uint8_t* aT, const uint8_t* aTs, uint16_t* dwd,
+                     hipStream_t s) {
+  gmx::Params w{};
+  w.offsets = offsets; w.offsets_pad = offsets_pad; w.E = E; w.n = n; w.d = d; w.f = f;
+  w.P = moe_mx_pad_cap(n, E);
+  w.a0 = dyT; w.a0s = dyTs; w.b0 = aT; w.b0s = aTs; w.o0 = dwd;
+  return gmx::launch<gmx::WGRAD_DOWN>(w, s);
+}
+
+int gg_mx_dgrad_gate_up(int E, int n, int d, int f, const int32_t* offsets, const uint8_t* dgq, const uint8_t* dgs,
+                        const uint8_t* duq, const uint8_t* dus, const uint8_t* wgtq, const uint8_t* wgts,
+                        const uint8_t* wutq, const uint8_t* wuts, uint16_t* dxp, hipStream_t s) {
+  gmx::Params q{};
+  q.offsets = offsets; q.E = E; q.n = n; q.d = d; q.f = f;
+  q.a0 = dgq; q.a0s = dgs; q.a1 = duq; q.a1s = dus;
+  q.b0 = wgtq; q.b0s = wgts; q.b1 = wutq; q.b1s = wuts; q.o0 = dxp;
+  return gmx::launch<gmx::DGRAD2>(q, s);
+}
+
+int gg_mx_wgrad_gate_up(int E, int n, int d, int f, const int32_t* offsets, const int32_t* offsets_pad,
+                        const uint8_t* dgT, const uint8_t* dgTs, const uint8_t* duT, const uint8_t* duTs,
+                        const uint8_t* xT, const uint8_t* xTs, uint16_t* dwg, uint16_t* dwu, hipStream_t s) {
+  gmx::Params r{};
+  r.offsets = offsets; r.offsets_pad = offsets_pad; r.E = E; r.n = n; r.d = d; r.f = f;
+  r.P = moe_mx_pad_cap(n, E);
+  r.a0 = dgT; r.a0s = dgTs; r.a1 = duT; r.a1s = duTs;
+  r.b0 = xT; r.b0s = xTs; r.o0 = dwg; r.o1 = dwu;
+  return gmx::launch<gmx::WGRAD_GU>(r, s);
+}
+
 int gg_mx_backward(int E, int n, int d, int f, const int32_t* offsets, const int32_t* offsets_pad,
                    const int32_t* row_token, const uint16_t* x, const uint16_t* g, const uint16_t* u,
                    const uint16_t* a, const uint16_t* dyexp, const uint8_t* wgtq, const uint8_t* wgts,
@@ -627,37 +667,26 @@ int gg_mx_backward(int E, int n, int d, int f, const int32_t* offsets, const int
                    uint16_t* du, uint16_t* dxp, uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, uint8_t* ws,
                    hipStream_t s) {
   const MxBwdLayout L(E, n, d, f);
-  const int P = moe_mx_pad_cap(n, E);
   // dgrad through W_down: dYexp quantised along d
   if (int st = mxfp8_quantize(dyexp, 1, n, d, 0, ws + L.dyq, ws + L.dys, s)) return st;
-  gmx::Params p{};
-  p.offsets = offsets; p.E = E; p.n = n; p.d = d; p.f = f;
-  p.a0 = ws + L.dyq; p.a0s = ws + L.dys; p.b0 = wdtq; p.b0s = wdts; p.g = g; p.u = u; p.o0 = dg; p.o1 = du;
-  if (int st = gmx::launch<gmx::DGRAD1>(p, s)) return st;
-  // wgrad operands along grouped tokens
+  if (int st = gg_mx_dgrad_down(E, n, d, f, offsets, ws + L.dyq, ws + L.dys, wdtq, wdts, g, u, dg, du, s)) return st;
+  // wgrad of W_down: operands along grouped tokens
   if (int st = mxfp8_quantize_grouped(dyexp, nullptr, offsets, offsets_pad, E, n, d, ws + L.dyT, ws + L.dyTs, s)) return st;
   if (int st = mxfp8_quantize_grouped(a, nullptr, offsets, offsets_pad, E, n, f, ws + L.aT, ws + L.aTs, s)) return st;
-  gmx::Params w{};
-  w.offsets = offsets; w.offsets_pad = offsets_pad; w.E = E; w.n = n; w.d = d; w.f = f; w.P = P;
-  w.a0 = ws + L.dyT; w.a0s = ws + L.dyTs; w.b0 = ws + L.aT; w.b0s = ws + L.aTs; w.o0 = dwd;
-  if (int st = gmx::launch<gmx::WGRAD_DOWN>(w, s)) return st;
+  if (int st = gg_mx_wgrad_down(E, n, d, f, offsets, offsets_pad, ws + L.dyT, ws + L.dyTs, ws + L.aT, ws + L.aTs, dwd, s))
+    return st;
   // dgrad through W_gate, W_up: dG, dU quantised along f
   if (int st = mxfp8_quantize(dg, 1, n, f, 0, ws + L.dgq, ws + L.dgs, s)) return st;
   if (int st = mxfp8_quantize(du, 1, n, f, 0, ws + L.duq, ws + L.dus, s)) return st;
-  gmx::Params q{};
-  q.offsets = offsets; q.E = E; q.n = n; q.d = d; q.f = f;
-  q.a0 = ws + L.dgq; q.a0s = ws + L.dgs; q.a1 = ws + L.duq; q.a1s = ws + L.dus;
-  q.b0 = wgtq; q.b0s = wgts; q.b1 = wutq; q.b1s = wuts; q.o0 = dxp;
-  if (int st = gmx::launch<gmx::DGRAD2>(q, s)) return st;
+  if (int st = gg_mx_dgrad_gate_up(E, n, d, f, offsets, ws + L.dgq, ws + L.dgs, ws + L.duq, ws + L.dus, wgtq, wgts,
+                                   wutq, wuts, dxp, s))
+    return st;
   // wgrad of W_gate, W_up
   if (int st = mxfp8_quantize_grouped(dg, nullptr, offsets, offsets_pad, E, n, f, ws + L.dgT, ws + L.dgTs, s)) return st;
   if (int st = mxfp8_quantize_grouped(du, nullptr, offsets, offsets_pad, E, n, f, ws + L.duT, ws + L.duTs, s)) return st;
   if (int st = mxfp8_quantize_grouped(x, row_token, offsets, offsets_pad, E, n, d, ws + L.xT, ws + L.xTs, s)) return st;
-  gmx::Params r{};
-  r.offsets = offsets; r.offsets_pad = offsets_pad; r.E = E; r.n = n; r.d = d; r.f = f; r.P = P;
-  r.a0 = ws + L.dgT; r.a0s = ws + L.dgTs; r.a1 = ws + L.duT; r.a1s = ws + L.duTs;
-  r.b0 = ws + L.xT; r.b0s = ws + L.xTs; r.o0 = dwg; r.o1 = dwu;
-  return gmx::launch<gmx::WGRAD_GU>(r, s);
+  return gg_mx_wgrad_gate_up(E, n, d, f, offsets, offsets_pad, ws + L.dgT, ws + L.dgTs, ws + L.duT, ws + L.duTs,
+                             ws + L.xT, ws + L.xTs, dwg, dwu, s);
 }
 
 }  // namespace moe

@@ -1,8 +1,12 @@
 """One MoE layer step (forward + backward) on one GPU's share, composed from the C entry points.
 
-Forward:  [router_project] -> route_topk -> permute -> grouped_gemm_swiglu -> unpermute_combine
-Backward: unpermute_combine_bwd -> grouped_gemm_swiglu_bwd -> route_topk_bwd
+Forward:  [router_project] -> route_topk -> permute -> grouped_gemm_gate_up -> grouped_gemm_down
+          -> unpermute_combine
+Backward: unpermute_combine_bwd -> grouped_gemm_dgrad_down -> grouped_gemm_wgrad_down
+          -> grouped_gemm_dgrad_gate_up -> grouped_gemm_wgrad_gate_up -> route_topk_bwd
           -> [router_project_bwd] -> permute_bwd (+ the router's dx term)
+The grouped products are issued one kernel per call (the same kernels, in the same order, as the
+composite grouped_gemm_swiglu / grouped_gemm_swiglu_bwd), so each can be timed on its own.
 MXFP8 adds the block quantisation of x (before the permute; row blocks commute with the row
 permutation) and of the expert weights in both contraction directions; router, combine,
 permute-backward and route-backward stay bf16/fp32.
@@ -46,64 +50,109 @@ class Weights:
         return q
 
 
-def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, gate_up_events=None):
+class _Span:
+    """Records an optional (start, end) torch.cuda.Event pair on the current stream around one
+    library call: events[name] if the caller asked for that name."""
+
+    def __init__(self, events, name):
+        self.pair = events.get(name) if events else None
+
+    def __enter__(self):
+        if self.pair is not None:
+            self.pair[0].record()
+
+    def __exit__(self, *exc):
+        if self.pair is not None:
+            self.pair[1].record()
+        return False
+
+
+# names of the calls `forward` and `backward` can bracket with events; each is one grouped GEMM
+# kernel ("down" under MXFP8 also quantises a along f first)
+GEMM_CALLS = ("gate_up", "down", "dgrad_down", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up")
+
+
+def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=None):
     """Layer forward.  x [T, d] bf16; logits [T, E] fp32 unless weights.w_r is given.
     Returns the context dict that `backward` consumes (all intermediate tensors), with y.
-    gate_up_events: optional (start, end) torch.cuda.Event pair recorded on the current stream
-    around the first grouped product (the benchmark times that kernel with them)."""
+    events: optional {name: (start, end)} of torch.cuda.Event pairs, recorded on the current
+    stream around the grouped-GEMM calls named in GEMM_CALLS."""
     ctx = dict(x=x, k=k, mxfp8=mxfp8)
     if logits is None:
         logits = ops.router_project(x, weights.w_r)
     ctx["logits"] = logits
     r = ops.route_topk(logits, k, want_probs=want_probs, pad=32 if mxfp8 else None)
     ctx.update(r)
-    ev0, ev1 = gate_up_events if gate_up_events is not None else (None, None)
     if not mxfp8:
         xp = ops.permute(x, r["dest"])
         ctx["xp"] = xp
-        if ev0 is not None:
-            ev0.record()
-        g, u, a = ops.grouped_gemm_gate_up(xp, r["offsets"], weights.w_gate, weights.w_up)
-        if ev1 is not None:
-            ev1.record()
-        yexp = ops.grouped_gemm_down(a, r["offsets"], weights.w_down)
+        with _Span(events, "gate_up"):
+            g, u, a = ops.grouped_gemm_gate_up(xp, r["offsets"], weights.w_gate, weights.w_up)
+        with _Span(events, "down"):
+            yexp = ops.grouped_gemm_down(a, r["offsets"], weights.w_down)
     else:
         q = weights.mx or weights.quantize_mx()
         xq, xs = ops.mxfp8_quantize(x, 0)
         xpq, xps = ops.permute(xq, r["dest"], x_scale=xs)
         ctx["xq"], ctx["xs"], ctx["xpq"], ctx["xps"] = xq, xs, xpq, xps
-        if ev0 is not None:
-            ev0.record()
-        g, u, a = ops.grouped_gemm_gate_up(xpq, r["offsets"], q["wg"], q["wu"], scales=(xps, q["wg_s"], q["wu_s"]))
-        if ev1 is not None:
-            ev1.record()
-        yexp = ops.grouped_gemm_down(a, r["offsets"], q["wd"], w_down_scale=q["wd_s"])
+        with _Span(events, "gate_up"):
+            g, u, a = ops.grouped_gemm_gate_up(xpq, r["offsets"], q["wg"], q["wu"],
+                                               scales=(xps, q["wg_s"], q["wu_s"]))
+        with _Span(events, "down"):
+            yexp = ops.grouped_gemm_down(a, r["offsets"], q["wd"], w_down_scale=q["wd_s"])
     ctx.update(g=g, u=u, a=a, yexp=yexp)
     ctx["y"] = ops.unpermute_combine(yexp, r["topk_gate"], r["dest"])
     return ctx
 
 
-def backward(ctx, weights, dy):
+def backward(ctx, weights, dy, events=None):
     """Layer backward from dy [T, d] bf16.  Returns dict with dx, d_logits, dw_gate, dw_up,
-    dw_down (and dw_r, dx_router when the layer owns its router) plus the intermediates."""
+    dw_down (and dw_r, dx_router when the layer owns its router) plus the intermediates.
+    events: as for `forward`."""
     out = {}
     dyexp, dgate = ops.unpermute_combine_bwd(dy, ctx["yexp"], ctx["topk_gate"], ctx["dest"])
     out.update(dyexp=dyexp, d_gate=dgate)
+    off = ctx["offsets"]
+    g, u, a = ctx["g"], ctx["u"], ctx["a"]
     if not ctx["mxfp8"]:
-        gb = ops.grouped_gemm_swiglu_bwd(ctx["xp"], ctx["g"], ctx["u"], ctx["a"], dyexp, ctx["offsets"],
-                                         weights.w_gate, weights.w_up, weights.w_down)
+        with _Span(events, "dgrad_down"):
+            dg, du = ops.grouped_gemm_dgrad_down(dyexp, off, weights.w_down, g, u)
+        with _Span(events, "wgrad_down"):
+            dw_down = ops.grouped_gemm_wgrad_down(dyexp, a, off, g.shape[0])
+        with _Span(events, "dgrad_gate_up"):
+            dxp = ops.grouped_gemm_dgrad_gate_up(dg, du, off, weights.w_gate, weights.w_up)
+        with _Span(events, "wgrad_gate_up"):
+            dw_gate, dw_up = ops.grouped_gemm_wgrad_gate_up(dg, du, ctx["xp"], off, g.shape[0])
     else:
+        # MXFP8: every operand quantised along its product's contraction dim (rows for the dgrads,
+        # grouped tokens padded to 32 for the wgrads), then one kernel per product
         q = weights.mx
-        gb = ops.grouped_gemm_swiglu_bwd(ctx["x"], ctx["g"], ctx["u"], ctx["a"], dyexp, ctx["offsets"],
-                                         q["wg_t"], q["wu_t"], q["wd_t"],
-                                         scales=(q["wg_t_s"], q["wu_t_s"], q["wd_t_s"]),
-                                         offsets_pad=ctx["offsets_pad"], row_token=ctx["row_token"])
-    out.update(gb)
+        n = g.shape[0]
+        pad = ctx["offsets_pad"]
+        dyq, dys = ops.mxfp8_quantize(dyexp, 0)
+        with _Span(events, "dgrad_down"):
+            dg, du = ops.grouped_gemm_dgrad_down(dyq, off, q["wd_t"], g, u, scales=(dys, q["wd_t_s"]))
+        dyT, dyTs = ops.mxfp8_quantize_grouped(dyexp, off, pad, n)
+        aT, aTs = ops.mxfp8_quantize_grouped(a, off, pad, n)
+        with _Span(events, "wgrad_down"):
+            dw_down = ops.grouped_gemm_wgrad_down(dyT, aT, off, n, offsets_pad=pad, scales=(dyTs, aTs))
+        dgq, dgs = ops.mxfp8_quantize(dg, 0)
+        duq, dus = ops.mxfp8_quantize(du, 0)
+        with _Span(events, "dgrad_gate_up"):
+            dxp = ops.grouped_gemm_dgrad_gate_up(dgq, duq, off, q["wg_t"], q["wu_t"],
+                                                 scales=(dgs, dus, q["wg_t_s"], q["wu_t_s"]))
+        dgT, dgTs = ops.mxfp8_quantize_grouped(dg, off, pad, n)
+        duT, duTs = ops.mxfp8_quantize_grouped(du, off, pad, n)
+        xT, xTs = ops.mxfp8_quantize_grouped(ctx["x"], off, pad, n, row_token=ctx["row_token"])
+        with _Span(events, "wgrad_gate_up"):
+            dw_gate, dw_up = ops.grouped_gemm_wgrad_gate_up(dgT, duT, xT, off, n, offsets_pad=pad,
+                                                            scales=(dgTs, duTs, xTs))
+    out.update(dg=dg, du=du, dxp=dxp, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
     E = ctx["logits"].shape[1]
     out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E)
     addend = None
     if weights.w_r is not None:
         addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])
         out["dx_router"] = addend
-    out["dx"] = ops.permute_bwd(gb["dxp"], ctx["dest"], addend=addend)
+    out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
     return out

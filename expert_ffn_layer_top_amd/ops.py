@@ -296,3 +296,93 @@ def grouped_gemm_swiglu_bwd(x_rows, g, u, a, dyexp, offsets, w_gate, w_up, w_dow
          _ptr(sc[1]), _ptr(w_down), _ptr(sc[2]), _ptr(out["dg"]), _ptr(out["du"]), _ptr(out["dxp"]),
          _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(ws), nbytes, _stream(g))
     return out
+
+
+# ------------------------------------------------- backward grouped GEMMs, one kernel per call
+
+def _bwd_dtype(scales, n_scales):
+    if scales is None:
+        return BF16, (None,) * n_scales
+    assert len(scales) == n_scales
+    return MXFP8, scales
+
+
+def grouped_gemm_dgrad_down(dyexp, offsets, w_down_t, g, u, scales=None):
+    """(dg, du) [n,f] bf16: da = dyexp W_down[e] through the SwiGLU backward of (g, u).
+    bf16: dyexp [n,d], w_down_t = W_down [E,d,f].  MXFP8: dyexp [n,d] E4M3, w_down_t [E,f,d] E4M3,
+    scales = (dyexp_scale [n,d/32], w_down_t_scale [E,f,d/32])."""
+    _check(offsets, torch.int32, "offsets", 1)
+    _check(g, torch.bfloat16, "g", 2)
+    _check(u, torch.bfloat16, "u", 2)
+    dtype, sc = _bwd_dtype(scales, 2)
+    n, f = g.shape
+    E = offsets.shape[0] - 1
+    d = dyexp.shape[1]
+    wdt = torch.bfloat16 if dtype == BF16 else torch.uint8
+    _check(dyexp, wdt, "dyexp", 2)
+    _check(w_down_t, wdt, "w_down_t", 3)
+    dg = _empty((n, f), torch.bfloat16, g)
+    du = _empty((n, f), torch.bfloat16, g)
+    call("moe_grouped_gemm_dgrad_down", dtype, E, n, d, f, _ptr(offsets), _ptr(dyexp), _ptr(sc[0]),
+         _ptr(w_down_t), _ptr(sc[1]), _ptr(g), _ptr(u), _ptr(dg), _ptr(du), _stream(g))
+    return dg, du
+
+
+def grouped_gemm_wgrad_down(dyexp_t, a_t, offsets, n, offsets_pad=None, scales=None):
+    """dw_down [E,d,f] bf16 = dyexp_e^T a_e.  bf16: dyexp_t = dyexp [n,d], a_t = a [n,f].
+    MXFP8: grouped-token quantised [d,P], [f,P] with scales = (dyexp_t_scale, a_t_scale)."""
+    _check(offsets, torch.int32, "offsets", 1)
+    dtype, sc = _bwd_dtype(scales, 2)
+    E = offsets.shape[0] - 1
+    wdt = torch.bfloat16 if dtype == BF16 else torch.uint8
+    _check(dyexp_t, wdt, "dyexp_t", 2)
+    _check(a_t, wdt, "a_t", 2)
+    if dtype == BF16:
+        d, f = dyexp_t.shape[1], a_t.shape[1]
+    else:
+        d, f = dyexp_t.shape[0], a_t.shape[0]
+    dw = _empty((E, d, f), torch.bfloat16, dyexp_t)
+    call("moe_grouped_gemm_wgrad_down", dtype, E, n, d, f, _ptr(offsets), _ptr(offsets_pad), _ptr(dyexp_t),
+         _ptr(sc[0]), _ptr(a_t), _ptr(sc[1]), _ptr(dw), _stream(dyexp_t))
+    return dw
+
+
+def grouped_gemm_dgrad_gate_up(dg, du, offsets, w_gate_t, w_up_t, scales=None):
+    """dxp [n,d] bf16 = dg W_gate[e] + du W_up[e].  bf16: dg, du [n,f], w_*_t = forward weights
+    [E,f,d].  MXFP8: dg, du [n,f] E4M3, w_*_t [E,d,f] E4M3, scales = (dg_scale, du_scale,
+    w_gate_t_scale, w_up_t_scale)."""
+    _check(offsets, torch.int32, "offsets", 1)
+    dtype, sc = _bwd_dtype(scales, 4)
+    wdt = torch.bfloat16 if dtype == BF16 else torch.uint8
+    for t, name in ((dg, "dg"), (du, "du")):
+        _check(t, wdt, name, 2)
+    for t, name in ((w_gate_t, "w_gate_t"), (w_up_t, "w_up_t")):
+        _check(t, wdt, name, 3)
+    n, f = dg.shape
+    E = offsets.shape[0] - 1
+    d = w_gate_t.shape[2] if dtype == BF16 else w_gate_t.shape[1]
+    dxp = _empty((n, d), torch.bfloat16, dg)
+    call("moe_grouped_gemm_dgrad_gate_up", dtype, E, n, d, f, _ptr(offsets), _ptr(dg), _ptr(sc[0]), _ptr(du),
+         _ptr(sc[1]), _ptr(w_gate_t), _ptr(sc[2]), _ptr(w_up_t), _ptr(sc[3]), _ptr(dxp), _stream(dg))
+    return dxp
+
+
+def grouped_gemm_wgrad_gate_up(dg_t, du_t, xp_t, offsets, n, offsets_pad=None, scales=None):
+    """(dw_gate, dw_up) [E,f,d] bf16 = dg_e^T xp_e, du_e^T xp_e.  bf16: the row tensors dg, du
+    [n,f], xp [n,d].  MXFP8: grouped-token quantised [f,P], [f,P], [d,P] with scales =
+    (dg_t_scale, du_t_scale, xp_t_scale)."""
+    _check(offsets, torch.int32, "offsets", 1)
+    dtype, sc = _bwd_dtype(scales, 3)
+    E = offsets.shape[0] - 1
+    wdt = torch.bfloat16 if dtype == BF16 else torch.uint8
+    for t, name in ((dg_t, "dg_t"), (du_t, "du_t"), (xp_t, "xp_t")):
+        _check(t, wdt, name, 2)
+    if dtype == BF16:
+        f, d = dg_t.shape[1], xp_t.shape[1]
+    else:
+        f, d = dg_t.shape[0], xp_t.shape[0]
+    dwg = _empty((E, f, d), torch.bfloat16, dg_t)
+    dwu = _empty((E, f, d), torch.bfloat16, dg_t)
+    call("moe_grouped_gemm_wgrad_gate_up", dtype, E, n, d, f, _ptr(offsets), _ptr(offsets_pad), _ptr(dg_t),
+         _ptr(sc[0]), _ptr(du_t), _ptr(sc[1]), _ptr(xp_t), _ptr(sc[2]), _ptr(dwg), _ptr(dwu), _stream(dg_t))
+    return dwg, dwu

@@ -232,6 +232,45 @@ int moe_grouped_gemm_swiglu_bwd(int dtype, int E, int n, int d, int f, const int
                                 uint16_t* dxp, uint16_t* dw_gate, uint16_t* dw_up,
                                 uint16_t* dw_down, void* ws, size_t ws_bytes, void* stream);
 
+/* The four products of moe_grouped_gemm_swiglu_bwd as separate calls, one grouped GEMM kernel
+ * each, on operands the caller has already put in the form the kernel reads (same results as the
+ * composite, which is built from them; none needs a workspace).
+ *
+ * dgrad_down:    dg, du [n,f] from dyexp and the SwiGLU backward of (g, u) as above.
+ *   bf16: dyexp [n,d], w_down_t = the forward W_down [E,d,f]; scales NULL.
+ *   MXFP8: dyexp [n,d] E4M3 + dyexp_scale [n,d/32] (row blocks along d); w_down_t [E,f,d] E4M3 +
+ *   scale [E,f,d/32] (mxfp8_quantize axis 1 of W_down).
+ * wgrad_down:    dw_down [E,d,f] = dyexp_e^T a_e.
+ * dgrad_gate_up: dxp [n,d] = dg W_gate[e] + du W_up[e].
+ *   bf16: dg, du [n,f]; w_gate_t, w_up_t = the forward weights [E,f,d]; scales NULL.
+ *   MXFP8: dg, du [n,f] E4M3 + scales [n,f/32]; w_gate_t, w_up_t [E,d,f] E4M3 + [E,d,f/32].
+ * wgrad_gate_up: dw_gate, dw_up [E,f,d] = dg_e^T xp_e, du_e^T xp_e.
+ *   The wgrad operands ("*_t") are token-major:
+ *   bf16: the row tensors themselves (dyexp [n,d], a [n,f], dg, du [n,f], xp [n,d]);
+ *     offsets_pad and all scales NULL.
+ *   MXFP8: mxfp8_quantize_grouped outputs, [C, P] E4M3 + [C, P/32] with P = moe_mx_pad_cap(n, E)
+ *     and offsets_pad the route's 32-padded offsets.
+ * Weight gradients of experts with no rows are written as zeros. */
+int moe_grouped_gemm_dgrad_down(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                                const void* dyexp, const uint8_t* dyexp_scale, const void* w_down_t,
+                                const uint8_t* w_down_t_scale, const uint16_t* g,
+                                const uint16_t* u, uint16_t* dg, uint16_t* du, void* stream);
+int moe_grouped_gemm_wgrad_down(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                                const int32_t* offsets_pad_or_null, const void* dyexp_t,
+                                const uint8_t* dyexp_t_scale, const void* a_t,
+                                const uint8_t* a_t_scale, uint16_t* dw_down, void* stream);
+int moe_grouped_gemm_dgrad_gate_up(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                                   const void* dg, const uint8_t* dg_scale, const void* du,
+                                   const uint8_t* du_scale, const void* w_gate_t,
+                                   const uint8_t* w_gate_t_scale, const void* w_up_t,
+                                   const uint8_t* w_up_t_scale, uint16_t* dxp, void* stream);
+int moe_grouped_gemm_wgrad_gate_up(int dtype, int E, int n, int d, int f, const int32_t* offsets,
+                                   const int32_t* offsets_pad_or_null, const void* dg_t,
+                                   const uint8_t* dg_t_scale, const void* du_t,
+                                   const uint8_t* du_t_scale, const void* xp_t,
+                                   const uint8_t* xp_t_scale, uint16_t* dw_gate, uint16_t* dw_up,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

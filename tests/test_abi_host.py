@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) >= 21
+    assert len(names) >= 25
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for n in sorted(names):
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -51,7 +51,7 @@ def test_version_and_status_strings():
 
 def test_workspace_sizes_from_host_scalars():
     L = _lib.lib
-    assert L.moe_route_workspace_bytes(8192, 64, 4) == 32 * 64 * 4
+    assert L.moe_route_workspace_bytes(8192, 64, 4) == (8192 // 64) * 64 * 4     # one histogram per 64 tokens
     assert L.moe_route_workspace_bytes(1, 1, 1) == 4
     assert L.moe_gg_workspace_bytes(0, 64, 32768, 2048, 1024) == 0          # bf16 needs none
     mx = L.moe_gg_workspace_bytes(1, 64, 131072, 7168, 2048)
@@ -87,6 +87,20 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_grouped_gemm_swiglu(1, 8, 256, 192, 256, *args, 0, None) == UNSUPPORTED
     assert L.moe_grouped_gemm_swiglu(1, 8, 256, 256, 256, *args, 0, None) == WORKSPACE
     assert L.moe_grouped_gemm_swiglu(0, 8, 256, 128, 256, fake, fake, fake, *[fake] * 11, 0, None) == INVALID
+    # per-kernel backward GEMMs: bf16 takes no scales nor offsets_pad; MXFP8 needs them; null outputs
+    assert L.moe_grouped_gemm_dgrad_down(0, 8, 256, 128, 256, fake, fake, fake, fake, None, fake, fake, fake,
+                                         fake, None) == INVALID
+    assert L.moe_grouped_gemm_dgrad_down(1, 8, 256, 128, 256, fake, fake, None, fake, fake, fake, fake, fake,
+                                         fake, None) == INVALID
+    assert L.moe_grouped_gemm_wgrad_down(0, 8, 256, 128, 256, fake, fake, fake, None, fake, None, fake,
+                                         None) == INVALID
+    assert L.moe_grouped_gemm_wgrad_down(1, 8, 256, 128, 256, fake, None, fake, fake, fake, fake, fake,
+                                         None) == INVALID
+    assert L.moe_grouped_gemm_dgrad_gate_up(0, 8, 256, 128, 256, fake, fake, None, fake, None, fake, None,
+                                            fake, None, None, None) == INVALID
+    assert L.moe_grouped_gemm_wgrad_gate_up(1, 8, 256, 192, 256, fake, fake, *[fake] * 8, None) == UNSUPPORTED
+    assert L.moe_grouped_gemm_wgrad_gate_up(0, 8, 256, 128, 256, fake, None, fake, None, fake, None, fake, None,
+                                            fake, None, None) == INVALID
     # router backward: dw_r requested without workspace
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, fake, None, 0, None) == WORKSPACE
     msg = L.moe_last_error_string().decode()

@@ -171,3 +171,58 @@ def test_grouped_gemm_mxfp8_forward_backward(case):
     for e in np.nonzero(p["counts"] == 0)[0]:
         for key in ("dw_gate", "dw_up", "dw_down"):
             assert np.all(bits(out[key])[e] == 0)
+
+
+# ------------------------------------------------ one kernel per call = the composite
+
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
+def test_backward_per_kernel_calls_match_composite(mx):
+    """The four backward products called one by one (on operands quantised by the standalone
+    quantisers, for MXFP8) give the composite's bytes exactly."""
+    from expert_ffn_layer_top_amd import ops
+    p = problem(T=600, d=512, E=5, k=2, f=384, seed=21, empty=(3,))
+    n = p["n"]
+    note(f"gg per-kernel backward, mx={mx}")
+    off_d = i32_to_dev(p["off"])
+    dy_d = bf16_to_dev(p["dyexp"])
+    Wd = {w: bf16_to_dev(p[w]) for w in ("wg", "wu", "wd")}
+    if not mx:
+        xp_d = bf16_to_dev(p["xp"])
+        g, u, a, _ = ops.grouped_gemm_swiglu(xp_d, off_d, Wd["wg"], Wd["wu"], Wd["wd"])
+        ref = ops.grouped_gemm_swiglu_bwd(xp_d, g, u, a, dy_d, off_d, Wd["wg"], Wd["wu"], Wd["wd"])
+        dg, du = ops.grouped_gemm_dgrad_down(dy_d, off_d, Wd["wd"], g, u)
+        dwd = ops.grouped_gemm_wgrad_down(dy_d, a, off_d, n)
+        dxp = ops.grouped_gemm_dgrad_gate_up(dg, du, off_d, Wd["wg"], Wd["wu"])
+        dwg, dwu = ops.grouped_gemm_wgrad_gate_up(dg, du, xp_d, off_d, n)
+    else:
+        x_d = bf16_to_dev(p["x"])
+        xq, xs = ops.mxfp8_quantize(x_d, 0)
+        xpq, xps = ops.permute(xq, i32_to_dev(p["dest"]), x_scale=xs)
+        Q = {}
+        for w in ("wg", "wu", "wd"):
+            Q[w] = ops.mxfp8_quantize(Wd[w], 0)
+            Q[w + "_t"] = ops.mxfp8_quantize(Wd[w], 1)
+        g, u, a, _ = ops.grouped_gemm_swiglu(xpq, off_d, Q["wg"][0], Q["wu"][0], Q["wd"][0],
+                                             scales=(xps, Q["wg"][1], Q["wu"][1], Q["wd"][1]))
+        offp_d = i32_to_dev(p["offp"])
+        rt_d = i32_to_dev(p["row_token"])
+        ref = ops.grouped_gemm_swiglu_bwd(x_d, g, u, a, dy_d, off_d, Q["wg_t"][0], Q["wu_t"][0], Q["wd_t"][0],
+                                          scales=(Q["wg_t"][1], Q["wu_t"][1], Q["wd_t"][1]),
+                                          offsets_pad=offp_d, row_token=rt_d)
+        dyq, dys = ops.mxfp8_quantize(dy_d, 0)
+        dg, du = ops.grouped_gemm_dgrad_down(dyq, off_d, Q["wd_t"][0], g, u, scales=(dys, Q["wd_t"][1]))
+        dyT, dyTs = ops.mxfp8_quantize_grouped(dy_d, off_d, offp_d, n)
+        aT, aTs = ops.mxfp8_quantize_grouped(a, off_d, offp_d, n)
+        dwd = ops.grouped_gemm_wgrad_down(dyT, aT, off_d, n, offsets_pad=offp_d, scales=(dyTs, aTs))
+        dgq, dgs = ops.mxfp8_quantize(dg, 0)
+        duq, dus = ops.mxfp8_quantize(du, 0)
+        dxp = ops.grouped_gemm_dgrad_gate_up(dgq, duq, off_d, Q["wg_t"][0], Q["wu_t"][0],
+                                             scales=(dgs, dus, Q["wg_t"][1], Q["wu_t"][1]))
+        dgT, dgTs = ops.mxfp8_quantize_grouped(dg, off_d, offp_d, n)
+        duT, duTs = ops.mxfp8_quantize_grouped(du, off_d, offp_d, n)
+        xT, xTs = ops.mxfp8_quantize_grouped(x_d, off_d, offp_d, n, row_token=rt_d)
+        dwg, dwu = ops.grouped_gemm_wgrad_gate_up(dgT, duT, xT, off_d, n, offsets_pad=offp_d,
+                                                  scales=(dgTs, duTs, xTs))
+    got = dict(dg=dg, du=du, dxp=dxp, dw_gate=dwg, dw_up=dwu, dw_down=dwd)
+    for key, t in got.items():
+        assert np.array_equal(bits(t), bits(ref[key])), f"{key}: per-kernel call differs from the composite"
