@@ -29,6 +29,15 @@ int check_launch(const char* what);
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int cu_count();
+
+// Workgroups of a persistent grouped-GEMM launch: the tile upper bound rounded up to a multiple
+// of 8 (one per XCD slot), at most one per compute unit.  The environment variable
+// MOE_GG_WORKGROUPS lowers the cap (a multiple of 8, at least 8): tests use it to run many
+// tiles per workgroup at small shapes.
+int gemm_workgroups(long long tiles_upper);
+
 // Shared shape rules of the ABI.
 int check_layer_shape(int T, int E, int k);
 

@@ -5,8 +5,9 @@
 // the GPU": the many small per-expert products run as one grouped operation; [card]
 // "Supercharging Olmo-core ...", "Summary": the grouped GEMMs are device-scheduled.  Here the
 // per-expert row counts exist only on the device: every workgroup reads `offsets`, builds the
-// per-expert tile prefix in LDS and maps its own id to (expert, m-tile, n-tile).  The host
-// launches an upper bound of tiles computed from T*k alone; surplus workgroups exit at once.
+// per-expert tile prefix and walks its own list of (expert, m-tile, n-tile) tiles.  The host
+// launches at most one workgroup per compute unit (persistent); the tile list follows from the
+// device-side counts alone.
 //
 // Products (rows r of expert e are offsets[e] .. offsets[e+1]-1):
 //   FWD1   [G | U] = Xp W_gate^T | Xp W_up^T, epilogue G, U, A = silu(G) * U        (K = d)
@@ -18,15 +19,16 @@
 //
 // Tiling: 256 x 256 outputs per 256-thread workgroup, four waves in a 2 x 2 grid, each wave
 // owning 128 x 128 outputs as 8 x 8 MFMA 16x16 tiles (256 fp32 accumulators per lane, AGPRs).  K
-// steps of 32 run through a five-deep ring of LDS stages (5 x 32 KiB = the whole 160 KiB LDS).
+// steps of 64 (two 32-deep MFMA sub-steps) run through two LDS rings of 32 KiB stages: two
+// stages for the M-side operand and three for the N-side one (the whole 160 KiB LDS).
 //
 // Operand staging.  Every operand tile goes from HBM/L2 to LDS by the LDS-DMA form of the
 // buffer load (16 bytes per lane, written to a wave-contiguous 1 KiB LDS span), so no operand
 // passes through VGPRs and no wave spends VALU time on copies.  Two LDS layouts:
-//   KC  operand stored K-contiguous (rows x K): LDS [256 rows][32 k] (64 B rows); MFMA fragments
-//       are one ds_read_b128 per lane.
+//   KC  operand stored K-contiguous (rows x K): LDS [256 rows][64 k] (128 B rows: each row one
+//       whole 128-byte line of the source); MFMA fragments are one ds_read_b128 per lane.
 //   KS  operand stored K-strided (K x columns: the weights in the dgrad products, the
-//       token-major activations in the wgrad products): LDS [32 k][256 columns] (512 B rows),
+//       token-major activations in the wgrad products): LDS [64 k][256 columns] (512 B rows),
 //       kept in the source layout; fragments come from two ds_read_b64_tr_b16 per lane, which
 //       transpose 4 x 4 blocks of 16-bit elements across each group of 16 lanes.
 // Both layouts XOR-swizzle 16-byte chunks within a row (the DMA source address of each lane is
@@ -34,12 +36,14 @@
 // every operand to its valid extent: rows past an expert's last row (wgrad K tails) and past
 // the tensor end read as zeros, and so do K steps past the last one.
 //
-// Pipeline.  Three K steps are in flight.  In the middle of step kt (after its fourth MFMA row)
-// every wave waits for its own DMA of tile kt+1 and joins a barrier; past it, all of tile kt+1
-// is in LDS and every wave has finished reading tile kt-1, so the DMA of tile kt+4 goes into
-// that stage.  Fragment reads run one MFMA row ahead of their use.  They are inline asm with
-// explicit lgkmcnt waits: the stage is a runtime index (the loop is unrolled by two, not by the
-// ring length), and the compiler, which cannot tell which stage a read touches, would otherwise
+// Pipeline.  Each wave streams one operand (waves 0, 1 the N side, waves 2, 3 the M side, half a
+// stage each).  In the middle of step g (after its fourth MFMA row) every wave waits for its own
+// DMA of step g+1 and joins a barrier; past it all of step g+1 is in LDS, every wave has finished
+// reading the M-side stage of step g and the N-side stage of step g-1, so the DMA of step g+2
+// goes into those stages.  Steps run on across a workgroup's tiles: the DMA of the next tile's
+// first steps overlaps the current tile's last steps and its epilogue.  Fragment reads run one
+// MFMA row ahead of their use.  They are inline asm with explicit lgkmcnt waits: the stage is a
+// runtime index, and the compiler, which cannot tell which stage a read touches, would otherwise
 // wait for every outstanding DMA before each read.  The MFMA computes the transposed tile
 // (weights / N side as the first operand), so each lane ends with 4 consecutive output columns
 // of one row.
@@ -179,9 +183,15 @@ __device__ __forceinline__ int k_total(const Params& p) {
 // loads complete in order, so one deep ring shared with a shallow one would wait at the
 // shallow one's pace.
 struct OpLoad {
-  __amdgpu_buffer_rsrc_t r0, r1;   // r1: second tensor (FWD1 B half 1: W_up; DGRAD2 K >= f)
-  int vo[16];
+  int vo[16];                      // per-lane byte offsets of the 16 DMA instructions (tile-independent)
   int step;                        // bytes to advance per K step (KC: 128; KS: 64 rows)
+};
+
+// One tile's DMA sources for this wave: its operand bounded to the tile's valid extent.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t r0, r1;   // r1: second tensor (FWD1 B half 1: W_up; DGRAD2 K >= f)
+  int nreal;                       // K steps holding data
+  int nk;                          // K steps run: at least 2 (see the kernel's pipeline notes)
 };
 
 // KC operand: LDS rows 128h .. 128h + 127 of a [256 rows][64 k] stage, 8 rows per instruction;
@@ -206,21 +216,21 @@ __device__ __forceinline__ void ks_offsets(int h, int ldb, int (&vo)[16]) {
   }
 }
 
-// Issues this wave's DMA of K step kt into stage `st` of its operand's ring.  Steps past the
-// last one (kt >= nk) read through an empty descriptor, so the stage fills with zeros and its
-// MFMAs add nothing.
+// Issues this wave's DMA of K step k of the tile `src` into stage `st` of its operand's ring.
+// Steps past the tile's data (k >= nreal) read through an empty descriptor, so the stage fills
+// with zeros and its MFMAs add nothing.
 template <int MODE>
-__device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& ld, bool role_b, int h, int kt, int nk,
-                                            int st) {
-  __amdgpu_buffer_rsrc_t r = ld.r0;
-  int soff = kt * ld.step;
+__device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& ld, const TileSrc& src, bool role_b, int h,
+                                            int k, int st) {
+  __amdgpu_buffer_rsrc_t r = src.r0;
+  int soff = k * ld.step;
   if constexpr (MODE == FWD1) {
-    if (role_b && h) r = ld.r1;
+    if (role_b && h) r = src.r1;
   } else if constexpr (MODE == DGRAD2) {
     const int kf = p.f / BK;   // K steps per half
-    if (kt >= kf) { r = ld.r1; soff = (kt - kf) * ld.step; }
+    if (k >= kf) { r = src.r1; soff = (k - kf) * ld.step; }
   }
-  if (kt >= nk) { r = make_rsrc(p.a0, 0); soff = 0; }
+  if (k >= src.nreal) { r = make_rsrc(p.a0, 0); soff = 0; }
   uint8_t* dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * (OP_BYTES / 2);
 #pragma unroll
   for (int i = 0; i < 16; ++i) dma16(r, dst + i * 1024, ld.vo[i], soff);
@@ -308,6 +318,15 @@ __device__ __forceinline__ void pin_acc_row(f32x4 (&r)[8]) {
                "+a"(r[7]));
 }
 
+// Keeps column J of the accumulators (acc[0..7][J]) in AGPRs up to this point: the epilogue pins
+// each column just before it reads it, so the compiler copies the accumulators out one column
+// at a time rather than all 256 at once.
+template <int J>
+__device__ __forceinline__ void pin_acc_col(f32x4 (&acc)[8][8]) {
+  asm volatile("" : "+a"(acc[0][J]), "+a"(acc[1][J]), "+a"(acc[2][J]), "+a"(acc[3][J]), "+a"(acc[4][J]),
+               "+a"(acc[5][J]), "+a"(acc[6][J]), "+a"(acc[7][J]));
+}
+
 // Fragment index (units of 16 rows/columns) of B fragment i for wave column wn (FWD1 pairs gate
 // rows with up rows).
 template <int MODE, int I>
@@ -325,14 +344,15 @@ __device__ __forceinline__ int bfrag_base(int wn) {
 // the 8 A fragments.  Fragment reads run one row ahead of their use, from small register sets:
 //   a[8]      A fragments of this sub-step (read during the previous one), an[8] the next's;
 //   b[2]      ping-pong: B fragment i+1 is read while row i runs.
-// Sub-step 0 prefetches sub-step 1 from the same stages.  Sub-step 1 opens tile kt+1 before its
-// row 4: each wave waits for its own DMA of that tile and joins a barrier; past it every wave
-// has finished reading A of tile kt (consumed by the end of sub-step 0) and B of tile kt-1, so
-// the DMA of tile kt+2 goes into those stages.  Rows 4..7 then read tile kt+1's first A
-// fragments, and row 7 its first B fragment.
+// Sub-step 0 prefetches sub-step 1 from the same stages.  Sub-step 1 opens K step g+1 (g = this
+// step in the workgroup's stream of steps over its tiles) before its row 4: each wave waits for
+// its own DMA of that step and joins a barrier; past it every wave has finished reading A of step
+// g (consumed by the end of sub-step 0) and B of step g-1, so the DMA of step g+2 (step `ik` of
+// tile `isrc`) goes into those stages.  Rows 4..7 then read step g+1's first A fragments, and
+// row 7 its first B fragment.
 template <int MODE, int S>
 __device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool role_b, int h, const FragAddr& fa,
-                                         int kt, int nk, int sa, int sb, bf16x8 (&a)[8], bf16x8 (&an)[8],
+                                         const TileSrc& isrc, int ik, int sa, int sb, bf16x8 (&a)[8], bf16x8 (&an)[8],
                                          bf16x8 (&b)[2], f32x4 (&acc)[8][8]) {
   constexpr bool AKC = Traits<MODE>::A_KC, BKC = Traits<MODE>::B_KC;
   constexpr int RA = AKC ? 1 : 2;   // LDS reads per A fragment
@@ -348,7 +368,7 @@ __device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool
   static_for<0, 8>([&](auto i) {
     if constexpr (S == 1 && i == 4) {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      issue_stage<MODE>(p, ld, role_b, h, kt + 2, nk, role_b ? sbp : sa);
+      issue_stage<MODE>(p, ld, isrc, role_b, h, ik, role_b ? sbp : sa);
     }
     if constexpr (i < 7) read_frag<BKC, S, bfrag_c<MODE, i + 1>()>(b[(i + 1) & 1], b_cur, fa, qb);
     else if constexpr (S == 0) read_frag<BKC, 1, bfrag_c<MODE, 0>()>(b[0], b_cur, fa, qb);
@@ -444,25 +464,110 @@ __device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int&
   }
 }
 
+// Writes the tile's results from the accumulators.  Lane holds, for MFMA tile (i, j), output row
+// 16j + lane%16 of the wave's rows and 4 consecutive columns 4*(lane/16) .. +3 of the wave's
+// 16-column group i.
 template <int MODE>
-__global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+__device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (&acc)[8][8], int wm, int wn,
+                                         int lane) {
+  const int rl = lane & 15;
+  const int cq = 4 * (lane >> 4);
+  if constexpr (MODE == FWD1) {
+    static_for<0, 8>([&](auto j) {
+      pin_acc_col<j>(acc);
+      const int row = t.m0 + 128 * wm + 16 * j + rl;
+      if (row < t.m_end) {
+        static_for<0, 4>([&](auto i) {
+          const int col = t.n0 + 64 * wn + 16 * i + cq;
+          if (col >= p.f) return;
+          const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
+          float av[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
+          const long long o = static_cast<long long>(row) * p.f + col;
+          st4(p.o0 + o, gv[0], gv[1], gv[2], gv[3]);
+          st4(p.o1 + o, uv[0], uv[1], uv[2], uv[3]);
+          st4(p.o2 + o, av[0], av[1], av[2], av[3]);
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one row at a time: bounds the epilogue's registers
+    });
+  } else if constexpr (MODE == DGRAD1) {
+    // g and u of one row of MFMA tiles (8 loads each) are loaded a row ahead of their use, so 16
+    // loads are in flight while the previous row is computed and stored.  Rows past the expert
+    // and columns past f load from a valid address (the tile's first row / column 0) and are not
+    // stored.
+    uint2 gw[2][8], uw[2][8];
+    auto load_row = [&](auto j) {
+      const int row = t.m0 + 128 * wm + 16 * j + rl;
+      const int rowc = row < t.m_end ? row : t.m0;
+      static_for<0, 8>([&](auto i) {
+        const int col = t.n0 + 128 * wn + 16 * i + cq;
+        const long long o = static_cast<long long>(rowc) * p.f + (col < p.f ? col : 0);
+        gw[j & 1][i] = *reinterpret_cast<const uint2*>(p.g + o);
+        uw[j & 1][i] = *reinterpret_cast<const uint2*>(p.u + o);
+      });
+    };
+    load_row(std::integral_constant<int, 0>{});
+    static_for<0, 8>([&](auto j) {
+      if constexpr (j < 7) load_row(std::integral_constant<int, j + 1>{});
+      pin_acc_col<j>(acc);
+      const int row = t.m0 + 128 * wm + 16 * j + rl;
+      static_for<0, 8>([&](auto i) {
+        const int col = t.n0 + 128 * wn + 16 * i + cq;
+        // The empty asm consumes the loaded values on every path (the compiler would otherwise sink
+        // the only uses into the store's branch and treat the loads as still pending on the other
+        // path, then wait for memory inside the next tile's K loop before reusing the registers).
+        const uint2 g2 = gw[j & 1][i], u2 = uw[j & 1][i];
+        asm volatile("" ::"v"(g2), "v"(u2));
+        const float gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
+        const float uv[4] = {bf16_lo(u2.x), bf16_hi(u2.x), bf16_lo(u2.y), bf16_hi(u2.y)};
+        const f32x4 dav = acc[i][j];
+        float dg[4], du[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sg = sigmoidf_(gv[q]);
+          dg[q] = dav[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+          du[q] = dav[q] * gv[q] * sg;
+        }
+        if (row < t.m_end && col < p.f) {
+          const long long o = static_cast<long long>(row) * p.f + col;
+          st4(p.o0 + o, dg[0], dg[1], dg[2], dg[3]);
+          st4(p.o1 + o, du[0], du[1], du[2], du[3]);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else {
+    // plain stores: FWD2 -> yexp [n][d]; DGRAD2 -> dxp [n][d]; WGRAD -> dW[e] [Mtot][Ntot]
+    const int Ntot = n_total<MODE>(p);
+    uint16_t* out = p.o0;
+    if constexpr (Traits<MODE>::WGRAD) {
+      const int Mtot = m_total_wgrad<MODE>(p);
+      out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
+    }
+    static_for<0, 8>([&](auto j) {
+      pin_acc_col<j>(acc);
+      const int row = t.m0 + 128 * wm + 16 * j + rl;
+      if (row < t.m_end) {
+        static_for<0, 8>([&](auto i) {
+          const int col = t.n0 + 128 * wn + 16 * i + cq;
+          if (col >= Ntot) return;
+          const f32x4 v = acc[i][j];
+          st4(out + static_cast<long long>(row) * Ntot + col, v[0], v[1], v[2], v[3]);
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+}
 
-  // ---- device-side schedule: count tiles, remap the block id XCD-major, find the tile
-  const int NTW = n_tile_width<MODE>();
-  const int ntiles_n = (n_total<MODE>(p) + NTW - 1) / NTW;
-  const int bid = blockIdx.x;
+// The tile with linear id `lid` (< the launch's tile count).  Linear ids run n-tile fastest, then
+// m-tile, then (weight gradients) expert.
+template <int MODE>
+__device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int ntiles_n, int lid) {
   Tile t;
   if constexpr (!Traits<MODE>::WGRAD) {
-    const MTiles mts = mtile_scan(p.offsets, p.E);
-    const int total_tiles = mts.total * ntiles_n;
-    const int tot8 = (total_tiles + 7) & ~7;
-    if (bid >= tot8) return;
-    const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
-    if (lid >= total_tiles) return;
     const int mt_glob = lid / ntiles_n;
     const int nt = lid - mt_glob * ntiles_n;
     int e, first;
@@ -470,24 +575,14 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     t.e = e;
     t.m0 = p.offsets[e] + (mt_glob - first) * BM;
     t.m_end = p.offsets[e + 1];
-    t.n0 = nt * NTW;
+    t.n0 = nt * n_tile_width<MODE>();
     t.half = 0;
     t.k_begin = 0;
     t.k_len = k_total<MODE>(p);
   } else {
     const int Mtot = m_total_wgrad<MODE>(p);
     const int mt = (Mtot + BM - 1) / BM;
-    const int mtt = mt * (MODE == WGRAD_GU ? 2 : 1);
-    const int total_tiles = p.E * mtt * ntiles_n;
-    const int tot8 = (total_tiles + 7) & ~7;
-    if (bid >= tot8) return;
-    // Weight-gradient tiles cost in proportion to their expert's rows.  With balanced experts,
-    // keep each XCD on a contiguous run of tiles (experts' operand rows shared in its L2); when
-    // one expert holds more than twice the mean, deal tiles round-robin over the XCDs instead
-    // (block ids go to XCDs round-robin), so a hot expert's tiles run on every XCD at once.
-    const int lid = wgrad_skewed(p.offsets, p.E, p.n) ? bid : (bid & 7) * (tot8 >> 3) + (bid >> 3);
-    if (lid >= total_tiles) return;
-    const int per_e = mtt * ntiles_n;
+    const int per_e = mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
     t.e = lid / per_e;
     const int rem = lid - t.e * per_e;
     const int mi = rem / ntiles_n;
@@ -509,176 +604,239 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   t.half = __builtin_amdgcn_readfirstlane(t.half);
   t.k_begin = __builtin_amdgcn_readfirstlane(t.k_begin);
   t.k_len = __builtin_amdgcn_readfirstlane(t.k_len);
-  const int nk = (t.k_len + BK - 1) / BK;
+  return t;
+}
 
-  // ---- this wave's DMA operand, bounded to its valid extent (role: waves 0, 1 -> B; 2, 3 -> A)
-  const bool role_b = wave < 2;
-  const int h = wave & 1;
-  OpLoad ld;
+// A source that supplies only zeros (the step after a workgroup's last tile).
+__device__ __forceinline__ TileSrc empty_src(const Params& p) {
+  TileSrc s;
+  s.r0 = make_rsrc(p.a0, 0);
+  s.r1 = s.r0;
+  s.nreal = 0;
+  s.nk = 2;
+  return s;
+}
+
+// This wave's DMA operand for tile t, bounded to its valid extent (role: waves 0, 1 -> B;
+// 2, 3 -> A; h = which half of the stage the wave fills).
+template <int MODE>
+__device__ __forceinline__ TileSrc tile_src(const Params& p, const Tile& t, bool role_b, int h) {
+  TileSrc s;
+  s.nreal = (t.k_len + BK - 1) / BK;
+  s.nk = s.nreal < 2 ? 2 : s.nreal;
   if (!role_b) {
     if constexpr (MODE == FWD1 || MODE == FWD2 || MODE == DGRAD1) {
       const int K = k_total<MODE>(p);
       const long long rem_rows = static_cast<long long>(p.n) - t.m0;
-      ld.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K * 2);
-      ld.r1 = ld.r0;
-      ld.step = BK * 2;
-      kc_offsets(128 * h, K * 2, ld.vo);
+      s.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K * 2);
+      s.r1 = s.r0;
     } else if constexpr (MODE == DGRAD2) {
       const long long rem_rows = static_cast<long long>(p.n) - t.m0;
-      ld.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
-      ld.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
-      ld.step = BK * 2;
-      kc_offsets(128 * h, p.f * 2, ld.vo);
+      s.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
+      s.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * p.f, rem_rows * p.f * 2);
     } else {
       // WGRAD: M side is a token-major activation [n][Mtot], rows k_begin .. k_begin + k_len
       const int Mtot = m_total_wgrad<MODE>(p);
       const uint16_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
-      ld.r0 = make_rsrc(base + static_cast<long long>(t.k_begin) * Mtot + t.m0,
-                        static_cast<long long>(t.k_len) * Mtot * 2 - t.m0 * 2);
-      ld.r1 = ld.r0;
-      ld.step = BK * Mtot * 2;
-      ks_offsets(h, Mtot * 2, ld.vo);
+      s.r0 = make_rsrc(base + static_cast<long long>(t.k_begin) * Mtot + t.m0,
+                       static_cast<long long>(t.k_len) * Mtot * 2 - t.m0 * 2);
+      s.r1 = s.r0;
     }
   } else {
     if constexpr (MODE == FWD1) {
       // B half 0: W_gate[e] rows n0 .. n0 + 127; half 1: W_up[e] rows n0 .. n0 + 127
       const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
       const long long bytes = static_cast<long long>(p.f - t.n0) * p.d * 2;
-      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
-      ld.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
-      ld.step = BK * 2;
-      kc_offsets(0, p.d * 2, ld.vo);
+      s.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
+      s.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, bytes);
     } else if constexpr (MODE == FWD2) {
       // W_down[e] [d][f], rows n0 .. (K = f contiguous)
       const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
-      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.f,
-                        static_cast<long long>(p.d - t.n0) * p.f * 2);
-      ld.r1 = ld.r0;
-      ld.step = BK * 2;
-      kc_offsets(128 * h, p.f * 2, ld.vo);
+      s.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.f,
+                       static_cast<long long>(p.d - t.n0) * p.f * 2);
+      s.r1 = s.r0;
     } else if constexpr (MODE == DGRAD1) {
       // W_down[e] [d][f]: element (k = d index, n = f index), rows k, columns n0 ..
       const long long eoff = static_cast<long long>(t.e) * p.d * p.f;
-      ld.r0 = make_rsrc(p.b0 + eoff + t.n0, static_cast<long long>(p.d) * p.f * 2 - t.n0 * 2);
-      ld.r1 = ld.r0;
-      ld.step = BK * p.f * 2;
-      ks_offsets(h, p.f * 2, ld.vo);
+      s.r0 = make_rsrc(p.b0 + eoff + t.n0, static_cast<long long>(p.d) * p.f * 2 - t.n0 * 2);
+      s.r1 = s.r0;
     } else if constexpr (MODE == DGRAD2) {
       // W_gate[e] / W_up[e] [f][d]: element (k = f index, n = d index)
       const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
       const long long bytes = static_cast<long long>(p.f) * p.d * 2 - t.n0 * 2;
-      ld.r0 = make_rsrc(p.b0 + eoff + t.n0, bytes);
-      ld.r1 = make_rsrc(p.b1 + eoff + t.n0, bytes);
-      ld.step = BK * p.d * 2;
-      ks_offsets(h, p.d * 2, ld.vo);
+      s.r0 = make_rsrc(p.b0 + eoff + t.n0, bytes);
+      s.r1 = make_rsrc(p.b1 + eoff + t.n0, bytes);
     } else {
       // WGRAD: N side is a token-major activation [n][Ntot]
       const int Ntot = n_total<MODE>(p);
-      ld.r0 = make_rsrc(p.b0 + static_cast<long long>(t.k_begin) * Ntot + t.n0,
-                        static_cast<long long>(t.k_len) * Ntot * 2 - t.n0 * 2);
-      ld.r1 = ld.r0;
+      s.r0 = make_rsrc(p.b0 + static_cast<long long>(t.k_begin) * Ntot + t.n0,
+                       static_cast<long long>(t.k_len) * Ntot * 2 - t.n0 * 2);
+      s.r1 = s.r0;
+    }
+  }
+  return s;
+}
+
+// This wave's per-lane DMA offsets and K-step stride; they depend on the launch, not the tile.
+template <int MODE>
+__device__ __forceinline__ OpLoad op_load(const Params& p, bool role_b, int h) {
+  OpLoad ld;
+  if (!role_b) {
+    if constexpr (MODE == FWD1 || MODE == FWD2 || MODE == DGRAD1) {
+      ld.step = BK * 2;
+      kc_offsets(128 * h, k_total<MODE>(p) * 2, ld.vo);
+    } else if constexpr (MODE == DGRAD2) {
+      ld.step = BK * 2;
+      kc_offsets(128 * h, p.f * 2, ld.vo);
+    } else {
+      const int Mtot = m_total_wgrad<MODE>(p);
+      ld.step = BK * Mtot * 2;
+      ks_offsets(h, Mtot * 2, ld.vo);
+    }
+  } else {
+    if constexpr (MODE == FWD1) {
+      ld.step = BK * 2;
+      kc_offsets(0, p.d * 2, ld.vo);
+    } else if constexpr (MODE == FWD2) {
+      ld.step = BK * 2;
+      kc_offsets(128 * h, p.f * 2, ld.vo);
+    } else if constexpr (MODE == DGRAD1) {
+      ld.step = BK * p.f * 2;
+      ks_offsets(h, p.f * 2, ld.vo);
+    } else if constexpr (MODE == DGRAD2) {
+      ld.step = BK * p.d * 2;
+      ks_offsets(h, p.d * 2, ld.vo);
+    } else {
+      const int Ntot = n_total<MODE>(p);
       ld.step = BK * Ntot * 2;
       ks_offsets(h, Ntot * 2, ld.vo);
     }
   }
+  return ld;
+}
 
-  f32x4 acc[8][8];
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // initialisation -> first MFMA: pin the zeroed registers ahead of the wait states
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
+  asm volatile("s_nop 7" ::: "memory");
+}
 
-  if (nk > 0) {
-    // accumulator initialisation -> first MFMA: pin the zeroed registers ahead of the wait states
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
-    asm volatile("s_nop 7" ::: "memory");
-    // ---- prologue: tiles 0 and 1 in flight, then tile 0 everywhere
-    issue_stage<MODE>(p, ld, role_b, h, 0, nk, 0);
-    issue_stage<MODE>(p, ld, role_b, h, 1, nk, 1);
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-    const FragAddr fa = frag_addr();
-    const uint32_t a0 = lds_addr(lds_ring) + A_RING, b0 = lds_addr(lds_ring) + B_RING;
-    const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
-    bf16x8 fa0[8], fa1[8], fb[2];
-    static_for<0, 8>([&](auto j) { read_frag<Traits<MODE>::A_KC, 0, j>(fa0[j], a0, fa, qa); });
-    read_frag<Traits<MODE>::B_KC, 0, bfrag_c<MODE, 0>()>(fb[0], b0, fa, qb);
-    int sa = 0, sb = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      sub_step<MODE, 0>(p, ld, role_b, h, fa, kt, nk, sa, sb, fa0, fa1, fb, acc);
-      sub_step<MODE, 1>(p, ld, role_b, h, fa, kt, nk, sa, sb, fa1, fa0, fb, acc);
-      sa = sa + 1 == NA ? 0 : sa + 1;
-      sb = sb + 1 == NB ? 0 : sb + 1;
-    }
-    // no LDS-DMA may still be writing when the workgroup ends; the last MFMA results settle
-    // before the epilogue's VALU reads them
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
-  }
+// Persistent: the host launches at most one workgroup per compute unit, and each workgroup runs
+// a list of tiles.  Schedule: every workgroup counts the tiles from `offsets` once.  Balanced
+// launches give XCD x (block ids b with b % 8 == x) the contiguous run of tiles
+// [x * per, (x + 1) * per), per = ceil(tiles / 8), which its workgroups take in strides of the
+// number of workgroups on the XCD, so the tiles that run at once on one XCD share operand rows in
+// its L2.  Weight gradients whose largest expert holds more than twice the mean rows deal tiles
+// round-robin over all workgroups instead, so the hot expert's (long) tiles spread over the chip.
+// The K steps of a workgroup's tiles form one stream through the LDS rings: the DMA of the next
+// tile's first two steps is issued during the current tile's last two, so it lands while the
+// current tile's epilogue runs.  Each tile runs at least two K steps (zero-filled past its data),
+// so the step two ahead always belongs to the current or the next tile.
+template <int MODE>
+__global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- epilogue: lane holds, for MFMA tile (i, j), output row 16j + lane%16 of the wave's
-  // rows and 4 consecutive columns 4*(lane/16) .. +3 of the wave's 16-column group i.
-  const int rl = lane & 15;
-  const int cq = 4 * (lane >> 4);
-  if constexpr (MODE == FWD1) {
-    static_for<0, 8>([&](auto j) {
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row >= t.m_end) return;
-      static_for<0, 4>([&](auto i) {
-        const int col = t.n0 + 64 * wn + 16 * i + cq;
-        if (col >= p.f) return;
-        const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
-        float av[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
-        const long long o = static_cast<long long>(row) * p.f + col;
-        st4(p.o0 + o, gv[0], gv[1], gv[2], gv[3]);
-        st4(p.o1 + o, uv[0], uv[1], uv[2], uv[3]);
-        st4(p.o2 + o, av[0], av[1], av[2], av[3]);
-      });
-    });
-  } else if constexpr (MODE == DGRAD1) {
-    static_for<0, 8>([&](auto j) {
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row >= t.m_end) return;
-      static_for<0, 8>([&](auto i) {
-        const int col = t.n0 + 128 * wn + 16 * i + cq;
-        if (col >= p.f) return;
-        const long long o = static_cast<long long>(row) * p.f + col;
-        const uint2 gw = *reinterpret_cast<const uint2*>(p.g + o);
-        const uint2 uw = *reinterpret_cast<const uint2*>(p.u + o);
-        const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
-        const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
-        const f32x4 dav = acc[i][j];
-        float dg[4], du[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sg = sigmoidf_(gv[q]);
-          dg[q] = dav[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-          du[q] = dav[q] * gv[q] * sg;
-        }
-        st4(p.o0 + o, dg[0], dg[1], dg[2], dg[3]);
-        st4(p.o1 + o, du[0], du[1], du[2], du[3]);
-      });
-    });
+  // ---- device-side schedule
+  const int NTW = n_tile_width<MODE>();
+  const int ntiles_n = (n_total<MODE>(p) + NTW - 1) / NTW;
+  MTiles mts{};
+  int total;
+  bool deal = false;
+  if constexpr (!Traits<MODE>::WGRAD) {
+    mts = mtile_scan(p.offsets, p.E);
+    total = mts.total * ntiles_n;
   } else {
-    // plain stores: FWD2 -> yexp [n][d]; DGRAD2 -> dxp [n][d]; WGRAD -> dW[e] [Mtot][Ntot]
-    const int Ntot = n_total<MODE>(p);
-    uint16_t* out = p.o0;
-    if constexpr (Traits<MODE>::WGRAD) {
-      const int Mtot = m_total_wgrad<MODE>(p);
-      out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
-    }
-    static_for<0, 8>([&](auto j) {
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row >= t.m_end) return;
-      static_for<0, 8>([&](auto i) {
-        const int col = t.n0 + 128 * wn + 16 * i + cq;
-        if (col >= Ntot) return;
-        const f32x4 v = acc[i][j];
-        st4(out + static_cast<long long>(row) * Ntot + col, v[0], v[1], v[2], v[3]);
-      });
-    });
+    const int mt = (m_total_wgrad<MODE>(p) + BM - 1) / BM;
+    total = p.E * mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
+    deal = wgrad_skewed(p.offsets, p.E, p.n);
   }
+  const int G = gridDim.x;     // a multiple of 8
+  const int bid = blockIdx.x;
+  int lid, lstep, lend;
+  if (deal) {
+    lid = bid;
+    lstep = G;
+    lend = total;
+  } else {
+    const int per = (total + 7) >> 3;
+    const int x = bid & 7;
+    lid = x * per + (bid >> 3);
+    lstep = G >> 3;
+    lend = (x + 1) * per < total ? (x + 1) * per : total;
+  }
+  lid = __builtin_amdgcn_readfirstlane(lid);
+  lstep = __builtin_amdgcn_readfirstlane(lstep);
+  lend = __builtin_amdgcn_readfirstlane(lend);
+  if (lid >= lend) return;
+
+  const bool role_b = wave < 2;
+  const int h = wave & 1;
+  const OpLoad ld = op_load<MODE>(p, role_b, h);
+  Tile t = tile_at<MODE>(p, mts, ntiles_n, lid);
+  TileSrc cur = tile_src<MODE>(p, t, role_b, h);
+  int lid_n = lid + lstep;
+  Tile tn = t;
+  TileSrc nxt = empty_src(p);
+  if (lid_n < lend) {
+    tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
+    nxt = tile_src<MODE>(p, tn, role_b, h);
+  }
+
+  f32x4 acc[8][8];
+  zero_acc(acc);
+  // ---- prologue: steps 0 and 1 in flight, then step 0 everywhere
+  issue_stage<MODE>(p, ld, cur, role_b, h, 0, 0);
+  issue_stage<MODE>(p, ld, cur, role_b, h, 1, 1);
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  const FragAddr fa = frag_addr();
+  const uint32_t a0 = lds_addr(lds_ring) + A_RING, b0 = lds_addr(lds_ring) + B_RING;
+  const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
+  bf16x8 fa0[8], fa1[8], fb[2];
+  static_for<0, 8>([&](auto j) { read_frag<Traits<MODE>::A_KC, 0, j>(fa0[j], a0, fa, qa); });
+  read_frag<Traits<MODE>::B_KC, 0, bfrag_c<MODE, 0>()>(fb[0], b0, fa, qb);
+  int sa = 0, sb = 0, kt = 0;
+  for (;;) {
+    sub_step<MODE, 0>(p, ld, role_b, h, fa, cur, 0, sa, sb, fa0, fa1, fb, acc);
+    {
+      const bool here = kt + 2 < cur.nk;
+      TileSrc is;
+      is.r0 = here ? cur.r0 : nxt.r0;
+      is.r1 = here ? cur.r1 : nxt.r1;
+      is.nreal = here ? cur.nreal : nxt.nreal;
+      is.nk = 0;
+      sub_step<MODE, 1>(p, ld, role_b, h, fa, is, here ? kt + 2 : kt + 2 - cur.nk, sa, sb, fa1, fa0, fb, acc);
+    }
+    sa = sa + 1 == NA ? 0 : sa + 1;
+    sb = sb + 1 == NB ? 0 : sb + 1;
+    if (++kt < cur.nk) continue;
+    // ---- tile done.  The next tile's first fragments (fa0, fb[0]) are complete before the
+    // epilogue, and the last MFMA results settle before its VALU reads them.
+    lgkm_wait<0>(fb[0], fa0);
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+    epilogue<MODE>(p, t, acc, wm, wn, lane);
+    if (lid_n >= lend) break;
+    zero_acc(acc);
+    t = tn;
+    cur = nxt;
+    kt = 0;
+    lid_n += lstep;
+    if (lid_n < lend) {
+      tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
+      nxt = tile_src<MODE>(p, tn, role_b, h);
+    } else {
+      nxt = empty_src(p);
+    }
+  }
+  // no LDS-DMA may still be writing when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
 // Upper bound of tiles for a launch, from host scalars only.
@@ -695,8 +853,9 @@ inline long long grid_upper(int mode, int E, int n, int d, int f) {
 
 template <int MODE>
 int launch(const Params& p, hipStream_t s) {
-  const long long g = (grid_upper(MODE, p.E, p.n, p.d, p.f) + 7) / 8 * 8;
-  MOE_REQUIRE(g < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many tiles");
+  const long long upper = grid_upper(MODE, p.E, p.n, p.d, p.f);
+  MOE_REQUIRE(upper < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many tiles");
+  const int g = gemm_workgroups(upper);
   // every buffer offset the kernel forms stays below 2^31 bytes
   MOE_REQUIRE(static_cast<long long>(p.n) * (p.d > p.f ? p.d : p.f) * 2 < 0x7fffffffLL &&
                   static_cast<long long>(p.d) * p.f * 2 < 0x7fffffffLL,

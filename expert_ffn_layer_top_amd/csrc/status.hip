@@ -1,6 +1,7 @@
 // Status codes, per-thread last-error text and the shared shape rules of the C ABI.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 
 #include "common.h"
 
@@ -20,6 +21,29 @@ int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return MOE_OK;
+}
+
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int gemm_workgroups(long long tiles_upper) {
+  long long g = (tiles_upper + 7) / 8 * 8;
+  long long cap = cu_count() / 8 * 8;
+  if (const char* env = getenv("MOE_GG_WORKGROUPS")) {
+    const long long v = atoll(env) / 8 * 8;
+    if (v >= 8 && v < cap) cap = v;
+  }
+  if (cap < 8) cap = 8;
+  return static_cast<int>(g < cap ? g : cap);
 }
 
 int check_layer_shape(int T, int E, int k) {

@@ -226,3 +226,33 @@ def test_backward_per_kernel_calls_match_composite(mx):
     got = dict(dg=dg, du=du, dxp=dxp, dw_gate=dwg, dw_up=dwu, dw_down=dwd)
     for key, t in got.items():
         assert np.array_equal(bits(t), bits(ref[key])), f"{key}: per-kernel call differs from the composite"
+
+
+# ------------------------------------------------ persistent launch: many tiles per workgroup
+
+@pytest.mark.parametrize("case", [BF16_CASES[0], BF16_CASES[2], BF16_CASES[4]], ids=case_id)
+def test_bf16_few_workgroups_bit_identical(case, monkeypatch):
+    """With 8 workgroups each runs many tiles in a row (the next tile's first K steps stream in
+    during the previous tile's epilogue); every output must match the default launch bit for bit,
+    and the default launch matches the oracle (test above)."""
+    from expert_ffn_layer_top_amd import ops
+    p = problem(**case)
+    n = p["n"]
+    off_d = i32_to_dev(p["off"])
+    xp_d = bf16_to_dev(p["xp"])
+    dy_d = bf16_to_dev(p["dyexp"])
+    W = [bf16_to_dev(p[w]) for w in ("wg", "wu", "wd")]
+
+    def run():
+        g, u, a, y = ops.grouped_gemm_swiglu(xp_d, off_d, *W)
+        b = ops.grouped_gemm_swiglu_bwd(xp_d, g, u, a, dy_d, off_d, *W)
+        return [bits(t) for t in (g, u, a, y, b["dg"], b["du"], b["dxp"], b["dw_gate"], b["dw_up"], b["dw_down"])]
+
+    note(f"gg bf16 default launch {case}")
+    ref = run()
+    monkeypatch.setenv("MOE_GG_WORKGROUPS", "8")
+    note(f"gg bf16 8 workgroups {case}")
+    got = run()
+    names = ("g", "u", "a", "yexp", "dg", "du", "dxp", "dw_gate", "dw_up", "dw_down")
+    for nm, r, o in zip(names, ref, got):
+        assert np.array_equal(r, o), f"{nm}: 8-workgroup launch differs from the default launch"
