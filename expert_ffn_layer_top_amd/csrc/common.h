@@ -55,9 +55,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two fp32 -> packed pair of bf16 (low half = a).
+// Two fp32 -> packed pair of bf16 (low half = a), round-to-nearest-even, in one instruction
+// (v_cvt_pk_bf16_f32).  Finite values and infinities convert exactly as f32_to_bf16 does; a NaN
+// stays a NaN (its payload may differ).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
