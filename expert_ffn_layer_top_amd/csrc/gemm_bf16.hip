@@ -37,12 +37,12 @@
 // the tensor end read as zeros, and so do K steps past the last one.
 //
 // Pipeline.  Each wave streams one operand (waves 0, 1 the N side, waves 2, 3 the M side, half a
-// stage each).  In the middle of step g (after its fourth MFMA row) every wave waits for its own
+// stage each).  Half-way through step g (before its second sub-step) every wave waits for its own
 // DMA of step g+1 and joins a barrier; past it all of step g+1 is in LDS, every wave has finished
 // reading the M-side stage of step g and the N-side stage of step g-1, so the DMA of step g+2
 // goes into those stages.  Steps run on across a workgroup's tiles: the DMA of the next tile's
-// first steps overlaps the current tile's last steps and its epilogue.  Fragment reads run one
-// MFMA row ahead of their use.  They are inline asm with explicit lgkmcnt waits: the stage is a
+// first steps overlaps the current tile's last steps and its epilogue.  B fragment reads run two
+// MFMA rows ahead of their use, A fragments a sub-step ahead.  They are inline asm with explicit lgkmcnt waits: the stage is a
 // runtime index, and the compiler, which cannot tell which stage a read touches, would otherwise
 // wait for every outstanding DMA before each read.  The MFMA computes the transposed tile
 // (weights / N side as the first operand), so each lane ends with 4 consecutive output columns
@@ -71,6 +71,7 @@ constexpr int NA = 2;
 constexpr int NB = 3;
 constexpr int A_RING = 0;
 constexpr int B_RING = NA * OP_BYTES;
+constexpr int DMA_ROWS = 8;                       // MFMA rows a stage's DMA issue is spread over
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;      // raw buffer, 32-bit data format (gfx9 family)
 
 __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[(NA + NB) * OP_BYTES];
@@ -216,24 +217,43 @@ __device__ __forceinline__ void ks_offsets(int h, int ldb, int (&vo)[16]) {
   }
 }
 
-// Issues this wave's DMA of K step k of the tile `src` into stage `st` of its operand's ring.
-// Steps past the tile's data (k >= nreal) read through an empty descriptor, so the stage fills
-// with zeros and its MFMAs add nothing.
+// Where this wave's DMA of K step k of the tile `src` reads and writes (stage `st` of its
+// operand's ring).  Steps past the tile's data (k >= nreal) read through an empty descriptor,
+// so the stage fills with zeros and its MFMAs add nothing.
+struct StageIssue {
+  __amdgpu_buffer_rsrc_t r;
+  int soff;
+  uint8_t* dst;
+};
+
+template <int MODE>
+__device__ __forceinline__ StageIssue stage_issue(const Params& p, const OpLoad& ld, const TileSrc& src, bool role_b,
+                                                  int h, int k, int st) {
+  StageIssue si;
+  si.r = src.r0;
+  si.soff = k * ld.step;
+  if constexpr (MODE == FWD1) {
+    if (role_b && h) si.r = src.r1;
+  } else if constexpr (MODE == DGRAD2) {
+    const int kf = p.f / BK;   // K steps per half
+    if (k >= kf) { si.r = src.r1; si.soff = (k - kf) * ld.step; }
+  }
+  if (k >= src.nreal) { si.r = make_rsrc(p.a0, 0); si.soff = 0; }
+  si.dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * (OP_BYTES / 2);
+  return si;
+}
+
+// DMA instructions FIRST .. FIRST + COUNT - 1 (of 16, 1 KiB each) of a stage.
+template <int FIRST, int COUNT>
+__device__ __forceinline__ void issue_part(const OpLoad& ld, const StageIssue& si) {
+#pragma unroll
+  for (int i = FIRST; i < FIRST + COUNT; ++i) dma16(si.r, si.dst + i * 1024, ld.vo[i], si.soff);
+}
+
 template <int MODE>
 __device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& ld, const TileSrc& src, bool role_b, int h,
                                             int k, int st) {
-  __amdgpu_buffer_rsrc_t r = src.r0;
-  int soff = k * ld.step;
-  if constexpr (MODE == FWD1) {
-    if (role_b && h) r = src.r1;
-  } else if constexpr (MODE == DGRAD2) {
-    const int kf = p.f / BK;   // K steps per half
-    if (k >= kf) { r = src.r1; soff = (k - kf) * ld.step; }
-  }
-  if (k >= src.nreal) { r = make_rsrc(p.a0, 0); soff = 0; }
-  uint8_t* dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * (OP_BYTES / 2);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dma16(r, dst + i * 1024, ld.vo[i], soff);
+  issue_part<0, 16>(ld, stage_issue<MODE>(p, ld, src, role_b, h, k, st));
 }
 
 // ---------------------------------------------------------------- fragments
@@ -340,20 +360,40 @@ __device__ __forceinline__ int bfrag_base(int wn) {
   return MODE == FWD1 ? 4 * wn : 8 * wn;
 }
 
-// One 32-deep sub-step S of K tile kt, as 8 rows of 8 MFMAs; row i multiplies B fragment i by
-// the 8 A fragments.  Fragment reads run one row ahead of their use, from small register sets:
-//   a[8]      A fragments of this sub-step (read during the previous one), an[8] the next's;
-//   b[2]      ping-pong: B fragment i+1 is read while row i runs.
-// Sub-step 0 prefetches sub-step 1 from the same stages.  Sub-step 1 opens K step g+1 (g = this
-// step in the workgroup's stream of steps over its tiles) before its row 4: each wave waits for
-// its own DMA of that step and joins a barrier; past it every wave has finished reading A of step
-// g (consumed by the end of sub-step 0) and B of step g-1, so the DMA of step g+2 (step `ik` of
-// tile `isrc`) goes into those stages.  Rows 4..7 then read step g+1's first A fragments, and
-// row 7 its first B fragment.
+// LDS reads a row of MFMAs may still leave outstanding when it waits for its B fragment (see
+// sub_step), capped at the counter's 4-bit range (a lower count only waits for more).
+template <int I, int RA, int RB>
+__device__ __forceinline__ constexpr int row_wait() {
+  constexpr int n = 2 * RB + RA * (I == 0 || I == 5 ? 2 : I == 1 || I == 4 ? 4 : I == 2 || I == 3 ? 6 : 0);
+  return n < 15 ? n : 15;
+}
+
+// Waits until at most N LDS reads are outstanding and ties every fragment register, so no MFMA
+// can be scheduled above the wait (used before the epilogue with N = 0).
+template <int N>
+__device__ __forceinline__ void lgkm_wait_all(bf16x8 (&b)[4], bf16x8 (&a)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%12)"
+               : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]),
+                 "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+               : "n"(N));
+}
+
+// One 32-deep sub-step S of a K step, as 8 rows of 8 MFMAs; row i multiplies B fragment i by the
+// 8 A fragments.  Registers: a[8] the A fragments of this sub-step, an[8] the next sub-step's
+// (read two per row in rows 0..3), b[4] the B fragments, read two rows ahead of their use (row i
+// reads row i + 2's; rows 6 and 7 read the next sub-step's rows 0 and 1).  Each row waits only
+// for its own B fragment (row_wait counts the reads issued after it).
+// Sub-step 0 reads the A fragments of sub-step 1 from the same stages.  Sub-step 1 opens K step
+// g+1 (g = this step in the workgroup's stream of steps over its tiles) before its row 0: each
+// wave waits for its own DMA of that step and joins a barrier; past it all of step g+1 is in
+// LDS and every wave has finished reading the M-side stage of step g (its A fragments are all in
+// registers) and the N-side stage of step g-1, so the DMA of step g+2 (step `ik` of tile `isrc`)
+// goes into those stages.  Rows 0..3 then read step g+1's first A fragments, and rows 6, 7 its
+// first two B fragments.
 template <int MODE, int S>
 __device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool role_b, int h, const FragAddr& fa,
                                          const TileSrc& isrc, int ik, int sa, int sb, bf16x8 (&a)[8], bf16x8 (&an)[8],
-                                         bf16x8 (&b)[2], f32x4 (&acc)[8][8]) {
+                                         bf16x8 (&b)[4], f32x4 (&acc)[8][8]) {
   constexpr bool AKC = Traits<MODE>::A_KC, BKC = Traits<MODE>::B_KC;
   constexpr int RA = AKC ? 1 : 2;   // LDS reads per A fragment
   constexpr int RB = BKC ? 1 : 2;
@@ -365,22 +405,28 @@ __device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool
   const uint32_t ring = lds_addr(lds_ring);
   const uint32_t a_cur = ring + A_RING + sa * OP_BYTES, a_nxt = ring + A_RING + san * OP_BYTES;
   const uint32_t b_cur = ring + B_RING + sb * OP_BYTES, b_nxt = ring + B_RING + sbn * OP_BYTES;
+  StageIssue si{};
   static_for<0, 8>([&](auto i) {
-    if constexpr (S == 1 && i == 4) {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      issue_stage<MODE>(p, ld, isrc, role_b, h, ik, role_b ? sbp : sa);
+    if constexpr (S == 1) {
+      if constexpr (i == 0) {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        si = stage_issue<MODE>(p, ld, isrc, role_b, h, ik, role_b ? sbp : sa);
+      }
+      // the stage's 16 DMA instructions, spread over the rows so the wave keeps issuing MFMAs
+      // while the texture addresser works through them
+      if constexpr (i < DMA_ROWS) issue_part<i * (16 / DMA_ROWS), 16 / DMA_ROWS>(ld, si);
     }
-    if constexpr (i < 7) read_frag<BKC, S, bfrag_c<MODE, i + 1>()>(b[(i + 1) & 1], b_cur, fa, qb);
-    else if constexpr (S == 0) read_frag<BKC, 1, bfrag_c<MODE, 0>()>(b[0], b_cur, fa, qb);
-    else read_frag<BKC, 0, bfrag_c<MODE, 0>()>(b[0], b_nxt, fa, qb);
-    if constexpr (i >= 4) {
+    if constexpr (i < 6) read_frag<BKC, S, bfrag_c<MODE, i + 2>()>(b[(i + 2) & 3], b_cur, fa, qb);
+    else if constexpr (S == 0) read_frag<BKC, 1, bfrag_c<MODE, i - 6>()>(b[(i + 2) & 3], b_cur, fa, qb);
+    else read_frag<BKC, 0, bfrag_c<MODE, i - 6>()>(b[(i + 2) & 3], b_nxt, fa, qb);
+    if constexpr (i < 4) {
       constexpr int SN = S ^ 1;
       const uint32_t src = S == 0 ? a_cur : a_nxt;
-      read_frag<AKC, SN, 2 * (i - 4)>(an[2 * (i - 4)], src, fa, qa);
-      read_frag<AKC, SN, 2 * (i - 4) + 1>(an[2 * (i - 4) + 1], src, fa, qa);
+      read_frag<AKC, SN, 2 * i>(an[2 * i], src, fa, qa);
+      read_frag<AKC, SN, 2 * i + 1>(an[2 * i + 1], src, fa, qa);
     }
-    lgkm_wait<RB + (i >= 4 ? 2 * RA : 0)>(b[i & 1], a);
-    static_for<0, 8>([&](auto j) { mfma_acc(acc[i][j], b[i & 1], a[j]); });
+    lgkm_wait<row_wait<i, RA, RB>()>(b[i & 3], a);
+    static_for<0, 8>([&](auto j) { mfma_acc(acc[i][j], b[i & 3], a[j]); });
   });
 }
 
@@ -799,9 +845,10 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   const FragAddr fa = frag_addr();
   const uint32_t a0 = lds_addr(lds_ring) + A_RING, b0 = lds_addr(lds_ring) + B_RING;
   const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
-  bf16x8 fa0[8], fa1[8], fb[2];
+  bf16x8 fa0[8], fa1[8], fb[4];
   static_for<0, 8>([&](auto j) { read_frag<Traits<MODE>::A_KC, 0, j>(fa0[j], a0, fa, qa); });
   read_frag<Traits<MODE>::B_KC, 0, bfrag_c<MODE, 0>()>(fb[0], b0, fa, qb);
+  read_frag<Traits<MODE>::B_KC, 0, bfrag_c<MODE, 1>()>(fb[1], b0, fa, qb);
   int sa = 0, sb = 0, kt = 0;
   for (;;) {
     sub_step<MODE, 0>(p, ld, role_b, h, fa, cur, 0, sa, sb, fa0, fa1, fb, acc);
@@ -817,9 +864,9 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     sa = sa + 1 == NA ? 0 : sa + 1;
     sb = sb + 1 == NB ? 0 : sb + 1;
     if (++kt < cur.nk) continue;
-    // ---- tile done.  The next tile's first fragments (fa0, fb[0]) are complete before the
-    // epilogue, and the last MFMA results settle before its VALU reads them.
-    lgkm_wait<0>(fb[0], fa0);
+    // ---- tile done.  The next tile's first fragments (fa0, fb[0], fb[1]) are complete before
+    // the epilogue, and the last MFMA results settle before its VALU reads them.
+    lgkm_wait_all<0>(fb, fa0);
     asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
     epilogue<MODE>(p, t, acc, wm, wn, lane);
     if (lid_n >= lend) break;

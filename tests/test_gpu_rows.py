@@ -61,6 +61,12 @@ def test_combine_and_backward(T, d, E, k):
     rdy, rdg = moe.combine_bwd(dy, yexp, gate, dest)
     assert_close(codecs.bf16_to_f64(bits(dyexp)), rdy, BF16_TOL, "dyexp")
     assert_close(host(dgate), rdg, 1e-4, "d_gate")
+    # each dyexp element is one fp32 product g * dy rounded once to bf16 (nearest-even): the
+    # bits are fixed, which pins the kernels' fp32 -> bf16 rounding exactly
+    prod = gate.astype(np.float32)[:, :, None] * codecs.bf16_to_f64(dy).astype(np.float32)[:, None, :]
+    want = np.zeros((T * k, d), np.uint16)
+    want[dest.reshape(-1)] = codecs.f32_to_bf16(prod).reshape(T * k, d)
+    assert np.array_equal(bits(dyexp), want), "dyexp is not the bf16 rounding of the fp32 product"
 
 
 @pytest.mark.parametrize("T,d,E,k", SHAPES)
