@@ -432,11 +432,57 @@ __device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool
 
 // ---------------------------------------------------------------- epilogue helpers
 
-__device__ __forceinline__ void st4(uint16_t* p, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// The epilogue writes through buffer descriptors: an element a lane must not write (a row past
+// the expert's or the matrix's end, a column group past the matrix) gets a byte offset past any
+// buffer, and the hardware drops the store (a load there reads zero).  No lane-dependent
+// branches, so the compiler schedules the whole epilogue as one block.
+constexpr uint32_t OOB = 0x80000000u;
+
+// Where this lane's outputs go, relative to the wave's first output element (row0, col0) of a
+// row-major output with row pitch `ld` elements: row[j] is the byte offset of row 16j + lane%16,
+// column 4*(lane/16), or OOB past `rows_valid` rows; ni is the number of 16-column groups inside
+// the matrix (wave-uniform; `cols_valid` is a multiple of 16).
+struct WaveOut {
+  uint32_t row[8];
+  int ni;
+};
+
+__device__ __forceinline__ WaveOut wave_out(int rows_valid, int cols_valid, int ld, int lane) {
+  WaveOut w;
+  const int rl = lane & 15, cq = 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 16 * j + rl;
+    w.row[j] = r < rows_valid ? static_cast<uint32_t>((r * ld + cq) * 2) : OOB;
+  }
+  w.ni = cols_valid <= 0 ? 0 : (cols_valid >= 128 ? 8 : cols_valid / 16);
+  w.ni = __builtin_amdgcn_readfirstlane(w.ni);
+  return w;
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Byte offset of this lane's 4 elements in MFMA tile (i, j): column group i is 16 elements on.
+template <int I, int J>
+__device__ __forceinline__ uint32_t out_off(const WaveOut& w) {
+  return I < w.ni ? w.row[J] + 32u * I : OOB;
+}
+
+// Descriptor over a row-major [rows][ld] bf16 output from element (row0, col0) to its end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const uint16_t* base, long long rows, int ld, int row0,
+                                                         int col0) {
+  const long long start = static_cast<long long>(row0) * ld + col0;
+  return make_rsrc(base + start, (rows * ld - start) * 2);
+}
+
+__device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+  const u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(off), 0, 0);
+}
+
+// Logistic function with the hardware reciprocal (v_rcp_f32, about 1 ulp): far below the bf16
+// rounding the results get.  Saturates to 0 / 1 for large |x|.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // ---------------------------------------------------------------- the kernel
 
@@ -516,56 +562,53 @@ __device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int&
 template <int MODE>
 __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (&acc)[8][8], int wm, int wn,
                                          int lane) {
-  const int rl = lane & 15;
-  const int cq = 4 * (lane >> 4);
+  const int row0 = t.m0 + 128 * wm;
+  const int rows_valid = t.m_end - row0;
   if constexpr (MODE == FWD1) {
+    // G, U, A [n][f]: gate accumulators in tiles i < 4, up in i + 4 (same columns)
+    const int col0 = t.n0 + 64 * wn;
+    const WaveOut w = wave_out(rows_valid, p.f - col0, p.f, lane);
+    const auto rg = out_rsrc(p.o0, p.n, p.f, row0, col0);
+    const auto ru = out_rsrc(p.o1, p.n, p.f, row0, col0);
+    const auto ra = out_rsrc(p.o2, p.n, p.f, row0, col0);
     static_for<0, 8>([&](auto j) {
       pin_acc_col<j>(acc);
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row < t.m_end) {
-        static_for<0, 4>([&](auto i) {
-          const int col = t.n0 + 64 * wn + 16 * i + cq;
-          if (col >= p.f) return;
-          const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
-          float av[4];
+      static_for<0, 4>([&](auto i) {
+        const uint32_t off = out_off<i, j>(w);
+        const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
+        float av[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
-          const long long o = static_cast<long long>(row) * p.f + col;
-          st4(p.o0 + o, gv[0], gv[1], gv[2], gv[3]);
-          st4(p.o1 + o, uv[0], uv[1], uv[2], uv[3]);
-          st4(p.o2 + o, av[0], av[1], av[2], av[3]);
-        });
-      }
+        for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
+        st4(rg, off, gv[0], gv[1], gv[2], gv[3]);
+        st4(ru, off, uv[0], uv[1], uv[2], uv[3]);
+        st4(ra, off, av[0], av[1], av[2], av[3]);
+      });
       __builtin_amdgcn_sched_barrier(0);   // one row at a time: bounds the epilogue's registers
     });
   } else if constexpr (MODE == DGRAD1) {
-    // g and u of one row of MFMA tiles (8 loads each) are loaded a row ahead of their use, so 16
-    // loads are in flight while the previous row is computed and stored.  Rows past the expert
-    // and columns past f load from a valid address (the tile's first row / column 0) and are not
-    // stored.
-    uint2 gw[2][8], uw[2][8];
+    // dG, dU [n][f] from dA and the saved G, U (read through the same offsets; rows and columns
+    // outside the matrix read zero and are not stored).  A row of MFMA tiles is loaded a row
+    // ahead of its use.
+    const int col0 = t.n0 + 128 * wn;
+    const WaveOut w = wave_out(rows_valid, p.f - col0, p.f, lane);
+    const auto rgi = out_rsrc(p.g, p.n, p.f, row0, col0);
+    const auto rui = out_rsrc(p.u, p.n, p.f, row0, col0);
+    const auto rdg = out_rsrc(p.o0, p.n, p.f, row0, col0);
+    const auto rdu = out_rsrc(p.o1, p.n, p.f, row0, col0);
+    u32x2 gw[2][8], uw[2][8];
     auto load_row = [&](auto j) {
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      const int rowc = row < t.m_end ? row : t.m0;
       static_for<0, 8>([&](auto i) {
-        const int col = t.n0 + 128 * wn + 16 * i + cq;
-        const long long o = static_cast<long long>(rowc) * p.f + (col < p.f ? col : 0);
-        gw[j & 1][i] = *reinterpret_cast<const uint2*>(p.g + o);
-        uw[j & 1][i] = *reinterpret_cast<const uint2*>(p.u + o);
+        const int off = static_cast<int>(out_off<i, j>(w));
+        gw[j & 1][i] = __builtin_amdgcn_raw_buffer_load_b64(rgi, off, 0, 0);
+        uw[j & 1][i] = __builtin_amdgcn_raw_buffer_load_b64(rui, off, 0, 0);
       });
     };
     load_row(std::integral_constant<int, 0>{});
     static_for<0, 8>([&](auto j) {
       if constexpr (j < 7) load_row(std::integral_constant<int, j + 1>{});
       pin_acc_col<j>(acc);
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
       static_for<0, 8>([&](auto i) {
-        const int col = t.n0 + 128 * wn + 16 * i + cq;
-        // The empty asm consumes the loaded values on every path (the compiler would otherwise sink
-        // the only uses into the store's branch and treat the loads as still pending on the other
-        // path, then wait for memory inside the next tile's K loop before reusing the registers).
-        const uint2 g2 = gw[j & 1][i], u2 = uw[j & 1][i];
-        asm volatile("" ::"v"(g2), "v"(u2));
+        const u32x2 g2 = gw[j & 1][i], u2 = uw[j & 1][i];
         const float gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
         const float uv[4] = {bf16_lo(u2.x), bf16_hi(u2.x), bf16_lo(u2.y), bf16_hi(u2.y)};
         const f32x4 dav = acc[i][j];
@@ -576,33 +619,31 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
           dg[q] = dav[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
           du[q] = dav[q] * gv[q] * sg;
         }
-        if (row < t.m_end && col < p.f) {
-          const long long o = static_cast<long long>(row) * p.f + col;
-          st4(p.o0 + o, dg[0], dg[1], dg[2], dg[3]);
-          st4(p.o1 + o, du[0], du[1], du[2], du[3]);
-        }
+        const uint32_t off = out_off<i, j>(w);
+        st4(rdg, off, dg[0], dg[1], dg[2], dg[3]);
+        st4(rdu, off, du[0], du[1], du[2], du[3]);
       });
       __builtin_amdgcn_sched_barrier(0);
     });
   } else {
     // plain stores: FWD2 -> yexp [n][d]; DGRAD2 -> dxp [n][d]; WGRAD -> dW[e] [Mtot][Ntot]
     const int Ntot = n_total<MODE>(p);
-    uint16_t* out = p.o0;
+    const int col0 = t.n0 + 128 * wn;
+    const uint16_t* out = p.o0;
+    long long rows = p.n;
     if constexpr (Traits<MODE>::WGRAD) {
       const int Mtot = m_total_wgrad<MODE>(p);
       out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
+      rows = Mtot;
     }
+    const WaveOut w = wave_out(rows_valid, Ntot - col0, Ntot, lane);
+    const auto r = out_rsrc(out, rows, Ntot, row0, col0);
     static_for<0, 8>([&](auto j) {
       pin_acc_col<j>(acc);
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row < t.m_end) {
-        static_for<0, 8>([&](auto i) {
-          const int col = t.n0 + 128 * wn + 16 * i + cq;
-          if (col >= Ntot) return;
-          const f32x4 v = acc[i][j];
-          st4(out + static_cast<long long>(row) * Ntot + col, v[0], v[1], v[2], v[3]);
-        });
-      }
+      static_for<0, 8>([&](auto i) {
+        const f32x4 v = acc[i][j];
+        st4(r, out_off<i, j>(w), v[0], v[1], v[2], v[3]);
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
   }
