@@ -480,6 +480,62 @@ __device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t off, floa
   __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(off), 0, 0);
 }
 
+// ---- epilogue staging through LDS.  During a tile's epilogue the N-side stage of its last K
+// step is free (every wave has read it; the stream's next DMA into it comes a step later), so
+// each wave stages its 128 x 128 outputs there through its own 8 KiB, 32 rows per round: the
+// MFMA layout goes in as 8-byte pieces, comes out as whole 256-byte rows, and leaves in 16-byte
+// stores that cover full 128-byte lines (the MFMA layout alone gives 32-byte pieces of 16 rows
+// per store, which the memory system takes several times longer to absorb).  16-byte chunks are
+// XOR-swizzled by row so both access patterns spread over the LDS banks.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int STG_BYTES = 8192;   // per wave
+
+__device__ __forceinline__ void ds_w64(uint32_t addr, const u32x2& v) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void ds_r128(u32x4& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+}
+
+__device__ __forceinline__ void lgkm_wait_rows(u32x4 (&v)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])::"memory");
+}
+
+// Stores the wave's 128 x 128 accumulators as bf16 to a row-major output of pitch `ld` through
+// the descriptor `r` (based at the wave's first output element), staging through `stg`.  Rows at
+// or past `rows_valid` and columns at or past `cols_valid` (relative to the wave) are dropped.
+__device__ __forceinline__ void store_staged(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t r, int rows_valid,
+                                             int cols_valid, int ld, uint32_t stg, int lane) {
+  const int rl = lane & 15, g = lane >> 4;
+  static_for<0, 4>([&](auto q) {
+    pin_acc_col<2 * q>(acc);
+    pin_acc_col<2 * q + 1>(acc);
+    static_for<0, 2>([&](auto jj) {
+      const uint32_t rowb = stg + (16 * jj + rl) * 256 + ((g & 1) << 3);
+      static_for<0, 8>([&](auto i) {
+        const f32x4 v = acc[i][2 * q + jj];
+        const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        ds_w64(rowb + ((((2 * i) | (g >> 1)) ^ rl) << 4), w);
+      });
+    });
+    u32x4 rd[8];
+    static_for<0, 8>([&](auto k) {
+      const int row = 4 * k + g;   // row within the round
+      ds_r128(rd[k], stg + row * 256 + ((rl ^ (row & 15)) << 4));
+    });
+    lgkm_wait_rows(rd);
+    static_for<0, 8>([&](auto k) {
+      const int rr = 32 * q + 4 * k + g;   // row within the wave
+      const int cb = 8 * rl;               // column within the wave
+      const uint32_t off = rr < rows_valid && cb < cols_valid ? static_cast<uint32_t>((rr * ld + cb) * 2) : OOB;
+      __builtin_amdgcn_raw_buffer_store_b128(rd[k], r, static_cast<int>(off), 0, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // Logistic function with the hardware reciprocal (v_rcp_f32, about 1 ulp): far below the bf16
 // rounding the results get.  Saturates to 0 / 1 for large |x|.
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
@@ -561,7 +617,7 @@ __device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int&
 // 16-column group i.
 template <int MODE>
 __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (&acc)[8][8], int wm, int wn,
-                                         int lane) {
+                                         int lane, uint32_t stg) {
   const int row0 = t.m0 + 128 * wm;
   const int rows_valid = t.m_end - row0;
   if constexpr (MODE == FWD1) {
@@ -636,16 +692,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
       out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
       rows = Mtot;
     }
-    const WaveOut w = wave_out(rows_valid, Ntot - col0, Ntot, lane);
-    const auto r = out_rsrc(out, rows, Ntot, row0, col0);
-    static_for<0, 8>([&](auto j) {
-      pin_acc_col<j>(acc);
-      static_for<0, 8>([&](auto i) {
-        const f32x4 v = acc[i][j];
-        st4(r, out_off<i, j>(w), v[0], v[1], v[2], v[3]);
-      });
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    store_staged(acc, out_rsrc(out, rows, Ntot, row0, col0), rows_valid, Ntot - col0, Ntot, stg, lane);
   }
 }
 
@@ -909,7 +956,10 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     // the epilogue, and the last MFMA results settle before its VALU reads them.
     lgkm_wait_all<0>(fb, fa0);
     asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-    epilogue<MODE>(p, t, acc, wm, wn, lane);
+    // every wave is done with the N-side stage of the last step: it stages the epilogue
+    asm volatile("s_barrier" ::: "memory");
+    const uint32_t stg = lds_addr(lds_ring) + B_RING + (sb == 0 ? NB - 1 : sb - 1) * OP_BYTES + wave * STG_BYTES;
+    epilogue<MODE>(p, t, acc, wm, wn, lane, stg);
     if (lid_n >= lend) break;
     zero_acc(acc);
     t = tn;
