@@ -503,32 +503,38 @@ __device__ __forceinline__ void lgkm_wait_rows(u32x4 (&v)[8]) {
                : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])::"memory");
 }
 
-// Stores the wave's 128 x 128 accumulators as bf16 to a row-major output of pitch `ld` through
-// the descriptor `r` (based at the wave's first output element), staging through `stg`.  Rows at
-// or past `rows_valid` and columns at or past `cols_valid` (relative to the wave) are dropped.
-__device__ __forceinline__ void store_staged(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t r, int rows_valid,
-                                             int cols_valid, int ld, uint32_t stg, int lane) {
+// Stores a wave's 128 x 16*NI bf16 outputs to a row-major output of pitch `ld` through the
+// descriptor `r` (based at the wave's first output element), staging through `stg`.  val(i, j)
+// gives the 4 packed values this lane holds for MFMA tile (i, j) (row 16j + lane%16, columns
+// 16i + 4*(lane/16) .. +3).  Rows at or past `rows_valid` and columns at or past `cols_valid`
+// (relative to the wave) are dropped.  A round covers 256/NI rows (8 KiB); a row is 2*NI chunks.
+template <int NI, class Val>
+__device__ __forceinline__ void store_staged(Val&& val, __amdgpu_buffer_rsrc_t r, int rows_valid, int cols_valid,
+                                             int ld, uint32_t stg, int lane) {
+  constexpr int CH = 2 * NI;            // 16-byte chunks per row
+  constexpr int RB = 32 * NI;           // bytes per row
+  constexpr int JR = 16 / NI;           // MFMA row blocks per round
+  constexpr int RPI = 64 / CH;          // rows per 16-byte read instruction
   const int rl = lane & 15, g = lane >> 4;
-  static_for<0, 4>([&](auto q) {
-    pin_acc_col<2 * q>(acc);
-    pin_acc_col<2 * q + 1>(acc);
-    static_for<0, 2>([&](auto jj) {
-      const uint32_t rowb = stg + (16 * jj + rl) * 256 + ((g & 1) << 3);
-      static_for<0, 8>([&](auto i) {
-        const f32x4 v = acc[i][2 * q + jj];
-        const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        ds_w64(rowb + ((((2 * i) | (g >> 1)) ^ rl) << 4), w);
+  const int lr = lane / CH, lc = lane % CH;
+  static_for<0, 8 / JR>([&](auto q) {
+    static_for<0, JR>([&](auto jj) {
+      const int row = 16 * jj + rl;
+      const uint32_t rowb = stg + row * RB + ((g & 1) << 3);
+      static_for<0, NI>([&](auto i) {
+        const u32x2 w = val(i, std::integral_constant<int, JR * q + jj>{});
+        ds_w64(rowb + ((((2 * i) | (g >> 1)) ^ (row & (CH - 1))) << 4), w);
       });
     });
     u32x4 rd[8];
     static_for<0, 8>([&](auto k) {
-      const int row = 4 * k + g;   // row within the round
-      ds_r128(rd[k], stg + row * 256 + ((rl ^ (row & 15)) << 4));
+      const int row = RPI * k + lr;   // row within the round
+      ds_r128(rd[k], stg + row * RB + ((lc ^ (row & (CH - 1))) << 4));
     });
     lgkm_wait_rows(rd);
     static_for<0, 8>([&](auto k) {
-      const int rr = 32 * q + 4 * k + g;   // row within the wave
-      const int cb = 8 * rl;               // column within the wave
+      const int rr = 16 * JR * q + RPI * k + lr;   // row within the wave
+      const int cb = 8 * lc;                       // column within the wave
       const uint32_t off = rr < rows_valid && cb < cols_valid ? static_cast<uint32_t>((rr * ld + cb) * 2) : OOB;
       __builtin_amdgcn_raw_buffer_store_b128(rd[k], r, static_cast<int>(off), 0, 0);
     });
@@ -621,26 +627,31 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
   const int row0 = t.m0 + 128 * wm;
   const int rows_valid = t.m_end - row0;
   if constexpr (MODE == FWD1) {
-    // G, U, A [n][f]: gate accumulators in tiles i < 4, up in i + 4 (same columns)
+    // G, U, A [n][f]: gate accumulators in tiles i < 4, up in i + 4 (same columns); each output
+    // is staged in turn
     const int col0 = t.n0 + 64 * wn;
-    const WaveOut w = wave_out(rows_valid, p.f - col0, p.f, lane);
-    const auto rg = out_rsrc(p.o0, p.n, p.f, row0, col0);
-    const auto ru = out_rsrc(p.o1, p.n, p.f, row0, col0);
-    const auto ra = out_rsrc(p.o2, p.n, p.f, row0, col0);
-    static_for<0, 8>([&](auto j) {
+    const int cv = p.f - col0;
+    auto gval = [&](auto i, auto j) -> u32x2 {
       pin_acc_col<j>(acc);
-      static_for<0, 4>([&](auto i) {
-        const uint32_t off = out_off<i, j>(w);
-        const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
-        float av[4];
+      const f32x4 v = acc[i][j];
+      return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    auto uval = [&](auto i, auto j) -> u32x2 {
+      pin_acc_col<j>(acc);
+      const f32x4 v = acc[i + 4][j];
+      return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    auto aval = [&](auto i, auto j) -> u32x2 {
+      pin_acc_col<j>(acc);
+      const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
+      float av[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
-        st4(rg, off, gv[0], gv[1], gv[2], gv[3]);
-        st4(ru, off, uv[0], uv[1], uv[2], uv[3]);
-        st4(ra, off, av[0], av[1], av[2], av[3]);
-      });
-      __builtin_amdgcn_sched_barrier(0);   // one row at a time: bounds the epilogue's registers
-    });
+      for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
+      return u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+    };
+    store_staged<4>(gval, out_rsrc(p.o0, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
+    store_staged<4>(uval, out_rsrc(p.o1, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
+    store_staged<4>(aval, out_rsrc(p.o2, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
   } else if constexpr (MODE == DGRAD1) {
     // dG, dU [n][f] from dA and the saved G, U (read through the same offsets; rows and columns
     // outside the matrix read zero and are not stored).  A row of MFMA tiles is loaded a row
@@ -692,7 +703,12 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
       out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
       rows = Mtot;
     }
-    store_staged(acc, out_rsrc(out, rows, Ntot, row0, col0), rows_valid, Ntot - col0, Ntot, stg, lane);
+    auto val = [&](auto i, auto j) -> u32x2 {
+      pin_acc_col<j>(acc);
+      const f32x4 v = acc[i][j];
+      return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    store_staged<8>(val, out_rsrc(out, rows, Ntot, row0, col0), rows_valid, Ntot - col0, Ntot, stg, lane);
   }
 }
 
