@@ -434,50 +434,17 @@ __device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-// The epilogue writes through buffer descriptors: an element a lane must not write (a row past
-// the expert's or the matrix's end, a column group past the matrix) gets a byte offset past any
-// buffer, and the hardware drops the store (a load there reads zero).  No lane-dependent
-// branches, so the compiler schedules the whole epilogue as one block.
+// The epilogue reads and writes through buffer descriptors: an element a lane must not touch (a
+// row past the expert's or the matrix's end, a column past the matrix) gets a byte offset past
+// any buffer, so the hardware drops the store and a load there reads zero.  No lane-dependent
+// branches, so the compiler schedules the whole epilogue as straight-line code.
 constexpr uint32_t OOB = 0x80000000u;
-
-// Where this lane's outputs go, relative to the wave's first output element (row0, col0) of a
-// row-major output with row pitch `ld` elements: row[j] is the byte offset of row 16j + lane%16,
-// column 4*(lane/16), or OOB past `rows_valid` rows; ni is the number of 16-column groups inside
-// the matrix (wave-uniform; `cols_valid` is a multiple of 16).
-struct WaveOut {
-  uint32_t row[8];
-  int ni;
-};
-
-__device__ __forceinline__ WaveOut wave_out(int rows_valid, int cols_valid, int ld, int lane) {
-  WaveOut w;
-  const int rl = lane & 15, cq = 4 * (lane >> 4);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 16 * j + rl;
-    w.row[j] = r < rows_valid ? static_cast<uint32_t>((r * ld + cq) * 2) : OOB;
-  }
-  w.ni = cols_valid <= 0 ? 0 : (cols_valid >= 128 ? 8 : cols_valid / 16);
-  w.ni = __builtin_amdgcn_readfirstlane(w.ni);
-  return w;
-}
-
-// Byte offset of this lane's 4 elements in MFMA tile (i, j): column group i is 16 elements on.
-template <int I, int J>
-__device__ __forceinline__ uint32_t out_off(const WaveOut& w) {
-  return I < w.ni ? w.row[J] + 32u * I : OOB;
-}
 
 // Descriptor over a row-major [rows][ld] bf16 output from element (row0, col0) to its end.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const uint16_t* base, long long rows, int ld, int row0,
                                                          int col0) {
   const long long start = static_cast<long long>(row0) * ld + col0;
   return make_rsrc(base + start, (rows * ld - start) * 2);
-}
-
-__device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
-  const u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(off), 0, 0);
 }
 
 // ---- epilogue staging through LDS.  During a tile's epilogue the N-side stage of its last K
@@ -494,6 +461,10 @@ __device__ __forceinline__ void ds_w64(uint32_t addr, const u32x2& v) {
   asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
+__device__ __forceinline__ void ds_w128(uint32_t addr, const u32x4& v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ void ds_r128(u32x4& v, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
 }
@@ -508,38 +479,80 @@ __device__ __forceinline__ void lgkm_wait_rows(u32x4 (&v)[8]) {
 // gives the 4 packed values this lane holds for MFMA tile (i, j) (row 16j + lane%16, columns
 // 16i + 4*(lane/16) .. +3).  Rows at or past `rows_valid` and columns at or past `cols_valid`
 // (relative to the wave) are dropped.  A round covers 256/NI rows (8 KiB); a row is 2*NI chunks.
-template <int NI, class Val>
-__device__ __forceinline__ void store_staged(Val&& val, __amdgpu_buffer_rsrc_t r, int rows_valid, int cols_valid,
-                                             int ld, uint32_t stg, int lane) {
+// One round of store_staged: the packed values v[jj][i] of MFMA tiles (i, JR q + jj) go to LDS in
+// the MFMA layout, come back as whole rows and leave in 16-byte stores.
+template <int NI>
+__device__ __forceinline__ void stage_out_round(const u32x2 (&v)[16 / NI][NI], int q, __amdgpu_buffer_rsrc_t r,
+                                                int rows_valid, int cols_valid, int ld, uint32_t stg, int lane) {
   constexpr int CH = 2 * NI;            // 16-byte chunks per row
   constexpr int RB = 32 * NI;           // bytes per row
   constexpr int JR = 16 / NI;           // MFMA row blocks per round
   constexpr int RPI = 64 / CH;          // rows per 16-byte read instruction
   const int rl = lane & 15, g = lane >> 4;
   const int lr = lane / CH, lc = lane % CH;
+  static_for<0, JR>([&](auto jj) {
+    const int row = 16 * jj + rl;
+    const uint32_t rowb = stg + row * RB + ((g & 1) << 3);
+    static_for<0, NI>([&](auto i) { ds_w64(rowb + ((((2 * i) | (g >> 1)) ^ (row & (CH - 1))) << 4), v[jj][i]); });
+  });
+  u32x4 rd[8];
+  static_for<0, 8>([&](auto k) {
+    const int row = RPI * k + lr;   // row within the round
+    ds_r128(rd[k], stg + row * RB + ((lc ^ (row & (CH - 1))) << 4));
+  });
+  lgkm_wait_rows(rd);
+  static_for<0, 8>([&](auto k) {
+    const int rr = 16 * JR * q + RPI * k + lr;   // row within the wave
+    const int cb = 8 * lc;                       // column within the wave
+    const uint32_t off = rr < rows_valid && cb < cols_valid ? static_cast<uint32_t>((rr * ld + cb) * 2) : OOB;
+    __builtin_amdgcn_raw_buffer_store_b128(rd[k], r, static_cast<int>(off), 0, 0);
+  });
+}
+
+// Stores a wave's 128 x 16*NI bf16 outputs to a row-major output of pitch `ld` through the
+// descriptor `r` (based at the wave's first output element), staging through `stg`.  val(i, j)
+// gives the 4 packed values this lane holds for MFMA tile (i, j) (row 16j + lane%16, columns
+// 16i + 4*(lane/16) .. +3).  Rows at or past `rows_valid` and columns at or past `cols_valid`
+// (relative to the wave) are dropped.  A round covers 256/NI rows (8 KiB); a row is 2*NI chunks.
+template <int NI, class Val>
+__device__ __forceinline__ void store_staged(Val&& val, __amdgpu_buffer_rsrc_t r, int rows_valid, int cols_valid,
+                                             int ld, uint32_t stg, int lane) {
+  constexpr int JR = 16 / NI;
   static_for<0, 8 / JR>([&](auto q) {
+    u32x2 v[JR][NI];
     static_for<0, JR>([&](auto jj) {
-      const int row = 16 * jj + rl;
-      const uint32_t rowb = stg + row * RB + ((g & 1) << 3);
-      static_for<0, NI>([&](auto i) {
-        const u32x2 w = val(i, std::integral_constant<int, JR * q + jj>{});
-        ds_w64(rowb + ((((2 * i) | (g >> 1)) ^ (row & (CH - 1))) << 4), w);
-      });
+      static_for<0, NI>([&](auto i) { v[jj][i] = val(i, std::integral_constant<int, JR * q + jj>{}); });
     });
-    u32x4 rd[8];
-    static_for<0, 8>([&](auto k) {
-      const int row = RPI * k + lr;   // row within the round
-      ds_r128(rd[k], stg + row * RB + ((lc ^ (row & (CH - 1))) << 4));
-    });
-    lgkm_wait_rows(rd);
-    static_for<0, 8>([&](auto k) {
-      const int rr = 16 * JR * q + RPI * k + lr;   // row within the wave
-      const int cb = 8 * lc;                       // column within the wave
-      const uint32_t off = rr < rows_valid && cb < cols_valid ? static_cast<uint32_t>((rr * ld + cb) * 2) : OOB;
-      __builtin_amdgcn_raw_buffer_store_b128(rd[k], r, static_cast<int>(off), 0, 0);
-    });
+    stage_out_round<NI>(v, q, r, rows_valid, cols_valid, ld, stg, lane);
     __builtin_amdgcn_sched_barrier(0);
   });
+}
+
+__device__ __forceinline__ void ds_r64(u32x2& v, uint32_t addr) {
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+}
+
+__device__ __forceinline__ void lgkm_wait_tiles(u32x2 (&v)[2][8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]), "+v"(v[0][4]), "+v"(v[0][5]),
+                 "+v"(v[0][6]), "+v"(v[0][7]), "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
+                 "+v"(v[1][4]), "+v"(v[1][5]), "+v"(v[1][6]), "+v"(v[1][7])::"memory");
+}
+
+// The reverse of a staged round for 128-column waves: 32 rows read from global memory as whole
+// rows (held in `in`, 8 pieces of 16 bytes per lane) go through LDS into the MFMA layout.
+__device__ __forceinline__ void stage_in_round(const u32x4 (&in)[8], u32x2 (&v)[2][8], uint32_t stg, int lane) {
+  const int rl = lane & 15, g = lane >> 4;
+  static_for<0, 8>([&](auto k) {
+    const int row = 4 * k + g;
+    ds_w128(stg + row * 256 + ((rl ^ (row & 15)) << 4), in[k]);
+  });
+  static_for<0, 2>([&](auto jj) {
+    const int row = 16 * jj + rl;
+    const uint32_t rowb = stg + row * 256 + ((g & 1) << 3);
+    static_for<0, 8>([&](auto i) { ds_r64(v[jj][i], rowb + ((((2 * i) | (g >> 1)) ^ (row & 15)) << 4)); });
+  });
+  lgkm_wait_tiles(v);
 }
 
 // Logistic function with the hardware reciprocal (v_rcp_f32, about 1 ulp): far below the bf16
@@ -653,43 +666,52 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
     store_staged<4>(uval, out_rsrc(p.o1, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
     store_staged<4>(aval, out_rsrc(p.o2, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
   } else if constexpr (MODE == DGRAD1) {
-    // dG, dU [n][f] from dA and the saved G, U (read through the same offsets; rows and columns
-    // outside the matrix read zero and are not stored).  A row of MFMA tiles is loaded a row
-    // ahead of its use.
+    // dG, dU [n][f] from dA and the saved G, U, 32 rows per round: G and U come in as whole rows
+    // (rows and columns outside the matrix read zero and are not stored) and reach the MFMA
+    // layout through LDS; dG and dU leave the same way.
     const int col0 = t.n0 + 128 * wn;
-    const WaveOut w = wave_out(rows_valid, p.f - col0, p.f, lane);
+    const int cv = p.f - col0;
     const auto rgi = out_rsrc(p.g, p.n, p.f, row0, col0);
     const auto rui = out_rsrc(p.u, p.n, p.f, row0, col0);
     const auto rdg = out_rsrc(p.o0, p.n, p.f, row0, col0);
     const auto rdu = out_rsrc(p.o1, p.n, p.f, row0, col0);
-    u32x2 gw[2][8], uw[2][8];
-    auto load_row = [&](auto j) {
-      static_for<0, 8>([&](auto i) {
-        const int off = static_cast<int>(out_off<i, j>(w));
-        gw[j & 1][i] = __builtin_amdgcn_raw_buffer_load_b64(rgi, off, 0, 0);
-        uw[j & 1][i] = __builtin_amdgcn_raw_buffer_load_b64(rui, off, 0, 0);
+    const int lr = lane >> 4, lc = lane & 15;
+    u32x4 gl[8], ul[8];
+    auto load_round = [&](const __amdgpu_buffer_rsrc_t& rs, int q, u32x4 (&dst)[8]) {
+      static_for<0, 8>([&](auto k) {
+        const int rr = 32 * q + 4 * k + lr, cb = 8 * lc;
+        const int off = rr < rows_valid && cb < cv ? (rr * p.f + cb) * 2 : static_cast<int>(OOB);
+        dst[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
       });
     };
-    load_row(std::integral_constant<int, 0>{});
-    static_for<0, 8>([&](auto j) {
-      if constexpr (j < 7) load_row(std::integral_constant<int, j + 1>{});
-      pin_acc_col<j>(acc);
-      static_for<0, 8>([&](auto i) {
-        const u32x2 g2 = gw[j & 1][i], u2 = uw[j & 1][i];
-        const float gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
-        const float uv[4] = {bf16_lo(u2.x), bf16_hi(u2.x), bf16_lo(u2.y), bf16_hi(u2.y)};
-        const f32x4 dav = acc[i][j];
-        float dg[4], du[4];
+    static_for<0, 4>([&](auto q) {
+      load_round(rgi, q, gl);
+      load_round(rui, q, ul);
+      u32x2 gm[2][8], um[2][8];
+      stage_in_round(gl, gm, stg, lane);
+      stage_in_round(ul, um, stg, lane);
+      pin_acc_col<2 * q>(acc);
+      pin_acc_col<2 * q + 1>(acc);
+      // dG, dU replace G, U in place (fewer live registers)
+      static_for<0, 2>([&](auto jj) {
+        static_for<0, 8>([&](auto i) {
+          const u32x2 g2 = gm[jj][i], u2 = um[jj][i];
+          const float gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
+          const float uv[4] = {bf16_lo(u2.x), bf16_hi(u2.x), bf16_lo(u2.y), bf16_hi(u2.y)};
+          const f32x4 dav = acc[i][2 * q + jj];
+          float dg[4], du[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sg = sigmoidf_(gv[q]);
-          dg[q] = dav[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-          du[q] = dav[q] * gv[q] * sg;
-        }
-        const uint32_t off = out_off<i, j>(w);
-        st4(rdg, off, dg[0], dg[1], dg[2], dg[3]);
-        st4(rdu, off, du[0], du[1], du[2], du[3]);
+          for (int e = 0; e < 4; ++e) {
+            const float sg = sigmoidf_(gv[e]);
+            dg[e] = dav[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+            du[e] = dav[e] * gv[e] * sg;
+          }
+          gm[jj][i] = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          um[jj][i] = u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+        });
       });
+      stage_out_round<8>(gm, q, rdg, rows_valid, cv, p.f, stg, lane);
+      stage_out_round<8>(um, q, rdu, rows_valid, cv, p.f, stg, lane);
       __builtin_amdgcn_sched_barrier(0);
     });
   } else {
