@@ -12,7 +12,9 @@ Prints one JSON line with the throughput (tokens/s), the roofline of the dominan
 oracle's throughput on the host cores over a bounded token sample (a baseline only).  Every
 grouped-GEMM call of the step is one kernel and is bracketed with HIP events on the stream it
 runs on, during the timed steps; the dominant kernel is the one with the largest average
-duration (under MXFP8 the forward down call, which also quantises A, is not a candidate).  Its
+duration (under MXFP8 the forward down call, which also quantises A, is not a candidate).  The
+routing and row-movement calls are timed the same way and reported as achieved HBM GB/s on their
+algorithmic bytes (`rows_hbm_gbs`, against the 8000 GB/s peak).  The dominant GEMM's
 `traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary kept
 in profiles/, and is null when that summary is missing or was taken on other kernel sources.
 
@@ -97,6 +99,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0):
         w.quantize_mx()
     x, dy, logits = inputs["x"], inputs["dy"], inputs.get("logits")
     calls = layer.GEMM_CALLS if not cfg.forward_only else ("gate_up", "down")
+    rows = layer.ROW_CALLS if not cfg.forward_only else ("route", "permute", "combine")
 
     def step(events=None):
         if cfg.mxfp8:
@@ -108,7 +111,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [{c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in calls}
+    evs = [{c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in calls + rows}
            for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -116,8 +119,8 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0):
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gemm_ms = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / steps for c in calls}
-    return elapsed, gemm_ms
+    avg = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / steps for c in calls + rows}
+    return elapsed, {c: avg[c] for c in calls}, {c: avg[c] for c in rows}
 
 
 def traffic_of(cfg, call):
@@ -131,6 +134,19 @@ def traffic_of(cfg, call):
             or t.get("kernel") != profsum.kernel_name(call, dtype)):
         return None
     return float(t["traffic_bytes"])
+
+
+def row_bytes(cfg, call):
+    """Algorithmic HBM bytes of the routing and row-movement calls (each element read or written
+    once; bf16 rows, E4M3 rows + E8M0 scales for the MXFP8 permute, fp32 gates and logits)."""
+    T, d, E, k = float(cfg.T), cfg.d, cfg.E, cfg.k
+    eb = 1 + 1 / 32 if cfg.mxfp8 else 2
+    return {"route": T * (4 * E + 12 * k),
+            "permute": (1 + k) * T * d * eb + 4 * T * k,
+            "combine": (k + 1) * T * d * 2 + 8 * T * k,
+            "combine_bwd": (2 * k + 1) * T * d * 2 + 12 * T * k,
+            "permute_bwd": (k + 1) * T * d * 2 + 4 * T * k,
+            "route_bwd": T * (4 * E + 12 * k)}[call]
 
 
 def gemm_bytes(cfg, call):
@@ -181,7 +197,7 @@ def main():
               file=sys.stderr)
         return 2
     cfg = workload_config(args)
-    elapsed, gemm_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe)
+    elapsed, gemm_ms, row_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
     flops = gemm_flops(cfg)
@@ -213,6 +229,9 @@ def main():
                      "algorithmic_bytes": round(gemm_bytes(cfg, dom))},
         "gemm_ms": {c: round(v, 4) for c, v in gemm_ms.items()},
         "gemm_tflops": {c: round(flops[c] / (v * 1e-3) / 1e12, 1) for c, v in gemm_ms.items()},
+        "rows_us": {c: round(v * 1e3, 1) for c, v in row_ms.items()},
+        "rows_hbm_gbs": {c: round(row_bytes(cfg, c) / (v * 1e-3) / 1e9, 1) for c, v in row_ms.items()},
+        "hbm_peak_gbs": HBM_PEAK_GBS,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)

@@ -67,24 +67,28 @@ class _Span:
         return False
 
 
-# names of the calls `forward` and `backward` can bracket with events; each is one grouped GEMM
-# kernel ("down" under MXFP8 also quantises a along f first)
+# names of the calls `forward` and `backward` can bracket with events: each grouped-GEMM call is
+# one kernel ("down" under MXFP8 also quantises a along f first); ROW_CALLS are the routing and
+# row-movement calls (route: its three kernels)
 GEMM_CALLS = ("gate_up", "down", "dgrad_down", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up")
+ROW_CALLS = ("route", "permute", "combine", "combine_bwd", "permute_bwd", "route_bwd")
 
 
 def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=None):
     """Layer forward.  x [T, d] bf16; logits [T, E] fp32 unless weights.w_r is given.
     Returns the context dict that `backward` consumes (all intermediate tensors), with y.
     events: optional {name: (start, end)} of torch.cuda.Event pairs, recorded on the current
-    stream around the grouped-GEMM calls named in GEMM_CALLS."""
+    stream around the calls named in GEMM_CALLS and ROW_CALLS."""
     ctx = dict(x=x, k=k, mxfp8=mxfp8)
     if logits is None:
         logits = ops.router_project(x, weights.w_r)
     ctx["logits"] = logits
-    r = ops.route_topk(logits, k, want_probs=want_probs, pad=32 if mxfp8 else None)
+    with _Span(events, "route"):
+        r = ops.route_topk(logits, k, want_probs=want_probs, pad=32 if mxfp8 else None)
     ctx.update(r)
     if not mxfp8:
-        xp = ops.permute(x, r["dest"])
+        with _Span(events, "permute"):
+            xp = ops.permute(x, r["dest"])
         ctx["xp"] = xp
         with _Span(events, "gate_up"):
             g, u, a = ops.grouped_gemm_gate_up(xp, r["offsets"], weights.w_gate, weights.w_up)
@@ -93,7 +97,8 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
     else:
         q = weights.mx or weights.quantize_mx()
         xq, xs = ops.mxfp8_quantize(x, 0)
-        xpq, xps = ops.permute(xq, r["dest"], x_scale=xs)
+        with _Span(events, "permute"):
+            xpq, xps = ops.permute(xq, r["dest"], x_scale=xs)
         ctx["xq"], ctx["xs"], ctx["xpq"], ctx["xps"] = xq, xs, xpq, xps
         with _Span(events, "gate_up"):
             g, u, a = ops.grouped_gemm_gate_up(xpq, r["offsets"], q["wg"], q["wu"],
@@ -101,7 +106,8 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
         with _Span(events, "down"):
             yexp = ops.grouped_gemm_down(a, r["offsets"], q["wd"], w_down_scale=q["wd_s"])
     ctx.update(g=g, u=u, a=a, yexp=yexp)
-    ctx["y"] = ops.unpermute_combine(yexp, r["topk_gate"], r["dest"])
+    with _Span(events, "combine"):
+        ctx["y"] = ops.unpermute_combine(yexp, r["topk_gate"], r["dest"])
     return ctx
 
 
@@ -110,7 +116,8 @@ def backward(ctx, weights, dy, events=None):
     dw_down (and dw_r, dx_router when the layer owns its router) plus the intermediates.
     events: as for `forward`."""
     out = {}
-    dyexp, dgate = ops.unpermute_combine_bwd(dy, ctx["yexp"], ctx["topk_gate"], ctx["dest"])
+    with _Span(events, "combine_bwd"):
+        dyexp, dgate = ops.unpermute_combine_bwd(dy, ctx["yexp"], ctx["topk_gate"], ctx["dest"])
     out.update(dyexp=dyexp, d_gate=dgate)
     off = ctx["offsets"]
     g, u, a = ctx["g"], ctx["u"], ctx["a"]
@@ -149,10 +156,12 @@ def backward(ctx, weights, dy, events=None):
                                                             scales=(dgTs, duTs, xTs))
     out.update(dg=dg, du=du, dxp=dxp, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
     E = ctx["logits"].shape[1]
-    out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E)
+    with _Span(events, "route_bwd"):
+        out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E)
     addend = None
     if weights.w_r is not None:
         addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])
         out["dx_router"] = addend
-    out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
+    with _Span(events, "permute_bwd"):
+        out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
     return out
