@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_epilogue.h"
 
 namespace moe {
 namespace gg {
@@ -338,15 +339,6 @@ __device__ __forceinline__ void pin_acc_row(f32x4 (&r)[8]) {
                "+a"(r[7]));
 }
 
-// Keeps column J of the accumulators (acc[0..7][J]) in AGPRs up to this point: the epilogue pins
-// each column just before it reads it, so the compiler copies the accumulators out one column
-// at a time rather than all 256 at once.
-template <int J>
-__device__ __forceinline__ void pin_acc_col(f32x4 (&acc)[8][8]) {
-  asm volatile("" : "+a"(acc[0][J]), "+a"(acc[1][J]), "+a"(acc[2][J]), "+a"(acc[3][J]), "+a"(acc[4][J]),
-               "+a"(acc[5][J]), "+a"(acc[6][J]), "+a"(acc[7][J]));
-}
-
 // Fragment index (units of 16 rows/columns) of B fragment i for wave column wn (FWD1 pairs gate
 // rows with up rows).
 template <int MODE, int I>
@@ -430,134 +422,11 @@ __device__ __forceinline__ void sub_step(const Params& p, const OpLoad& ld, bool
   });
 }
 
-// ---------------------------------------------------------------- epilogue helpers
+// ---------------------------------------------------------------- epilogue
 
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-// The epilogue reads and writes through buffer descriptors: an element a lane must not touch (a
-// row past the expert's or the matrix's end, a column past the matrix) gets a byte offset past
-// any buffer, so the hardware drops the store and a load there reads zero.  No lane-dependent
-// branches, so the compiler schedules the whole epilogue as straight-line code.
-constexpr uint32_t OOB = 0x80000000u;
-
-// Descriptor over a row-major [rows][ld] bf16 output from element (row0, col0) to its end.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const uint16_t* base, long long rows, int ld, int row0,
-                                                         int col0) {
-  const long long start = static_cast<long long>(row0) * ld + col0;
-  return make_rsrc(base + start, (rows * ld - start) * 2);
-}
-
-// ---- epilogue staging through LDS.  During a tile's epilogue the N-side stage of its last K
-// step is free (every wave has read it; the stream's next DMA into it comes a step later), so
-// each wave stages its 128 x 128 outputs there through its own 8 KiB, 32 rows per round: the
-// MFMA layout goes in as 8-byte pieces, comes out as whole 256-byte rows, and leaves in 16-byte
-// stores that cover full 128-byte lines (the MFMA layout alone gives 32-byte pieces of 16 rows
-// per store, which the memory system takes several times longer to absorb).  16-byte chunks are
-// XOR-swizzled by row so both access patterns spread over the LDS banks.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-constexpr int STG_BYTES = 8192;   // per wave
-
-__device__ __forceinline__ void ds_w64(uint32_t addr, const u32x2& v) {
-  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
-}
-
-__device__ __forceinline__ void ds_w128(uint32_t addr, const u32x4& v) {
-  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
-}
-
-__device__ __forceinline__ void ds_r128(u32x4& v, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-}
-
-__device__ __forceinline__ void lgkm_wait_rows(u32x4 (&v)[8]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])::"memory");
-}
-
-// Stores a wave's 128 x 16*NI bf16 outputs to a row-major output of pitch `ld` through the
-// descriptor `r` (based at the wave's first output element), staging through `stg`.  val(i, j)
-// gives the 4 packed values this lane holds for MFMA tile (i, j) (row 16j + lane%16, columns
-// 16i + 4*(lane/16) .. +3).  Rows at or past `rows_valid` and columns at or past `cols_valid`
-// (relative to the wave) are dropped.  A round covers 256/NI rows (8 KiB); a row is 2*NI chunks.
-// One round of store_staged: the packed values v[jj][i] of MFMA tiles (i, JR q + jj) go to LDS in
-// the MFMA layout, come back as whole rows and leave in 16-byte stores.
-template <int NI>
-__device__ __forceinline__ void stage_out_round(const u32x2 (&v)[16 / NI][NI], int q, __amdgpu_buffer_rsrc_t r,
-                                                int rows_valid, int cols_valid, int ld, uint32_t stg, int lane) {
-  constexpr int CH = 2 * NI;            // 16-byte chunks per row
-  constexpr int RB = 32 * NI;           // bytes per row
-  constexpr int JR = 16 / NI;           // MFMA row blocks per round
-  constexpr int RPI = 64 / CH;          // rows per 16-byte read instruction
-  const int rl = lane & 15, g = lane >> 4;
-  const int lr = lane / CH, lc = lane % CH;
-  static_for<0, JR>([&](auto jj) {
-    const int row = 16 * jj + rl;
-    const uint32_t rowb = stg + row * RB + ((g & 1) << 3);
-    static_for<0, NI>([&](auto i) { ds_w64(rowb + ((((2 * i) | (g >> 1)) ^ (row & (CH - 1))) << 4), v[jj][i]); });
-  });
-  u32x4 rd[8];
-  static_for<0, 8>([&](auto k) {
-    const int row = RPI * k + lr;   // row within the round
-    ds_r128(rd[k], stg + row * RB + ((lc ^ (row & (CH - 1))) << 4));
-  });
-  lgkm_wait_rows(rd);
-  static_for<0, 8>([&](auto k) {
-    const int rr = 16 * JR * q + RPI * k + lr;   // row within the wave
-    const int cb = 8 * lc;                       // column within the wave
-    const uint32_t off = rr < rows_valid && cb < cols_valid ? static_cast<uint32_t>((rr * ld + cb) * 2) : OOB;
-    __builtin_amdgcn_raw_buffer_store_b128(rd[k], r, static_cast<int>(off), 0, 0);
-  });
-}
-
-// Stores a wave's 128 x 16*NI bf16 outputs to a row-major output of pitch `ld` through the
-// descriptor `r` (based at the wave's first output element), staging through `stg`.  val(i, j)
-// gives the 4 packed values this lane holds for MFMA tile (i, j) (row 16j + lane%16, columns
-// 16i + 4*(lane/16) .. +3).  Rows at or past `rows_valid` and columns at or past `cols_valid`
-// (relative to the wave) are dropped.  A round covers 256/NI rows (8 KiB); a row is 2*NI chunks.
-template <int NI, class Val>
-__device__ __forceinline__ void store_staged(Val&& val, __amdgpu_buffer_rsrc_t r, int rows_valid, int cols_valid,
-                                             int ld, uint32_t stg, int lane) {
-  constexpr int JR = 16 / NI;
-  static_for<0, 8 / JR>([&](auto q) {
-    u32x2 v[JR][NI];
-    static_for<0, JR>([&](auto jj) {
-      static_for<0, NI>([&](auto i) { v[jj][i] = val(i, std::integral_constant<int, JR * q + jj>{}); });
-    });
-    stage_out_round<NI>(v, q, r, rows_valid, cols_valid, ld, stg, lane);
-    __builtin_amdgcn_sched_barrier(0);
-  });
-}
-
-__device__ __forceinline__ void ds_r64(u32x2& v, uint32_t addr) {
-  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-}
-
-__device__ __forceinline__ void lgkm_wait_tiles(u32x2 (&v)[2][8]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]), "+v"(v[0][4]), "+v"(v[0][5]),
-                 "+v"(v[0][6]), "+v"(v[0][7]), "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
-                 "+v"(v[1][4]), "+v"(v[1][5]), "+v"(v[1][6]), "+v"(v[1][7])::"memory");
-}
-
-// The reverse of a staged round for 128-column waves: 32 rows read from global memory as whole
-// rows (held in `in`, 8 pieces of 16 bytes per lane) go through LDS into the MFMA layout.
-__device__ __forceinline__ void stage_in_round(const u32x4 (&in)[8], u32x2 (&v)[2][8], uint32_t stg, int lane) {
-  const int rl = lane & 15, g = lane >> 4;
-  static_for<0, 8>([&](auto k) {
-    const int row = 4 * k + g;
-    ds_w128(stg + row * 256 + ((rl ^ (row & 15)) << 4), in[k]);
-  });
-  static_for<0, 2>([&](auto jj) {
-    const int row = 16 * jj + rl;
-    const uint32_t rowb = stg + row * 256 + ((g & 1) << 3);
-    static_for<0, 8>([&](auto i) { ds_r64(v[jj][i], rowb + ((((2 * i) | (g >> 1)) ^ (row & 15)) << 4)); });
-  });
-  lgkm_wait_tiles(v);
-}
-
-// Logistic function with the hardware reciprocal (v_rcp_f32, about 1 ulp): far below the bf16
-// rounding the results get.  Saturates to 0 / 1 for large |x|.
-__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+// The LDS each wave stages its epilogue through: 8 KiB of the N-side stage of the tile's last K
+// step, which every wave has finished reading (the stream's next DMA into it comes a step later).
+constexpr int STG_BYTES = 8192;
 
 // ---------------------------------------------------------------- the kernel
 
@@ -631,106 +500,30 @@ __device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int&
   }
 }
 
-// Writes the tile's results from the accumulators.  Lane holds, for MFMA tile (i, j), output row
-// 16j + lane%16 of the wave's rows and 4 consecutive columns 4*(lane/16) .. +3 of the wave's
-// 16-column group i.
+// Writes the tile's results from the accumulators (helpers in gemm_epilogue.h): SwiGLU on the
+// gate/up product, its backward on the down dgrad, plain stores otherwise.
 template <int MODE>
 __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (&acc)[8][8], int wm, int wn,
                                          int lane, uint32_t stg) {
   const int row0 = t.m0 + 128 * wm;
   const int rows_valid = t.m_end - row0;
   if constexpr (MODE == FWD1) {
-    // G, U, A [n][f]: gate accumulators in tiles i < 4, up in i + 4 (same columns); each output
-    // is staged in turn
-    const int col0 = t.n0 + 64 * wn;
-    const int cv = p.f - col0;
-    auto gval = [&](auto i, auto j) -> u32x2 {
-      pin_acc_col<j>(acc);
-      const f32x4 v = acc[i][j];
-      return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    };
-    auto uval = [&](auto i, auto j) -> u32x2 {
-      pin_acc_col<j>(acc);
-      const f32x4 v = acc[i + 4][j];
-      return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    };
-    auto aval = [&](auto i, auto j) -> u32x2 {
-      pin_acc_col<j>(acc);
-      const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
-      float av[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
-      return u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
-    };
-    store_staged<4>(gval, out_rsrc(p.o0, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
-    store_staged<4>(uval, out_rsrc(p.o1, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
-    store_staged<4>(aval, out_rsrc(p.o2, p.n, p.f, row0, col0), rows_valid, cv, p.f, stg, lane);
+    gep::epi_gate_up<2>(acc, p.o0, p.o1, p.o2, p.n, p.f, row0, rows_valid, t.n0 + 64 * wn, stg, lane);
   } else if constexpr (MODE == DGRAD1) {
-    // dG, dU [n][f] from dA and the saved G, U, 32 rows per round: G and U come in as whole rows
-    // (rows and columns outside the matrix read zero and are not stored) and reach the MFMA
-    // layout through LDS; dG and dU leave the same way.
-    const int col0 = t.n0 + 128 * wn;
-    const int cv = p.f - col0;
-    const auto rgi = out_rsrc(p.g, p.n, p.f, row0, col0);
-    const auto rui = out_rsrc(p.u, p.n, p.f, row0, col0);
-    const auto rdg = out_rsrc(p.o0, p.n, p.f, row0, col0);
-    const auto rdu = out_rsrc(p.o1, p.n, p.f, row0, col0);
-    const int lr = lane >> 4, lc = lane & 15;
-    u32x4 gl[8], ul[8];
-    auto load_round = [&](const __amdgpu_buffer_rsrc_t& rs, int q, u32x4 (&dst)[8]) {
-      static_for<0, 8>([&](auto k) {
-        const int rr = 32 * q + 4 * k + lr, cb = 8 * lc;
-        const int off = rr < rows_valid && cb < cv ? (rr * p.f + cb) * 2 : static_cast<int>(OOB);
-        dst[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-      });
-    };
-    static_for<0, 4>([&](auto q) {
-      load_round(rgi, q, gl);
-      load_round(rui, q, ul);
-      u32x2 gm[2][8], um[2][8];
-      stage_in_round(gl, gm, stg, lane);
-      stage_in_round(ul, um, stg, lane);
-      pin_acc_col<2 * q>(acc);
-      pin_acc_col<2 * q + 1>(acc);
-      // dG, dU replace G, U in place (fewer live registers)
-      static_for<0, 2>([&](auto jj) {
-        static_for<0, 8>([&](auto i) {
-          const u32x2 g2 = gm[jj][i], u2 = um[jj][i];
-          const float gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
-          const float uv[4] = {bf16_lo(u2.x), bf16_hi(u2.x), bf16_lo(u2.y), bf16_hi(u2.y)};
-          const f32x4 dav = acc[i][2 * q + jj];
-          float dg[4], du[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sg = sigmoidf_(gv[e]);
-            dg[e] = dav[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
-            du[e] = dav[e] * gv[e] * sg;
-          }
-          gm[jj][i] = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-          um[jj][i] = u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-        });
-      });
-      stage_out_round<8>(gm, q, rdg, rows_valid, cv, p.f, stg, lane);
-      stage_out_round<8>(um, q, rdu, rows_valid, cv, p.f, stg, lane);
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    // 16 rows per round: the dgrad epilogue holds G, U and dA values at once, so its rounds are
+    // half the plain ones' to stay within the registers the K loop leaves
+    gep::epi_swiglu_bwd<1>(acc, p.g, p.u, p.o0, p.o1, p.n, p.f, row0, rows_valid, t.n0 + 128 * wn, stg, lane);
   } else {
-    // plain stores: FWD2 -> yexp [n][d]; DGRAD2 -> dxp [n][d]; WGRAD -> dW[e] [Mtot][Ntot]
+    // FWD2 -> yexp [n][d]; DGRAD2 -> dxp [n][d]; WGRAD -> dW[e] [Mtot][Ntot]
     const int Ntot = n_total<MODE>(p);
-    const int col0 = t.n0 + 128 * wn;
-    const uint16_t* out = p.o0;
+    uint16_t* out = p.o0;
     long long rows = p.n;
     if constexpr (Traits<MODE>::WGRAD) {
       const int Mtot = m_total_wgrad<MODE>(p);
       out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
       rows = Mtot;
     }
-    auto val = [&](auto i, auto j) -> u32x2 {
-      pin_acc_col<j>(acc);
-      const f32x4 v = acc[i][j];
-      return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    };
-    store_staged<8>(val, out_rsrc(out, rows, Ntot, row0, col0), rows_valid, Ntot - col0, Ntot, stg, lane);
+    gep::epi_plain<2>(acc, out, rows, Ntot, row0, rows_valid, t.n0 + 128 * wn, stg, lane);
   }
 }
 
