@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_epilogue.h"
 
 namespace moe {
 namespace gmx {
@@ -54,7 +55,9 @@ constexpr int A_RING = 0;
 constexpr int B_RING = NSTG * OP_BYTES;
 constexpr int SA_RING = 2 * NSTG * OP_BYTES;
 constexpr int SB_RING = SA_RING + NSTG * SC_BYTES;
-constexpr int LDS_TOTAL = SB_RING + NSTG * SC_BYTES;   // 144 KiB
+constexpr int STG_RING = SB_RING + NSTG * SC_BYTES;    // epilogue staging, 4 KiB per wave
+constexpr int STG_BYTES = 4096;
+constexpr int LDS_TOTAL = STG_RING + 4 * STG_BYTES;    // 160 KiB
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;      // raw buffer, 32-bit data format (gfx9 family)
 
 __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[LDS_TOTAL];
@@ -192,13 +195,13 @@ __device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int&
   }
 }
 
-// One wave's share of an operand stage: 128 rows x 128 bytes of data (16 DMA instructions) and
-// the rows' 4-byte scale words (2 dword DMA instructions).
+// One wave's share of an operand stage: 128 rows x 128 bytes of data (16 DMA instructions of
+// 16 bytes per lane) and the rows' scale bytes (8 byte-DMA instructions).  The offsets depend on
+// the launch, not the tile.
 struct OpLoad {
-  __amdgpu_buffer_rsrc_t r0, r1, s0, s1;   // data / scale descriptors (r1, s1: second tensor)
   int vo[16];
   int so[8];
-  int step, sstep;                         // bytes per K step (data, scales)
+  int step, sstep;   // bytes per K step (data, scales)
 };
 
 // Rows row0 .. row0 + 127 of a row-major byte tensor with `ldb` bytes per row, and their scale
@@ -215,28 +218,46 @@ __device__ __forceinline__ void op_offsets(int row0, int ldb, int lds_, OpLoad& 
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) ld.so[i] = (row0 + 16 * i + (L >> 2)) * lds_ + (L & 3);
+  ld.step = BK;
+  ld.sstep = BK / 32;
 }
 
+// One tile's DMA sources for this wave: data and scale descriptors bounded to the tile's valid
+// extent (r1, s1: the second tensor of FWD1's B half 1 and of DGRAD2's second K half).
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t r0, r1, s0, s1;
+  int nk;   // K steps
+};
+
+// Where K step k of tile `src` is read from; steps past the tile read zeros.
+struct StepSrc {
+  __amdgpu_buffer_rsrc_t r, rs;
+  int soff, ssoff;
+};
+
 template <int MODE>
-__device__ __forceinline__ void issue_stage(const Params& p, const OpLoad& ld, bool role_b, int h, int kt, int nk,
-                                            int st) {
-  __amdgpu_buffer_rsrc_t r = ld.r0, rs = ld.s0;
-  int soff = kt * ld.step, ssoff = kt * ld.sstep;
+__device__ __forceinline__ StepSrc step_src(const Params& p, const OpLoad& ld, const TileSrc& src, bool role_b, int h,
+                                            int k) {
+  StepSrc ss{src.r0, src.s0, k * ld.step, k * ld.sstep};
   if constexpr (MODE == FWD1) {
-    if (role_b && h) { r = ld.r1; rs = ld.s1; }
+    if (role_b && h) { ss.r = src.r1; ss.rs = src.s1; }
   } else if constexpr (MODE == DGRAD2) {
     const int kf = p.f / BK;
-    if (kt >= kf) { r = ld.r1; rs = ld.s1; soff = (kt - kf) * ld.step; ssoff = (kt - kf) * ld.sstep; }
+    if (k >= kf) { ss.r = src.r1; ss.rs = src.s1; ss.soff = (k - kf) * ld.step; ss.ssoff = (k - kf) * ld.sstep; }
   }
-  if (kt >= nk) { r = make_rsrc(p.a0, 0); rs = r; soff = 0; ssoff = 0; }
-  uint8_t* dst = lds_ring + (role_b ? B_RING : A_RING) + st * OP_BYTES + h * (OP_BYTES / 2);
+  if (k >= src.nk) { ss.r = make_rsrc(p.a0, 0); ss.rs = ss.r; ss.soff = 0; ss.ssoff = 0; }
+  return ss;
+}
+
+// DMA instructions of a stage: data pieces [D0, D0 + ND) and scale pieces [S0, S0 + NS).
+template <int D0, int ND, int S0, int NS>
+__device__ __forceinline__ void issue_part(const OpLoad& ld, const StepSrc& ss, uint8_t* dst, uint8_t* sdst) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, ld.vo[i], soff, 0, 0);
-  uint8_t* sdst = lds_ring + (role_b ? SB_RING : SA_RING) + st * SC_BYTES + h * (SC_BYTES / 2);
+  for (int i = D0; i < D0 + ND; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss.r, (lds_void*)(dst + i * 1024), 16, ld.vo[i], ss.soff, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sdst + i * 256), 1, ld.so[i], ssoff, 0, 0);
+  for (int i = S0; i < S0 + NS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss.rs, (lds_void*)(sdst + i * 256), 1, ld.so[i], ss.ssoff, 0, 0);
 }
 
 // acc += x * y (scaled fp8), accumulating in place in AGPRs (tied inline asm; callers cover the
@@ -250,6 +271,17 @@ __device__ __forceinline__ void mfma_acc(f32x4& c, const i32x8& x, const i32x8& 
 __device__ __forceinline__ void pin_acc_row(f32x4 (&r)[8]) {
   asm volatile("" : "+a"(r[0]), "+a"(r[1]), "+a"(r[2]), "+a"(r[3]), "+a"(r[4]), "+a"(r[5]), "+a"(r[6]),
                "+a"(r[7]));
+}
+
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // initialisation -> first MFMA: pin the zeroed registers ahead of the wait states
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
+  asm volatile("s_nop 7" ::: "memory");
 }
 
 // Fragment q (16 rows) of a stage: lane l reads row 16q + l % 16, chunks l/16 and 4 + l/16, and
@@ -292,30 +324,12 @@ __device__ __forceinline__ int bfrag_base(int wn) {
   return MODE == FWD1 ? 4 * wn : 8 * wn;
 }
 
-__device__ __forceinline__ void st4(uint16_t* p, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
-}
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-
+// The tile with linear id `lid` (< the launch's tile count): n-tile fastest, then m-tile, then
+// (weight gradients) expert.
 template <int MODE>
-__global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- device-side schedule (as in the bf16 kernels)
-  const int NTW = n_tile_width<MODE>();
-  const int ntiles_n = (n_total<MODE>(p) + NTW - 1) / NTW;
-  const int bid = blockIdx.x;
+__device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int ntiles_n, int lid) {
   Tile t;
   if constexpr (!Traits<MODE>::WGRAD) {
-    const MTiles mts = mtile_scan(p.offsets, p.E);
-    const int total_tiles = mts.total * ntiles_n;
-    const int tot8 = (total_tiles + 7) & ~7;
-    if (bid >= tot8) return;
-    const int lid = (bid & 7) * (tot8 >> 3) + (bid >> 3);
-    if (lid >= total_tiles) return;
     const int mt_glob = lid / ntiles_n;
     const int nt = lid - mt_glob * ntiles_n;
     int e, first;
@@ -323,24 +337,14 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
     t.e = e;
     t.m0 = p.offsets[e] + (mt_glob - first) * BM;
     t.m_end = p.offsets[e + 1];
-    t.n0 = nt * NTW;
+    t.n0 = nt * n_tile_width<MODE>();
     t.half = 0;
     t.k_begin = 0;
     t.k_len = k_total<MODE>(p);
   } else {
     const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
     const int mt = (Mtot + BM - 1) / BM;
-    const int mtt = mt * (MODE == WGRAD_GU ? 2 : 1);
-    const int total_tiles = p.E * mtt * ntiles_n;
-    const int tot8 = (total_tiles + 7) & ~7;
-    if (bid >= tot8) return;
-    // Weight-gradient tiles cost in proportion to their expert's rows.  With balanced experts,
-    // keep each XCD on a contiguous run of tiles (experts' operand rows shared in its L2); when
-    // one expert holds more than twice the mean, deal tiles round-robin over the XCDs instead
-    // (block ids go to XCDs round-robin), so a hot expert's tiles run on every XCD at once.
-    const int lid = wgrad_skewed(p.offsets, p.E, p.n) ? bid : (bid & 7) * (tot8 >> 3) + (bid >> 3);
-    if (lid >= total_tiles) return;
-    const int per_e = mtt * ntiles_n;
+    const int per_e = mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
     t.e = lid / per_e;
     const int rem = lid - t.e * per_e;
     const int mi = rem / ntiles_n;
@@ -352,7 +356,7 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
     t.k_begin = p.offsets_pad[t.e];
     t.k_len = p.offsets_pad[t.e + 1] - t.k_begin;
   }
-  // the tile is uniform; without this the descriptors below would look divergent
+  // the tile is uniform; without this the descriptors built from it would look divergent
   t.e = __builtin_amdgcn_readfirstlane(t.e);
   t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
   t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);
@@ -360,54 +364,57 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
   t.half = __builtin_amdgcn_readfirstlane(t.half);
   t.k_begin = __builtin_amdgcn_readfirstlane(t.k_begin);
   t.k_len = __builtin_amdgcn_readfirstlane(t.k_len);
-  const int nk = (t.k_len + BK - 1) / BK;
+  return t;
+}
 
-  // ---- this wave's DMA operand (waves 0, 1 -> B; 2, 3 -> A), bounded to its valid extent
-  const bool role_b = wave < 2;
-  const int h = wave & 1;
-  OpLoad ld;
+__device__ __forceinline__ TileSrc empty_src(const Params& p) {
+  TileSrc s;
+  s.r0 = make_rsrc(p.a0, 0);
+  s.r1 = s.r0;
+  s.s0 = s.r0;
+  s.s1 = s.r0;
+  s.nk = 0;
+  return s;
+}
+
+// This wave's DMA sources for tile t (waves 0, 1 -> B; 2, 3 -> A), bounded to its valid extent.
+template <int MODE>
+__device__ __forceinline__ TileSrc tile_src(const Params& p, const Tile& t, bool role_b) {
+  TileSrc s;
+  s.nk = (t.k_len + BK - 1) / BK;
   if (!role_b) {
     if constexpr (!Traits<MODE>::WGRAD) {
       const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
       const long long rem_rows = static_cast<long long>(p.n) - t.m0;
-      ld.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K);
-      ld.s0 = make_rsrc(p.a0s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
-      ld.r1 = ld.r0;
-      ld.s1 = ld.s0;
+      s.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K);
+      s.s0 = make_rsrc(p.a0s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
+      s.r1 = s.r0;
+      s.s1 = s.s0;
       if constexpr (MODE == DGRAD2) {
-        ld.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * K, rem_rows * K);
-        ld.s1 = make_rsrc(p.a1s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
+        s.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * K, rem_rows * K);
+        s.s1 = make_rsrc(p.a1s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
       }
-      ld.step = BK;
-      ld.sstep = BK / 32;
-      op_offsets(128 * h, K, K / 32, ld);
     } else {
       // [Mtot][P]: rows m0 .., columns from the expert's first padded position
       const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
       const uint8_t* base = (MODE == WGRAD_GU && t.half) ? p.a1 : p.a0;
       const uint8_t* sbase = (MODE == WGRAD_GU && t.half) ? p.a1s : p.a0s;
       const long long rem_rows = static_cast<long long>(Mtot) - t.m0;
-      ld.r0 = make_rsrc(base + static_cast<long long>(t.m0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
-      ld.s0 = make_rsrc(sbase + static_cast<long long>(t.m0) * (p.P / 32) + t.k_begin / 32,
-                        rem_rows * (p.P / 32) - t.k_begin / 32);
-      ld.r1 = ld.r0;
-      ld.s1 = ld.s0;
-      ld.step = BK;
-      ld.sstep = BK / 32;
-      op_offsets(128 * h, p.P, p.P / 32, ld);
+      s.r0 = make_rsrc(base + static_cast<long long>(t.m0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
+      s.s0 = make_rsrc(sbase + static_cast<long long>(t.m0) * (p.P / 32) + t.k_begin / 32,
+                       rem_rows * (p.P / 32) - t.k_begin / 32);
+      s.r1 = s.r0;
+      s.s1 = s.s0;
     }
   } else {
     if constexpr (MODE == FWD1) {
       const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
       const long long esoff = static_cast<long long>(t.e) * p.f * (p.d / 32);
       const long long rows = p.f - t.n0;
-      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
-      ld.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
-      ld.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
-      ld.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
-      ld.step = BK;
-      ld.sstep = BK / 32;
-      op_offsets(0, p.d, p.d / 32, ld);
+      s.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
+      s.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
+      s.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
+      s.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
     } else if constexpr (!Traits<MODE>::WGRAD) {
       // weights [E][Ntot][K'] quantised along K' (K' = K, or f per half for DGRAD2)
       const int Ntot = n_total<MODE>(p);
@@ -415,52 +422,152 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
       const long long eoff = static_cast<long long>(t.e) * Ntot * K;
       const long long esoff = static_cast<long long>(t.e) * Ntot * (K / 32);
       const long long rows = Ntot - t.n0;
-      ld.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * K, rows * K);
-      ld.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
-      ld.r1 = ld.r0;
-      ld.s1 = ld.s0;
+      s.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * K, rows * K);
+      s.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
+      s.r1 = s.r0;
+      s.s1 = s.s0;
       if constexpr (MODE == DGRAD2) {
-        ld.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * K, rows * K);
-        ld.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
+        s.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * K, rows * K);
+        s.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
       }
-      ld.step = BK;
-      ld.sstep = BK / 32;
-      op_offsets(128 * h, K, K / 32, ld);
     } else {
       const int Ntot = n_total<MODE>(p);
       const long long rem_rows = static_cast<long long>(Ntot) - t.n0;
-      ld.r0 = make_rsrc(p.b0 + static_cast<long long>(t.n0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
-      ld.s0 = make_rsrc(p.b0s + static_cast<long long>(t.n0) * (p.P / 32) + t.k_begin / 32,
-                        rem_rows * (p.P / 32) - t.k_begin / 32);
-      ld.r1 = ld.r0;
-      ld.s1 = ld.s0;
-      ld.step = BK;
-      ld.sstep = BK / 32;
-      op_offsets(128 * h, p.P, p.P / 32, ld);
+      s.r0 = make_rsrc(p.b0 + static_cast<long long>(t.n0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
+      s.s0 = make_rsrc(p.b0s + static_cast<long long>(t.n0) * (p.P / 32) + t.k_begin / 32,
+                       rem_rows * (p.P / 32) - t.k_begin / 32);
+      s.r1 = s.r0;
+      s.s1 = s.s0;
     }
   }
+  return s;
+}
+
+template <int MODE>
+__device__ __forceinline__ OpLoad op_load(const Params& p, bool role_b, int h) {
+  OpLoad ld;
+  if constexpr (Traits<MODE>::WGRAD) {
+    op_offsets(128 * h, p.P, p.P / 32, ld);
+  } else {
+    const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
+    op_offsets(role_b && MODE == FWD1 ? 0 : 128 * h, K, K / 32, ld);
+  }
+  return ld;
+}
+
+// Writes the tile's results from the accumulators (helpers in gemm_epilogue.h), staged through
+// this wave's 4 KiB of the staging area.
+template <int MODE>
+__device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (&acc)[8][8], int wm, int wn,
+                                         int lane, uint32_t stg) {
+  const int row0 = t.m0 + 128 * wm;
+  const int rows_valid = t.m_end - row0;
+  if constexpr (MODE == FWD1) {
+    gep::epi_gate_up<1>(acc, p.o0, p.o1, p.o2, p.n, p.f, row0, rows_valid, t.n0 + 64 * wn, stg, lane);
+  } else if constexpr (MODE == DGRAD1) {
+    gep::epi_swiglu_bwd<1>(acc, p.g, p.u, p.o0, p.o1, p.n, p.f, row0, rows_valid, t.n0 + 128 * wn, stg, lane);
+  } else {
+    const int Ntot = n_total<MODE>(p);
+    uint16_t* out = p.o0;
+    long long rows = p.n;
+    if constexpr (Traits<MODE>::WGRAD) {
+      const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
+      out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
+      rows = Mtot;
+    }
+    gep::epi_plain<1>(acc, out, rows, Ntot, row0, rows_valid, t.n0 + 128 * wn, stg, lane);
+  }
+}
+
+// Persistent, as the bf16 kernels: at most one workgroup per compute unit, each running a list of
+// tiles (XCD-contiguous runs, or round-robin for weight gradients with a hot expert).  The K
+// steps of a workgroup's tiles form one stream through the two-stage rings: the barrier opening
+// step g waits for its DMA, and the DMA of step g+1 (in this tile or the next one) then goes into
+// the stages step g-1 used, spread over the first MFMA rows so the wave keeps issuing MFMAs.
+template <int MODE>
+__global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- device-side schedule
+  const int NTW = n_tile_width<MODE>();
+  const int ntiles_n = (n_total<MODE>(p) + NTW - 1) / NTW;
+  MTiles mts{};
+  int total;
+  bool deal = false;
+  if constexpr (!Traits<MODE>::WGRAD) {
+    mts = mtile_scan(p.offsets, p.E);
+    total = mts.total * ntiles_n;
+  } else {
+    const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
+    total = p.E * ((Mtot + BM - 1) / BM) * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
+    deal = wgrad_skewed(p.offsets, p.E, p.n);
+  }
+  const int G = gridDim.x;   // a multiple of 8
+  const int bid = blockIdx.x;
+  int lid, lstep, lend;
+  if (deal) {
+    lid = bid;
+    lstep = G;
+    lend = total;
+  } else {
+    const int per = (total + 7) >> 3;
+    const int x = bid & 7;
+    lid = x * per + (bid >> 3);
+    lstep = G >> 3;
+    lend = (x + 1) * per < total ? (x + 1) * per : total;
+  }
+  lid = __builtin_amdgcn_readfirstlane(lid);
+  lstep = __builtin_amdgcn_readfirstlane(lstep);
+  lend = __builtin_amdgcn_readfirstlane(lend);
+  if (lid >= lend) return;
+
+  const bool role_b = wave < 2;
+  const int h = wave & 1;
+  const OpLoad ld = op_load<MODE>(p, role_b, h);
+  Tile t = tile_at<MODE>(p, mts, ntiles_n, lid);
+  TileSrc cur = tile_src<MODE>(p, t, role_b);
+  int lid_n = lid + lstep;
+  Tile tn = t;
+  TileSrc nxt = empty_src(p);
+  if (lid_n < lend) {
+    tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
+    nxt = tile_src<MODE>(p, tn, role_b);
+  }
+
+  const uint32_t ring = lds_addr(lds_ring);
+  const uint32_t stg = ring + STG_RING + wave * STG_BYTES;
+  // per-lane fragment addresses: row l % 16 of each 16-row fragment, chunks l/16 and 4 + l/16
+  const uint32_t kc0 = kc_off(lane & 15, lane >> 4), kc1 = kc_off(lane & 15, 4 + (lane >> 4));
+  const uint32_t srow = 16 * (lane & 15) + 4 * (lane >> 4);   // dword slot (row, K block l/16)
+  const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
+  uint8_t* const dst0 = lds_ring + (role_b ? B_RING : A_RING) + h * (OP_BYTES / 2);
+  uint8_t* const sdst0 = lds_ring + (role_b ? SB_RING : SA_RING) + h * (SC_BYTES / 2);
 
   f32x4 acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (nk > 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pin_acc_row(acc[i]);
-    asm volatile("s_nop 7" ::: "memory");
-    // per-lane fragment addresses: row l % 16 of each 16-row fragment, chunks l/16 and 4 + l/16
-    const uint32_t kc0 = kc_off(lane & 15, lane >> 4), kc1 = kc_off(lane & 15, 4 + (lane >> 4));
-    const uint32_t srow = 16 * (lane & 15) + 4 * (lane >> 4);   // dword slot (row, K block l/16)
-    const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
-    const uint32_t ring = lds_addr(lds_ring);
-    issue_stage<MODE>(p, ld, role_b, h, 0, nk, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      // tile kt in LDS everywhere; every wave is done with tile kt-1, whose stages take tile kt+1
+  zero_acc(acc);
+  // `ready`: step 0 of the current tile has been issued into stage st.  An expert without rows
+  // (weight gradients) has an all-zero tile and no steps: nothing of it is streamed, and the
+  // step 0 of the tile after it is issued when that tile becomes current.
+  int st = 0, kt = 0;
+  bool ready = false;
+  for (;;) {
+    if (!ready && cur.nk > 0) {
+      issue_part<0, 16, 0, 8>(ld, step_src<MODE>(p, ld, cur, role_b, h, 0), dst0 + st * OP_BYTES,
+                              sdst0 + st * SC_BYTES);
+      ready = true;
+    }
+    bool next_ready = false;
+    while (kt < cur.nk) {
+      // step kt in LDS everywhere; every wave is done with step kt-1, whose stages take the next
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      issue_stage<MODE>(p, ld, role_b, h, kt + 1, nk, st ^ 1);
+      const bool here = kt + 1 < cur.nk;
+      next_ready = !here && nxt.nk > 0;
+      const StepSrc ns = here ? step_src<MODE>(p, ld, cur, role_b, h, kt + 1) : step_src<MODE>(p, ld, nxt, role_b, h, 0);
+      uint8_t* const dst = dst0 + (st ^ 1) * OP_BYTES;
+      uint8_t* const sdst = sdst0 + (st ^ 1) * SC_BYTES;
       const uint32_t a_base = ring + A_RING + st * OP_BYTES, b_base = ring + B_RING + st * OP_BYTES;
       const uint32_t sa_base = ring + SA_RING + st * SC_BYTES, sb_base = ring + SB_RING + st * SC_BYTES;
       i32x8 fa[8], fb[2];
@@ -471,76 +578,36 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
       int live = 0xff;
       if constexpr (Traits<MODE>::WGRAD) live = (kt * BK + 32 * (lane >> 4) < t.k_len) ? 0xff : 0;
       static_for<0, 8>([&](auto i) {
-        if constexpr (i < 7) read_frag<bfrag_c<MODE, i + 1>()>(fb[(i + 1) & 1], xb[(i + 1) & 1], b_base, sb_base, kc0, kc1, srow, qb);
+        // the next step's DMA, 6 instructions in each of the first four rows
+        if constexpr (i < 4) issue_part<4 * i, 4, 2 * i, 2>(ld, ns, dst, sdst);
+        if constexpr (i < 7)
+          read_frag<bfrag_c<MODE, i + 1>()>(fb[(i + 1) & 1], xb[(i + 1) & 1], b_base, sb_base, kc0, kc1, srow, qb);
         lgkm_wait<i < 7 ? 3 : 0>(fb[i & 1], xb[i & 1], fa, xa);
         const int sbv = xb[i & 1] & live;
         static_for<0, 8>([&](auto j) { mfma_acc(acc[i][j], fb[i & 1], fa[j], sbv, xa[j] & live); });
       });
+      st ^= 1;
+      ++kt;
     }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
-  }
-
-  const int rl = lane & 15;
-  const int cq = 4 * (lane >> 4);
-  if constexpr (MODE == FWD1) {
-    static_for<0, 8>([&](auto j) {
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row >= t.m_end) return;
-      static_for<0, 4>([&](auto i) {
-        const int col = t.n0 + 64 * wn + 16 * i + cq;
-        if (col >= p.f) return;
-        const f32x4 gv = acc[i][j], uv = acc[i + 4][j];
-        float av[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
-        const long long o = static_cast<long long>(row) * p.f + col;
-        st4(p.o0 + o, gv[0], gv[1], gv[2], gv[3]);
-        st4(p.o1 + o, uv[0], uv[1], uv[2], uv[3]);
-        st4(p.o2 + o, av[0], av[1], av[2], av[3]);
-      });
-    });
-  } else if constexpr (MODE == DGRAD1) {
-    static_for<0, 8>([&](auto j) {
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row >= t.m_end) return;
-      static_for<0, 8>([&](auto i) {
-        const int col = t.n0 + 128 * wn + 16 * i + cq;
-        if (col >= p.f) return;
-        const long long o = static_cast<long long>(row) * p.f + col;
-        const uint2 gw = *reinterpret_cast<const uint2*>(p.g + o);
-        const uint2 uw = *reinterpret_cast<const uint2*>(p.u + o);
-        const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
-        const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
-        const f32x4 dav = acc[i][j];
-        float dg[4], du[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sg = sigmoidf_(gv[q]);
-          dg[q] = dav[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-          du[q] = dav[q] * gv[q] * sg;
-        }
-        st4(p.o0 + o, dg[0], dg[1], dg[2], dg[3]);
-        st4(p.o1 + o, du[0], du[1], du[2], du[3]);
-      });
-    });
-  } else {
-    const int Ntot = n_total<MODE>(p);
-    uint16_t* out = p.o0;
-    if constexpr (Traits<MODE>::WGRAD) {
-      const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
-      out = (MODE == WGRAD_GU && t.half ? p.o1 : p.o0) + static_cast<long long>(t.e) * Mtot * Ntot;
+    // ---- tile done (or empty): the last MFMA results settle before the epilogue reads them
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+    epilogue<MODE>(p, t, acc, wm, wn, lane, stg);
+    if (lid_n >= lend) break;
+    zero_acc(acc);
+    ready = next_ready;
+    t = tn;
+    cur = nxt;
+    kt = 0;
+    lid_n += lstep;
+    if (lid_n < lend) {
+      tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
+      nxt = tile_src<MODE>(p, tn, role_b);
+    } else {
+      nxt = empty_src(p);
     }
-    static_for<0, 8>([&](auto j) {
-      const int row = t.m0 + 128 * wm + 16 * j + rl;
-      if (row >= t.m_end) return;
-      static_for<0, 8>([&](auto i) {
-        const int col = t.n0 + 128 * wn + 16 * i + cq;
-        if (col >= Ntot) return;
-        const f32x4 v = acc[i][j];
-        st4(out + static_cast<long long>(row) * Ntot + col, v[0], v[1], v[2], v[3]);
-      });
-    });
   }
+  // no LDS-DMA may still be writing when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
 inline long long grid_upper(int mode, int E, int n, int d, int f) {
@@ -556,8 +623,9 @@ inline long long grid_upper(int mode, int E, int n, int d, int f) {
 
 template <int MODE>
 int launch(const Params& p, hipStream_t s) {
-  const long long g = (grid_upper(MODE, p.E, p.n, p.d, p.f) + 7) / 8 * 8;
-  MOE_REQUIRE(g < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many tiles");
+  const long long upper = grid_upper(MODE, p.E, p.n, p.d, p.f);
+  MOE_REQUIRE(upper < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many tiles");
+  const int g = gemm_workgroups(upper);
   // every buffer offset the kernel forms stays below 2^31 bytes
   const long long big = static_cast<long long>(p.n) * (p.d > p.f ? p.d : p.f);
   const long long wbig = static_cast<long long>(p.d) * p.f;

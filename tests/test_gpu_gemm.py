@@ -256,3 +256,40 @@ def test_bf16_few_workgroups_bit_identical(case, monkeypatch):
     names = ("g", "u", "a", "yexp", "dg", "du", "dxp", "dw_gate", "dw_up", "dw_down")
     for nm, r, o in zip(names, ref, got):
         assert np.array_equal(r, o), f"{nm}: 8-workgroup launch differs from the default launch"
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=case_id)
+def test_mxfp8_few_workgroups_bit_identical(case, monkeypatch):
+    """MXFP8 products with 8 workgroups (many tiles each, empty experts among them) give the
+    default launch's bytes exactly."""
+    from expert_ffn_layer_top_amd import ops
+    p = problem(**case)
+    x_d = bf16_to_dev(p["x"])
+    xq, xs = ops.mxfp8_quantize(x_d, 0)
+    xpq, xps = ops.permute(xq, i32_to_dev(p["dest"]), x_scale=xs)
+    Wd = {w: bf16_to_dev(p[w]) for w in ("wg", "wu", "wd")}
+    Q = {}
+    for w in ("wg", "wu", "wd"):
+        Q[w] = ops.mxfp8_quantize(Wd[w], 0)
+        Q[w + "_t"] = ops.mxfp8_quantize(Wd[w], 1)
+    off_d = i32_to_dev(p["off"])
+    offp_d = i32_to_dev(p["offp"])
+    rt_d = i32_to_dev(p["row_token"])
+    dy_d = bf16_to_dev(p["dyexp"])
+
+    def run():
+        g, u, a, y = ops.grouped_gemm_swiglu(xpq, off_d, Q["wg"][0], Q["wu"][0], Q["wd"][0],
+                                             scales=(xps, Q["wg"][1], Q["wu"][1], Q["wd"][1]))
+        b = ops.grouped_gemm_swiglu_bwd(x_d, g, u, a, dy_d, off_d, Q["wg_t"][0], Q["wu_t"][0], Q["wd_t"][0],
+                                        scales=(Q["wg_t"][1], Q["wu_t"][1], Q["wd_t"][1]),
+                                        offsets_pad=offp_d, row_token=rt_d)
+        return [bits(t) for t in (g, u, a, y, b["dg"], b["du"], b["dxp"], b["dw_gate"], b["dw_up"], b["dw_down"])]
+
+    note(f"gg mxfp8 default launch {case}")
+    ref = run()
+    monkeypatch.setenv("MOE_GG_WORKGROUPS", "8")
+    note(f"gg mxfp8 8 workgroups {case}")
+    got = run()
+    names = ("g", "u", "a", "yexp", "dg", "du", "dxp", "dw_gate", "dw_up", "dw_down")
+    for nm, r, o in zip(names, ref, got):
+        assert np.array_equal(r, o), f"{nm}: 8-workgroup launch differs from the default launch"
