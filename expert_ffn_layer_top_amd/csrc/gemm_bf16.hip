@@ -51,6 +51,7 @@
 
 #include "common.h"
 #include "gemm_epilogue.h"
+#include "gemm_sched.h"
 
 namespace moe {
 namespace gg {
@@ -430,75 +431,7 @@ constexpr int STG_BYTES = 8192;
 
 // ---------------------------------------------------------------- the kernel
 
-// m-tile prefix over experts, computed by every wave from one round of loads (no LDS: the whole
-// LDS is the operand rings).  Lane l holds experts l, l + 64, l + 128, l + 192.
-struct MTiles {
-  int tiles[4], excl[4];
-  int total;
-};
-
-__device__ __forceinline__ MTiles mtile_scan(const int32_t* __restrict__ offsets, int E) {
-  const int lane = threadIdx.x & 63;
-  MTiles m;
-  int lo[4], hi[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ex = 64 * r + lane;
-    lo[r] = ex < E ? offsets[ex] : 0;
-    hi[r] = ex < E ? offsets[ex + 1] : 0;
-  }
-  int carry = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tiles = (hi[r] - lo[r] + BM - 1) / BM;
-    int incl = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    m.tiles[r] = tiles;
-    m.excl[r] = carry + incl - tiles;
-    carry += __shfl(incl, 63, 64);
-  }
-  m.total = __builtin_amdgcn_readfirstlane(carry);
-  return m;
-}
-
-// True when some expert's row count exceeds twice the mean (n / E, rounded up).
-__device__ __forceinline__ bool wgrad_skewed(const int32_t* __restrict__ offsets, int E, int n) {
-  const int lane = threadIdx.x & 63;
-  int cmax = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ex = 64 * r + lane;
-    const int c = ex < E ? offsets[ex + 1] - offsets[ex] : 0;
-    cmax = c > cmax ? c : cmax;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int v = __shfl_xor(cmax, o, 64);
-    cmax = v > cmax ? v : cmax;
-  }
-  cmax = __builtin_amdgcn_readfirstlane(cmax);
-  return cmax > 2 * ((n + E - 1) / E);
-}
-
-// The expert owning global m-tile mt (< total) and that expert's first m-tile.
-__device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int& first) {
-  const int lane = threadIdx.x & 63;
-  e = 0;
-  first = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const unsigned long long hit = __ballot(m.tiles[r] > 0 && m.excl[r] <= mt && mt < m.excl[r] + m.tiles[r]);
-    if (hit) {
-      const int src = __ffsll(static_cast<long long>(hit)) - 1;
-      e = 64 * r + src;
-      first = __shfl(m.excl[r], src, 64);
-    }
-  }
-}
+using gsched::MTiles;
 
 // Writes the tile's results from the accumulators (helpers in gemm_epilogue.h): SwiGLU on the
 // gate/up product, its backward on the down dgrad, plain stores otherwise.
@@ -536,7 +469,7 @@ __device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int 
     const int mt_glob = lid / ntiles_n;
     const int nt = lid - mt_glob * ntiles_n;
     int e, first;
-    mtile_find(mts, mt_glob, e, first);
+    gsched::mtile_find(mts, mt_glob, e, first);
     t.e = e;
     t.m0 = p.offsets[e] + (mt_glob - first) * BM;
     t.m_end = p.offsets[e + 1];
@@ -716,12 +649,12 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   int total;
   bool deal = false;
   if constexpr (!Traits<MODE>::WGRAD) {
-    mts = mtile_scan(p.offsets, p.E);
+    mts = gsched::mtile_scan<BM>(p.offsets, p.E);
     total = mts.total * ntiles_n;
   } else {
     const int mt = (m_total_wgrad<MODE>(p) + BM - 1) / BM;
     total = p.E * mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
-    deal = wgrad_skewed(p.offsets, p.E, p.n);
+    deal = gsched::wgrad_skewed(p.offsets, p.E, p.n);
   }
   const int G = gridDim.x;     // a multiple of 8
   const int bid = blockIdx.x;

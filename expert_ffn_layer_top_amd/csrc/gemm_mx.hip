@@ -20,9 +20,9 @@
 // waves of 128 x 128 (256 fp32 accumulators per lane in AGPRs), K stages of 128 elements = one
 // 128-byte row per operand row, XOR-swizzled 16-byte chunks, LDS-DMA buffer loads.  Waves 0-1
 // stream the N-side operand and waves 2-3 the M-side one, two stages each; each stage also
-// carries the 4 scale bytes of every row.  The barrier opening tile
-// kt sits at the start of step kt: past it every wave has finished tile kt-1, so the DMA of tile
-// kt+1 goes into its stages while tile kt is consumed.  The MFMA lane layout (checked on the
+// carries the 4 scale bytes of every row.  The barrier opening K step g sits at its start: past
+// it every wave has finished step g-1, so the DMA of step g+1 goes into that step's stages while
+// step g is consumed.  The MFMA lane layout (checked on the
 // device): lane l holds row l % 16, K bytes 16*(l/16) .. +15 and 64 + 16*(l/16) .. +15 of the
 // 128-wide step, and supplies the scale of row l % 16, K block l/16.
 //
@@ -34,6 +34,7 @@
 
 #include "common.h"
 #include "gemm_epilogue.h"
+#include "gemm_sched.h"
 
 namespace moe {
 namespace gmx {
@@ -127,73 +128,7 @@ __device__ __forceinline__ int k_total(const Params& p) {
   return 0;
 }
 
-// m-tile prefix over experts from one round of loads (lane l holds experts l + 64 r).
-struct MTiles {
-  int tiles[4], excl[4];
-  int total;
-};
-
-__device__ __forceinline__ MTiles mtile_scan(const int32_t* __restrict__ offsets, int E) {
-  const int lane = threadIdx.x & 63;
-  MTiles m;
-  int lo[4], hi[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ex = 64 * r + lane;
-    lo[r] = ex < E ? offsets[ex] : 0;
-    hi[r] = ex < E ? offsets[ex + 1] : 0;
-  }
-  int carry = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tiles = (hi[r] - lo[r] + BM - 1) / BM;
-    int incl = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    m.tiles[r] = tiles;
-    m.excl[r] = carry + incl - tiles;
-    carry += __shfl(incl, 63, 64);
-  }
-  m.total = __builtin_amdgcn_readfirstlane(carry);
-  return m;
-}
-
-// True when some expert's row count exceeds twice the mean (n / E, rounded up).
-__device__ __forceinline__ bool wgrad_skewed(const int32_t* __restrict__ offsets, int E, int n) {
-  const int lane = threadIdx.x & 63;
-  int cmax = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ex = 64 * r + lane;
-    const int c = ex < E ? offsets[ex + 1] - offsets[ex] : 0;
-    cmax = c > cmax ? c : cmax;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int v = __shfl_xor(cmax, o, 64);
-    cmax = v > cmax ? v : cmax;
-  }
-  cmax = __builtin_amdgcn_readfirstlane(cmax);
-  return cmax > 2 * ((n + E - 1) / E);
-}
-
-__device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int& first) {
-  const int lane = threadIdx.x & 63;
-  e = 0;
-  first = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const unsigned long long hit = __ballot(m.tiles[r] > 0 && m.excl[r] <= mt && mt < m.excl[r] + m.tiles[r]);
-    if (hit) {
-      const int src = __ffsll(static_cast<long long>(hit)) - 1;
-      e = 64 * r + src;
-      first = __shfl(m.excl[r], src, 64);
-    }
-  }
-}
+using gsched::MTiles;
 
 // One wave's share of an operand stage: 128 rows x 128 bytes of data (16 DMA instructions of
 // 16 bytes per lane) and the rows' scale bytes (8 byte-DMA instructions).  The offsets depend on
@@ -333,7 +268,7 @@ __device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int 
     const int mt_glob = lid / ntiles_n;
     const int nt = lid - mt_glob * ntiles_n;
     int e, first;
-    mtile_find(mts, mt_glob, e, first);
+    gsched::mtile_find(mts, mt_glob, e, first);
     t.e = e;
     t.m0 = p.offsets[e] + (mt_glob - first) * BM;
     t.m_end = p.offsets[e + 1];
@@ -498,12 +433,12 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
   int total;
   bool deal = false;
   if constexpr (!Traits<MODE>::WGRAD) {
-    mts = mtile_scan(p.offsets, p.E);
+    mts = gsched::mtile_scan<BM>(p.offsets, p.E);
     total = mts.total * ntiles_n;
   } else {
     const int Mtot = (MODE == WGRAD_DOWN) ? p.d : p.f;
     total = p.E * ((Mtot + BM - 1) / BM) * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
-    deal = wgrad_skewed(p.offsets, p.E, p.n);
+    deal = gsched::wgrad_skewed(p.offsets, p.E, p.n);
   }
   const int G = gridDim.x;   // a multiple of 8
   const int bid = blockIdx.x;

@@ -26,8 +26,8 @@ CSRC = os.path.join(PKG, "csrc")
 
 # the files a grouped-GEMM kernel is compiled from, per dtype
 SOURCES = {
-    "bf16": ("gemm_bf16.hip", "gemm_epilogue.h", "common.h"),
-    "mxfp8": ("gemm_mx.hip", "gemm_epilogue.h", "common.h", "mx_common.h"),
+    "bf16": ("gemm_bf16.hip", "gemm_epilogue.h", "gemm_sched.h", "common.h"),
+    "mxfp8": ("gemm_mx.hip", "gemm_epilogue.h", "gemm_sched.h", "common.h", "mx_common.h"),
 }
 
 # rocprofv3 kernel name of each grouped-GEMM call (the kernel template's mode number)
