@@ -113,7 +113,9 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
 
 def backward(ctx, weights, dy, events=None):
     """Layer backward from dy [T, d] bf16.  Returns dict with dx, d_logits, dw_gate, dw_up,
-    dw_down (and dw_r, dx_router when the layer owns its router) plus the intermediates.
+    dw_down (and dw_r, dx_router when the layer owns its router) plus the intermediates (under
+    MXFP8, "mx" holds the quantised backward operands: row blocks dyq/dgq/duq, grouped token
+    blocks dyT/aT/dgT/duT/xT, each with its scales).
     events: as for `forward`."""
     out = {}
     with _Span(events, "combine_bwd"):
@@ -154,6 +156,8 @@ def backward(ctx, weights, dy, events=None):
         with _Span(events, "wgrad_gate_up"):
             dw_gate, dw_up = ops.grouped_gemm_wgrad_gate_up(dgT, duT, xT, off, n, offsets_pad=pad,
                                                             scales=(dgTs, duTs, xTs))
+        out["mx"] = dict(dyq=dyq, dys=dys, dyT=dyT, dyTs=dyTs, aT=aT, aTs=aTs, dgq=dgq, dgs=dgs, duq=duq,
+                         dus=dus, dgT=dgT, dgTs=dgTs, duT=duT, duTs=duTs, xT=xT, xTs=xTs)
     out.update(dg=dg, du=du, dxp=dxp, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
     E = ctx["logits"].shape[1]
     with _Span(events, "route_bwd"):
