@@ -28,6 +28,7 @@ constexpr int kRouteBlock = 64;    // tokens per block (one bit each in a 64-bit
 constexpr int kGroup = 16;         // lanes per token
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
+constexpr int kScanBatch = 16;   // hist loads in flight per scan thread
 
 // Order-preserving map of a float to uint32 (larger float -> larger key); -0 is folded to +0
 // so that equal logits compare equal.
@@ -163,20 +164,35 @@ __global__ __launch_bounds__(1024) void route_scan(int32_t* __restrict__ hist, i
   const int per = (nb + nparts - 1) / nparts;
   const int b0 = min(nb, part * per);
   const int b1 = min(nb, b0 + per);
+  // the run's entries are read in batches of kScanBatch independent loads; a run that fits one
+  // batch stays in registers for the rewrite
+  int vals[kScanBatch];
   int sum = 0;
-  if (e < E) {
-    for (int b = b0; b < b1; ++b) sum += hist[static_cast<long long>(b) * E + e];
+  for (int c0 = b0; c0 < b1; c0 += kScanBatch) {
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      vals[i] = (e < E && c0 + i < b1) ? hist[static_cast<long long>(c0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) sum += vals[i];
   }
   s_part[threadIdx.x] = sum;
   __syncthreads();
   int run = 0;
   for (int q = 0; q < part; ++q) run += s_part[(q << ep_log2) + e];
   if (e < E) {
-    for (int b = b0; b < b1; ++b) {
-      const long long o = static_cast<long long>(b) * E + e;
-      const int v = hist[o];
-      hist[o] = run;
-      run += v;
+    for (int c0 = b0; c0 < b1; c0 += kScanBatch) {
+      if (b1 - b0 > kScanBatch) {
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i)
+          vals[i] = c0 + i < b1 ? hist[static_cast<long long>(c0 + i) * E + e] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (c0 + i < b1) {
+          hist[static_cast<long long>(c0 + i) * E + e] = run;
+          run += vals[i];
+        }
+      }
     }
   }
   if (threadIdx.x < kMaxE) {

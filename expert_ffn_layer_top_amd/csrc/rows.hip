@@ -5,10 +5,13 @@
 // on the GPU": routed token rows are written straight into the experts' input buffers; the
 // combine returns each token the gate-weighted sum of its experts' outputs.
 //
-// Layout of the work: one wave per token.  The wave reads the token's k destination rows once
-// (lanes j < k load dest[t, j], then every lane gets all k by shuffles), then streams the row
-// in 16-byte chunks (lane c handles chunks c, c + 64, ...), so every global access is a fully
-// coalesced 1 KiB wave transaction.  Accumulation is fp32 in slot order j = 0..k-1.
+// Layout of the work: the permute, the combine and the permute backward give each wave one
+// 1 KiB segment of one token's row (lane c moves 16-byte chunk c of it), so every global access
+// is a fully coalesced 1 KiB wave transaction, each lane has its k row accesses in flight at once,
+// and the many small work items keep a launch's last round short.  The token's k destination
+// rows (and gates) are read once per wave (lanes j < k load dest[t, j]) and kept in scalar
+// registers.  The combine backward, which also reduces whole rows to dot products, gives each
+// wave one token.  Accumulation is fp32 in slot order j = 0..k-1.
 #include "common.h"
 
 namespace moe {
@@ -17,52 +20,72 @@ namespace {
 constexpr int kMaxK = 16;
 constexpr int kWaves = 4;   // tokens per 256-thread block
 
-__device__ __forceinline__ void load_dest(const int32_t* __restrict__ dest, long long t, int k, int lane,
-                                          long long (&rows)[kMaxK]) {
-  const int mine = (lane < k) ? dest[t * k + lane] : 0;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) rows[j] = __shfl(mine, j, 64);
-}
-
-// Chunks per lane per batch: every lane issues all loads of a batch before using any, so each
-// wave keeps several 1 KiB transactions per row in flight.  The two backward kernels gain from
-// it; permute and combine keep one chunk per batch, where the higher occupancy serves better.
-constexpr int kUFwd = 1;
+// Chunks per lane per batch in the combine backward (one wave per token, for its row dot
+// products): every lane issues all loads of a batch before using any, so each wave keeps several
+// 1 KiB transactions per row in flight.
 constexpr int kUBwd = 4;
 
+// Work items of the permute, the combine and the permute backward: one 1 KiB segment (64 lanes
+// x 16 bytes) of one token's row per wave, four waves to a 256-thread block, the segments of a
+// token on consecutive waves.  Small items keep the last round of a launch short; each lane keeps
+// its k row loads in flight together.
+constexpr int kSegChunks = 64;   // 16-byte chunks per segment
+
+struct SegItem {
+  long long t;   // token (wave-uniform)
+  int c;         // this lane's 16-byte chunk within the row
+};
+
+__device__ __forceinline__ SegItem seg_item(int nseg) {
+  const long long i = static_cast<long long>(blockIdx.x) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  SegItem it;
+  it.t = i / nseg;
+  it.c = static_cast<int>(i - it.t * nseg) * kSegChunks + (threadIdx.x & 63);
+  return it;
+}
+
+// The token's k destination rows (and optionally its k gates), as wave-uniform scalars.
+template <int KM>
+__device__ __forceinline__ void dest_rows(const int32_t* __restrict__ dest, long long t, int k, int (&rows)[KM]) {
+  const int lane = threadIdx.x & 63;
+  const int mine = (lane < k) ? dest[t * k + lane] : 0;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) rows[j] = __builtin_amdgcn_readlane(mine, j);
+}
+
+template <int KM>
+__device__ __forceinline__ void gates_of(const float* __restrict__ gate, long long t, int k, float (&g)[KM]) {
+  const int lane = threadIdx.x & 63;
+  const float mine = (lane < k) ? gate[t * k + lane] : 0.f;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) g[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), j));
+}
+
+// xp[dest[t,j]] = x[t] for rows of `pitch` bytes (bf16, or E4M3 bytes plus a scale row of
+// `spitch` bytes, copied by the token's first segment).
+template <int KM>
 __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
-                                                      const int32_t* __restrict__ dest, int T, int k,
+                                                      const int32_t* __restrict__ dest, int T, int k, int nseg,
                                                       long long pitch, long long spitch, uint8_t* __restrict__ xp,
                                                       uint8_t* __restrict__ xps) {
-  const long long t = static_cast<long long>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  long long rows[kMaxK];
-  load_dest(dest, t, k, lane, rows);
+  const SegItem it = seg_item(nseg);
+  if (it.t >= T) return;
+  int rows[KM];
+  dest_rows<KM>(dest, it.t, k, rows);
   const int chunks = static_cast<int>(pitch / 16);
-  const uint4* src = reinterpret_cast<const uint4*>(x + t * pitch);
-  for (int c0 = lane; c0 < chunks; c0 += 64 * kUFwd) {
-    uint4 v[kUFwd];
+  if (it.c < chunks) {
+    const uint4 v = reinterpret_cast<const uint4*>(x + it.t * pitch)[it.c];
 #pragma unroll
-    for (int u = 0; u < kUFwd; ++u)
-      if (c0 + 64 * u < chunks) v[u] = src[c0 + 64 * u];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        uint4* dst = reinterpret_cast<uint4*>(xp + rows[j] * pitch);
-#pragma unroll
-        for (int u = 0; u < kUFwd; ++u)
-          if (c0 + 64 * u < chunks) dst[c0 + 64 * u] = v[u];
-      }
-    }
+    for (int j = 0; j < KM; ++j)
+      if (j < k) reinterpret_cast<uint4*>(xp + rows[j] * pitch)[it.c] = v;
   }
-  if (xs != nullptr) {
+  if (xs != nullptr && it.c < kSegChunks) {
     // scale rows: d/32 bytes, an even count; copied in 2-byte units
-    const uint16_t* sc = reinterpret_cast<const uint16_t*>(xs + t * spitch);
-    for (int c = lane; c < spitch / 2; c += 64) {
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(xs + it.t * spitch);
+    for (int c = it.c; c < spitch / 2; c += 64) {
       const uint16_t v = sc[c];
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j)
+      for (int j = 0; j < KM; ++j)
         if (j < k) reinterpret_cast<uint16_t*>(xps + rows[j] * spitch)[c] = v;
     }
   }
@@ -79,68 +102,52 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
 }
 
 // y[t] = sum_j gate[t,j] * yexp[dest[t,j]]   (bf16 rows of d elements), fp32 in slot order
+template <int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ yexp, const float* __restrict__ gate,
-                                                      const int32_t* __restrict__ dest, int T, int d, int k,
+                                                      const int32_t* __restrict__ dest, int T, int d, int k, int nseg,
                                                       uint16_t* __restrict__ y) {
-  const long long t = static_cast<long long>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  long long rows[kMaxK];
-  load_dest(dest, t, k, lane, rows);
-  const float gmine = (lane < k) ? gate[t * k + lane] : 0.f;
-  float g[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) g[j] = __shfl(gmine, j, 64);
+  const SegItem it = seg_item(nseg);
+  if (it.t >= T) return;
+  int rows[KM];
+  float g[KM];
+  dest_rows<KM>(dest, it.t, k, rows);
+  gates_of<KM>(gate, it.t, k, g);
   const int chunks = d / 8;
-  for (int c0 = lane; c0 < chunks; c0 += 64 * kUFwd) {
-    float acc[kUFwd][8];
+  if (it.c >= chunks) return;
+  uint4 v[KM];
 #pragma unroll
-    for (int u = 0; u < kUFwd; ++u)
+  for (int j = 0; j < KM; ++j)
+    if (j < k) v[j] = reinterpret_cast<const uint4*>(yexp + static_cast<long long>(rows[j]) * d)[it.c];
+  float acc[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        const uint4* row = reinterpret_cast<const uint4*>(yexp + rows[j] * d);
-        uint4 v[kUFwd];
+  for (int j = 0; j < KM; ++j) {
+    if (j < k) {
+      float f[8];
+      unpack8(v[j], f);
 #pragma unroll
-        for (int u = 0; u < kUFwd; ++u)
-          if (c0 + 64 * u < chunks) v[u] = row[c0 + 64 * u];
-#pragma unroll
-        for (int u = 0; u < kUFwd; ++u) {
-          if (c0 + 64 * u < chunks) {
-            float f[8];
-            unpack8(v[u], f);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g[j], f[i], acc[u][i]);
-          }
-        }
-      }
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
     }
-    uint4* out = reinterpret_cast<uint4*>(y + t * d);
-#pragma unroll
-    for (int u = 0; u < kUFwd; ++u)
-      if (c0 + 64 * u < chunks) out[c0 + 64 * u] = pack8(acc[u]);
   }
+  reinterpret_cast<uint4*>(y + it.t * d)[it.c] = pack8(acc);
 }
 
 // dyexp[dest[t,j]] = bf16(gate[t,j] * dy[t]);  d_gate[t,j] = <dy[t], yexp[dest[t,j]]>
+template <int KM>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ yexp,
                                                           const float* __restrict__ gate, const int32_t* __restrict__ dest,
                                                           int T, int d, int k, uint16_t* __restrict__ dyexp,
                                                           float* __restrict__ dgate) {
-  const long long t = static_cast<long long>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const long long t = static_cast<long long>(blockIdx.x) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
-  long long rows[kMaxK];
-  load_dest(dest, t, k, lane, rows);
-  const float gmine = (lane < k) ? gate[t * k + lane] : 0.f;
-  float g[kMaxK], dot[kMaxK];
+  int rows[KM];
+  float g[KM], dot[KM];
+  dest_rows<KM>(dest, t, k, rows);
+  gates_of<KM>(gate, t, k, g);
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    g[j] = __shfl(gmine, j, 64);
-    dot[j] = 0.f;
-  }
+  for (int j = 0; j < KM; ++j) dot[j] = 0.f;
   const int chunks = d / 8;
   const uint4* dyrow = reinterpret_cast<const uint4*>(dy + t * d);
   for (int c0 = lane; c0 < chunks; c0 += 64 * kUBwd) {
@@ -149,10 +156,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
     for (int u = 0; u < kUBwd; ++u)
       if (c0 + 64 * u < chunks) vdy[u] = dyrow[c0 + 64 * u];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j < k) {
-        const uint4* yrow = reinterpret_cast<const uint4*>(yexp + rows[j] * d);
-        uint4* orow = reinterpret_cast<uint4*>(dyexp + rows[j] * d);
+        const uint4* yrow = reinterpret_cast<const uint4*>(yexp + static_cast<long long>(rows[j]) * d);
+        uint4* orow = reinterpret_cast<uint4*>(dyexp + static_cast<long long>(rows[j]) * d);
         uint4 vy[kUBwd];
 #pragma unroll
         for (int u = 0; u < kUBwd; ++u)
@@ -176,60 +183,48 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
   }
   float mine = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     const float s = wave_sum(dot[j]);   // every lane takes part, also for j >= k (zeros)
     if (lane == j) mine = s;
   }
   if (lane < k) dgate[t * k + lane] = mine;
 }
 
-// dx[t] = sum_j dxp[dest[t,j]] (+ addend[t])
+// dx[t] = sum_j dxp[dest[t,j]] (+ addend[t]), fp32 in slot order after the addend
+template <int KM>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(const uint16_t* __restrict__ dxp, const int32_t* __restrict__ dest,
-                                                          int T, int d, int k, const float* __restrict__ addend,
+                                                          int T, int d, int k, int nseg, const float* __restrict__ addend,
                                                           uint16_t* __restrict__ dx) {
-  const long long t = static_cast<long long>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  long long rows[kMaxK];
-  load_dest(dest, t, k, lane, rows);
+  const SegItem it = seg_item(nseg);
+  if (it.t >= T) return;
+  int rows[KM];
+  dest_rows<KM>(dest, it.t, k, rows);
   const int chunks = d / 8;
-  for (int c0 = lane; c0 < chunks; c0 += 64 * kUBwd) {
-    float acc[kUBwd][8];
+  if (it.c >= chunks) return;
+  uint4 v[KM];
 #pragma unroll
-    for (int u = 0; u < kUBwd; ++u) {
+  for (int j = 0; j < KM; ++j)
+    if (j < k) v[j] = reinterpret_cast<const uint4*>(dxp + static_cast<long long>(rows[j]) * d)[it.c];
+  float acc[8];
+  if (addend != nullptr) {
+    const float4* a = reinterpret_cast<const float4*>(addend + it.t * d + 8 * it.c);
+    const float4 a0 = a[0], a1 = a[1];
+    acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
+    acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
+  } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
-      if (addend != nullptr && c0 + 64 * u < chunks) {
-        const float4* a = reinterpret_cast<const float4*>(addend + t * d + 8 * (c0 + 64 * u));
-        const float4 a0 = a[0], a1 = a[1];
-        acc[u][0] = a0.x; acc[u][1] = a0.y; acc[u][2] = a0.z; acc[u][3] = a0.w;
-        acc[u][4] = a1.x; acc[u][5] = a1.y; acc[u][6] = a1.z; acc[u][7] = a1.w;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        const uint4* row = reinterpret_cast<const uint4*>(dxp + rows[j] * d);
-        uint4 v[kUBwd];
-#pragma unroll
-        for (int u = 0; u < kUBwd; ++u)
-          if (c0 + 64 * u < chunks) v[u] = row[c0 + 64 * u];
-#pragma unroll
-        for (int u = 0; u < kUBwd; ++u) {
-          if (c0 + 64 * u < chunks) {
-            float f[8];
-            unpack8(v[u], f);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[u][i] += f[i];
-          }
-        }
-      }
-    }
-    uint4* out = reinterpret_cast<uint4*>(dx + t * d);
-#pragma unroll
-    for (int u = 0; u < kUBwd; ++u)
-      if (c0 + 64 * u < chunks) out[c0 + 64 * u] = pack8(acc[u]);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   }
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < k) {
+      float f[8];
+      unpack8(v[j], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+    }
+  }
+  reinterpret_cast<uint4*>(dx + it.t * d)[it.c] = pack8(acc);
 }
 
 int check_rows(int T, int d, int k) {
@@ -241,6 +236,20 @@ int check_rows(int T, int d, int k) {
 }
 
 unsigned grid_for(int T) { return static_cast<unsigned>((T + kWaves - 1) / kWaves); }
+
+// Segments per row of `chunks` 16-byte chunks, and the launch grid for T tokens of them.
+int segs_of(long long chunks) { return static_cast<int>((chunks + kSegChunks - 1) / kSegChunks); }
+unsigned seg_grid(int T, int nseg) {
+  return static_cast<unsigned>((static_cast<long long>(T) * nseg + kWaves - 1) / kWaves);
+}
+
+// Instantiation for k: the smallest of 4, 8, 16 that holds it (fewer registers for small k).
+#define MOE_SEG_LAUNCH(KERNEL, GRID, STREAM, K, ...)                              \
+  do {                                                                           \
+    if ((K) <= 4) KERNEL<4><<<(GRID), 256, 0, (STREAM)>>>(__VA_ARGS__);         \
+    else if ((K) <= 8) KERNEL<8><<<(GRID), 256, 0, (STREAM)>>>(__VA_ARGS__);    \
+    else KERNEL<16><<<(GRID), 256, 0, (STREAM)>>>(__VA_ARGS__);                 \
+  } while (0)
 
 }  // namespace
 }  // namespace moe
@@ -265,8 +274,10 @@ extern "C" int moe_permute(int dtype, const void* x, const uint8_t* x_scale, con
   } else {
     return set_error(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   }
-  permute_kernel<<<grid_for(T), 256, 0, as_stream(stream)>>>(
-      static_cast<const uint8_t*>(x), x_scale, dest, T, k, pitch, spitch, static_cast<uint8_t*>(xp), xp_scale);
+  const int nseg = segs_of(pitch / 16);
+  MOE_REQUIRE(static_cast<long long>(T) * nseg * 64 < (1LL << 32), MOE_ERR_UNSUPPORTED, "too many row segments");
+  MOE_SEG_LAUNCH(permute_kernel, seg_grid(T, nseg), as_stream(stream), k, static_cast<const uint8_t*>(x), x_scale, dest,
+                 T, k, nseg, pitch, spitch, static_cast<uint8_t*>(xp), xp_scale);
   return check_launch("permute");
 }
 
@@ -275,7 +286,9 @@ extern "C" int moe_unpermute_combine(const uint16_t* yexp, const float* gate, co
   if (int st = check_rows(T, d, k)) return st;
   MOE_CHECK_PTR(yexp); MOE_CHECK_PTR(gate); MOE_CHECK_PTR(dest); MOE_CHECK_PTR(y);
   MOE_CHECK_ALIGN(yexp); MOE_CHECK_ALIGN(y);
-  combine_kernel<<<grid_for(T), 256, 0, as_stream(stream)>>>(yexp, gate, dest, T, d, k, y);
+  const int nseg = segs_of(d / 8);
+  MOE_REQUIRE(static_cast<long long>(T) * nseg * 64 < (1LL << 32), MOE_ERR_UNSUPPORTED, "too many row segments");
+  MOE_SEG_LAUNCH(combine_kernel, seg_grid(T, nseg), as_stream(stream), k, yexp, gate, dest, T, d, k, nseg, y);
   return check_launch("combine");
 }
 
@@ -286,7 +299,7 @@ extern "C" int moe_unpermute_combine_bwd(const uint16_t* dy, const uint16_t* yex
   MOE_CHECK_PTR(dy); MOE_CHECK_PTR(yexp); MOE_CHECK_PTR(gate); MOE_CHECK_PTR(dest);
   MOE_CHECK_PTR(dyexp); MOE_CHECK_PTR(dgate);
   MOE_CHECK_ALIGN(dy); MOE_CHECK_ALIGN(yexp); MOE_CHECK_ALIGN(dyexp);
-  combine_bwd_kernel<<<grid_for(T), 256, 0, as_stream(stream)>>>(dy, yexp, gate, dest, T, d, k, dyexp, dgate);
+  MOE_SEG_LAUNCH(combine_bwd_kernel, grid_for(T), as_stream(stream), k, dy, yexp, gate, dest, T, d, k, dyexp, dgate);
   return check_launch("combine_bwd");
 }
 
@@ -296,6 +309,8 @@ extern "C" int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, 
   MOE_CHECK_PTR(dxp); MOE_CHECK_PTR(dest); MOE_CHECK_PTR(dx);
   MOE_CHECK_ALIGN(dxp); MOE_CHECK_ALIGN(dx);
   if (addend) MOE_CHECK_ALIGN(addend);
-  permute_bwd_kernel<<<grid_for(T), 256, 0, as_stream(stream)>>>(dxp, dest, T, d, k, addend, dx);
+  const int nseg = segs_of(d / 8);
+  MOE_REQUIRE(static_cast<long long>(T) * nseg * 64 < (1LL << 32), MOE_ERR_UNSUPPORTED, "too many row segments");
+  MOE_SEG_LAUNCH(permute_bwd_kernel, seg_grid(T, nseg), as_stream(stream), k, dxp, dest, T, d, k, nseg, addend, dx);
   return check_launch("permute_bwd");
 }

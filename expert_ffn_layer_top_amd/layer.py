@@ -2,9 +2,9 @@
 
 Forward:  [router_project] -> route_topk -> permute -> grouped_gemm_gate_up -> grouped_gemm_down
           -> unpermute_combine
-Backward: unpermute_combine_bwd -> grouped_gemm_dgrad_down -> grouped_gemm_wgrad_down
-          -> grouped_gemm_dgrad_gate_up -> grouped_gemm_wgrad_gate_up -> route_topk_bwd
-          -> [router_project_bwd] -> permute_bwd (+ the router's dx term)
+Backward: unpermute_combine_bwd -> route_topk_bwd -> [router_project_bwd]
+          -> grouped_gemm_dgrad_down -> grouped_gemm_wgrad_down -> grouped_gemm_dgrad_gate_up
+          -> permute_bwd (+ the router's dx term) -> grouped_gemm_wgrad_gate_up
 The grouped products are issued one kernel per call (the same kernels, in the same order, as the
 composite grouped_gemm_swiglu / grouped_gemm_swiglu_bwd), so each can be timed on its own.
 MXFP8 adds the block quantisation of x (before the permute; row blocks commute with the row
@@ -116,11 +116,23 @@ def backward(ctx, weights, dy, events=None):
     dw_down (and dw_r, dx_router when the layer owns its router) plus the intermediates (under
     MXFP8, "mx" holds the quantised backward operands: row blocks dyq/dgq/duq, grouped token
     blocks dyT/aT/dgT/duT/xT, each with its scales).
-    events: as for `forward`."""
+    events: as for `forward`.
+
+    Each call follows the call that produced its input where the dependencies allow (the router
+    gradients right after the combine backward, the permute backward right after the product
+    that writes dXp), so its input is still in the last-level cache; the arithmetic does not
+    depend on the order."""
     out = {}
     with _Span(events, "combine_bwd"):
         dyexp, dgate = ops.unpermute_combine_bwd(dy, ctx["yexp"], ctx["topk_gate"], ctx["dest"])
     out.update(dyexp=dyexp, d_gate=dgate)
+    E = ctx["logits"].shape[1]
+    with _Span(events, "route_bwd"):
+        out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E)
+    addend = None
+    if weights.w_r is not None:
+        addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])
+        out["dx_router"] = addend
     off = ctx["offsets"]
     g, u, a = ctx["g"], ctx["u"], ctx["a"]
     if not ctx["mxfp8"]:
@@ -130,6 +142,8 @@ def backward(ctx, weights, dy, events=None):
             dw_down = ops.grouped_gemm_wgrad_down(dyexp, a, off, g.shape[0])
         with _Span(events, "dgrad_gate_up"):
             dxp = ops.grouped_gemm_dgrad_gate_up(dg, du, off, weights.w_gate, weights.w_up)
+        with _Span(events, "permute_bwd"):
+            out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
         with _Span(events, "wgrad_gate_up"):
             dw_gate, dw_up = ops.grouped_gemm_wgrad_gate_up(dg, du, ctx["xp"], off, g.shape[0])
     else:
@@ -150,6 +164,8 @@ def backward(ctx, weights, dy, events=None):
         with _Span(events, "dgrad_gate_up"):
             dxp = ops.grouped_gemm_dgrad_gate_up(dgq, duq, off, q["wg_t"], q["wu_t"],
                                                  scales=(dgs, dus, q["wg_t_s"], q["wu_t_s"]))
+        with _Span(events, "permute_bwd"):
+            out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
         dgT, dgTs = ops.mxfp8_quantize_grouped(dg, off, pad, n)
         duT, duTs = ops.mxfp8_quantize_grouped(du, off, pad, n)
         xT, xTs = ops.mxfp8_quantize_grouped(ctx["x"], off, pad, n, row_token=ctx["row_token"])
@@ -159,13 +175,4 @@ def backward(ctx, weights, dy, events=None):
         out["mx"] = dict(dyq=dyq, dys=dys, dyT=dyT, dyTs=dyTs, aT=aT, aTs=aTs, dgq=dgq, dgs=dgs, duq=duq,
                          dus=dus, dgT=dgT, dgTs=dgTs, duT=duT, duTs=duTs, xT=xT, xTs=xTs)
     out.update(dg=dg, du=du, dxp=dxp, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
-    E = ctx["logits"].shape[1]
-    with _Span(events, "route_bwd"):
-        out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E)
-    addend = None
-    if weights.w_r is not None:
-        addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])
-        out["dx_router"] = addend
-    with _Span(events, "permute_bwd"):
-        out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
     return out
