@@ -4,81 +4,250 @@
 //   backward  dx_router[T,d] = d_logits[T,E] @ w_r^T
 //             dw_r[d,E]      = x^T @ d_logits      (K = T: split over token chunks, partial sums
 //                                                   reduced in a fixed order -> deterministic)
-// These products have one small dimension (E <= 256) and stay in fp32, so they run on the vector
-// ALUs: 64 x 64 output tiles, 256 threads with 4 x 4 outputs each, K steps of 32 staged in LDS
-// with the next step's global loads issued before the current step's FMAs.
+//
+// fp32 products on the bf16 matrix cores.  Every fp32 operand value v is split exactly into three
+// bf16 parts, v = hi + mid + lo: hi = bf16(v) (round to nearest even), mid = bf16(v - hi),
+// lo = v - hi - mid.  Each subtraction is exact (its operands lie within a factor of two of each
+// other), and what remains after hi and mid spans at most 8 significant bits, so lo is exact too.
+// A product of two bf16 parts is exact in fp32, and v_mfma_f32_16x16x32_bf16 accumulates in fp32,
+// so the result keeps fp32 accuracy:
+//   x (bf16, exact) times an fp32 operand:  x*hi + x*mid + x*lo                 (3 products)
+//   fp32 times fp32:  hi*hi + hi*mid + mid*hi + hi*lo + lo*hi + mid*mid  (6; the rest are below
+//                     2^-24 of the product)
+// Tiles: 64 x 64 outputs per 256-thread workgroup (four waves of 32 x 32 = 2 x 2 MFMA tiles), K
+// chunks of 64 staged in LDS as fp32 with K contiguous for both operands; the next chunk's global
+// loads are issued before the current chunk's products.  MFMA lane layout (as in the grouped
+// GEMMs): an operand lane l holds row (or column) l % 16 and K elements 8 (l / 16) .. + 7; the
+// result lane l holds column l % 16 and rows 4 (l / 16) .. + 3.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int TM = 64, TN = 64, TK = 32;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// C[M,N] (+)= sum_{k in [k_lo, k_hi)} A(m,k) B(k,n); A element (m,k) at A[m*a_sm + k*a_sk]
-// (bf16 bits when A_BF16), B element (k,n) at B[k*b_sk + n*b_sn] (fp32).  C row-major, pitch N.
-template <bool A_BF16, bool A_KFAST, bool B_KFAST>
-__global__ __launch_bounds__(256) void small_gemm(const void* __restrict__ Av, long long a_sm, long long a_sk,
-                                                  const float* __restrict__ B, long long b_sk, long long b_sn, int M,
-                                                  int N, int K, int k_chunk, float* __restrict__ C,
-                                                  long long c_split_stride) {
-  __shared__ float As[TK][TM + 1];
-  __shared__ float Bs[TK][TN + 1];
-  const int tid = threadIdx.x;
-  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
-  const int k_lo = blockIdx.z * k_chunk;
-  const int k_hi = min(K, k_lo + k_chunk);
-  float* Cz = C + blockIdx.z * c_split_stride;
-  const int tm = (tid & 15) * 4, tn = (tid >> 4) * 4;
-  float acc[4][4] = {};
+constexpr int TM = 64, TN = 64, TK = 64;
+constexpr int LDK = TK + 4;   // LDS row pitch (floats): rows of a fragment read fall on distinct banks
 
-  // each thread stages 8 elements of A and 8 of B per K step: element e = tid + 256*i of the
-  // TK x 64 tile, with consecutive threads walking the operand's unit-stride dimension
-  float ra[8], rb[8];
-  auto load = [&](int kb) {
+// Operand sources.  A is [M][K]; B is [K][N].
+enum Src {
+  A_X_KC = 0,    // A = x [M=T][K=d] bf16, K contiguous              (forward)
+  A_F_KC = 1,    // A = d_logits [M=T][K=E] fp32, K contiguous       (dx)
+  A_X_MC = 2,    // A[m][k] = x[k][m], x [K=T][M=d] bf16             (dw)
+  B_F_NC = 3,    // B = [K][N] fp32, N contiguous (w_r for forward, d_logits for dw)
+  B_F_KC = 4,    // B[k][n] = w_r[n][k], w_r [N=d][K=E] fp32          (dx)
+};
+
+// NE consecutive elements (row, col .. col + NE - 1) of a row-major matrix with `pitch` elements
+// per row; elements of rows at or past row_lim or columns at or past col_lim read 0.  One vector
+// load when the piece is whole and `vec` says fp32 rows are 16-byte aligned.
+template <int NE, bool BF16>
+__device__ __forceinline__ void piece(const void* __restrict__ base, long long pitch, int row, int row_lim, int col,
+                                      int col_lim, bool vec, float* v) {
+  if (row >= row_lim) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + 256 * i;
-      const int ka = A_KFAST ? (e & 31) : (e >> 6), ma = A_KFAST ? (e >> 5) : (e & 63);
-      const int kbb = B_KFAST ? (e & 31) : (e >> 6), nb = B_KFAST ? (e >> 5) : (e & 63);
-      float av = 0.f, bv = 0.f;
-      if (kb + ka < k_hi && m0 + ma < M) {
-        const long long off = static_cast<long long>(m0 + ma) * a_sm + static_cast<long long>(kb + ka) * a_sk;
-        av = A_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(Av)[off]) : static_cast<const float*>(Av)[off];
+    for (int i = 0; i < NE; ++i) v[i] = 0.f;
+    return;
+  }
+  const long long off = static_cast<long long>(row) * pitch + col;
+  if constexpr (BF16) {
+    static_assert(NE == 8, "bf16 pieces are 16 bytes");
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    if (col + 8 <= col_lim) {
+      const uint4 t = *reinterpret_cast<const uint4*>(p);
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = col + i < col_lim ? bf16_to_f32(p[i]) : 0.f;
+    }
+  } else {
+    static_assert(NE == 4, "fp32 pieces are 16 bytes");
+    const float* p = static_cast<const float*>(base) + off;
+    if (vec && col + 4 <= col_lim) {
+      const float4 t = *reinterpret_cast<const float4*>(p);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = col + i < col_lim ? p[i] : 0.f;
+    }
+  }
+}
+
+// One workgroup's share of a chunk: 16 values per thread for each operand (64 x 64 = 4096).
+struct Chunk {
+  float a[16], b[16];
+};
+
+// Piece p of a chunk: bf16 sources in 8-element pieces (8 per 64-element row), fp32 sources in
+// 4-element pieces (16 per row); "row" is the source's row (m, or k for x^T), "col" its
+// contiguous index.
+template <int SA>
+__device__ __forceinline__ void load_a(const void* __restrict__ A, int M, int K, int k_hi, int m0, int k0, int tid,
+                                       bool vec, float (&a)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (SA == A_X_KC) {          // x [T][d]: row m, col k
+      if (i < 2) {
+        const int p = tid + 256 * i;
+        piece<8, true>(A, K, m0 + (p >> 3), M, k0 + (p & 7) * 8, k_hi, vec, a + 8 * i);
       }
-      if (kb + kbb < k_hi && n0 + nb < N)
-        bv = B[static_cast<long long>(kb + kbb) * b_sk + static_cast<long long>(n0 + nb) * b_sn];
-      ra[i] = av;
-      rb[i] = bv;
+    } else if constexpr (SA == A_X_MC) {   // x [T][d]: row k, col m
+      if (i < 2) {
+        const int p = tid + 256 * i;
+        piece<8, true>(A, M, k0 + (p >> 3), k_hi, m0 + (p & 7) * 8, M, vec, a + 8 * i);
+      }
+    } else {                               // d_logits [T][E]: row m, col k
+      const int p = tid + 256 * i;
+      piece<4, false>(A, K, m0 + (p >> 4), M, k0 + (p & 15) * 4, k_hi, vec, a + 4 * i);
     }
-  };
-  load(k_lo);
-  for (int kb = k_lo; kb < k_hi; kb += TK) {
-    __syncthreads();
+  }
+}
+
+template <int SB>
+__device__ __forceinline__ void load_b(const float* __restrict__ B, int N, int K, int k_hi, int n0, int k0, int tid,
+                                       bool vec, float (&b)[16]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + 256 * i;
-      if (A_KFAST) As[e & 31][e >> 5] = ra[i]; else As[e >> 6][e & 63] = ra[i];
-      if (B_KFAST) Bs[e & 31][e >> 5] = rb[i]; else Bs[e >> 6][e & 63] = rb[i];
-    }
-    __syncthreads();
-    if (kb + TK < k_hi) load(kb + TK);
-#pragma unroll 8
-    for (int kk = 0; kk < TK; ++kk) {
-      float a[4], b[4];
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i;
+    if constexpr (SB == B_F_NC) piece<4, false>(B, N, k0 + (p >> 4), k_hi, n0 + (p & 15) * 4, N, vec, b + 4 * i);
+    else piece<4, false>(B, K, n0 + (p >> 4), N, k0 + (p & 15) * 4, k_hi, vec, b + 4 * i);   // w_r [d][E]
+  }
+}
+
+// Chunk registers -> LDS, both operands as [row][k] fp32.
+template <int SA, int SB>
+__device__ __forceinline__ void store_chunk(const Chunk& ch, float (*As)[LDK], float (*Bs)[LDK], int tid) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = As[kk][tm + i]; b[i] = Bs[kk][tn + i]; }
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i;
+    if constexpr (SA == A_X_KC) {
+      if (i < 2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 8; ++j) As[p >> 3][(p & 7) * 8 + j] = ch.a[8 * i + j];
+      }
+    } else if constexpr (SA == A_X_MC) {
+      if (i < 2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) As[(p & 7) * 8 + j][p >> 3] = ch.a[8 * i + j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) As[p >> 4][(p & 15) * 4 + j] = ch.a[4 * i + j];
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int m = m0 + tm + i, n = n0 + tn + j;
-      if (m < M && n < N) Cz[static_cast<long long>(m) * N + n] = acc[i][j];
+      if constexpr (SB == B_F_NC) Bs[(p & 15) * 4 + j][p >> 4] = ch.b[4 * i + j];
+      else Bs[p >> 4][(p & 15) * 4 + j] = ch.b[4 * i + j];
+    }
+  }
+}
+
+// v = hi + mid + lo exactly (see the file comment).
+__device__ __forceinline__ void split3(const float (&v)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = static_cast<__bf16>(v[i]);
+    const float r = v[i] - static_cast<float>(h);
+    const __bf16 m = static_cast<__bf16>(r);
+    hi[i] = h;
+    mid[i] = m;
+    lo[i] = static_cast<__bf16>(r - static_cast<float>(m));
+  }
+}
+
+__device__ __forceinline__ void frag(const float (*S)[LDK], int row, int k, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(&S[row][k]);
+  const float4 b = *reinterpret_cast<const float4*>(&S[row][k + 4]);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// C[M][N] (row pitch N; + blockIdx.z * c_split for split-K partials) over K range
+// [blockIdx.z * k_chunk, + k_chunk).  `vec`: fp32 rows are 16-byte aligned (their length is a
+// multiple of 4), so fp32 pieces load as float4.
+template <int SA, int SB>
+__global__ __launch_bounds__(256) void router_gemm(const void* __restrict__ A, const float* __restrict__ B, int M,
+                                                   int N, int K, int k_chunk, int vec, float* __restrict__ C,
+                                                   long long c_split) {
+  constexpr bool A_EXACT = SA != A_F_KC;   // bf16 source: one part
+  __shared__ __attribute__((aligned(16))) float As[TM][LDK];
+  __shared__ __attribute__((aligned(16))) float Bs[TN][LDK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
+  const int k_lo = blockIdx.z * k_chunk;
+  const int k_hi = min(K, k_lo + k_chunk);   // loads past k_hi read zero
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Chunk ch;
+  auto fetch = [&](int k0) {
+    load_a<SA>(A, M, K, k_hi, m0, k0, tid, vec, ch.a);
+    load_b<SB>(B, N, K, k_hi, n0, k0, tid, vec, ch.b);
+  };
+  fetch(k_lo);
+  for (int k0 = k_lo; k0 < k_hi; k0 += TK) {
+    __syncthreads();
+    store_chunk<SA, SB>(ch, As, Bs, tid);
+    __syncthreads();
+    if (k0 + TK < k_hi) fetch(k0 + TK);
+#pragma unroll
+    for (int kk = 0; kk < TK; kk += 32) {
+      const int kf = kk + 8 * (lane >> 4);
+      bf16x8 ah[2], am[2], al[2], bh[2], bm[2], bl[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float v[8];
+        frag(As, 32 * wm + 16 * t + (lane & 15), kf, v);
+        split3(v, ah[t], am[t], al[t]);
+        frag(Bs, 32 * wn + 16 * t + (lane & 15), kf, v);
+        split3(v, bh[t], bm[t], bl[t]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          f32x4 c = acc[i][j];
+          if constexpr (A_EXACT) {
+            c = mfma(ah[i], bl[j], c);
+            c = mfma(ah[i], bm[j], c);
+            c = mfma(ah[i], bh[j], c);
+          } else {
+            c = mfma(am[i], bm[j], c);
+            c = mfma(al[i], bh[j], c);
+            c = mfma(ah[i], bl[j], c);
+            c = mfma(am[i], bh[j], c);
+            c = mfma(ah[i], bm[j], c);
+            c = mfma(ah[i], bh[j], c);
+          }
+          acc[i][j] = c;
+        }
+    }
+  }
+  float* Cz = C + blockIdx.z * c_split;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 32 * wn + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 32 * wm + 16 * i + 4 * (lane >> 4) + r;
+        if (m < M && n < N) Cz[static_cast<long long>(m) * N + n] = acc[i][j][r];
+      }
     }
 }
 
@@ -96,6 +265,11 @@ constexpr int kSplitTokens = 1024;   // tokens per split of the dw_r reduction
 
 int n_splits(int T) { return (T + kSplitTokens - 1) / kSplitTokens; }
 
+// fp32 rows of E elements load as float4 when E is a multiple of 4 and both bases are 16-byte aligned.
+int f32_rows_aligned(int E, const void* p, const void* q) {
+  return E % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && (reinterpret_cast<uintptr_t>(q) & 15u) == 0;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -105,8 +279,11 @@ extern "C" int moe_router_project(const uint16_t* x, const float* w_r, int T, in
                                   void* stream) {
   MOE_CHECK_PTR(x); MOE_CHECK_PTR(w_r); MOE_CHECK_PTR(logits);
   MOE_REQUIRE(T >= 1 && d >= 1 && E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "need T, d >= 1 and 1 <= E <= 256");
+  MOE_REQUIRE(d % 8 == 0, MOE_ERR_UNSUPPORTED, "router: d must be a multiple of 8");
+  MOE_CHECK_ALIGN(x);
   dim3 grid((T + TM - 1) / TM, (E + TN - 1) / TN, 1);
-  small_gemm<true, true, false><<<grid, 256, 0, as_stream(stream)>>>(x, d, 1, w_r, E, 1, T, E, d, d, logits, 0);
+  router_gemm<A_X_KC, B_F_NC><<<grid, 256, 0, as_stream(stream)>>>(x, w_r, T, E, d, d, f32_rows_aligned(E, w_r, w_r),
+                                                                   logits, 0);
   return check_launch("router_project");
 }
 
@@ -120,6 +297,9 @@ extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const
                                       void* stream) {
   MOE_CHECK_PTR(x); MOE_CHECK_PTR(w_r); MOE_CHECK_PTR(d_logits);
   MOE_REQUIRE(T >= 1 && d >= 1 && E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "need T, d >= 1 and 1 <= E <= 256");
+  MOE_REQUIRE(d % 8 == 0, MOE_ERR_UNSUPPORTED, "router: d must be a multiple of 8");
+  MOE_CHECK_ALIGN(x);
+  const int vec = f32_rows_aligned(E, w_r, d_logits);
   hipStream_t s = as_stream(stream);
   if (dw_r != nullptr) {
     const size_t need = moe_router_bwd_workspace_bytes(T, d, E);
@@ -128,7 +308,7 @@ extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const
   if (dx_router != nullptr) {
     // dx[t, c] = sum_e dl[t, e] * w_r[c, e]
     dim3 grid((T + TM - 1) / TM, (d + TN - 1) / TN, 1);
-    small_gemm<false, true, true><<<grid, 256, 0, s>>>(d_logits, E, 1, w_r, 1, E, T, d, E, E, dx_router, 0);
+    router_gemm<A_F_KC, B_F_KC><<<grid, 256, 0, s>>>(d_logits, w_r, T, d, E, E, vec, dx_router, 0);
     if (int st = check_launch("router_project_bwd dx")) return st;
   }
   if (dw_r != nullptr) {
@@ -136,8 +316,8 @@ extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const
     const int S = n_splits(T);
     float* part = static_cast<float*>(ws);
     dim3 grid((d + TM - 1) / TM, (E + TN - 1) / TN, S);
-    small_gemm<true, false, false><<<grid, 256, 0, s>>>(x, 1, d, d_logits, E, 1, d, E, T, kSplitTokens, part,
-                                          static_cast<long long>(d) * E);
+    router_gemm<A_X_MC, B_F_NC><<<grid, 256, 0, s>>>(x, d_logits, d, E, T, kSplitTokens, vec, part,
+                                                     static_cast<long long>(d) * E);
     if (int st = check_launch("router_project_bwd dw partial")) return st;
     const long long count = static_cast<long long>(d) * E;
     reduce_splits<<<static_cast<unsigned>((count + 255) / 256), 256, 0, s>>>(part, S, count, dw_r);

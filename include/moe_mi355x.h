@@ -80,7 +80,10 @@ const char* moe_last_error_string(void);
 /* logits[T,E] = x[T,d] (bf16) @ w_r[d,E] (fp32), fp32 accumulation.
  * The router's projection that scores every expert for every token ([news] lead paragraphs).
  * Used where the router weight is part of the layer (the router-driven workloads); callers that
- * already hold logits skip it. */
+ * already hold logits skip it.  Computed on the bf16 matrix cores from an exact three-part bf16
+ * split of each fp32 value (fp32 accuracy; the summation order is the hardware's, not a
+ * sequential dot product).  d must be a multiple of 8 and x 16-byte aligned (MOE_ERR_UNSUPPORTED
+ * / MOE_ERR_INVALID_ARG otherwise); any E in [1, 256]. */
 int moe_router_project(const uint16_t* x, const float* w_r, int T, int d, int E, float* logits,
                        void* stream);
 
@@ -88,8 +91,9 @@ int moe_router_project(const uint16_t* x, const float* w_r, int T, int d, int E,
 size_t moe_router_bwd_workspace_bytes(int T, int d, int E);
 
 /* Backward of moe_router_project:  dx_router[T,d] = d_logits @ w_r^T (fp32),
- * dw_r[d,E] = x^T @ d_logits (fp32; summed over token chunks in a fixed order).  Either output
- * may be NULL to skip it; ws (>= moe_router_bwd_workspace_bytes) is needed only for dw_r. */
+ * dw_r[d,E] = x^T @ d_logits (fp32; summed over token chunks in a fixed order, so repeated calls
+ * give identical bits).  Either output may be NULL to skip it; ws (>= moe_router_bwd_workspace_bytes)
+ * is needed only for dw_r.  Same arithmetic and argument limits as moe_router_project. */
 int moe_router_project_bwd(const uint16_t* x, const float* w_r, const float* d_logits, int T, int d,
                            int E, float* dx_router_or_null, float* dw_r_or_null, void* ws,
                            size_t ws_bytes, void* stream);

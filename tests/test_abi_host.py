@@ -101,6 +101,10 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_grouped_gemm_wgrad_gate_up(1, 8, 256, 192, 256, fake, fake, *[fake] * 8, None) == UNSUPPORTED
     assert L.moe_grouped_gemm_wgrad_gate_up(0, 8, 256, 128, 256, fake, None, fake, None, fake, None, fake, None,
                                             fake, None, None) == INVALID
+    # router: d a multiple of 8, x 16-byte aligned
+    assert L.moe_router_project(fake, fake, 64, 12, 8, fake, None) == UNSUPPORTED
+    assert L.moe_router_project(ctypes.c_void_p(0x1008), fake, 64, 128, 8, fake, None) == INVALID
+    assert L.moe_router_project_bwd(fake, fake, fake, 64, 12, 8, fake, None, None, 0, None) == UNSUPPORTED
     # router backward: dw_r requested without workspace
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, fake, None, 0, None) == WORKSPACE
     msg = L.moe_last_error_string().decode()

@@ -85,7 +85,8 @@ def test_route_topk_bwd(T, E, k):
     assert np.all(out[~mask] == 0.0)
 
 
-@pytest.mark.parametrize("T,d,E", [(256, 128, 8), (300, 512, 64), (1000, 7168, 64)])
+@pytest.mark.parametrize("T,d,E", [(256, 128, 8), (300, 512, 64), (1000, 7168, 64), (130, 200, 5), (257, 136, 12),
+                                   (64, 8, 1), (70, 64, 256)])
 def test_router_project_and_bwd(T, d, E):
     from expert_ffn_layer_top_amd import ops
     rng = np.random.default_rng(d + E)
@@ -100,3 +101,6 @@ def test_router_project_and_bwd(T, d, E):
     rdx, rdw = moe.router_project_bwd(x, w_r, dl)
     assert_close(host(dx), rdx, 1e-5, "dx_router")
     assert_close(host(dw), rdw, 1e-5, "dw_r")
+    # fixed-order split-K reduction: a repeat gives the same bits
+    dx2, dw2 = ops.router_project_bwd(xd, wd, f32_to_dev(dl))
+    assert np.array_equal(host(dw2), host(dw)) and np.array_equal(host(dx2), host(dx))
