@@ -29,9 +29,9 @@ __device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits) {
   return s;
 }
 
-// E4M3 code of bf16 value `b` divided by 2^shared (round-to-nearest-even, saturating).
-__device__ __forceinline__ uint32_t mx_encode(uint32_t b, int shared) {
-  const uint32_t sign = (b & 0x8000u) ? 0x80u : 0u;
+// bf16 value `b` divided by 2^shared, as a signed fp32 with its magnitude clamped to 448 (the
+// largest E4M3 value: larger magnitudes saturate).  Exact wherever the E4M3 code depends on it.
+__device__ __forceinline__ float mx_scaled(uint32_t b, int shared) {
   const uint32_t mag = b & 0x7fffu;
   float a;
   if ((mag >> 7) != 0) {
@@ -44,15 +44,24 @@ __device__ __forceinline__ uint32_t mx_encode(uint32_t b, int shared) {
     a = (ex < -126) ? 0.f : static_cast<float>(mag) * __uint_as_float(static_cast<uint32_t>(ex + 127) << 23);
   }
   a = fminf(a, 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: E4M3 subnormal spacing 2^-9
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // 0..8 (8 = smallest normal)
-  } else {
-    const uint32_t u = __float_as_uint(a);
-    const uint32_t r = (u + 0x7ffffu + ((u >> 20) & 1u)) >> 20;  // exponent|3-bit mantissa, RNE
-    code = r - (120u << 3);                  // rebias 127 -> 7
-  }
-  return code | sign;
+  return __uint_as_float(__float_as_uint(a) | ((b & 0x8000u) << 16));
+}
+
+// E4M3 codes of two values from mx_scaled, in bytes 0 and 1: the hardware conversion to the
+// OCP E4M3 format, rounding to nearest even (|a| <= 448, so nothing overflows; values below the
+// smallest subnormal round to a zero of their sign).
+__device__ __forceinline__ uint32_t e4m3x2(float a0, float a1) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false)) & 0xffffu;
+}
+
+// E4M3 codes of bf16 values b0, b1 divided by 2^shared (round-to-nearest-even, saturating).
+__device__ __forceinline__ uint32_t mx_encode2(uint32_t b0, uint32_t b1, int shared) {
+  return e4m3x2(mx_scaled(b0, shared), mx_scaled(b1, shared));
+}
+
+// Four codes in one word (bytes 0..3 from b0..b3).
+__device__ __forceinline__ uint32_t mx_encode4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3, int shared) {
+  return mx_encode2(b0, b1, shared) | (mx_encode2(b2, b3, shared) << 16);
 }
 
 }  // namespace moe

@@ -5,7 +5,9 @@
 //   cols     blocks along the strided dim, output transposed (each block contiguous again);
 //   grouped  token-axis blocks restarting at each expert group (padded to 32 rows), output
 //            transposed to [C, padded tokens]: the weight-gradient operands.
-// All are HBM-bound: 2 bytes read, 1 + 1/32 bytes written per element.
+// rows and cols also come together from one read of the input (the weights, which the products
+// need quantised along each of their two dims).  All are HBM-bound: 2 bytes read, 1 + 1/32
+// bytes written per element and output.
 #include "mx_common.h"
 
 namespace moe {
@@ -32,14 +34,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, 64)));
   if (!live) return;
   const int sh = mx_shared_exp(amax);
-  uint32_t o0 = 0, o1 = 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    o0 |= mx_encode(w[i] & 0xffffu, sh) << (16 * i);
-    o0 |= mx_encode(w[i] >> 16, sh) << (16 * i + 8);
-    o1 |= mx_encode(w[i + 2] & 0xffffu, sh) << (16 * i);
-    o1 |= mx_encode(w[i + 2] >> 16, sh) << (16 * i + 8);
-  }
+  const uint32_t o0 = mx_encode2(w[0] & 0xffffu, w[0] >> 16, sh) | (mx_encode2(w[1] & 0xffffu, w[1] >> 16, sh) << 16);
+  const uint32_t o1 = mx_encode2(w[2] & 0xffffu, w[2] >> 16, sh) | (mx_encode2(w[3] & 0xffffu, w[3] >> 16, sh) << 16);
   *reinterpret_cast<uint2*>(q + e0) = make_uint2(o0, o1);
   if ((threadIdx.x & 3) == 0) scale[e0 / 32] = static_cast<uint8_t>(sh + 127);
 }
@@ -70,8 +66,7 @@ __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    o[i] = mx_encode(vals[4 * i], sh) | (mx_encode(vals[4 * i + 1], sh) << 8) |
-           (mx_encode(vals[4 * i + 2], sh) << 16) | (mx_encode(vals[4 * i + 3], sh) << 24);
+    o[i] = mx_encode4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3], sh);
   }
   uint8_t* dst = q + c * out_pitch + pos0 + blk * 32;
   reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -104,6 +99,66 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
   if (r0 + blk * 32 >= rows) return;
   quant_tile_columns(tile, kTC, r0, rows, q + b * cols * static_cast<long long>(rows) + static_cast<long long>(c0) * rows,
                      scale + b * cols * static_cast<long long>(rows / 32) + static_cast<long long>(c0) * (rows / 32));
+}
+
+// ---- both layouts from one read (the weights, quantised along each of their two dims every
+// step): the 128 x 64 tile of the column quantiser, staged in LDS once, also gives its 128 x 2
+// row blocks (one per thread; output in the input's layout).  Column tiles run fastest in the
+// grid, so the two tiles that write the halves of one 128-byte output row line run side by side.
+// in [batch][rows][cols] -> q [batch][rows][cols] + scale [batch][rows][cols/32] and
+// qT [batch][cols][rows] + scaleT [batch][cols][rows/32].
+// grid: (cols/64, ceil(rows/128), batch); rows % 32 == 0, cols % 64 == 0.
+__global__ __launch_bounds__(256) void quant_both_kernel(const uint16_t* __restrict__ in, int rows, int cols,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
+                                                         uint8_t* __restrict__ qT, uint8_t* __restrict__ scaleT) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTP][kPitch];
+  const long long b = blockIdx.z;
+  const int c0 = blockIdx.x * kTC;
+  const int r0 = blockIdx.y * kTP;
+  const long long plane = static_cast<long long>(rows) * cols;
+  const uint16_t* src = in + b * plane;
+  const int cc = threadIdx.x & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (threadIdx.x >> 3) + 32 * i;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < rows) v = *reinterpret_cast<const uint4*>(src + static_cast<long long>(r0 + r) * cols + c0 + 8 * cc);
+    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[r][8 * cc]);
+    t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
+  }
+  __syncthreads();
+  // row blocks: row t/2, columns 32 (t%2) .. + 31 of the tile
+  {
+    const int r = threadIdx.x >> 1, blk = threadIdx.x & 1;
+    if (r0 + r < rows) {
+      uint32_t vals[32];
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&tile[r][32 * blk]);
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t x = w[i];
+        vals[2 * i] = x & 0xffffu;
+        vals[2 * i + 1] = x >> 16;
+        amax = max(amax, max(x & 0x7fffu, (x >> 16) & 0x7fffu));
+      }
+      const int sh = mx_shared_exp(amax);
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        o[i] = mx_encode4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3], sh);
+      }
+      const long long row = r0 + r;
+      uint8_t* dst = q + b * plane + row * cols + c0 + 32 * blk;
+      reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      scale[b * (plane / 32) + row * (cols / 32) + c0 / 32 + blk] = static_cast<uint8_t>(sh + 127);
+    }
+  }
+  // column blocks, as the column quantiser
+  const int blk = threadIdx.x & 3;
+  if (r0 + blk * 32 >= rows) return;
+  quant_tile_columns(tile, kTC, r0, rows, qT + b * plane + static_cast<long long>(c0) * rows,
+                     scaleT + b * (plane / 32) + static_cast<long long>(c0) * (rows / 32));
 }
 
 // Grouped token-axis blocks.  Padded position p in [offsets_pad[e], offsets_pad[e+1]) holds
@@ -185,6 +240,19 @@ extern "C" int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols,
   dim3 grid((rows + kTP - 1) / kTP, cols / kTC, batch);
   quant_cols_kernel<<<grid, 256, 0, s>>>(in, rows, cols, q, scale);
   return check_launch("mxfp8_quantize cols");
+}
+
+extern "C" int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int cols, uint8_t* q, uint8_t* scale,
+                                   uint8_t* qT, uint8_t* scaleT, void* stream) {
+  MOE_CHECK_PTR(in); MOE_CHECK_PTR(q); MOE_CHECK_PTR(scale); MOE_CHECK_PTR(qT); MOE_CHECK_PTR(scaleT);
+  MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(q); MOE_CHECK_ALIGN(qT);
+  MOE_REQUIRE(batch >= 1 && rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG, "sizes must be positive");
+  MOE_REQUIRE(rows % 32 == 0 && cols % 64 == 0, MOE_ERR_UNSUPPORTED, "need rows %% 32 == 0, cols %% 64 == 0");
+  MOE_REQUIRE(batch <= 65535, MOE_ERR_UNSUPPORTED, "batch too large");
+  MOE_REQUIRE((rows + kTP - 1) / kTP <= 65535, MOE_ERR_UNSUPPORTED, "too many rows");
+  dim3 grid(cols / kTC, (rows + kTP - 1) / kTP, batch);
+  quant_both_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, rows, cols, q, scale, qT, scaleT);
+  return check_launch("mxfp8_quantize_both");
 }
 
 extern "C" int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_token, const int32_t* offsets,

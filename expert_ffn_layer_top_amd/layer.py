@@ -38,14 +38,11 @@ class Weights:
 
     def quantize_mx(self):
         """MXFP8 copies of the expert weights, blocks along each product's contraction dim:
-        forward (gate/up along d, down along f) and dgrad (gate/up along f, down along d)."""
+        forward (gate/up along d, down along f) and dgrad (gate/up along f, down along d), both
+        from one read of each weight."""
         q = {}
-        q["wg"], q["wg_s"] = ops.mxfp8_quantize(self.w_gate, 0)
-        q["wu"], q["wu_s"] = ops.mxfp8_quantize(self.w_up, 0)
-        q["wd"], q["wd_s"] = ops.mxfp8_quantize(self.w_down, 0)
-        q["wg_t"], q["wg_t_s"] = ops.mxfp8_quantize(self.w_gate, 1)
-        q["wu_t"], q["wu_t_s"] = ops.mxfp8_quantize(self.w_up, 1)
-        q["wd_t"], q["wd_t_s"] = ops.mxfp8_quantize(self.w_down, 1)
+        for name, w in (("wg", self.w_gate), ("wu", self.w_up), ("wd", self.w_down)):
+            q[name], q[name + "_s"], q[name + "_t"], q[name + "_t_s"] = ops.mxfp8_quantize_both(w)
         self.mx = q
         return q
 

@@ -184,6 +184,25 @@ def mxfp8_quantize(x, axis):
     return q, s
 
 
+def mxfp8_quantize_both(x):
+    """x [..., R, C] bf16 (2-D or 3-D) -> (q, s) as mxfp8_quantize(x, 0) and (qT, sT) as
+    mxfp8_quantize(x, 1), from one read of x."""
+    _check(x, torch.bfloat16, "x")
+    if x.dim() == 2:
+        batch, (R, C) = 1, x.shape
+    elif x.dim() == 3:
+        batch, R, C = x.shape
+    else:
+        raise ValueError("x must be 2-D or 3-D")
+    lead = x.shape[:-2]
+    q = _empty((*lead, R, C), torch.uint8, x)
+    s = _empty((*lead, R, C // 32), torch.uint8, x)
+    qT = _empty((*lead, C, R), torch.uint8, x)
+    sT = _empty((*lead, C, R // 32), torch.uint8, x)
+    call("mxfp8_quantize_both", _ptr(x), batch, R, C, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT), _stream(x))
+    return q, s, qT, sT
+
+
 def mx_pad_cap(n, E):
     return lib.moe_mx_pad_cap(n, E)
 

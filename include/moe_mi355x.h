@@ -162,6 +162,14 @@ int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int 
 int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, uint8_t* q,
                    uint8_t* scale, void* stream);
 
+/* Both mxfp8_quantize layouts of one input from a single read of it: q/scale as axis 0 and
+ * qT/scaleT as axis 1, bit-identical to the two separate calls.  For the expert weights, which
+ * the forward and the dgrad products need quantised along each of their two dims
+ * ([news] "MXFP8 reduces compute and memory costs").  rows % 32 == 0 and cols % 64 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise); in, q, qT 16-byte aligned; outputs as for mxfp8_quantize. */
+int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int cols, uint8_t* q, uint8_t* scale,
+                        uint8_t* qT, uint8_t* scaleT, void* stream);
+
 /* Token-axis MXFP8 blocks restarting at each expert group (the weight-gradient operands).
  * Row r of the grouped tensor is in[r] (row_token NULL; in is [n,C]) or in[row_token[r]]
  * (in is the token-major source [T,C]).  Expert e's rows [offsets[e], offsets[e+1]) go to

@@ -101,6 +101,10 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_grouped_gemm_wgrad_gate_up(1, 8, 256, 192, 256, fake, fake, *[fake] * 8, None) == UNSUPPORTED
     assert L.moe_grouped_gemm_wgrad_gate_up(0, 8, 256, 128, 256, fake, None, fake, None, fake, None, fake, None,
                                             fake, None, None) == INVALID
+    # two-layout quantiser: rows % 32, cols % 64
+    assert L.mxfp8_quantize_both(fake, 1, 48, 64, fake, fake, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp8_quantize_both(fake, 1, 64, 96, fake, fake, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp8_quantize_both(fake, 1, 64, 64, fake, None, fake, fake, None) == INVALID
     # router: d a multiple of 8, x 16-byte aligned
     assert L.moe_router_project(fake, fake, 64, 12, 8, fake, None) == UNSUPPORTED
     assert L.moe_router_project(ctypes.c_void_p(0x1008), fake, 64, 128, 8, fake, None) == INVALID

@@ -83,6 +83,23 @@ def test_cols_transposed(B, R, C):
     assert np.array_equal(host(s), rs) and np.array_equal(host(q), rq)
 
 
+@pytest.mark.parametrize("B,R,C", [(1, 32, 64), (1, 288, 192), (3, 256, 128), (2, 160, 320), (4, 2048, 1024),
+                                   (1, 7168, 2048)])
+def test_rows_and_cols_from_one_read(B, R, C):
+    """The two-layout quantiser (used for the weights) against the oracle in both layouts, on
+    shapes with partial 128 x 128 tiles in either dimension and a per-row dynamic range."""
+    from expert_ffn_layer_top_amd import ops
+    rng = np.random.default_rng(7 * B + R + C)
+    v = rng.standard_normal((B, R, C)).astype(np.float32) * np.exp(rng.standard_normal((B, R, 1)) * 3).astype(np.float32)
+    x = to_bf16_bits(v)
+    note(f"mxfp8 both B={B} R={R} C={C}")
+    q, s, qT, sT = ops.mxfp8_quantize_both(bf16_to_dev(x))
+    rq, rs = mxfp8.quantize_rows(x)
+    cq, cs = mxfp8.quantize_cols(x)
+    assert np.array_equal(host(s), rs) and np.array_equal(host(q), rq)
+    assert np.array_equal(host(sT), cs) and np.array_equal(host(qT), cq)
+
+
 @pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
 @pytest.mark.parametrize("gather", [False, True])
 def test_grouped_token_blocks(T, E, k, C, gather):
