@@ -103,62 +103,77 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
 
 // ---- both layouts from one read (the weights, quantised along each of their two dims every
 // step): the 128 x 64 tile of the column quantiser, staged in LDS once, also gives its 128 x 2
-// row blocks (one per thread; output in the input's layout).  Column tiles run fastest in the
-// grid, so the two tiles that write the halves of one 128-byte output row line run side by side.
+// row blocks (one per thread; output in the input's layout).  A workgroup walks kBothTiles
+// column tiles of one 128-row band, loading the next tile into registers while it quantises the
+// current one, so each compute unit keeps more of the input in flight.
 // in [batch][rows][cols] -> q [batch][rows][cols] + scale [batch][rows][cols/32] and
 // qT [batch][cols][rows] + scaleT [batch][cols][rows/32].
-// grid: (cols/64, ceil(rows/128), batch); rows % 32 == 0, cols % 64 == 0.
+// grid: (ceil(cols / (64 kBothTiles)), ceil(rows/128), batch); rows % 32 == 0, cols % 64 == 0.
+constexpr int kBothTiles = 4;
+
+__device__ __forceinline__ void load_tile_regs(const uint16_t* __restrict__ src, int rows, int cols, int r0, int c0,
+                                               uint4 (&v)[4]) {
+  const int cc = threadIdx.x & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (threadIdx.x >> 3) + 32 * i;
+    v[i] = make_uint4(0, 0, 0, 0);
+    if (r0 + r < rows && c0 < cols)
+      v[i] = *reinterpret_cast<const uint4*>(src + static_cast<long long>(r0 + r) * cols + c0 + 8 * cc);
+  }
+}
+
 __global__ __launch_bounds__(256) void quant_both_kernel(const uint16_t* __restrict__ in, int rows, int cols,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
                                                          uint8_t* __restrict__ qT, uint8_t* __restrict__ scaleT) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTP][kPitch];
   const long long b = blockIdx.z;
-  const int c0 = blockIdx.x * kTC;
   const int r0 = blockIdx.y * kTP;
   const long long plane = static_cast<long long>(rows) * cols;
   const uint16_t* src = in + b * plane;
   const int cc = threadIdx.x & 7;
+  int c0 = blockIdx.x * kTC * kBothTiles;
+  uint4 v[4];
+  load_tile_regs(src, rows, cols, r0, c0, v);
+  for (int it = 0; it < kBothTiles && c0 < cols; ++it, c0 += kTC) {
+    __syncthreads();   // the previous tile's readers are done with the LDS tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (threadIdx.x >> 3) + 32 * i;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < rows) v = *reinterpret_cast<const uint4*>(src + static_cast<long long>(r0 + r) * cols + c0 + 8 * cc);
-    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[r][8 * cc]);
-    t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
-  }
-  __syncthreads();
-  // row blocks: row t/2, columns 32 (t%2) .. + 31 of the tile
-  {
-    const int r = threadIdx.x >> 1, blk = threadIdx.x & 1;
-    if (r0 + r < rows) {
-      uint32_t vals[32];
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(&tile[r][32 * blk]);
-      uint32_t amax = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t x = w[i];
-        vals[2 * i] = x & 0xffffu;
-        vals[2 * i + 1] = x >> 16;
-        amax = max(amax, max(x & 0x7fffu, (x >> 16) & 0x7fffu));
-      }
-      const int sh = mx_shared_exp(amax);
-      uint32_t o[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o[i] = mx_encode4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3], sh);
-      }
-      const long long row = r0 + r;
-      uint8_t* dst = q + b * plane + row * cols + c0 + 32 * blk;
-      reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      scale[b * (plane / 32) + row * (cols / 32) + c0 / 32 + blk] = static_cast<uint8_t>(sh + 127);
+    for (int i = 0; i < 4; ++i) {
+      uint32_t* t = reinterpret_cast<uint32_t*>(&tile[(threadIdx.x >> 3) + 32 * i][8 * cc]);
+      t[0] = v[i].x; t[1] = v[i].y; t[2] = v[i].z; t[3] = v[i].w;
     }
+    __syncthreads();
+    if (it + 1 < kBothTiles) load_tile_regs(src, rows, cols, r0, c0 + kTC, v);
+    // row blocks: row t/2, columns 32 (t%2) .. + 31 of the tile
+    {
+      const int r = threadIdx.x >> 1, blk = threadIdx.x & 1;
+      if (r0 + r < rows) {
+        uint32_t vals[32];
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&tile[r][32 * blk]);
+        uint32_t amax = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t x = w[i];
+          vals[2 * i] = x & 0xffffu;
+          vals[2 * i + 1] = x >> 16;
+          amax = max(amax, max(x & 0x7fffu, (x >> 16) & 0x7fffu));
+        }
+        const int sh = mx_shared_exp(amax);
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = mx_encode4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3], sh);
+        const long long row = r0 + r;
+        uint8_t* dst = q + b * plane + row * cols + c0 + 32 * blk;
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        scale[b * (plane / 32) + row * (cols / 32) + c0 / 32 + blk] = static_cast<uint8_t>(sh + 127);
+      }
+    }
+    // column blocks, as the column quantiser
+    if (r0 + (threadIdx.x & 3) * 32 < rows)
+      quant_tile_columns(tile, kTC, r0, rows, qT + b * plane + static_cast<long long>(c0) * rows,
+                         scaleT + b * (plane / 32) + static_cast<long long>(c0) * (rows / 32));
   }
-  // column blocks, as the column quantiser
-  const int blk = threadIdx.x & 3;
-  if (r0 + blk * 32 >= rows) return;
-  quant_tile_columns(tile, kTC, r0, rows, qT + b * plane + static_cast<long long>(c0) * rows,
-                     scaleT + b * (plane / 32) + static_cast<long long>(c0) * (rows / 32));
 }
 
 // Grouped token-axis blocks.  Padded position p in [offsets_pad[e], offsets_pad[e+1]) holds
@@ -250,7 +265,7 @@ extern "C" int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int 
   MOE_REQUIRE(rows % 32 == 0 && cols % 64 == 0, MOE_ERR_UNSUPPORTED, "need rows %% 32 == 0, cols %% 64 == 0");
   MOE_REQUIRE(batch <= 65535, MOE_ERR_UNSUPPORTED, "batch too large");
   MOE_REQUIRE((rows + kTP - 1) / kTP <= 65535, MOE_ERR_UNSUPPORTED, "too many rows");
-  dim3 grid(cols / kTC, (rows + kTP - 1) / kTP, batch);
+  dim3 grid((cols / kTC + kBothTiles - 1) / kBothTiles, (rows + kTP - 1) / kTP, batch);
   quant_both_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, rows, cols, q, scale, qT, scaleT);
   return check_launch("mxfp8_quantize_both");
 }
