@@ -2,6 +2,9 @@
 
     python -m expert_ffn_layer_top_amd.profsum kernels DIR --title TEXT --command TEXT
         per-kernel calls / total / average / share of a --kernel-trace run
+    python -m expert_ffn_layer_top_amd.profsum counters DIR --counter NAME [--counter NAME ...]
+            [--match TEXT] --title TEXT --command TEXT
+        per-kernel mean of each counter (or derived metric, e.g. MfmaUtil) of a --pmc run
     python -m expert_ffn_layer_top_amd.profsum traffic --fetch DIR --write DIR --kernel NAME
             --call CALL --workload NAME --copy-bytes N --command-fetch TEXT --command-write TEXT
         HBM bytes per dispatch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run, each
@@ -104,6 +107,20 @@ def cmd_kernels(a):
               f"{max(v) / 1e3:10.2f} {100.0 * sum(v) / total:6.2f}  {k}")
 
 
+def cmd_counters(a):
+    """Per-kernel mean over dispatches of each counter of a --pmc run (derived metrics included)."""
+    cols = {c: counter_values(a.dir, c) for c in a.counter}
+    kernels = sorted({k for v in cols.values() for k in v if a.match in k})
+    print(f"# {a.title}")
+    print(f"# command: {a.command}")
+    print("# mean over dispatches of each counter, per kernel (rocprofv3 --pmc, CSV output)")
+    print(f"{'dispatches':>10} " + " ".join(f"{c:>28}" for c in a.counter) + "  kernel")
+    for k in kernels:
+        n = max(len(cols[c].get(k, [])) for c in a.counter)
+        vals = [statistics.mean(cols[c][k]) if cols[c].get(k) else float("nan") for c in a.counter]
+        print(f"{n:10d} " + " ".join(f"{v:28.6g}" for v in vals) + f"  {k}")
+
+
 def _one(values, name, what):
     hits = {k: v for k, v in values.items() if name in k}
     if len(hits) != 1:
@@ -166,6 +183,12 @@ def main(argv=None):
     k.add_argument("dir")
     k.add_argument("--title", required=True)
     k.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--counter", action="append", required=True)
+    c.add_argument("--match", default="", help="only kernels whose name contains this")
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -176,7 +199,7 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     a = ap.parse_args(argv)
-    (cmd_kernels if a.cmd == "kernels" else cmd_traffic)(a)
+    {"kernels": cmd_kernels, "counters": cmd_counters, "traffic": cmd_traffic}[a.cmd](a)
     return 0
 
 
