@@ -50,7 +50,7 @@ constexpr int BN = 256;
 constexpr int BK = 128;                           // fp8 elements (bytes) per K step
 constexpr int NTH = 256;
 constexpr int OP_BYTES = BM * BK;                 // 32 KiB per operand per stage
-constexpr int SC_BYTES = BM * 4 * 4;              // scales: one dword slot per (row, K block)
+constexpr int SC_BYTES = BM * 16;                 // scales: 16 bytes per row (see OpLoad)
 constexpr int NSTG = 2;                           // stages per operand ring
 constexpr int A_RING = 0;
 constexpr int B_RING = NSTG * OP_BYTES;
@@ -131,19 +131,29 @@ __device__ __forceinline__ int k_total(const Params& p) {
 using gsched::MTiles;
 
 // One wave's share of an operand stage: 128 rows x 128 bytes of data (16 DMA instructions of
-// 16 bytes per lane) and the rows' scale bytes (8 byte-DMA instructions).  The offsets depend on
-// the launch, not the tile.
+// 16 bytes per lane) and the rows' scale bytes, one lane per row and dword (2 dword instructions,
+// 4 for the weight gradients).  The offsets depend on the launch, not the tile.
+//
+// A K step needs 4 scale bytes per row (4 blocks of 32).
+// - Forward and dgrad operands (row-major scales [rows][K/32], K a multiple of 128): the 4 bytes
+//   are one aligned dword of the row; two dword loads per wave (lane = row) put row R of the
+//   stage at 4 R (the dword form of the LDS-DMA load writes lane l's dword at its base + 4 l).
+//   Each such load touches a separate cache line per row, as many lines as the step's data.
+//   When K is a multiple of 512, scale groups replace them: every fourth K step loads the 16
+//   scale bytes of four steps per row (one 16-byte load per row, into one of two group
+//   buffers: row R at 16 R), a quarter of the lines.
+// - Weight-gradient operands (block-major scales [P/32][C]): a step's 4 block rows of the
+//   wave's 128 channels are 4 runs of 128 contiguous bytes; one 16-byte load per lane (lane l:
+//   block l / 8, channels 16 (l % 8) ..) takes them and the next step's 4 (unused), stored
+//   [block][128 channels] per wave half.
 struct OpLoad {
   int vo[16];
-  int so[8];
-  int step, sstep;   // bytes per K step (data, scales)
+  int so[2];    // scale instructions (lane offsets)
+  int sstep;    // scale bytes per K step
 };
 
 // Rows row0 .. row0 + 127 of a row-major byte tensor with `ldb` bytes per row, and their scale
-// bytes (`lds_` bytes per row).  The byte form of the LDS-DMA load puts each lane's byte in a
-// dword slot of its own (checked on the device), so a stage keeps one dword per (row, K block):
-// 8 instructions of 16 rows x 4 blocks.  Bytes also serve the weight-gradient operands, whose
-// scales start at an expert's padded position / 32 and need not be 4-byte aligned.
+// dwords (`lds_` scale bytes per row, a multiple of 4): instruction i covers rows 64 i + lane.
 __device__ __forceinline__ void op_offsets(int row0, int ldb, int lds_, OpLoad& ld) {
   const int L = threadIdx.x & 63;
 #pragma unroll
@@ -152,9 +162,19 @@ __device__ __forceinline__ void op_offsets(int row0, int ldb, int lds_, OpLoad& 
     ld.vo[i] = (row0 + r) * ldb + 16 * ((L & 7) ^ kc_swz(r));
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ld.so[i] = (row0 + 16 * i + (L >> 2)) * lds_ + (L & 3);
-  ld.step = BK;
+  for (int i = 0; i < 2; ++i) ld.so[i] = (row0 + 64 * i + L) * lds_;
   ld.sstep = BK / 32;
+}
+
+// Scale group load J (rows 64 J + lane of the wave's half; the half adds 2048).
+template <int J>
+__device__ __forceinline__ void issue_sgrp(const OpLoad& ld, __amdgpu_buffer_rsrc_t rs, int ssoff, uint8_t* gdst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(gdst + 1024 * J), 16, ld.so[J], ssoff, 0, 0);
+}
+
+// Block-major scale load of a weight-gradient step (the wave half's slot: [8 blocks][128]).
+__device__ __forceinline__ void issue_sblk(const OpLoad& ld, __amdgpu_buffer_rsrc_t rs, int ssoff, uint8_t* sdst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)sdst, 16, ld.so[0], ssoff, 0, 0);
 }
 
 // One tile's DMA sources for this wave: data and scale descriptors bounded to the tile's valid
@@ -171,20 +191,20 @@ struct StepSrc {
 };
 
 template <int MODE>
-__device__ __forceinline__ StepSrc step_src(const Params& p, const OpLoad& ld, const TileSrc& src, bool role_b, int h,
+__device__ __forceinline__ StepSrc step_src(const Params& p, int sstep, const TileSrc& src, bool role_b, int h,
                                             int k) {
-  StepSrc ss{src.r0, src.s0, k * ld.step, k * ld.sstep};
+  StepSrc ss{src.r0, src.s0, k * BK, k * sstep};
   if constexpr (MODE == FWD1) {
     if (role_b && h) { ss.r = src.r1; ss.rs = src.s1; }
   } else if constexpr (MODE == DGRAD2) {
     const int kf = p.f / BK;
-    if (k >= kf) { ss.r = src.r1; ss.rs = src.s1; ss.soff = (k - kf) * ld.step; ss.ssoff = (k - kf) * ld.sstep; }
+    if (k >= kf) { ss.r = src.r1; ss.rs = src.s1; ss.soff = (k - kf) * BK; ss.ssoff = (k - kf) * sstep; }
   }
   if (k >= src.nk) { ss.r = make_rsrc(p.a0, 0); ss.rs = ss.r; ss.soff = 0; ss.ssoff = 0; }
   return ss;
 }
 
-// DMA instructions of a stage: data pieces [D0, D0 + ND) and scale pieces [S0, S0 + NS).
+// DMA instructions of a stage: data pieces [D0, D0 + ND) and per-row scale dwords [S0, S0 + NS).
 template <int D0, int ND, int S0, int NS>
 __device__ __forceinline__ void issue_part(const OpLoad& ld, const StepSrc& ss, uint8_t* dst, uint8_t* sdst) {
 #pragma unroll
@@ -192,7 +212,7 @@ __device__ __forceinline__ void issue_part(const OpLoad& ld, const StepSrc& ss, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ss.r, (lds_void*)(dst + i * 1024), 16, ld.vo[i], ss.soff, 0, 0);
 #pragma unroll
   for (int i = S0; i < S0 + NS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss.rs, (lds_void*)(sdst + i * 256), 1, ld.so[i], ss.ssoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss.rs, (lds_void*)(sdst + 256 * i), 4, ld.so[i], ss.ssoff, 0, 0);
 }
 
 // acc += x * y (scaled fp8), accumulating in place in AGPRs (tied inline asm; callers cover the
@@ -220,23 +240,26 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
 }
 
 // Fragment q (16 rows) of a stage: lane l reads row 16q + l % 16, chunks l/16 and 4 + l/16, and
-// the scale slot of that row and K block l/16.
+// the scale byte of that row and K block l/16 (`sq`: the lane's scale byte in fragment 0).
 template <int OFF>
 __device__ __forceinline__ void ds_b128(i32x4& v, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
 template <int OFF>
-__device__ __forceinline__ void ds_b32(int& v, uint32_t addr) {
-  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+__device__ __forceinline__ void ds_u8(int& v, uint32_t addr) {
+  asm volatile("ds_read_u8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
 
-template <int Q>
+// SST: bytes of scale slots per 16 rows (64 for dword slots, 256 for scale groups, 16 for the
+// block-major weight-gradient slots); `sq`: this lane's scale byte in fragment 0 of its operand
+// (the fragment offset qoff included).
+template <int Q, int SST>
 __device__ __forceinline__ void read_frag(i32x8& v, int& sw, uint32_t base, uint32_t sbase, uint32_t kc0,
-                                          uint32_t kc1, uint32_t srow, int qoff) {
+                                          uint32_t kc1, uint32_t sq, int qoff) {
   i32x4 lo, hi;
   ds_b128<2048 * Q>(lo, base + kc0 + 2048 * qoff);
   ds_b128<2048 * Q>(hi, base + kc1 + 2048 * qoff);
-  ds_b32<256 * Q>(sw, sbase + srow + 256 * qoff);
+  ds_u8<SST * Q>(sw, sbase + sq);
   v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -336,8 +359,9 @@ __device__ __forceinline__ TileSrc tile_src(const Params& p, const Tile& t, bool
       const uint8_t* sbase = (MODE == WGRAD_GU && t.half) ? p.a1s : p.a0s;
       const long long rem_rows = static_cast<long long>(Mtot) - t.m0;
       s.r0 = make_rsrc(base + static_cast<long long>(t.m0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
-      s.s0 = make_rsrc(sbase + static_cast<long long>(t.m0) * (p.P / 32) + t.k_begin / 32,
-                       rem_rows * (p.P / 32) - t.k_begin / 32);
+      // block-major scales [P/32][Mtot]: block rows from the expert's first, channels from m0
+      const long long sb0 = static_cast<long long>(t.k_begin / 32) * Mtot + t.m0;
+      s.s0 = make_rsrc(sbase + sb0, static_cast<long long>(p.P / 32) * Mtot - sb0);
       s.r1 = s.r0;
       s.s1 = s.s0;
     }
@@ -369,8 +393,8 @@ __device__ __forceinline__ TileSrc tile_src(const Params& p, const Tile& t, bool
       const int Ntot = n_total<MODE>(p);
       const long long rem_rows = static_cast<long long>(Ntot) - t.n0;
       s.r0 = make_rsrc(p.b0 + static_cast<long long>(t.n0) * p.P + t.k_begin, rem_rows * p.P - t.k_begin);
-      s.s0 = make_rsrc(p.b0s + static_cast<long long>(t.n0) * (p.P / 32) + t.k_begin / 32,
-                       rem_rows * (p.P / 32) - t.k_begin / 32);
+      const long long sb0 = static_cast<long long>(t.k_begin / 32) * Ntot + t.n0;
+      s.s0 = make_rsrc(p.b0s + sb0, static_cast<long long>(p.P / 32) * Ntot - sb0);
       s.r1 = s.r0;
       s.s1 = s.s0;
     }
@@ -383,6 +407,11 @@ __device__ __forceinline__ OpLoad op_load(const Params& p, bool role_b, int h) {
   OpLoad ld;
   if constexpr (Traits<MODE>::WGRAD) {
     op_offsets(128 * h, p.P, p.P / 32, ld);
+    // block-major scales of a [C][P] operand: lane l reads block l / 8, channels 16 (l % 8) ..
+    const int C = role_b ? n_total<MODE>(p) : (MODE == WGRAD_DOWN ? p.d : p.f);
+    const int L = threadIdx.x & 63;
+    ld.so[0] = (L >> 3) * C + 128 * h + 16 * (L & 7);
+    ld.sstep = (BK / 32) * C;
   } else {
     const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
     op_offsets(role_b && MODE == FWD1 ? 0 : 128 * h, K, K / 32, ld);
@@ -419,8 +448,9 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
 // steps of a workgroup's tiles form one stream through the two-stage rings: the barrier opening
 // step g waits for its DMA, and the DMA of step g+1 (in this tile or the next one) then goes into
 // the stages step g-1 used, spread over the first MFMA rows so the wave keeps issuing MFMAs.
-template <int MODE>
+template <int MODE, bool SGRP>
 __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
+  static_assert(!(SGRP && Traits<MODE>::WGRAD), "scale groups serve the forward and dgrad products");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -462,6 +492,9 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
   const bool role_b = wave < 2;
   const int h = wave & 1;
   const OpLoad ld = op_load<MODE>(p, role_b, h);
+  constexpr bool WG = Traits<MODE>::WGRAD;
+  constexpr int NSC = (SGRP || WG) ? 0 : 2;   // per-step, per-row scale dword instructions
+  constexpr int SST = SGRP ? 256 : (WG ? 16 : 64);
   Tile t = tile_at<MODE>(p, mts, ntiles_n, lid);
   TileSrc cur = tile_src<MODE>(p, t, role_b);
   int lid_n = lid + lstep;
@@ -476,10 +509,19 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
   const uint32_t stg = ring + STG_RING + wave * STG_BYTES;
   // per-lane fragment addresses: row l % 16 of each 16-row fragment, chunks l/16 and 4 + l/16
   const uint32_t kc0 = kc_off(lane & 15, lane >> 4), kc1 = kc_off(lane & 15, 4 + (lane >> 4));
-  const uint32_t srow = 16 * (lane & 15) + 4 * (lane >> 4);   // dword slot (row, K block l/16)
   const int qa = 8 * wm, qb = bfrag_base<MODE>(wn);
+  // scale byte of (row l % 16, K block l/16) in fragment 0 of each operand (scale groups add
+  // 4 (step % 4) per step; weight gradients: fragments 8.. are the second wave half's slot)
+  auto sq_of = [&](int qoff) -> uint32_t {
+    if constexpr (SGRP) return 16 * (lane & 15) + (lane >> 4) + 256 * qoff;
+    if constexpr (WG) return (qoff >> 3) * 1024 + 128 * (lane >> 4) + (lane & 15);
+    return 4 * (lane & 15) + (lane >> 4) + 64 * qoff;
+  };
+  const uint32_t sqa = sq_of(qa), sqb = sq_of(qb);
   uint8_t* const dst0 = lds_ring + (role_b ? B_RING : A_RING) + h * (OP_BYTES / 2);
-  uint8_t* const sdst0 = lds_ring + (role_b ? SB_RING : SA_RING) + h * (SC_BYTES / 2);
+  uint8_t* const sdst0 = lds_ring + (role_b ? SB_RING : SA_RING) + h * (SGRP ? 2048 : (WG ? 1024 : 512));
+  // scale groups: ig = buffer the next group load goes to, rg = buffer of the current step's group
+  int ig = 0, rg = 1;
 
   f32x4 acc[8][8];
   zero_acc(acc);
@@ -490,8 +532,14 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
   bool ready = false;
   for (;;) {
     if (!ready && cur.nk > 0) {
-      issue_part<0, 16, 0, 8>(ld, step_src<MODE>(p, ld, cur, role_b, h, 0), dst0 + st * OP_BYTES,
-                              sdst0 + st * SC_BYTES);
+      const StepSrc s0 = step_src<MODE>(p, ld.sstep, cur, role_b, h, 0);
+      issue_part<0, 16, 0, NSC>(ld, s0, dst0 + st * OP_BYTES, sdst0 + st * SC_BYTES);
+      if constexpr (WG) issue_sblk(ld, s0.rs, s0.ssoff, sdst0 + st * SC_BYTES);
+      if constexpr (SGRP) {
+        issue_sgrp<0>(ld, s0.rs, s0.ssoff, sdst0 + ig * SC_BYTES);
+        issue_sgrp<1>(ld, s0.rs, s0.ssoff, sdst0 + ig * SC_BYTES);
+        ig ^= 1;
+      }
       ready = true;
     }
     bool next_ready = false;
@@ -500,27 +548,39 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       const bool here = kt + 1 < cur.nk;
       next_ready = !here && nxt.nk > 0;
-      const StepSrc ns = here ? step_src<MODE>(p, ld, cur, role_b, h, kt + 1) : step_src<MODE>(p, ld, nxt, role_b, h, 0);
+      const StepSrc ns = here ? step_src<MODE>(p, ld.sstep, cur, role_b, h, kt + 1) : step_src<MODE>(p, ld.sstep, nxt, role_b, h, 0);
       uint8_t* const dst = dst0 + (st ^ 1) * OP_BYTES;
       uint8_t* const sdst = sdst0 + (st ^ 1) * SC_BYTES;
       const uint32_t a_base = ring + A_RING + st * OP_BYTES, b_base = ring + B_RING + st * OP_BYTES;
-      const uint32_t sa_base = ring + SA_RING + st * SC_BYTES, sb_base = ring + SB_RING + st * SC_BYTES;
+      if constexpr (SGRP) rg ^= (kt & 3) == 0 ? 1 : 0;
+      const uint32_t sc_off = SGRP ? rg * SC_BYTES + 4 * (kt & 3) : st * SC_BYTES;
+      const uint32_t sa_base = ring + SA_RING + sc_off, sb_base = ring + SB_RING + sc_off;
+      // scale groups: the step issued below starts a group (steps per tile are a multiple of 4)
+      const bool gnew = SGRP && (((here ? kt + 1 : 0) & 3) == 0);
+      uint8_t* const gdst = sdst0 + ig * SC_BYTES;
       i32x8 fa[8], fb[2];
       int xa[8], xb[2];
-      static_for<0, 8>([&](auto j) { read_frag<j>(fa[j], xa[j], a_base, sa_base, kc0, kc1, srow, qa); });
-      read_frag<bfrag_c<MODE, 0>()>(fb[0], xb[0], b_base, sb_base, kc0, kc1, srow, qb);
+      static_for<0, 8>([&](auto j) { read_frag<j, SST>(fa[j], xa[j], a_base, sa_base, kc0, kc1, sqa, qa); });
+      read_frag<bfrag_c<MODE, 0>(), SST>(fb[0], xb[0], b_base, sb_base, kc0, kc1, sqb, qb);
       // K blocks past the expert's padded range (wgrad only): scale 0 on both sides -> exact zero
       int live = 0xff;
       if constexpr (Traits<MODE>::WGRAD) live = (kt * BK + 32 * (lane >> 4) < t.k_len) ? 0xff : 0;
       static_for<0, 8>([&](auto i) {
-        // the next step's DMA, 6 instructions in each of the first four rows
-        if constexpr (i < 4) issue_part<4 * i, 4, 2 * i, 2>(ld, ns, dst, sdst);
+        // the next step's DMA: 4 data instructions in each of the first four rows, one scale
+        // instruction in each of the first NSC (or a scale group load in each of the first two
+        // when the next step starts a group)
+        if constexpr (i < 4) issue_part<4 * i, 4, i, (i < NSC ? 1 : 0)>(ld, ns, dst, sdst);
+        if constexpr (SGRP && i < 2) {
+          if (gnew) issue_sgrp<i>(ld, ns.rs, ns.ssoff, gdst);
+        }
+        if constexpr (WG && i == 0) issue_sblk(ld, ns.rs, ns.ssoff, sdst);
         if constexpr (i < 7)
-          read_frag<bfrag_c<MODE, i + 1>()>(fb[(i + 1) & 1], xb[(i + 1) & 1], b_base, sb_base, kc0, kc1, srow, qb);
+          read_frag<bfrag_c<MODE, i + 1>(), SST>(fb[(i + 1) & 1], xb[(i + 1) & 1], b_base, sb_base, kc0, kc1, sqb, qb);
         lgkm_wait<i < 7 ? 3 : 0>(fb[i & 1], xb[i & 1], fa, xa);
         const int sbv = xb[i & 1] & live;
         static_for<0, 8>([&](auto j) { mfma_acc(acc[i][j], fb[i & 1], fa[j], sbv, xa[j] & live); });
       });
+      if (gnew) ig ^= 1;
       st ^= 1;
       ++kt;
     }
@@ -567,7 +627,13 @@ int launch(const Params& p, hipStream_t s) {
   const long long pbig = static_cast<long long>(p.P) * (p.d > p.f ? p.d : p.f);
   MOE_REQUIRE(big < 0x7fffffffLL && wbig < 0x7fffffffLL && pbig < 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
               "MXFP8 grouped GEMM: an operand exceeds 2 GiB");
-  mx_grouped_gemm_kernel<MODE><<<static_cast<unsigned>(g), NTH, 0, s>>>(p);
+  // scale groups when every operand row's scale bytes are a multiple of 16 (K per tensor a
+  // multiple of 512: steps per tile and per DGRAD2 half then come in fours)
+  const int kh = MODE == DGRAD2 ? p.f : (MODE == FWD1 || MODE == DGRAD1 ? p.d : p.f);
+  if (!Traits<MODE>::WGRAD && kh % 512 == 0)
+    mx_grouped_gemm_kernel<MODE, !Traits<MODE>::WGRAD><<<static_cast<unsigned>(g), NTH, 0, s>>>(p);
+  else
+    mx_grouped_gemm_kernel<MODE, false><<<static_cast<unsigned>(g), NTH, 0, s>>>(p);
   return check_launch("grouped_gemm_mxfp8");
 }
 

@@ -4,7 +4,9 @@
 //   rows     blocks along the contiguous dim, output in the input's layout;
 //   cols     blocks along the strided dim, output transposed (each block contiguous again);
 //   grouped  token-axis blocks restarting at each expert group (padded to 32 rows), output
-//            transposed to [C, padded tokens]: the weight-gradient operands.
+//            transposed to [C, padded tokens]: the weight-gradient operands.  Their scales are
+//            stored block-major, [padded tokens / 32, C], so the scales of one K step of the
+//            weight-gradient products (4 blocks) for consecutive channels are contiguous.
 // rows and cols also come together from one read of the input (the weights, which the products
 // need quantised along each of their two dims).  All are HBM-bound: 2 bytes read, 1 + 1/32
 // bytes written per element and output.
@@ -47,10 +49,11 @@ constexpr int kPitch = kTC + 2;  // LDS row pitch in bf16 (33 words: column read
 
 // Each of the 256 threads quantises one (column, 32-position block) of the staged tile and
 // writes 32 bytes of q and one scale byte.  Lanes 4c..4c+3 take the 4 blocks of column c, so
-// they write 128 contiguous bytes.
+// they write 128 contiguous bytes.  The scale of (column c, block b) goes to
+// scale[c * s_col + b * s_blk] (b counted from position 0; `scale` based at the tile's column 0).
 __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch], int ncols, long long pos0,
                                                    long long out_pitch, uint8_t* __restrict__ q,
-                                                   uint8_t* __restrict__ scale) {
+                                                   uint8_t* __restrict__ scale, long long s_col, long long s_blk) {
   const int c = threadIdx.x >> 2;
   const int blk = threadIdx.x & 3;
   if (c >= ncols) return;
@@ -71,7 +74,7 @@ __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch
   uint8_t* dst = q + c * out_pitch + pos0 + blk * 32;
   reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
   reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  scale[c * (out_pitch / 32) + (pos0 / 32) + blk] = static_cast<uint8_t>(sh + 127);
+  scale[c * s_col + (pos0 / 32 + blk) * s_blk] = static_cast<uint8_t>(sh + 127);
 }
 
 // in [batch][rows][cols] -> q [batch][cols][rows], scale [batch][cols][rows/32]
@@ -98,7 +101,8 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
   const int blk = threadIdx.x & 3;
   if (r0 + blk * 32 >= rows) return;
   quant_tile_columns(tile, kTC, r0, rows, q + b * cols * static_cast<long long>(rows) + static_cast<long long>(c0) * rows,
-                     scale + b * cols * static_cast<long long>(rows / 32) + static_cast<long long>(c0) * (rows / 32));
+                     scale + b * cols * static_cast<long long>(rows / 32) + static_cast<long long>(c0) * (rows / 32),
+                     rows / 32, 1);
 }
 
 // ---- both layouts from one read (the weights, quantised along each of their two dims every
@@ -172,14 +176,14 @@ __global__ __launch_bounds__(256) void quant_both_kernel(const uint16_t* __restr
     // column blocks, as the column quantiser
     if (r0 + (threadIdx.x & 3) * 32 < rows)
       quant_tile_columns(tile, kTC, r0, rows, qT + b * plane + static_cast<long long>(c0) * rows,
-                         scaleT + b * (plane / 32) + static_cast<long long>(c0) * (rows / 32));
+                         scaleT + b * (plane / 32) + static_cast<long long>(c0) * (rows / 32), rows / 32, 1);
   }
 }
 
 // Grouped token-axis blocks.  Padded position p in [offsets_pad[e], offsets_pad[e+1]) holds
 // grouped row r = offsets[e] + (p - offsets_pad[e]) if r < offsets[e+1], else zero; positions
 // from offsets_pad[E] to n_pad_cap hold zeros.  Row r's data is in[row_token ? row_token[r] : r].
-// grid: (n_pad_cap/128, C/64).
+// q [C][n_pad_cap], scale [n_pad_cap/32][C].  grid: (n_pad_cap/128, C/64).
 __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __restrict__ in,
                                                             const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ offsets,
@@ -223,8 +227,7 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
     t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
   }
   __syncthreads();
-  quant_tile_columns(tile, kTC, p0, n_pad_cap, q + static_cast<long long>(c0) * n_pad_cap,
-                     scale + static_cast<long long>(c0) * (n_pad_cap / 32));
+  quant_tile_columns(tile, kTC, p0, n_pad_cap, q + static_cast<long long>(c0) * n_pad_cap, scale + c0, 1, C);
 }
 
 }  // namespace

@@ -208,7 +208,8 @@ def mx_pad_cap(n, E):
 
 
 def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None):
-    """Token-axis blocks per expert group: (qT [C, P], sT [C, P/32]), P = mx_pad_cap(n, E)."""
+    """Token-axis blocks per expert group: (qT [C, P], sT [P/32, C]), P = mx_pad_cap(n, E); the
+    scales are block-major (sT[b, c]: channel c, position block b)."""
     _check(x, torch.bfloat16, "x", 2)
     _check(offsets, torch.int32, "offsets", 1)
     _check(offsets_pad, torch.int32, "offsets_pad", 1)
@@ -216,7 +217,7 @@ def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None):
     C = x.shape[1]
     P = mx_pad_cap(n, E)
     q = _empty((C, P), torch.uint8, x)
-    s = _empty((C, P // 32), torch.uint8, x)
+    s = _empty((P // 32, C), torch.uint8, x)
     call("mxfp8_quantize_grouped", _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(offsets_pad), E, n, C,
          _ptr(q), _ptr(s), _stream(x))
     return q, s

@@ -176,8 +176,10 @@ int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int cols, uint8
  * positions [offsets_pad[e], offsets_pad[e] + count_e) of a padded token axis; padding
  * positions up to offsets_pad[e+1] hold zeros, and so does everything from offsets_pad[E] to
  * n_pad_cap.  offsets_pad must be the 32-padded prefix sum from moe_route_topk (pad = 32).
- *   out qT [C, n_pad_cap] E4M3, scaleT [C, n_pad_cap/32] E8M0, n_pad_cap = n + 32*E rounded
- *   up to a multiple of 128 (moe_mx_pad_cap). */
+ *   out qT [C, n_pad_cap] E4M3, n_pad_cap = n + 32*E rounded up to a multiple of 128
+ *   (moe_mx_pad_cap); scaleT [n_pad_cap/32, C] E8M0, block-major: the scale of channel c and
+ *   position block b is scaleT[b * C + c] (one weight-gradient K step of consecutive channels
+ *   reads contiguous bytes). */
 int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_token_or_null,
                            const int32_t* offsets, const int32_t* offsets_pad, int E, int n, int C,
                            uint8_t* qT, uint8_t* scaleT, void* stream);
@@ -260,8 +262,8 @@ int moe_grouped_gemm_swiglu_bwd(int dtype, int E, int n, int d, int f, const int
  *   The wgrad operands ("*_t") are token-major:
  *   bf16: the row tensors themselves (dyexp [n,d], a [n,f], dg, du [n,f], xp [n,d]);
  *     offsets_pad and all scales NULL.
- *   MXFP8: mxfp8_quantize_grouped outputs, [C, P] E4M3 + [C, P/32] with P = moe_mx_pad_cap(n, E)
- *     and offsets_pad the route's 32-padded offsets.
+ *   MXFP8: mxfp8_quantize_grouped outputs, [C, P] E4M3 + block-major scales [P/32, C], with
+ *     P = moe_mx_pad_cap(n, E) and offsets_pad the route's 32-padded offsets.
  * Weight gradients of experts with no rows are written as zeros. */
 int moe_grouped_gemm_dgrad_down(int dtype, int E, int n, int d, int f, const int32_t* offsets,
                                 const void* dyexp, const uint8_t* dyexp_scale, const void* w_down_t,

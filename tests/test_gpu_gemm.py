@@ -100,6 +100,8 @@ MX_CASES = [
     dict(T=600, d=512, E=5, k=2, f=384, seed=11, empty=(2,)),
     dict(T=300, d=256, E=4, k=2, f=256, seed=12, hot=0),
     dict(T=1000, d=384, E=9, k=3, f=128, seed=13, empty=(4,)),
+    # contraction dims multiples of 512: the forward and dgrad products load scales in groups
+    dict(T=700, d=1024, E=6, k=2, f=512, seed=14, empty=(3,)),
 ]
 
 

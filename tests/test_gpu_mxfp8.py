@@ -121,6 +121,7 @@ def test_grouped_token_blocks(T, E, k, C, gather):
     rq, rs = mxfp8.quantize_grouped(xp, off, offp)
     P = ops.mx_pad_cap(n, E)
     q, s = host(q), host(s)
-    assert q.shape == (C, P)
+    assert q.shape == (C, P) and s.shape == (P // 32, C)
+    s = s.T                                               # block-major on the device
     assert np.array_equal(q[:, : offp[E]], rq) and np.array_equal(s[:, : offp[E] // 32], rs)
     assert np.all(q[:, offp[E]:] == 0) and np.all(s[:, offp[E] // 32:] == 0)

@@ -263,7 +263,7 @@ def test_mxfp8_full_size():
 
         def grouped(dev_q, dev_s, src_rows_bits, C, name):
             gq = host(dev_q[:, p0:p0 + span])
-            gs = host(dev_s[:, p0 // 32:(p0 + span) // 32])
+            gs = host(dev_s[p0 // 32:(p0 + span) // 32, :]).T   # scales are block-major
             rq_, rs_ = mxfp8.quantize_grouped(src_rows_bits, one_off, one_pad)
             assert gq.shape == (C, span) and np.array_equal(gq, rq_) and np.array_equal(gs, rs_), f"{name}[{e}]"
             return mxfp8.dequantize_blocks(gq, gs)
