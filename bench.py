@@ -131,7 +131,7 @@ def traffic_of(cfg, call):
     path = os.path.join(ROOT, "profiles", f"{call}_{dtype}_{tag}_traffic.txt")
     t = profsum.read_traffic(path)
     if (t is None or t.get("source_sha256") != profsum.source_sha256(dtype)
-            or t.get("kernel") != profsum.kernel_name(call, dtype)):
+            or t.get("kernel") != profsum.kernel_name(call, dtype, cfg.d, cfg.f)):
         return None
     return float(t["traffic_bytes"])
 
@@ -224,7 +224,7 @@ def main():
                    "top_k": cfg.k, "d_ff": cfg.f, "fwd_bwd": not cfg.forward_only},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic_of(cfg, dom),
-                     "kernel": f"{profsum.kernel_name(dom, dtype)} ({dom})",
+                     "kernel": f"{profsum.kernel_name(dom, dtype, cfg.d, cfg.f)} ({dom})",
                      "avg_ms": round(gemm_ms[dom], 4), "flop_per_launch": flops[dom],
                      "algorithmic_bytes": round(gemm_bytes(cfg, dom))},
         "gemm_ms": {c: round(v, 4) for c, v in gemm_ms.items()},

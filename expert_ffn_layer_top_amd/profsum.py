@@ -38,9 +38,19 @@ CALL_MODE = {"gate_up": 0, "down": 1, "dgrad_down": 2, "dgrad_gate_up": 3, "wgra
 COPY_KERNEL = "neg_kernel"
 
 
-def kernel_name(call, dtype):
-    ns = "moe::gg::grouped_gemm_kernel" if dtype == "bf16" else "moe::gmx::mx_grouped_gemm_kernel"
-    return f"{ns}<{CALL_MODE[call]}>"
+def mx_scale_groups(call, d, f):
+    """Whether the MXFP8 kernel of `call` loads its scales in four-step groups: the library does
+    so for the forward and dgrad products whose contraction dim per operand is a multiple of 512."""
+    k = {"gate_up": d, "down": f, "dgrad_down": d, "dgrad_gate_up": f}.get(call)
+    return k is not None and k % 512 == 0
+
+
+def kernel_name(call, dtype, d, f):
+    """rocprofv3 name of the kernel behind a grouped-GEMM call at model dims d, f."""
+    if dtype == "bf16":
+        return f"moe::gg::grouped_gemm_kernel<{CALL_MODE[call]}>"
+    flag = "true" if mx_scale_groups(call, d, f) else "false"
+    return f"moe::gmx::mx_grouped_gemm_kernel<{CALL_MODE[call]}, {flag}>"
 
 
 def source_sha256(dtype):
