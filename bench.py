@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--recompute", action="store_true",
+                    help="per-layer activation recompute: the backward re-runs the gate/up product")
     return ap.parse_args()
 
 
@@ -71,7 +73,7 @@ def gemm_flops(cfg):
     """Algorithmic flop of each grouped-GEMM call over the routed rows (n = T k)."""
     ndf = float(cfg.n) * cfg.d * cfg.f
     return {"gate_up": 4 * ndf, "down": 2 * ndf, "dgrad_down": 2 * ndf, "wgrad_down": 2 * ndf,
-            "dgrad_gate_up": 4 * ndf, "wgrad_gate_up": 4 * ndf}
+            "dgrad_gate_up": 4 * ndf, "wgrad_gate_up": 4 * ndf, "recompute": 4 * ndf}
 
 
 def copy_probe(nbytes):
@@ -84,7 +86,7 @@ def copy_probe(nbytes):
     del src, dst
 
 
-def run_gpu(cfg, steps, warmup, probe_bytes=0):
+def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False):
     import torch
 
     import synth
@@ -99,12 +101,14 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0):
         w.quantize_mx()
     x, dy, logits = inputs["x"], inputs["dy"], inputs.get("logits")
     calls = layer.GEMM_CALLS if not cfg.forward_only else ("gate_up", "down")
+    if recompute and not cfg.forward_only:
+        calls = calls + (layer.RECOMPUTE_CALL,)
     rows = layer.ROW_CALLS if not cfg.forward_only else ("route", "permute", "combine")
 
     def step(events=None):
         if cfg.mxfp8:
             w.quantize_mx()                  # weights are re-quantised every step (both directions)
-        ctx = layer.forward(x, w, cfg.k, logits=logits, mxfp8=cfg.mxfp8, events=events)
+        ctx = layer.forward(x, w, cfg.k, logits=logits, mxfp8=cfg.mxfp8, events=events, recompute=recompute)
         if not cfg.forward_only:
             layer.backward(ctx, w, dy, events=events)
 
@@ -154,6 +158,8 @@ def gemm_bytes(cfg, call):
     once (bf16 2 B; MXFP8 operands 1 B + 1/32 B of scale)."""
     n, d, f, E = float(cfg.n), cfg.d, cfg.f, cfg.E
     ob = 1 + 1 / 32 if cfg.mxfp8 else 2
+    if call == "recompute":
+        call = "gate_up"
     return {"gate_up": ob * (n * d + 2 * E * f * d) + 2 * 3 * n * f,
             "down": ob * (n * f + E * d * f) + 2 * n * d,
             "dgrad_down": ob * (n * d + E * d * f) + 2 * 2 * n * f + 2 * 2 * n * f,
@@ -197,11 +203,11 @@ def main():
               file=sys.stderr)
         return 2
     cfg = workload_config(args)
-    elapsed, gemm_ms, row_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe)
+    elapsed, gemm_ms, row_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe, args.recompute)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
     flops = gemm_flops(cfg)
-    cand = [c for c in gemm_ms if not (cfg.mxfp8 and c == "down")]
+    cand = [c for c in gemm_ms if not (cfg.mxfp8 and c == "down") and c != "recompute"]
     dom = max(cand, key=lambda c: gemm_ms[c])
     achieved = flops[dom] / (gemm_ms[dom] * 1e-3) / 1e12
     peak = PEAK_MXFP8_TFLOPS if cfg.mxfp8 else PEAK_BF16_TFLOPS
@@ -221,7 +227,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": describe(cfg), "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
-                   "top_k": cfg.k, "d_ff": cfg.f, "fwd_bwd": not cfg.forward_only},
+                   "top_k": cfg.k, "d_ff": cfg.f, "fwd_bwd": not cfg.forward_only,
+                   "activation_recompute": bool(args.recompute)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic_of(cfg, dom),
                      "kernel": f"{profsum.kernel_name(dom, dtype, cfg.d, cfg.f)} ({dom})",

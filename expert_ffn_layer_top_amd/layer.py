@@ -65,17 +65,23 @@ class _Span:
 
 
 # names of the calls `forward` and `backward` can bracket with events: each grouped-GEMM call is
-# one kernel ("down" under MXFP8 also quantises a along f first); ROW_CALLS are the routing and
+# one kernel ("down" under MXFP8 also quantises a along f first; "recompute" is the gate/up product
+# again, in the backward of a forward run with recompute=True); ROW_CALLS are the routing and
 # row-movement calls (route: its three kernels)
 GEMM_CALLS = ("gate_up", "down", "dgrad_down", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up")
+RECOMPUTE_CALL = "recompute"
 ROW_CALLS = ("route", "permute", "combine", "combine_bwd", "permute_bwd", "route_bwd")
 
 
-def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=None):
+def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=None, recompute=False):
     """Layer forward.  x [T, d] bf16; logits [T, E] fp32 unless weights.w_r is given.
     Returns the context dict that `backward` consumes (all intermediate tensors), with y.
     events: optional {name: (start, end)} of torch.cuda.Event pairs, recorded on the current
-    stream around the calls named in GEMM_CALLS and ROW_CALLS."""
+    stream around the calls named in GEMM_CALLS and ROW_CALLS.
+    recompute: keep neither G, U nor A (3 n f bf16 values) for the backward, which then runs the
+    gate/up product again on the kept permuted input (per-layer activation recompute, [card]
+    "Supercharging Olmo-core ...": used at the largest scale).  The kernels are deterministic,
+    so the backward's results are bit-identical either way."""
     ctx = dict(x=x, k=k, mxfp8=mxfp8)
     if logits is None:
         logits = ops.router_project(x, weights.w_r)
@@ -102,7 +108,11 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
                                                scales=(xps, q["wg_s"], q["wu_s"]))
         with _Span(events, "down"):
             yexp = ops.grouped_gemm_down(a, r["offsets"], q["wd"], w_down_scale=q["wd_s"])
-    ctx.update(g=g, u=u, a=a, yexp=yexp)
+    if recompute:
+        del g, u, a
+        ctx.update(g=None, u=None, a=None, yexp=yexp)
+    else:
+        ctx.update(g=g, u=u, a=a, yexp=yexp)
     with _Span(events, "combine"):
         ctx["y"] = ops.unpermute_combine(yexp, r["topk_gate"], r["dest"])
     return ctx
@@ -132,6 +142,15 @@ def backward(ctx, weights, dy, events=None):
         out["dx_router"] = addend
     off = ctx["offsets"]
     g, u, a = ctx["g"], ctx["u"], ctx["a"]
+    if g is None:
+        # activation recompute: the forward's gate/up product again (same kernel, same inputs)
+        with _Span(events, RECOMPUTE_CALL):
+            if not ctx["mxfp8"]:
+                g, u, a = ops.grouped_gemm_gate_up(ctx["xp"], off, weights.w_gate, weights.w_up)
+            else:
+                q = weights.mx
+                g, u, a = ops.grouped_gemm_gate_up(ctx["xpq"], off, q["wg"], q["wu"],
+                                                   scales=(ctx["xps"], q["wg_s"], q["wu_s"]))
     if not ctx["mxfp8"]:
         with _Span(events, "dgrad_down"):
             dg, du = ops.grouped_gemm_dgrad_down(dyexp, off, weights.w_down, g, u)

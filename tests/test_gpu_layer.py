@@ -144,3 +144,27 @@ def test_balanced_full_size_backward_samples(balanced_run):
     dxp = bits(out["dxp"])
     dx_ref = moe.permute_bwd(dxp, dest[toks])
     assert_close(codecs.bf16_to_f64(bits(out["dx"])[toks]), dx_ref, BF16_TOL, "dx tokens")
+
+
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
+def test_activation_recompute_bit_identical(mx):
+    """Per-layer activation recompute: the forward keeps no G, U, A and the backward runs the
+    gate/up product again; every backward output equals the stored-activation run bit for bit."""
+    import torch
+    from expert_ffn_layer_top_amd import layer
+    base = synth.CONFIGS["mxfp8" if mx else "tiny"]
+    cfg = base.with_(T=640, d=512, E=6, k=2, f=512) if mx else base
+    inputs = synth.make_inputs(cfg)
+    t = synth.to_torch(inputs, torch.device("cuda:0"))
+    w = layer.Weights(t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"))
+    outs = []
+    for rc in (False, True):
+        note(f"layer recompute={rc} mxfp8={mx} T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f}")
+        ctx = layer.forward(t["x"], w, cfg.k, logits=t.get("logits"), mxfp8=mx, recompute=rc)
+        assert (ctx["g"] is None) == rc and (ctx["a"] is None) == rc
+        outs.append((ctx, layer.backward(ctx, w, t["dy"])))
+    torch.cuda.synchronize()
+    (c0, o0), (c1, o1) = outs
+    assert torch.equal(c0["y"], c1["y"])
+    for key in ("dx", "d_logits", "dw_gate", "dw_up", "dw_down", "dg", "du", "dxp"):
+        assert torch.equal(o0[key], o1[key]), f"{key}: recompute run differs"
