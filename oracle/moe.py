@@ -260,6 +260,40 @@ def route_topk_bwd(gate, topk_idx, d_gate, E):
     return dl
 
 
+def router_balance(probs, counts, k):
+    """Load-balancing score of the router and balance statistics of the actual load.
+
+    The pages name a routing-balance score and warn that it can improve while the real
+    workload grows less balanced ("token gerrymandering"); they give no formula.  Reading:
+    the usual auxiliary load-balancing loss of top-k routers, next to statistics of the
+    counts themselves, so both views can be compared.
+      f_e      = counts[e] / (T k)          share of routed (token, slot) pairs expert e gets
+      P_e      = mean over tokens of probs[t, e]   (full softmax over all experts)
+      aux      = E * sum_e f_e P_e          1 when f or P is uniform, E when both sit on one expert
+      load_max = E * max_e f_e              largest expert load over the mean load
+      prob_max = E * max_e P_e
+      load_cv  = std_e(f) / mean_e(f)        (population standard deviation)
+    Returns dict(aux, load_max, prob_max, load_cv, p_mean [E]) in float64.
+    """
+    pr = np.asarray(probs, dtype=np.float64)
+    T, E = pr.shape
+    f = np.asarray(counts, dtype=np.float64) / (T * k)
+    P = pr.sum(axis=0) / T
+    return dict(aux=E * float(np.sum(f * P)), load_max=E * float(f.max()), prob_max=E * float(P.max()),
+                load_cv=float(f.std() / f.mean()), p_mean=P)
+
+
+def router_balance_bwd(probs, counts, k, weight):
+    """Gradient of weight * aux (router_balance) w.r.t. the logits, the counts held constant
+    (they come from a discrete selection).  With c_e = weight * E * f_e / T = d(weight aux)/dp[t,e]
+    and the softmax Jacobian dp[t,e]/dlogits[t,e'] = p[t,e] (delta_ee' - p[t,e']):
+        d_logits[t, e'] = p[t, e'] * (c_e' - sum_e p[t, e] c_e)."""
+    pr = np.asarray(probs, dtype=np.float64)
+    T, E = pr.shape
+    c = weight * E * (np.asarray(counts, dtype=np.float64) / (T * k)) / T
+    return pr * (c[None, :] - (pr @ c)[:, None])
+
+
 def router_project_bwd(x_bf16, w_r, d_logits):
     """Backward of logits = x @ w_r:  dx_router = d_logits @ w_r^T,  dw_r = x^T @ d_logits."""
     X = bf16_to_f64(x_bf16)
