@@ -24,6 +24,9 @@ SIGNATURES = {
     "moe_route_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_route_topk": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _sz, _p]),
     "moe_route_topk_bwd": (_i, [_p, _p, _p, _i, _i, _i, _p, _p]),
+    "moe_route_balance_workspace_bytes": (_sz, [_i, _i]),
+    "moe_route_balance": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _sz, _p]),
+    "moe_route_topk_bwd_balance": (_i, [_p, _p, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p]),
     "moe_permute": (_i, [_i, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
     "moe_unpermute_combine": (_i, [_p, _p, _p, _i, _i, _i, _p, _p]),
     "moe_unpermute_combine_bwd": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),

@@ -242,13 +242,30 @@ __global__ __launch_bounds__(256) void route_finalize(const int32_t* __restrict_
   if (row_token != nullptr) row_token[r] = static_cast<int32_t>(t);
 }
 
+// One wave per token.  With `probs` given, the gradient of the balance score (weighted) is added:
+// c_e = cscale * counts[e] (cscale = weight E / (T^2 k)) and the term p[t,e] (c_e - sum_e' p c).
 __global__ __launch_bounds__(256) void route_topk_bwd_kernel(const float* __restrict__ gate,
                                                              const int32_t* __restrict__ idx,
                                                              const float* __restrict__ dgate, int T,
-                                                             int E, int k, float* __restrict__ dlogits) {
+                                                             int E, int k, const float* __restrict__ probs,
+                                                             const int32_t* __restrict__ counts, float cscale,
+                                                             float* __restrict__ dlogits) {
   const long long t = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
+  // balance term: this lane's experts e = lane + 64 i (E <= 256)
+  float pb[kMaxE / 64], cb[kMaxE / 64];
+  float pc = 0.f;
+  if (probs != nullptr) {
+#pragma unroll
+    for (int i = 0; i < kMaxE / 64; ++i) {
+      const int e = lane + 64 * i;
+      pb[i] = e < E ? probs[t * E + e] : 0.f;
+      cb[i] = e < E ? cscale * static_cast<float>(counts[e]) : 0.f;
+      pc += pb[i] * cb[i];
+    }
+    pc = wave_sum(pc);
+  }
   const float g_l = (lane < k) ? gate[t * k + lane] : 0.f;
   const float dg_l = (lane < k) ? dgate[t * k + lane] : 0.f;
   const int e_l = (lane < k) ? idx[t * k + lane] : -1;
@@ -262,12 +279,68 @@ __global__ __launch_bounds__(256) void route_topk_bwd_kernel(const float* __rest
     ej[j] = __shfl(e_l, j, 64);
     vj[j] = __shfl(val_l, j, 64);
   }
-  for (int e = lane; e < E; e += 64) {
+#pragma unroll
+  for (int i = 0; i < kMaxE / 64; ++i) {
+    const int e = lane + 64 * i;
+    if (e >= E) break;
     float v = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
       if (j < k && ej[j] == e) v = vj[j];
+    if (probs != nullptr) v += pb[i] * (cb[i] - pc);
     dlogits[t * E + e] = v;
+  }
+}
+
+// ---- balance score: P_e = mean_t probs[t,e] by a fixed-order two-pass sum, then the statistics
+constexpr int kBalTokens = 256;   // tokens per first-pass block
+
+// part[b][e] = sum of probs[t][e] over block b's tokens (thread e sums column e; E <= 256).
+__global__ __launch_bounds__(256) void balance_partial(const float* __restrict__ probs, int T, int E,
+                                                       float* __restrict__ part) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const long long t0 = static_cast<long long>(blockIdx.x) * kBalTokens;
+  const long long t1 = min(static_cast<long long>(T), t0 + kBalTokens);
+  float s = 0.f;
+  for (long long t = t0; t < t1; ++t) s += probs[t * E + e];
+  part[static_cast<long long>(blockIdx.x) * E + e] = s;
+}
+
+// One block: P_e, then aux = E sum f_e P_e, load_max = E max f, prob_max = E max P,
+// load_cv = std(f) / mean(f), with f_e = counts[e] / (T k).
+__global__ __launch_bounds__(256) void balance_finish(const float* __restrict__ part, int nb, int T, int E, int k,
+                                                      const int32_t* __restrict__ counts, float* __restrict__ p_mean,
+                                                      float* __restrict__ stats) {
+  __shared__ float red[3][256];
+  const int e = threadIdx.x;
+  float P = 0.f, f = 0.f;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) P += part[static_cast<long long>(b) * E + e];
+    P /= static_cast<float>(T);
+    f = static_cast<float>(counts[e]) / (static_cast<float>(T) * static_cast<float>(k));
+    p_mean[e] = P;
+  }
+  red[0][e] = f * P;
+  red[1][e] = f;
+  red[2][e] = P;
+  __syncthreads();
+  if (e == 0) {
+    float fp = 0.f, fmax = 0.f, pmax = 0.f, fs = 0.f;
+    for (int i = 0; i < E; ++i) {   // fixed order
+      fp += red[0][i];
+      fmax = fmaxf(fmax, red[1][i]);
+      pmax = fmaxf(pmax, red[2][i]);
+      fs += red[1][i];
+    }
+    const float mean = fs / E;
+    float ss = 0.f;                 // squared deviations (no cancellation when the load is even)
+    for (int i = 0; i < E; ++i) ss += (red[1][i] - mean) * (red[1][i] - mean);
+    const float var = ss / E;
+    stats[0] = E * fp;
+    stats[1] = E * fmax;
+    stats[2] = E * pmax;
+    stats[3] = mean > 0.f ? sqrtf(var) / mean : 0.f;
   }
 }
 
@@ -321,6 +394,39 @@ extern "C" int moe_route_topk_bwd(const float* topk_gate, const int32_t* topk_id
                                   int T, int E, int k, float* d_logits, void* stream) {
   if (int st = check_layer_shape(T, E, k)) return st;
   MOE_CHECK_PTR(topk_gate); MOE_CHECK_PTR(topk_idx); MOE_CHECK_PTR(d_gate); MOE_CHECK_PTR(d_logits);
-  route_topk_bwd_kernel<<<(T + 3) / 4, 256, 0, as_stream(stream)>>>(topk_gate, topk_idx, d_gate, T, E, k, d_logits);
+  route_topk_bwd_kernel<<<(T + 3) / 4, 256, 0, as_stream(stream)>>>(topk_gate, topk_idx, d_gate, T, E, k, nullptr,
+                                                                    nullptr, 0.f, d_logits);
   return check_launch("route_topk_bwd");
+}
+
+extern "C" int moe_route_topk_bwd_balance(const float* topk_gate, const int32_t* topk_idx, const float* d_gate,
+                                          const float* probs, const int32_t* counts, float weight, int T, int E,
+                                          int k, float* d_logits, void* stream) {
+  if (int st = check_layer_shape(T, E, k)) return st;
+  MOE_CHECK_PTR(topk_gate); MOE_CHECK_PTR(topk_idx); MOE_CHECK_PTR(d_gate); MOE_CHECK_PTR(d_logits);
+  MOE_CHECK_PTR(probs); MOE_CHECK_PTR(counts);
+  MOE_REQUIRE(std::isfinite(weight), MOE_ERR_INVALID_ARG, "balance weight must be finite");
+  const double cscale = static_cast<double>(weight) * E / (static_cast<double>(T) * T * k);
+  route_topk_bwd_kernel<<<(T + 3) / 4, 256, 0, as_stream(stream)>>>(topk_gate, topk_idx, d_gate, T, E, k, probs,
+                                                                    counts, static_cast<float>(cscale), d_logits);
+  return check_launch("route_topk_bwd_balance");
+}
+
+extern "C" size_t moe_route_balance_workspace_bytes(int T, int E) {
+  if (T < 1 || E < 1) return 0;
+  return static_cast<size_t>((T + kBalTokens - 1) / kBalTokens) * E * sizeof(float);
+}
+
+extern "C" int moe_route_balance(const float* probs, const int32_t* counts, int T, int E, int k, float* p_mean,
+                                 float* stats, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_layer_shape(T, E, k)) return st;
+  MOE_CHECK_PTR(probs); MOE_CHECK_PTR(counts); MOE_CHECK_PTR(p_mean); MOE_CHECK_PTR(stats);
+  const size_t need = moe_route_balance_workspace_bytes(T, E);
+  MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "route balance workspace: need %zu bytes", need);
+  const int nb = (T + kBalTokens - 1) / kBalTokens;
+  hipStream_t s = as_stream(stream);
+  balance_partial<<<nb, 256, 0, s>>>(probs, T, E, static_cast<float*>(ws));
+  if (int st = check_launch("route_balance partial")) return st;
+  balance_finish<<<1, 256, 0, s>>>(static_cast<const float*>(ws), nb, T, E, k, counts, p_mean, stats);
+  return check_launch("route_balance finish");
 }

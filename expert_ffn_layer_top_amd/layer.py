@@ -73,7 +73,8 @@ RECOMPUTE_CALL = "recompute"
 ROW_CALLS = ("route", "permute", "combine", "combine_bwd", "permute_bwd", "route_bwd")
 
 
-def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=None, recompute=False):
+def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=None, recompute=False,
+            balance_weight=None):
     """Layer forward.  x [T, d] bf16; logits [T, E] fp32 unless weights.w_r is given.
     Returns the context dict that `backward` consumes (all intermediate tensors), with y.
     events: optional {name: (start, end)} of torch.cuda.Event pairs, recorded on the current
@@ -81,14 +82,21 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
     recompute: keep neither G, U nor A (3 n f bf16 values) for the backward, which then runs the
     gate/up product again on the kept permuted input (per-layer activation recompute, [card]
     "Supercharging Olmo-core ...": used at the largest scale).  The kernels are deterministic,
-    so the backward's results are bit-identical either way."""
-    ctx = dict(x=x, k=k, mxfp8=mxfp8)
+    so the backward's results are bit-identical either way.
+    balance_weight: also compute the router's load-balancing score and the balance statistics of
+    the actual load (ctx["balance"]: p_mean [E], stats [aux, load_max, prob_max, load_cv]), and
+    add the gradient of balance_weight * aux to d_logits in the backward."""
+    ctx = dict(x=x, k=k, mxfp8=mxfp8, balance_weight=balance_weight)
+    want_probs = want_probs or balance_weight is not None
     if logits is None:
         logits = ops.router_project(x, weights.w_r)
     ctx["logits"] = logits
     with _Span(events, "route"):
         r = ops.route_topk(logits, k, want_probs=want_probs, pad=32 if mxfp8 else None)
     ctx.update(r)
+    if balance_weight is not None:
+        p_mean, stats = ops.route_balance(r["probs"], r["counts"], k)
+        ctx["balance"] = dict(p_mean=p_mean, stats=stats)
     if not mxfp8:
         with _Span(events, "permute"):
             xp = ops.permute(x, r["dest"])
@@ -135,7 +143,10 @@ def backward(ctx, weights, dy, events=None):
     out.update(dyexp=dyexp, d_gate=dgate)
     E = ctx["logits"].shape[1]
     with _Span(events, "route_bwd"):
-        out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E)
+        bal = None
+        if ctx.get("balance_weight") is not None:
+            bal = (ctx["probs"], ctx["counts"], ctx["balance_weight"])
+        out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E, balance=bal)
     addend = None
     if weights.w_r is not None:
         addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])

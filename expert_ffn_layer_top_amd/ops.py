@@ -91,16 +91,39 @@ def route_topk(logits, k, want_probs=False, pad=None, want_row_token=True):
     return out
 
 
-def route_topk_bwd(topk_gate, topk_idx, d_gate, E):
-    """d_logits [T,E] fp32."""
+def route_topk_bwd(topk_gate, topk_idx, d_gate, E, balance=None):
+    """d_logits [T,E] fp32.  balance = (probs [T,E] fp32, counts [E] int32, weight): also the
+    gradient of weight * the balance score (route_balance), counts held fixed."""
     _check(topk_gate, torch.float32, "topk_gate", 2)
     _check(topk_idx, torch.int32, "topk_idx", 2)
     _check(d_gate, torch.float32, "d_gate", 2)
     T, k = topk_idx.shape
     dl = _empty((T, E), torch.float32, topk_gate)
-    call("moe_route_topk_bwd", _ptr(topk_gate), _ptr(topk_idx), _ptr(d_gate), T, E, k, _ptr(dl),
-         _stream(topk_gate))
+    if balance is None:
+        call("moe_route_topk_bwd", _ptr(topk_gate), _ptr(topk_idx), _ptr(d_gate), T, E, k, _ptr(dl),
+             _stream(topk_gate))
+    else:
+        probs, counts, weight = balance
+        _check(probs, torch.float32, "probs", 2)
+        _check(counts, torch.int32, "counts", 1)
+        assert probs.shape == (T, E) and counts.shape == (E,)
+        call("moe_route_topk_bwd_balance", _ptr(topk_gate), _ptr(topk_idx), _ptr(d_gate), _ptr(probs),
+             _ptr(counts), float(weight), T, E, k, _ptr(dl), _stream(topk_gate))
     return dl
+
+
+def route_balance(probs, counts, k):
+    """(p_mean [E] fp32, stats [4] fp32 = aux, load_max, prob_max, load_cv), on the device."""
+    _check(probs, torch.float32, "probs", 2)
+    _check(counts, torch.int32, "counts", 1)
+    T, E = probs.shape
+    p_mean = _empty((E,), torch.float32, probs)
+    stats = _empty((4,), torch.float32, probs)
+    nbytes = lib.moe_route_balance_workspace_bytes(T, E)
+    ws = _empty((max(nbytes, 1),), torch.uint8, probs)
+    call("moe_route_balance", _ptr(probs), _ptr(counts), T, E, k, _ptr(p_mean), _ptr(stats), _ptr(ws), nbytes,
+         _stream(probs))
+    return p_mean, stats
 
 
 # ---------------------------------------------------------------- rows

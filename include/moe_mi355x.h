@@ -123,6 +123,27 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, 
 int moe_route_topk_bwd(const float* topk_gate, const int32_t* topk_idx, const float* d_gate, int T,
                        int E, int k, float* d_logits, void* stream);
 
+/* Router load-balancing score and balance statistics of the actual load ([news] "Four failure
+ * modes from the report": a routing-balance score can improve while the workload grows less
+ * balanced, "token gerrymandering"; the pages give no formula, this is the usual auxiliary
+ * load-balancing loss of top-k routers):
+ *   f_e = counts[e] / (T k),  P_e = mean over tokens of probs[t, e]
+ *   out  p_mean [E] fp32 = P;  stats [4] fp32 = { aux = E sum_e f_e P_e, load_max = E max_e f_e,
+ *        prob_max = E max_e P_e, load_cv = std_e(f) / mean_e(f) }
+ *   in   probs [T,E] fp32 (moe_route_topk's full softmax), counts [E] int32 (its counts)
+ *   ws   at least moe_route_balance_workspace_bytes(T, E) bytes (contents ignored).
+ * Sums run in a fixed order: results are bit-reproducible. */
+size_t moe_route_balance_workspace_bytes(int T, int E);
+int moe_route_balance(const float* probs, const int32_t* counts, int T, int E, int k, float* p_mean,
+                      float* stats, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_route_topk_bwd plus the gradient of weight * aux (moe_route_balance), counts held fixed:
+ * d_logits[t,e] += p[t,e] (c_e - sum_e' p[t,e'] c_e'), c_e = weight E f_e / T.  Written, not
+ * accumulated (the whole d_logits [T,E] is produced).  weight must be finite. */
+int moe_route_topk_bwd_balance(const float* topk_gate, const int32_t* topk_idx, const float* d_gate,
+                               const float* probs, const int32_t* counts, float weight, int T, int E,
+                               int k, float* d_logits, void* stream);
+
 /* ---------------------------------------------------------------- rows */
 
 /* Rowwise permute: xp[dest[t,j], :] = x[t, :] for every slot j, a bit copy

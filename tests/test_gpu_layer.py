@@ -168,3 +168,26 @@ def test_activation_recompute_bit_identical(mx):
     assert torch.equal(c0["y"], c1["y"])
     for key in ("dx", "d_logits", "dw_gate", "dw_up", "dw_down", "dg", "du", "dxp"):
         assert torch.equal(o0[key], o1[key]), f"{key}: recompute run differs"
+
+
+def test_layer_balance_score_in_step():
+    """balance_weight: the forward reports the balance score and load statistics, and the
+    backward's d_logits carries the score's gradient on top of the route term."""
+    import torch
+    from expert_ffn_layer_top_amd import layer
+    cfg = synth.CONFIGS["tiny"]
+    inputs = synth.make_inputs(cfg)
+    t = synth.to_torch(inputs, torch.device("cuda:0"))
+    w = layer.Weights(t["w_gate"], t["w_up"], t["w_down"], w_r=t["w_r"])
+    note("layer tiny with balance score")
+    wb = 0.5
+    ctx = layer.forward(t["x"], w, cfg.k, balance_weight=wb)
+    out = layer.backward(ctx, w, t["dy"])
+    torch.cuda.synchronize()
+    probs, counts = host(ctx["probs"]), host(ctx["counts"])
+    ref = moe.router_balance(probs, counts, cfg.k)
+    stats = host(ctx["balance"]["stats"])
+    assert abs(stats[0] - ref["aux"]) < 1e-5 * ref["aux"] and stats[1] == np.float32(ref["load_max"])
+    d_ref = (moe.route_topk_bwd(host(ctx["topk_gate"]), host(ctx["topk_idx"]), host(out["d_gate"]), cfg.E)
+             + moe.router_balance_bwd(probs, counts, cfg.k, wb))
+    assert_close(host(out["d_logits"]), d_ref, 1e-5, "d_logits with balance term")
