@@ -183,7 +183,10 @@ __global__ __launch_bounds__(256) void quant_both_kernel(const uint16_t* __restr
 // Grouped token-axis blocks.  Padded position p in [offsets_pad[e], offsets_pad[e+1]) holds
 // grouped row r = offsets[e] + (p - offsets_pad[e]) if r < offsets[e+1], else zero; positions
 // from offsets_pad[E] to n_pad_cap hold zeros.  Row r's data is in[row_token ? row_token[r] : r].
-// q [C][n_pad_cap], scale [n_pad_cap/32][C].  grid: (n_pad_cap/128, C/64).
+// q [C][n_pad_cap], scale [n_pad_cap/32][C].  A workgroup takes a 128-position band and walks
+// kBothTiles column tiles of it (the rows' adjacent 128-byte pieces, read close together in time,
+// with the next tile's loads in flight while the current one is quantised); the band's source
+// rows are looked up once.  grid: (n_pad_cap/128, ceil(C / (64 kBothTiles))).
 __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __restrict__ in,
                                                             const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ offsets,
@@ -200,7 +203,6 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
   }
   __syncthreads();
   const long long p0 = static_cast<long long>(blockIdx.x) * kTP;
-  const int c0 = blockIdx.y * kTC;
   if (threadIdx.x < kTP) {
     const long long p = p0 + threadIdx.x;
     long long src = -1;
@@ -217,17 +219,30 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
   }
   __syncthreads();
   const int cc = threadIdx.x & 7;
+  long long src[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (threadIdx.x >> 3) + 32 * i;
-    const long long src = s_src[r];
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (src >= 0) v = *reinterpret_cast<const uint4*>(in + src * C + c0 + 8 * cc);
-    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[r][8 * cc]);
-    t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
+  for (int i = 0; i < 4; ++i) src[i] = s_src[(threadIdx.x >> 3) + 32 * i];
+  auto load = [&](int c0, uint4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (src[i] >= 0 && c0 < C) v[i] = *reinterpret_cast<const uint4*>(in + src[i] * C + c0 + 8 * cc);
+    }
+  };
+  int c0 = blockIdx.y * kTC * kBothTiles;
+  uint4 v[4];
+  load(c0, v);
+  for (int it = 0; it < kBothTiles && c0 < C; ++it, c0 += kTC) {
+    __syncthreads();   // the previous tile's readers are done with the LDS tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t* t = reinterpret_cast<uint32_t*>(&tile[(threadIdx.x >> 3) + 32 * i][8 * cc]);
+      t[0] = v[i].x; t[1] = v[i].y; t[2] = v[i].z; t[3] = v[i].w;
+    }
+    __syncthreads();
+    if (it + 1 < kBothTiles) load(c0 + kTC, v);
+    quant_tile_columns(tile, kTC, p0, n_pad_cap, q + static_cast<long long>(c0) * n_pad_cap, scale + c0, 1, C);
   }
-  __syncthreads();
-  quant_tile_columns(tile, kTC, p0, n_pad_cap, q + static_cast<long long>(c0) * n_pad_cap, scale + c0, 1, C);
 }
 
 }  // namespace
@@ -282,7 +297,7 @@ extern "C" int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_tok
   MOE_REQUIRE(n >= 1 && C >= 64 && C % 64 == 0, MOE_ERR_UNSUPPORTED, "need n >= 1 and C a multiple of 64");
   const int cap = moe_mx_pad_cap(n, E);
   MOE_REQUIRE(cap > 0, MOE_ERR_UNSUPPORTED, "padded token axis too long");
-  dim3 grid(cap / kTP, C / kTC);
+  dim3 grid(cap / kTP, (C / kTC + kBothTiles - 1) / kBothTiles);
   quant_grouped_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, row_token, offsets, offsets_pad, E, C, cap, qT, scaleT);
   return check_launch("mxfp8_quantize_grouped");
 }
