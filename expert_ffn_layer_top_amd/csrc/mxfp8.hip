@@ -183,12 +183,15 @@ __global__ __launch_bounds__(256) void quant_both_kernel(const uint16_t* __restr
 // Grouped token-axis blocks.  Padded position p in [offsets_pad[e], offsets_pad[e+1]) holds
 // grouped row r = offsets[e] + (p - offsets_pad[e]) if r < offsets[e+1], else zero; positions
 // from offsets_pad[E] to n_pad_cap hold zeros.  Row r's data is in[row_token ? row_token[r] : r].
+// With row_gate, grouped row r is bf16(row_gate[r] * in[row_token[r]]) (fp32 product, round to
+// nearest even): the rows the fused MXFP8 combine backward never writes in bf16.
 // q [C][n_pad_cap], scale [n_pad_cap/32][C].  A workgroup takes a 128-position band and walks
 // kBothTiles column tiles of it (the rows' adjacent 128-byte pieces, read close together in time,
 // with the next tile's loads in flight while the current one is quantised); the band's source
 // rows are looked up once.  grid: (n_pad_cap/128, ceil(C / (64 kBothTiles))).
 __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __restrict__ in,
                                                             const int32_t* __restrict__ row_token,
+                                                            const float* __restrict__ row_gate,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ offsets_pad, int E, int C,
                                                             long long n_pad_cap, uint8_t* __restrict__ q,
@@ -197,6 +200,7 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
   __shared__ int s_off[257];
   __shared__ int s_offp[257];
   __shared__ long long s_src[kTP];
+  __shared__ float s_gate[kTP];
   for (int i = threadIdx.x; i <= E; i += 256) {
     s_off[i] = offsets[i];
     s_offp[i] = offsets_pad[i];
@@ -213,15 +217,22 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
         if (s_offp[mid] <= p) lo = mid; else hi = mid - 1;
       }
       const long long r = s_off[lo] + (p - s_offp[lo]);
-      if (r < s_off[lo + 1]) src = row_token ? row_token[r] : r;
+      if (r < s_off[lo + 1]) {
+        src = row_token ? row_token[r] : r;
+        if (row_gate) s_gate[threadIdx.x] = row_gate[r];
+      }
     }
     s_src[threadIdx.x] = src;
   }
   __syncthreads();
   const int cc = threadIdx.x & 7;
   long long src[4];
+  float gt[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) src[i] = s_src[(threadIdx.x >> 3) + 32 * i];
+  for (int i = 0; i < 4; ++i) {
+    src[i] = s_src[(threadIdx.x >> 3) + 32 * i];
+    gt[i] = (row_gate && src[i] >= 0) ? s_gate[(threadIdx.x >> 3) + 32 * i] : 1.f;
+  }
   auto load = [&](int c0, uint4 (&v)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -229,10 +240,23 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
       if (src[i] >= 0 && c0 < C) v[i] = *reinterpret_cast<const uint4*>(in + src[i] * C + c0 + 8 * cc);
     }
   };
+  // the gated rows, formed once the loads have landed (just before the tile goes to LDS)
+  auto gated = [&](uint4 (&v)[4]) {
+    if (!row_gate) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(gt[i] * bf16_lo(w[h]), gt[i] * bf16_hi(w[h]));
+      v[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
   int c0 = blockIdx.y * kTC * kBothTiles;
   uint4 v[4];
   load(c0, v);
   for (int it = 0; it < kBothTiles && c0 < C; ++it, c0 += kTC) {
+    gated(v);
     __syncthreads();   // the previous tile's readers are done with the LDS tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -288,9 +312,9 @@ extern "C" int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int 
   return check_launch("mxfp8_quantize_both");
 }
 
-extern "C" int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_token, const int32_t* offsets,
-                                      const int32_t* offsets_pad, int E, int n, int C, uint8_t* qT, uint8_t* scaleT,
-                                      void* stream) {
+static int quantize_grouped(const uint16_t* in, const int32_t* row_token, const float* row_gate,
+                            const int32_t* offsets, const int32_t* offsets_pad, int E, int n, int C, uint8_t* qT,
+                            uint8_t* scaleT, void* stream) {
   MOE_CHECK_PTR(in); MOE_CHECK_PTR(offsets); MOE_CHECK_PTR(offsets_pad); MOE_CHECK_PTR(qT); MOE_CHECK_PTR(scaleT);
   MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(qT);
   MOE_REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "E must be in [1, 256]");
@@ -298,6 +322,20 @@ extern "C" int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_tok
   const int cap = moe_mx_pad_cap(n, E);
   MOE_REQUIRE(cap > 0, MOE_ERR_UNSUPPORTED, "padded token axis too long");
   dim3 grid(cap / kTP, (C / kTC + kBothTiles - 1) / kBothTiles);
-  quant_grouped_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, row_token, offsets, offsets_pad, E, C, cap, qT, scaleT);
+  quant_grouped_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, row_token, row_gate, offsets, offsets_pad, E, C, cap,
+                                                             qT, scaleT);
   return check_launch("mxfp8_quantize_grouped");
+}
+
+extern "C" int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_token, const int32_t* offsets,
+                                      const int32_t* offsets_pad, int E, int n, int C, uint8_t* qT, uint8_t* scaleT,
+                                      void* stream) {
+  return quantize_grouped(in, row_token, nullptr, offsets, offsets_pad, E, n, C, qT, scaleT, stream);
+}
+
+extern "C" int mxfp8_quantize_grouped_gated(const uint16_t* in, const int32_t* row_token, const float* row_gate,
+                                            const int32_t* offsets, const int32_t* offsets_pad, int E, int n, int C,
+                                            uint8_t* qT, uint8_t* scaleT, void* stream) {
+  MOE_CHECK_PTR(row_token); MOE_CHECK_PTR(row_gate);
+  return quantize_grouped(in, row_token, row_gate, offsets, offsets_pad, E, n, C, qT, scaleT, stream);
 }

@@ -12,7 +12,7 @@
 // rows (and gates) are read once per wave (lanes j < k load dest[t, j]) and kept in scalar
 // registers.  The combine backward, which also reduces whole rows to dot products, gives each
 // wave one token.  Accumulation is fp32 in slot order j = 0..k-1.
-#include "common.h"
+#include "mx_common.h"
 
 namespace moe {
 namespace {
@@ -190,6 +190,83 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
   if (lane < k) dgate[t * k + lane] = mine;
 }
 
+// The same with dyexp leaving as MXFP8 row blocks: the bf16 values bf16(gate[t,j] * dy[t]) are
+// formed in registers and quantised there (32-element blocks = 4 lanes, amax by shuffles), so
+// dyq / dys hold exactly what mxfp8_quantize gives for the bf16 rows, which are never written.
+// row_gate[dest[t,j]] = gate[t,j] lets the grouped quantiser rebuild the same rows from dy.
+template <int KM>
+__global__ __launch_bounds__(256) void combine_bwd_mx_kernel(const uint16_t* __restrict__ dy,
+                                                             const uint16_t* __restrict__ yexp,
+                                                             const float* __restrict__ gate,
+                                                             const int32_t* __restrict__ dest, int T, int d, int k,
+                                                             uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys,
+                                                             float* __restrict__ row_gate, float* __restrict__ dgate) {
+  const long long t = static_cast<long long>(blockIdx.x) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  int rows[KM];
+  float g[KM], dot[KM];
+  dest_rows<KM>(dest, t, k, rows);
+  gates_of<KM>(gate, t, k, g);
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    dot[j] = 0.f;
+    if (j < k && lane == j) row_gate[rows[j]] = g[j];
+  }
+  const int chunks = d / 8;   // a multiple of 8: a 4-lane block group is all in range or all out
+  const uint4* dyrow = reinterpret_cast<const uint4*>(dy + t * d);
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kUBwd) {
+    uint4 vdy[kUBwd];
+#pragma unroll
+    for (int u = 0; u < kUBwd; ++u)
+      if (c0 + 64 * u < chunks) vdy[u] = dyrow[c0 + 64 * u];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < k) {
+        const uint4* yrow = reinterpret_cast<const uint4*>(yexp + static_cast<long long>(rows[j]) * d);
+        uint4 vy[kUBwd];
+#pragma unroll
+        for (int u = 0; u < kUBwd; ++u)
+          if (c0 + 64 * u < chunks) vy[u] = yrow[c0 + 64 * u];
+#pragma unroll
+        for (int u = 0; u < kUBwd; ++u) {
+          const int c = c0 + 64 * u;
+          if (c < chunks) {
+            float fdy[8], fy[8], o[8];
+            unpack8(vdy[u], fdy);
+            unpack8(vy[u], fy);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              dot[j] = fmaf(fdy[i], fy[i], dot[j]);
+              o[i] = g[j] * fdy[i];
+            }
+            const uint4 b = pack8(o);   // the bf16 dyexp values
+            const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+            uint32_t amax = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+            amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1, 64)));
+            amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, 64)));
+            const int sh = mx_shared_exp(amax);
+            const uint32_t lo = mx_encode4(w[0] & 0xffffu, w[0] >> 16, w[1] & 0xffffu, w[1] >> 16, sh);
+            const uint32_t hi = mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh);
+            const long long r = rows[j];
+            *reinterpret_cast<uint2*>(dyq + r * d + 8 * c) = make_uint2(lo, hi);
+            if ((lane & 3) == 0) dys[r * (d / 32) + c / 4] = static_cast<uint8_t>(sh + 127);
+          }
+        }
+      }
+    }
+  }
+  float mine = 0.f;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const float s = wave_sum(dot[j]);
+    if (lane == j) mine = s;
+  }
+  if (lane < k) dgate[t * k + lane] = mine;
+}
+
 // dx[t] = sum_j dxp[dest[t,j]] (+ addend[t]), fp32 in slot order after the addend
 template <int KM>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(const uint16_t* __restrict__ dxp, const int32_t* __restrict__ dest,
@@ -301,6 +378,18 @@ extern "C" int moe_unpermute_combine_bwd(const uint16_t* dy, const uint16_t* yex
   MOE_CHECK_ALIGN(dy); MOE_CHECK_ALIGN(yexp); MOE_CHECK_ALIGN(dyexp);
   MOE_SEG_LAUNCH(combine_bwd_kernel, grid_for(T), as_stream(stream), k, dy, yexp, gate, dest, T, d, k, dyexp, dgate);
   return check_launch("combine_bwd");
+}
+
+extern "C" int moe_unpermute_combine_bwd_mx(const uint16_t* dy, const uint16_t* yexp, const float* gate,
+                                            const int32_t* dest, int T, int d, int k, uint8_t* dyexp_q,
+                                            uint8_t* dyexp_scale, float* row_gate, float* dgate, void* stream) {
+  if (int st = check_rows(T, d, k)) return st;
+  MOE_CHECK_PTR(dy); MOE_CHECK_PTR(yexp); MOE_CHECK_PTR(gate); MOE_CHECK_PTR(dest);
+  MOE_CHECK_PTR(dyexp_q); MOE_CHECK_PTR(dyexp_scale); MOE_CHECK_PTR(row_gate); MOE_CHECK_PTR(dgate);
+  MOE_CHECK_ALIGN(dy); MOE_CHECK_ALIGN(yexp); MOE_CHECK_ALIGN(dyexp_q);
+  MOE_SEG_LAUNCH(combine_bwd_mx_kernel, grid_for(T), as_stream(stream), k, dy, yexp, gate, dest, T, d, k, dyexp_q,
+                 dyexp_scale, row_gate, dgate);
+  return check_launch("combine_bwd_mx");
 }
 
 extern "C" int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int k,

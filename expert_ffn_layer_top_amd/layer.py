@@ -9,7 +9,9 @@ The grouped products are issued one kernel per call (the same kernels, in the sa
 composite grouped_gemm_swiglu / grouped_gemm_swiglu_bwd), so each can be timed on its own.
 MXFP8 adds the block quantisation of x (before the permute; row blocks commute with the row
 permutation) and of the expert weights in both contraction directions; router, combine,
-permute-backward and route-backward stay bf16/fp32.
+permute-backward and route-backward stay bf16/fp32.  Its combine backward is the fused producer
+(unpermute_combine_bwd_mx): dYexp leaves as MXFP8 row blocks and per-row gates, and the grouped
+token blocks of dYexp are rebuilt from dy and those gates, so the bf16 dYexp is never written.
 
 Every step is a library call on the current stream; this module only sequences them and holds
 the tensors one step passes to the next.  ([news] "Ai2 rebuilds Olmo's training stack ...",
@@ -139,7 +141,12 @@ def backward(ctx, weights, dy, events=None):
     depend on the order."""
     out = {}
     with _Span(events, "combine_bwd"):
-        dyexp, dgate = ops.unpermute_combine_bwd(dy, ctx["yexp"], ctx["topk_gate"], ctx["dest"])
+        if not ctx["mxfp8"]:
+            dyexp, dgate = ops.unpermute_combine_bwd(dy, ctx["yexp"], ctx["topk_gate"], ctx["dest"])
+        else:
+            # fused MXFP8 producer: dYexp leaves as row blocks only (bf16 rows never written)
+            dyexp = None
+            dyq, dys, row_gate, dgate = ops.unpermute_combine_bwd_mx(dy, ctx["yexp"], ctx["topk_gate"], ctx["dest"])
     out.update(dyexp=dyexp, d_gate=dgate)
     E = ctx["logits"].shape[1]
     with _Span(events, "route_bwd"):
@@ -179,10 +186,9 @@ def backward(ctx, weights, dy, events=None):
         q = weights.mx
         n = g.shape[0]
         pad = ctx["offsets_pad"]
-        dyq, dys = ops.mxfp8_quantize(dyexp, 0)
         with _Span(events, "dgrad_down"):
             dg, du = ops.grouped_gemm_dgrad_down(dyq, off, q["wd_t"], g, u, scales=(dys, q["wd_t_s"]))
-        dyT, dyTs = ops.mxfp8_quantize_grouped(dyexp, off, pad, n)
+        dyT, dyTs = ops.mxfp8_quantize_grouped(dy, off, pad, n, row_token=ctx["row_token"], row_gate=row_gate)
         aT, aTs = ops.mxfp8_quantize_grouped(a, off, pad, n)
         with _Span(events, "wgrad_down"):
             dw_down = ops.grouped_gemm_wgrad_down(dyT, aT, off, n, offsets_pad=pad, scales=(dyTs, aTs))
@@ -199,6 +205,7 @@ def backward(ctx, weights, dy, events=None):
         with _Span(events, "wgrad_gate_up"):
             dw_gate, dw_up = ops.grouped_gemm_wgrad_gate_up(dgT, duT, xT, off, n, offsets_pad=pad,
                                                             scales=(dgTs, duTs, xTs))
+        out["row_gate"] = row_gate
         out["mx"] = dict(dyq=dyq, dys=dys, dyT=dyT, dyTs=dyTs, aT=aT, aTs=aTs, dgq=dgq, dgs=dgs, duq=duq,
                          dus=dus, dgT=dgT, dgTs=dgTs, duT=duT, duTs=duTs, xT=xT, xTs=xTs)
     out.update(dg=dg, du=du, dxp=dxp, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)

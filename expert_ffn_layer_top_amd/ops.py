@@ -172,6 +172,25 @@ def unpermute_combine_bwd(dy, yexp, topk_gate, dest):
     return dyexp, dgate
 
 
+def unpermute_combine_bwd_mx(dy, yexp, topk_gate, dest):
+    """(dyq [n,d] E4M3, dys [n,d/32] E8M0, row_gate [n] fp32, d_gate [T,k] fp32): the combine
+    backward with dyexp emitted only as MXFP8 row blocks (the bf16 rows are never written)."""
+    _check(dy, torch.bfloat16, "dy", 2)
+    _check(yexp, torch.bfloat16, "yexp", 2)
+    _check(topk_gate, torch.float32, "topk_gate", 2)
+    _check(dest, torch.int32, "dest", 2)
+    T, d = dy.shape
+    k = dest.shape[1]
+    n = T * k
+    dyq = _empty((n, d), torch.uint8, dy)
+    dys = _empty((n, d // 32), torch.uint8, dy)
+    row_gate = _empty((n,), torch.float32, dy)
+    dgate = _empty((T, k), torch.float32, dy)
+    call("moe_unpermute_combine_bwd_mx", _ptr(dy), _ptr(yexp), _ptr(topk_gate), _ptr(dest), T, d, k, _ptr(dyq),
+         _ptr(dys), _ptr(row_gate), _ptr(dgate), _stream(dy))
+    return dyq, dys, row_gate, dgate
+
+
 def permute_bwd(dxp, dest, addend=None):
     _check(dxp, torch.bfloat16, "dxp", 2)
     _check(dest, torch.int32, "dest", 2)
@@ -230,9 +249,10 @@ def mx_pad_cap(n, E):
     return lib.moe_mx_pad_cap(n, E)
 
 
-def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None):
+def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None, row_gate=None):
     """Token-axis blocks per expert group: (qT [C, P], sT [P/32, C]), P = mx_pad_cap(n, E); the
-    scales are block-major (sT[b, c]: channel c, position block b)."""
+    scales are block-major (sT[b, c]: channel c, position block b).  row_token: rows gathered
+    from a token-major x; row_gate [n] (with row_token): row r is bf16(row_gate[r] * x[row_token[r]])."""
     _check(x, torch.bfloat16, "x", 2)
     _check(offsets, torch.int32, "offsets", 1)
     _check(offsets_pad, torch.int32, "offsets_pad", 1)
@@ -241,8 +261,15 @@ def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None):
     P = mx_pad_cap(n, E)
     q = _empty((C, P), torch.uint8, x)
     s = _empty((P // 32, C), torch.uint8, x)
-    call("mxfp8_quantize_grouped", _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(offsets_pad), E, n, C,
-         _ptr(q), _ptr(s), _stream(x))
+    if row_gate is None:
+        call("mxfp8_quantize_grouped", _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(offsets_pad), E, n, C,
+             _ptr(q), _ptr(s), _stream(x))
+    else:
+        _check(row_gate, torch.float32, "row_gate", 1)
+        if row_token is None:
+            raise ValueError("row_gate needs row_token")
+        call("mxfp8_quantize_grouped_gated", _ptr(x), _ptr(row_token), _ptr(row_gate), _ptr(offsets),
+             _ptr(offsets_pad), E, n, C, _ptr(q), _ptr(s), _stream(x))
     return q, s
 
 

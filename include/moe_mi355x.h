@@ -164,6 +164,16 @@ int moe_unpermute_combine_bwd(const uint16_t* dy, const uint16_t* yexp, const fl
                               const int32_t* dest, int T, int d, int k, uint16_t* dyexp,
                               float* d_gate, void* stream);
 
+/* The combine backward for MXFP8 backward products (fused producer): the rows of dyexp,
+ * bf16(gate[t,j] * dy[t]), are formed in registers and leave only as MXFP8 row blocks along d,
+ * byte-identical to mxfp8_quantize(dyexp, axis 0) of the bf16 rows, which are never written.
+ *   out  dyexp_q [n,d] E4M3, dyexp_scale [n,d/32] E8M0, row_gate [n] fp32 (row_gate[dest[t,j]] =
+ *        gate[t,j], for mxfp8_quantize_grouped_gated), d_gate [T,k] fp32 as
+ *        moe_unpermute_combine_bwd.  Shapes and alignment as moe_unpermute_combine_bwd. */
+int moe_unpermute_combine_bwd_mx(const uint16_t* dy, const uint16_t* yexp, const float* topk_gate,
+                                 const int32_t* dest, int T, int d, int k, uint8_t* dyexp_q,
+                                 uint8_t* dyexp_scale, float* row_gate, float* d_gate, void* stream);
+
 /* Backward of the permute: dx[t] = sum_j dxp[dest[t,j]] (+ dx_addend[t] if given, the fp32
  * router-path term), fp32 accumulation, bf16 out. */
 int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int k,
@@ -204,6 +214,14 @@ int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int cols, uint8
 int mxfp8_quantize_grouped(const uint16_t* in, const int32_t* row_token_or_null,
                            const int32_t* offsets, const int32_t* offsets_pad, int E, int n, int C,
                            uint8_t* qT, uint8_t* scaleT, void* stream);
+
+/* As mxfp8_quantize_grouped with row_token (required) and a per-row gate: grouped row r is
+ * bf16(row_gate[r] * in[row_token[r]]) (fp32 product, round to nearest even) -- with `in` = dy and
+ * row_gate from moe_unpermute_combine_bwd_mx, exactly the bf16 dyexp rows that call never
+ * writes, so the output equals mxfp8_quantize_grouped(dyexp) byte for byte. */
+int mxfp8_quantize_grouped_gated(const uint16_t* in, const int32_t* row_token, const float* row_gate,
+                                 const int32_t* offsets, const int32_t* offsets_pad, int E, int n,
+                                 int C, uint8_t* qT, uint8_t* scaleT, void* stream);
 
 /* Length of the padded token axis used by mxfp8_quantize_grouped and the MXFP8 backward. */
 int moe_mx_pad_cap(int n, int E);

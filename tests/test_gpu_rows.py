@@ -96,3 +96,36 @@ def test_identity_experts_combine_returns_input():
     xf = codecs.bf16_to_f64(x)
     err = np.abs(codecs.bf16_to_f64(bits(y)) - xf)
     assert np.all(err <= 2.0 ** -8 * np.abs(xf) + 1e-6)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(300, 256, 8, 2), (1000, 512, 16, 4), (257, 192, 40, 8), (64, 128, 16, 16)])
+def test_combine_bwd_fused_mxfp8_producer(T, d, E, k):
+    """The fused MXFP8 combine backward writes exactly the bytes of quantising the bf16 path's
+    dYexp (row blocks), the same d_gate bits, and per-row gates with which the gated grouped
+    quantiser reproduces the grouped token blocks of that dYexp byte for byte."""
+    import torch
+    from expert_ffn_layer_top_amd import ops
+    from oracle import moe
+    rng = np.random.default_rng(T + d + k)
+    logits = rng.standard_normal((T, E))
+    logits[:, E // 3] -= 100.0                                 # an empty expert group
+    idx, gate, _ = moe.route_topk(logits, k)
+    _, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=32)
+    n = T * k
+    dy = to_bf16_bits((rng.standard_normal((T, d)) * np.exp(rng.standard_normal((T, 1)))).astype(np.float32))
+    yexp = to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+    dev = lambda a, dt: torch.as_tensor(np.ascontiguousarray(a), dtype=dt).to("cuda:0")
+    dy_d, ye_d = bf16_to_dev(dy), bf16_to_dev(yexp)
+    g_d, dest_d = dev(gate.astype(np.float32), torch.float32), i32_to_dev(dest)
+    note(f"combine_bwd mx T={T} d={d} E={E} k={k}")
+    dyexp, dgate = ops.unpermute_combine_bwd(dy_d, ye_d, g_d, dest_d)
+    rq, rs = ops.mxfp8_quantize(dyexp, 0)
+    dyq, dys, row_gate, dgate_mx = ops.unpermute_combine_bwd_mx(dy_d, ye_d, g_d, dest_d)
+    assert torch.equal(dyq, rq) and torch.equal(dys, rs)
+    assert torch.equal(dgate_mx, dgate)
+    rg = host(row_gate)
+    assert np.array_equal(rg[dest.ravel()], gate.astype(np.float32).ravel())
+    off_d, offp_d, rt_d = i32_to_dev(off), i32_to_dev(offp), i32_to_dev(row_token)
+    gq, gs = ops.mxfp8_quantize_grouped(dyexp, off_d, offp_d, n)
+    hq, hs = ops.mxfp8_quantize_grouped(dy_d, off_d, offp_d, n, row_token=rt_d, row_gate=row_gate)
+    assert torch.equal(hq, gq) and torch.equal(hs, gs)

@@ -87,6 +87,23 @@ def _check_routing(cfg, logits, ctx):
     return counts, off, dest, row_token, offp
 
 
+def _dyexp_rows(inputs, ctx, out, dest, rows):
+    """bf16 bits of dYexp rows: the GPU's own, or under the fused MXFP8 combine backward (which
+    never writes them) bf16(gate * dy) formed on the host from the GPU's gates, exactly as that
+    kernel forms them (fp32 product, round to nearest even)."""
+    if out["dyexp"] is not None:
+        return _rows_bits(out["dyexp"], rows)
+    T, k = dest.shape
+    tok_of, slot_of = np.empty(T * k, np.int64), np.empty(T * k, np.int64)
+    tok_of[dest.ravel()] = np.repeat(np.arange(T), k)
+    slot_of[dest.ravel()] = np.tile(np.arange(k), T)
+    rows = np.asarray(rows)
+    tok, slot = tok_of[rows], slot_of[rows]
+    g = host(ctx["topk_gate"])[tok, slot].astype(np.float32)
+    dyf = codecs.bf16_to_f64(inputs["dy"][tok]).astype(np.float32)
+    return synth.to_bf16_bits((dyf * g[:, None]).astype(np.float32))
+
+
 def _check_combine_and_bwd(cfg, inputs, ctx, out, dest, toks):
     """y, dYexp and d_gate on sampled tokens (GPU's own Yexp and gates); d_logits in full."""
     k = cfg.k
@@ -96,7 +113,7 @@ def _check_combine_and_bwd(cfg, inputs, ctx, out, dest, toks):
     local = np.arange(len(toks) * k).reshape(len(toks), k)
     assert_close(_f64(_rows_bits(ctx["y"], toks)), moe.combine(ye, gate[toks], local), BF16_TOL, "y tokens")
     rdy, rdg = moe.combine_bwd(inputs["dy"][toks], ye, gate[toks], local)
-    assert_close(_f64(_rows_bits(out["dyexp"], trow)), rdy, BF16_TOL, "dYexp tokens")
+    assert_close(_f64(_dyexp_rows(inputs, ctx, out, dest, trow)), rdy, BF16_TOL, "dYexp tokens")
     assert_close(host(out["d_gate"])[toks], rdg, 1e-4, "d_gate tokens")
     assert_close(host(out["d_logits"]), moe.route_topk_bwd(gate, host(ctx["topk_idx"]), host(out["d_gate"]), cfg.E),
                  1e-5, "d_logits")
@@ -236,7 +253,9 @@ def test_mxfp8_full_size():
 
     # dgrad products: operands quantised along the contraction dim, bit for bit, then the products
     mx = out["mx"]
-    dy_r = _rows_bits(out["dyexp"], rows)
+    assert out["dyexp"] is None                                      # fused producer: no bf16 dYexp
+    assert np.array_equal(host(out["row_gate"])[dest.ravel()], host(ctx["topk_gate"]).ravel())
+    dy_r = _dyexp_rows(inputs, ctx, out, dest, rows)
     dyq_r, dys_r = mxfp8.quantize_rows(dy_r)
     assert np.array_equal(host(_dev_rows(mx["dyq"], rows)), dyq_r) and np.array_equal(host(_dev_rows(mx["dys"], rows)), dys_r)
     dA = per_expert(lambda e, m: m @ deq["wd_t", e].T, mxfp8.dequantize_blocks(dyq_r, dys_r), cfg.f)
@@ -268,7 +287,7 @@ def test_mxfp8_full_size():
             assert gq.shape == (C, span) and np.array_equal(gq, rq_) and np.array_equal(gs, rs_), f"{name}[{e}]"
             return mxfp8.dequantize_blocks(gq, gs)
 
-        dyT = grouped(mx["dyT"], mx["dyTs"], _rows_bits(out["dyexp"], er), cfg.d, "dyexp^T")
+        dyT = grouped(mx["dyT"], mx["dyTs"], _dyexp_rows(inputs, ctx, out, dest, er), cfg.d, "dyexp^T")
         aT = grouped(mx["aT"], mx["aTs"], _rows_bits(ctx["a"], er), cfg.f, "a^T")
         dgT = grouped(mx["dgT"], mx["dgTs"], _rows_bits(out["dg"], er), cfg.f, "dg^T")
         duT = grouped(mx["duT"], mx["duTs"], _rows_bits(out["du"], er), cfg.f, "du^T")
