@@ -191,3 +191,46 @@ def test_layer_balance_score_in_step():
     d_ref = (moe.route_topk_bwd(host(ctx["topk_gate"]), host(ctx["topk_idx"]), host(out["d_gate"]), cfg.E)
              + moe.router_balance_bwd(probs, counts, cfg.k, wb))
     assert_close(host(out["d_logits"]), d_ref, 1e-5, "d_logits with balance term")
+
+
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
+def test_step_captured_in_hip_graph(mx):
+    """Nothing in the step waits on the host (routing metadata stays on the device), so the whole
+    forward + backward can be captured in one HIP graph; three replays, with eager steps between
+    them, each reproduce the eager results bit for bit."""
+    import torch
+    from expert_ffn_layer_top_amd import layer
+    cfg = synth.CONFIGS["mxfp8" if mx else "balanced"].with_(T=1024, d=512, E=8, k=2, f=512)
+    inputs = synth.make_inputs(cfg)
+    t = synth.to_torch(inputs, torch.device("cuda:0"))
+    w = layer.Weights(t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"))
+    keys = ("dx", "d_logits", "dw_gate", "dw_up", "dw_down")
+
+    def step():
+        if mx:
+            w.quantize_mx()
+        ctx = layer.forward(t["x"], w, cfg.k, logits=t.get("logits"), mxfp8=mx)
+        return ctx, layer.backward(ctx, w, t["dy"])
+
+    note(f"graph capture mxfp8={mx} T={cfg.T} d={cfg.d} E={cfg.E}")
+    ctx, out = step()
+    torch.cuda.synchronize()
+    ref = {k: out[k].clone() for k in keys}
+    ref["y"] = ctx["y"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gctx, gout = step()
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gctx["y"], ref["y"]), f"replay {i}: y"
+        for k in keys:
+            assert torch.equal(gout[k], ref[k]), f"replay {i}: {k}"
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
