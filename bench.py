@@ -14,7 +14,8 @@ oracle's throughput on the host cores over a bounded token sample (a baseline on
 After the warm-up, an instrumented pass of K steps brackets every call of the step with HIP
 events on the stream it runs on (each grouped-GEMM call is one kernel): its averages give
 `gemm_ms` / `gemm_tflops` and, for the routing and row-movement calls, achieved HBM GB/s on their
-algorithmic bytes (`rows_hbm_gbs`, against the 8000 GB/s peak), and they pick the dominant
+algorithmic bytes (`rows_hbm_gbs`, against the 8000 GB/s peak; `aux_hbm_gbs` likewise for the
+router products and the MXFP8 quantisers where the workload has them), and they pick the dominant
 kernel, the GEMM with the largest average duration (under MXFP8 the forward down call, which
 also quantises A, is not a candidate).  Then the timed region runs K more steps with only the
 dominant kernel bracketed: `value` and `ms_per_step` come from it, and so does the roofline's
@@ -69,7 +70,7 @@ def describe(cfg):
     kind = {"roundrobin": "balanced (round-robin) routing", "normal": "random N(0,1) logits",
             "zipf": "Zipf-skewed routing", "router": "router-projected logits"}[cfg.logits]
     prec = "MXFP8 expert GEMMs" if cfg.mxfp8 else "bf16"
-    return (f"MoE layer fwd+bwd, {kind}: T={cfg.T}, d_model={cfg.d}, E={cfg.E}, top-{cfg.k}, "
+    return (f"MoE layer {'forward' if cfg.forward_only else 'fwd+bwd'}, {kind}: T={cfg.T}, d_model={cfg.d}, E={cfg.E}, top-{cfg.k}, "
             f"SwiGLU d_ff={cfg.f}, {prec}, fp32 accumulate, seed {cfg.seed}")
 
 
@@ -108,10 +109,21 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False):
     if recompute and not cfg.forward_only:
         calls = calls + (layer.RECOMPUTE_CALL,)
     rows = layer.ROW_CALLS if not cfg.forward_only else ("route", "permute", "combine")
+    # router products and MXFP8 quantisers, where the workload has them
+    aux = ()
+    if cfg.logits == "router":
+        aux += layer.ROUTER_CALLS if not cfg.forward_only else ("router",)
+    if cfg.mxfp8:
+        aux += ("quant_w",) + (layer.QUANT_CALLS if not cfg.forward_only else ("quant_x",))
 
     def step(events=None):
         if cfg.mxfp8:
+            qw = events.get("quant_w") if events else None
+            if qw:
+                qw[0].record()
             w.quantize_mx()                  # weights are re-quantised every step (both directions)
+            if qw:
+                qw[1].record()
         ctx = layer.forward(x, w, cfg.k, logits=logits, mxfp8=cfg.mxfp8, events=events, recompute=recompute)
         if not cfg.forward_only:
             layer.backward(ctx, w, dy, events=events)
@@ -126,12 +138,13 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False):
     for _ in range(warmup):
         step()
     # instrumented pass: every call bracketed
-    evs = pairs(calls + rows)
+    evs = pairs(calls + rows + aux)
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     gemm_ms = {c: mean_ms(evs, c) for c in calls}
     row_ms = {c: mean_ms(evs, c) for c in rows}
+    aux_ms = {c: mean_ms(evs, c) for c in aux}
     cand = [c for c in calls if not (cfg.mxfp8 and c == "down") and c != layer.RECOMPUTE_CALL]
     dom = max(cand, key=lambda c: gemm_ms[c])
     # timed region: the dominant kernel alone bracketed
@@ -142,7 +155,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False):
         step(evd[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    return elapsed, gemm_ms, row_ms, dom, mean_ms(evd, dom)
+    return elapsed, gemm_ms, row_ms, aux_ms, dom, mean_ms(evd, dom)
 
 
 def traffic_of(cfg, call):
@@ -169,6 +182,19 @@ def row_bytes(cfg, call):
             "combine_bwd": (2 * k + 1) * T * d * 2 + 12 * T * k,
             "permute_bwd": (k + 1) * T * d * 2 + 4 * T * k,
             "route_bwd": T * (4 * E + 12 * k)}[call]
+
+
+def aux_bytes(cfg, call):
+    """Algorithmic HBM bytes of the router products and the MXFP8 quantiser calls: each element
+    read or written once (quantisers: 2 B read, 1 + 1/32 B written per element and layout; the
+    grouped token blocks counted over the n routed rows, padding excluded)."""
+    T, d, E, n, f = float(cfg.T), cfg.d, cfg.E, float(cfg.n), cfg.f
+    q = 2 + 1 + 1 / 32
+    return {"router": T * d * 2 + d * E * 4 + T * E * 4,
+            "router_bwd": T * E * 4 * 2 + d * E * 4 * 2 + T * d * 4 + T * d * 2,
+            "quant_w": 3 * E * d * f * (2 + 2 * (1 + 1 / 32)),
+            "quant_x": T * d * q, "quant_dg": n * f * q, "quant_du": n * f * q, "quant_dyT": n * d * q,
+            "quant_aT": n * f * q, "quant_dgT": n * f * q, "quant_duT": n * f * q, "quant_xT": n * d * q}[call]
 
 
 def gemm_bytes(cfg, call):
@@ -221,8 +247,8 @@ def main():
               file=sys.stderr)
         return 2
     cfg = workload_config(args)
-    elapsed, gemm_ms, row_ms, dom, dom_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe,
-                                                    args.recompute)
+    elapsed, gemm_ms, row_ms, aux_ms, dom, dom_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe,
+                                                            args.recompute)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
     flops = gemm_flops(cfg)
@@ -257,6 +283,9 @@ def main():
         "rows_hbm_gbs": {c: round(row_bytes(cfg, c) / (v * 1e-3) / 1e9, 1) for c, v in row_ms.items()},
         "hbm_peak_gbs": HBM_PEAK_GBS,
     }
+    if aux_ms:
+        out["aux_us"] = {c: round(v * 1e3, 1) for c, v in aux_ms.items()}
+        out["aux_hbm_gbs"] = {c: round(aux_bytes(cfg, c) / (v * 1e-3) / 1e9, 1) for c, v in aux_ms.items()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

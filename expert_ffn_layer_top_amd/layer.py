@@ -72,6 +72,10 @@ class _Span:
 # row-movement calls (route: its three kernels)
 GEMM_CALLS = ("gate_up", "down", "dgrad_down", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up")
 RECOMPUTE_CALL = "recompute"
+# the router products (layers that own their router) and the MXFP8 quantiser calls (each one
+# kernel; under MXFP8 "quant_dyT" gathers dy with the combine backward's row gates)
+ROUTER_CALLS = ("router", "router_bwd")
+QUANT_CALLS = ("quant_x", "quant_dg", "quant_du", "quant_dyT", "quant_aT", "quant_dgT", "quant_duT", "quant_xT")
 ROW_CALLS = ("route", "permute", "combine", "combine_bwd", "permute_bwd", "route_bwd")
 
 
@@ -91,7 +95,8 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
     ctx = dict(x=x, k=k, mxfp8=mxfp8, balance_weight=balance_weight)
     want_probs = want_probs or balance_weight is not None
     if logits is None:
-        logits = ops.router_project(x, weights.w_r)
+        with _Span(events, "router"):
+            logits = ops.router_project(x, weights.w_r)
     ctx["logits"] = logits
     with _Span(events, "route"):
         r = ops.route_topk(logits, k, want_probs=want_probs, pad=32 if mxfp8 else None)
@@ -109,7 +114,8 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
             yexp = ops.grouped_gemm_down(a, r["offsets"], weights.w_down)
     else:
         q = weights.mx or weights.quantize_mx()
-        xq, xs = ops.mxfp8_quantize(x, 0)
+        with _Span(events, "quant_x"):
+            xq, xs = ops.mxfp8_quantize(x, 0)
         with _Span(events, "permute"):
             xpq, xps = ops.permute(xq, r["dest"], x_scale=xs)
         ctx["xq"], ctx["xs"], ctx["xpq"], ctx["xps"] = xq, xs, xpq, xps
@@ -156,7 +162,8 @@ def backward(ctx, weights, dy, events=None):
         out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E, balance=bal)
     addend = None
     if weights.w_r is not None:
-        addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])
+        with _Span(events, "router_bwd"):
+            addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])
         out["dx_router"] = addend
     off = ctx["offsets"]
     g, u, a = ctx["g"], ctx["u"], ctx["a"]
@@ -188,20 +195,27 @@ def backward(ctx, weights, dy, events=None):
         pad = ctx["offsets_pad"]
         with _Span(events, "dgrad_down"):
             dg, du = ops.grouped_gemm_dgrad_down(dyq, off, q["wd_t"], g, u, scales=(dys, q["wd_t_s"]))
-        dyT, dyTs = ops.mxfp8_quantize_grouped(dy, off, pad, n, row_token=ctx["row_token"], row_gate=row_gate)
-        aT, aTs = ops.mxfp8_quantize_grouped(a, off, pad, n)
+        with _Span(events, "quant_dyT"):
+            dyT, dyTs = ops.mxfp8_quantize_grouped(dy, off, pad, n, row_token=ctx["row_token"], row_gate=row_gate)
+        with _Span(events, "quant_aT"):
+            aT, aTs = ops.mxfp8_quantize_grouped(a, off, pad, n)
         with _Span(events, "wgrad_down"):
             dw_down = ops.grouped_gemm_wgrad_down(dyT, aT, off, n, offsets_pad=pad, scales=(dyTs, aTs))
-        dgq, dgs = ops.mxfp8_quantize(dg, 0)
-        duq, dus = ops.mxfp8_quantize(du, 0)
+        with _Span(events, "quant_dg"):
+            dgq, dgs = ops.mxfp8_quantize(dg, 0)
+        with _Span(events, "quant_du"):
+            duq, dus = ops.mxfp8_quantize(du, 0)
         with _Span(events, "dgrad_gate_up"):
             dxp = ops.grouped_gemm_dgrad_gate_up(dgq, duq, off, q["wg_t"], q["wu_t"],
                                                  scales=(dgs, dus, q["wg_t_s"], q["wu_t_s"]))
         with _Span(events, "permute_bwd"):
             out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
-        dgT, dgTs = ops.mxfp8_quantize_grouped(dg, off, pad, n)
-        duT, duTs = ops.mxfp8_quantize_grouped(du, off, pad, n)
-        xT, xTs = ops.mxfp8_quantize_grouped(ctx["x"], off, pad, n, row_token=ctx["row_token"])
+        with _Span(events, "quant_dgT"):
+            dgT, dgTs = ops.mxfp8_quantize_grouped(dg, off, pad, n)
+        with _Span(events, "quant_duT"):
+            duT, duTs = ops.mxfp8_quantize_grouped(du, off, pad, n)
+        with _Span(events, "quant_xT"):
+            xT, xTs = ops.mxfp8_quantize_grouped(ctx["x"], off, pad, n, row_token=ctx["row_token"])
         with _Span(events, "wgrad_gate_up"):
             dw_gate, dw_up = ops.grouped_gemm_wgrad_gate_up(dgT, duT, xT, off, n, offsets_pad=pad,
                                                             scales=(dgTs, duTs, xTs))
