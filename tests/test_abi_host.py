@@ -113,3 +113,25 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, fake, None, 0, None) == WORKSPACE
     msg = L.moe_last_error_string().decode()
     assert "workspace" in msg
+
+
+def test_argument_checks_of_balance_and_fused_producer():
+    L = _lib.lib
+    fake = ctypes.c_void_p(0x1000)
+    # balance score: shape, null pointers, workspace
+    assert L.moe_route_balance(fake, fake, 0, 8, 2, fake, fake, fake, 1 << 20, None) == UNSUPPORTED
+    assert L.moe_route_balance(fake, fake, 64, 300, 2, fake, fake, fake, 1 << 20, None) == UNSUPPORTED
+    assert L.moe_route_balance(fake, None, 64, 8, 2, fake, fake, fake, 1 << 20, None) == INVALID
+    assert L.moe_route_balance(fake, fake, 1000, 8, 2, fake, fake, fake, 4, None) == WORKSPACE
+    assert L.moe_route_balance_workspace_bytes(1000, 8) == 4 * 8 * 4          # 4 blocks of 256 tokens
+    # route backward with the balance term: null probs, non-finite weight, k > E
+    assert L.moe_route_topk_bwd_balance(fake, fake, fake, None, fake, 0.1, 64, 8, 2, fake, None) == INVALID
+    assert L.moe_route_topk_bwd_balance(fake, fake, fake, fake, fake, float("nan"), 64, 8, 2, fake, None) == INVALID
+    assert L.moe_route_topk_bwd_balance(fake, fake, fake, fake, fake, 0.1, 64, 4, 5, fake, None) == UNSUPPORTED
+    # fused MXFP8 combine backward: d a multiple of 64, every output pointer given
+    assert L.moe_unpermute_combine_bwd_mx(fake, fake, fake, fake, 16, 96, 2, fake, fake, fake, fake, None) == UNSUPPORTED
+    assert L.moe_unpermute_combine_bwd_mx(fake, fake, fake, fake, 16, 128, 2, fake, fake, None, fake, None) == INVALID
+    # gated grouped quantiser: row_token and row_gate required, C a multiple of 64
+    assert L.mxfp8_quantize_grouped_gated(fake, None, fake, fake, fake, 8, 64, 128, fake, fake, None) == INVALID
+    assert L.mxfp8_quantize_grouped_gated(fake, fake, None, fake, fake, 8, 64, 128, fake, fake, None) == INVALID
+    assert L.mxfp8_quantize_grouped_gated(fake, fake, fake, fake, fake, 8, 64, 96, fake, fake, None) == UNSUPPORTED
