@@ -19,8 +19,10 @@
 // Tile geometry and staging follow the bf16 kernels: 256 x 256 outputs per workgroup, four
 // waves of 128 x 128 (256 fp32 accumulators per lane in AGPRs), K stages of 128 elements = one
 // 128-byte row per operand row, XOR-swizzled 16-byte chunks, LDS-DMA buffer loads.  Waves 0-1
-// stream the N-side operand and waves 2-3 the M-side one, two stages each; each stage also
-// carries the 4 scale bytes of every row.  The barrier opening K step g sits at its start: past
+// stream the N-side operand and waves 2-3 the M-side one, two stages each; every K step needs the
+// 4 scale bytes of each row too, loaded by the same waves as the cache lines allow (see OpLoad:
+// per step, in four-step groups, or block-major for the weight gradients).  The barrier opening
+// K step g sits at its start: past
 // it every wave has finished step g-1, so the DMA of step g+1 goes into that step's stages while
 // step g is consumed.  The MFMA lane layout (checked on the
 // device): lane l holds row l % 16, K bytes 16*(l/16) .. +15 and 64 + 16*(l/16) .. +15 of the
