@@ -11,7 +11,10 @@ the timed region.  The default workload is the balanced-routing layer (8192 toke
 Prints one JSON line with the throughput (tokens/s), the roofline of the dominant kernel and the
 oracle's throughput on the host cores over a bounded token sample (a baseline only).
 
-After the warm-up, an instrumented pass of K steps brackets every call of the step with HIP
+After the W warm-up steps, untimed steps continue until --settle seconds (default 1) after the
+first one: a fresh process on a fresh box stalls for milliseconds around its first steps and its
+clocks ramp over the next tens of steps.  Then an instrumented pass of K steps brackets every
+call of the step with HIP
 events on the stream it runs on (each grouped-GEMM call is one kernel): its averages give
 `gemm_ms` / `gemm_tflops` and, for the routing and row-movement calls, achieved HBM GB/s on their
 algorithmic bytes (`rows_hbm_gbs`, against the 8000 GB/s peak; `aux_hbm_gbs` likewise for the
@@ -28,6 +31,7 @@ before the warm-up: the plain copy kernel that calibrates the HBM byte counters.
 """
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -53,6 +57,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                    help="after the warm-up, keep stepping (untimed) until this long after the first step")
+    ap.add_argument("--flush", action="store_true",
+                    help="instrumented pass: write 1 GiB of scratch between steps (cold L2 and last-level cache)")
     ap.add_argument("--recompute", action="store_true",
                     help="per-layer activation recompute: the backward re-runs the gate/up product")
     return ap.parse_args()
@@ -91,7 +99,7 @@ def copy_probe(nbytes):
     del src, dst
 
 
-def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False):
+def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=False, settle=1.0):
     import torch
 
     import synth
@@ -135,11 +143,27 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False):
     def mean_ms(evs, c):
         return sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / len(evs)
 
+    t_first = time.perf_counter()
     for _ in range(warmup):
         step()
+    torch.cuda.synchronize()
+    # settle: a fresh process stalls for milliseconds around its first steps and the clocks ramp
+    # over the next tens of steps, which per-kernel events do not see but a short wall-clock
+    # region does; untimed steps until `settle` seconds after the first one
+    while time.perf_counter() - t_first < settle:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    # no collector pauses in the measured passes (a full collection can stall the host for tens of
+    # milliseconds while the GPU drains its queue): collect now, re-enable at the end
+    gc.collect()
+    gc.disable()
     # instrumented pass: every call bracketed
     evs = pairs(calls + rows + aux)
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev) if flush else None
     for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(float(i))          # 1 GiB written: evicts the step's data from L2 and MALL
         step(evs[i])
     torch.cuda.synchronize()
     gemm_ms = {c: mean_ms(evs, c) for c in calls}
@@ -155,6 +179,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False):
         step(evd[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     return elapsed, gemm_ms, row_ms, aux_ms, dom, mean_ms(evd, dom)
 
 
@@ -248,7 +273,7 @@ def main():
         return 2
     cfg = workload_config(args)
     elapsed, gemm_ms, row_ms, aux_ms, dom, dom_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe,
-                                                            args.recompute)
+                                                            args.recompute, args.flush, args.settle)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
     flops = gemm_flops(cfg)
@@ -271,7 +296,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(cfg), "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
                    "top_k": cfg.k, "d_ff": cfg.f, "fwd_bwd": not cfg.forward_only,
-                   "activation_recompute": bool(args.recompute)},
+                   "activation_recompute": bool(args.recompute), "instrumented_pass_flushed": bool(args.flush)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic_of(cfg, dom),
                      "kernel": f"{profsum.kernel_name(dom, dtype, cfg.d, cfg.f)} ({dom})",
