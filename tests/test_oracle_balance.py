@@ -77,3 +77,21 @@ def test_brute_force_loop():
         pe = sum(probs[t, e] for t in range(T)) / T
         aux += fe * pe
     assert abs(moe.router_balance(probs, counts, k)["aux"] - E * aux) < 1e-13
+
+
+def test_gradient_matches_torch_autograd():
+    """CPU torch autograd in float64 through softmax and the score, counts held constant."""
+    import torch
+    rng = np.random.default_rng(11)
+    T, E, k, wgt = 40, 9, 3, 1.7
+    logits = rng.standard_normal((T, E)) * 2
+    idx, _, _ = moe.route_topk(logits, k)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    lt = torch.tensor(logits, dtype=torch.float64, requires_grad=True)
+    p = torch.softmax(lt, dim=1)
+    f = torch.tensor(counts / (T * k), dtype=torch.float64)
+    aux = E * torch.sum(f * p.mean(dim=0))
+    (wgt * aux).backward()
+    g = moe.router_balance_bwd(_softmax(logits), counts, k, wgt)
+    assert np.max(np.abs(lt.grad.numpy() - g)) < 1e-15
+    assert abs(aux.item() - moe.router_balance(_softmax(logits), counts, k)["aux"]) < 1e-14

@@ -118,3 +118,36 @@ def test_zipf_routing_is_skewed():
     assert counts[0] == cfg.T                       # the hottest expert takes every token
     assert (counts == 0).sum() > 50                 # many experts get nothing
     assert counts.max() / counts.sum() > 0.10
+
+
+def test_metadata_invariants_on_generated_ties():
+    """Hypothesis-generated logits drawn from a few values (many exact ties): the selection keeps
+    the lower expert id on ties, dest is a bijection onto 0..T*k-1, rows run expert-major and
+    token-ascending, and counts sum to T*k."""
+    from hypothesis import given, settings, strategies as st
+
+    @settings(max_examples=60, deadline=None)
+    @given(T=st.integers(1, 24), E=st.integers(1, 10), data=st.data())
+    def check(T, E, data):
+        k = data.draw(st.integers(1, E))
+        vals = data.draw(st.lists(st.sampled_from([-1.0, 0.0, 0.5, 2.0]), min_size=T * E, max_size=T * E))
+        logits = np.array(vals).reshape(T, E)
+        idx, gate, _ = moe.route_topk(logits, k)
+        for t in range(T):
+            chosen = list(idx[t])
+            # descending logits, ties to the lower id: exactly the first k of a stable sort
+            order = sorted(range(E), key=lambda e: (-logits[t, e], e))
+            assert chosen == order[:k]
+        assert np.allclose(gate.sum(axis=1), 1.0)
+        counts, off, dest, row_token, _ = moe.route_metadata(idx, E)
+        assert counts.sum() == T * k and off[-1] == T * k
+        assert sorted(dest.ravel().tolist()) == list(range(T * k))
+        for t in range(T):
+            for j in range(k):
+                r = dest[t, j]
+                assert row_token[r] == t and off[idx[t, j]] <= r < off[idx[t, j] + 1]
+        for e in range(E):
+            toks = row_token[off[e]:off[e + 1]]
+            assert list(toks) == sorted(toks)
+
+    check()
