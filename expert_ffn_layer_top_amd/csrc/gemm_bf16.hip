@@ -630,7 +630,8 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
 // [x * per, (x + 1) * per), per = ceil(tiles / 8), which its workgroups take in strides of the
 // number of workgroups on the XCD, so the tiles that run at once on one XCD share operand rows in
 // its L2.  Weight gradients whose largest expert holds more than twice the mean rows deal tiles
-// round-robin over all workgroups instead, so the hot expert's (long) tiles spread over the chip.
+// round-robin over all workgroups instead (snake order: odd rounds run the workgroups backwards),
+// so the hot experts' (long) tiles spread over the chip and do not pile up on the same ones.
 // The K steps of a workgroup's tiles form one stream through the LDS rings: the DMA of the next
 // tile's first two steps is issued during the current tile's last two, so it lands while the
 // current tile's epilogue runs.  Each tile runs at least two K steps (zero-filled past its data),
@@ -680,7 +681,12 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   const OpLoad ld = op_load<MODE>(p, role_b, h);
   Tile t = tile_at<MODE>(p, mts, ntiles_n, lid);
   TileSrc cur = tile_src<MODE>(p, t, role_b, h);
-  int lid_n = lid + lstep;
+  // round-robin deal in snake order: round r gives workgroup b tile r G + b (r even) or
+  // r G + G - 1 - b (r odd), so the workgroups holding the first (hottest, lowest-id) experts'
+  // tiles take the lightest of the next round's
+  int rn = 1;
+  auto deal_lid = [&](int r) { return r * G + ((r & 1) ? (G - 1 - bid) : bid); };
+  int lid_n = deal ? deal_lid(1) : lid + lstep;
   Tile tn = t;
   TileSrc nxt = empty_src(p);
   if (lid_n < lend) {
@@ -729,7 +735,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     t = tn;
     cur = nxt;
     kt = 0;
-    lid_n += lstep;
+    lid_n = deal ? deal_lid(++rn) : lid_n + lstep;
     if (lid_n < lend) {
       tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
       nxt = tile_src<MODE>(p, tn, role_b, h);

@@ -499,7 +499,12 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
   constexpr int SST = SGRP ? 256 : (WG ? 16 : 64);
   Tile t = tile_at<MODE>(p, mts, ntiles_n, lid);
   TileSrc cur = tile_src<MODE>(p, t, role_b);
-  int lid_n = lid + lstep;
+  // round-robin deal in snake order: round r gives workgroup b tile r G + b (r even) or
+  // r G + G - 1 - b (r odd), so the workgroups holding the first (hottest, lowest-id) experts'
+  // tiles take the lightest of the next round's
+  int rn = 1;
+  auto deal_lid = [&](int r) { return r * G + ((r & 1) ? (G - 1 - bid) : bid); };
+  int lid_n = deal ? deal_lid(1) : lid + lstep;
   Tile tn = t;
   TileSrc nxt = empty_src(p);
   if (lid_n < lend) {
@@ -595,7 +600,7 @@ __global__ __launch_bounds__(NTH, 1) void mx_grouped_gemm_kernel(Params p) {
     t = tn;
     cur = nxt;
     kt = 0;
-    lid_n += lstep;
+    lid_n = deal ? deal_lid(++rn) : lid_n + lstep;
     if (lid_n < lend) {
       tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
       nxt = tile_src<MODE>(p, tn, role_b);
