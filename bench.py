@@ -150,10 +150,12 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=False, set
     # settle: a fresh process stalls for milliseconds around its first steps and the clocks ramp
     # over the next tens of steps, which per-kernel events do not see but a short wall-clock
     # region does; untimed steps until `settle` seconds after the first one
+    settled = 0
     while time.perf_counter() - t_first < settle:
         for _ in range(4):
             step()
         torch.cuda.synchronize()
+        settled += 4
     # no collector pauses in the measured passes (a full collection can stall the host for tens of
     # milliseconds while the GPU drains its queue): collect now, re-enable at the end
     gc.collect()
@@ -180,7 +182,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=False, set
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.enable()
-    return elapsed, gemm_ms, row_ms, aux_ms, dom, mean_ms(evd, dom)
+    return elapsed, gemm_ms, row_ms, aux_ms, dom, mean_ms(evd, dom), settled
 
 
 def traffic_of(cfg, call):
@@ -272,8 +274,8 @@ def main():
               file=sys.stderr)
         return 2
     cfg = workload_config(args)
-    elapsed, gemm_ms, row_ms, aux_ms, dom, dom_ms = run_gpu(cfg, args.steps, args.warmup, args.copy_probe,
-                                                            args.recompute, args.flush, args.settle)
+    elapsed, gemm_ms, row_ms, aux_ms, dom, dom_ms, settled = run_gpu(cfg, args.steps, args.warmup, args.copy_probe,
+                                                                     args.recompute, args.flush, args.settle)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
     flops = gemm_flops(cfg)
@@ -288,6 +290,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settled,          # untimed steps after the warm-up (--settle seconds)
+        "instrumented_steps": args.steps,  # untimed pass with every call bracketed
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
