@@ -25,6 +25,7 @@ where it is silent is listed in the design notes of the repository.
 Modules
   codecs   bf16 / E4M3 / E8M0 bit codecs
   moe      the layer's steps, forward and backward, one function per library entry point
+  moe_mx   the layer with every expert product on MXFP8 operands, as a chain of those steps
   mxfp8    MX block quantisation (row blocks, column blocks, grouped token blocks)
   sampled  per-row / per-expert evaluators for checking full-size runs on samples
 
@@ -32,4 +33,4 @@ Every function here is pinned in tests/test_oracle_*.py against something other 
 itself (brute force, closed forms, invariants, CPU torch, exhaustive enumeration).
 """
 
-from . import codecs, moe, mxfp8, sampled  # noqa: F401
+from . import codecs, moe, moe_mx, mxfp8, sampled  # noqa: F401

@@ -24,8 +24,13 @@ from .codecs import bf16_to_f64, e4m3_encode_rne_sat, e4m3_to_f64, e8m0_to_f64
 BLOCK = 32
 
 
-def quantize_blocks(v_bf16):
+def quantize_blocks(v_bf16, scale_mode=0):
     """Quantise bf16 blocks along the last axis (length a multiple of 32).
+
+    scale_mode 0 is the rule above.  scale_mode 1 takes instead the smallest power of two X with
+    amax / X <= 448 (E4M3's largest value), so no element saturates: since 448 = 1.75 * 2^8 this
+    is shared = floor(log2 amax) - 8, plus one when amax's significand exceeds 1.75 (the
+    rounded-up scale some training recipes use; the MX definition's rule is mode 0).
 
     Returns (q uint8, same shape; scale uint8, last axis / 32).
     """
@@ -33,10 +38,14 @@ def quantize_blocks(v_bf16):
     *lead, C = v.shape
     if C % BLOCK:
         raise ValueError("quantize_blocks: last axis must be a multiple of 32")
+    if scale_mode not in (0, 1):
+        raise ValueError("quantize_blocks: scale_mode must be 0 or 1")
     vb = v.reshape(*lead, C // BLOCK, BLOCK)
     amax = np.max(np.abs(vb), axis=-1)
     mant, ex = np.frexp(amax)            # amax = mant * 2^ex, mant in [0.5, 1)
     e = ex.astype(np.int64) - 1          # floor(log2(amax)) for amax > 0
+    if scale_mode == 1:
+        e = e + (2 * mant > 1.75)        # significand 2 * mant in [1, 2)
     shared = np.clip(e - 8, -127, 127)
     shared = np.where(amax == 0, -127, shared)
     scale = (shared + 127).astype(np.uint8)
@@ -53,16 +62,16 @@ def dequantize_blocks(q, scale):
     return (qv.reshape(*lead, C // BLOCK, BLOCK) * s[..., None]).reshape(*lead, C)
 
 
-def quantize_rows(x_bf16):
+def quantize_rows(x_bf16, scale_mode=0):
     """Blocks along the contiguous (last) dimension; output in the input's layout."""
-    return quantize_blocks(x_bf16)
+    return quantize_blocks(x_bf16, scale_mode)
 
 
-def quantize_cols(x_bf16):
+def quantize_cols(x_bf16, scale_mode=0):
     """Blocks along the strided (first) dimension of a [..., R, C] tensor; the output is
     transposed to [..., C, R] so that each block is contiguous again."""
     x = np.asarray(x_bf16, dtype=np.uint16)
-    return quantize_blocks(np.swapaxes(x, -1, -2).copy())
+    return quantize_blocks(np.swapaxes(x, -1, -2).copy(), scale_mode)
 
 
 def quantize_grouped(x_bf16, offsets, offsets_pad, row_token=None):

@@ -121,3 +121,40 @@ def test_e8m0_decode():
     assert np.isnan(codecs.e8m0_to_f64(np.array([255], dtype=np.uint8)))[0]
     ref = torch.from_numpy(s.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
     assert np.array_equal(codecs.e8m0_to_f64(s), ref)
+
+
+# ---------------------------------------------------------------- f64 -> bf16 (fp32 storage)
+
+def _bf16_neighbours():
+    """Finite positive bf16 values v with an even last mantissa bit and their successors."""
+    b = np.arange(0x0080, 0x7F7F, 2, dtype=np.uint32).astype(np.uint16)     # normals, even mantissa
+    return b, codecs.bf16_to_f64(b), codecs.bf16_to_f64(b + 1)
+
+
+def test_f64_to_bf16_equals_f32_rounding_on_f32_values():
+    # values representable in fp32 take one rounding, pinned above against torch
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    x = x[np.isfinite(x)]
+    assert np.array_equal(codecs.f64_to_bf16(x.astype(np.float64)), codecs.f32_to_bf16(x))
+
+
+def test_f64_to_bf16_rounds_through_fp32():
+    # The helper models an fp32 accumulator stored as bf16: first to fp32 (nearest even), then to
+    # bf16 (nearest even).  Just above a bf16 midpoint m (itself an fp32 value), an excess below
+    # half an fp32 ulp is lost in the first rounding, so the tie goes to the even neighbour; an
+    # excess above it rounds away, as a single rounding would.
+    b, v, w = _bf16_neighbours()
+    m = (v + w) / 2
+    assert np.array_equal(codecs.f64_to_bf16(m), b)                          # exact tie -> even
+    assert np.array_equal(codecs.f64_to_bf16(m * (1 + 2.0 ** -30)), b)       # below half an fp32 ulp
+    assert np.array_equal(codecs.f64_to_bf16(m * (1 + 2.0 ** -20)), b + 1)   # above it
+    assert np.array_equal(codecs.f64_to_bf16(-m * (1 + 2.0 ** -20)), (b + 1) | 0x8000)
+
+
+def test_f64_to_bf16_error_bound_and_monotone():
+    rng = np.random.default_rng(10)
+    x = np.sort(rng.standard_normal(100_000) * np.exp2(rng.integers(-60, 60, size=100_000)))
+    r = codecs.bf16_to_f64(codecs.f64_to_bf16(x))
+    assert np.all(np.abs(r - x) <= (2.0 ** -8 + 2.0 ** -24) * np.abs(x))   # half a bf16 ulp + fp32 step
+    assert np.all(np.diff(r) >= 0)

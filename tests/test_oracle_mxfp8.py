@@ -160,3 +160,46 @@ def test_mx_product_exact_on_representable_operands():
     got = mxfp8.mx_gemm_nt(qa, sa, qb, sb)
     want = a.astype(np.int64) @ b.astype(np.int64).T
     assert np.array_equal(got, want.astype(np.float64))
+
+
+# ---------------------------------------------------------------- scale_mode 1 (rounded-up scale)
+
+def test_ceil_scale_is_smallest_power_of_two_without_saturation():
+    # every bf16 significand (1 + M/128) at several exponents: the scale X of mode 1 is the
+    # smallest power of two with amax / X <= 448
+    for e in (-120, -10, 0, 3, 50, 119):
+        for M in range(128):
+            amax = (1 + M / 128) * 2.0 ** e
+            v = np.zeros(32, dtype=np.float32)
+            v[11] = -amax
+            q, s = mxfp8.quantize_blocks(block_of(v), scale_mode=1)
+            X = 2.0 ** (int(s[0, 0]) - 127)
+            assert amax / X <= 448, (e, M)
+            if s[0, 0] > 0:                  # (the scale byte's floor 2^-127 may bind below that)
+                assert amax / (X / 2) > 448, (e, M)
+
+
+def test_ceil_scale_against_floor_rule():
+    # mode 1 equals mode 0 except when amax's significand exceeds 1.75 (bf16 mantissa field
+    # above 96), where the scale is one larger; equal scales give equal codes
+    rng = np.random.default_rng(5)
+    x = to_bf16_bits((rng.standard_normal((400, 64)) * np.exp2(rng.integers(-30, 30, (400, 1)))).astype(np.float32))
+    q0, s0 = mxfp8.quantize_rows(x)
+    q1, s1 = mxfp8.quantize_rows(x, scale_mode=1)
+    amax_bits = np.max(x.reshape(400, 2, 32) & 0x7FFF, axis=-1)
+    up = (amax_bits & 0x7F) > 96
+    assert up.any() and (~up).any()
+    assert np.array_equal(s1.astype(int) - s0.astype(int), up.astype(int))
+    same = np.repeat(~up, 32, axis=1)
+    assert np.array_equal(q1[same], q0[same])
+
+
+def test_ceil_scale_roundtrip_never_saturates():
+    rng = np.random.default_rng(6)
+    x = to_bf16_bits((rng.standard_normal((300, 96)) * 100).astype(np.float32))
+    q, s = mxfp8.quantize_rows(x, scale_mode=1)
+    v = codecs.bf16_to_f64(x)
+    r = mxfp8.dequantize_blocks(q, s)
+    X = np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=1)
+    assert np.all(np.abs(r - v) <= np.maximum(2.0 ** -4 * np.abs(v), 2.0 ** -10 * X))
+    assert not np.any((q & 0x7F) == 0x7E) or np.all(np.abs(v[(q & 0x7F) == 0x7E]) <= 448 * X[(q & 0x7F) == 0x7E])
