@@ -59,7 +59,22 @@ int check_gg_shape(int dtype, int E, int n, int d, int f) {
   const int q = dtype == MOE_MXFP8 ? 128 : 64;
   MOE_REQUIRE(d >= q && d % q == 0 && f >= q && f % q == 0, MOE_ERR_UNSUPPORTED,
               "d and f must be positive multiples of %d for this dtype", q);
-  MOE_REQUIRE(static_cast<long long>(n) * (d > f ? d : f) < (1LL << 40), MOE_ERR_UNSUPPORTED, "tensor too large");
+  // Everything the kernels of any call (the composite ones included) check at launch, checked
+  // here first, so that an unsupported size is reported before anything is enqueued: buffer
+  // offsets below 2^31 bytes for every operand, and tile counts below 2^31.
+  const long long eb = dtype == MOE_MXFP8 ? 1 : 2;
+  const long long dmax = d > f ? d : f;
+  MOE_REQUIRE(static_cast<long long>(n) * dmax * eb < 0x7fffffffLL && static_cast<long long>(d) * f * eb < 0x7fffffffLL,
+              MOE_ERR_UNSUPPORTED, "grouped GEMM: an operand exceeds 2 GiB");
+  if (dtype == MOE_MXFP8) {
+    const int P = moe_mx_pad_cap(n, E);
+    MOE_REQUIRE(P > 0 && static_cast<long long>(P) * dmax < 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
+                "grouped GEMM: the padded token axis of the weight-gradient operands exceeds 2 GiB");
+  }
+  const long long mtiles = static_cast<long long>(n) / 256 + E;
+  MOE_REQUIRE(mtiles * ((dmax + 127) / 128) < (1LL << 31) &&
+                  static_cast<long long>(E) * 2 * ((f + 255) / 256) * ((d + 255) / 256) < (1LL << 31),
+              MOE_ERR_UNSUPPORTED, "grouped GEMM: too many tiles");
   return MOE_OK;
 }
 

@@ -664,7 +664,7 @@ int gg_mx_down(int E, int n, int d, int f, const int32_t* offsets, const uint16_
                const uint8_t* wds, uint16_t* yexp, uint8_t* ws, hipStream_t s) {
   uint8_t* aq = ws;
   uint8_t* as = ws + static_cast<size_t>(n) * f;
-  if (int st = mxfp8_quantize(a, 1, n, f, 0, aq, as, s)) return st;
+  if (int st = mxfp8_quantize(a, 1, n, f, 0, 0, aq, as, s)) return st;
   gmx::Params q{};
   q.offsets = offsets; q.E = E; q.n = n; q.d = d; q.f = f;
   q.a0 = aq; q.a0s = as; q.b0 = wdq; q.b0s = wds; q.o0 = yexp;
@@ -744,7 +744,7 @@ int gg_mx_backward(int E, int n, int d, int f, const int32_t* offsets, const int
                    hipStream_t s) {
   const MxBwdLayout L(E, n, d, f);
   // dgrad through W_down: dYexp quantised along d
-  if (int st = mxfp8_quantize(dyexp, 1, n, d, 0, ws + L.dyq, ws + L.dys, s)) return st;
+  if (int st = mxfp8_quantize(dyexp, 1, n, d, 0, 0, ws + L.dyq, ws + L.dys, s)) return st;
   if (int st = gg_mx_dgrad_down(E, n, d, f, offsets, ws + L.dyq, ws + L.dys, wdtq, wdts, g, u, dg, du, s)) return st;
   // wgrad of W_down: operands along grouped tokens
   if (int st = mxfp8_quantize_grouped(dyexp, nullptr, offsets, offsets_pad, E, n, d, ws + L.dyT, ws + L.dyTs, s)) return st;
@@ -752,8 +752,8 @@ int gg_mx_backward(int E, int n, int d, int f, const int32_t* offsets, const int
   if (int st = gg_mx_wgrad_down(E, n, d, f, offsets, offsets_pad, ws + L.dyT, ws + L.dyTs, ws + L.aT, ws + L.aTs, dwd, s))
     return st;
   // dgrad through W_gate, W_up: dG, dU quantised along f
-  if (int st = mxfp8_quantize(dg, 1, n, f, 0, ws + L.dgq, ws + L.dgs, s)) return st;
-  if (int st = mxfp8_quantize(du, 1, n, f, 0, ws + L.duq, ws + L.dus, s)) return st;
+  if (int st = mxfp8_quantize(dg, 1, n, f, 0, 0, ws + L.dgq, ws + L.dgs, s)) return st;
+  if (int st = mxfp8_quantize(du, 1, n, f, 0, 0, ws + L.duq, ws + L.dus, s)) return st;
   if (int st = gg_mx_dgrad_gate_up(E, n, d, f, offsets, ws + L.dgq, ws + L.dgs, ws + L.duq, ws + L.dus, wgtq, wgts,
                                    wutq, wuts, dxp, s))
     return st;

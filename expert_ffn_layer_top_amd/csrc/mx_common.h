@@ -14,14 +14,20 @@ namespace moe {
 
 // floor(log2(amax)) - 8 clamped to [-127, 127], from the magnitude bits of a bf16 amax
 // (amax_bits = max over the block of (bits & 0x7fff)).  Returns -127 for an all-zero block.
-__device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits) {
+// mode 1 (the rounded-up scale): the smallest power of two X with amax / X <= 448, i.e. one more
+// when amax's significand exceeds 1.75 (448 = 1.75 * 2^8), so that no element saturates.
+__device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits, int mode = 0) {
   if (amax_bits == 0) return -127;
   const int eb = static_cast<int>(amax_bits >> 7);
+  const int man = static_cast<int>(amax_bits & 0x7f);
   int e;
   if (eb > 0) {
     e = eb - 127;
-  } else {                                   // bf16 subnormal: m * 2^-133, m in [1, 127]
-    e = (31 - __clz(static_cast<int>(amax_bits & 0x7f))) - 133;
+    if (mode == 1 && man > 96) ++e;          // significand 1 + man/128 > 1.75
+  } else {                                   // bf16 subnormal: man * 2^-133, man in [1, 127]
+    const int top = 31 - __clz(man);
+    e = top - 133;
+    if (mode == 1 && 4 * man > (7 << top)) ++e;   // significand man / 2^top > 1.75
   }
   int s = e - 8;
   s = s < -127 ? -127 : s;

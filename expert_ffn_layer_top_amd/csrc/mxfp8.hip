@@ -17,7 +17,8 @@ namespace {
 
 // ---- rows: 4 lanes per 32-element block, 8 elements (16 bytes) per lane
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ in, long long total,
-                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
+                                                         int mode) {
   const long long g = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   const long long e0 = g * 8;
   const bool live = e0 < total;
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1, 64)));
   amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, 64)));
   if (!live) return;
-  const int sh = mx_shared_exp(amax);
+  const int sh = mx_shared_exp(amax, mode);
   const uint32_t o0 = mx_encode2(w[0] & 0xffffu, w[0] >> 16, sh) | (mx_encode2(w[1] & 0xffffu, w[1] >> 16, sh) << 16);
   const uint32_t o1 = mx_encode2(w[2] & 0xffffu, w[2] >> 16, sh) | (mx_encode2(w[3] & 0xffffu, w[3] >> 16, sh) << 16);
   *reinterpret_cast<uint2*>(q + e0) = make_uint2(o0, o1);
@@ -53,7 +54,8 @@ constexpr int kPitch = kTC + 2;  // LDS row pitch in bf16 (33 words: column read
 // scale[c * s_col + b * s_blk] (b counted from position 0; `scale` based at the tile's column 0).
 __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch], int ncols, long long pos0,
                                                    long long out_pitch, uint8_t* __restrict__ q,
-                                                   uint8_t* __restrict__ scale, long long s_col, long long s_blk) {
+                                                   uint8_t* __restrict__ scale, long long s_col, long long s_blk,
+                                                   int mode = 0) {
   const int c = threadIdx.x >> 2;
   const int blk = threadIdx.x & 3;
   if (c >= ncols) return;
@@ -65,7 +67,7 @@ __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch
     const uint32_t m = vals[i] & 0x7fffu;
     amax = m > amax ? m : amax;
   }
-  const int sh = mx_shared_exp(amax);
+  const int sh = mx_shared_exp(amax, mode);
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -80,7 +82,8 @@ __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch
 // in [batch][rows][cols] -> q [batch][cols][rows], scale [batch][cols][rows/32]
 // grid: (ceil(rows/128), ceil(cols/64), batch); rows % 32 == 0, cols % 64 == 0.
 __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ in, int rows, int cols,
-                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
+                                                         int mode) {
   __shared__ uint16_t tile[kTP][kPitch];
   const long long b = blockIdx.z;
   const int r0 = blockIdx.x * kTP;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
   if (r0 + blk * 32 >= rows) return;
   quant_tile_columns(tile, kTC, r0, rows, q + b * cols * static_cast<long long>(rows) + static_cast<long long>(c0) * rows,
                      scale + b * cols * static_cast<long long>(rows / 32) + static_cast<long long>(c0) * (rows / 32),
-                     rows / 32, 1);
+                     rows / 32, 1, mode);
 }
 
 // ---- both layouts from one read (the weights, quantised along each of their two dims every
@@ -279,23 +282,25 @@ extern "C" int moe_mx_pad_cap(int n, int E) {
   return cap < (1LL << 31) ? static_cast<int>(cap) : -1;
 }
 
-extern "C" int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, uint8_t* q,
-                              uint8_t* scale, void* stream) {
+extern "C" int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, int scale_mode,
+                              uint8_t* q, uint8_t* scale, void* stream) {
   MOE_CHECK_PTR(in); MOE_CHECK_PTR(q); MOE_CHECK_PTR(scale);
   MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(q);
   MOE_REQUIRE(batch >= 1 && rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG, "sizes must be positive");
+  MOE_REQUIRE(scale_mode == 0 || scale_mode == 1, MOE_ERR_INVALID_ARG, "scale_mode must be 0 or 1");
   hipStream_t s = as_stream(stream);
   if (axis == 0) {
     MOE_REQUIRE(cols % 32 == 0, MOE_ERR_UNSUPPORTED, "axis 0 needs cols %% 32 == 0");
     const long long total = static_cast<long long>(batch) * rows * cols;
-    quant_rows_kernel<<<static_cast<unsigned>((total / 8 + 255) / 256), 256, 0, s>>>(in, total, q, scale);
+    quant_rows_kernel<<<static_cast<unsigned>((total / 8 + 255) / 256), 256, 0, s>>>(in, total, q, scale,
+                                                                                    scale_mode);
     return check_launch("mxfp8_quantize rows");
   }
   MOE_REQUIRE(axis == 1, MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
   MOE_REQUIRE(rows % 32 == 0 && cols % 64 == 0, MOE_ERR_UNSUPPORTED, "axis 1 needs rows %% 32 == 0, cols %% 64 == 0");
   MOE_REQUIRE(batch <= 65535, MOE_ERR_UNSUPPORTED, "batch too large");
   dim3 grid((rows + kTP - 1) / kTP, cols / kTC, batch);
-  quant_cols_kernel<<<grid, 256, 0, s>>>(in, rows, cols, q, scale);
+  quant_cols_kernel<<<grid, 256, 0, s>>>(in, rows, cols, q, scale, scale_mode);
   return check_launch("mxfp8_quantize cols");
 }
 

@@ -356,10 +356,14 @@ extern "C" size_t moe_route_workspace_bytes(int T, int E, int k) {
   return nb * static_cast<size_t>(E) * sizeof(int32_t);
 }
 
-extern "C" int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
-                              float* topk_gate, float* probs, int32_t* counts, int32_t* offsets,
-                              int32_t* offsets_pad, int pad, int32_t* dest, int32_t* row_token,
-                              void* ws, size_t ws_bytes, void* stream) {
+namespace moe {
+namespace {
+
+// Host-visible checks of the route's arguments, shared by its entry points (everything but the
+// workspace).
+int check_route_args(const float* logits, int T, int E, int k, const int32_t* topk_idx, const float* topk_gate,
+                     const float* probs, const int32_t* counts, const int32_t* offsets, const int32_t* offsets_pad,
+                     int pad, const int32_t* dest, const int32_t* row_token) {
   if (int st = check_layer_shape(T, E, k)) return st;
   MOE_CHECK_PTR(logits); MOE_CHECK_PTR(topk_idx); MOE_CHECK_PTR(topk_gate);
   MOE_CHECK_PTR(counts); MOE_CHECK_PTR(offsets); MOE_CHECK_PTR(dest);
@@ -368,12 +372,16 @@ extern "C" int moe_route_topk(const float* logits, int T, int E, int k, int32_t*
   if (probs) MOE_CHECK_ALIGN(probs);
   if (offsets_pad) { MOE_CHECK_ALIGN(offsets_pad); MOE_REQUIRE(pad >= 1, MOE_ERR_INVALID_ARG, "pad must be >= 1"); }
   if (row_token) MOE_CHECK_ALIGN(row_token);
-  const size_t need = moe_route_workspace_bytes(T, E, k);
-  MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "route workspace: need %zu bytes", need);
-  MOE_CHECK_ALIGN(ws);
-  hipStream_t s = as_stream(stream);
+  return MOE_OK;
+}
+
+// The three kernels of the route, with `hist` (moe_route_workspace_bytes bytes of device memory)
+// as the per-block expert counts.  route_topk_local writes every entry before route_scan reads
+// it, so the buffer needs no clearing.
+int enqueue_route(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_gate, float* probs,
+                  int32_t* counts, int32_t* offsets, int32_t* offsets_pad, int pad, int32_t* dest,
+                  int32_t* row_token, int32_t* hist, hipStream_t s) {
   const int nb = (T + kRouteBlock - 1) / kRouteBlock;
-  int32_t* hist = static_cast<int32_t*>(ws);
   const int nq = (E + kGroup - 1) / kGroup;
   if (nq <= 1) route_topk_local<1><<<nb, 1024, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
   else if (nq <= 2) route_topk_local<2><<<nb, 1024, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, probs, dest, hist);
@@ -388,6 +396,23 @@ extern "C" int moe_route_topk(const float* logits, int T, int E, int k, int32_t*
   const long long n = static_cast<long long>(T) * k;
   route_finalize<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(topk_idx, dest, hist, offsets, T, k, E, row_token);
   return check_launch("route_finalize");
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                              float* topk_gate, float* probs, int32_t* counts, int32_t* offsets,
+                              int32_t* offsets_pad, int pad, int32_t* dest, int32_t* row_token,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_route_args(logits, T, E, k, topk_idx, topk_gate, probs, counts, offsets, offsets_pad, pad, dest,
+                                row_token))
+    return st;
+  const size_t need = moe_route_workspace_bytes(T, E, k);
+  MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "route workspace: need %zu bytes", need);
+  MOE_CHECK_ALIGN(ws);
+  return enqueue_route(logits, T, E, k, topk_idx, topk_gate, probs, counts, offsets, offsets_pad, pad, dest, row_token,
+                       static_cast<int32_t*>(ws), as_stream(stream));
 }
 
 extern "C" int moe_route_topk_bwd(const float* topk_gate, const int32_t* topk_idx, const float* d_gate,

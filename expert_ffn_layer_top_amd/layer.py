@@ -33,10 +33,16 @@ class Weights:
     w_down: torch.Tensor                 # [E, d, f] bf16
     w_r: torch.Tensor = None             # [d, E] fp32, when the layer owns its router
     mx: dict = field(default_factory=dict)
+    mx_key: tuple = None                 # the bf16 weights the MXFP8 copies were made from
 
     @property
     def E(self):
         return self.w_gate.shape[0]
+
+    def _key(self):
+        # storage and in-place version of each bf16 weight: an optimizer step that updates a
+        # weight in place bumps its version, a new tensor changes its storage
+        return tuple((t.data_ptr(), t._version) for t in (self.w_gate, self.w_up, self.w_down))
 
     def quantize_mx(self):
         """MXFP8 copies of the expert weights, blocks along each product's contraction dim:
@@ -46,7 +52,15 @@ class Weights:
         for name, w in (("wg", self.w_gate), ("wu", self.w_up), ("wd", self.w_down)):
             q[name], q[name + "_s"], q[name + "_t"], q[name + "_t_s"] = ops.mxfp8_quantize_both(w)
         self.mx = q
+        self.mx_key = self._key()
         return q
+
+    def mx_current(self):
+        """The MXFP8 copies of the weights as they are now: quantised again whenever a bf16 weight
+        was replaced or modified in place since the copies were made."""
+        if not self.mx or self.mx_key != self._key():
+            return self.quantize_mx()
+        return self.mx
 
 
 class _Span:
@@ -89,6 +103,9 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
     gate/up product again on the kept permuted input (per-layer activation recompute, [card]
     "Supercharging Olmo-core ...": used at the largest scale).  The kernels are deterministic,
     so the backward's results are bit-identical either way.
+    mxfp8: the expert products run on MXFP8 operands; the weights' MXFP8 copies are made on the
+    first such forward and again whenever a bf16 weight was replaced or changed in place
+    (Weights.mx_current), so an optimizer step between two forwards is always seen.
     balance_weight: also compute the router's load-balancing score and the balance statistics of
     the actual load (ctx["balance"]: p_mean [E], stats [aux, load_max, prob_max, load_cv]), and
     add the gradient of balance_weight * aux to d_logits in the backward."""
@@ -113,12 +130,13 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
         with _Span(events, "down"):
             yexp = ops.grouped_gemm_down(a, r["offsets"], weights.w_down)
     else:
-        q = weights.mx or weights.quantize_mx()
+        q = weights.mx_current()
         with _Span(events, "quant_x"):
             xq, xs = ops.mxfp8_quantize(x, 0)
         with _Span(events, "permute"):
             xpq, xps = ops.permute(xq, r["dest"], x_scale=xs)
         ctx["xq"], ctx["xs"], ctx["xpq"], ctx["xps"] = xq, xs, xpq, xps
+        ctx["mx_weights"] = q            # the backward uses the copies this forward used
         with _Span(events, "gate_up"):
             g, u, a = ops.grouped_gemm_gate_up(xpq, r["offsets"], q["wg"], q["wu"],
                                                scales=(xps, q["wg_s"], q["wu_s"]))
@@ -173,7 +191,7 @@ def backward(ctx, weights, dy, events=None):
             if not ctx["mxfp8"]:
                 g, u, a = ops.grouped_gemm_gate_up(ctx["xp"], off, weights.w_gate, weights.w_up)
             else:
-                q = weights.mx
+                q = ctx["mx_weights"]
                 g, u, a = ops.grouped_gemm_gate_up(ctx["xpq"], off, q["wg"], q["wu"],
                                                    scales=(ctx["xps"], q["wg_s"], q["wu_s"]))
     if not ctx["mxfp8"]:
@@ -190,7 +208,7 @@ def backward(ctx, weights, dy, events=None):
     else:
         # MXFP8: every operand quantised along its product's contraction dim (rows for the dgrads,
         # grouped tokens padded to 32 for the wgrads), then one kernel per product
-        q = weights.mx
+        q = ctx["mx_weights"]
         n = g.shape[0]
         pad = ctx["offsets_pad"]
         with _Span(events, "dgrad_down"):

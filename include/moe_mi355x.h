@@ -37,8 +37,10 @@
  *     moe_route_topk with the same T, k).  A failed kernel launch returns MOE_ERR_HIP; its
  *     text is in moe_last_error_string() (per calling thread).  Asynchronous faults surface
  *     at the caller's next synchronisation.
- *   - Shapes: 1 <= E <= 256, 1 <= k <= min(E, 16), T >= 1, T*k < 2^31, d and f multiples of
- *     64 (of 32 for the MXFP8 scale layout, implied).  Anything else: MOE_ERR_UNSUPPORTED.
+ *   - Shapes: 1 <= E <= 256, 1 <= k <= min(E, 16), T >= 1, T*k < 2^31; d and f multiples of
+ *     64 for bf16, of 128 for the MXFP8 grouped GEMMs (their K steps are 128 elements, four
+ *     E8M0 blocks); MXFP8 row tensors need their blocked dimension a multiple of 32.  Anything
+ *     else: MOE_ERR_UNSUPPORTED.
  *
  * Layouts (n = T*k routed rows):
  *   x [T,d] bf16; router weight w_r [d,E] fp32; logits [T,E] fp32;
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_MI355X_ABI_VERSION 1
+#define MOE_MI355X_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -90,7 +92,9 @@ int moe_router_project(const uint16_t* x, const float* w_r, int T, int d, int E,
 /* Workspace for moe_router_project_bwd (the split-K partial sums of dw_r). */
 size_t moe_router_bwd_workspace_bytes(int T, int d, int E);
 
-/* Backward of moe_router_project:  dx_router[T,d] = d_logits @ w_r^T (fp32),
+/* Backward of moe_router_project ([news] lead paragraphs: the stack trains the model, router
+ * included, so the projection that scores the experts has a gradient):
+ * dx_router[T,d] = d_logits @ w_r^T (fp32),
  * dw_r[d,E] = x^T @ d_logits (fp32; summed over token chunks in a fixed order, so repeated calls
  * give identical bits).  Either output may be NULL to skip it; ws (>= moe_router_bwd_workspace_bytes)
  * is needed only for dw_r.  Same arithmetic and argument limits as moe_router_project. */
@@ -118,7 +122,9 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, 
                    int32_t* offsets_pad_or_null, int pad, int32_t* dest, int32_t* row_token_or_null,
                    void* ws, size_t ws_bytes, void* stream);
 
-/* Backward of the renormalised gates with the selection held fixed:
+/* Backward of the renormalised gates with the selection held fixed ([news] lead paragraphs: the
+ * router sends each token to a small selection of experts; training differentiates the gates
+ * of that selection, not the discrete choice):
  * d_logits[t, idx[t,j]] = g_j * (dg_j - sum_i g_i dg_i), 0 for experts not chosen.  [T,E] fp32. */
 int moe_route_topk_bwd(const float* topk_gate, const int32_t* topk_idx, const float* d_gate, int T,
                        int E, int k, float* d_logits, void* stream);
@@ -153,12 +159,15 @@ int moe_route_topk_bwd_balance(const float* topk_gate, const int32_t* topk_idx, 
 int moe_permute(int dtype, const void* x, const uint8_t* x_scale_or_null, const int32_t* dest,
                 int T, int d, int k, void* xp, uint8_t* xp_scale_or_null, void* stream);
 
-/* Weighted unpermute-combine: y[t] = sum_j topk_gate[t,j] * yexp[dest[t,j]], fp32 in slot order,
- * bf16 out. */
+/* Weighted unpermute-combine, the return path of the rowwise exchange ([news] "Routing work stays
+ * on the GPU": routed rows live in expert buffers; the lead paragraphs: each token's output is
+ * its chosen experts' outputs weighted by the router):
+ * y[t] = sum_j topk_gate[t,j] * yexp[dest[t,j]], fp32 in slot order, bf16 out. */
 int moe_unpermute_combine(const uint16_t* yexp, const float* topk_gate, const int32_t* dest, int T,
                           int d, int k, uint16_t* y, void* stream);
 
-/* Backward of the combine: dyexp[dest[t,j]] = bf16(gate[t,j] * dy[t]);
+/* Backward of the combine (the gradient flows back along the same rowwise path, [news] "Routing
+ * work stays on the GPU"): dyexp[dest[t,j]] = bf16(gate[t,j] * dy[t]);
  * d_gate[t,j] = <dy[t], yexp[dest[t,j]]> (fp32). */
 int moe_unpermute_combine_bwd(const uint16_t* dy, const uint16_t* yexp, const float* topk_gate,
                               const int32_t* dest, int T, int d, int k, uint16_t* dyexp,
@@ -174,8 +183,10 @@ int moe_unpermute_combine_bwd_mx(const uint16_t* dy, const uint16_t* yexp, const
                                  const int32_t* dest, int T, int d, int k, uint8_t* dyexp_q,
                                  uint8_t* dyexp_scale, float* row_gate, float* d_gate, void* stream);
 
-/* Backward of the permute: dx[t] = sum_j dxp[dest[t,j]] (+ dx_addend[t] if given, the fp32
- * router-path term), fp32 accumulation, bf16 out. */
+/* Backward of the permute: each token gathers the gradients of its k expert rows back from the
+ * expert buffers ([news] "Routing work stays on the GPU", the rowwise write run in reverse):
+ * dx[t] = sum_j dxp[dest[t,j]] (+ dx_addend[t] if given, the fp32 router-path term), fp32
+ * accumulation, bf16 out. */
 int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int k,
                     const float* dx_addend_or_null, uint16_t* dx, void* stream);
 
@@ -183,15 +194,19 @@ int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int 
 
 /* MXFP8 block quantisation of a bf16 tensor in[batch][rows][cols]
  * ([news] "MXFP8 reduces compute and memory costs").  Per block of 32 bf16 values:
- * amax = max|v|; scale byte s = clamp(floor(log2 amax) - 8, -127, 127) + 127 (s = 0 when
- * amax = 0); q = E4M3(v / 2^(s-127)) with round-to-nearest-even, magnitudes above 448 saturate
- * to 448, signs (and -0) kept.
+ * amax = max|v|; scale byte s = clamp(e - 8, -127, 127) + 127 (s = 0 when amax = 0), with
+ *   scale_mode 0: e = floor(log2 amax) (the MX definition's rule; every other entry point of
+ *                 this library quantises this way);
+ *   scale_mode 1: e = floor(log2 amax) + 1 when amax's significand exceeds 1.75, else as mode 0:
+ *                 the smallest power-of-two scale with amax / scale <= 448, so nothing saturates;
+ * q = E4M3(v / 2^(s-127)) with round-to-nearest-even, magnitudes above 448 saturate to 448,
+ * signs (and -0) kept.  Any other scale_mode: MOE_ERR_INVALID_ARG.
  *   axis 0: blocks along cols (the contiguous dim): q [batch][rows][cols], scale [batch][rows][cols/32]
  *           (cols % 32 == 0)
  *   axis 1: blocks along rows (the strided dim), output transposed:
  *           q [batch][cols][rows], scale [batch][cols][rows/32]   (rows % 32 == 0) */
-int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, uint8_t* q,
-                   uint8_t* scale, void* stream);
+int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, int scale_mode,
+                   uint8_t* q, uint8_t* scale, void* stream);
 
 /* Both mxfp8_quantize layouts of one input from a single read of it: q/scale as axis 0 and
  * qT/scaleT as axis 1, bit-identical to the two separate calls.  For the expert weights, which
@@ -201,7 +216,9 @@ int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, 
 int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int cols, uint8_t* q, uint8_t* scale,
                         uint8_t* qT, uint8_t* scaleT, void* stream);
 
-/* Token-axis MXFP8 blocks restarting at each expert group (the weight-gradient operands).
+/* Token-axis MXFP8 blocks restarting at each expert group: the weight-gradient operands, whose
+ * product contracts over each expert's tokens ([news] "MXFP8 reduces compute and memory costs":
+ * one scale per small block of values, here blocks of 32 tokens of one expert).
  * Row r of the grouped tensor is in[r] (row_token NULL; in is [n,C]) or in[row_token[r]]
  * (in is the token-major source [T,C]).  Expert e's rows [offsets[e], offsets[e+1]) go to
  * positions [offsets_pad[e], offsets_pad[e] + count_e) of a padded token axis; padding
@@ -262,7 +279,10 @@ int moe_grouped_gemm_down(int dtype, int E, int n, int d, int f, const int32_t* 
                           const uint16_t* a, const void* w_down, const uint8_t* w_down_scale,
                           uint16_t* yexp, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward of moe_grouped_gemm_swiglu (dgrad and wgrad grouped GEMMs).
+/* Backward of moe_grouped_gemm_swiglu: the dgrad and wgrad grouped GEMMs that training the
+ * experts needs ([news] "Routing work stays on the GPU": grouped GEMM; [card] "Summary":
+ * device-scheduled grouped GEMMs in the training stack; "MXFP8 reduces compute and memory
+ * costs" for the MXFP8 form).
  *   da = dyexp W_down[e];  dg = da * u * s * (1 + g (1 - s)),  du = da * g * s,  s = sigmoid(g)
  *   dxp = dg W_gate[e] + du W_up[e]
  *   dw_down[e] = dyexp_e^T a_e,  dw_gate[e] = dg_e^T xp_e,  dw_up[e] = du_e^T xp_e

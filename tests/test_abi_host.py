@@ -43,7 +43,7 @@ def test_every_declared_function_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert _lib.lib.moe_abi_version() == 1
+    assert _lib.lib.moe_abi_version() == 2
     assert _lib.lib.moe_status_string(0) == b"ok"
     assert b"workspace" in _lib.lib.moe_status_string(3)
     assert _lib.lib.moe_status_string(99) == b"unknown status"
@@ -80,8 +80,10 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_permute(0, fake, fake, fake, 16, 128, 2, fake, fake, None) == INVALID
     assert L.moe_permute(7, fake, None, fake, 16, 128, 2, fake, None, None) == UNSUPPORTED
     # quantiser: bad axis, cols not a multiple of 32
-    assert L.mxfp8_quantize(fake, 1, 64, 64, 2, fake, fake, None) == INVALID
-    assert L.mxfp8_quantize(fake, 1, 64, 48, 0, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp8_quantize(fake, 1, 64, 64, 2, 0, fake, fake, None) == INVALID
+    assert L.mxfp8_quantize(fake, 1, 64, 48, 0, 0, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp8_quantize(fake, 1, 64, 64, 0, 2, fake, fake, None) == INVALID       # scale_mode 0 or 1
+    assert L.mxfp8_quantize(fake, 1, 64, 64, 0, -1, fake, fake, None) == INVALID
     # grouped GEMM: MXFP8 needs d, f multiples of 128 and a workspace
     args = [fake] * 14
     assert L.moe_grouped_gemm_swiglu(1, 8, 256, 192, 256, *args, 0, None) == UNSUPPORTED

@@ -40,6 +40,12 @@ BF16_CASES = [
     dict(T=700, d=256, E=4, k=2, f=192, seed=3, hot=1),
     dict(T=300, d=320, E=1, k=1, f=448, seed=4),
     dict(T=1100, d=256, E=16, k=4, f=256, seed=5, empty=(0, 15)),
+    # fewer rows than one 256-row tile
+    dict(T=1, d=128, E=4, k=1, f=128, seed=6),
+    dict(T=3, d=192, E=8, k=2, f=256, seed=7),
+    # one expert far above twice the mean rows (every token picks expert 0): the weight
+    # gradients deal their tiles round-robin in snake order
+    dict(T=700, d=256, E=8, k=2, f=256, seed=8, hot=0),
 ]
 
 
@@ -102,6 +108,13 @@ MX_CASES = [
     dict(T=1000, d=384, E=9, k=3, f=128, seed=13, empty=(4,)),
     # contraction dims multiples of 512: the forward and dgrad products load scales in groups
     dict(T=700, d=1024, E=6, k=2, f=512, seed=14, empty=(3,)),
+    # fewer rows than one tile; a single dense expert; top-1 routing
+    dict(T=1, d=128, E=4, k=1, f=128, seed=15),
+    dict(T=3, d=256, E=8, k=2, f=128, seed=16),
+    dict(T=200, d=256, E=1, k=1, f=256, seed=17),
+    dict(T=500, d=128, E=6, k=1, f=256, seed=18),
+    # a hot expert far above twice the mean: round-robin (snake) deal of the weight gradients
+    dict(T=600, d=256, E=8, k=2, f=256, seed=19, hot=0),
 ]
 
 
@@ -232,7 +245,7 @@ def test_backward_per_kernel_calls_match_composite(mx):
 
 # ------------------------------------------------ persistent launch: many tiles per workgroup
 
-@pytest.mark.parametrize("case", [BF16_CASES[0], BF16_CASES[2], BF16_CASES[4]], ids=case_id)
+@pytest.mark.parametrize("case", [BF16_CASES[0], BF16_CASES[2], BF16_CASES[4], BF16_CASES[7]], ids=case_id)
 def test_bf16_few_workgroups_bit_identical(case, monkeypatch):
     """With 8 workgroups each runs many tiles in a row (the next tile's first K steps stream in
     during the previous tile's epilogue); every output must match the default launch bit for bit,

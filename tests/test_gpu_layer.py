@@ -2,6 +2,9 @@
 
   tiny      (256 tokens, d 128, 8 experts, top-2, d_ff 256, router weight): the float64 oracle
             runs the whole layer independently, router included.
+  mxfp8     small MXFP8 layers (router weight, every expert product on E4M3 operands): the
+            oracle's MXFP8 chain runs the whole layer from the GPU's logits, and the difference
+            to the unquantised float64 layer is reported (not gated).
   balanced  (8192 tokens, d 2048, 64 experts, top-4, d_ff 1024, round-robin logits): the
             benchmarked workload, at full size, in the same launch configuration the benchmark
             times.  Integer outputs are checked in full; float outputs on sampled rows, tokens
@@ -13,8 +16,8 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import codecs, moe, sampled
-from tests.gpu_util import BF16_TOL, assert_close, bits, host, note
+from oracle import codecs, moe, moe_mx, sampled
+from tests.gpu_util import BF16_TOL, assert_close, bits, host, note, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +63,75 @@ def test_tiny_layer_end_to_end_independent():
     assert_close(host(out["dw_r"]), dwr, BF16_TOL, "dw_r")
     for key in ("dw_gate", "dw_up", "dw_down"):
         assert_close(codecs.bf16_to_f64(bits(out[key])), bwd[key], BF16_TOL, key)
+
+
+def _check_mx_chain(cfg, inputs, ctx, out, what):
+    """The GPU's MXFP8 layer against the oracle's MXFP8 chain run independently on the same
+    inputs (routing from the GPU's own fp32 logits, which are checked against the oracle first):
+    every float output within the bf16 bar.  Also prints the end-to-end difference to the
+    unquantised float64 layer (MXFP8 rounding itself; reported, not gated)."""
+    x, w_r, wg, wu, wd, dy = (inputs[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "dy"))
+    lg = host(ctx["logits"])
+    assert_close(lg, moe.router_project(x, w_r), 1e-5, f"{what}: logits")
+    qw = moe_mx.quantize_weights(wg, wu, wd)
+    fwd = moe_mx.layer_forward_mx(x, w_r, cfg.k, qw, logits=lg)
+    assert np.array_equal(host(ctx["dest"]), fwd["dest"])
+    bwd = moe_mx.layer_backward_mx(fwd, x, dy, w_r, qw)
+    got = dict(y=codecs.bf16_to_f64(bits(ctx["y"])), dx=codecs.bf16_to_f64(bits(out["dx"])),
+               d_logits=host(out["d_logits"]), dw_r=host(out["dw_r"]),
+               dw_gate=codecs.bf16_to_f64(bits(out["dw_gate"])), dw_up=codecs.bf16_to_f64(bits(out["dw_up"])),
+               dw_down=codecs.bf16_to_f64(bits(out["dw_down"])))
+    want = dict(y=fwd["y"], dx=bwd["dx"], d_logits=bwd["d_logits"], dw_r=bwd["dw_r"], dw_gate=bwd["dw_gate"],
+                dw_up=bwd["dw_up"], dw_down=bwd["dw_down"])
+    for key in got:
+        assert_close(got[key], want[key], BF16_TOL, f"{what}: {key} (MXFP8 chain)")
+    # end-to-end difference to the unquantised layer (same routing), reported only
+    ref = moe.layer_forward(x, lg, cfg.k, wg, wu, wd)
+    rb = moe.layer_backward(ref, dy, wg, wu, wd)
+    add, dwr = moe.router_project_bwd(x, w_r, rb["d_logits"])
+    unq = dict(y=ref["y"], dx=rb["dx"] + add, d_logits=rb["d_logits"], dw_r=dwr, dw_gate=rb["dw_gate"],
+               dw_up=rb["dw_up"], dw_down=rb["dw_down"])
+    report = ", ".join(f"{k} {rel_err(got[k], unq[k]):.3f}" for k in got)
+    print(f"[MXFP8 vs unquantised float64 layer, max-rel-to-norm, not gated] {what}: {report}", flush=True)
+
+
+MX_LAYER_SHAPES = [dict(T=640, d=512, E=6, k=2, f=512), dict(T=200, d=256, E=1, k=1, f=256),
+                   dict(T=300, d=256, E=8, k=1, f=384)]
+
+
+@pytest.mark.parametrize("shape", MX_LAYER_SHAPES, ids=lambda s: "-".join(f"{k}{v}" for k, v in s.items()))
+def test_mxfp8_layer_against_oracle_chain(shape):
+    cfg = synth.CONFIGS["mxfp8"].with_(**shape)
+    inputs = synth.make_inputs(cfg)
+    note(f"layer mxfp8 fwd+bwd {shape}")
+    ctx, out = _run_layer(cfg, inputs)
+    _check_mx_chain(cfg, inputs, ctx, out, f"mxfp8 {shape}")
+
+
+def test_mxfp8_weights_requantised_after_in_place_update():
+    """An in-place change of a bf16 expert weight between two steps reaches the MXFP8 products:
+    the second step equals a step of fresh Weights built from the updated tensors."""
+    import torch
+    from expert_ffn_layer_top_amd import layer
+    cfg = synth.CONFIGS["mxfp8"].with_(T=256, d=256, E=4, k=2, f=256)
+    inputs = synth.make_inputs(cfg)
+    t = synth.to_torch(inputs, torch.device("cuda:0"))
+    w = layer.Weights(t["w_gate"], t["w_up"], t["w_down"], w_r=t["w_r"])
+    note("layer mxfp8 weight update between steps")
+    y0 = layer.forward(t["x"], w, cfg.k, mxfp8=True)["y"].clone()
+    with torch.no_grad():
+        w.w_gate.mul_(0.5)
+        w.w_down.add_(0.01)
+    ctx1 = layer.forward(t["x"], w, cfg.k, mxfp8=True)
+    out1 = layer.backward(ctx1, w, t["dy"])
+    fresh = layer.Weights(w.w_gate.clone(), w.w_up.clone(), w.w_down.clone(), w_r=t["w_r"])
+    ctx2 = layer.forward(t["x"], fresh, cfg.k, mxfp8=True)
+    out2 = layer.backward(ctx2, fresh, t["dy"])
+    torch.cuda.synchronize()
+    assert not torch.equal(ctx1["y"], y0)
+    assert torch.equal(ctx1["y"], ctx2["y"])
+    for key in ("dx", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(out1[key], out2[key]), key
 
 
 @pytest.fixture(scope="module")
@@ -168,6 +240,9 @@ def test_activation_recompute_bit_identical(mx):
     assert torch.equal(c0["y"], c1["y"])
     for key in ("dx", "d_logits", "dw_gate", "dw_up", "dw_down", "dg", "du", "dxp"):
         assert torch.equal(o0[key], o1[key]), f"{key}: recompute run differs"
+    if mx:
+        # and the recompute run itself against the oracle's MXFP8 chain at this shape
+        _check_mx_chain(cfg, inputs, c1, o1, "mxfp8 recompute")
 
 
 def test_layer_balance_score_in_step():

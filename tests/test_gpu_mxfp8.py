@@ -20,10 +20,10 @@ def finite_patterns():
     return b
 
 
-def check_rows(x_bits):
+def check_rows(x_bits, scale_mode=0):
     from expert_ffn_layer_top_amd import ops
-    q, s = ops.mxfp8_quantize(bf16_to_dev(x_bits), 0)
-    rq, rs = mxfp8.quantize_rows(x_bits)
+    q, s = ops.mxfp8_quantize(bf16_to_dev(x_bits), 0, scale_mode=scale_mode)
+    rq, rs = mxfp8.quantize_rows(x_bits, scale_mode=scale_mode)
     assert np.array_equal(host(s), rs), "scales differ"
     assert np.array_equal(host(q), rq), "elements differ"
 
@@ -36,22 +36,26 @@ def test_every_bf16_pattern_in_natural_blocks():
     check_rows(np.ascontiguousarray(b.reshape(32, 2048).T).reshape(64, 1024))
 
 
-def test_every_bf16_pattern_against_every_block_scale():
+@pytest.mark.parametrize("scale_mode", [0, 1])
+def test_every_bf16_pattern_against_every_block_scale(scale_mode):
     """Each bf16 pattern next to an anchor that fixes the block's scale, for anchors spanning the
-    scale range: exercises subnormal, normal and saturating encodes of every mantissa."""
+    scale range: exercises subnormal, normal and saturating encodes of every mantissa.  Under
+    scale_mode 1 the anchors with a significand above 1.75 raise the scale by one."""
     b = finite_patterns()
     mags = b & 0x7FFF
     for anchor_exp in (-120, -60, -10, 0, 7, 60, 120):
-        anchor = to_bf16_bits(np.array([1.5 * 2.0 ** anchor_exp], dtype=np.float32))[0]
-        sel = b[mags <= anchor]                                  # values not above the anchor
-        sel = sel[: (len(sel) // 31) * 31].reshape(-1, 31)
-        blocks = np.concatenate([np.full((sel.shape[0], 1), anchor, dtype=np.uint16), sel], axis=1)
-        nb = blocks.shape[0] // 32 * 32                          # rows of 32 blocks each
-        note(f"mxfp8 rows: anchor 2^{anchor_exp}, {nb} blocks")
-        check_rows(blocks[:nb].reshape(-1, 1024))
+        for sig in (1.5, 1.75, 1.7578125, 1.9921875):
+            anchor = to_bf16_bits(np.array([sig * 2.0 ** anchor_exp], dtype=np.float32))[0]
+            sel = b[mags <= anchor]                              # values not above the anchor
+            sel = sel[: (len(sel) // 31) * 31].reshape(-1, 31)
+            blocks = np.concatenate([np.full((sel.shape[0], 1), anchor, dtype=np.uint16), sel], axis=1)
+            nb = blocks.shape[0] // 32 * 32                      # rows of 32 blocks each
+            note(f"mxfp8 rows mode {scale_mode}: anchor {sig} * 2^{anchor_exp}, {nb} blocks")
+            check_rows(blocks[:nb].reshape(-1, 1024), scale_mode)
 
 
-def test_edge_blocks():
+@pytest.mark.parametrize("scale_mode", [0, 1])
+def test_edge_blocks(scale_mode):
     vals = np.zeros((8, 32), dtype=np.float32)
     vals[1, 5] = -0.0                                     # signed zero, all-zero block
     vals[2, 0] = 448.0 * 2.0 ** 20                        # exact 448 multiple
@@ -60,8 +64,8 @@ def test_edge_blocks():
     vals[5, :2] = [2.0 ** -130, -2.0 ** -133]             # bf16 subnormals only
     vals[6, :3] = [1e30, 1e-30, -1e20]                    # wide dynamic range
     vals[7] = np.linspace(-1, 1, 32)
-    note("mxfp8 rows: edge blocks")
-    check_rows(to_bf16_bits(vals.reshape(1, 256)))
+    note(f"mxfp8 rows mode {scale_mode}: edge blocks")
+    check_rows(to_bf16_bits(vals.reshape(1, 256)), scale_mode)
 
 
 @pytest.mark.parametrize("R,C", [(1, 32), (3, 64), (300, 2048), (1025, 7168)])
@@ -73,13 +77,14 @@ def test_rows_random(R, C):
 
 
 @pytest.mark.parametrize("B,R,C", [(1, 32, 64), (1, 288, 192), (3, 256, 128), (2, 2048, 1024), (1, 7168, 2048)])
-def test_cols_transposed(B, R, C):
+@pytest.mark.parametrize("scale_mode", [0, 1])
+def test_cols_transposed(B, R, C, scale_mode):
     from expert_ffn_layer_top_amd import ops
     rng = np.random.default_rng(B * R + C)
     x = to_bf16_bits(rng.standard_normal((B, R, C)).astype(np.float32))
-    note(f"mxfp8 cols B={B} R={R} C={C}")
-    q, s = ops.mxfp8_quantize(bf16_to_dev(x), 1)
-    rq, rs = mxfp8.quantize_cols(x)
+    note(f"mxfp8 cols B={B} R={R} C={C} mode {scale_mode}")
+    q, s = ops.mxfp8_quantize(bf16_to_dev(x), 1, scale_mode=scale_mode)
+    rq, rs = mxfp8.quantize_cols(x, scale_mode=scale_mode)
     assert np.array_equal(host(s), rs) and np.array_equal(host(q), rq)
 
 

@@ -16,7 +16,7 @@ import pytest
 
 import synth
 from oracle import codecs, moe, mxfp8, sampled
-from tests.gpu_util import BF16_TOL, MX_TOL, assert_close, bits, host, note
+from tests.gpu_util import BF16_TOL, MX_TOL, assert_close, bits, host, note, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -302,4 +302,15 @@ def test_mxfp8_full_size():
     assert_close(host(out["dw_r"]), dwr, BF16_TOL, "dW_r")
     assert_close(host(_dev_rows(out["dx_router"], toks)), add[toks], BF16_TOL, "dx router term tokens")
     _check_dx(cfg, out, dest, toks, addend=host(_dev_rows(out["dx_router"], toks)))
+
+    # end-to-end difference of y to the unquantised float64 layer on the sampled tokens (the
+    # GPU's routing, bf16 weights, no MXFP8 anywhere): the MXFP8 rounding itself, reported only
+    idx, gt = host(ctx["topk_idx"])[toks], host(ctx["topk_gate"])[toks]
+    _, _, _, Yu = sampled.ffn_forward_rows(np.repeat(x[toks], k, axis=0), idx.ravel(),
+                                           inputs["w_gate"], inputs["w_up"], inputs["w_down"])
+    yu = np.einsum("tk,tkd->td", gt, Yu.reshape(len(toks), k, cfg.d))
+    e = rel_err(_f64(_rows_bits(ctx["y"], toks)), yu)
+    e2 = float(np.linalg.norm(_f64(_rows_bits(ctx["y"], toks)) - yu) / np.linalg.norm(yu))
+    print(f"[MXFP8 vs unquantised float64 layer, not gated] y on {len(toks)} sampled tokens: "
+          f"max-rel-to-norm {e:.4f}, relative L2 {e2:.4f}", flush=True)
     del torch
