@@ -1,39 +1,48 @@
 """Benchmark of the MoE layer step (forward + backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload balanced] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mxfp8] [--experts E]
+                    [--no-flush] [--no-cpu-baseline] [--recompute] [--copy-probe BYTES]
 
-A step is one pass of the whole hot path over one batch of synthetic input: router top-k and
-metadata, permute, the two forward grouped GEMMs, combine, then combine backward, the four
-backward grouped GEMMs, route backward and permute backward.  Inputs are resident in HBM before
-the timed region.  The default workload is the balanced-routing layer (8192 tokens, d 2048,
-64 experts, top-4, SwiGLU d_ff 1024, bf16, round-robin logits), fwd+bwd.
+A step is one pass of the whole hot path over one batch of synthetic input.  The default
+workload is the largest one, the MXFP8 layer: 32768 tokens, d_model 7168, 64 experts, top-4,
+SwiGLU d_ff 2048, every expert product on E4M3 operands with one E8M0 scale per 32 elements
+along its contraction dimension.  Its step is: the expert weights quantised in both contraction
+directions, the router projection, router top-k and metadata, x quantised and permuted, the two
+forward grouped GEMMs (A quantised between them), combine; then the fused combine backward
+(dYexp leaves as MXFP8 row blocks), route and router backward, the four backward grouped GEMMs
+with their operands quantised (row blocks for the dgrads, grouped token blocks for the wgrads)
+and the permute backward.  Inputs are resident in HBM before any timed region.
 
-Prints one JSON line with the throughput (tokens/s), the roofline of the dominant kernel and the
-oracle's throughput on the host cores over a bounded token sample (a baseline only).
+Protocol (events are created before the first warm-up step):
+  1. W warm-up steps.
+  2. Instrumented pass, K steps.  Before each, 1 GiB of scratch is written (cold L2 and
+     last-level cache; --no-flush skips it).  Every call of the step is bracketed with HIP events
+     on the stream it runs on, and so is the whole step.  Gives per-call medians: TFLOP/s of each
+     grouped GEMM (`gemm_ms`, `gemm_tflops`), achieved HBM GB/s of the routing and row calls
+     (`rows_*`) and of the router products and MXFP8 quantisers (`aux_*`) on their algorithmic
+     bytes, and the cold step time (`step_ms_flushed`: median, p10, p90).  It also picks the
+     dominant kernel: the grouped GEMM with the largest median (under MXFP8 the forward down call,
+     which also quantises A, is not a candidate).
+  3. Timed region, K steps back to back (warm: in training the layer's input was just written by
+     the layer before it): an event at every step boundary and a pair around the dominant GEMM.
+     `value` = T K / wall-clock seconds, `ms_per_step` = wall-clock / K, `step_ms` = median, p10,
+     p90 of the per-step event durations; the roofline's duration is the dominant GEMM's mean.
+  4. MXFP8: K more steps without re-quantising the weights (training quantises them once per
+     optimizer step): `ms_per_step_excl_weight_quant` (wall-clock / K).
 
-After the W warm-up steps, untimed steps continue until --settle seconds (default 1) after the
-first one: a fresh process on a fresh box stalls for milliseconds around its first steps and its
-clocks ramp over the next tens of steps.  Then an instrumented pass of K steps brackets every
-call of the step with HIP
-events on the stream it runs on (each grouped-GEMM call is one kernel): its averages give
-`gemm_ms` / `gemm_tflops` and, for the routing and row-movement calls, achieved HBM GB/s on their
-algorithmic bytes (`rows_hbm_gbs`, against the 8000 GB/s peak; `aux_hbm_gbs` likewise for the
-router products and the MXFP8 quantisers where the workload has them), and they pick the dominant
-kernel, the GEMM with the largest average duration (under MXFP8 the forward down call, which
-also quantises A, is not a candidate).  Then the timed region runs K more steps with only the
-dominant kernel bracketed: `value` and `ms_per_step` come from it, and so does the roofline's
-average duration (an event pair around every call costs the step 2-5%).  The dominant GEMM's
-`traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary kept
-in profiles/, and is null when that summary is missing or was taken on other kernel sources.
+`roofline.traffic` and the counter columns (`*_traffic_bytes`, `*_counter_gbs`) come from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the workload under profiles/ (hbm_traffic_<workload>.txt,
+written by `python -m expert_ffn_layer_top_amd.profsum step-traffic` from two runs of this script
+with --copy-probe), per call, and are null for a call whose kernel sources changed since.
 
---copy-probe N runs torch's elementwise negation over an fp32 buffer of N bytes three times
-before the warm-up: the plain copy kernel that calibrates the HBM byte counters.
+`cpu_baseline` times the oracle as it stands on the host cores over a bounded sample of the
+same workload (see cpu_baseline_*), as a baseline only.
 """
 
 import argparse
-import gc
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -45,6 +54,7 @@ METRIC = "MoE-layer fwd+bwd tokens/s/GPU; grouped-GEMM TFLOP/s as % of MFMA peak
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_MXFP8_TFLOPS = 5000.0
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 1 << 30
 
 
 def parse():
@@ -52,15 +62,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="balanced", choices=["tiny", "balanced", "sweep", "skewed", "mxfp8"])
+    ap.add_argument("--workload", default="mxfp8", choices=["tiny", "balanced", "sweep", "skewed", "mxfp8"])
     ap.add_argument("--experts", type=int, default=None, help="expert count for the sweep workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
-                    help="after the warm-up, keep stepping (untimed) until this long after the first step")
-    ap.add_argument("--flush", action="store_true",
-                    help="instrumented pass: write 1 GiB of scratch between steps (cold L2 and last-level cache)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="first run torch's negation over an fp32 buffer of BYTES three times (the "
+                         "plain copy kernel that calibrates the HBM byte counters)")
+    ap.add_argument("--no-flush", action="store_true", help="instrumented pass without the 1 GiB flush")
     ap.add_argument("--recompute", action="store_true",
                     help="per-layer activation recompute: the backward re-runs the gate/up product")
     return ap.parse_args()
@@ -74,154 +82,26 @@ def workload_config(args):
     return cfg
 
 
+def workload_tag(cfg):
+    return cfg.name if cfg.name != "sweep" else f"sweep_E{cfg.E}"
+
+
 def describe(cfg):
     kind = {"roundrobin": "balanced (round-robin) routing", "normal": "random N(0,1) logits",
             "zipf": "Zipf-skewed routing", "router": "router-projected logits"}[cfg.logits]
-    prec = "MXFP8 expert GEMMs" if cfg.mxfp8 else "bf16"
-    return (f"MoE layer {'forward' if cfg.forward_only else 'fwd+bwd'}, {kind}: T={cfg.T}, d_model={cfg.d}, E={cfg.E}, top-{cfg.k}, "
-            f"SwiGLU d_ff={cfg.f}, {prec}, fp32 accumulate, seed {cfg.seed}")
+    prec = ("MXFP8 expert GEMMs (E4M3 + E8M0 per 32 along K), weights re-quantised every step"
+            if cfg.mxfp8 else "bf16")
+    return (f"MoE layer {'forward' if cfg.forward_only else 'fwd+bwd'}, {kind}: T={cfg.T}, d_model={cfg.d}, "
+            f"E={cfg.E}, top-{cfg.k}, SwiGLU d_ff={cfg.f}, {prec}, fp32 accumulate, seed {cfg.seed}")
 
+
+# ------------------------------------------------------------------ algorithmic work
 
 def gemm_flops(cfg):
     """Algorithmic flop of each grouped-GEMM call over the routed rows (n = T k)."""
     ndf = float(cfg.n) * cfg.d * cfg.f
     return {"gate_up": 4 * ndf, "down": 2 * ndf, "dgrad_down": 2 * ndf, "wgrad_down": 2 * ndf,
             "dgrad_gate_up": 4 * ndf, "wgrad_gate_up": 4 * ndf, "recompute": 4 * ndf}
-
-
-def copy_probe(nbytes):
-    import torch
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.neg(src, out=dst)
-    torch.cuda.synchronize()
-    del src, dst
-
-
-def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=False, settle=1.0):
-    import torch
-
-    import synth
-    from expert_ffn_layer_top_amd import layer
-
-    dev = torch.device("cuda:0")
-    if probe_bytes:
-        copy_probe(probe_bytes)
-    inputs = synth.to_torch(synth.make_inputs(cfg), dev)
-    w = layer.Weights(inputs["w_gate"], inputs["w_up"], inputs["w_down"], w_r=inputs.get("w_r"))
-    if cfg.mxfp8:
-        w.quantize_mx()
-    x, dy, logits = inputs["x"], inputs["dy"], inputs.get("logits")
-    calls = layer.GEMM_CALLS if not cfg.forward_only else ("gate_up", "down")
-    if recompute and not cfg.forward_only:
-        calls = calls + (layer.RECOMPUTE_CALL,)
-    rows = layer.ROW_CALLS if not cfg.forward_only else ("route", "permute", "combine")
-    # router products and MXFP8 quantisers, where the workload has them
-    aux = ()
-    if cfg.logits == "router":
-        aux += layer.ROUTER_CALLS if not cfg.forward_only else ("router",)
-    if cfg.mxfp8:
-        aux += ("quant_w",) + (layer.QUANT_CALLS if not cfg.forward_only else ("quant_x",))
-
-    def step(events=None):
-        if cfg.mxfp8:
-            qw = events.get("quant_w") if events else None
-            if qw:
-                qw[0].record()
-            w.quantize_mx()                  # weights are re-quantised every step (both directions)
-            if qw:
-                qw[1].record()
-        ctx = layer.forward(x, w, cfg.k, logits=logits, mxfp8=cfg.mxfp8, events=events, recompute=recompute)
-        if not cfg.forward_only:
-            layer.backward(ctx, w, dy, events=events)
-
-    def pairs(names):
-        return [{c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in names}
-                for _ in range(steps)]
-
-    def mean_ms(evs, c):
-        return sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / len(evs)
-
-    t_first = time.perf_counter()
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    # settle: a fresh process stalls for milliseconds around its first steps and the clocks ramp
-    # over the next tens of steps, which per-kernel events do not see but a short wall-clock
-    # region does; untimed steps until `settle` seconds after the first one
-    settled = 0
-    while time.perf_counter() - t_first < settle:
-        for _ in range(4):
-            step()
-        torch.cuda.synchronize()
-        settled += 4
-    # no collector pauses in the measured passes (a full collection can stall the host for tens of
-    # milliseconds while the GPU drains its queue): collect now, re-enable at the end
-    gc.collect()
-    gc.disable()
-    # instrumented pass: every call bracketed
-    evs = pairs(calls + rows + aux)
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev) if flush else None
-    for i in range(steps):
-        if scratch is not None:
-            scratch.fill_(float(i))          # 1 GiB written: evicts the step's data from L2 and MALL
-        step(evs[i])
-    torch.cuda.synchronize()
-    gemm_ms = {c: mean_ms(evs, c) for c in calls}
-    row_ms = {c: mean_ms(evs, c) for c in rows}
-    aux_ms = {c: mean_ms(evs, c) for c in aux}
-    cand = [c for c in calls if not (cfg.mxfp8 and c == "down") and c != layer.RECOMPUTE_CALL]
-    dom = max(cand, key=lambda c: gemm_ms[c])
-    # timed region: the dominant kernel alone bracketed
-    evd = pairs((dom,))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evd[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gc.enable()
-    return elapsed, gemm_ms, row_ms, aux_ms, dom, mean_ms(evd, dom), settled
-
-
-def traffic_of(cfg, call):
-    """HBM bytes per launch of `call` from its counter summary, if it matches the current sources."""
-    from expert_ffn_layer_top_amd import profsum
-    dtype = "mxfp8" if cfg.mxfp8 else "bf16"
-    tag = cfg.name if cfg.name != "sweep" else f"sweep_E{cfg.E}"
-    path = os.path.join(ROOT, "profiles", f"{call}_{dtype}_{tag}_traffic.txt")
-    t = profsum.read_traffic(path)
-    if (t is None or t.get("source_sha256") != profsum.source_sha256(dtype)
-            or t.get("kernel") != profsum.kernel_name(call, dtype, cfg.d, cfg.f)):
-        return None
-    return float(t["traffic_bytes"])
-
-
-def row_bytes(cfg, call):
-    """Algorithmic HBM bytes of the routing and row-movement calls (each element read or written
-    once; bf16 rows, E4M3 rows + E8M0 scales for the MXFP8 permute, fp32 gates and logits)."""
-    T, d, E, k = float(cfg.T), cfg.d, cfg.E, cfg.k
-    eb = 1 + 1 / 32 if cfg.mxfp8 else 2
-    return {"route": T * (4 * E + 12 * k),
-            "permute": (1 + k) * T * d * eb + 4 * T * k,
-            "combine": (k + 1) * T * d * 2 + 8 * T * k,
-            "combine_bwd": (2 * k + 1) * T * d * 2 + 12 * T * k,
-            "permute_bwd": (k + 1) * T * d * 2 + 4 * T * k,
-            "route_bwd": T * (4 * E + 12 * k)}[call]
-
-
-def aux_bytes(cfg, call):
-    """Algorithmic HBM bytes of the router products and the MXFP8 quantiser calls: each element
-    read or written once (quantisers: 2 B read, 1 + 1/32 B written per element and layout; the
-    grouped token blocks counted over the n routed rows, padding excluded)."""
-    T, d, E, n, f = float(cfg.T), cfg.d, cfg.E, float(cfg.n), cfg.f
-    q = 2 + 1 + 1 / 32
-    return {"router": T * d * 2 + d * E * 4 + T * E * 4,
-            "router_bwd": T * E * 4 * 2 + d * E * 4 * 2 + T * d * 4 + T * d * 2,
-            "quant_w": 3 * E * d * f * (2 + 2 * (1 + 1 / 32)),
-            "quant_x": T * d * q, "quant_dg": n * f * q, "quant_du": n * f * q, "quant_dyT": n * d * q,
-            "quant_aT": n * f * q, "quant_dgT": n * f * q, "quant_duT": n * f * q, "quant_xT": n * d * q}[call]
 
 
 def gemm_bytes(cfg, call):
@@ -239,11 +119,205 @@ def gemm_bytes(cfg, call):
             "wgrad_gate_up": ob * (2 * n * f + n * d) + 2 * 2 * E * f * d}[call]
 
 
-def cpu_baseline(cfg, sample_tokens):
+def row_bytes(cfg, call):
+    """Algorithmic HBM bytes of the routing and row-movement calls: every element they must read
+    or write, once (bf16 rows 2 B; MXFP8 rows 1 B + 1/32 B of scale; fp32 gates, logits and the
+    router's dx term; int32 indices)."""
+    T, d, E, k = float(cfg.T), cfg.d, cfg.E, cfg.k
+    n = T * k
+    mx = 1 + 1 / 32
+    router = cfg.logits == "router"
+    if call == "route":          # logits in; topk_idx, gates, dest, row_token out
+        return T * 4 * E + n * 16
+    if call == "permute":        # x rows (and scales) in, k copies out, dest in
+        return (1 + k) * T * d * (mx if cfg.mxfp8 else 2) + 4 * n
+    if call == "combine":        # yexp rows, gates, dest in; y out
+        return (n + T) * d * 2 + 8 * n
+    if call == "combine_bwd":    # dy, yexp rows, gates, dest in; dyexp (bf16, or MX row blocks + row gates), d_gate out
+        out = n * d * mx + 4 * n if cfg.mxfp8 else n * d * 2
+        return T * d * 2 + n * d * 2 + 8 * n + out + 4 * n
+    if call == "permute_bwd":    # dxp rows, dest (and the router's fp32 dx term) in; dx out
+        return (n + T) * d * 2 + 4 * n + (T * d * 4 if router else 0)
+    if call == "route_bwd":      # gates, idx, d_gate in; d_logits out
+        return T * 4 * E + 12 * n
+    raise KeyError(call)
+
+
+def aux_bytes(cfg, call):
+    """Algorithmic HBM bytes of the router products and the MXFP8 quantiser calls, each element
+    read or written once (quantisers: 2 B read, 1 + 1/32 B written per element; the grouped token
+    blocks write their padded token axis, and a gather through row_token reads each source row
+    once)."""
+    T, d, E, n, f = float(cfg.T), cfg.d, cfg.E, float(cfg.n), cfg.f
+    mx = 1 + 1 / 32
+    P = float(((cfg.n + 32 * cfg.E + 127) // 128) * 128)   # padded token axis of the grouped blocks
+    if call == "router":         # x, w_r in; logits out
+        return T * d * 2 + d * E * 4 + T * E * 4
+    if call == "router_bwd":     # d_logits, w_r, x in; dx term (fp32), dw_r out
+        return T * E * 4 + d * E * 4 + T * d * 2 + T * d * 4 + d * E * 4
+    if call == "quant_w":        # three weights, both layouts from one read
+        return 3 * E * d * f * (2 + 2 * mx)
+    if call == "quant_x":
+        return T * d * (2 + mx)
+    if call in ("quant_dg", "quant_du"):
+        return n * f * (2 + mx)
+    if call == "quant_dyT":      # dy gathered through row_token with the row gates
+        return T * d * 2 + n * 8 + P * d * mx
+    if call == "quant_xT":
+        return T * d * 2 + n * 4 + P * d * mx
+    if call in ("quant_aT", "quant_dgT", "quant_duT"):
+        return n * f * 2 + P * f * mx
+    raise KeyError(call)
+
+
+# ------------------------------------------------------------------ GPU timing
+
+def copy_probe(nbytes):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def pct(v, q):
+    """Percentile q (0..100) of a list, linear interpolation."""
+    s = sorted(v)
+    if len(s) == 1:
+        return s[0]
+    x = (len(s) - 1) * q / 100.0
+    i = int(x)
+    j = min(i + 1, len(s) - 1)
+    return s[i] + (s[j] - s[i]) * (x - i)
+
+
+def dist(v):
+    return {"median": round(statistics.median(v), 4), "p10": round(pct(v, 10), 4), "p90": round(pct(v, 90), 4)}
+
+
+def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=True):
+    import torch
+
+    import synth
+    from expert_ffn_layer_top_amd import layer
+
+    dev = torch.device("cuda:0")
+    if probe_bytes:
+        copy_probe(probe_bytes)
+    inputs = synth.to_torch(synth.make_inputs(cfg), dev)
+    w = layer.Weights(inputs["w_gate"], inputs["w_up"], inputs["w_down"], w_r=inputs.get("w_r"))
+    x, dy, logits = inputs["x"], inputs["dy"], inputs.get("logits")
+    calls = layer.GEMM_CALLS if not cfg.forward_only else ("gate_up", "down")
+    if recompute and not cfg.forward_only:
+        calls = calls + (layer.RECOMPUTE_CALL,)
+    rows = layer.ROW_CALLS if not cfg.forward_only else ("route", "permute", "combine")
+    aux = ()
+    if cfg.logits == "router":
+        aux += layer.ROUTER_CALLS if not cfg.forward_only else ("router",)
+    if cfg.mxfp8:
+        aux += ("quant_w",) + (layer.QUANT_CALLS if not cfg.forward_only else ("quant_x",))
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(events=None, quant_weights=True):
+        if cfg.mxfp8 and quant_weights:
+            qw = events.get("quant_w") if events else None
+            if qw:
+                qw[0].record()
+            w.quantize_mx()                  # the weights in both contraction directions
+            if qw:
+                qw[1].record()
+        elif cfg.mxfp8 and not w.mx:
+            w.quantize_mx()
+        ctx = layer.forward(x, w, cfg.k, logits=logits, mxfp8=cfg.mxfp8, events=events, recompute=recompute)
+        if not cfg.forward_only:
+            layer.backward(ctx, w, dy, events=events)
+
+    # every event of the run exists before the first step
+    names = calls + rows + aux
+    inst = [{c: (ev(), ev()) for c in names + ("step",)} for _ in range(steps)]
+    bounds = [ev() for _ in range(steps + 1)]
+    bounds_nq = [ev() for _ in range(steps + 1)]
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # instrumented pass (cold caches unless --no-flush)
+    for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(float(i))          # 1 GiB written: evicts the step's data from L2 and MALL
+        inst[i]["step"][0].record()
+        step(inst[i])
+        inst[i]["step"][1].record()
+    torch.cuda.synchronize()
+
+    def med(c):
+        return statistics.median(e[c][0].elapsed_time(e[c][1]) for e in inst)
+
+    gemm_ms = {c: med(c) for c in calls}
+    row_ms = {c: med(c) for c in rows}
+    aux_ms = {c: med(c) for c in aux}
+    step_flushed = [e["step"][0].elapsed_time(e["step"][1]) for e in inst]
+    cand = [c for c in calls if not (cfg.mxfp8 and c == "down") and c != layer.RECOMPUTE_CALL]
+    dom = max(cand, key=lambda c: gemm_ms[c])
+    domev = [{dom: (ev(), ev())} for _ in range(steps)]
+    torch.cuda.synchronize()
+
+    # timed region: steps back to back
+    t0 = time.perf_counter()
+    bounds[0].record()
+    for i in range(steps):
+        step(domev[i])
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps)]
+    dom_ms = statistics.mean(e[dom][0].elapsed_time(e[dom][1]) for e in domev)
+
+    res = dict(elapsed=elapsed, gemm_ms=gemm_ms, row_ms=row_ms, aux_ms=aux_ms, dom=dom, dom_ms=dom_ms,
+               step_ms=step_ms, step_flushed=step_flushed)
+    if cfg.mxfp8:
+        # the same steps with the weights quantised once, outside the region
+        t0 = time.perf_counter()
+        bounds_nq[0].record()
+        for i in range(steps):
+            step(quant_weights=False)
+            bounds_nq[i + 1].record()
+        torch.cuda.synchronize()
+        res["elapsed_nq"] = time.perf_counter() - t0
+        res["step_ms_nq"] = [bounds_nq[i].elapsed_time(bounds_nq[i + 1]) for i in range(steps)]
+    return res
+
+
+# ------------------------------------------------------------------ counters and CPU baseline
+
+def step_traffic(cfg):
+    """{call: HBM bytes per call} from the workload's counter summary, for the calls whose kernel
+    sources are unchanged since the counters were taken (others are left out)."""
+    from expert_ffn_layer_top_amd import profsum
+    t = profsum.read_step_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_tag(cfg)}.txt"))
+    if t is None:
+        return {}
+    dtype = "mxfp8" if cfg.mxfp8 else "bf16"
+    return {c: v["traffic_bytes"] for c, v in t.items()
+            if v["source_sha256"] == profsum.files_sha256(profsum.call_sources(c, dtype))}
+
+
+def _blas_threads():
+    import threadpoolctl
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    return max((p.get("num_threads", 1) for p in blas), default=1)
+
+
+def cpu_baseline_bf16(cfg, sample_tokens):
     """The oracle as it stands, on the first `sample_tokens` tokens of the same workload (same
     weights, same routing construction), forward + backward, timed on the host cores."""
     import numpy as np
-    import threadpoolctl
 
     import synth
     from oracle import moe
@@ -259,13 +333,68 @@ def cpu_baseline(cfg, sample_tokens):
         if "w_r" in inputs:
             moe.router_project_bwd(x, inputs["w_r"], bwd["d_logits"])
     secs = time.perf_counter() - t0
-    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
-    threads = max((p.get("num_threads", 1) for p in blas), default=1)
+    threads = _blas_threads()
     assert np.isfinite(fwd["y"]).all()
     return dict(value=s / secs, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"first {s} of {cfg.T} tokens, full expert weights, fwd+bwd, float64 numpy "
                        f"({secs:.1f} s; BLAS threads {threads}, affinity {len(os.sched_getaffinity(0))} cores)")
 
+
+def cpu_baseline_mx(cfg, sample_tokens=1024, sample_rows=128):
+    """The MXFP8 oracle chain (oracle.moe_mx) on a bounded sample, scaled to the whole step.
+
+    Its per-step work has three parts that scale differently, each timed on a sample:
+      per token   router projection and its backward, route and metadata, permute, combine, their
+                  backward, on the first `sample_tokens` tokens (scaled by T / sample);
+      per expert  the MX quantisation of one expert's three weights in both directions (x E);
+      per row     one expert's forward and backward products on `sample_rows` of its rows, with
+                  every activation quantisation (x n / rows)."""
+    import numpy as np
+
+    import synth
+    from oracle import moe, moe_mx, mxfp8
+
+    s = min(sample_tokens, cfg.T)
+    x = synth.gen_x(cfg)[:s]
+    dy = synth.gen_dy(cfg)[:s]
+    w_r = synth.gen_router_weight(cfg)
+    wg, wu, wd = synth.gen_expert_weights(cfg.with_(E=1))      # one expert's shapes, drawn for timing only
+    t0 = time.perf_counter()
+    logits = moe.router_project(x, w_r)
+    idx, gate, _ = moe.route_topk(logits, cfg.k)
+    counts, off, dest, row_token, offp = moe.route_metadata(idx, cfg.E)
+    xq, xs = mxfp8.quantize_rows(x)
+    moe.permute(xq, dest), moe.permute(xs, dest)
+    yexp = np.zeros((s * cfg.k, cfg.d))
+    y = moe.combine(yexp, gate, dest)
+    _, dg = moe.combine_bwd(dy, yexp, gate, dest)
+    dl = moe.route_topk_bwd(gate, idx, dg, cfg.E)
+    add, _ = moe.router_project_bwd(x, w_r, dl)
+    moe.permute_bwd(yexp, dest, addend=add)
+    t_tok = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    qw = moe_mx.quantize_weights(wg, wu, wd)
+    t_w = time.perf_counter() - t0
+    R = sample_rows
+    xr = np.repeat(x, (R + s - 1) // s, axis=0)[:R]
+    dyr = np.repeat(dy, (R + s - 1) // s, axis=0)[:R]
+    t0 = time.perf_counter()
+    rq, rs = mxfp8.quantize_rows(xr)
+    G, U, A, Y = moe_mx.expert_forward(rq, rs, qw, 0)
+    moe_mx.expert_backward(dyr, G, U, A, xr, qw, 0)
+    t_rows = time.perf_counter() - t0
+    step_s = t_tok * cfg.T / s + t_w * cfg.E + t_rows * cfg.n / R
+    threads = _blas_threads()
+    assert np.isfinite(y).all()
+    return dict(value=cfg.T / step_s, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"MXFP8 oracle chain, three timed parts scaled to the whole step: per-token work on the first "
+                        f"{s} of {cfg.T} tokens ({t_tok:.2f} s, x {cfg.T // s}), one expert's weight quantisation "
+                        f"({t_w:.2f} s, x {cfg.E}), one expert's fwd+bwd products on {R} rows ({t_rows:.2f} s, "
+                        f"x {cfg.n // R}); estimated {step_s:.0f} s per step; float64 numpy, BLAS threads {threads}, "
+                        f"affinity {len(os.sched_getaffinity(0))} cores"))
+
+
+# ------------------------------------------------------------------ main
 
 def main():
     args = parse()
@@ -274,25 +403,30 @@ def main():
               file=sys.stderr)
         return 2
     cfg = workload_config(args)
-    elapsed, gemm_ms, row_ms, aux_ms, dom, dom_ms, settled = run_gpu(cfg, args.steps, args.warmup, args.copy_probe,
-                                                                     args.recompute, args.flush, args.settle)
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = cfg.T * args.steps / elapsed
+    r = run_gpu(cfg, args.steps, args.warmup, args.copy_probe, args.recompute, flush=not args.no_flush)
+    K = args.steps
     flops = gemm_flops(cfg)
-    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
+    dom = r["dom"]
+    achieved = flops[dom] / (r["dom_ms"] * 1e-3) / 1e12
     peak = PEAK_MXFP8_TFLOPS if cfg.mxfp8 else PEAK_BF16_TFLOPS
+    traffic = step_traffic(cfg)
     from expert_ffn_layer_top_amd import profsum
     dtype = "mxfp8" if cfg.mxfp8 else "bf16"
+    flushed = not args.no_flush
+
+    def counter_gbs(calls_ms):
+        return {c: round(traffic[c] / (v * 1e-3) / 1e9, 1) for c, v in calls_ms.items() if c in traffic}
+
     out = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": round(cfg.T * K / r["elapsed"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "settle_steps": settled,          # untimed steps after the warm-up (--settle seconds)
-        "instrumented_steps": args.steps,  # untimed pass with every call bracketed
-        "ms_per_step": round(ms_per_step, 4),
+        "instrumented_steps": K,           # untimed pass with every call bracketed
+        "ms_per_step": round(r["elapsed"] * 1e3 / K, 4),
+        "step_ms": dist(r["step_ms"]),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -300,23 +434,32 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(cfg), "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
                    "top_k": cfg.k, "d_ff": cfg.f, "fwd_bwd": not cfg.forward_only,
-                   "activation_recompute": bool(args.recompute), "instrumented_pass_flushed": bool(args.flush)},
+                   "activation_recompute": bool(args.recompute), "instrumented_pass_flushed": flushed},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": traffic_of(cfg, dom),
+                     "frac": round(achieved / peak, 4), "traffic": traffic.get(dom),
                      "kernel": f"{profsum.kernel_name(dom, dtype, cfg.d, cfg.f)} ({dom})",
-                     "avg_ms": round(dom_ms, 4), "flop_per_launch": flops[dom],
+                     "avg_ms": round(r["dom_ms"], 4), "flop_per_launch": flops[dom],
                      "algorithmic_bytes": round(gemm_bytes(cfg, dom))},
-        "gemm_ms": {c: round(v, 4) for c, v in gemm_ms.items()},
-        "gemm_tflops": {c: round(flops[c] / (v * 1e-3) / 1e12, 1) for c, v in gemm_ms.items()},
-        "rows_us": {c: round(v * 1e3, 1) for c, v in row_ms.items()},
-        "rows_hbm_gbs": {c: round(row_bytes(cfg, c) / (v * 1e-3) / 1e9, 1) for c, v in row_ms.items()},
-        "hbm_peak_gbs": HBM_PEAK_GBS,
     }
-    if aux_ms:
-        out["aux_us"] = {c: round(v * 1e3, 1) for c, v in aux_ms.items()}
-        out["aux_hbm_gbs"] = {c: round(aux_bytes(cfg, c) / (v * 1e-3) / 1e9, 1) for c, v in aux_ms.items()}
+    if cfg.mxfp8:
+        out["ms_per_step_excl_weight_quant"] = round(r["elapsed_nq"] * 1e3 / K, 4)
+        out["step_ms_excl_weight_quant"] = dist(r["step_ms_nq"])
+    out["step_ms_flushed"] = dist(r["step_flushed"])
+    out["gemm_ms"] = {c: round(v, 4) for c, v in r["gemm_ms"].items()}
+    out["gemm_tflops"] = {c: round(flops[c] / (v * 1e-3) / 1e12, 1) for c, v in r["gemm_ms"].items()}
+    out["rows_us"] = {c: round(v * 1e3, 1) for c, v in r["row_ms"].items()}
+    out["rows_hbm_gbs"] = {c: round(row_bytes(cfg, c) / (v * 1e-3) / 1e9, 1) for c, v in r["row_ms"].items()}
+    out["rows_counter_gbs"] = counter_gbs(r["row_ms"])
+    if r["aux_ms"]:
+        out["aux_us"] = {c: round(v * 1e3, 1) for c, v in r["aux_ms"].items()}
+        out["aux_hbm_gbs"] = {c: round(aux_bytes(cfg, c) / (v * 1e-3) / 1e9, 1) for c, v in r["aux_ms"].items()}
+        out["aux_counter_gbs"] = counter_gbs(r["aux_ms"])
+    out["counter_bytes_over_algorithmic"] = {
+        c: round(traffic[c] / (row_bytes(cfg, c) if c in r["row_ms"] else aux_bytes(cfg, c)), 3)
+        for c in list(r["row_ms"]) + list(r["aux_ms"]) if c in traffic}
+    out["hbm_peak_gbs"] = HBM_PEAK_GBS
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline_mx(cfg) if cfg.mxfp8 else cpu_baseline_bf16(cfg, 8192)
     print(json.dumps(out), flush=True)
     return 0
 
