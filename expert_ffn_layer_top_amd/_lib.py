@@ -23,6 +23,7 @@ SIGNATURES = {
     "moe_router_project_bwd": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _sz, _p]),
     "moe_route_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_route_topk": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _sz, _p]),
+    "moe_route_topk_noalloc": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p]),
     "moe_route_topk_bwd": (_i, [_p, _p, _p, _i, _i, _i, _p, _p]),
     "moe_route_balance_workspace_bytes": (_sz, [_i, _i]),
     "moe_route_balance": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _sz, _p]),

@@ -18,6 +18,7 @@
 //   route_finalize     dest = offsets[e] + rows of e in earlier blocks + rank in block;
 //                      row_token[dest] = token.
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 
@@ -398,6 +399,35 @@ int enqueue_route(const float* logits, int T, int E, int k, int32_t* topk_idx, f
   return check_launch("route_finalize");
 }
 
+// ---- the no-allocation variant's scratch: the per-block counts in a file-scope device array.
+// Every GPU the library runs on holds its own copy until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device with that device
+// current, and every launch takes that pointer.
+__device__ __align__(256) int32_t scratch[MOE_ROUTE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(MOE_ERR_HIP, "route (no-alloc): hipGetDevice: %s", hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "route (no-alloc): device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_error(MOE_ERR_HIP, "route (no-alloc): hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -413,6 +443,24 @@ extern "C" int moe_route_topk(const float* logits, int T, int E, int k, int32_t*
   MOE_CHECK_ALIGN(ws);
   return enqueue_route(logits, T, E, k, topk_idx, topk_gate, probs, counts, offsets, offsets_pad, pad, dest, row_token,
                        static_cast<int32_t*>(ws), as_stream(stream));
+}
+
+extern "C" int moe_route_topk_noalloc(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                                      float* topk_gate, float* probs, int32_t* counts, int32_t* offsets,
+                                      int32_t* offsets_pad, int pad, int32_t* dest, int32_t* row_token,
+                                      void* stream) {
+  if (int st = check_route_args(logits, T, E, k, topk_idx, topk_gate, probs, counts, offsets, offsets_pad, pad, dest,
+                                row_token))
+    return st;
+  const size_t need = moe_route_workspace_bytes(T, E, k);
+  MOE_REQUIRE(need <= MOE_ROUTE_NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED,
+              "route (no-alloc): T=%d, E=%d needs %zu bytes of scratch, above the built-in %zu "
+              "(ceil(T/64) * E * 4 must not exceed it); use moe_route_topk with a workspace",
+              T, E, need, static_cast<size_t>(MOE_ROUTE_NOALLOC_SCRATCH_BYTES));
+  void* ptr = nullptr;
+  if (int st = scratch_address(&ptr)) return st;
+  return enqueue_route(logits, T, E, k, topk_idx, topk_gate, probs, counts, offsets, offsets_pad, pad, dest, row_token,
+                       static_cast<int32_t*>(ptr), as_stream(stream));
 }
 
 extern "C" int moe_route_topk_bwd(const float* topk_gate, const int32_t* topk_idx, const float* d_gate,

@@ -122,6 +122,22 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, 
                    int32_t* offsets_pad_or_null, int pad, int32_t* dest, int32_t* row_token_or_null,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* moe_route_topk for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments (minus the workspace)
+ * and bit-identical outputs; the per-block expert counts live instead in a fixed scratch array
+ * that the library holds on every GPU it runs on (MOE_ROUTE_NOALLOC_SCRATCH_BYTES per GPU, kept
+ * until the process ends; its device address is looked up on the first call on each device).
+ * The call allocates nothing, clears nothing (every scratch entry it reads it has first written
+ * in the same call) and needs ceil(T/64) * E * 4 <= MOE_ROUTE_NOALLOC_SCRATCH_BYTES (e.g.
+ * T <= 262144 at E = 256), else MOE_ERR_UNSUPPORTED before anything is enqueued.
+ * All calls on one GPU share its scratch: calls that can overlap on the device (other streams,
+ * other host threads) race and give undefined results; serialise them on one stream. */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_route_topk_noalloc(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                           float* topk_gate, float* probs_or_null, int32_t* counts, int32_t* offsets,
+                           int32_t* offsets_pad_or_null, int pad, int32_t* dest,
+                           int32_t* row_token_or_null, void* stream);
+
 /* Backward of the renormalised gates with the selection held fixed ([news] lead paragraphs: the
  * router sends each token to a small selection of experts; training differentiates the gates
  * of that selection, not the discrete choice):

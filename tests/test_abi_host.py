@@ -137,3 +137,15 @@ def test_argument_checks_of_balance_and_fused_producer():
     assert L.mxfp8_quantize_grouped_gated(fake, None, fake, fake, fake, 8, 64, 128, fake, fake, None) == INVALID
     assert L.mxfp8_quantize_grouped_gated(fake, fake, None, fake, fake, 8, 64, 128, fake, fake, None) == INVALID
     assert L.mxfp8_quantize_grouped_gated(fake, fake, fake, fake, fake, 8, 64, 96, fake, fake, None) == UNSUPPORTED
+
+
+def test_noalloc_route_rejects_sizes_beyond_its_scratch():
+    L = _lib.lib
+    fake = ctypes.c_void_p(0x1000)
+    # ceil(T/64) * E * 4 bytes of per-block counts must fit the fixed scratch (4 MiB): T = 262144
+    # at E = 256 fits exactly, one more block does not; rejected before anything is enqueued
+    assert L.moe_route_topk_noalloc(fake, 262144 + 64, 256, 2, *[fake] * 6, 32, fake, None, None) == UNSUPPORTED
+    assert b"scratch" in L.moe_last_error_string()
+    # the route's own argument checks come first
+    assert L.moe_route_topk_noalloc(fake, 0, 8, 2, *[fake] * 6, 32, fake, None, None) == UNSUPPORTED
+    assert L.moe_route_topk_noalloc(None, 64, 8, 2, *[fake] * 6, 32, fake, None, None) == INVALID
