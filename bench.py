@@ -71,6 +71,7 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="instrumented pass without the 1 GiB flush")
     ap.add_argument("--recompute", action="store_true",
                     help="per-layer activation recompute: the backward re-runs the gate/up product")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
     return ap.parse_args()
 
 
@@ -294,6 +295,67 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=True):
     return res
 
 
+# ------------------------------------------------------------------ measured ceilings
+
+def measured_ceilings():
+    """What this GPU sustains on its two bounding resources, from the self-written probes in
+    libmoe_probe.so (expert_ffn_layer_top_amd/probe/ceiling.hip), timed with HIP events on the
+    current stream: MFMA-only loops (bf16 16x16x32 and block-scaled fp8 16x16x128, one and four
+    waves per SIMD) and a 1 GiB streaming copy and read.  Each is run twice; the second run counts."""
+    import ctypes
+
+    import torch
+    from expert_ffn_layer_top_amd import build as _b
+    if not os.path.exists(_b.PROBE_LIB):
+        raise RuntimeError(f"{_b.PROBE_LIB} is missing: build it with `python -m expert_ffn_layer_top_amd.build`")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.probe_mfma_flop.restype = ctypes.c_double
+    lib.probe_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(fn):
+        ms = None
+        for _ in range(2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            st = fn()
+            b.record()
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"probe launch failed ({st})")
+            ms = a.elapsed_time(b)
+        return ms
+
+    out = {}
+    for name, fp8, iters in (("mfma_bf16", 0, 20000), ("mfma_fp8", 1, 10000)):
+        for waves in (1, 4):
+            blocks = cus * waves                      # 4 waves per block: `waves` per SIMD
+            buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+            ms = timed(lambda: lib.probe_mfma(fp8, blocks, iters, ctypes.c_void_p(buf.data_ptr()),
+                                              ctypes.c_void_p(stream)))
+            out[f"{name}_tflops_{waves}w"] = round(lib.probe_mfma_flop(fp8, blocks, iters) / (ms * 1e-3) / 1e12, 1)
+            del buf
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    red = torch.empty(cus * 8, dtype=torch.int32, device=dev)
+    ms = timed(lambda: lib.probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                                      cus * 8, ctypes.c_void_p(stream)))
+    out["hbm_copy_gbs"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    ms = timed(lambda: lib.probe_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(red.data_ptr()),
+                                      cus * 8, ctypes.c_void_p(stream)))
+    out["hbm_read_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del src, dst, red
+    out["probe"] = ("expert_ffn_layer_top_amd/probe/ceiling.hip: MFMA-only loops (16 independent "
+                    "accumulators per wave, register operands), 1 GiB copy (read + write bytes) and read")
+    return out
+
+
 # ------------------------------------------------------------------ counters and CPU baseline
 
 def step_traffic(cfg):
@@ -458,6 +520,11 @@ def main():
         c: round(traffic[c] / (row_bytes(cfg, c) if c in r["row_ms"] else aux_bytes(cfg, c)), 3)
         for c in list(r["row_ms"]) + list(r["aux_ms"]) if c in traffic}
     out["hbm_peak_gbs"] = HBM_PEAK_GBS
+    if not args.no_ceilings:
+        c = measured_ceilings()
+        out["measured_ceilings"] = c
+        mf = c["mfma_fp8_tflops_4w" if cfg.mxfp8 else "mfma_bf16_tflops_4w"]
+        out["roofline"]["frac_of_measured_mfma_ceiling"] = round(achieved / mf, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_mx(cfg) if cfg.mxfp8 else cpu_baseline_bf16(cfg, 8192)
     print(json.dumps(out), flush=True)

@@ -3,8 +3,10 @@
     python -m expert_ffn_layer_top_amd.build [--jobs N] [--verbose]
 
 Each csrc/*.hip is compiled to an object under _build/ (in parallel), then linked into
-expert_ffn_layer_top_amd/libmoe_mi355x.so.  Always recompiles: this is the "does it build"
-step, and it must reflect the sources as they are.
+expert_ffn_layer_top_amd/libmoe_mi355x.so.  The ceiling probes (probe/*.hip: MFMA-only loops and
+streaming copies the benchmark times beside the layer) go into a separate libmoe_probe.so, which
+is not part of the layer's ABI.  Always recompiles: this is the "does it build" step, and it
+must reflect the sources as they are.
 """
 
 import argparse
@@ -16,8 +18,10 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
+PROBE = os.path.join(PKG, "probe")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -40,19 +44,24 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(jobs=8, verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    if not srcs:
-        raise RuntimeError(f"no HIP sources under {CSRC}")
+def _link(srcs, lib, jobs, verbose):
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         futs = [ex.submit(_run, [HIPCC, *CFLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
         for fut in futs:
             fut.result()
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs=8, verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    if not srcs:
+        raise RuntimeError(f"no HIP sources under {CSRC}")
+    _link(srcs, LIB, jobs, verbose)
+    _link(sorted(glob.glob(os.path.join(PROBE, "*.hip"))), PROBE_LIB, jobs, verbose)
     return LIB
 
 
