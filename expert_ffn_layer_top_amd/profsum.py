@@ -356,13 +356,15 @@ def cmd_step_kernels(a):
     print(f"# command: {a.command}")
     print(f"# per-call kernel time (sum of the call's dispatches, end - start) over {len(steps)} complete "
           f"{'flushed ' if flushed else ''}steps, microseconds")
-    print(f"{'call':<14} {'median_us':>10} {'mean_us':>10} {'min_us':>10} {'max_us':>10}  kernels")
+    dtype = "mxfp8" if a.workload.startswith("mxfp8") else "bf16"
+    print(f"{'call':<14} {'median_us':>10} {'mean_us':>10} {'min_us':>10} {'max_us':>10}  source_sha256  kernels")
     total = 0.0
     for call, pats in seq:
         v = [p[call] / 1e3 for p in steps]
         total += statistics.median(v)
         kern = "+".join(b if t is None else f"{b}<{t.rstrip(',')}>" for b, t in pats)
-        print(f"{call:<14} {statistics.median(v):10.1f} {statistics.mean(v):10.1f} {min(v):10.1f} {max(v):10.1f}  {kern}")
+        print(f"{call:<14} {statistics.median(v):10.1f} {statistics.mean(v):10.1f} {min(v):10.1f} {max(v):10.1f}  "
+              f"{files_sha256(call_sources(call, dtype))}  {kern}")
     print(f"{'sum':<14} {total:10.1f}")
 
 
