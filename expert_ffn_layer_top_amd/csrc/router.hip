@@ -251,6 +251,151 @@ __global__ __launch_bounds__(256) void router_gemm(const void* __restrict__ A, c
     }
 }
 
+// ---- forward: logits = x @ w_r, read-bound on x.  A workgroup takes 128 tokens (four waves of
+// 32) x 64 experts.  Per K chunk of 64, the chunk of w_r is split once (hi, mid, lo) into LDS as
+// bf16 [part][expert][k] (double-buffered: chunk c + 1 is split while chunk c's products run);
+// both the w_r chunks and each wave's x fragments (straight from global memory into registers,
+// in the MFMA layout) are loaded FDEPTH chunks ahead, so the token stream keeps enough loads in
+// flight without staging x in LDS.  The
+// products and their order per accumulator (chunks of 64, K halves of 32, then lo, mid, hi) are
+// those of router_gemm, so the logits are the same bits.
+constexpr int FT = 128, FE = 64, FK = 64;
+constexpr int FPITCH = FK + 8;   // bf16 per LDS row (144 bytes: a fragment read spreads over all banks)
+constexpr int FDEPTH = 4;        // x chunks in flight per wave
+
+
+__global__ __launch_bounds__(256) void router_fwd_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w_r,
+                                                         int T, int d, int E, float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[2][3][FE][FPITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * FT + 32 * wave, n0 = blockIdx.y * FE;
+  // chunks, padded to a multiple of FDEPTH: the chunks past d read zeros (their products add
+  // +0), so every load of the loop is unconditional
+  const int nk = ((d + FK - 1) / FK + FDEPTH - 1) / FDEPTH * FDEPTH;
+  // All loads are unconditional buffer loads (a lane outside the matrix gets an offset past the
+  // buffer and reads zero): without branches around them the compiler counts them exactly and
+  // keeps FDEPTH chunks in flight.  x's descriptor starts at the workgroup's first token.
+  constexpr uint32_t OOB = 0x80000000u;
+  const int tw = blockIdx.x * FT;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + static_cast<long long>(tw) * d), 0, min(T - tw, FT) * d * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w_r), 0, static_cast<int>(static_cast<long long>(d) * E * 4),
+                                        0x00020000);
+  // x fragment (row tile i, K half kk) of chunk c: lane row l % 16, K 8 (l / 16) .. + 7.  The
+  // lane's part of the offset is fixed; the chunk's is a scalar offset.  A piece at or past d
+  // reads zero: its offset is pushed past the buffer (the lane part when the piece straddles d's
+  // last 32-wide K block, which only happens when d is not a multiple of 32).
+  uint32_t va[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) va[i] = static_cast<uint32_t>(((32 * wave + 16 * i + (lane & 15)) * d + 8 * (lane >> 4)) * 2);
+  const int klane = 8 * (lane >> 4);
+  auto load_a = [&](int c, bf16x8 (&a)[2][2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kb = c * FK + 32 * kk;
+      const int soff = kb < d ? 2 * kb : 0x40000000;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t v = kb + klane < d ? va[i] : OOB;
+        a[i][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(v), soff, 0));
+      }
+    }
+  };
+  // w_r chunk: thread -> expert n0 + lane, rows k0 + 16 wave .. + 15 (coalesced across lanes);
+  // row validity is uniform (a scalar offset past the buffer), expert validity the lane's
+  const int be = n0 + lane;
+  const uint32_t vb = be < E ? static_cast<uint32_t>((16 * wave * E + be) * 4) : OOB;
+  auto load_b = [&](int c, float (&b)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k = c * FK + 16 * wave + r;
+      const int soff = k < d ? (c * FK + r) * E * 4 : 0x40000000;
+      b[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, static_cast<int>(vb), soff, 0));
+    }
+  };
+  auto store_b = [&](int buf, const float (&b)[16]) {
+    bf16x8 hi[2], mid[2], lo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = b[8 * h + i];
+      split3(v, hi[h], mid[h], lo[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<bf16x8*>(&Bs[buf][0][lane][16 * wave + 8 * h]) = hi[h];
+      *reinterpret_cast<bf16x8*>(&Bs[buf][1][lane][16 * wave + 8 * h]) = mid[h];
+      *reinterpret_cast<bf16x8*>(&Bs[buf][2][lane][16 * wave + 8 * h]) = lo[h];
+    }
+  };
+
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 ar[FDEPTH][2][2];
+  float br[FDEPTH][16];
+#pragma unroll
+  for (int s = 0; s < FDEPTH; ++s) {
+    load_a(s, ar[s]);
+    load_b(s, br[s]);
+  }
+  store_b(0, br[0]);
+  load_b(FDEPTH, br[0]);
+  __syncthreads();
+  // chunk c: its products from Bs[c % 2], and in the same stretch of code (no barrier between,
+  // so the split's VALU work overlaps the matrix cores) the split of chunk c + 1 into the other
+  // buffer, whose last readers finished before the barrier that closed chunk c - 1
+  for (int c0 = 0; c0 < nk; c0 += FDEPTH) {
+#pragma unroll
+    for (int s = 0; s < FDEPTH; ++s) {
+      const int c = c0 + s;
+      {
+        const int buf = c & 1;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 bp[3][4];
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              bp[p][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][p][16 * j + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              f32x4 cc = acc[i][j];
+              cc = mfma(ar[s][i][kk], bp[2][j], cc);
+              cc = mfma(ar[s][i][kk], bp[1][j], cc);
+              cc = mfma(ar[s][i][kk], bp[0][j], cc);
+              acc[i][j] = cc;
+            }
+        }
+        const int sn = (s + 1) % FDEPTH;
+        store_b(buf ^ 1, br[sn]);
+        load_b(c + 1 + FDEPTH, br[sn]);
+        load_a(c + FDEPTH, ar[s]);
+        __syncthreads();
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = n0 + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 16 * i + 4 * (lane >> 4) + r;
+        if (t < T && e < E) logits[static_cast<long long>(t) * E + e] = acc[i][j][r];
+      }
+    }
+}
+
 // out[i] = sum_s part[s][i], s ascending (fixed order)
 __global__ __launch_bounds__(256) void reduce_splits(const float* __restrict__ part, int S, long long count,
                                                      float* __restrict__ out) {
@@ -281,9 +426,11 @@ extern "C" int moe_router_project(const uint16_t* x, const float* w_r, int T, in
   MOE_REQUIRE(T >= 1 && d >= 1 && E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "need T, d >= 1 and 1 <= E <= 256");
   MOE_REQUIRE(d % 8 == 0, MOE_ERR_UNSUPPORTED, "router: d must be a multiple of 8");
   MOE_CHECK_ALIGN(x);
-  dim3 grid((T + TM - 1) / TM, (E + TN - 1) / TN, 1);
-  router_gemm<A_X_KC, B_F_NC><<<grid, 256, 0, as_stream(stream)>>>(x, w_r, T, E, d, d, f32_rows_aligned(E, w_r, w_r),
-                                                                   logits, 0);
+  // the kernel's buffer offsets (a 128-token slice of x, all of w_r) stay below 2^31 bytes
+  MOE_REQUIRE(static_cast<long long>(FT) * d * 2 < 0x7fffffffLL && static_cast<long long>(d) * E * 4 < 0x7fffffffLL,
+              MOE_ERR_UNSUPPORTED, "router: d too large");
+  dim3 grid((T + FT - 1) / FT, (E + FE - 1) / FE, 1);
+  router_fwd_kernel<<<grid, 256, 0, as_stream(stream)>>>(x, w_r, T, d, E, logits);
   return check_launch("router_project");
 }
 
