@@ -396,23 +396,296 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const uint16_t* __restr
     }
 }
 
-// out[i] = sum_s part[s][i], s ascending (fixed order)
-__global__ __launch_bounds__(256) void reduce_splits(const float* __restrict__ part, int S, long long count,
-                                                     float* __restrict__ out) {
-  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= count) return;
-  float s = 0.f;
-  for (int z = 0; z < S; ++z) s += part[z * count + i];
-  out[i] = s;
-}
+// ---- backward.  Both products run on bf16 parts of the fp32 operands, split once per call into
+// the workspace (zero-padded to EP = E rounded up to 64 experts, so every fragment load is a whole
+// 16-byte piece): d_logits -> dl parts [3][T][EP], w_r -> w parts [3][d][EP].
 
-constexpr int kSplitTokens = 1024;   // tokens per split of the dw_r reduction
+constexpr int kSplitTokens = 2048;   // tokens per split of the dw_r reduction
 
 int n_splits(int T) { return (T + kSplitTokens - 1) / kSplitTokens; }
+int padded_experts(int E) { return (E + 63) / 64 * 64; }
 
-// fp32 rows of E elements load as float4 when E is a multiple of 4 and both bases are 16-byte aligned.
-int f32_rows_aligned(int E, const void* p, const void* q) {
-  return E % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && (reinterpret_cast<uintptr_t>(q) & 15u) == 0;
+// Workspace layout (byte offsets): dw_r partials [S][d][EP] fp32, dl parts, w parts.
+struct BwdWs {
+  size_t dls, wps, total;
+  BwdWs(int T, int d, int E) {
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t EP = static_cast<size_t>(padded_experts(E));
+    dls = al(static_cast<size_t>(n_splits(T)) * d * EP * 4);
+    wps = dls + al(3 * static_cast<size_t>(T) * EP * 2);
+    total = wps + al(3 * static_cast<size_t>(d) * EP * 2);
+  }
+};
+
+// rows x E fp32 -> 3 x rows x EP bf16 parts (hi, mid, lo; zero past E).  One thread per output
+// element of a part.
+__global__ __launch_bounds__(256) void split_parts(const float* __restrict__ src, long long rows, int E, int EP,
+                                                   __bf16* __restrict__ dst) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long count = rows * EP;
+  if (i >= count) return;
+  const long long r = i / EP;
+  const int e = static_cast<int>(i - r * EP);
+  const float v = e < E ? src[r * E + e] : 0.f;
+  const __bf16 h = static_cast<__bf16>(v);
+  const float rem = v - static_cast<float>(h);
+  const __bf16 m = static_cast<__bf16>(rem);
+  dst[i] = h;
+  dst[count + i] = m;
+  dst[2 * count + i] = static_cast<__bf16>(rem - static_cast<float>(m));
+}
+
+// dx_router[t][c] = sum_e dl[t][e] w_r[c][e] over the six products of parts whose sum keeps fp32
+// accuracy, smallest first: (mid, mid), (lo, hi), (hi, lo), (mid, hi), (hi, mid), (hi, hi)
+// (dl part, w part).  A workgroup takes 128 channels x 256 tokens (four waves of 128 x 64); per
+// 64-expert chunk the w parts go to LDS (shared by the waves) and each wave's dl fragments come
+// straight from global memory.  The MFMA computes D[channel][token], so each lane ends with 4
+// consecutive channels of one token: one 16-byte store.
+constexpr int XC = 128, XT = 256, XPITCH = 64 + 8;   // bf16 per LDS row (144 bytes)
+constexpr int OPITCH = XC + 4;                        // fp32 per output staging row (528 bytes)
+static_assert(4 * 16 * OPITCH * 4 <= 3 * XC * XPITCH * 2, "output staging fits the w area");
+
+__global__ __launch_bounds__(256, 2) void router_dx_kernel(const __bf16* __restrict__ dlp, const __bf16* __restrict__ wp,
+                                                        int T, int d, int EP, float* __restrict__ dx) {
+  __shared__ __attribute__((aligned(16))) __bf16 Ws[3][XC][XPITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = blockIdx.x * XC, tw = blockIdx.y * XT + 64 * wave;
+  constexpr uint32_t OOB = 0x80000000u;
+  const long long pd = static_cast<long long>(d) * EP, pt = static_cast<long long>(T) * EP;
+  // the workgroup's 128 channel rows of each w part, and the wave's 64 token rows of each dl part
+  const int crows = min(XC, d - c0);
+  const int trows = max(0, min(64, T - tw));
+  __amdgpu_buffer_rsrc_t wr[3], dr[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    wr[q] = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(wp + q * pd + static_cast<long long>(c0) * EP), 0,
+                                              crows * EP * 2, 0x00020000);
+    dr[q] = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dlp + q * pt + static_cast<long long>(max(tw, 0)) * EP),
+                                              0, trows * EP * 2, 0x00020000);
+  }
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // w chunk loads: thread -> channel row tid / 2, experts 32 (tid % 2) .. + 31 of each part
+  const int wrow = tid >> 1, wcol = 32 * (tid & 1);
+  for (int e0 = 0; e0 < EP; e0 += 64) {
+    uint4 wv[3][4];
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        wv[q][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 wr[q], static_cast<int>((wrow * EP + e0 + wcol + 8 * u) * 2), 0, 0));
+    if (e0 > 0) __syncthreads();   // the previous chunk's readers are done
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&Ws[q][wrow][wcol + 8 * u]) = wv[q][u];
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // the wave's dl fragments of this K half: token tile j, part p (lane row l % 16, experts
+      // 8 (l / 16) .. + 7)
+      bf16x8 df[3][4];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * j + (lane & 15);
+          const uint32_t off = r < trows ? static_cast<uint32_t>((r * EP + e0 + 32 * ks + 8 * (lane >> 4)) * 2) : OOB;
+          df[p][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dr[p], static_cast<int>(off), 0, 0));
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bf16x8 wf[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          wf[q] = *reinterpret_cast<const bf16x8*>(&Ws[q][16 * i + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 c = acc[i][j];
+          c = mfma(wf[1], df[1][j], c);   // (mid, mid)
+          c = mfma(wf[0], df[2][j], c);   // (lo, hi)
+          c = mfma(wf[2], df[0][j], c);   // (hi, lo)
+          c = mfma(wf[0], df[1][j], c);   // (mid, hi)
+          c = mfma(wf[1], df[0][j], c);   // (hi, mid)
+          c = mfma(wf[0], df[0][j], c);   // (hi, hi)
+          acc[i][j] = c;
+        }
+      }
+    }
+  }
+  // Output through LDS (the w area, free once every wave is past its products): per round, one
+  // token tile (16 tokens x the wave's 128 channels) goes in as each lane's 4-channel pieces and
+  // comes out as 16-byte pieces of whole 512-byte row spans, 2 rows per store instruction.
+  __syncthreads();
+  float* stg = reinterpret_cast<float*>(&Ws[0][0][0]) + wave * (16 * OPITCH);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<float4*>(stg + (lane & 15) * OPITCH + 16 * i + 4 * (lane >> 4)) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(stg + (2 * u + (lane >> 5)) * OPITCH + 4 * (lane & 31));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = tw + 16 * j + 2 * u + (lane >> 5);
+      const int c = c0 + 4 * (lane & 31);
+      if (t < T && c < d) *reinterpret_cast<float4*>(dx + static_cast<long long>(t) * d + c) = v[u];
+    }
+  }
+}
+
+// dw_r partial of token split z: part[z][c][e] = sum over the split's tokens t of dl[t][e] x[t][c]
+// (x exact in bf16: three products, lo, mid, hi).  A workgroup takes 256 channels x 64 experts
+// (four waves of 64 channels); per step of 32 tokens, the x rows and the dl parts' rows go to
+// LDS in their source layout (token-major), and both MFMA operands come from transposing reads
+// (ds_read_b64_tr_b16: 4 x 4 blocks of 16-bit elements across each group of 16 lanes), the
+// token axis being the contraction.  Loads run one step ahead in registers.  D[expert][channel]
+// per MFMA: each lane ends with 4 consecutive experts of one channel.
+constexpr int WC = 256, WSTEP = 32;
+constexpr int XSP = WC + 16;   // bf16 per x row in LDS (544 bytes)
+constexpr int DSP = 64 + 16;   // bf16 per dl row in LDS (160 bytes)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Two transposing reads (K rows 8 g + 0..3 and 8 g + 4..7 of the lane's column); the caller
+// waits (lgkm_all) before using the halves.
+__device__ __forceinline__ void tr_read(s16x4 (&h)[2], uint32_t a0, uint32_t a1) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(h[0]) : "v"(a0));
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(h[1]) : "v"(a1));
+}
+__device__ __forceinline__ bf16x8 tr_join(const s16x4 (&h)[2]) {
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4, h[0]), __builtin_bit_cast(bf16x4, h[1]), 0, 1, 2, 3, 4, 5, 6,
+                                 7);
+}
+// Waits for this wave's LDS reads and ties the 16 fragments read for a step.
+__device__ __forceinline__ void lgkm_all(s16x4 (&xh)[4][2], s16x4 (&dh)[4][3][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(xh[0][0]), "+v"(xh[0][1]), "+v"(xh[1][0]), "+v"(xh[1][1]), "+v"(xh[2][0]), "+v"(xh[2][1]),
+                 "+v"(xh[3][0]), "+v"(xh[3][1]));
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    asm volatile("" : "+v"(dh[a][0][0]), "+v"(dh[a][0][1]), "+v"(dh[a][1][0]), "+v"(dh[a][1][1]), "+v"(dh[a][2][0]),
+                 "+v"(dh[a][2][1]));
+}
+
+__global__ __launch_bounds__(256) void router_dw_kernel(const uint16_t* __restrict__ x, const __bf16* __restrict__ dlp,
+                                                        int T, int d, int EP, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) __bf16 Xs[2][WSTEP][XSP];
+  __shared__ __attribute__((aligned(16))) __bf16 Ds[2][3][WSTEP][DSP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = blockIdx.x * WC, e0 = blockIdx.y * 64, z = blockIdx.z;
+  const int ts = z * kSplitTokens, te = min(T, ts + kSplitTokens);
+  const int nrows = te - ts;
+  constexpr uint32_t OOB = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + static_cast<long long>(ts) * d), 0, nrows * d * 2, 0x00020000);
+  const long long pt = static_cast<long long>(T) * EP;
+  __amdgpu_buffer_rsrc_t dr[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    dr[p] = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dlp + p * pt + static_cast<long long>(ts) * EP), 0,
+                                              nrows * EP * 2, 0x00020000);
+  // step loads: x row tid / 8, channels 32 (tid % 8) .. + 31 (4 pieces); dl part u: token row
+  // tid / 8, experts 8 (tid % 8) .. + 7
+  const int xrow = tid >> 3, xcol = 32 * (tid & 7);
+  auto load = [&](int step, uint4 (&xv)[4], uint4 (&dv)[3]) {
+    const int r = step * WSTEP + xrow;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + xcol + 8 * u;
+      const uint32_t off = (r < nrows && c < d) ? static_cast<uint32_t>((r * d + c) * 2) : OOB;
+      xv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off), 0, 0));
+    }
+    const int tr = step * WSTEP + xrow;
+    const uint32_t doff = tr < nrows ? static_cast<uint32_t>((tr * EP + e0 + 8 * (tid & 7)) * 2) : OOB;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      dv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(dr[u], static_cast<int>(doff), 0, 0));
+  };
+  auto store = [&](int buf, const uint4 (&xv)[4], const uint4 (&dv)[3]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&Xs[buf][xrow][xcol + 8 * u]) = xv[u];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) *reinterpret_cast<uint4*>(&Ds[buf][u][xrow][8 * (tid & 7)]) = dv[u];
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transposing-read lane addresses: lane (g, i) reads row 8 g + 4 h + i / 4, columns 4 (i % 4)
+  const int g = lane >> 4, i = lane & 15;
+  const uint32_t xs0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)&Xs[0][0][0]));
+  const uint32_t ds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)&Ds[0][0][0][0]));
+  uint32_t xo[2], dof[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * g + 4 * h + (i >> 2), col = 4 * (i & 3);
+    xo[h] = static_cast<uint32_t>((row * XSP + 64 * wave + col) * 2);
+    dof[h] = static_cast<uint32_t>((row * DSP + col) * 2);
+  }
+  const int nsteps = (nrows + WSTEP - 1) / WSTEP;
+  uint4 xv[4], dv[3];
+  load(0, xv, dv);
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    store(buf, xv, dv);
+    if (step + 1 < nsteps) load(step + 1, xv, dv);
+    __syncthreads();
+    const uint32_t xb = xs0 + buf * (WSTEP * XSP * 2), db = ds0 + buf * (3 * WSTEP * DSP * 2);
+    s16x4 xh[4][2], dh[4][3][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tr_read(xh[b], xb + xo[0] + 32 * b, xb + xo[1] + 32 * b);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        tr_read(dh[a][p], db + p * (WSTEP * DSP * 2) + dof[0] + 32 * a, db + p * (WSTEP * DSP * 2) + dof[1] + 32 * a);
+    lgkm_all(xh, dh);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bf16x8 xf = tr_join(xh[b]);
+        f32x4 c = acc[a][b];
+        c = mfma(tr_join(dh[a][2]), xf, c);
+        c = mfma(tr_join(dh[a][1]), xf, c);
+        c = mfma(tr_join(dh[a][0]), xf, c);
+        acc[a][b] = c;
+      }
+    }
+  }
+  // part[z][c][e .. e + 3]
+  float* pz = part + static_cast<long long>(z) * d * EP;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + 64 * wave + 16 * b + (lane & 15);
+      const int e = e0 + 16 * a + 4 * (lane >> 4);
+      if (c < d)
+        *reinterpret_cast<float4*>(pz + static_cast<long long>(c) * EP + e) =
+            make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+    }
+}
+
+// dw_r[c][e] = sum_z part[z][c][e], z ascending (fixed order)
+__global__ __launch_bounds__(256) void reduce_splits(const float* __restrict__ part, int S, int d, int E, int EP,
+                                                     float* __restrict__ dw) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<long long>(d) * E) return;
+  const long long c = i / E;
+  const int e = static_cast<int>(i - c * E);
+  float s = 0.f;
+  for (int z = 0; z < S; ++z) s += part[(static_cast<long long>(z) * d + c) * EP + e];
+  dw[i] = s;
 }
 
 }  // namespace
@@ -436,7 +709,7 @@ extern "C" int moe_router_project(const uint16_t* x, const float* w_r, int T, in
 
 extern "C" size_t moe_router_bwd_workspace_bytes(int T, int d, int E) {
   if (T < 1 || d < 1 || E < 1) return 0;
-  return static_cast<size_t>(n_splits(T)) * d * E * sizeof(float);
+  return BwdWs(T, d, E).total;
 }
 
 extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const float* d_logits, int T, int d,
@@ -446,28 +719,41 @@ extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const
   MOE_REQUIRE(T >= 1 && d >= 1 && E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "need T, d >= 1 and 1 <= E <= 256");
   MOE_REQUIRE(d % 8 == 0, MOE_ERR_UNSUPPORTED, "router: d must be a multiple of 8");
   MOE_CHECK_ALIGN(x);
-  const int vec = f32_rows_aligned(E, w_r, d_logits);
+  if (dx_router == nullptr && dw_r == nullptr) return MOE_OK;
+  const int EP = padded_experts(E);
+  // the kernels' buffer offsets stay below 2^31 bytes
+  MOE_REQUIRE(static_cast<long long>(kSplitTokens) * d * 2 < 0x7fffffffLL &&
+                  static_cast<long long>(XC) * EP * 2 < 0x7fffffffLL,
+              MOE_ERR_UNSUPPORTED, "router: d too large");
+  if (dx_router != nullptr) MOE_CHECK_ALIGN(dx_router);
+  const BwdWs L(T, d, E);
+  MOE_REQUIRE(ws != nullptr && ws_bytes >= L.total, MOE_ERR_WORKSPACE, "router bwd workspace: need %zu bytes", L.total);
+  MOE_CHECK_ALIGN(ws);
   hipStream_t s = as_stream(stream);
-  if (dw_r != nullptr) {
-    const size_t need = moe_router_bwd_workspace_bytes(T, d, E);
-    MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "router bwd workspace: need %zu bytes", need);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  __bf16* dlp = reinterpret_cast<__bf16*>(w8 + L.dls);
+  __bf16* wp = reinterpret_cast<__bf16*>(w8 + L.wps);
+  {
+    const long long n1 = static_cast<long long>(T) * EP;
+    split_parts<<<static_cast<unsigned>((n1 + 255) / 256), 256, 0, s>>>(d_logits, T, E, EP, dlp);
+    if (int st = check_launch("router_project_bwd split dl")) return st;
   }
   if (dx_router != nullptr) {
-    // dx[t, c] = sum_e dl[t, e] * w_r[c, e]
-    dim3 grid((T + TM - 1) / TM, (d + TN - 1) / TN, 1);
-    router_gemm<A_F_KC, B_F_KC><<<grid, 256, 0, s>>>(d_logits, w_r, T, d, E, E, vec, dx_router, 0);
+    const long long n2 = static_cast<long long>(d) * EP;
+    split_parts<<<static_cast<unsigned>((n2 + 255) / 256), 256, 0, s>>>(w_r, d, E, EP, wp);
+    if (int st = check_launch("router_project_bwd split w")) return st;
+    dim3 grid((d + XC - 1) / XC, (T + XT - 1) / XT, 1);
+    router_dx_kernel<<<grid, 256, 0, s>>>(dlp, wp, T, d, EP, dx_router);
     if (int st = check_launch("router_project_bwd dx")) return st;
   }
   if (dw_r != nullptr) {
-    // dw_r[c, e] = sum_t x[t, c] * dl[t, e], split over token chunks
     const int S = n_splits(T);
-    float* part = static_cast<float*>(ws);
-    dim3 grid((d + TM - 1) / TM, (E + TN - 1) / TN, S);
-    router_gemm<A_X_MC, B_F_NC><<<grid, 256, 0, s>>>(x, d_logits, d, E, T, kSplitTokens, vec, part,
-                                                     static_cast<long long>(d) * E);
+    float* part = reinterpret_cast<float*>(w8);
+    dim3 grid((d + WC - 1) / WC, EP / 64, S);
+    router_dw_kernel<<<grid, 256, 0, s>>>(x, dlp, T, d, EP, part);
     if (int st = check_launch("router_project_bwd dw partial")) return st;
     const long long count = static_cast<long long>(d) * E;
-    reduce_splits<<<static_cast<unsigned>((count + 255) / 256), 256, 0, s>>>(part, S, count, dw_r);
+    reduce_splits<<<static_cast<unsigned>((count + 255) / 256), 256, 0, s>>>(part, S, d, E, EP, dw_r);
     if (int st = check_launch("router_project_bwd dw reduce")) return st;
   }
   return MOE_OK;

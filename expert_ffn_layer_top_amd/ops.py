@@ -93,7 +93,7 @@ def router_project_bwd(x, w_r, d_logits, want_dx=True, want_dw=True):
     _on_gpu(x, w_r, d_logits)
     dx = _empty((T, d), torch.float32, x) if want_dx else None
     dw = _empty((d, E), torch.float32, x) if want_dw else None
-    nbytes = lib.moe_router_bwd_workspace_bytes(T, d, E) if want_dw else 0
+    nbytes = lib.moe_router_bwd_workspace_bytes(T, d, E) if (want_dx or want_dw) else 0
     ws = _empty((max(nbytes, 1),), torch.uint8, x)
     call("moe_router_project_bwd", _ptr(x), _ptr(w_r), _ptr(d_logits), T, d, E, _ptr(dx), _ptr(dw),
          _ptr(ws), nbytes, _stream(x))

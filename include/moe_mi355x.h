@@ -89,15 +89,19 @@ const char* moe_last_error_string(void);
 int moe_router_project(const uint16_t* x, const float* w_r, int T, int d, int E, float* logits,
                        void* stream);
 
-/* Workspace for moe_router_project_bwd (the split-K partial sums of dw_r). */
+/* Workspace for moe_router_project_bwd: the three bf16 parts of d_logits and of w_r (expert axis
+ * zero-padded to a multiple of 64) and the split-K partial sums of dw_r. */
 size_t moe_router_bwd_workspace_bytes(int T, int d, int E);
 
 /* Backward of moe_router_project ([news] lead paragraphs: the stack trains the model, router
  * included, so the projection that scores the experts has a gradient):
- * dx_router[T,d] = d_logits @ w_r^T (fp32),
- * dw_r[d,E] = x^T @ d_logits (fp32; summed over token chunks in a fixed order, so repeated calls
- * give identical bits).  Either output may be NULL to skip it; ws (>= moe_router_bwd_workspace_bytes)
- * is needed only for dw_r.  Same arithmetic and argument limits as moe_router_project. */
+ * dx_router[T,d] = d_logits @ w_r^T (fp32: the six products of the operands' bf16 parts that keep
+ *                  fp32 accuracy),
+ * dw_r[d,E] = x^T @ d_logits (fp32: x exact times the three parts of d_logits; summed over
+ *             2048-token chunks in a fixed order, so repeated calls give identical bits).
+ * Either output may be NULL to skip it; ws (>= moe_router_bwd_workspace_bytes) is needed whenever
+ * one is requested (MOE_ERR_WORKSPACE otherwise); dx_router must be 16-byte aligned.  Argument
+ * limits as moe_router_project. */
 int moe_router_project_bwd(const uint16_t* x, const float* w_r, const float* d_logits, int T, int d,
                            int E, float* dx_router_or_null, float* dw_r_or_null, void* ws,
                            size_t ws_bytes, void* stream);

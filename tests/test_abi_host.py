@@ -58,7 +58,12 @@ def test_workspace_sizes_from_host_scalars():
     assert mx > 131072 * (7168 + 2 * 2048)                                    # monotone, covers the row operands
     assert L.moe_gg_workspace_bytes(1, 64, 131072, 7168, 2048) <= L.moe_gg_workspace_bytes(1, 64, 131072 * 2, 7168, 2048)
     assert L.moe_mx_pad_cap(512, 8) == 768 and L.moe_mx_pad_cap(100, 1) == 256
-    assert L.moe_router_bwd_workspace_bytes(32768, 7168, 64) == 32 * 7168 * 64 * 4
+    # dw_r partials over 2048-token splits, then the bf16 parts of d_logits and of w_r (experts
+    # padded to 64), each region 256-byte aligned
+    al = lambda b: (b + 255) // 256 * 256
+    for T, d, E in ((32768, 7168, 64), (1000, 136, 5), (70, 64, 256)):
+        S, EP = -(-T // 2048), -(-E // 64) * 64
+        assert L.moe_router_bwd_workspace_bytes(T, d, E) == al(S * d * EP * 4) + al(3 * T * EP * 2) + al(3 * d * EP * 2)
 
 
 def test_argument_checks_return_status_without_launching():
@@ -111,10 +116,13 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_router_project(fake, fake, 64, 12, 8, fake, None) == UNSUPPORTED
     assert L.moe_router_project(ctypes.c_void_p(0x1008), fake, 64, 128, 8, fake, None) == INVALID
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 12, 8, fake, None, None, 0, None) == UNSUPPORTED
-    # router backward: dw_r requested without workspace
+    # router backward: either output requested without workspace
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, fake, None, 0, None) == WORKSPACE
     msg = L.moe_last_error_string().decode()
     assert "workspace" in msg
+    assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, fake, None, None, 0, None) == WORKSPACE
+    # nothing requested: nothing to do
+    assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, None, None, 0, None) == 0
 
 
 def test_argument_checks_of_balance_and_fused_producer():
