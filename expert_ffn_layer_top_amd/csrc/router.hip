@@ -14,11 +14,10 @@
 //   x (bf16, exact) times an fp32 operand:  x*hi + x*mid + x*lo                 (3 products)
 //   fp32 times fp32:  hi*hi + hi*mid + mid*hi + hi*lo + lo*hi + mid*mid  (6; the rest are below
 //                     2^-24 of the product)
-// Tiles: 64 x 64 outputs per 256-thread workgroup (four waves of 32 x 32 = 2 x 2 MFMA tiles), K
-// chunks of 64 staged in LDS as fp32 with K contiguous for both operands; the next chunk's global
-// loads are issued before the current chunk's products.  MFMA lane layout (as in the grouped
-// GEMMs): an operand lane l holds row (or column) l % 16 and K elements 8 (l / 16) .. + 7; the
-// result lane l holds column l % 16 and rows 4 (l / 16) .. + 3.
+// MFMA lane layout (as in the grouped GEMMs): an operand lane l holds row (or column) l % 16 and
+// K elements 8 (l / 16) .. + 7; the result lane l holds column l % 16 and rows 4 (l / 16) .. + 3.
+// Kernels: router_fwd_kernel (forward); split_parts, router_dx_kernel, router_dw_kernel and
+// reduce_splits (backward), each described where it is defined.
 #include "common.h"
 
 namespace moe {
@@ -26,128 +25,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int TM = 64, TN = 64, TK = 64;
-constexpr int LDK = TK + 4;   // LDS row pitch (floats): rows of a fragment read fall on distinct banks
-
-// Operand sources.  A is [M][K]; B is [K][N].
-enum Src {
-  A_X_KC = 0,    // A = x [M=T][K=d] bf16, K contiguous              (forward)
-  A_F_KC = 1,    // A = d_logits [M=T][K=E] fp32, K contiguous       (dx)
-  A_X_MC = 2,    // A[m][k] = x[k][m], x [K=T][M=d] bf16             (dw)
-  B_F_NC = 3,    // B = [K][N] fp32, N contiguous (w_r for forward, d_logits for dw)
-  B_F_KC = 4,    // B[k][n] = w_r[n][k], w_r [N=d][K=E] fp32          (dx)
-};
-
-// NE consecutive elements (row, col .. col + NE - 1) of a row-major matrix with `pitch` elements
-// per row; elements of rows at or past row_lim or columns at or past col_lim read 0.  One vector
-// load when the piece is whole and `vec` says fp32 rows are 16-byte aligned.
-template <int NE, bool BF16>
-__device__ __forceinline__ void piece(const void* __restrict__ base, long long pitch, int row, int row_lim, int col,
-                                      int col_lim, bool vec, float* v) {
-  if (row >= row_lim) {
-#pragma unroll
-    for (int i = 0; i < NE; ++i) v[i] = 0.f;
-    return;
-  }
-  const long long off = static_cast<long long>(row) * pitch + col;
-  if constexpr (BF16) {
-    static_assert(NE == 8, "bf16 pieces are 16 bytes");
-    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
-    if (col + 8 <= col_lim) {
-      const uint4 t = *reinterpret_cast<const uint4*>(p);
-      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = col + i < col_lim ? bf16_to_f32(p[i]) : 0.f;
-    }
-  } else {
-    static_assert(NE == 4, "fp32 pieces are 16 bytes");
-    const float* p = static_cast<const float*>(base) + off;
-    if (vec && col + 4 <= col_lim) {
-      const float4 t = *reinterpret_cast<const float4*>(p);
-      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = col + i < col_lim ? p[i] : 0.f;
-    }
-  }
-}
-
-// One workgroup's share of a chunk: 16 values per thread for each operand (64 x 64 = 4096).
-struct Chunk {
-  float a[16], b[16];
-};
-
-// Piece p of a chunk: bf16 sources in 8-element pieces (8 per 64-element row), fp32 sources in
-// 4-element pieces (16 per row); "row" is the source's row (m, or k for x^T), "col" its
-// contiguous index.
-template <int SA>
-__device__ __forceinline__ void load_a(const void* __restrict__ A, int M, int K, int k_hi, int m0, int k0, int tid,
-                                       bool vec, float (&a)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (SA == A_X_KC) {          // x [T][d]: row m, col k
-      if (i < 2) {
-        const int p = tid + 256 * i;
-        piece<8, true>(A, K, m0 + (p >> 3), M, k0 + (p & 7) * 8, k_hi, vec, a + 8 * i);
-      }
-    } else if constexpr (SA == A_X_MC) {   // x [T][d]: row k, col m
-      if (i < 2) {
-        const int p = tid + 256 * i;
-        piece<8, true>(A, M, k0 + (p >> 3), k_hi, m0 + (p & 7) * 8, M, vec, a + 8 * i);
-      }
-    } else {                               // d_logits [T][E]: row m, col k
-      const int p = tid + 256 * i;
-      piece<4, false>(A, K, m0 + (p >> 4), M, k0 + (p & 15) * 4, k_hi, vec, a + 4 * i);
-    }
-  }
-}
-
-template <int SB>
-__device__ __forceinline__ void load_b(const float* __restrict__ B, int N, int K, int k_hi, int n0, int k0, int tid,
-                                       bool vec, float (&b)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = tid + 256 * i;
-    if constexpr (SB == B_F_NC) piece<4, false>(B, N, k0 + (p >> 4), k_hi, n0 + (p & 15) * 4, N, vec, b + 4 * i);
-    else piece<4, false>(B, K, n0 + (p >> 4), N, k0 + (p & 15) * 4, k_hi, vec, b + 4 * i);   // w_r [d][E]
-  }
-}
-
-// Chunk registers -> LDS, both operands as [row][k] fp32.
-template <int SA, int SB>
-__device__ __forceinline__ void store_chunk(const Chunk& ch, float (*As)[LDK], float (*Bs)[LDK], int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = tid + 256 * i;
-    if constexpr (SA == A_X_KC) {
-      if (i < 2) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) As[p >> 3][(p & 7) * 8 + j] = ch.a[8 * i + j];
-      }
-    } else if constexpr (SA == A_X_MC) {
-      if (i < 2) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) As[(p & 7) * 8 + j][p >> 3] = ch.a[8 * i + j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) As[p >> 4][(p & 15) * 4 + j] = ch.a[4 * i + j];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = tid + 256 * i;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (SB == B_F_NC) Bs[(p & 15) * 4 + j][p >> 4] = ch.b[4 * i + j];
-      else Bs[p >> 4][(p & 15) * 4 + j] = ch.b[4 * i + j];
-    }
-  }
-}
 
 // v = hi + mid + lo exactly (see the file comment).
 __device__ __forceinline__ void split3(const float (&v)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
@@ -162,93 +39,8 @@ __device__ __forceinline__ void split3(const float (&v)[8], bf16x8& hi, bf16x8& 
   }
 }
 
-__device__ __forceinline__ void frag(const float (*S)[LDK], int row, int k, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(&S[row][k]);
-  const float4 b = *reinterpret_cast<const float4*>(&S[row][k + 4]);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// C[M][N] (row pitch N; + blockIdx.z * c_split for split-K partials) over K range
-// [blockIdx.z * k_chunk, + k_chunk).  `vec`: fp32 rows are 16-byte aligned (their length is a
-// multiple of 4), so fp32 pieces load as float4.
-template <int SA, int SB>
-__global__ __launch_bounds__(256) void router_gemm(const void* __restrict__ A, const float* __restrict__ B, int M,
-                                                   int N, int K, int k_chunk, int vec, float* __restrict__ C,
-                                                   long long c_split) {
-  constexpr bool A_EXACT = SA != A_F_KC;   // bf16 source: one part
-  __shared__ __attribute__((aligned(16))) float As[TM][LDK];
-  __shared__ __attribute__((aligned(16))) float Bs[TN][LDK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
-  const int k_lo = blockIdx.z * k_chunk;
-  const int k_hi = min(K, k_lo + k_chunk);   // loads past k_hi read zero
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  Chunk ch;
-  auto fetch = [&](int k0) {
-    load_a<SA>(A, M, K, k_hi, m0, k0, tid, vec, ch.a);
-    load_b<SB>(B, N, K, k_hi, n0, k0, tid, vec, ch.b);
-  };
-  fetch(k_lo);
-  for (int k0 = k_lo; k0 < k_hi; k0 += TK) {
-    __syncthreads();
-    store_chunk<SA, SB>(ch, As, Bs, tid);
-    __syncthreads();
-    if (k0 + TK < k_hi) fetch(k0 + TK);
-#pragma unroll
-    for (int kk = 0; kk < TK; kk += 32) {
-      const int kf = kk + 8 * (lane >> 4);
-      bf16x8 ah[2], am[2], al[2], bh[2], bm[2], bl[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float v[8];
-        frag(As, 32 * wm + 16 * t + (lane & 15), kf, v);
-        split3(v, ah[t], am[t], al[t]);
-        frag(Bs, 32 * wn + 16 * t + (lane & 15), kf, v);
-        split3(v, bh[t], bm[t], bl[t]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          f32x4 c = acc[i][j];
-          if constexpr (A_EXACT) {
-            c = mfma(ah[i], bl[j], c);
-            c = mfma(ah[i], bm[j], c);
-            c = mfma(ah[i], bh[j], c);
-          } else {
-            c = mfma(am[i], bm[j], c);
-            c = mfma(al[i], bh[j], c);
-            c = mfma(ah[i], bl[j], c);
-            c = mfma(am[i], bh[j], c);
-            c = mfma(ah[i], bm[j], c);
-            c = mfma(ah[i], bh[j], c);
-          }
-          acc[i][j] = c;
-        }
-    }
-  }
-  float* Cz = C + blockIdx.z * c_split;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + 32 * wn + 16 * j + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 32 * wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < M && n < N) Cz[static_cast<long long>(m) * N + n] = acc[i][j][r];
-      }
-    }
 }
 
 // ---- forward: logits = x @ w_r, read-bound on x.  A workgroup takes 128 tokens (four waves of
@@ -256,9 +48,8 @@ __global__ __launch_bounds__(256) void router_gemm(const void* __restrict__ A, c
 // bf16 [part][expert][k] (double-buffered: chunk c + 1 is split while chunk c's products run);
 // both the w_r chunks and each wave's x fragments (straight from global memory into registers,
 // in the MFMA layout) are loaded FDEPTH chunks ahead, so the token stream keeps enough loads in
-// flight without staging x in LDS.  The
-// products and their order per accumulator (chunks of 64, K halves of 32, then lo, mid, hi) are
-// those of router_gemm, so the logits are the same bits.
+// flight without staging x in LDS.  Per accumulator the products run in a fixed order (chunks of
+// 64, K halves of 32, then lo, mid, hi).
 constexpr int FT = 128, FE = 64, FK = 64;
 constexpr int FPITCH = FK + 8;   // bf16 per LDS row (144 bytes: a fragment read spreads over all banks)
 constexpr int FDEPTH = 4;        // x chunks in flight per wave

@@ -92,7 +92,7 @@ def step_sequence(mxfp8, router, forward_only=False):
     if mxfp8:
         seq.append(("quant_w", [("quant_both_kernel", None)] * 3))
     if router:
-        seq.append(("router", [("router_gemm", None)]))
+        seq.append(("router", [("router_fwd_kernel", None)]))
     seq.append(("route", [("route_topk_local", None), ("route_scan", None), ("route_finalize", None)]))
     if mxfp8:
         seq += [("quant_x", [("quant_rows_kernel", None)]), ("permute", [("permute_kernel", None)]),
@@ -105,7 +105,8 @@ def step_sequence(mxfp8, router, forward_only=False):
     seq.append(("combine_bwd", [("combine_bwd_mx_kernel" if mxfp8 else "combine_bwd_kernel", None)]))
     seq.append(("route_bwd", [("route_topk_bwd_kernel", None)]))
     if router:
-        seq.append(("router_bwd", [("router_gemm", None), ("router_gemm", None), ("reduce_splits", None)]))
+        seq.append(("router_bwd", [("split_parts", None), ("split_parts", None), ("router_dx_kernel", None),
+                                   ("router_dw_kernel", None), ("reduce_splits", None)]))
     if mxfp8:
         qg = ("quant_grouped_kernel", None)
         seq += [("dgrad_down", [g(2)]), ("quant_dyT", [qg]), ("quant_aT", [qg]), ("wgrad_down", [g(4)]),
