@@ -35,39 +35,25 @@ __device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits, int mode = 0) {
   return s;
 }
 
-// bf16 value `b` divided by 2^shared, as a signed fp32 with its magnitude clamped to 448 (the
-// largest E4M3 value: larger magnitudes saturate).  Exact wherever the E4M3 code depends on it.
+// bf16 value `b` divided by 2^shared, as a signed fp32 clamped to [-448, 448] (the largest E4M3
+// magnitude: larger ones saturate).  The bf16 bits in the top half of a word are the fp32 value
+// exactly (subnormals included), and 2^-shared is a normal fp32 (a bf16 amax puts shared in
+// [-127, 120]), so the product is exact whenever it is at least 2^-126; a smaller one (rounded,
+// possibly to a signed zero) is far below half the smallest E4M3 subnormal, 2^-10, and encodes as
+// a zero of its sign either way.  Needs fp32 denormals preserved (the compiler's default here).
 __device__ __forceinline__ float mx_scaled(uint32_t b, int shared) {
-  const uint32_t mag = b & 0x7fffu;
-  float a;
-  if ((mag >> 7) != 0) {
-    // normal bf16: scale by 2^-shared (a normal fp32 power of two); exact unless the result
-    // is below 2^-126, where the E4M3 code is a signed zero either way
-    a = __uint_as_float(mag << 16) * __uint_as_float(static_cast<uint32_t>(127 - shared) << 23);
-  } else {
-    // bf16 subnormal m * 2^-133: build m * 2^(-133 - shared) without touching fp32 denormals
-    const int ex = -133 - shared;
-    a = (ex < -126) ? 0.f : static_cast<float>(mag) * __uint_as_float(static_cast<uint32_t>(ex + 127) << 23);
-  }
-  a = fminf(a, 448.0f);
-  return __uint_as_float(__float_as_uint(a) | ((b & 0x8000u) << 16));
+  const float a = __uint_as_float(b << 16) * __uint_as_float(static_cast<uint32_t>(127 - shared) << 23);
+  return __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
 }
 
-// E4M3 codes of two values from mx_scaled, in bytes 0 and 1: the hardware conversion to the
-// OCP E4M3 format, rounding to nearest even (|a| <= 448, so nothing overflows; values below the
-// smallest subnormal round to a zero of their sign).
-__device__ __forceinline__ uint32_t e4m3x2(float a0, float a1) {
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false)) & 0xffffu;
-}
-
-// E4M3 codes of bf16 values b0, b1 divided by 2^shared (round-to-nearest-even, saturating).
-__device__ __forceinline__ uint32_t mx_encode2(uint32_t b0, uint32_t b1, int shared) {
-  return e4m3x2(mx_scaled(b0, shared), mx_scaled(b1, shared));
-}
-
-// Four codes in one word (bytes 0..3 from b0..b3).
+// E4M3 codes of bf16 values b0..b3 divided by 2^shared, in bytes 0..3 of one word: the hardware
+// conversion to the OCP E4M3 format, rounding to nearest even (inputs are within +-448, so
+// nothing overflows; values below the smallest subnormal give a zero of their sign).  The second
+// conversion writes the high half of the first one's result.
 __device__ __forceinline__ uint32_t mx_encode4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3, int shared) {
-  return mx_encode2(b0, b1, shared) | (mx_encode2(b2, b3, shared) << 16);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(b0, shared), mx_scaled(b1, shared), 0, false);
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(b2, shared), mx_scaled(b3, shared), lo, true));
 }
 
 }  // namespace moe

@@ -37,8 +37,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, 64)));
   if (!live) return;
   const int sh = mx_shared_exp(amax, mode);
-  const uint32_t o0 = mx_encode2(w[0] & 0xffffu, w[0] >> 16, sh) | (mx_encode2(w[1] & 0xffffu, w[1] >> 16, sh) << 16);
-  const uint32_t o1 = mx_encode2(w[2] & 0xffffu, w[2] >> 16, sh) | (mx_encode2(w[3] & 0xffffu, w[3] >> 16, sh) << 16);
+  const uint32_t o0 = mx_encode4(w[0] & 0xffffu, w[0] >> 16, w[1] & 0xffffu, w[1] >> 16, sh);
+  const uint32_t o1 = mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh);
   *reinterpret_cast<uint2*>(q + e0) = make_uint2(o0, o1);
   if ((threadIdx.x & 3) == 0) scale[e0 / 32] = static_cast<uint8_t>(sh + 127);
 }

@@ -88,7 +88,7 @@ def test_cols_transposed(B, R, C, scale_mode):
     assert np.array_equal(host(s), rs) and np.array_equal(host(q), rq)
 
 
-@pytest.mark.parametrize("B,R,C", [(1, 32, 64), (1, 288, 192), (3, 256, 128), (2, 160, 320), (4, 2048, 1024),
+@pytest.mark.parametrize("B,R,C", [(1, 32, 64), (1, 288, 192), (3, 256, 128), (2, 160, 320), (5, 96, 320), (4, 2048, 1024),
                                    (1, 7168, 2048)])
 def test_rows_and_cols_from_one_read(B, R, C):
     """The two-layout quantiser (used for the weights) against the oracle in both layouts, on
