@@ -301,7 +301,9 @@ def measured_ceilings():
     """What this GPU sustains on its two bounding resources, from the self-written probes in
     libmoe_probe.so (expert_ffn_layer_top_amd/probe/ceiling.hip), timed with HIP events on the
     current stream: MFMA-only loops (bf16 16x16x32 and block-scaled fp8 16x16x128, one and four
-    waves per SIMD) and a 1 GiB streaming copy and read.  Each is run twice; the second run counts."""
+    waves per SIMD), a 1 GiB streaming copy and read, and the grouped GEMMs' LDS-DMA operand stream
+    without the MFMAs (L2-resident panels; panels from HBM in the products' tile cells), with the
+    GEMM rate that stream alone allows.  Each is run twice; the second run counts."""
     import ctypes
 
     import torch
@@ -351,8 +353,30 @@ def measured_ceilings():
                                       cus * 8, ctypes.c_void_p(stream)))
     out["hbm_read_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     del src, dst, red
+    # the grouped GEMMs' operand stream alone (LDS-DMA, 256-row panels, 128-byte K steps), on
+    # L2-resident panels and on panels arriving from HBM in the products' 8 x 4 cells; a 256 x 256
+    # tile does 256 * 256 * 2 * K flops per 512 * K-step bytes: 256 flop per streamed byte in fp8
+    # (K = 128 per step), 128 in bf16 (K = 64)
+    lib.probe_dma_bytes.restype = ctypes.c_double
+    lib.probe_dma_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.probe_dma_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    kbytes, rounds, pbytes = 7168, 4, 512 << 20
+    npanels = pbytes // (256 * kbytes)
+    pa = torch.ones(pbytes, dtype=torch.uint8, device=dev)
+    pb = torch.ones(pbytes, dtype=torch.uint8, device=dev)
+    for name, shared in (("lds_dma_l2_gbs", 1), ("lds_dma_hbm_cells_gbs", 0)):
+        ms = timed(lambda: lib.probe_dma_stream(ctypes.c_void_p(pa.data_ptr()), ctypes.c_void_p(pb.data_ptr()), kbytes,
+                                                npanels, rounds, shared, cus, ctypes.c_void_p(stream)))
+        out[name] = round(lib.probe_dma_bytes(cus, kbytes, rounds) / (ms * 1e-3) / 1e9, 1)
+    del pa, pb
+    out["gemm_stream_bound_tflops"] = {"mxfp8": round(out["lds_dma_hbm_cells_gbs"] * 0.256, 1),
+                                       "bf16": round(out["lds_dma_hbm_cells_gbs"] * 0.128, 1)}
     out["probe"] = ("expert_ffn_layer_top_amd/probe/ceiling.hip: MFMA-only loops (16 independent "
-                    "accumulators per wave, register operands), 1 GiB copy (read + write bytes) and read")
+                    "accumulators per wave, register operands), 1 GiB copy (read + write bytes) and read, "
+                    "LDS-DMA operand stream of 256-row panels (shared: L2-resident; cells: 8 x 4 panels per "
+                    "XCD per round from 512 MiB buffers); gemm_stream_bound_tflops = the cells rate times the "
+                    "flops a 256 x 256 tile does per streamed byte")
     return out
 
 

@@ -10,6 +10,14 @@
 //                     operands, unit scales): the MXFP8 grouped GEMMs' instruction.
 //   probe_copy        HBM copy: 16 bytes per lane read and written, grid-stride over the buffer.
 //   probe_read        HBM read: 16 bytes per lane read and summed; one word per block written.
+//   probe_dma_stream  the grouped GEMMs' operand stream alone: one workgroup per compute unit
+//                     moves 256-row A and B panels into LDS with LDS-DMA buffer loads (16 bytes
+//                     per lane, 8 rows x 128 bytes per instruction), 128 bytes of every row per K
+//                     step, two 64 KiB stages, one barrier per step; no MFMAs, nothing read back.
+//                     Shared mode: every workgroup streams the same two panels (L2-resident after
+//                     the first pass).  Fresh mode: the 32 workgroups of an XCD form a cell of 8
+//                     A panels x 4 B panels, a new cell per round, drawn from buffers larger than
+//                     the last-level cache (the products' tile order, on data arriving from HBM).
 // Each result is written so the compiler keeps the work; the host times the launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -92,6 +100,37 @@ __global__ __launch_bounds__(256) void mfma_fp8_loop(int iters, float* __restric
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kStage = 65536;    // one K step of both panels: 2 x 256 rows x 128 bytes
+
+__global__ __launch_bounds__(256, 1) void dma_stream_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                            int kbytes, int rounds, int npanels, int shared) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int row = 128 * (wave & 1) + (lane >> 3);          // first row of this lane, 8 rows per load
+  const int voff = row * kbytes + 16 * (lane & 7);
+  const int steps = kbytes / 128;
+  int g = 0;
+  for (int r = 0; r < rounds; ++r) {
+    const int pa = shared ? 0 : ((xcd * rounds + r) * 8 + (j & 7)) % npanels;
+    const int pb = shared ? 0 : ((xcd * rounds + r) * 4 + (j >> 3)) % npanels;
+    const uint8_t* base = wave < 2 ? b + static_cast<long long>(pb) * 256 * kbytes
+                                   : a + static_cast<long long>(pa) * 256 * kbytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, 256 * kbytes, 0x00020000);
+    for (int k = 0; k < steps; ++k, ++g) {
+      uint8_t* dst = ring + kStage * (g & 1) + 16384 * wave;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 1024 * i), 16, voff + 8 * i * kbytes, 128 * k, 0, 0);
+      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");   // the previous step has landed
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                    long long n16) {
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
@@ -147,5 +186,23 @@ extern "C" int probe_read(const void* src, long long bytes, unsigned* out, int b
   if (bytes % 16 || src == nullptr || out == nullptr || blocks < 1) return -1;
   read_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(static_cast<const uint4*>(src),
                                                                           bytes / 16, out);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Bytes one probe_dma_stream launch moves into LDS.
+extern "C" double probe_dma_bytes(int blocks, int kbytes, int rounds) {
+  return static_cast<double>(blocks) * rounds * (kbytes / 128) * kStage;
+}
+
+// a and b: npanels panels of 256 rows x kbytes each (kbytes a multiple of 128, 256 * kbytes
+// < 2^31), 16-byte aligned.  One workgroup per compute unit: `blocks` = the CU count (a multiple
+// of 8, 32 per XCD for the fresh mode's cells).
+extern "C" int probe_dma_stream(const void* a, const void* b, int kbytes, int npanels, int rounds, int shared,
+                                int blocks, void* stream) {
+  if (a == nullptr || b == nullptr || kbytes < 128 || kbytes % 128 || 256LL * kbytes >= (1LL << 31) || npanels < 1 ||
+      rounds < 1 || blocks < 8 || blocks % 8)
+    return -1;
+  dma_stream_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), kbytes, rounds, npanels, shared);
   return static_cast<int>(hipGetLastError());
 }
