@@ -130,7 +130,11 @@ __device__ __forceinline__ void load_tile_regs(const uint16_t* __restrict__ src,
   }
 }
 
-__global__ __launch_bounds__(256) void quant_both_kernel(const uint16_t* __restrict__ in, int rows, int cols,
+// At most two waves per SIMD (two workgroups per compute unit): measured 8-10% faster than the
+// six the registers would allow, and faster than one, three or four (each workgroup's 128 source
+// rows are read as 128-byte pieces, and fewer bands in flight at once keep the DRAM and L2 traffic
+// of the two output layouts more local).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void quant_both_kernel(const uint16_t* __restrict__ in, int rows, int cols,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
                                                          uint8_t* __restrict__ qT, uint8_t* __restrict__ scaleT) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTP][kPitch];
