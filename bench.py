@@ -369,14 +369,29 @@ def measured_ceilings():
         ms = timed(lambda: lib.probe_dma_stream(ctypes.c_void_p(pa.data_ptr()), ctypes.c_void_p(pb.data_ptr()), kbytes,
                                                 npanels, rounds, shared, cus, ctypes.c_void_p(stream)))
         out[name] = round(lib.probe_dma_bytes(cus, kbytes, rounds) / (ms * 1e-3) / 1e9, 1)
-    del pa, pb
+    # the products' K step alone (stream + fragment reads + block-scaled fp8 MFMAs, no scales,
+    # no epilogue), and with one part removed at a time
+    lib.probe_kstep_flop.restype = ctypes.c_double
+    lib.probe_kstep_flop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.probe_kstep.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    kout = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    ks = {}
+    for name, v in (("4_waves", 0), ("8_waves", 1), ("4_waves_no_dma", 2), ("4_waves_no_lds_reads", 3)):
+        ms = timed(lambda: lib.probe_kstep(v, ctypes.c_void_p(pa.data_ptr()), ctypes.c_void_p(pb.data_ptr()), kbytes,
+                                           npanels, 8, cus, ctypes.c_void_p(kout.data_ptr()), ctypes.c_void_p(stream)))
+        ks[name] = round(lib.probe_kstep_flop(cus, kbytes, 8) / (ms * 1e-3) / 1e12, 1)
+    out["mx_kstep_tflops"] = ks
+    del pa, pb, kout
     out["gemm_stream_bound_tflops"] = {"mxfp8": round(out["lds_dma_hbm_cells_gbs"] * 0.256, 1),
                                        "bf16": round(out["lds_dma_hbm_cells_gbs"] * 0.128, 1)}
     out["probe"] = ("expert_ffn_layer_top_amd/probe/ceiling.hip: MFMA-only loops (16 independent "
                     "accumulators per wave, register operands), 1 GiB copy (read + write bytes) and read, "
                     "LDS-DMA operand stream of 256-row panels (shared: L2-resident; cells: 8 x 4 panels per "
                     "XCD per round from 512 MiB buffers); gemm_stream_bound_tflops = the cells rate times the "
-                    "flops a 256 x 256 tile does per streamed byte")
+                    "flops a 256 x 256 tile does per streamed byte; mx_kstep_tflops = the MX products' K step "
+                    "alone (that stream, fragment reads, block-scaled MFMAs) in four and eight waves and with "
+                    "the DMA or the fragment reads removed")
     return out
 
 

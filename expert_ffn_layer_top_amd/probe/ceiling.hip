@@ -18,9 +18,17 @@
 //                     the first pass).  Fresh mode: the 32 workgroups of an XCD form a cell of 8
 //                     A panels x 4 B panels, a new cell per round, drawn from buffers larger than
 //                     the last-level cache (the products' tile order, on data arriving from HBM).
+//   probe_kstep       the MX products' K step without scales or epilogue: the LDS-DMA stream
+//                     above (cells from HBM) feeding ds_read_b128 fragments and block-scaled
+//                     16x16x128 fp8 MFMAs on a 256 x 256 tile, K = 7168.  Variants: 0 four
+//                     waves of 128 x 128 (the kernels' layout), 1 eight waves of 64 x 128 (two per
+//                     SIMD), 2 variant 0 without the DMA after the first step, 3 variant 0 with the
+//                     fragments read once (no LDS reads in the K loop).
 // Each result is written so the compiler keeps the work; the host times the launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace {
 
@@ -131,6 +139,145 @@ __global__ __launch_bounds__(256, 1) void dma_stream_kernel(const uint8_t* __res
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int B, int E, class F>
+__device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    sfor<B + 1, E>(f);
+  }
+}
+
+// ---- probe_kstep.  Stage layout as in the MX products: 256 A rows then 256 B rows of 128 bytes,
+// each row's eight 16-byte chunks XOR-swizzled by (row / 2) % 8.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+template <int OFF>
+__device__ __forceinline__ void ds_b128(i32x4& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+// fragment q of an operand stage: lane l reads row 16 q + l % 16, chunks l / 16 and 4 + l / 16
+template <int Q>
+__device__ __forceinline__ void frag(i32x8& v, uint32_t base, uint32_t kc0, uint32_t kc1) {
+  i32x4 lo, hi;
+  ds_b128<2048 * Q>(lo, base + kc0);
+  ds_b128<2048 * Q>(hi, base + kc1);
+  v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void mfma(f32x4& c, const i32x8& x, const i32x8& y, int s) {
+  asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]" : "+a"(c) : "v"(x), "v"(y), "v"(s));
+}
+template <int N, int NA>
+__device__ __forceinline__ void wait_lgkm(i32x8& b, i32x8 (&a)[NA]) {
+  if constexpr (NA == 8)
+    asm volatile("s_waitcnt lgkmcnt(%9)" : "+v"(b), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]),
+                 "+v"(a[5]), "+v"(a[6]), "+v"(a[7]) : "n"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(b), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(N));
+}
+
+// NW waves, each with NAF A fragments (16 NAF rows) and NBF B fragments (16 NBF columns) of the
+// 256 x 256 tile; ABL 1 drops the DMA after the first step, ABL 2 the fragment reads in the K loop.
+template <int NW, int NAF, int NBF, int ABL = 0>
+__global__ __launch_bounds__(NW * 64, 1) void kstep_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                           int kbytes, int rounds, int npanels, float* __restrict__ out) {
+  constexpr int WM = 256 / (16 * NAF);        // waves along M
+  constexpr int PER = 64 / NW;                // DMA instructions per wave per step
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WM, wn = wave / WM;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  // DMA: group g of 64 (8 rows x 128 bytes each): g < 32 A rows 8 g.., else B rows 8 (g - 32)..
+  int vo[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = wave * PER + i;
+    const int row = 8 * (g & 31) + (lane >> 3);
+    vo[i] = row * kbytes + 16 * ((lane & 7) ^ swz(row));
+  }
+  const bool is_a = wave * PER < 32;   // PER divides 32: a wave's groups are all A or all B
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const uint32_t kc0 = (lane & 15) * 128 + (((lane >> 4) ^ swz(lane & 15)) << 4);
+  const uint32_t kc1 = (lane & 15) * 128 + (((4 + (lane >> 4)) ^ swz(lane & 15)) << 4);
+  const int unit = 127;
+  f32x4 acc[NBF][NAF];
+#pragma unroll
+  for (int i = 0; i < NBF; ++i)
+#pragma unroll
+    for (int q = 0; q < NAF; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  asm volatile("s_nop 7" ::: "memory");
+  const int steps = kbytes / 128;
+  int g = 0;
+  __amdgpu_buffer_rsrc_t rs;
+  auto set_panel = [&](int r) {
+    const int pa = ((xcd * rounds + r) * 8 + (j & 7)) % npanels;
+    const int pb = ((xcd * rounds + r) * 4 + (j >> 3)) % npanels;
+    const uint8_t* base = is_a ? a + static_cast<long long>(pa) * 256 * kbytes : b + static_cast<long long>(pb) * 256 * kbytes;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, 256 * kbytes, 0x00020000);
+  };
+  auto issue = [&](auto i0, auto n, int stage, int k) {
+    uint8_t* dst = ring + kStage * stage + 1024 * (wave * PER);
+    sfor<decltype(i0)::value, decltype(i0)::value + decltype(n)::value>([&](auto i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 1024 * i), 16, vo[i], 128 * k, 0, 0);
+    });
+  };
+  // prologue: step 0
+  set_panel(0);
+  issue(std::integral_constant<int, 0>{}, std::integral_constant<int, PER>{}, 0, 0);
+  i32x8 ga[NAF], gb[2];   // ABL 2: fragments read once, reused every step
+  if constexpr (ABL == 2) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint32_t abase = lds0 + 2048 * NAF * wm, bbase = lds0 + 32768 + 2048 * NBF * wn;
+    sfor<0, NAF>([&](auto q) { frag<q>(ga[q], abase, kc0, kc1); });
+    frag<0>(gb[0], bbase, kc0, kc1);
+    frag<1>(gb[1], bbase, kc0, kc1);
+    wait_lgkm<0>(gb[0], ga);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(gb[1]));
+  }
+  for (int r = 0; r < rounds; ++r) {
+    for (int k = 0; k < steps; ++k, ++g) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      const int st = g & 1;
+      const bool last = k + 1 == steps;
+      if (last && r + 1 < rounds) set_panel(r + 1);
+      const int kn = last ? 0 : k + 1;
+      const bool more = !(last && r + 1 == rounds);
+      const uint32_t abase = lds0 + kStage * st + 2048 * NAF * wm;
+      const uint32_t bbase = lds0 + kStage * st + 32768 + 2048 * NBF * wn;
+      if constexpr (ABL == 2) {
+        sfor<0, NBF>([&](auto i) {
+          if constexpr (i < 4) {
+            if (more) issue(std::integral_constant<int, i * PER / 4>{}, std::integral_constant<int, PER / 4>{}, st ^ 1, kn);
+          }
+          sfor<0, NAF>([&](auto q) { mfma(acc[i][q], gb[i & 1], ga[q], unit); });
+        });
+      } else {
+        i32x8 fa[NAF], fb[2];
+        sfor<0, NAF>([&](auto q) { frag<q>(fa[q], abase, kc0, kc1); });
+        frag<0>(fb[0], bbase, kc0, kc1);
+        sfor<0, NBF>([&](auto i) {
+          if constexpr (i < 4 && ABL != 1) {
+            if (more) issue(std::integral_constant<int, i * PER / 4>{}, std::integral_constant<int, PER / 4>{}, st ^ 1, kn);
+          }
+          if constexpr (i + 1 < NBF) frag<i + 1>(fb[(i + 1) & 1], bbase, kc0, kc1);
+          wait_lgkm<(i + 1 < NBF) ? 2 : 0>(fb[i & 1], fa);
+          sfor<0, NAF>([&](auto q) { mfma(acc[i][q], fb[i & 1], fa[q], unit); });
+        });
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NBF; ++i)
+#pragma unroll
+    for (int q = 0; q < NAF; ++q) s += acc[i][q][0] + acc[i][q][1] + acc[i][q][2] + acc[i][q][3];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                    long long n16) {
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
@@ -204,5 +351,27 @@ extern "C" int probe_dma_stream(const void* a, const void* b, int kbytes, int np
     return -1;
   dma_stream_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
       static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), kbytes, rounds, npanels, shared);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Flop per probe_kstep launch.
+extern "C" double probe_kstep_flop(int blocks, int kbytes, int rounds) {
+  return static_cast<double>(blocks) * rounds * 256.0 * 256.0 * kbytes * 2.0;
+}
+
+// a, b as for probe_dma_stream; out: blocks * 512 floats.
+extern "C" int probe_kstep(int variant, const void* a, const void* b, int kbytes, int npanels, int rounds, int blocks,
+                           float* out, void* stream) {
+  if (a == nullptr || b == nullptr || out == nullptr || kbytes < 128 || kbytes % 128 || 256LL * kbytes >= (1LL << 31) ||
+      npanels < 1 || rounds < 1 || blocks < 8 || blocks % 8)
+    return -1;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* A = static_cast<const uint8_t*>(a);
+  const uint8_t* B = static_cast<const uint8_t*>(b);
+  if (variant == 0) kstep_kernel<4, 8, 8><<<blocks, 256, 0, s>>>(A, B, kbytes, rounds, npanels, out);
+  else if (variant == 1) kstep_kernel<8, 4, 8><<<blocks, 512, 0, s>>>(A, B, kbytes, rounds, npanels, out);
+  else if (variant == 2) kstep_kernel<4, 8, 8, 1><<<blocks, 256, 0, s>>>(A, B, kbytes, rounds, npanels, out);
+  else if (variant == 3) kstep_kernel<4, 8, 8, 2><<<blocks, 256, 0, s>>>(A, B, kbytes, rounds, npanels, out);
+  else return -1;
   return static_cast<int>(hipGetLastError());
 }
