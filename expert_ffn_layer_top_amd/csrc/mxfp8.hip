@@ -114,9 +114,20 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
 // column tiles of one 128-row band, loading the next tile into registers while it quantises the
 // current one, so each compute unit keeps more of the input in flight.
 // in [batch][rows][cols] -> q [batch][rows][cols] + scale [batch][rows][cols/32] and
-// qT [batch][cols][rows] + scaleT [batch][cols][rows/32].
-// grid: (ceil(cols / (64 kBothTiles)), ceil(rows/128), batch); rows % 32 == 0, cols % 64 == 0.
+// qT [batch][cols][rows] + scaleT [batch][cols][rows/32].  rows % 32 == 0, cols % 64 == 0.
+// 1-D grid of cgroups * bands * batch blocks, work items ordered column groups fastest, then bands,
+// then matrices, dealt to the XCDs in contiguous runs (xcd_run_item).
 constexpr int kBothTiles = 4;
+
+// Work item of block `id` when XCD x (block ids = x mod 8, each XCD with its own L2) takes the
+// contiguous run of items [start(x), start(x + 1)): the workgroups that fill one scale line (the
+// column groups of a band) then run side by side on one XCD, whose L2 merges their bytes before
+// the line is written back (dealt round-robin, a line's pieces sat in up to eight L2s).
+__device__ __forceinline__ long long xcd_run_item(long long id, long long total) {
+  const long long per = total >> 3, extra = total & 7;
+  const long long x = id & 7, j = id >> 3;
+  return x * per + (x < extra ? x : extra) + j;
+}
 
 __device__ __forceinline__ void load_tile_regs(const uint16_t* __restrict__ src, int rows, int cols, int r0, int c0,
                                                uint4 (&v)[4]) {
@@ -136,14 +147,17 @@ __device__ __forceinline__ void load_tile_regs(const uint16_t* __restrict__ src,
 // of the two output layouts more local).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void quant_both_kernel(const uint16_t* __restrict__ in, int rows, int cols,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
-                                                         uint8_t* __restrict__ qT, uint8_t* __restrict__ scaleT) {
+                                                         uint8_t* __restrict__ qT, uint8_t* __restrict__ scaleT,
+                                                         int cgroups, int bands, long long total) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTP][kPitch];
-  const long long b = blockIdx.z;
-  const int r0 = blockIdx.y * kTP;
+  const long long item = xcd_run_item(blockIdx.x, total);
+  const long long b = item / (static_cast<long long>(cgroups) * bands);
+  const int rest = static_cast<int>(item - b * cgroups * bands);
+  const int r0 = (rest / cgroups) * kTP;
   const long long plane = static_cast<long long>(rows) * cols;
   const uint16_t* src = in + b * plane;
   const int cc = threadIdx.x & 7;
-  int c0 = blockIdx.x * kTC * kBothTiles;
+  int c0 = (rest % cgroups) * kTC * kBothTiles;
   uint4 v[4];
   load_tile_regs(src, rows, cols, r0, c0, v);
   for (int it = 0; it < kBothTiles && c0 < cols; ++it, c0 += kTC) {
@@ -324,10 +338,11 @@ extern "C" int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int 
   MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(q); MOE_CHECK_ALIGN(qT);
   MOE_REQUIRE(batch >= 1 && rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG, "sizes must be positive");
   MOE_REQUIRE(rows % 32 == 0 && cols % 64 == 0, MOE_ERR_UNSUPPORTED, "need rows %% 32 == 0, cols %% 64 == 0");
-  MOE_REQUIRE(batch <= 65535, MOE_ERR_UNSUPPORTED, "batch too large");
-  MOE_REQUIRE((rows + kTP - 1) / kTP <= 65535, MOE_ERR_UNSUPPORTED, "too many rows");
-  dim3 grid((cols / kTC + kBothTiles - 1) / kBothTiles, (rows + kTP - 1) / kTP, batch);
-  quant_both_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, rows, cols, q, scale, qT, scaleT);
+  const int cgroups = (cols / kTC + kBothTiles - 1) / kBothTiles, bands = (rows + kTP - 1) / kTP;
+  const long long total = static_cast<long long>(cgroups) * bands * batch;
+  MOE_REQUIRE(total <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "too many tiles");
+  quant_both_kernel<<<static_cast<unsigned>(total), 256, 0, as_stream(stream)>>>(in, rows, cols, q, scale, qT, scaleT,
+                                                                                 cgroups, bands, total);
   return check_launch("mxfp8_quantize_both");
 }
 
