@@ -160,13 +160,13 @@ def aux_bytes(cfg, call):
         return 3 * E * d * f * (2 + 2 * mx)
     if call == "quant_x":
         return T * d * (2 + mx)
-    if call in ("quant_dg", "quant_du"):
-        return n * f * (2 + mx)
+    if call in ("quant_dg", "quant_du"):   # both layouts from one read
+        return n * f * (2 + mx) + P * f * mx
     if call == "quant_dyT":      # dy gathered through row_token with the row gates
         return T * d * 2 + n * 8 + P * d * mx
     if call == "quant_xT":
         return T * d * 2 + n * 4 + P * d * mx
-    if call in ("quant_aT", "quant_dgT", "quant_duT"):
+    if call == "quant_aT":
         return n * f * 2 + P * f * mx
     raise KeyError(call)
 

@@ -209,7 +209,10 @@ constexpr int kGroupTiles = 4;
 // from offsets_pad[E] to n_pad_cap hold zeros.  Row r's data is in[row_token ? row_token[r] : r].
 // With row_gate, grouped row r is bf16(row_gate[r] * in[row_token[r]]) (fp32 product, round to
 // nearest even): the rows the fused MXFP8 combine backward never writes in bf16.
-// q [C][n_pad_cap], scale [n_pad_cap/32][C].  A workgroup takes a 128-position band and walks
+// q [C][n_pad_cap], scale [n_pad_cap/32][C].  With ROWS (contiguous rows, no gather, no gate), the
+// same tiles also give the real rows' row blocks: qr [n][C], sr [n][C/32], as mxfp8_quantize along
+// the rows, so a tensor both products need (dG, dU) is read once for its two layouts.
+// A workgroup takes a 128-position band and walks
 // kGroupTiles column tiles of it (the rows' adjacent 128-byte pieces, read close together in time,
 // with the next tile's loads in flight while the current one is quantised); the band's source
 // rows are looked up once.  Without a gather (contiguous rows), the column groups of one band
@@ -218,13 +221,15 @@ constexpr int kGroupTiles = 4;
 // gather through row_token the bands come first (measured slightly faster), as they do whenever
 // there are more than 65535 bands.  grid: (ceil(C / (64 kGroupTiles)), n_pad_cap/128), or
 // transposed (bands in x).
+template <bool ROWS>
 __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __restrict__ in,
                                                             const int32_t* __restrict__ row_token,
                                                             const float* __restrict__ row_gate,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ offsets_pad, int E, int C,
                                                             long long n_pad_cap, uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ scale, int bands_in_x) {
+                                                            uint8_t* __restrict__ scale, int bands_in_x,
+                                                            uint8_t* __restrict__ qr, uint8_t* __restrict__ sr) {
   const int band = bands_in_x ? blockIdx.x : blockIdx.y;
   const int cgroup = bands_in_x ? blockIdx.y : blockIdx.x;
   __shared__ uint16_t tile[kTP][kPitch];
@@ -288,6 +293,27 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
   load(c0, v);
   for (int it = 0; it < kGroupTiles && c0 < C; ++it, c0 += kTC) {
     gated(v);
+    if constexpr (ROWS) {
+      // row blocks from the registers: v[i] is columns c0 + 8 (t % 8) .. + 7 of row src[i], so a
+      // 32-column block is 4 adjacent lanes (amax by two shuffles), each writing 8 codes
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t amax = 0;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) amax = max(amax, max(w[h] & 0x7fffu, (w[h] >> 16) & 0x7fffu));
+        amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1, 64)));
+        amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, 64)));
+        if (src[i] >= 0 && c0 < C) {
+          const int sh = mx_shared_exp(amax);
+          const uint32_t o0 = mx_encode4(w[0] & 0xffffu, w[0] >> 16, w[1] & 0xffffu, w[1] >> 16, sh);
+          const uint32_t o1 = mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh);
+          const int col = c0 + 8 * cc;
+          *reinterpret_cast<uint2*>(qr + src[i] * C + col) = make_uint2(o0, o1);
+          if ((cc & 3) == 0) sr[src[i] * (C / 32) + col / 32] = static_cast<uint8_t>(sh + 127);
+        }
+      }
+    }
     __syncthreads();   // the previous tile's readers are done with the LDS tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -348,7 +374,7 @@ extern "C" int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int 
 
 static int quantize_grouped(const uint16_t* in, const int32_t* row_token, const float* row_gate,
                             const int32_t* offsets, const int32_t* offsets_pad, int E, int n, int C, uint8_t* qT,
-                            uint8_t* scaleT, void* stream) {
+                            uint8_t* scaleT, void* stream, uint8_t* q_rows = nullptr, uint8_t* s_rows = nullptr) {
   MOE_CHECK_PTR(in); MOE_CHECK_PTR(offsets); MOE_CHECK_PTR(offsets_pad); MOE_CHECK_PTR(qT); MOE_CHECK_PTR(scaleT);
   MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(qT);
   MOE_REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "E must be in [1, 256]");
@@ -358,8 +384,12 @@ static int quantize_grouped(const uint16_t* in, const int32_t* row_token, const 
   const int bands = cap / kTP, cgroups = (C / kTC + kGroupTiles - 1) / kGroupTiles;
   const int bands_in_x = (bands > 65535 || row_token != nullptr) ? 1 : 0;
   dim3 grid(bands_in_x ? bands : cgroups, bands_in_x ? cgroups : bands);
-  quant_grouped_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, row_token, row_gate, offsets, offsets_pad, E, C, cap,
-                                                             qT, scaleT, bands_in_x);
+  if (q_rows != nullptr)
+    quant_grouped_kernel<true><<<grid, 256, 0, as_stream(stream)>>>(in, row_token, row_gate, offsets, offsets_pad, E, C,
+                                                                    cap, qT, scaleT, bands_in_x, q_rows, s_rows);
+  else
+    quant_grouped_kernel<false><<<grid, 256, 0, as_stream(stream)>>>(in, row_token, row_gate, offsets, offsets_pad, E,
+                                                                     C, cap, qT, scaleT, bands_in_x, nullptr, nullptr);
   return check_launch("mxfp8_quantize_grouped");
 }
 
@@ -374,4 +404,12 @@ extern "C" int mxfp8_quantize_grouped_gated(const uint16_t* in, const int32_t* r
                                             uint8_t* qT, uint8_t* scaleT, void* stream) {
   MOE_CHECK_PTR(row_token); MOE_CHECK_PTR(row_gate);
   return quantize_grouped(in, row_token, row_gate, offsets, offsets_pad, E, n, C, qT, scaleT, stream);
+}
+
+extern "C" int mxfp8_quantize_rows_grouped(const uint16_t* in, const int32_t* offsets, const int32_t* offsets_pad,
+                                           int E, int n, int C, uint8_t* q_rows, uint8_t* s_rows, uint8_t* qT,
+                                           uint8_t* scaleT, void* stream) {
+  MOE_CHECK_PTR(q_rows); MOE_CHECK_PTR(s_rows);
+  MOE_CHECK_ALIGN(q_rows);
+  return quantize_grouped(in, nullptr, nullptr, offsets, offsets_pad, E, n, C, qT, scaleT, stream, q_rows, s_rows);
 }

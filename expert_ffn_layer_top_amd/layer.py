@@ -89,7 +89,7 @@ RECOMPUTE_CALL = "recompute"
 # the router products (layers that own their router) and the MXFP8 quantiser calls (each one
 # kernel; under MXFP8 "quant_dyT" gathers dy with the combine backward's row gates)
 ROUTER_CALLS = ("router", "router_bwd")
-QUANT_CALLS = ("quant_x", "quant_dg", "quant_du", "quant_dyT", "quant_aT", "quant_dgT", "quant_duT", "quant_xT")
+QUANT_CALLS = ("quant_x", "quant_dg", "quant_du", "quant_dyT", "quant_aT", "quant_xT")
 ROW_CALLS = ("route", "permute", "combine", "combine_bwd", "permute_bwd", "route_bwd")
 
 
@@ -219,19 +219,17 @@ def backward(ctx, weights, dy, events=None):
             aT, aTs = ops.mxfp8_quantize_grouped(a, off, pad, n)
         with _Span(events, "wgrad_down"):
             dw_down = ops.grouped_gemm_wgrad_down(dyT, aT, off, n, offsets_pad=pad, scales=(dyTs, aTs))
+        # dG and dU each read once for both layouts: row blocks for the gate/up dgrad, grouped
+        # token blocks for the gate/up weight gradient
         with _Span(events, "quant_dg"):
-            dgq, dgs = ops.mxfp8_quantize(dg, 0)
+            dgq, dgs, dgT, dgTs = ops.mxfp8_quantize_rows_grouped(dg, off, pad)
         with _Span(events, "quant_du"):
-            duq, dus = ops.mxfp8_quantize(du, 0)
+            duq, dus, duT, duTs = ops.mxfp8_quantize_rows_grouped(du, off, pad)
         with _Span(events, "dgrad_gate_up"):
             dxp = ops.grouped_gemm_dgrad_gate_up(dgq, duq, off, q["wg_t"], q["wu_t"],
                                                  scales=(dgs, dus, q["wg_t_s"], q["wu_t_s"]))
         with _Span(events, "permute_bwd"):
             out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
-        with _Span(events, "quant_dgT"):
-            dgT, dgTs = ops.mxfp8_quantize_grouped(dg, off, pad, n)
-        with _Span(events, "quant_duT"):
-            duT, duTs = ops.mxfp8_quantize_grouped(du, off, pad, n)
         with _Span(events, "quant_xT"):
             xT, xTs = ops.mxfp8_quantize_grouped(ctx["x"], off, pad, n, row_token=ctx["row_token"])
         with _Span(events, "wgrad_gate_up"):

@@ -329,6 +329,28 @@ def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None, row_gate=
     return q, s
 
 
+def mxfp8_quantize_rows_grouped(x, offsets, offsets_pad):
+    """Both MXFP8 layouts of a grouped [n, C] bf16 tensor from one read: (q [n, C], s [n, C/32])
+    row blocks as mxfp8_quantize(x, 0) and (qT [C, P], sT [P/32, C]) grouped token blocks as
+    mxfp8_quantize_grouped(x, offsets, offsets_pad, n)."""
+    _check(offsets, torch.int32, "offsets", ndim=1)
+    E = offsets.shape[0] - 1
+    _need(E >= 1, "offsets must hold E + 1 >= 2 entries")
+    _check(offsets_pad, torch.int32, "offsets_pad", (E + 1,))
+    _check(x, torch.bfloat16, "x", ndim=2)
+    n, C = x.shape
+    _need(C % 64 == 0, "C must be a multiple of 64")
+    _on_gpu(x, offsets, offsets_pad)
+    P = mx_pad_cap(n, E)
+    q = _empty((n, C), torch.uint8, x)
+    s = _empty((n, C // 32), torch.uint8, x)
+    qT = _empty((C, P), torch.uint8, x)
+    sT = _empty((P // 32, C), torch.uint8, x)
+    call("mxfp8_quantize_rows_grouped", _ptr(x), _ptr(offsets), _ptr(offsets_pad), E, n, C, _ptr(q), _ptr(s),
+         _ptr(qT), _ptr(sT), _stream(x))
+    return q, s, qT, sT
+
+
 # ---------------------------------------------------------------- grouped GEMMs
 
 def gg_workspace(dtype, E, n, d, f, like):

@@ -110,9 +110,9 @@ def step_sequence(mxfp8, router, forward_only=False):
     if mxfp8:
         qg = ("quant_grouped_kernel", None)
         seq += [("dgrad_down", [g(2)]), ("quant_dyT", [qg]), ("quant_aT", [qg]), ("wgrad_down", [g(4)]),
-                ("quant_dg", [("quant_rows_kernel", None)]), ("quant_du", [("quant_rows_kernel", None)]),
+                ("quant_dg", [qg]), ("quant_du", [qg]),
                 ("dgrad_gate_up", [g(3)]), ("permute_bwd", [("permute_bwd_kernel", None)]),
-                ("quant_dgT", [qg]), ("quant_duT", [qg]), ("quant_xT", [qg]), ("wgrad_gate_up", [g(5)])]
+                ("quant_xT", [qg]), ("wgrad_gate_up", [g(5)])]
     else:
         seq += [("dgrad_down", [g(2)]), ("wgrad_down", [g(4)]), ("dgrad_gate_up", [g(3)]),
                 ("permute_bwd", [("permute_bwd_kernel", None)]), ("wgrad_gate_up", [g(5)])]

@@ -260,6 +260,18 @@ int mxfp8_quantize_grouped_gated(const uint16_t* in, const int32_t* row_token, c
                                  const int32_t* offsets, const int32_t* offsets_pad, int E, int n,
                                  int C, uint8_t* qT, uint8_t* scaleT, void* stream);
 
+/* Both MXFP8 layouts of a grouped [n, C] bf16 tensor from one read ([news] "MXFP8 reduces compute
+ * and memory costs": the expert products run on 8-bit operands with a scale per small block; the
+ * backward's dG and dU feed one product contracting over C and one contracting over tokens):
+ *   q_rows [n, C] E4M3 + s_rows [n, C/32] E8M0: row blocks, byte-identical to
+ *     mxfp8_quantize(in, 1, n, C, axis 0, scale_mode 0);
+ *   qT, scaleT: the grouped token blocks, byte-identical to mxfp8_quantize_grouped(in, NULL, ...).
+ * Same requirements and errors as mxfp8_quantize_grouped (C a multiple of 64, 1 <= E <= 256),
+ * plus q_rows and s_rows non-NULL and q_rows 16-byte aligned. */
+int mxfp8_quantize_rows_grouped(const uint16_t* in, const int32_t* offsets, const int32_t* offsets_pad, int E,
+                                int n, int C, uint8_t* q_rows, uint8_t* s_rows, uint8_t* qT, uint8_t* scaleT,
+                                void* stream);
+
 /* Length of the padded token axis used by mxfp8_quantize_grouped and the MXFP8 backward. */
 int moe_mx_pad_cap(int n, int E);
 

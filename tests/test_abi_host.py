@@ -112,6 +112,13 @@ def test_argument_checks_return_status_without_launching():
     assert L.mxfp8_quantize_both(fake, 1, 48, 64, fake, fake, fake, fake, None) == UNSUPPORTED
     assert L.mxfp8_quantize_both(fake, 1, 64, 96, fake, fake, fake, fake, None) == UNSUPPORTED
     assert L.mxfp8_quantize_both(fake, 1, 64, 64, fake, None, fake, fake, None) == INVALID
+    # rows + grouped quantiser: C % 64, E range, row outputs required
+    assert L.mxfp8_quantize_rows_grouped(fake, fake, fake, 4, 100, 96, fake, fake, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp8_quantize_rows_grouped(fake, fake, fake, 0, 100, 128, fake, fake, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp8_quantize_rows_grouped(fake, fake, fake, 4, 100, 128, None, fake, fake, fake, None) == INVALID
+    assert L.mxfp8_quantize_rows_grouped(fake, fake, fake, 4, 100, 128, fake, None, fake, fake, None) == INVALID
+    assert L.mxfp8_quantize_rows_grouped(fake, fake, fake, 4, 100, 128, ctypes.c_void_p(0x1008), fake, fake, fake,
+                                         None) == INVALID
     # router: d a multiple of 8, x 16-byte aligned
     assert L.moe_router_project(fake, fake, 64, 12, 8, fake, None) == UNSUPPORTED
     assert L.moe_router_project(ctypes.c_void_p(0x1008), fake, 64, 128, 8, fake, None) == INVALID

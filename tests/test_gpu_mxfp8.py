@@ -106,6 +106,29 @@ def test_rows_and_cols_from_one_read(B, R, C):
 
 
 @pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
+def test_rows_and_grouped_from_one_read(T, E, k, C):
+    """Both layouts of a grouped tensor from one read (the backward's dG, dU) against the oracle's
+    row blocks and grouped token blocks, with an empty expert group and ragged group sizes."""
+    from expert_ffn_layer_top_amd import ops
+    rng = np.random.default_rng(3 * T + E + C)
+    logits = rng.standard_normal((T, E))
+    logits[:, E // 2] -= 100.0                            # an empty expert group
+    idx, _, _ = moe.route_topk(logits, k)
+    _, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=32)
+    n = T * k
+    v = rng.standard_normal((n, C)).astype(np.float32) * np.exp(rng.standard_normal((n, 1)) * 3).astype(np.float32)
+    xp = to_bf16_bits(v)
+    note(f"mxfp8 rows+grouped T={T} E={E} k={k} C={C}")
+    q, s, qT, sT = ops.mxfp8_quantize_rows_grouped(bf16_to_dev(xp), i32_to_dev(off), i32_to_dev(offp))
+    rq, rs = mxfp8.quantize_rows(xp)
+    assert np.array_equal(host(q), rq) and np.array_equal(host(s), rs)
+    gq, gs = mxfp8.quantize_grouped(xp, off, offp)
+    qT, sT = host(qT), host(sT).T
+    assert np.array_equal(qT[:, : offp[E]], gq) and np.array_equal(sT[:, : offp[E] // 32], gs)
+    assert np.all(qT[:, offp[E]:] == 0) and np.all(sT[:, offp[E] // 32:] == 0)
+
+
+@pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
 @pytest.mark.parametrize("gather", [False, True])
 def test_grouped_token_blocks(T, E, k, C, gather):
     from expert_ffn_layer_top_amd import ops
