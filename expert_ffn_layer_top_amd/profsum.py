@@ -110,7 +110,7 @@ def step_sequence(mxfp8, router, forward_only=False):
     if mxfp8:
         qg = ("quant_grouped_kernel", None)
         seq += [("dgrad_down", [g(2)]), ("quant_dyT", [qg]), ("quant_aT", [qg]), ("wgrad_down", [g(4)]),
-                ("quant_dg", [qg]), ("quant_du", [qg]),
+                ("quant_dg", [("quant_rows_grouped_kernel", None)]), ("quant_du", [("quant_rows_grouped_kernel", None)]),
                 ("dgrad_gate_up", [g(3)]), ("permute_bwd", [("permute_bwd_kernel", None)]),
                 ("quant_xT", [qg]), ("wgrad_gate_up", [g(5)])]
     else:
