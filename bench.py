@@ -130,8 +130,8 @@ def row_bytes(cfg, call):
     router = cfg.logits == "router"
     if call == "route":          # logits in; topk_idx, gates, dest, row_token out
         return T * 4 * E + n * 16
-    if call == "permute":        # x rows (and scales) in, k copies out, dest in
-        return (1 + k) * T * d * (mx if cfg.mxfp8 else 2) + 4 * n
+    if call == "permute":        # x rows in, k copies out (MXFP8: quantised on the way), dest in
+        return T * d * 2 + n * d * (mx if cfg.mxfp8 else 2) + 4 * n
     if call == "combine":        # yexp rows, gates, dest in; y out
         return (n + T) * d * 2 + 8 * n
     if call == "combine_bwd":    # dy, yexp rows, gates, dest in; dyexp (bf16, or MX row blocks + row gates), d_gate out
@@ -158,8 +158,6 @@ def aux_bytes(cfg, call):
         return T * E * 4 + d * E * 4 + T * d * 2 + T * d * 4 + d * E * 4
     if call == "quant_w":        # three weights, both layouts from one read
         return 3 * E * d * f * (2 + 2 * mx)
-    if call == "quant_x":
-        return T * d * (2 + mx)
     if call in ("quant_dg", "quant_du"):   # both layouts from one read
         return n * f * (2 + mx) + P * f * mx
     if call == "quant_dyT":      # dy gathered through row_token with the row gates
@@ -218,7 +216,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=True):
     if cfg.logits == "router":
         aux += layer.ROUTER_CALLS if not cfg.forward_only else ("router",)
     if cfg.mxfp8:
-        aux += ("quant_w",) + (layer.QUANT_CALLS if not cfg.forward_only else ("quant_x",))
+        aux += ("quant_w",) + (layer.QUANT_CALLS if not cfg.forward_only else ())
 
     def ev():
         return torch.cuda.Event(enable_timing=True)

@@ -91,6 +91,44 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict_
   }
 }
 
+// MXFP8 permute straight from bf16 x: xpq[dest[t,j]] / xps[dest[t,j]] = the row blocks of x[t]
+// (E4M3 codes and E8M0 scales, as mxfp8_quantize along the rows), so the quantised rows go into
+// the expert buffers without a token-major quantised copy.  A 32-element block is 4 adjacent
+// lanes of the wave's 1 KiB segment (amax by two shuffles); each lane writes 8 codes per
+// destination and the block's first lane its scale byte.  d a multiple of 32.
+template <int KM>
+__global__ __launch_bounds__(256) void permute_mx_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ dest,
+                                                         int T, int d, int k, int nseg, uint8_t* __restrict__ xpq,
+                                                         uint8_t* __restrict__ xps) {
+  const SegItem it = seg_item(nseg);
+  if (it.t >= T) return;
+  int rows[KM];
+  dest_rows<KM>(dest, it.t, k, rows);
+  const int e0 = 8 * it.c;                      // first element of this lane's chunk
+  const bool live = e0 < d;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (live) v = *reinterpret_cast<const uint4*>(x + it.t * d + e0);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) amax = max(amax, max(w[h] & 0x7fffu, (w[h] >> 16) & 0x7fffu));
+  amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1, 64)));
+  amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, 64)));
+  if (!live) return;
+  const int sh = mx_shared_exp(amax);
+  const uint2 o = make_uint2(mx_encode4(w[0] & 0xffffu, w[0] >> 16, w[1] & 0xffffu, w[1] >> 16, sh),
+                             mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh));
+  const uint8_t sb = static_cast<uint8_t>(sh + 127);
+  const int sp = d / 32;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < k) {
+      *reinterpret_cast<uint2*>(xpq + static_cast<long long>(rows[j]) * d + e0) = o;
+      if ((it.c & 3) == 0) xps[static_cast<long long>(rows[j]) * sp + e0 / 32] = sb;
+    }
+  }
+}
+
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
   f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
@@ -356,6 +394,17 @@ extern "C" int moe_permute(int dtype, const void* x, const uint8_t* x_scale, con
   MOE_SEG_LAUNCH(permute_kernel, seg_grid(T, nseg), as_stream(stream), k, static_cast<const uint8_t*>(x), x_scale, dest,
                  T, k, nseg, pitch, spitch, static_cast<uint8_t*>(xp), xp_scale);
   return check_launch("permute");
+}
+
+extern "C" int moe_permute_quant_mx(const uint16_t* x, const int32_t* dest, int T, int d, int k, uint8_t* xpq,
+                                    uint8_t* xps, void* stream) {
+  if (int st = check_rows(T, d, k)) return st;
+  MOE_CHECK_PTR(x); MOE_CHECK_PTR(dest); MOE_CHECK_PTR(xpq); MOE_CHECK_PTR(xps);
+  MOE_CHECK_ALIGN(x); MOE_CHECK_ALIGN(xpq);
+  const int nseg = segs_of(d / 8);
+  MOE_REQUIRE(static_cast<long long>(T) * nseg * 64 < (1LL << 32), MOE_ERR_UNSUPPORTED, "too many row segments");
+  MOE_SEG_LAUNCH(permute_mx_kernel, seg_grid(T, nseg), as_stream(stream), k, x, dest, T, d, k, nseg, xpq, xps);
+  return check_launch("permute_quant_mx");
 }
 
 extern "C" int moe_unpermute_combine(const uint16_t* yexp, const float* gate, const int32_t* dest, int T, int d,

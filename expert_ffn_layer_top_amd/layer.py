@@ -7,8 +7,9 @@ Backward: unpermute_combine_bwd -> route_topk_bwd -> [router_project_bwd]
           -> permute_bwd (+ the router's dx term) -> grouped_gemm_wgrad_gate_up
 The grouped products are issued one kernel per call (the same kernels, in the same order, as the
 composite grouped_gemm_swiglu / grouped_gemm_swiglu_bwd), so each can be timed on its own.
-MXFP8 adds the block quantisation of x (before the permute; row blocks commute with the row
-permutation) and of the expert weights in both contraction directions; router, combine,
+MXFP8 adds the block quantisation of x (inside the permute, which writes the row blocks straight
+into the expert buffers; row blocks commute with the row permutation) and of the expert weights
+in both contraction directions; router, combine,
 permute-backward and route-backward stay bf16/fp32.  Its combine backward is the fused producer
 (unpermute_combine_bwd_mx): dYexp leaves as MXFP8 row blocks and per-row gates, and the grouped
 token blocks of dYexp are rebuilt from dy and those gates, so the bf16 dYexp is never written.
@@ -89,7 +90,7 @@ RECOMPUTE_CALL = "recompute"
 # the router products (layers that own their router) and the MXFP8 quantiser calls (each one
 # kernel; under MXFP8 "quant_dyT" gathers dy with the combine backward's row gates)
 ROUTER_CALLS = ("router", "router_bwd")
-QUANT_CALLS = ("quant_x", "quant_dg", "quant_du", "quant_dyT", "quant_aT", "quant_xT")
+QUANT_CALLS = ("quant_dg", "quant_du", "quant_dyT", "quant_aT", "quant_xT")
 ROW_CALLS = ("route", "permute", "combine", "combine_bwd", "permute_bwd", "route_bwd")
 
 
@@ -131,11 +132,10 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
             yexp = ops.grouped_gemm_down(a, r["offsets"], weights.w_down)
     else:
         q = weights.mx_current()
-        with _Span(events, "quant_x"):
-            xq, xs = ops.mxfp8_quantize(x, 0)
+        # x quantised along d on its way into the expert buffers (no token-major E4M3 copy)
         with _Span(events, "permute"):
-            xpq, xps = ops.permute(xq, r["dest"], x_scale=xs)
-        ctx["xq"], ctx["xs"], ctx["xpq"], ctx["xps"] = xq, xs, xpq, xps
+            xpq, xps = ops.permute_quant_mx(x, r["dest"])
+        ctx["xpq"], ctx["xps"] = xpq, xps
         ctx["mx_weights"] = q            # the backward uses the copies this forward used
         with _Span(events, "gate_up"):
             g, u, a = ops.grouped_gemm_gate_up(xpq, r["offsets"], q["wg"], q["wu"],

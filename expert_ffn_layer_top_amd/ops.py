@@ -187,6 +187,20 @@ def permute(x, dest, x_scale=None):
     return xp, xps
 
 
+def permute_quant_mx(x, dest):
+    """(xpq [n,d] E4M3, xps [n,d/32] E8M0): the row blocks of bf16 x permuted into the expert
+    buffers, as mxfp8_quantize(x, 0) followed by permute(.., x_scale=..), in one pass."""
+    _check(dest, torch.int32, "dest", ndim=2)
+    T, k = dest.shape
+    _check(x, torch.bfloat16, "x", (T, None))
+    _on_gpu(x, dest)
+    d = x.shape[1]
+    xpq = _empty((T * k, d), torch.uint8, x)
+    xps = _empty((T * k, d // 32), torch.uint8, x)
+    call("moe_permute_quant_mx", _ptr(x), _ptr(dest), T, d, k, _ptr(xpq), _ptr(xps), _stream(x))
+    return xpq, xps
+
+
 def unpermute_combine(yexp, topk_gate, dest):
     _check(dest, torch.int32, "dest", ndim=2)
     T, k = dest.shape

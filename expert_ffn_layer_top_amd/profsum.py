@@ -95,7 +95,7 @@ def step_sequence(mxfp8, router, forward_only=False):
         seq.append(("router", [("router_fwd_kernel", None)]))
     seq.append(("route", [("route_topk_local", None), ("route_scan", None), ("route_finalize", None)]))
     if mxfp8:
-        seq += [("quant_x", [("quant_rows_kernel", None)]), ("permute", [("permute_kernel", None)]),
+        seq += [("permute", [("permute_mx_kernel", None)]),
                 ("gate_up", [g(0)]), ("down", [("quant_rows_kernel", None), g(1)])]
     else:
         seq += [("permute", [("permute_kernel", None)]), ("gate_up", [g(0)]), ("down", [g(1)])]

@@ -179,6 +179,17 @@ int moe_route_topk_bwd_balance(const float* topk_gate, const int32_t* topk_idx, 
 int moe_permute(int dtype, const void* x, const uint8_t* x_scale_or_null, const int32_t* dest,
                 int T, int d, int k, void* xp, uint8_t* xp_scale_or_null, void* stream);
 
+/* MXFP8 permute straight from bf16 x ([news] "Routing work stays on the GPU" and "MXFP8 reduces
+ * compute and memory costs": routed rows go straight into the expert buffers, here already as
+ * 8-bit codes with a scale per 32-element block): xpq[dest[t,j]] and xps[dest[t,j]] are the row
+ * blocks of x[t] -- byte-identical to mxfp8_quantize(x, axis 0, scale_mode 0) followed by
+ * moe_permute(MOE_MXFP8, ...), without the token-major quantised copy.
+ *   in  x [T,d] bf16, dest [T,k] int32;  out xpq [n,d] E4M3, xps [n,d/32] E8M0 (n = T*k).
+ * Same shape rules and errors as moe_permute (d a positive multiple of 64, 1 <= k <= 16);
+ * x and xpq 16-byte aligned. */
+int moe_permute_quant_mx(const uint16_t* x, const int32_t* dest, int T, int d, int k, uint8_t* xpq, uint8_t* xps,
+                         void* stream);
+
 /* Weighted unpermute-combine, the return path of the rowwise exchange ([news] "Routing work stays
  * on the GPU": routed rows live in expert buffers; the lead paragraphs: each token's output is
  * its chosen experts' outputs weighted by the router):

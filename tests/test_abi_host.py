@@ -112,6 +112,11 @@ def test_argument_checks_return_status_without_launching():
     assert L.mxfp8_quantize_both(fake, 1, 48, 64, fake, fake, fake, fake, None) == UNSUPPORTED
     assert L.mxfp8_quantize_both(fake, 1, 64, 96, fake, fake, fake, fake, None) == UNSUPPORTED
     assert L.mxfp8_quantize_both(fake, 1, 64, 64, fake, None, fake, fake, None) == INVALID
+    # quantising permute: d % 64, k range, pointers, alignment
+    assert L.moe_permute_quant_mx(fake, fake, 8, 96, 2, fake, fake, None) == UNSUPPORTED
+    assert L.moe_permute_quant_mx(fake, fake, 8, 128, 17, fake, fake, None) == UNSUPPORTED
+    assert L.moe_permute_quant_mx(fake, fake, 8, 128, 2, fake, None, None) == INVALID
+    assert L.moe_permute_quant_mx(ctypes.c_void_p(0x1008), fake, 8, 128, 2, fake, fake, None) == INVALID
     # rows + grouped quantiser: C % 64, E range, row outputs required
     assert L.mxfp8_quantize_rows_grouped(fake, fake, fake, 4, 100, 96, fake, fake, fake, fake, None) == UNSUPPORTED
     assert L.mxfp8_quantize_rows_grouped(fake, fake, fake, 0, 100, 128, fake, fake, fake, fake, None) == UNSUPPORTED

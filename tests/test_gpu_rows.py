@@ -47,6 +47,23 @@ def test_permute_e4m3_bitexact(T, d, E, k):
 
 
 @pytest.mark.parametrize("T,d,E,k", SHAPES)
+def test_permute_quantising_bitexact(T, d, E, k):
+    """The MXFP8 permute from bf16 x: row blocks of x (the oracle's quantiser) permuted, byte for
+    byte; rows with a per-row dynamic range and every d from one segment to ragged last ones."""
+    from expert_ffn_layer_top_amd import ops
+    from oracle import mxfp8
+    rng = np.random.default_rng(T + d + 2)
+    v = rng.standard_normal((T, d)).astype(np.float32) * np.exp(rng.standard_normal((T, 1)) * 3).astype(np.float32)
+    x = to_bf16_bits(v)
+    _, dest = _routing(T, E, k, T * 11)
+    note(f"permute quantising T={T} d={d} k={k}")
+    xpq, xps = ops.permute_quant_mx(bf16_to_dev(x), i32_to_dev(dest))
+    rq, rs = mxfp8.quantize_rows(x)
+    assert np.array_equal(host(xpq), moe.permute(rq, dest))
+    assert np.array_equal(host(xps), moe.permute(rs, dest))
+
+
+@pytest.mark.parametrize("T,d,E,k", SHAPES)
 def test_combine_and_backward(T, d, E, k):
     from expert_ffn_layer_top_amd import ops
     rng = np.random.default_rng(T * d)
