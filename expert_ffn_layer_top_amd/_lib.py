@@ -39,6 +39,8 @@ SIGNATURES = {
     "mxfp8_quantize_grouped_gated": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
     "mxfp8_quantize_rows_grouped": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p]),
     "moe_permute_quant_mx": (_i, [_p, _p, _i, _i, _i, _p, _p, _p]),
+    "mxfp8_quantize_gemm": (_i, [_p, _i, _i, _i, _p, _p, _p]),
+    "mxfp8_scales_to_gemm": (_i, [_p, _i, _i, _i, _p, _p]),
     "moe_mx_pad_cap": (_i, [_i, _i]),
     "moe_gg_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_grouped_gemm_swiglu": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,

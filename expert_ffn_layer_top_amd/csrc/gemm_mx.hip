@@ -36,6 +36,7 @@
 
 #include "common.h"
 #include "gemm_epilogue.h"
+#include "mx_common.h"
 #include "gemm_sched.h"
 
 namespace moe {
@@ -364,14 +365,16 @@ __device__ __forceinline__ TileSrc tile_src(const Params& p, const Tile& t, bool
   if (!role_b) {
     if constexpr (!Traits<MODE>::WGRAD) {
       const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
+      const int G = mx_gemm_group(K);
       const long long rem_rows = static_cast<long long>(p.n) - t.m0;
+      const long long sbeg = static_cast<long long>(t.m0) * G, send = static_cast<long long>(p.n) * (K / 32);
       s.r0 = make_rsrc(p.a0 + static_cast<long long>(t.m0) * K, rem_rows * K);
-      s.s0 = make_rsrc(p.a0s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
+      s.s0 = make_rsrc(p.a0s + sbeg, send - sbeg);
       s.r1 = s.r0;
       s.s1 = s.s0;
       if constexpr (MODE == DGRAD2) {
         s.r1 = make_rsrc(p.a1 + static_cast<long long>(t.m0) * K, rem_rows * K);
-        s.s1 = make_rsrc(p.a1s + static_cast<long long>(t.m0) * (K / 32), rem_rows * (K / 32));
+        s.s1 = make_rsrc(p.a1s + sbeg, send - sbeg);
       }
     } else {
       // [Mtot][P]: rows m0 .., columns from the expert's first padded position
@@ -391,10 +394,12 @@ __device__ __forceinline__ TileSrc tile_src(const Params& p, const Tile& t, bool
       const long long eoff = static_cast<long long>(t.e) * p.f * p.d;
       const long long esoff = static_cast<long long>(t.e) * p.f * (p.d / 32);
       const long long rows = p.f - t.n0;
+      const int G = mx_gemm_group(p.d);
+      const long long sbeg = static_cast<long long>(t.n0) * G, send = static_cast<long long>(p.f) * (p.d / 32);
       s.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
       s.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * p.d, rows * p.d);
-      s.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
-      s.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (p.d / 32), rows * (p.d / 32));
+      s.s0 = make_rsrc(p.b0s + esoff + sbeg, send - sbeg);
+      s.s1 = make_rsrc(p.b1s + esoff + sbeg, send - sbeg);
     } else if constexpr (!Traits<MODE>::WGRAD) {
       // weights [E][Ntot][K'] quantised along K' (K' = K, or f per half for DGRAD2)
       const int Ntot = n_total<MODE>(p);
@@ -402,13 +407,15 @@ __device__ __forceinline__ TileSrc tile_src(const Params& p, const Tile& t, bool
       const long long eoff = static_cast<long long>(t.e) * Ntot * K;
       const long long esoff = static_cast<long long>(t.e) * Ntot * (K / 32);
       const long long rows = Ntot - t.n0;
+      const int G = mx_gemm_group(K);
+      const long long sbeg = static_cast<long long>(t.n0) * G, send = static_cast<long long>(Ntot) * (K / 32);
       s.r0 = make_rsrc(p.b0 + eoff + static_cast<long long>(t.n0) * K, rows * K);
-      s.s0 = make_rsrc(p.b0s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
+      s.s0 = make_rsrc(p.b0s + esoff + sbeg, send - sbeg);
       s.r1 = s.r0;
       s.s1 = s.s0;
       if constexpr (MODE == DGRAD2) {
         s.r1 = make_rsrc(p.b1 + eoff + static_cast<long long>(t.n0) * K, rows * K);
-        s.s1 = make_rsrc(p.b1s + esoff + static_cast<long long>(t.n0) * (K / 32), rows * (K / 32));
+        s.s1 = make_rsrc(p.b1s + esoff + sbeg, send - sbeg);
       }
     } else {
       const int Ntot = n_total<MODE>(p);
@@ -435,7 +442,10 @@ __device__ __forceinline__ OpLoad op_load(const Params& p, bool role_b, int h) {
     ld.sstep = (BK / 32) * C;
   } else {
     const int K = (MODE == DGRAD2) ? p.f : k_total<MODE>(p);
-    op_offsets(role_b && MODE == FWD1 ? 0 : 128 * h, K, K / 32, ld);
+    const int G = mx_gemm_group(K);
+    op_offsets(role_b && MODE == FWD1 ? 0 : 128 * h, K, G, ld);
+    const int R = role_b ? (MODE == FWD1 ? p.f : n_total<MODE>(p)) : p.n;
+    ld.sstep = (BK / 32) * R;
   }
   return ld;
 }
@@ -701,7 +711,7 @@ int gg_mx_down(int E, int n, int d, int f, const int32_t* offsets, const uint16_
                const uint8_t* wds, uint16_t* yexp, uint8_t* ws, hipStream_t s) {
   uint8_t* aq = ws;
   uint8_t* as = ws + static_cast<size_t>(n) * f;
-  if (int st = mxfp8_quantize(a, 1, n, f, 0, 0, aq, as, s)) return st;
+  if (int st = mxfp8_quantize_gemm(a, 1, n, f, aq, as, s)) return st;
   gmx::Params q{};
   q.offsets = offsets; q.E = E; q.n = n; q.d = d; q.f = f;
   q.a0 = aq; q.a0s = as; q.b0 = wdq; q.b0s = wds; q.o0 = yexp;
@@ -781,7 +791,7 @@ int gg_mx_backward(int E, int n, int d, int f, const int32_t* offsets, const int
                    hipStream_t s) {
   const MxBwdLayout L(E, n, d, f);
   // dgrad through W_down: dYexp quantised along d
-  if (int st = mxfp8_quantize(dyexp, 1, n, d, 0, 0, ws + L.dyq, ws + L.dys, s)) return st;
+  if (int st = mxfp8_quantize_gemm(dyexp, 1, n, d, ws + L.dyq, ws + L.dys, s)) return st;
   if (int st = gg_mx_dgrad_down(E, n, d, f, offsets, ws + L.dyq, ws + L.dys, wdtq, wdts, g, u, dg, du, s)) return st;
   // wgrad of W_down: operands along grouped tokens
   if (int st = mxfp8_quantize_grouped(dyexp, nullptr, offsets, offsets_pad, E, n, d, ws + L.dyT, ws + L.dyTs, s)) return st;
@@ -789,8 +799,8 @@ int gg_mx_backward(int E, int n, int d, int f, const int32_t* offsets, const int
   if (int st = gg_mx_wgrad_down(E, n, d, f, offsets, offsets_pad, ws + L.dyT, ws + L.dyTs, ws + L.aT, ws + L.aTs, dwd, s))
     return st;
   // dgrad through W_gate, W_up: dG, dU quantised along f
-  if (int st = mxfp8_quantize(dg, 1, n, f, 0, 0, ws + L.dgq, ws + L.dgs, s)) return st;
-  if (int st = mxfp8_quantize(du, 1, n, f, 0, 0, ws + L.duq, ws + L.dus, s)) return st;
+  if (int st = mxfp8_quantize_gemm(dg, 1, n, f, ws + L.dgq, ws + L.dgs, s)) return st;
+  if (int st = mxfp8_quantize_gemm(du, 1, n, f, ws + L.duq, ws + L.dus, s)) return st;
   if (int st = gg_mx_dgrad_gate_up(E, n, d, f, offsets, ws + L.dgq, ws + L.dgs, ws + L.duq, ws + L.dus, wgtq, wgts,
                                    wutq, wuts, dxp, s))
     return st;

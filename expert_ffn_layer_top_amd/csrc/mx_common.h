@@ -12,6 +12,18 @@
 
 namespace moe {
 
+// Layout of the block scales the MXFP8 grouped GEMMs read for their forward and dgrad operands
+// (a K step of a 256-row tile needs 4 scale bytes of every row): a matrix of R rows quantised
+// along K (K/32 scale bytes per row) stores the byte of row r, block b at ((b / G) R + r) G + b % G
+// with G = 16 when K is a multiple of 512, 4 when of 128, else 1, i.e. [K/32G][R][G]: the scales
+// of G consecutive blocks of consecutive rows are one contiguous run, one cache line per 128 / G
+// rows, where row-major scales take a line per row.  Batched matrices lay out each one alone.
+__host__ __device__ __forceinline__ int mx_gemm_group(long long K) { return K % 512 == 0 ? 16 : (K % 128 == 0 ? 4 : 1); }
+__host__ __device__ __forceinline__ long long mx_gemm_scale_index(long long r, long long b, long long R, long long K) {
+  const int G = mx_gemm_group(K);
+  return ((b / G) * R + r) * G + (b % G);
+}
+
 // floor(log2(amax)) - 8 clamped to [-127, 127], from the magnitude bits of a bf16 amax
 // (amax_bits = max over the block of (bits & 0x7fff)).  Returns -127 for an all-zero block.
 // mode 1 (the rounded-up scale): the smallest power of two X with amax / X <= 448, i.e. one more

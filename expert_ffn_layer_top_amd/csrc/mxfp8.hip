@@ -16,9 +16,11 @@ namespace moe {
 namespace {
 
 // ---- rows: 4 lanes per 32-element block, 8 elements (16 bytes) per lane
+// gemm_rows > 0: the input is [batch][gemm_rows][cols] and the scales go out in the GEMM layout
+// (mx_gemm_scale_index) of each matrix; else row-major [.][cols/32].
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ in, long long total,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
-                                                         int mode) {
+                                                         int mode, int gemm_rows, int cols) {
   const long long g = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   const long long e0 = g * 8;
   const bool live = e0 < total;
@@ -40,7 +42,16 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   const uint32_t o0 = mx_encode4(w[0] & 0xffffu, w[0] >> 16, w[1] & 0xffffu, w[1] >> 16, sh);
   const uint32_t o1 = mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh);
   *reinterpret_cast<uint2*>(q + e0) = make_uint2(o0, o1);
-  if ((threadIdx.x & 3) == 0) scale[e0 / 32] = static_cast<uint8_t>(sh + 127);
+  if ((threadIdx.x & 3) == 0) {
+    long long si = e0 / 32;
+    if (gemm_rows > 0) {
+      const long long plane = static_cast<long long>(gemm_rows) * cols;
+      const long long bi = e0 / plane, rem = e0 - bi * plane;
+      const long long r = rem / cols;
+      si = bi * (plane / 32) + mx_gemm_scale_index(r, (rem - r * cols) / 32, gemm_rows, cols);
+    }
+    scale[si] = static_cast<uint8_t>(sh + 127);
+  }
 }
 
 // ---- transposed layouts: a tile of 128 (strided-dim) positions x 64 columns staged in LDS.
@@ -52,10 +63,14 @@ constexpr int kPitch = kTC + 2;  // LDS row pitch in bf16 (33 words: column read
 // writes 32 bytes of q and one scale byte.  Lanes 4c..4c+3 take the 4 blocks of column c, so
 // they write 128 contiguous bytes.  The scale of (column c, block b) goes to
 // scale[c * s_col + b * s_blk] (b counted from position 0; `scale` based at the tile's column 0).
+// With gemm_R > 0 the scales go out in the GEMM layout instead: `scale` based at the matrix, the
+// byte of column gemm_c0 + c and block b (of the strided dim's gemm_K positions) at
+// mx_gemm_scale_index(gemm_c0 + c, b, gemm_R, gemm_K).
 __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch], int ncols, long long pos0,
                                                    long long out_pitch, uint8_t* __restrict__ q,
                                                    uint8_t* __restrict__ scale, long long s_col, long long s_blk,
-                                                   int mode = 0) {
+                                                   int mode = 0, long long gemm_R = 0, long long gemm_K = 0,
+                                                   long long gemm_c0 = 0) {
   const int c = threadIdx.x >> 2;
   const int blk = threadIdx.x & 3;
   if (c >= ncols) return;
@@ -76,7 +91,9 @@ __device__ __forceinline__ void quant_tile_columns(const uint16_t (*tile)[kPitch
   uint8_t* dst = q + c * out_pitch + pos0 + blk * 32;
   reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
   reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  scale[c * s_col + (pos0 / 32 + blk) * s_blk] = static_cast<uint8_t>(sh + 127);
+  const long long si = gemm_R > 0 ? mx_gemm_scale_index(gemm_c0 + c, pos0 / 32 + blk, gemm_R, gemm_K)
+                                  : c * s_col + (pos0 / 32 + blk) * s_blk;
+  scale[si] = static_cast<uint8_t>(sh + 127);
 }
 
 // in [batch][rows][cols] -> q [batch][cols][rows], scale [batch][cols][rows/32]
@@ -191,13 +208,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         uint8_t* dst = q + b * plane + row * cols + c0 + 32 * blk;
         reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
         reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        scale[b * (plane / 32) + row * (cols / 32) + c0 / 32 + blk] = static_cast<uint8_t>(sh + 127);
+        scale[b * (plane / 32) + mx_gemm_scale_index(row, c0 / 32 + blk, rows, cols)] =
+            static_cast<uint8_t>(sh + 127);
       }
     }
     // column blocks, as the column quantiser
     if (r0 + (threadIdx.x & 3) * 32 < rows)
       quant_tile_columns(tile, kTC, r0, rows, qT + b * plane + static_cast<long long>(c0) * rows,
-                         scaleT + b * (plane / 32) + static_cast<long long>(c0) * (rows / 32), rows / 32, 1);
+                         scaleT + b * (plane / 32), 0, 0, 0, cols, rows, c0);
   }
 }
 
@@ -210,8 +228,9 @@ constexpr int kGroupTiles = 4;
 // With row_gate, grouped row r is bf16(row_gate[r] * in[row_token[r]]) (fp32 product, round to
 // nearest even): the rows the fused MXFP8 combine backward never writes in bf16.
 // q [C][n_pad_cap], scale [n_pad_cap/32][C].  With ROWS (contiguous rows, no gather, no gate), the
-// same tiles also give the real rows' row blocks: qr [n][C], sr [n][C/32], as mxfp8_quantize along
-// the rows, so a tensor both products need (dG, dU) is read once for its two layouts.
+// same tiles also give the real rows' row blocks: qr [n][C] and their scales sr in the GEMM layout
+// (mx_gemm_scale_index, R = n), so a tensor both products need (dG, dU) is read once for its two
+// layouts.
 // A workgroup takes a 128-position band and walks
 // kGroupTiles column tiles of it (the rows' adjacent 128-byte pieces, read close together in time,
 // with the next tile's loads in flight while the current one is quantised); the band's source
@@ -229,7 +248,8 @@ __device__ __forceinline__ void quant_grouped_body(const uint16_t* __restrict__ 
                                                             const int32_t* __restrict__ offsets_pad, int E, int C,
                                                             long long n_pad_cap, uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ scale, int band, int cgroup,
-                                                            uint8_t* __restrict__ qr, uint8_t* __restrict__ sr) {
+                                                            uint8_t* __restrict__ qr, uint8_t* __restrict__ sr,
+                                                            long long nrows) {
   __shared__ uint16_t tile[kTP][kPitch];
   __shared__ int s_off[257];
   __shared__ int s_offp[257];
@@ -308,7 +328,7 @@ __device__ __forceinline__ void quant_grouped_body(const uint16_t* __restrict__ 
           const uint32_t o1 = mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh);
           const int col = c0 + 8 * cc;
           *reinterpret_cast<uint2*>(qr + src[i] * C + col) = make_uint2(o0, o1);
-          if ((cc & 3) == 0) sr[src[i] * (C / 32) + col / 32] = static_cast<uint8_t>(sh + 127);
+          if ((cc & 3) == 0) sr[mx_gemm_scale_index(src[i], col / 32, nrows, C)] = static_cast<uint8_t>(sh + 127);
         }
       }
     }
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
                                                             uint8_t* __restrict__ scale, int bands_in_x) {
   quant_grouped_body<false>(in, row_token, row_gate, offsets, offsets_pad, E, C, n_pad_cap, q, scale,
                             bands_in_x ? blockIdx.x : blockIdx.y, bands_in_x ? blockIdx.y : blockIdx.x, nullptr,
-                            nullptr);
+                            nullptr, 0);
 }
 
 // The rows + grouped form runs at most two waves per SIMD (8% faster than the four its registers
@@ -343,10 +363,10 @@ __global__ __launch_bounds__(256) void quant_grouped_kernel(const uint16_t* __re
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void quant_rows_grouped_kernel(
     const uint16_t* __restrict__ in, const int32_t* __restrict__ offsets, const int32_t* __restrict__ offsets_pad,
     int E, int C, long long n_pad_cap, uint8_t* __restrict__ q, uint8_t* __restrict__ scale, int cgroups,
-    long long total, uint8_t* __restrict__ qr, uint8_t* __restrict__ sr) {
+    long long total, uint8_t* __restrict__ qr, uint8_t* __restrict__ sr, long long nrows) {
   const long long item = xcd_run_item(blockIdx.x, total);
   quant_grouped_body<true>(in, nullptr, nullptr, offsets, offsets_pad, E, C, n_pad_cap, q, scale,
-                           static_cast<int>(item / cgroups), static_cast<int>(item % cgroups), qr, sr);
+                           static_cast<int>(item / cgroups), static_cast<int>(item % cgroups), qr, sr, nrows);
 }
 
 }  // namespace
@@ -370,7 +390,7 @@ extern "C" int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols,
     MOE_REQUIRE(cols % 32 == 0, MOE_ERR_UNSUPPORTED, "axis 0 needs cols %% 32 == 0");
     const long long total = static_cast<long long>(batch) * rows * cols;
     quant_rows_kernel<<<static_cast<unsigned>((total / 8 + 255) / 256), 256, 0, s>>>(in, total, q, scale,
-                                                                                    scale_mode);
+                                                                                    scale_mode, 0, cols);
     return check_launch("mxfp8_quantize rows");
   }
   MOE_REQUIRE(axis == 1, MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
@@ -411,7 +431,7 @@ static int quantize_grouped(const uint16_t* in, const int32_t* row_token, const 
     const long long total = static_cast<long long>(bands) * cgroups;
     MOE_REQUIRE(total <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "too many tiles");
     quant_rows_grouped_kernel<<<static_cast<unsigned>(total), 256, 0, as_stream(stream)>>>(
-        in, offsets, offsets_pad, E, C, cap, qT, scaleT, cgroups, total, q_rows, s_rows);
+        in, offsets, offsets_pad, E, C, cap, qT, scaleT, cgroups, total, q_rows, s_rows, n);
   } else
     quant_grouped_kernel<<<grid, 256, 0, as_stream(stream)>>>(in, row_token, row_gate, offsets, offsets_pad, E, C, cap,
                                                                qT, scaleT, bands_in_x);
@@ -437,4 +457,44 @@ extern "C" int mxfp8_quantize_rows_grouped(const uint16_t* in, const int32_t* of
   MOE_CHECK_PTR(q_rows); MOE_CHECK_PTR(s_rows);
   MOE_CHECK_ALIGN(q_rows);
   return quantize_grouped(in, nullptr, nullptr, offsets, offsets_pad, E, n, C, qT, scaleT, stream, q_rows, s_rows);
+}
+
+extern "C" int mxfp8_quantize_gemm(const uint16_t* in, int batch, int rows, int cols, uint8_t* q, uint8_t* scale,
+                                   void* stream) {
+  MOE_CHECK_PTR(in); MOE_CHECK_PTR(q); MOE_CHECK_PTR(scale);
+  MOE_CHECK_ALIGN(in); MOE_CHECK_ALIGN(q);
+  MOE_REQUIRE(batch >= 1 && rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG, "sizes must be positive");
+  MOE_REQUIRE(cols % 32 == 0, MOE_ERR_UNSUPPORTED, "need cols %% 32 == 0");
+  const long long total = static_cast<long long>(batch) * rows * cols;
+  MOE_REQUIRE(total / 8 / 256 < 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "tensor too large");
+  quant_rows_kernel<<<static_cast<unsigned>((total / 8 + 255) / 256), 256, 0, as_stream(stream)>>>(in, total, q, scale,
+                                                                                                 0, rows, cols);
+  return check_launch("mxfp8_quantize_gemm");
+}
+
+namespace moe {
+namespace {
+// out[matrix][mx_gemm_scale_index(r, b, rows, K)] = in[matrix][r][b], one byte per thread.
+__global__ __launch_bounds__(256) void scales_to_gemm_kernel(const uint8_t* __restrict__ in, long long total, int rows,
+                                                             int K, uint8_t* __restrict__ out) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long per = static_cast<long long>(rows) * (K / 32);
+  const long long m = i / per, rem = i - m * per;
+  const long long r = rem / (K / 32), b = rem - r * (K / 32);
+  out[m * per + mx_gemm_scale_index(r, b, rows, K)] = in[i];
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int mxfp8_scales_to_gemm(const uint8_t* in, int batch, int rows, int K, uint8_t* out, void* stream) {
+  MOE_CHECK_PTR(in); MOE_CHECK_PTR(out);
+  MOE_REQUIRE(batch >= 1 && rows >= 1 && K >= 32, MOE_ERR_INVALID_ARG, "sizes must be positive");
+  MOE_REQUIRE(K % 32 == 0, MOE_ERR_UNSUPPORTED, "need K %% 32 == 0");
+  MOE_REQUIRE(in != out, MOE_ERR_INVALID_ARG, "in and out must not alias");
+  const long long total = static_cast<long long>(batch) * rows * (K / 32);
+  MOE_REQUIRE(total / 256 < 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "tensor too large");
+  scales_to_gemm_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, as_stream(stream)>>>(in, total, rows, K,
+                                                                                                  out);
+  return check_launch("mxfp8_scales_to_gemm");
 }

@@ -91,9 +91,9 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict_
   }
 }
 
-// MXFP8 permute straight from bf16 x: xpq[dest[t,j]] / xps[dest[t,j]] = the row blocks of x[t]
-// (E4M3 codes and E8M0 scales, as mxfp8_quantize along the rows), so the quantised rows go into
-// the expert buffers without a token-major quantised copy.  A 32-element block is 4 adjacent
+// MXFP8 permute straight from bf16 x: xpq[dest[t,j]] = the E4M3 row blocks of x[t], their E8M0
+// scales into xps in the GEMM layout (mx_gemm_scale_index, R = T k), so the quantised rows go into
+// the expert buffers, ready for the gate/up product, without a token-major quantised copy.  A 32-element block is 4 adjacent
 // lanes of the wave's 1 KiB segment (amax by two shuffles); each lane writes 8 codes per
 // destination and the block's first lane its scale byte.  d a multiple of 32.
 template <int KM>
@@ -119,12 +119,12 @@ __global__ __launch_bounds__(256) void permute_mx_kernel(const uint16_t* __restr
   const uint2 o = make_uint2(mx_encode4(w[0] & 0xffffu, w[0] >> 16, w[1] & 0xffffu, w[1] >> 16, sh),
                              mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh));
   const uint8_t sb = static_cast<uint8_t>(sh + 127);
-  const int sp = d / 32;
+  const long long n = static_cast<long long>(T) * k;
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     if (j < k) {
       *reinterpret_cast<uint2*>(xpq + static_cast<long long>(rows[j]) * d + e0) = o;
-      if ((it.c & 3) == 0) xps[static_cast<long long>(rows[j]) * sp + e0 / 32] = sb;
+      if ((it.c & 3) == 0) xps[mx_gemm_scale_index(rows[j], e0 / 32, n, d)] = sb;
     }
   }
 }
@@ -230,7 +230,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
 
 // The same with dyexp leaving as MXFP8 row blocks: the bf16 values bf16(gate[t,j] * dy[t]) are
 // formed in registers and quantised there (32-element blocks = 4 lanes, amax by shuffles), so
-// dyq / dys hold exactly what mxfp8_quantize gives for the bf16 rows, which are never written.
+// dyq holds exactly what mxfp8_quantize gives for the bf16 rows, which are never written, and dys
+// the same scales in the GEMM layout (mx_gemm_scale_index, R = T k) the down dgrad reads.
 // row_gate[dest[t,j]] = gate[t,j] lets the grouped quantiser rebuild the same rows from dy.
 template <int KM>
 __global__ __launch_bounds__(256) void combine_bwd_mx_kernel(const uint16_t* __restrict__ dy,
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(256) void combine_bwd_mx_kernel(const uint16_t* __r
   float g[KM], dot[KM];
   dest_rows<KM>(dest, t, k, rows);
   gates_of<KM>(gate, t, k, g);
+  const long long nrows = static_cast<long long>(T) * k;
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     dot[j] = 0.f;
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(256) void combine_bwd_mx_kernel(const uint16_t* __r
             const uint32_t hi = mx_encode4(w[2] & 0xffffu, w[2] >> 16, w[3] & 0xffffu, w[3] >> 16, sh);
             const long long r = rows[j];
             *reinterpret_cast<uint2*>(dyq + r * d + 8 * c) = make_uint2(lo, hi);
-            if ((lane & 3) == 0) dys[r * (d / 32) + c / 4] = static_cast<uint8_t>(sh + 127);
+            if ((lane & 3) == 0) dys[mx_gemm_scale_index(r, c / 4, nrows, d)] = static_cast<uint8_t>(sh + 127);
           }
         }
       }

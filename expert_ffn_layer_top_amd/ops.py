@@ -189,7 +189,8 @@ def permute(x, dest, x_scale=None):
 
 def permute_quant_mx(x, dest):
     """(xpq [n,d] E4M3, xps [n,d/32] E8M0): the row blocks of bf16 x permuted into the expert
-    buffers, as mxfp8_quantize(x, 0) followed by permute(.., x_scale=..), in one pass."""
+    buffers, as mxfp8_quantize(x, 0) followed by permute(.., x_scale=..), in one pass, with xps
+    in the GEMM scale layout (bytes rearranged) for the gate/up product."""
     _check(dest, torch.int32, "dest", ndim=2)
     T, k = dest.shape
     _check(x, torch.bfloat16, "x", (T, None))
@@ -236,7 +237,8 @@ def unpermute_combine_bwd(dy, yexp, topk_gate, dest):
 
 def unpermute_combine_bwd_mx(dy, yexp, topk_gate, dest):
     """(dyq [n,d] E4M3, dys [n,d/32] E8M0, row_gate [n] fp32, d_gate [T,k] fp32): the combine
-    backward with dyexp emitted only as MXFP8 row blocks (the bf16 rows are never written)."""
+    backward with dyexp emitted only as MXFP8 row blocks (the bf16 rows are never written); dys
+    in the GEMM scale layout (bytes rearranged) for the down dgrad."""
     T, d, k = _combine_bwd_args(dy, yexp, topk_gate, dest)
     _need(d % 32 == 0, f"dy: d = {d} must be a multiple of 32")
     n = T * k
@@ -295,7 +297,8 @@ def mxfp8_quantize(x, axis, scale_mode=0):
 
 def mxfp8_quantize_both(x):
     """x [..., R, C] bf16 (2-D or 3-D) -> (q, s) as mxfp8_quantize(x, 0) and (qT, sT) as
-    mxfp8_quantize(x, 1), from one read of x."""
+    mxfp8_quantize(x, 1), from one read of x; s and sT in the GEMM scale layout of each matrix
+    (shapes as the row-major scales, bytes rearranged): the weights' operands of the products."""
     _check(x, torch.bfloat16, "x")
     batch, R, C = _rc(x)
     _need(R % 32 == 0 and C % 64 == 0, "need rows % 32 == 0 and cols % 64 == 0")
@@ -343,10 +346,40 @@ def mxfp8_quantize_grouped(x, offsets, offsets_pad, n, row_token=None, row_gate=
     return q, s
 
 
+def mxfp8_quantize_gemm(x):
+    """Row blocks of x [..., R, C] bf16 as mxfp8_quantize(x, 0): (q [..., R, C], s) with s the
+    scales in the GEMM scale layout of each [R, C] matrix (shaped [..., R, C/32] like the row-major
+    scales, bytes rearranged): an operand of the MXFP8 forward and dgrad grouped GEMMs."""
+    _check(x, torch.bfloat16, "x")
+    _need(x.dim() >= 2, "x must have at least 2 dims")
+    R, C = x.shape[-2], x.shape[-1]
+    _need(C % 32 == 0, f"x: C = {C} must be a multiple of 32")
+    batch = x.numel() // (R * C)
+    _on_gpu(x)
+    q = _empty(tuple(x.shape), torch.uint8, x)
+    s = _empty(tuple(x.shape[:-1]) + (C // 32,), torch.uint8, x)
+    call("mxfp8_quantize_gemm", _ptr(x), batch, R, C, _ptr(q), _ptr(s), _stream(x))
+    return q, s
+
+
+def mxfp8_scales_to_gemm(s, K):
+    """Row-major E8M0 scales [..., R, K/32] rearranged into the GEMM scale layout of each [R, K]
+    matrix (same shape, bytes rearranged)."""
+    _check(s, torch.uint8, "s")
+    _need(s.dim() >= 2 and K % 32 == 0 and s.shape[-1] == K // 32, "s must be [..., R, K/32]")
+    R = s.shape[-2]
+    batch = s.numel() // (R * (K // 32))
+    _on_gpu(s)
+    out = _empty(tuple(s.shape), torch.uint8, s)
+    call("mxfp8_scales_to_gemm", _ptr(s), batch, R, K, _ptr(out), _stream(s))
+    return out
+
+
 def mxfp8_quantize_rows_grouped(x, offsets, offsets_pad):
     """Both MXFP8 layouts of a grouped [n, C] bf16 tensor from one read: (q [n, C], s [n, C/32])
-    row blocks as mxfp8_quantize(x, 0) and (qT [C, P], sT [P/32, C]) grouped token blocks as
-    mxfp8_quantize_grouped(x, offsets, offsets_pad, n)."""
+    row blocks as mxfp8_quantize(x, 0) with s in the GEMM scale layout (bytes rearranged), and
+    (qT [C, P], sT [P/32, C]) grouped token blocks as mxfp8_quantize_grouped(x, offsets,
+    offsets_pad, n)."""
     _check(offsets, torch.int32, "offsets", ndim=1)
     E = offsets.shape[0] - 1
     _need(E >= 1, "offsets must hold E + 1 >= 2 entries")

@@ -47,6 +47,12 @@
  *   w_gate, w_up [E,f,d] bf16; w_down [E,d,f] bf16 (output features first);
  *   xp, yexp, dyexp, dxp [n,d] bf16; g, u, a, dg, du [n,f] bf16;
  *   topk_idx, dest [T,k] int32; topk_gate, d_gate [T,k] fp32; counts [E]; offsets [E+1].
+ *   GEMM scale layout: the E8M0 scales of an MXFP8 operand of the forward and dgrad grouped
+ *   GEMMs -- a matrix of R rows quantised along K, one scale per row and 32-element block b --
+ *   are stored as [K/(32G)][R][G]: the byte of row r, block b at ((b / G) * R + r) * G + b % G,
+ *   G = 16 when K is a multiple of 512, 4 when of 128, else 1 (R * K/32 bytes either way;
+ *   batched matrices each laid out alone).  A product's K step then reads the scales of its
+ *   256-row tile as one contiguous run.  mxfp8_scales_to_gemm converts row-major scales.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -181,10 +187,12 @@ int moe_permute(int dtype, const void* x, const uint8_t* x_scale_or_null, const 
 
 /* MXFP8 permute straight from bf16 x ([news] "Routing work stays on the GPU" and "MXFP8 reduces
  * compute and memory costs": routed rows go straight into the expert buffers, here already as
- * 8-bit codes with a scale per 32-element block): xpq[dest[t,j]] and xps[dest[t,j]] are the row
- * blocks of x[t] -- byte-identical to mxfp8_quantize(x, axis 0, scale_mode 0) followed by
- * moe_permute(MOE_MXFP8, ...), without the token-major quantised copy.
- *   in  x [T,d] bf16, dest [T,k] int32;  out xpq [n,d] E4M3, xps [n,d/32] E8M0 (n = T*k).
+ * 8-bit codes with a scale per 32-element block): xpq[dest[t,j]] are the E4M3 row blocks of x[t]
+ * and xps their scales in the GEMM scale layout (R = n, K = d), ready for the gate/up product --
+ * the codes byte-identical to mxfp8_quantize(x, axis 0, scale_mode 0) followed by
+ * moe_permute(MOE_MXFP8, ...), the scales the same bytes rearranged, without the token-major
+ * quantised copy.
+ *   in  x [T,d] bf16, dest [T,k] int32;  out xpq [n,d] E4M3, xps (n*d/32 bytes) E8M0 (n = T*k).
  * Same shape rules and errors as moe_permute (d a positive multiple of 64, 1 <= k <= 16);
  * x and xpq 16-byte aligned. */
 int moe_permute_quant_mx(const uint16_t* x, const int32_t* dest, int T, int d, int k, uint8_t* xpq, uint8_t* xps,
@@ -206,8 +214,9 @@ int moe_unpermute_combine_bwd(const uint16_t* dy, const uint16_t* yexp, const fl
 
 /* The combine backward for MXFP8 backward products (fused producer): the rows of dyexp,
  * bf16(gate[t,j] * dy[t]), are formed in registers and leave only as MXFP8 row blocks along d,
- * byte-identical to mxfp8_quantize(dyexp, axis 0) of the bf16 rows, which are never written.
- *   out  dyexp_q [n,d] E4M3, dyexp_scale [n,d/32] E8M0, row_gate [n] fp32 (row_gate[dest[t,j]] =
+ * byte-identical to mxfp8_quantize(dyexp, axis 0) of the bf16 rows, which are never written
+ * (the scales in the GEMM scale layout, R = n, K = d, for the down dgrad).
+ *   out  dyexp_q [n,d] E4M3, dyexp_scale (n*d/32 bytes) E8M0, row_gate [n] fp32 (row_gate[dest[t,j]] =
  *        gate[t,j], for mxfp8_quantize_grouped_gated), d_gate [T,k] fp32 as
  *        moe_unpermute_combine_bwd.  Shapes and alignment as moe_unpermute_combine_bwd. */
 int moe_unpermute_combine_bwd_mx(const uint16_t* dy, const uint16_t* yexp, const float* topk_gate,
@@ -239,11 +248,12 @@ int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int 
 int mxfp8_quantize(const uint16_t* in, int batch, int rows, int cols, int axis, int scale_mode,
                    uint8_t* q, uint8_t* scale, void* stream);
 
-/* Both mxfp8_quantize layouts of one input from a single read of it: q/scale as axis 0 and
- * qT/scaleT as axis 1, bit-identical to the two separate calls.  For the expert weights, which
- * the forward and the dgrad products need quantised along each of their two dims
- * ([news] "MXFP8 reduces compute and memory costs").  rows % 32 == 0 and cols % 64 == 0
- * (MOE_ERR_UNSUPPORTED otherwise); in, q, qT 16-byte aligned; outputs as for mxfp8_quantize. */
+/* Both mxfp8_quantize layouts of one input from a single read of it: q as axis 0 and qT as axis 1,
+ * bit-identical to the two separate calls, with the scales in the GEMM scale layout of each
+ * matrix (scale: R = rows, K = cols; scaleT: R = cols, K = rows; the same bytes as the separate
+ * calls' scales, rearranged).  For the expert weights, which the forward and the dgrad products
+ * need quantised along each of their two dims ([news] "MXFP8 reduces compute and memory costs").
+ * rows % 32 == 0 and cols % 64 == 0 (MOE_ERR_UNSUPPORTED otherwise); in, q, qT 16-byte aligned. */
 int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int cols, uint8_t* q, uint8_t* scale,
                         uint8_t* qT, uint8_t* scaleT, void* stream);
 
@@ -274,14 +284,28 @@ int mxfp8_quantize_grouped_gated(const uint16_t* in, const int32_t* row_token, c
 /* Both MXFP8 layouts of a grouped [n, C] bf16 tensor from one read ([news] "MXFP8 reduces compute
  * and memory costs": the expert products run on 8-bit operands with a scale per small block; the
  * backward's dG and dU feed one product contracting over C and one contracting over tokens):
- *   q_rows [n, C] E4M3 + s_rows [n, C/32] E8M0: row blocks, byte-identical to
- *     mxfp8_quantize(in, 1, n, C, axis 0, scale_mode 0);
+ *   q_rows [n, C] E4M3 + s_rows (n*C/32 bytes) E8M0: row blocks as
+ *     mxfp8_quantize(in, 1, n, C, axis 0, scale_mode 0), the scales in the GEMM scale layout
+ *     (R = n, K = C);
  *   qT, scaleT: the grouped token blocks, byte-identical to mxfp8_quantize_grouped(in, NULL, ...).
  * Same requirements and errors as mxfp8_quantize_grouped (C a multiple of 64, 1 <= E <= 256),
  * plus q_rows and s_rows non-NULL and q_rows 16-byte aligned. */
 int mxfp8_quantize_rows_grouped(const uint16_t* in, const int32_t* offsets, const int32_t* offsets_pad, int E,
                                 int n, int C, uint8_t* q_rows, uint8_t* s_rows, uint8_t* qT, uint8_t* scaleT,
                                 void* stream);
+
+/* Row blocks of in [batch][rows][cols] as mxfp8_quantize axis 0 (scale_mode 0), the scales in the
+ * GEMM scale layout of each matrix (R = rows, K = cols): an operand of the MXFP8 forward and dgrad
+ * grouped GEMMs ([news] "MXFP8 reduces compute and memory costs").  cols % 32 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise); in and q 16-byte aligned. */
+int mxfp8_quantize_gemm(const uint16_t* in, int batch, int rows, int cols, uint8_t* q, uint8_t* scale,
+                        void* stream);
+
+/* Row-major E8M0 scales in [batch][rows][K/32] (mxfp8_quantize axis 0, or axis 1 with rows and K
+ * the transposed output's) rearranged into the GEMM scale layout; for callers that quantise with
+ * mxfp8_quantize or permute with moe_permute and then call the MXFP8 grouped GEMMs.  K % 32 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise); in and out must not alias. */
+int mxfp8_scales_to_gemm(const uint8_t* in, int batch, int rows, int K, uint8_t* out, void* stream);
 
 /* Length of the padded token axis used by mxfp8_quantize_grouped and the MXFP8 backward. */
 int moe_mx_pad_cap(int n, int E);
@@ -298,8 +322,10 @@ size_t moe_gg_workspace_bytes(int dtype, int E, int n, int d, int f);
  *   g = xp W_gate[e]^T, u = xp W_up[e]^T, a = silu(g) * u  (stored bf16; a from fp32 g, u),
  *   yexp = a W_down[e]^T.
  * dtype MOE_BF16:  xp, w_* bf16; all *_scale NULL.
- * dtype MOE_MXFP8: xp [n,d] E4M3 + xp_scale [n,d/32]; w_gate, w_up [E,f,d] E4M3 + scales
- *   [E,f,d/32]; w_down [E,d,f] E4M3 + scale [E,d,f/32] (all blocks along the contraction dim).
+ * dtype MOE_MXFP8: xp [n,d] E4M3 + xp_scale; w_gate, w_up [E,f,d] E4M3 + scales; w_down [E,d,f]
+ *   E4M3 + scale (all blocks along the contraction dim; every scale in the GEMM scale layout:
+ *   xp_scale R = n, K = d; each expert's w_gate / w_up scales R = f, K = d, w_down's R = d,
+ *   K = f, as mxfp8_quantize_both writes them).
  *   a is quantised (rows, blocks along f) into the workspace before the second product.
  * Outputs g, u, a [n,f], yexp [n,d] bf16. */
 int moe_grouped_gemm_swiglu(int dtype, int E, int n, int d, int f, const int32_t* offsets,
@@ -333,9 +359,10 @@ int moe_grouped_gemm_down(int dtype, int E, int n, int d, int f, const int32_t* 
  * dtype MOE_BF16: x_rows = xp [n,d] bf16 (row_token NULL); w_* are the forward weights (bf16).
  * dtype MOE_MXFP8: x_rows = x [T,d] bf16 read through row_token (the token of each row);
  *   w_gate_t, w_up_t [E,d,f] and w_down_t [E,f,d] are the weights quantised along the dgrad
- *   contraction (mxfp8_quantize axis 1 per expert), with scales [E,d,f/32], [E,f,d/32];
- *   dyexp, dg|du are quantised along rows, and xp, a, dyexp, dg, du along grouped tokens
- *   (offsets_pad, pad 32), into the workspace.
+ *   contraction (mxfp8_quantize_both's qT per expert), with their scales in the GEMM scale
+ *   layout (R = d, K = f; R = f, K = d); dyexp, dg|du are quantised along rows (GEMM-layout
+ *   scales), and xp, a, dyexp, dg, du along grouped tokens (offsets_pad, pad 32), into the
+ *   workspace.
  * Outputs dg, du [n,f], dxp [n,d], dw_gate, dw_up [E,f,d], dw_down [E,d,f], all bf16. */
 int moe_grouped_gemm_swiglu_bwd(int dtype, int E, int n, int d, int f, const int32_t* offsets,
                                 const int32_t* offsets_pad_or_null,
@@ -354,12 +381,13 @@ int moe_grouped_gemm_swiglu_bwd(int dtype, int E, int n, int d, int f, const int
  *
  * dgrad_down:    dg, du [n,f] from dyexp and the SwiGLU backward of (g, u) as above.
  *   bf16: dyexp [n,d], w_down_t = the forward W_down [E,d,f]; scales NULL.
- *   MXFP8: dyexp [n,d] E4M3 + dyexp_scale [n,d/32] (row blocks along d); w_down_t [E,f,d] E4M3 +
- *   scale [E,f,d/32] (mxfp8_quantize axis 1 of W_down).
+ *   MXFP8: dyexp [n,d] E4M3 + dyexp_scale (row blocks along d; GEMM scale layout, R = n, K = d);
+ *   w_down_t [E,f,d] E4M3 + scale (W_down quantised along d: mxfp8_quantize_both's qT / scaleT).
  * wgrad_down:    dw_down [E,d,f] = dyexp_e^T a_e.
  * dgrad_gate_up: dxp [n,d] = dg W_gate[e] + du W_up[e].
  *   bf16: dg, du [n,f]; w_gate_t, w_up_t = the forward weights [E,f,d]; scales NULL.
- *   MXFP8: dg, du [n,f] E4M3 + scales [n,f/32]; w_gate_t, w_up_t [E,d,f] E4M3 + [E,d,f/32].
+ *   MXFP8: dg, du [n,f] E4M3 + scales (GEMM scale layout, R = n, K = f); w_gate_t, w_up_t
+ *   [E,d,f] E4M3 + scales (GEMM scale layout per expert, R = d, K = f).
  * wgrad_gate_up: dw_gate, dw_up [E,f,d] = dg_e^T xp_e, du_e^T xp_e.
  *   The wgrad operands ("*_t") are token-major:
  *   bf16: the row tensors themselves (dyexp [n,d], a [n,f], dg, du [n,f], xp [n,d]);

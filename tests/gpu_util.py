@@ -65,3 +65,21 @@ def assert_close(out, ref, tol, what):
     e = rel_err(out, ref)
     assert e <= tol, f"{what}: max-rel-to-norm error {e:.3e} > {tol:.1e}"
     return e
+
+
+def gemm_group(K):
+    """Bytes per run of the MXFP8 GEMM scale layout for contraction length K."""
+    return 16 if K % 512 == 0 else (4 if K % 128 == 0 else 1)
+
+
+def gemm_scales_to_rows(s, R, K):
+    """Host: the GEMM scale layout of one or more [R, K] matrices back to row-major [..., R, K/32]
+    (byte (r, b) of a matrix sits at ((b / G) R + r) G + b % G of its R * K/32 bytes).  Leading
+    dims are kept when s is shaped [..., R, K/32] (as the bindings return it)."""
+    s = np.ascontiguousarray(s)
+    G, nb = gemm_group(K), K // 32
+    if s.ndim >= 2 and s.shape[-2:] == (R, nb):
+        lead = s.shape[:-2]
+    else:
+        lead = () if s.size == R * nb else (s.size // (R * nb),)
+    return s.reshape(-1, nb // G, R, G).transpose(0, 2, 1, 3).reshape(lead + (R, nb))

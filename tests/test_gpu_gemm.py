@@ -102,6 +102,20 @@ def deq_w(q, s):
     return mxfp8.dequantize_blocks(host(q), host(s))
 
 
+def gemm_weights(ops, Wd):
+    """The experts' weights quantised for the MX products along each dim: Q with row-major
+    scales (mxfp8_quantize, for the oracle) and QG with the same scales in the GEMM scale layout
+    (the products' operands); "_t" = quantised along the weight's rows (the dgrad direction)."""
+    Q, QG = {}, {}
+    for w in ("wg", "wu", "wd"):
+        Q[w] = ops.mxfp8_quantize(Wd[w], 0)
+        Q[w + "_t"] = ops.mxfp8_quantize(Wd[w], 1)
+        R, C = Wd[w].shape[1], Wd[w].shape[2]
+        QG[w] = (Q[w][0], ops.mxfp8_scales_to_gemm(Q[w][1], C))
+        QG[w + "_t"] = (Q[w + "_t"][0], ops.mxfp8_scales_to_gemm(Q[w + "_t"][1], R))
+    return Q, QG
+
+
 MX_CASES = [
     dict(T=600, d=512, E=5, k=2, f=384, seed=11, empty=(2,)),
     dict(T=300, d=256, E=4, k=2, f=256, seed=12, hot=0),
@@ -130,11 +144,10 @@ def test_grouped_gemm_mxfp8_forward_backward(case):
     assert np.array_equal(host(xq), rq) and np.array_equal(host(xs), rs)
     dest_d = i32_to_dev(p["dest"])
     xpq, xps = ops.permute(xq, dest_d, x_scale=xs)
+    xps_g = ops.mxfp8_scales_to_gemm(xps, p["d"])             # the products read GEMM-layout scales
     Wd = {w: bf16_to_dev(p[w]) for w in ("wg", "wu", "wd")}
-    Q = {}
+    Q, QG = gemm_weights(ops, Wd)
     for w in ("wg", "wu", "wd"):
-        Q[w] = ops.mxfp8_quantize(Wd[w], 0)
-        Q[w + "_t"] = ops.mxfp8_quantize(Wd[w], 1)
         fq, fs = mxfp8.quantize_rows(p[w])
         assert np.array_equal(host(Q[w][0]), fq) and np.array_equal(host(Q[w][1]), fs)
         tq, ts = mxfp8.quantize_cols(p[w])
@@ -142,8 +155,8 @@ def test_grouped_gemm_mxfp8_forward_backward(case):
     off_d = i32_to_dev(p["off"])
 
     note(f"gg mxfp8 fwd {case}")
-    g, u, a, yexp = ops.grouped_gemm_swiglu(xpq, off_d, Q["wg"][0], Q["wu"][0], Q["wd"][0],
-                                            scales=(xps, Q["wg"][1], Q["wu"][1], Q["wd"][1]))
+    g, u, a, yexp = ops.grouped_gemm_swiglu(xpq, off_d, QG["wg"][0], QG["wu"][0], QG["wd"][0],
+                                            scales=(xps_g, QG["wg"][1], QG["wu"][1], QG["wd"][1]))
     Xd = mxfp8.dequantize_blocks(host(xpq), host(xps))
     G, U, A = moe.expert_gate_up(Xd, p["off"], deq_w(*Q["wg"]), deq_w(*Q["wu"]))
     assert_close(codecs.bf16_to_f64(bits(g)), G, MX_TOL, "G (MX)")
@@ -155,8 +168,8 @@ def test_grouped_gemm_mxfp8_forward_backward(case):
 
     note(f"gg mxfp8 bwd {case}")
     offp_d = i32_to_dev(p["offp"])
-    out = ops.grouped_gemm_swiglu_bwd(x_d, g, u, a, bf16_to_dev(p["dyexp"]), off_d, Q["wg_t"][0], Q["wu_t"][0],
-                                      Q["wd_t"][0], scales=(Q["wg_t"][1], Q["wu_t"][1], Q["wd_t"][1]),
+    out = ops.grouped_gemm_swiglu_bwd(x_d, g, u, a, bf16_to_dev(p["dyexp"]), off_d, QG["wg_t"][0], QG["wu_t"][0],
+                                      QG["wd_t"][0], scales=(QG["wg_t"][1], QG["wu_t"][1], QG["wd_t"][1]),
                                       offsets_pad=offp_d, row_token=i32_to_dev(p["row_token"]))
     dyq, dys = mxfp8.quantize_rows(p["dyexp"])
     dA = moe.expert_down(mxfp8.dequantize_blocks(dyq, dys), p["off"], deq_w(*Q["wd_t"]))
@@ -211,12 +224,8 @@ def test_backward_per_kernel_calls_match_composite(mx):
         dwg, dwu = ops.grouped_gemm_wgrad_gate_up(dg, du, xp_d, off_d, n)
     else:
         x_d = bf16_to_dev(p["x"])
-        xq, xs = ops.mxfp8_quantize(x_d, 0)
-        xpq, xps = ops.permute(xq, i32_to_dev(p["dest"]), x_scale=xs)
-        Q = {}
-        for w in ("wg", "wu", "wd"):
-            Q[w] = ops.mxfp8_quantize(Wd[w], 0)
-            Q[w + "_t"] = ops.mxfp8_quantize(Wd[w], 1)
+        xpq, xps = ops.permute_quant_mx(x_d, i32_to_dev(p["dest"]))
+        _, Q = gemm_weights(ops, Wd)
         g, u, a, _ = ops.grouped_gemm_swiglu(xpq, off_d, Q["wg"][0], Q["wu"][0], Q["wd"][0],
                                              scales=(xps, Q["wg"][1], Q["wu"][1], Q["wd"][1]))
         offp_d = i32_to_dev(p["offp"])
@@ -224,13 +233,13 @@ def test_backward_per_kernel_calls_match_composite(mx):
         ref = ops.grouped_gemm_swiglu_bwd(x_d, g, u, a, dy_d, off_d, Q["wg_t"][0], Q["wu_t"][0], Q["wd_t"][0],
                                           scales=(Q["wg_t"][1], Q["wu_t"][1], Q["wd_t"][1]),
                                           offsets_pad=offp_d, row_token=rt_d)
-        dyq, dys = ops.mxfp8_quantize(dy_d, 0)
+        dyq, dys = ops.mxfp8_quantize_gemm(dy_d)
         dg, du = ops.grouped_gemm_dgrad_down(dyq, off_d, Q["wd_t"][0], g, u, scales=(dys, Q["wd_t"][1]))
         dyT, dyTs = ops.mxfp8_quantize_grouped(dy_d, off_d, offp_d, n)
         aT, aTs = ops.mxfp8_quantize_grouped(a, off_d, offp_d, n)
         dwd = ops.grouped_gemm_wgrad_down(dyT, aT, off_d, n, offsets_pad=offp_d, scales=(dyTs, aTs))
-        dgq, dgs = ops.mxfp8_quantize(dg, 0)
-        duq, dus = ops.mxfp8_quantize(du, 0)
+        dgq, dgs = ops.mxfp8_quantize_gemm(dg)
+        duq, dus = ops.mxfp8_quantize_gemm(du)
         dxp = ops.grouped_gemm_dgrad_gate_up(dgq, duq, off_d, Q["wg_t"][0], Q["wu_t"][0],
                                              scales=(dgs, dus, Q["wg_t"][1], Q["wu_t"][1]))
         dgT, dgTs = ops.mxfp8_quantize_grouped(dg, off_d, offp_d, n)
@@ -280,13 +289,9 @@ def test_mxfp8_few_workgroups_bit_identical(case, monkeypatch):
     from expert_ffn_layer_top_amd import ops
     p = problem(**case)
     x_d = bf16_to_dev(p["x"])
-    xq, xs = ops.mxfp8_quantize(x_d, 0)
-    xpq, xps = ops.permute(xq, i32_to_dev(p["dest"]), x_scale=xs)
+    xpq, xps = ops.permute_quant_mx(x_d, i32_to_dev(p["dest"]))
     Wd = {w: bf16_to_dev(p[w]) for w in ("wg", "wu", "wd")}
-    Q = {}
-    for w in ("wg", "wu", "wd"):
-        Q[w] = ops.mxfp8_quantize(Wd[w], 0)
-        Q[w + "_t"] = ops.mxfp8_quantize(Wd[w], 1)
+    _, Q = gemm_weights(ops, Wd)
     off_d = i32_to_dev(p["off"])
     offp_d = i32_to_dev(p["offp"])
     rt_d = i32_to_dev(p["row_token"])

@@ -7,7 +7,7 @@ import pytest
 
 from oracle import codecs, moe, mxfp8
 from synth import to_bf16_bits
-from tests.gpu_util import bf16_to_dev, host, i32_to_dev, note
+from tests.gpu_util import bf16_to_dev, gemm_scales_to_rows, host, i32_to_dev, note, u8_to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -101,8 +101,25 @@ def test_rows_and_cols_from_one_read(B, R, C):
     q, s, qT, sT = ops.mxfp8_quantize_both(bf16_to_dev(x))
     rq, rs = mxfp8.quantize_rows(x)
     cq, cs = mxfp8.quantize_cols(x)
-    assert np.array_equal(host(s), rs) and np.array_equal(host(q), rq)
-    assert np.array_equal(host(sT), cs) and np.array_equal(host(qT), cq)
+    # scales in the GEMM scale layout of each matrix (R = rows, K = cols; transposed: R = cols, K = rows)
+    assert np.array_equal(gemm_scales_to_rows(host(s), R, C), rs) and np.array_equal(host(q), rq)
+    assert np.array_equal(gemm_scales_to_rows(host(sT), C, R), cs) and np.array_equal(host(qT), cq)
+
+
+@pytest.mark.parametrize("B,R,C", [(1, 32, 64), (3, 100, 128), (2, 257, 512), (1, 96, 7168), (4, 40, 2048)])
+def test_gemm_scale_layout_producers(B, R, C):
+    """Row blocks with GEMM-layout scales (mxfp8_quantize_gemm) and the conversion of row-major
+    scales into that layout (mxfp8_scales_to_gemm), against the oracle's row blocks."""
+    from expert_ffn_layer_top_amd import ops
+    rng = np.random.default_rng(B * R + C)
+    v = rng.standard_normal((B, R, C)).astype(np.float32) * np.exp(rng.standard_normal((B, R, 1)) * 3).astype(np.float32)
+    x = to_bf16_bits(v)
+    note(f"mxfp8 gemm-layout scales B={B} R={R} C={C}")
+    q, s = ops.mxfp8_quantize_gemm(bf16_to_dev(x))
+    rq, rs = mxfp8.quantize_rows(x)
+    assert np.array_equal(host(q), rq) and np.array_equal(gemm_scales_to_rows(host(s), R, C), rs)
+    s2 = ops.mxfp8_scales_to_gemm(u8_to_dev(rs), C)
+    assert np.array_equal(host(s2), host(s))
 
 
 @pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
@@ -121,7 +138,7 @@ def test_rows_and_grouped_from_one_read(T, E, k, C):
     note(f"mxfp8 rows+grouped T={T} E={E} k={k} C={C}")
     q, s, qT, sT = ops.mxfp8_quantize_rows_grouped(bf16_to_dev(xp), i32_to_dev(off), i32_to_dev(offp))
     rq, rs = mxfp8.quantize_rows(xp)
-    assert np.array_equal(host(q), rq) and np.array_equal(host(s), rs)
+    assert np.array_equal(host(q), rq) and np.array_equal(gemm_scales_to_rows(host(s), n, C), rs)
     gq, gs = mxfp8.quantize_grouped(xp, off, offp)
     qT, sT = host(qT), host(sT).T
     assert np.array_equal(qT[:, : offp[E]], gq) and np.array_equal(sT[:, : offp[E] // 32], gs)

@@ -6,8 +6,8 @@ import pytest
 
 from oracle import codecs, moe
 from synth import to_bf16_bits
-from tests.gpu_util import (BF16_TOL, assert_close, bf16_to_dev, bits, f32_to_dev, host, i32_to_dev, note,
-                            u8_to_dev)
+from tests.gpu_util import (BF16_TOL, assert_close, bf16_to_dev, bits, f32_to_dev, gemm_scales_to_rows, host,
+                            i32_to_dev, note, u8_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,8 @@ def test_permute_quantising_bitexact(T, d, E, k):
     xpq, xps = ops.permute_quant_mx(bf16_to_dev(x), i32_to_dev(dest))
     rq, rs = mxfp8.quantize_rows(x)
     assert np.array_equal(host(xpq), moe.permute(rq, dest))
-    assert np.array_equal(host(xps), moe.permute(rs, dest))
+    # scales in the GEMM scale layout (R = T k, K = d)
+    assert np.array_equal(gemm_scales_to_rows(host(xps), T * k, d), moe.permute(rs, dest))
 
 
 @pytest.mark.parametrize("T,d,E,k", SHAPES)
@@ -138,7 +139,8 @@ def test_combine_bwd_fused_mxfp8_producer(T, d, E, k):
     dyexp, dgate = ops.unpermute_combine_bwd(dy_d, ye_d, g_d, dest_d)
     rq, rs = ops.mxfp8_quantize(dyexp, 0)
     dyq, dys, row_gate, dgate_mx = ops.unpermute_combine_bwd_mx(dy_d, ye_d, g_d, dest_d)
-    assert torch.equal(dyq, rq) and torch.equal(dys, rs)
+    # dys: the same scales in the GEMM scale layout
+    assert torch.equal(dyq, rq) and torch.equal(dys, ops.mxfp8_scales_to_gemm(rs, d))
     assert torch.equal(dgate_mx, dgate)
     rg = host(row_gate)
     assert np.array_equal(rg[dest.ravel()], gate.astype(np.float32).ravel())

@@ -16,7 +16,7 @@ import pytest
 
 import synth
 from oracle import codecs, moe, mxfp8, sampled
-from tests.gpu_util import BF16_TOL, MX_TOL, assert_close, bits, host, note, rel_err
+from tests.gpu_util import BF16_TOL, MX_TOL, assert_close, bits, gemm_group, gemm_scales_to_rows, host, note, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +25,18 @@ def _dev_rows(t, rows):
     """Rows of a device tensor, gathered on the device (only the sample crosses to the host)."""
     import torch
     return t[torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)]
+
+
+def _gemm_scale_rows(t, rows, R, K):
+    """Row-major scale rows [len(rows), K/32] of a device tensor holding R rows' scales in the GEMM
+    scale layout (byte (r, b) at ((b / G) R + r) G + b % G), gathered on the device."""
+    import torch
+    G, nb = gemm_group(K), K // 32
+    r = np.asarray(rows, dtype=np.int64)[:, None]
+    b = np.arange(nb, dtype=np.int64)[None, :]
+    idx = ((b // G) * R + r) * G + b % G
+    flat = t.reshape(-1)
+    return host(flat[torch.as_tensor(idx.ravel(), device=t.device)]).reshape(len(rows), nb)
 
 
 def _rows_bits(t, rows):
@@ -214,7 +226,8 @@ def test_mxfp8_full_size():
     # bit on sampled rows
     chosen, _ = _chosen_experts(counts)
     rows, experts = _sample_rows(off, chosen, rng, 48, pool=chosen)
-    xpq_r, xps_r = host(_dev_rows(ctx["xpq"], rows)), host(_dev_rows(ctx["xps"], rows))
+    n = cfg.T * cfg.k
+    xpq_r, xps_r = host(_dev_rows(ctx["xpq"], rows)), _gemm_scale_rows(ctx["xps"], rows, n, cfg.d)
     rq, rs = mxfp8.quantize_rows(x[row_token[rows]])
     assert np.array_equal(xpq_r, rq) and np.array_equal(xps_r, rs)
 
@@ -224,7 +237,8 @@ def test_mxfp8_full_size():
     for e in chosen:
         for name, src, axis in (("wg", "w_gate", 0), ("wu", "w_up", 0), ("wd", "w_down", 0),
                                 ("wg_t", "w_gate", 1), ("wu_t", "w_up", 1), ("wd_t", "w_down", 1)):
-            bq, bs = host(q[name][e]), host(q[name + "_s"][e])
+            bq = host(q[name][e])
+            bs = gemm_scales_to_rows(host(q[name + "_s"][e]), bq.shape[0], bq.shape[1])   # GEMM layout
             ref = mxfp8.quantize_rows(inputs[src][e]) if axis == 0 else mxfp8.quantize_cols(inputs[src][e])
             assert np.array_equal(bq, ref[0]) and np.array_equal(bs, ref[1]), f"{name}[{e}]"
             deq[name, e] = mxfp8.dequantize_blocks(bq, bs)
@@ -256,7 +270,8 @@ def test_mxfp8_full_size():
     assert np.array_equal(host(out["row_gate"])[dest.ravel()], host(ctx["topk_gate"]).ravel())
     dy_r = _dyexp_rows(inputs, ctx, out, dest, rows)
     dyq_r, dys_r = mxfp8.quantize_rows(dy_r)
-    assert np.array_equal(host(_dev_rows(mx["dyq"], rows)), dyq_r) and np.array_equal(host(_dev_rows(mx["dys"], rows)), dys_r)
+    assert np.array_equal(host(_dev_rows(mx["dyq"], rows)), dyq_r)
+    assert np.array_equal(_gemm_scale_rows(mx["dys"], rows, n, cfg.d), dys_r)
     dA = per_expert(lambda e, m: m @ deq["wd_t", e].T, mxfp8.dequantize_blocks(dyq_r, dys_r), cfg.f)
     dG, dU = moe.swiglu_bwd(dA, _f64(g_r), _f64(u_r))
     dg_r, du_r = _rows_bits(out["dg"], rows), _rows_bits(out["du"], rows)
@@ -264,7 +279,9 @@ def test_mxfp8_full_size():
     assert_close(_f64(du_r), dU, MX_TOL, "dU rows (MX)")
     dgq, dgs = mxfp8.quantize_rows(dg_r)
     duq, dus = mxfp8.quantize_rows(du_r)
-    assert np.array_equal(host(_dev_rows(mx["dgq"], rows)), dgq) and np.array_equal(host(_dev_rows(mx["dus"], rows)), dus)
+    assert np.array_equal(host(_dev_rows(mx["dgq"], rows)), dgq) and np.array_equal(host(_dev_rows(mx["duq"], rows)), duq)
+    assert np.array_equal(_gemm_scale_rows(mx["dgs"], rows, n, cfg.f), dgs)
+    assert np.array_equal(_gemm_scale_rows(mx["dus"], rows, n, cfg.f), dus)
     dX = (per_expert(lambda e, m: m @ deq["wg_t", e].T, mxfp8.dequantize_blocks(dgq, dgs), cfg.d)
           + per_expert(lambda e, m: m @ deq["wu_t", e].T, mxfp8.dequantize_blocks(duq, dus), cfg.d))
     assert_close(_f64(_rows_bits(out["dxp"], rows)), dX, MX_TOL, "dXp rows (MX, chained)")
