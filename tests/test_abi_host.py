@@ -112,6 +112,13 @@ def test_argument_checks_return_status_without_launching():
     assert L.mxfp8_quantize_both(fake, 1, 48, 64, fake, fake, fake, fake, None) == UNSUPPORTED
     assert L.mxfp8_quantize_both(fake, 1, 64, 96, fake, fake, fake, fake, None) == UNSUPPORTED
     assert L.mxfp8_quantize_both(fake, 1, 64, 64, fake, None, fake, fake, None) == INVALID
+    # GEMM-layout quantiser and scale conversion: blocked dim % 32, pointers, no aliasing
+    assert L.mxfp8_quantize_gemm(fake, 1, 8, 48, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp8_quantize_gemm(fake, 1, 8, 64, fake, None, None) == INVALID
+    assert L.mxfp8_quantize_gemm(fake, 0, 8, 64, fake, fake, None) == INVALID
+    assert L.mxfp8_scales_to_gemm(fake, 1, 8, 48, ctypes.c_void_p(0x2000), None) == UNSUPPORTED
+    assert L.mxfp8_scales_to_gemm(fake, 1, 8, 64, fake, None) == INVALID
+    assert L.mxfp8_scales_to_gemm(fake, 1, 8, 64, None, None) == INVALID
     # quantising permute: d % 64, k range, pointers, alignment
     assert L.moe_permute_quant_mx(fake, fake, 8, 96, 2, fake, fake, None) == UNSUPPORTED
     assert L.moe_permute_quant_mx(fake, fake, 8, 128, 17, fake, fake, None) == UNSUPPORTED
