@@ -151,7 +151,7 @@ def aux_bytes(cfg, call):
     once)."""
     T, d, E, n, f = float(cfg.T), cfg.d, cfg.E, float(cfg.n), cfg.f
     mx = 1 + 1 / 32
-    P = float(((cfg.n + 32 * cfg.E + 127) // 128) * 128)   # padded token axis of the grouped blocks
+    P = float(((cfg.n + 128 * cfg.E + 127) // 128) * 128)   # padded token axis of the grouped blocks
     if call == "router":         # x, w_r in; logits out
         return T * d * 2 + d * E * 4 + T * E * 4
     if call == "router_bwd":     # d_logits, w_r, x in; dx term (fp32), dw_r out

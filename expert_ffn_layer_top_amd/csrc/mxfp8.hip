@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 using namespace moe;
 
 extern "C" int moe_mx_pad_cap(int n, int E) {
-  const long long cap = (static_cast<long long>(n) + 32LL * E + 127) / 128 * 128;
+  const long long cap = (static_cast<long long>(n) + 128LL * E + 127) / 128 * 128;
   return cap < (1LL << 31) ? static_cast<int>(cap) : -1;
 }
 

@@ -65,8 +65,9 @@ def _empty(shape, dtype, like):
 
 
 def _mx_pad_cap(n, E):
-    # moe_mx_pad_cap: n + 32 E rounded up to a multiple of 128 (the library's padded token axis)
-    return (n + 32 * E + 127) // 128 * 128
+    # moe_mx_pad_cap: n + 128 E rounded up to a multiple of 128 (the library's padded token axis,
+    # long enough for any pad up to 128)
+    return (n + 128 * E + 127) // 128 * 128
 
 
 # ---------------------------------------------------------------- router

@@ -123,7 +123,8 @@ size_t moe_route_workspace_bytes(int T, int E, int k);
  *        probs [T,E] (optional): full softmax;
  *        counts [E]: rows per expert; offsets [E+1]: exclusive prefix sum (offsets[E] = T*k);
  *        offsets_pad [E+1] (optional): prefix sum of counts rounded up to `pad` (pad >= 1; the
- *        MXFP8 token-block layout uses 32);
+ *        MXFP8 token-block layout takes 32, 64 or 128, and 128 is the fast choice: each
+ *        128-token K step of the weight gradients then starts on a cache line);
  *        dest [T,k]: row of (t, j) in the expert-major buffer, rows ordered by expert, then token;
  *        row_token [T*k] (optional): the token of each row.
  *   ws   at least moe_route_workspace_bytes(T,E,k) bytes of device memory (contents ignored). */
@@ -264,8 +265,9 @@ int mxfp8_quantize_both(const uint16_t* in, int batch, int rows, int cols, uint8
  * (in is the token-major source [T,C]).  Expert e's rows [offsets[e], offsets[e+1]) go to
  * positions [offsets_pad[e], offsets_pad[e] + count_e) of a padded token axis; padding
  * positions up to offsets_pad[e+1] hold zeros, and so does everything from offsets_pad[E] to
- * n_pad_cap.  offsets_pad must be the 32-padded prefix sum from moe_route_topk (pad = 32).
- *   out qT [C, n_pad_cap] E4M3, n_pad_cap = n + 32*E rounded up to a multiple of 128
+ * n_pad_cap.  offsets_pad must be the padded prefix sum from moe_route_topk with pad 32, 64 or
+ * 128 (scale blocks of 32 never straddle two experts, and offsets_pad[E] <= n_pad_cap).
+ *   out qT [C, n_pad_cap] E4M3, n_pad_cap = n + 128*E rounded up to a multiple of 128
  *   (moe_mx_pad_cap); scaleT [n_pad_cap/32, C] E8M0, block-major: the scale of channel c and
  *   position block b is scaleT[b * C + c] (one weight-gradient K step of consecutive channels
  *   reads contiguous bytes). */
@@ -307,7 +309,8 @@ int mxfp8_quantize_gemm(const uint16_t* in, int batch, int rows, int cols, uint8
  * (MOE_ERR_UNSUPPORTED otherwise); in and out must not alias. */
 int mxfp8_scales_to_gemm(const uint8_t* in, int batch, int rows, int K, uint8_t* out, void* stream);
 
-/* Length of the padded token axis used by mxfp8_quantize_grouped and the MXFP8 backward. */
+/* Length of the padded token axis used by mxfp8_quantize_grouped and the MXFP8 backward:
+ * n + 128*E rounded up to a multiple of 128 (room for any pad up to 128); -1 past 2^31 - 1. */
 int moe_mx_pad_cap(int n, int E);
 
 /* ---------------------------------------------------------------- grouped GEMMs */
@@ -361,7 +364,7 @@ int moe_grouped_gemm_down(int dtype, int E, int n, int d, int f, const int32_t* 
  *   w_gate_t, w_up_t [E,d,f] and w_down_t [E,f,d] are the weights quantised along the dgrad
  *   contraction (mxfp8_quantize_both's qT per expert), with their scales in the GEMM scale
  *   layout (R = d, K = f; R = f, K = d); dyexp, dg|du are quantised along rows (GEMM-layout
- *   scales), and xp, a, dyexp, dg, du along grouped tokens (offsets_pad, pad 32), into the
+ *   scales), and xp, a, dyexp, dg, du along grouped tokens (offsets_pad: pad 32, 64 or 128), into the
  *   workspace.
  * Outputs dg, du [n,f], dxp [n,d], dw_gate, dw_up [E,f,d], dw_down [E,d,f], all bf16. */
 int moe_grouped_gemm_swiglu_bwd(int dtype, int E, int n, int d, int f, const int32_t* offsets,
@@ -393,7 +396,7 @@ int moe_grouped_gemm_swiglu_bwd(int dtype, int E, int n, int d, int f, const int
  *   bf16: the row tensors themselves (dyexp [n,d], a [n,f], dg, du [n,f], xp [n,d]);
  *     offsets_pad and all scales NULL.
  *   MXFP8: mxfp8_quantize_grouped outputs, [C, P] E4M3 + block-major scales [P/32, C], with
- *     P = moe_mx_pad_cap(n, E) and offsets_pad the route's 32-padded offsets.
+ *     P = moe_mx_pad_cap(n, E) and offsets_pad the route's padded offsets (pad 32, 64 or 128).
  * Weight gradients of experts with no rows are written as zeros. */
 int moe_grouped_gemm_dgrad_down(int dtype, int E, int n, int d, int f, const int32_t* offsets,
                                 const void* dyexp, const uint8_t* dyexp_scale, const void* w_down_t,

@@ -57,7 +57,7 @@ def test_workspace_sizes_from_host_scalars():
     mx = L.moe_gg_workspace_bytes(1, 64, 131072, 7168, 2048)
     assert mx > 131072 * (7168 + 2 * 2048)                                    # monotone, covers the row operands
     assert L.moe_gg_workspace_bytes(1, 64, 131072, 7168, 2048) <= L.moe_gg_workspace_bytes(1, 64, 131072 * 2, 7168, 2048)
-    assert L.moe_mx_pad_cap(512, 8) == 768 and L.moe_mx_pad_cap(100, 1) == 256
+    assert L.moe_mx_pad_cap(512, 8) == 1536 and L.moe_mx_pad_cap(100, 1) == 256
     # dw_r partials over 2048-token splits, then the bf16 parts of d_logits and of w_r (experts
     # padded to 64), each region 256-byte aligned
     al = lambda b: (b + 255) // 256 * 256

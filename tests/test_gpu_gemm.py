@@ -16,7 +16,7 @@ from tests.gpu_util import BF16_TOL, MX_TOL, assert_close, bf16_to_dev, bits, ho
 pytestmark = pytest.mark.gpu
 
 
-def problem(T, d, E, k, f, seed, empty=(), hot=None, wstd=0.05):
+def problem(T, d, E, k, f, seed, empty=(), hot=None, wstd=0.05, pad=128):
     rng = np.random.default_rng(seed)
     x = to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
     logits = rng.standard_normal((T, E))
@@ -25,7 +25,7 @@ def problem(T, d, E, k, f, seed, empty=(), hot=None, wstd=0.05):
     if hot is not None:
         logits[:, hot] += 100.0
     idx, gate, _ = moe.route_topk(logits, k)
-    counts, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=32)
+    counts, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=pad)
     wg = to_bf16_bits((rng.standard_normal((E, f, d)) * wstd).astype(np.float32))
     wu = to_bf16_bits((rng.standard_normal((E, f, d)) * wstd).astype(np.float32))
     wd = to_bf16_bits((rng.standard_normal((E, d, f)) * wstd).astype(np.float32))
@@ -117,9 +117,10 @@ def gemm_weights(ops, Wd):
 
 
 MX_CASES = [
-    dict(T=600, d=512, E=5, k=2, f=384, seed=11, empty=(2,)),
+    # experts padded to 32 tokens on the weight gradients' token axis (the rest: 128)
+    dict(T=600, d=512, E=5, k=2, f=384, seed=11, empty=(2,), pad=32),
     dict(T=300, d=256, E=4, k=2, f=256, seed=12, hot=0),
-    dict(T=1000, d=384, E=9, k=3, f=128, seed=13, empty=(4,)),
+    dict(T=1000, d=384, E=9, k=3, f=128, seed=13, empty=(4,), pad=32),
     # contraction dims multiples of 512: the forward and dgrad products load scales in groups
     dict(T=700, d=1024, E=6, k=2, f=512, seed=14, empty=(3,)),
     # fewer rows than one tile; a single dense expert; top-1 routing
@@ -313,3 +314,35 @@ def test_mxfp8_few_workgroups_bit_identical(case, monkeypatch):
     names = ("g", "u", "a", "yexp", "dg", "du", "dxp", "dw_gate", "dw_up", "dw_down")
     for nm, r, o in zip(names, ref, got):
         assert np.array_equal(r, o), f"{nm}: 8-workgroup launch differs from the default launch"
+
+
+@pytest.mark.parametrize("case", [MX_CASES[0], MX_CASES[2], MX_CASES[8]], ids=case_id)
+def test_mxfp8_wgrad_pad_independent(case):
+    """The MXFP8 weight gradients with each expert padded to 32 and to 128 tokens on the token
+    axis: the 32-token scale blocks and the 128-token K steps start at the same rows of each
+    expert either way, so every weight gradient is bit-identical."""
+    from expert_ffn_layer_top_amd import ops
+    p = problem(**{**case, "pad": 32})
+    n = p["n"]
+    off_d = i32_to_dev(p["off"])
+    rt_d = i32_to_dev(p["row_token"])
+    x_d = bf16_to_dev(p["x"])
+    dy_d = bf16_to_dev(p["dyexp"])
+    rng = np.random.default_rng(case["seed"] + 100)
+    dg_d, du_d, a_d = (bf16_to_dev(to_bf16_bits(rng.standard_normal((n, p["f"])).astype(np.float32)))
+                       for _ in range(3))
+    outs = {}
+    for pad in (32, 128):
+        offp_d = i32_to_dev(p["offp"] if pad == 32 else problem(**{**case, "pad": 128})["offp"])
+        note(f"gg mxfp8 wgrad pad {pad} {case}")
+        dyT, dyTs = ops.mxfp8_quantize_grouped(dy_d, off_d, offp_d, n)
+        aT, aTs = ops.mxfp8_quantize_grouped(a_d, off_d, offp_d, n)
+        dgT, dgTs = ops.mxfp8_quantize_grouped(dg_d, off_d, offp_d, n)
+        duT, duTs = ops.mxfp8_quantize_grouped(du_d, off_d, offp_d, n)
+        xT, xTs = ops.mxfp8_quantize_grouped(x_d, off_d, offp_d, n, row_token=rt_d)
+        dwd = ops.grouped_gemm_wgrad_down(dyT, aT, off_d, n, offsets_pad=offp_d, scales=(dyTs, aTs))
+        dwg, dwu = ops.grouped_gemm_wgrad_gate_up(dgT, duT, xT, off_d, n, offsets_pad=offp_d,
+                                                  scales=(dgTs, duTs, xTs))
+        outs[pad] = [bits(t) for t in (dwd, dwg, dwu)]
+    for nm, r, o in zip(("dw_down", "dw_gate", "dw_up"), outs[32], outs[128]):
+        assert np.array_equal(r, o), f"{nm}: pad 128 differs from pad 32"

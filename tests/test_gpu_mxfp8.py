@@ -123,7 +123,8 @@ def test_gemm_scale_layout_producers(B, R, C):
 
 
 @pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
-def test_rows_and_grouped_from_one_read(T, E, k, C):
+@pytest.mark.parametrize("pad", [32, 128])
+def test_rows_and_grouped_from_one_read(T, E, k, C, pad):
     """Both layouts of a grouped tensor from one read (the backward's dG, dU) against the oracle's
     row blocks and grouped token blocks, with an empty expert group and ragged group sizes."""
     from expert_ffn_layer_top_amd import ops
@@ -131,11 +132,11 @@ def test_rows_and_grouped_from_one_read(T, E, k, C):
     logits = rng.standard_normal((T, E))
     logits[:, E // 2] -= 100.0                            # an empty expert group
     idx, _, _ = moe.route_topk(logits, k)
-    _, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=32)
+    _, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=pad)
     n = T * k
     v = rng.standard_normal((n, C)).astype(np.float32) * np.exp(rng.standard_normal((n, 1)) * 3).astype(np.float32)
     xp = to_bf16_bits(v)
-    note(f"mxfp8 rows+grouped T={T} E={E} k={k} C={C}")
+    note(f"mxfp8 rows+grouped T={T} E={E} k={k} C={C} pad={pad}")
     q, s, qT, sT = ops.mxfp8_quantize_rows_grouped(bf16_to_dev(xp), i32_to_dev(off), i32_to_dev(offp))
     rq, rs = mxfp8.quantize_rows(xp)
     assert np.array_equal(host(q), rq) and np.array_equal(gemm_scales_to_rows(host(s), n, C), rs)
@@ -147,17 +148,18 @@ def test_rows_and_grouped_from_one_read(T, E, k, C):
 
 @pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
 @pytest.mark.parametrize("gather", [False, True])
-def test_grouped_token_blocks(T, E, k, C, gather):
+@pytest.mark.parametrize("pad", [32, 128])
+def test_grouped_token_blocks(T, E, k, C, gather, pad):
     from expert_ffn_layer_top_amd import ops
     rng = np.random.default_rng(T + E + C)
     logits = rng.standard_normal((T, E))
     logits[:, E // 2] -= 100.0                            # an empty expert group
     idx, _, _ = moe.route_topk(logits, k)
-    _, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=32)
+    _, off, dest, row_token, offp = moe.route_metadata(idx, E, pad=pad)
     x = to_bf16_bits(rng.standard_normal((T, C)).astype(np.float32))
     xp = moe.permute(x, dest)
     n = T * k
-    note(f"mxfp8 grouped T={T} E={E} k={k} C={C} gather={gather}")
+    note(f"mxfp8 grouped T={T} E={E} k={k} C={C} gather={gather} pad={pad}")
     if gather:
         q, s = ops.mxfp8_quantize_grouped(bf16_to_dev(x), i32_to_dev(off), i32_to_dev(offp), n,
                                           row_token=i32_to_dev(row_token))

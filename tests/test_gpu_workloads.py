@@ -88,7 +88,8 @@ def _sample_rows(off, experts, rng, n_random, pool=None):
 
 def _check_routing(cfg, logits, ctx):
     idx, gate, _ = moe.route_topk(logits, cfg.k)
-    counts, off, dest, row_token, offp = moe.route_metadata(idx, cfg.E)
+    from expert_ffn_layer_top_amd import layer
+    counts, off, dest, row_token, offp = moe.route_metadata(idx, cfg.E, pad=layer.MX_PAD)
     assert np.array_equal(host(ctx["topk_idx"]), idx)
     assert np.array_equal(host(ctx["counts"]), counts) and np.array_equal(host(ctx["offsets"]), off)
     assert np.array_equal(host(ctx["dest"]), dest) and np.array_equal(host(ctx["row_token"]), row_token)
