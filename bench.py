@@ -122,8 +122,8 @@ def gemm_bytes(cfg, call):
 
 def row_bytes(cfg, call):
     """Algorithmic HBM bytes of the routing and row-movement calls: every element they must read
-    or write, once (bf16 rows 2 B; MXFP8 rows 1 B + 1/32 B of scale; fp32 gates, logits and the
-    router's dx term; int32 indices)."""
+    or write, once (bf16 rows 2 B; MXFP8 rows 1 B + 1/32 B of scale; fp32 gates and logits; int32
+    indices)."""
     T, d, E, k = float(cfg.T), cfg.d, cfg.E, cfg.k
     n = T * k
     mx = 1 + 1 / 32
@@ -137,8 +137,8 @@ def row_bytes(cfg, call):
     if call == "combine_bwd":    # dy, yexp rows, gates, dest in; dyexp (bf16, or MX row blocks + row gates), d_gate out
         out = n * d * mx + 4 * n if cfg.mxfp8 else n * d * 2
         return T * d * 2 + n * d * 2 + 8 * n + out + 4 * n
-    if call == "permute_bwd":    # dxp rows, dest (and the router's fp32 dx term) in; dx out
-        return (n + T) * d * 2 + 4 * n + (T * d * 4 if router else 0)
+    if call == "permute_bwd":    # dxp rows, dest (and d_logits, w_r for the router's dx term) in; dx out
+        return (n + T) * d * 2 + 4 * n + ((T + d) * E * 4 if router else 0)
     if call == "route_bwd":      # gates, idx, d_gate in; d_logits out
         return T * 4 * E + 12 * n
     raise KeyError(call)
@@ -154,8 +154,8 @@ def aux_bytes(cfg, call):
     P = float(((cfg.n + 128 * cfg.E + 127) // 128) * 128)   # padded token axis of the grouped blocks
     if call == "router":         # x, w_r in; logits out
         return T * d * 2 + d * E * 4 + T * E * 4
-    if call == "router_bwd":     # d_logits, w_r, x in; dx term (fp32), dw_r out
-        return T * E * 4 + d * E * 4 + T * d * 2 + T * d * 4 + d * E * 4
+    if call == "router_bwd":     # d_logits, x in; dw_r out (the dx term is the permute backward's)
+        return T * E * 4 + T * d * 2 + d * E * 4
     if call == "quant_w":        # three weights, both layouts from one read
         return 3 * E * d * f * (2 + 2 * mx)
     if call in ("quant_dg", "quant_du"):   # both layouts from one read
@@ -404,7 +404,7 @@ def step_traffic(cfg):
         return {}
     dtype = "mxfp8" if cfg.mxfp8 else "bf16"
     return {c: v["traffic_bytes"] for c, v in t.items()
-            if v["source_sha256"] == profsum.files_sha256(profsum.call_sources(c, dtype))}
+            if v["source_sha256"] == profsum.files_sha256(profsum.call_sources(c, dtype, cfg.logits == "router"))}
 
 
 def _blas_threads():

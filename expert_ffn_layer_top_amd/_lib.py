@@ -33,6 +33,7 @@ SIGNATURES = {
     "moe_unpermute_combine_bwd": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
     "moe_unpermute_combine_bwd_mx": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p]),
     "moe_permute_bwd": (_i, [_p, _p, _i, _i, _i, _p, _p, _p]),
+    "moe_permute_bwd_router": (_i, [_p, _p, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "mxfp8_quantize": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p]),
     "mxfp8_quantize_both": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _p]),
     "mxfp8_quantize_grouped": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),

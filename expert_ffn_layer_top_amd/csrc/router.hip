@@ -228,24 +228,46 @@ __global__ __launch_bounds__(256) void split_parts(const float* __restrict__ src
 
 // dx_router[t][c] = sum_e dl[t][e] w_r[c][e] over the six products of parts whose sum keeps fp32
 // accuracy, smallest first: (mid, mid), (lo, hi), (hi, lo), (mid, hi), (hi, mid), (hi, hi)
-// (dl part, w part).  A workgroup takes 128 channels x 256 tokens (four waves of 128 x 64); per
-// 64-expert chunk the w parts go to LDS (shared by the waves) and each wave's dl fragments come
-// straight from global memory.  The MFMA computes D[channel][token], so each lane ends with 4
-// consecutive channels of one token: one 16-byte store.
-constexpr int XC = 128, XT = 256, XPITCH = 64 + 8;   // bf16 per LDS row (144 bytes)
-constexpr int OPITCH = XC + 4;                        // fp32 per output staging row (528 bytes)
-static_assert(4 * 16 * OPITCH * 4 <= 3 * XC * XPITCH * 2, "output staging fits the w area");
+// (dl part, w part), per 32-expert K half in order.  A workgroup takes 16 NI channels x 64 NJ
+// tokens (four waves of 16 NI x 16 NJ); per 64-expert chunk the w parts go to LDS (shared by the
+// waves) and each wave's dl fragments come straight from global memory.  The MFMA computes
+// D[channel][token], so each lane ends with 4 consecutive channels of one token.  Every output
+// element gets the same MFMA sequence whatever NI and NJ, so the tile shape does not change a bit.
+// Unfused (128 x 256): the fp32 term is stored.  FUSED (64 x 128, so the small register and LDS
+// footprint lets five workgroups (k <= 4; four above) share a compute unit and keep many row loads
+// in flight): the permute backward in place of the fp32 store -- dxb[t][c] = bf16(dx_router[t][c]
+// + dxp[dest[t][0]][c] + ... + dxp[dest[t][k-1]][c]), summed in fp32 in that order (the router
+// term first, then the slots), which is moe_permute_bwd's sum with dx_router as its addend: the
+// same bytes as the two calls, without writing and re-reading the fp32 term (4 T d bytes each
+// way).  KM: the slot count rounded up to 4, 8 or 16 (unfused: unused).
+constexpr int XPITCH = 64 + 8;   // bf16 per LDS row of a w part (144 bytes)
 
-__global__ __launch_bounds__(256, 2) void router_dx_kernel(const __bf16* __restrict__ dlp, const __bf16* __restrict__ wp,
-                                                        int T, int d, int EP, float* __restrict__ dx) {
+template <int NI, int NJ>
+struct DxTile {
+  static constexpr int XC = 16 * NI, XT = 64 * NJ;    // workgroup: channels, tokens
+  static constexpr int OPITCH = XC + 4;               // fp32 per output staging row
+  static constexpr int TPR = 256 / XC;                // threads per channel row of the w fill
+  static constexpr int WPT = 64 / TPR / 8;            // 16-byte pieces per part per thread
+  static_assert(4 * 16 * OPITCH * 4 <= 3 * XC * XPITCH * 2, "output staging fits the w area");
+};
+
+template <bool FUSED, int NI, int NJ, int KM>
+__global__ __launch_bounds__(256, FUSED ? (KM <= 4 ? 5 : 4) : 2) void router_dx_kernel(const __bf16* __restrict__ dlp,
+                                                                    const __bf16* __restrict__ wp, int T, int d, int EP,
+                                                                    float* __restrict__ dx,
+                                                                    const uint16_t* __restrict__ dxp,
+                                                                    const int32_t* __restrict__ dest, int k,
+                                                                    uint16_t* __restrict__ dxb) {
+  using Tl = DxTile<NI, NJ>;
+  constexpr int XC = Tl::XC, XT = Tl::XT, OPITCH = Tl::OPITCH;
   __shared__ __attribute__((aligned(16))) __bf16 Ws[3][XC][XPITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c0 = blockIdx.x * XC, tw = blockIdx.y * XT + 64 * wave;
+  const int c0 = blockIdx.x * XC, tw = blockIdx.y * XT + 16 * NJ * wave;
   constexpr uint32_t OOB = 0x80000000u;
   const long long pd = static_cast<long long>(d) * EP, pt = static_cast<long long>(T) * EP;
-  // the workgroup's 128 channel rows of each w part, and the wave's 64 token rows of each dl part
+  // the workgroup's channel rows of each w part, and the wave's token rows of each dl part
   const int crows = min(XC, d - c0);
-  const int trows = max(0, min(64, T - tw));
+  const int trows = max(0, min(16 * NJ, T - tw));
   __amdgpu_buffer_rsrc_t wr[3], dr[3];
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
@@ -254,48 +276,48 @@ __global__ __launch_bounds__(256, 2) void router_dx_kernel(const __bf16* __restr
     dr[q] = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dlp + q * pt + static_cast<long long>(max(tw, 0)) * EP),
                                               0, trows * EP * 2, 0x00020000);
   }
-  f32x4 acc[8][4];
+  f32x4 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // w chunk loads: thread -> channel row tid / 2, experts 32 (tid % 2) .. + 31 of each part
-  const int wrow = tid >> 1, wcol = 32 * (tid & 1);
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // w chunk loads: thread -> channel row tid / TPR, experts 8 WPT (tid % TPR) .. of each part
+  const int wrow = tid / Tl::TPR, wcol = 8 * Tl::WPT * (tid % Tl::TPR);
   for (int e0 = 0; e0 < EP; e0 += 64) {
-    uint4 wv[3][4];
+    uint4 wv[3][Tl::WPT];
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < Tl::WPT; ++u)
         wv[q][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  wr[q], static_cast<int>((wrow * EP + e0 + wcol + 8 * u) * 2), 0, 0));
     if (e0 > 0) __syncthreads();   // the previous chunk's readers are done
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&Ws[q][wrow][wcol + 8 * u]) = wv[q][u];
+      for (int u = 0; u < Tl::WPT; ++u) *reinterpret_cast<uint4*>(&Ws[q][wrow][wcol + 8 * u]) = wv[q][u];
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       // the wave's dl fragments of this K half: token tile j, part p (lane row l % 16, experts
       // 8 (l / 16) .. + 7)
-      bf16x8 df[3][4];
+      bf16x8 df[3][NJ];
 #pragma unroll
       for (int p = 0; p < 3; ++p)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int r = 16 * j + (lane & 15);
           const uint32_t off = r < trows ? static_cast<uint32_t>((r * EP + e0 + 32 * ks + 8 * (lane >> 4)) * 2) : OOB;
           df[p][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dr[p], static_cast<int>(off), 0, 0));
         }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NI; ++i) {
         bf16x8 wf[3];
 #pragma unroll
         for (int q = 0; q < 3; ++q)
           wf[q] = *reinterpret_cast<const bf16x8*>(&Ws[q][16 * i + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           f32x4 c = acc[i][j];
           c = mfma(wf[1], df[1][j], c);   // (mid, mid)
           c = mfma(wf[0], df[2][j], c);   // (lo, hi)
@@ -309,24 +331,79 @@ __global__ __launch_bounds__(256, 2) void router_dx_kernel(const __bf16* __restr
     }
   }
   // Output through LDS (the w area, free once every wave is past its products): per round, one
-  // token tile (16 tokens x the wave's 128 channels) goes in as each lane's 4-channel pieces and
-  // comes out as 16-byte pieces of whole 512-byte row spans, 2 rows per store instruction.
+  // token tile (16 tokens x the wave's XC channels) goes in as each lane's 4-channel pieces.
   __syncthreads();
   float* stg = reinterpret_cast<float*>(&Ws[0][0][0]) + wave * (16 * OPITCH);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
+    if constexpr (FUSED) {
+      // out as 8-channel pieces (XC / 8 lanes per token); each lane adds its token's k permuted
+      // rows (16 bytes of bf16 each), the loads of UG tokens per lane in flight together: 64
+      // registers of rows whatever KM
+      constexpr int LPT = XC / 8;            // lanes per token
+      constexpr int TPI = 64 / LPT;          // tokens per instruction
+      constexpr int NU = 16 / TPI;           // instructions per tile
+      constexpr int UG = (16 / KM) < NU ? (16 / KM) : NU;
+      static_assert(UG >= 1 && NU % UG == 0, "load groups");
+      const int c = c0 + 8 * (lane % LPT);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<float4*>(stg + (lane & 15) * OPITCH + 16 * i + 4 * (lane >> 4)) =
-          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-    float4 v[8];
+      for (int ug = 0; ug < NU; ug += UG) {
+        uint4 pv[UG][KM];
+        int tv[UG];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(stg + (2 * u + (lane >> 5)) * OPITCH + 4 * (lane & 31));
+        for (int u = 0; u < UG; ++u) {
+          const int t = tw + 16 * j + TPI * (ug + u) + lane / LPT;
+          tv[u] = t < T && c < d ? t : -1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = tw + 16 * j + 2 * u + (lane >> 5);
-      const int c = c0 + 4 * (lane & 31);
-      if (t < T && c < d) *reinterpret_cast<float4*>(dx + static_cast<long long>(t) * d + c) = v[u];
+          for (int jj = 0; jj < KM; ++jj) {
+            pv[u][jj] = make_uint4(0, 0, 0, 0);
+            if (tv[u] >= 0 && jj < k) {
+              const long long row = dest[static_cast<long long>(t) * k + jj];
+              pv[u][jj] = *reinterpret_cast<const uint4*>(dxp + row * d + c);
+            }
+          }
+        }
+        if (ug == 0) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            *reinterpret_cast<float4*>(stg + (lane & 15) * OPITCH + 16 * i + 4 * (lane >> 4)) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+          const float* sp = stg + (TPI * (ug + u) + lane / LPT) * OPITCH + 8 * (lane % LPT);
+          const float4 a0 = *reinterpret_cast<const float4*>(sp), a1 = *reinterpret_cast<const float4*>(sp + 4);
+          float f[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+          for (int jj = 0; jj < KM; ++jj) {
+            if (jj < k) {
+              const uint4 w = pv[u][jj];
+              f[0] += bf16_lo(w.x); f[1] += bf16_hi(w.x); f[2] += bf16_lo(w.y); f[3] += bf16_hi(w.y);
+              f[4] += bf16_lo(w.z); f[5] += bf16_hi(w.z); f[6] += bf16_lo(w.w); f[7] += bf16_hi(w.w);
+            }
+          }
+          if (tv[u] >= 0)
+            *reinterpret_cast<uint4*>(dxb + static_cast<long long>(tv[u]) * d + c) =
+                make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                           pack_bf16x2(f[6], f[7]));
+        }
+      }
+    } else {
+      // out as 16-byte pieces of whole row spans, 2 rows per store instruction (XC = 128)
+      static_assert(FUSED || XC == 128, "the fp32 store takes 128-channel tiles");
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<float4*>(stg + (lane & 15) * OPITCH + 16 * i + 4 * (lane >> 4)) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(stg + (2 * u + (lane >> 5)) * OPITCH + 4 * (lane & 31));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = tw + 16 * j + 2 * u + (lane >> 5);
+        const int cc = c0 + 4 * (lane & 31);
+        if (t < T && cc < d) *reinterpret_cast<float4*>(dx + static_cast<long long>(t) * d + cc) = v[u];
+      }
     }
   }
 }
@@ -514,7 +591,7 @@ extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const
   const int EP = padded_experts(E);
   // the kernels' buffer offsets stay below 2^31 bytes
   MOE_REQUIRE(static_cast<long long>(kSplitTokens) * d * 2 < 0x7fffffffLL &&
-                  static_cast<long long>(XC) * EP * 2 < 0x7fffffffLL,
+                  static_cast<long long>(DxTile<8, 4>::XC) * EP * 2 < 0x7fffffffLL,
               MOE_ERR_UNSUPPORTED, "router: d too large");
   if (dx_router != nullptr) MOE_CHECK_ALIGN(dx_router);
   const BwdWs L(T, d, E);
@@ -533,8 +610,9 @@ extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const
     const long long n2 = static_cast<long long>(d) * EP;
     split_parts<<<static_cast<unsigned>((n2 + 255) / 256), 256, 0, s>>>(w_r, d, E, EP, wp);
     if (int st = check_launch("router_project_bwd split w")) return st;
-    dim3 grid((d + XC - 1) / XC, (T + XT - 1) / XT, 1);
-    router_dx_kernel<<<grid, 256, 0, s>>>(dlp, wp, T, d, EP, dx_router);
+    using Tl = DxTile<8, 4>;
+    dim3 grid((d + Tl::XC - 1) / Tl::XC, (T + Tl::XT - 1) / Tl::XT, 1);
+    router_dx_kernel<false, 8, 4, 1><<<grid, 256, 0, s>>>(dlp, wp, T, d, EP, dx_router, nullptr, nullptr, 0, nullptr);
     if (int st = check_launch("router_project_bwd dx")) return st;
   }
   if (dw_r != nullptr) {
@@ -548,4 +626,34 @@ extern "C" int moe_router_project_bwd(const uint16_t* x, const float* w_r, const
     if (int st = check_launch("router_project_bwd dw reduce")) return st;
   }
   return MOE_OK;
+}
+
+extern "C" int moe_permute_bwd_router(const uint16_t* dxp, const int32_t* dest, int T, int d, int k,
+                                      const float* w_r, const float* d_logits, int E, uint16_t* dx, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  MOE_CHECK_PTR(dxp); MOE_CHECK_PTR(dest); MOE_CHECK_PTR(w_r); MOE_CHECK_PTR(d_logits); MOE_CHECK_PTR(dx);
+  MOE_REQUIRE(T >= 1 && E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "need T >= 1 and 1 <= E <= 256");
+  MOE_REQUIRE(k >= 1 && k <= 16, MOE_ERR_UNSUPPORTED, "k must be in [1, 16]");
+  MOE_REQUIRE(d >= 64 && d % 64 == 0, MOE_ERR_UNSUPPORTED, "d must be a positive multiple of 64");
+  MOE_REQUIRE(static_cast<long long>(T) * k < (1LL << 31), MOE_ERR_UNSUPPORTED, "T*k must be < 2^31");
+  MOE_CHECK_ALIGN(dxp); MOE_CHECK_ALIGN(dx);
+  const int EP = padded_experts(E);
+  const BwdWs L(T, d, E);
+  MOE_REQUIRE(ws != nullptr && ws_bytes >= L.total, MOE_ERR_WORKSPACE, "router bwd workspace: need %zu bytes", L.total);
+  MOE_CHECK_ALIGN(ws);
+  hipStream_t s = as_stream(stream);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  __bf16* dlp = reinterpret_cast<__bf16*>(w8 + L.dls);
+  __bf16* wp = reinterpret_cast<__bf16*>(w8 + L.wps);
+  const long long n1 = static_cast<long long>(T) * EP, n2 = static_cast<long long>(d) * EP;
+  split_parts<<<static_cast<unsigned>((n1 + 255) / 256), 256, 0, s>>>(d_logits, T, E, EP, dlp);
+  if (int st = check_launch("permute_bwd_router split dl")) return st;
+  split_parts<<<static_cast<unsigned>((n2 + 255) / 256), 256, 0, s>>>(w_r, d, E, EP, wp);
+  if (int st = check_launch("permute_bwd_router split w")) return st;
+  using Tl = DxTile<4, 2>;
+  dim3 grid((d + Tl::XC - 1) / Tl::XC, (T + Tl::XT - 1) / Tl::XT, 1);
+  if (k <= 4) router_dx_kernel<true, 4, 2, 4><<<grid, 256, 0, s>>>(dlp, wp, T, d, EP, nullptr, dxp, dest, k, dx);
+  else if (k <= 8) router_dx_kernel<true, 4, 2, 8><<<grid, 256, 0, s>>>(dlp, wp, T, d, EP, nullptr, dxp, dest, k, dx);
+  else router_dx_kernel<true, 4, 2, 16><<<grid, 256, 0, s>>>(dlp, wp, T, d, EP, nullptr, dxp, dest, k, dx);
+  return check_launch("permute_bwd_router");
 }

@@ -2,9 +2,10 @@
 
 Forward:  [router_project] -> route_topk -> permute -> grouped_gemm_gate_up -> grouped_gemm_down
           -> unpermute_combine
-Backward: unpermute_combine_bwd -> route_topk_bwd -> [router_project_bwd]
+Backward: unpermute_combine_bwd -> route_topk_bwd -> [router_project_bwd: dw_r]
           -> grouped_gemm_dgrad_down -> grouped_gemm_wgrad_down -> grouped_gemm_dgrad_gate_up
-          -> permute_bwd (+ the router's dx term) -> grouped_gemm_wgrad_gate_up
+          -> permute_bwd (permute_bwd_router: with the router's dx term, computed in the same
+          kernel) -> grouped_gemm_wgrad_gate_up
 The grouped products are issued one kernel per call (the same kernels, in the same order, as the
 composite grouped_gemm_swiglu / grouped_gemm_swiglu_bwd), so each can be timed on its own.
 MXFP8 adds the block quantisation of x (inside the permute, which writes the row blocks straight
@@ -159,7 +160,7 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
 
 def backward(ctx, weights, dy, events=None):
     """Layer backward from dy [T, d] bf16.  Returns dict with dx, d_logits, dw_gate, dw_up,
-    dw_down (and dw_r, dx_router when the layer owns its router) plus the intermediates (under
+    dw_down (and dw_r when the layer owns its router) plus the intermediates (under
     MXFP8, "mx" holds the quantised backward operands: row blocks dyq/dgq/duq, grouped token
     blocks dyT/aT/dgT/duT/xT, each with its scales).
     events: as for `forward`.
@@ -183,11 +184,15 @@ def backward(ctx, weights, dy, events=None):
         if ctx.get("balance_weight") is not None:
             bal = (ctx["probs"], ctx["counts"], ctx["balance_weight"])
         out["d_logits"] = ops.route_topk_bwd(ctx["topk_gate"], ctx["topk_idx"], dgate, E, balance=bal)
-    addend = None
     if weights.w_r is not None:
         with _Span(events, "router_bwd"):
-            addend, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"])
-        out["dx_router"] = addend
+            _, out["dw_r"] = ops.router_project_bwd(ctx["x"], weights.w_r, out["d_logits"], want_dx=False)
+
+    def permute_bwd(dxp):
+        # the router's dx term, when the layer owns its router, joins the permuted rows' sum
+        if weights.w_r is None:
+            return ops.permute_bwd(dxp, ctx["dest"])
+        return ops.permute_bwd_router(dxp, ctx["dest"], weights.w_r, out["d_logits"])
     off = ctx["offsets"]
     g, u, a = ctx["g"], ctx["u"], ctx["a"]
     if g is None:
@@ -207,12 +212,12 @@ def backward(ctx, weights, dy, events=None):
         with _Span(events, "dgrad_gate_up"):
             dxp = ops.grouped_gemm_dgrad_gate_up(dg, du, off, weights.w_gate, weights.w_up)
         with _Span(events, "permute_bwd"):
-            out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
+            out["dx"] = permute_bwd(dxp)
         with _Span(events, "wgrad_gate_up"):
             dw_gate, dw_up = ops.grouped_gemm_wgrad_gate_up(dg, du, ctx["xp"], off, g.shape[0])
     else:
         # MXFP8: every operand quantised along its product's contraction dim (rows for the dgrads,
-        # grouped tokens padded to 32 for the wgrads), then one kernel per product
+        # grouped tokens padded to MX_PAD for the wgrads), then one kernel per product
         q = ctx["mx_weights"]
         n = g.shape[0]
         pad = ctx["offsets_pad"]
@@ -234,7 +239,7 @@ def backward(ctx, weights, dy, events=None):
             dxp = ops.grouped_gemm_dgrad_gate_up(dgq, duq, off, q["wg_t"], q["wu_t"],
                                                  scales=(dgs, dus, q["wg_t_s"], q["wu_t_s"]))
         with _Span(events, "permute_bwd"):
-            out["dx"] = ops.permute_bwd(dxp, ctx["dest"], addend=addend)
+            out["dx"] = permute_bwd(dxp)
         with _Span(events, "quant_xT"):
             xT, xTs = ops.mxfp8_quantize_grouped(ctx["x"], off, pad, n, row_token=ctx["row_token"])
         with _Span(events, "wgrad_gate_up"):

@@ -265,6 +265,25 @@ def permute_bwd(dxp, dest, addend=None):
     return dx
 
 
+def permute_bwd_router(dxp, dest, w_r, d_logits):
+    """dx [T,d] bf16 = permute_bwd(dxp, dest, addend=router_project_bwd(x, w_r, d_logits)[0]) in
+    one kernel, byte for byte."""
+    _check(dest, torch.int32, "dest", ndim=2)
+    T, k = dest.shape
+    _check(dxp, torch.bfloat16, "dxp", (T * k, None))
+    d = dxp.shape[1]
+    _check(w_r, torch.float32, "w_r", (d, None))
+    E = w_r.shape[1]
+    _check(d_logits, torch.float32, "d_logits", (T, E))
+    _on_gpu(dxp, dest, w_r, d_logits)
+    dx = _empty((T, d), torch.bfloat16, dxp)
+    nbytes = lib.moe_router_bwd_workspace_bytes(T, d, E)
+    ws = _empty((max(nbytes, 1),), torch.uint8, dxp)
+    call("moe_permute_bwd_router", _ptr(dxp), _ptr(dest), T, d, k, _ptr(w_r), _ptr(d_logits), E, _ptr(dx),
+         _ptr(ws), nbytes, _stream(dxp))
+    return dx
+
+
 # ---------------------------------------------------------------- MXFP8
 
 def _rc(x):

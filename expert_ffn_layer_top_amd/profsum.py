@@ -57,14 +57,15 @@ CALL_SOURCES = {
 GEMM_CALLS = ("gate_up", "down", "dgrad_down", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up")
 
 
-def call_sources(call, dtype):
-    """The csrc files whose code one call of the layer step runs."""
+def call_sources(call, dtype, router=False):
+    """The csrc files whose code one call of the layer step runs (router: the layer owns its
+    router, so the permute backward is the router file's fused kernel)."""
     if call in GEMM_CALLS or call == "recompute":
         src = SOURCES[dtype]
         return src + CALL_SOURCES["quant"] if (dtype == "mxfp8" and call == "down") else src
     if call in ("route", "route_bwd"):
         return CALL_SOURCES["route"]
-    if call in ("router", "router_bwd"):
+    if call in ("router", "router_bwd") or (call == "permute_bwd" and router):
         return CALL_SOURCES["router"]
     if call.startswith("quant_"):
         return CALL_SOURCES["quant"]
@@ -105,18 +106,24 @@ def step_sequence(mxfp8, router, forward_only=False):
     seq.append(("combine_bwd", [("combine_bwd_mx_kernel" if mxfp8 else "combine_bwd_kernel", None)]))
     seq.append(("route_bwd", [("route_topk_bwd_kernel", None)]))
     if router:
-        seq.append(("router_bwd", [("split_parts", None), ("split_parts", None), ("router_dx_kernel", None),
-                                   ("router_dw_kernel", None), ("reduce_splits", None)]))
+        seq.append(("router_bwd", [("split_parts", None), ("router_dw_kernel", None), ("reduce_splits", None)]))
+    # with a router, the permute backward adds the router's dx term in the same kernel
+    pb = ("permute_bwd", [("split_parts", None), ("split_parts", None), ("router_dx_kernel", "true,")] if router
+          else [("permute_bwd_kernel", None)])
     if mxfp8:
         qg = ("quant_grouped_kernel", None)
         seq += [("dgrad_down", [g(2)]), ("quant_dyT", [qg]), ("quant_aT", [qg]), ("wgrad_down", [g(4)]),
                 ("quant_dg", [("quant_rows_grouped_kernel", None)]), ("quant_du", [("quant_rows_grouped_kernel", None)]),
-                ("dgrad_gate_up", [g(3)]), ("permute_bwd", [("permute_bwd_kernel", None)]),
-                ("quant_xT", [qg]), ("wgrad_gate_up", [g(5)])]
+                ("dgrad_gate_up", [g(3)]), pb, ("quant_xT", [qg]), ("wgrad_gate_up", [g(5)])]
     else:
-        seq += [("dgrad_down", [g(2)]), ("wgrad_down", [g(4)]), ("dgrad_gate_up", [g(3)]),
-                ("permute_bwd", [("permute_bwd_kernel", None)]), ("wgrad_gate_up", [g(5)])]
+        seq += [("dgrad_down", [g(2)]), ("wgrad_down", [g(4)]), ("dgrad_gate_up", [g(3)]), pb,
+                ("wgrad_gate_up", [g(5)])]
     return seq
+
+
+def workload_router(workload):
+    """Whether the named workload's layer owns its router (router-projected logits)."""
+    return workload in ("mxfp8", "tiny")
 
 
 def workload_sequence(workload):
@@ -347,7 +354,8 @@ def cmd_step_traffic(a):
         fb = statistics.mean(p[call] for p in fs) * 1024.0 * ff
         wb = statistics.mean(p[call] for p in ws) * 1024.0 * fw
         kern = "+".join(b if t is None else f"{b}<{t.rstrip(',')}>" for b, t in pats)
-        print(f"{call:<14} {fb:14.0f} {wb:14.0f} {fb + wb:14.0f}  {files_sha256(call_sources(call, dtype))}  {kern}")
+        src = call_sources(call, dtype, workload_router(a.workload.split("_")[0]))
+        print(f"{call:<14} {fb:14.0f} {wb:14.0f} {fb + wb:14.0f}  {files_sha256(src)}  {kern}")
 
 
 def cmd_step_kernels(a):
@@ -365,7 +373,7 @@ def cmd_step_kernels(a):
         total += statistics.median(v)
         kern = "+".join(b if t is None else f"{b}<{t.rstrip(',')}>" for b, t in pats)
         print(f"{call:<14} {statistics.median(v):10.1f} {statistics.mean(v):10.1f} {min(v):10.1f} {max(v):10.1f}  "
-              f"{files_sha256(call_sources(call, dtype))}  {kern}")
+              f"{files_sha256(call_sources(call, dtype, workload_router(a.workload.split('_')[0])))}  {kern}")
     print(f"{'sum':<14} {total:10.1f}")
 
 

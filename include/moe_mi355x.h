@@ -231,6 +231,21 @@ int moe_unpermute_combine_bwd_mx(const uint16_t* dy, const uint16_t* yexp, const
 int moe_permute_bwd(const uint16_t* dxp, const int32_t* dest, int T, int d, int k,
                     const float* dx_addend_or_null, uint16_t* dx, void* stream);
 
+/* The permute backward of a layer that owns its router, with the router's dx term computed in
+ * the same kernel ([news] lead paragraphs: the router is trained with the layer, so x receives
+ * the router path's gradient beside the experts'; "Routing work stays on the GPU"):
+ *   dx[t] = bf16( dx_router[t] + dxp[dest[t,0]] + ... + dxp[dest[t,k-1]] ),
+ * dx_router = d_logits @ w_r^T as moe_router_project_bwd computes it, summed in fp32 in that
+ * order: byte-identical to moe_router_project_bwd (dx only) followed by moe_permute_bwd with its
+ * dx_router as the addend, without the fp32 term going to memory and back (4*T*d bytes each way).
+ *   dxp [T*k, d] bf16, dest [T,k], w_r [d,E] fp32, d_logits [T,E] fp32; dx [T,d] bf16 out.
+ * ws: moe_router_bwd_workspace_bytes(T, d, E) bytes (MOE_ERR_WORKSPACE otherwise).  Limits:
+ * T >= 1, 1 <= k <= 16, d a positive multiple of 64, 1 <= E <= 256, T*k < 2^31; dxp, dx and ws
+ * 16-byte aligned. */
+int moe_permute_bwd_router(const uint16_t* dxp, const int32_t* dest, int T, int d, int k, const float* w_r,
+                           const float* d_logits, int E, uint16_t* dx, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* ---------------------------------------------------------------- MXFP8 quantisation */
 
 /* MXFP8 block quantisation of a bf16 tensor in[batch][rows][cols]

@@ -142,6 +142,21 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, fake, None, None, 0, None) == WORKSPACE
     # nothing requested: nothing to do
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, None, None, 0, None) == 0
+    # permute backward with the router's dx term: the rows' limits, the router's, the workspace
+    pbr = L.moe_permute_bwd_router
+    assert pbr(fake, fake, 64, 128, 0, fake, fake, 8, fake, fake, 1 << 30, None) == UNSUPPORTED    # k = 0
+    assert pbr(fake, fake, 64, 128, 17, fake, fake, 8, fake, fake, 1 << 30, None) == UNSUPPORTED   # k > 16
+    assert pbr(fake, fake, 64, 96, 4, fake, fake, 8, fake, fake, 1 << 30, None) == UNSUPPORTED     # d % 64
+    assert pbr(fake, fake, 64, 128, 4, fake, fake, 0, fake, fake, 1 << 30, None) == UNSUPPORTED    # E = 0
+    assert pbr(fake, fake, 64, 128, 4, fake, fake, 257, fake, fake, 1 << 30, None) == UNSUPPORTED  # E > 256
+    assert pbr(fake, fake, 0, 128, 4, fake, fake, 8, fake, fake, 1 << 30, None) == UNSUPPORTED     # T = 0
+    assert pbr(None, fake, 64, 128, 4, fake, fake, 8, fake, fake, 1 << 30, None) == INVALID
+    assert pbr(fake, fake, 64, 128, 4, None, fake, 8, fake, fake, 1 << 30, None) == INVALID
+    assert pbr(fake, fake, 64, 128, 4, fake, fake, 8, None, fake, 1 << 30, None) == INVALID
+    assert pbr(fake, fake, 64, 128, 4, fake, fake, 8, ctypes.c_void_p(0x1008), fake, 1 << 30, None) == INVALID
+    need = L.moe_router_bwd_workspace_bytes(64, 128, 8)
+    assert pbr(fake, fake, 64, 128, 4, fake, fake, 8, fake, fake, need - 1, None) == WORKSPACE
+    assert pbr(fake, fake, 64, 128, 4, fake, fake, 8, fake, None, need, None) == WORKSPACE
 
 
 def test_argument_checks_of_balance_and_fused_producer():

@@ -5,8 +5,8 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import moe
-from tests.gpu_util import assert_close, bf16_to_dev, f32_to_dev, host, i32_to_dev, note
+from oracle import codecs, moe
+from tests.gpu_util import BF16_TOL, assert_close, bf16_to_dev, bits, f32_to_dev, host, i32_to_dev, note
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +104,29 @@ def test_router_project_and_bwd(T, d, E):
     # fixed-order split-K reduction: a repeat gives the same bits
     dx2, dw2 = ops.router_project_bwd(xd, wd, f32_to_dev(dl))
     assert np.array_equal(host(dw2), host(dw)) and np.array_equal(host(dx2), host(dx))
+
+
+@pytest.mark.parametrize("T,d,E,k", [(300, 192, 8, 2), (1000, 512, 64, 4), (257, 256, 5, 1), (100, 128, 16, 8),
+                                     (70, 64, 32, 16), (1, 64, 4, 3), (513, 7168, 64, 4)])
+def test_permute_bwd_with_router_term(T, d, E, k):
+    """The permute backward with the router's dx term in one kernel: byte-identical to the router
+    backward's fp32 dx followed by the permute backward with it as the addend, and within the bf16
+    bar of the oracle (ragged token tiles, d not a multiple of the 128-channel tile, k = 1..16)."""
+    from expert_ffn_layer_top_amd import ops
+    rng = np.random.default_rng(T + d + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, _, _ = moe.route_topk(logits, k)
+    _, _, dest, _, _ = moe.route_metadata(idx, E)
+    x = synth.to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    w_r = (rng.standard_normal((d, E)) * 0.02).astype(np.float32)
+    dl = rng.standard_normal((T, E)).astype(np.float32)
+    dxp = synth.to_bf16_bits(rng.standard_normal((T * k, d)).astype(np.float32))
+    note(f"permute_bwd_router T={T} d={d} E={E} k={k}")
+    dxp_d, dest_d, w_d, dl_d = bf16_to_dev(dxp), i32_to_dev(dest), f32_to_dev(w_r), f32_to_dev(dl)
+    fused = ops.permute_bwd_router(dxp_d, dest_d, w_d, dl_d)
+    addend, _ = ops.router_project_bwd(bf16_to_dev(x), w_d, dl_d, want_dw=False)
+    two = ops.permute_bwd(dxp_d, dest_d, addend=addend)
+    assert np.array_equal(bits(fused), bits(two)), "fused call differs from the two calls"
+    rdx, _ = moe.router_project_bwd(x, w_r, dl)
+    ref = moe.permute_bwd(dxp, dest, addend=rdx)
+    assert_close(codecs.bf16_to_f64(bits(fused)), ref, BF16_TOL, "dx")
