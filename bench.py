@@ -158,14 +158,12 @@ def aux_bytes(cfg, call):
         return T * E * 4 + T * d * 2 + d * E * 4
     if call == "quant_w":        # three weights, both layouts from one read
         return 3 * E * d * f * (2 + 2 * mx)
-    if call in ("quant_dg", "quant_du"):   # both layouts from one read
+    if call in ("quant_a", "quant_dg", "quant_du"):   # both layouts from one read
         return n * f * (2 + mx) + P * f * mx
     if call == "quant_dyT":      # dy gathered through row_token with the row gates
         return T * d * 2 + n * 8 + P * d * mx
     if call == "quant_xT":
         return T * d * 2 + n * 4 + P * d * mx
-    if call == "quant_aT":
-        return n * f * 2 + P * f * mx
     raise KeyError(call)
 
 
@@ -216,7 +214,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=True):
     if cfg.logits == "router":
         aux += layer.ROUTER_CALLS if not cfg.forward_only else ("router",)
     if cfg.mxfp8:
-        aux += ("quant_w",) + (layer.QUANT_CALLS if not cfg.forward_only else ())
+        aux += ("quant_w",) + layer.QUANT_CALLS_FWD + (layer.QUANT_CALLS if not cfg.forward_only else ())
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -262,7 +260,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=True):
     row_ms = {c: med(c) for c in rows}
     aux_ms = {c: med(c) for c in aux}
     step_flushed = [e["step"][0].elapsed_time(e["step"][1]) for e in inst]
-    cand = [c for c in calls if not (cfg.mxfp8 and c == "down") and c != layer.RECOMPUTE_CALL]
+    cand = [c for c in calls if c != layer.RECOMPUTE_CALL]
     dom = max(cand, key=lambda c: gemm_ms[c])
     domev = [{dom: (ev(), ev())} for _ in range(steps)]
     torch.cuda.synchronize()

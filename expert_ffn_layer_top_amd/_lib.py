@@ -48,6 +48,7 @@ SIGNATURES = {
                                      _p, _p, _p, _p, _p, _sz, _p]),
     "moe_grouped_gemm_gate_up": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_gemm_down": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_grouped_gemm_down_mx": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_gemm_swiglu_bwd": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p,
                                          _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                          _sz, _p]),

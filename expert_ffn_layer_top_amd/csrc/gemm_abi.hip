@@ -19,6 +19,8 @@ int gg_mx_gate_up(int E, int n, int d, int f, const int32_t* offsets, const uint
                   uint16_t* u, uint16_t* a, hipStream_t s);
 int gg_mx_down(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* a, const uint8_t* wdq,
                const uint8_t* wds, uint16_t* yexp, uint8_t* ws, hipStream_t s);
+int gg_mx_down_q(int E, int n, int d, int f, const int32_t* offsets, const uint8_t* aq, const uint8_t* as,
+                 const uint8_t* wdq, const uint8_t* wds, uint16_t* yexp, hipStream_t s);
 int gg_bf16_dgrad_down(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* dyexp,
                        const uint16_t* wd, const uint16_t* g, const uint16_t* u, uint16_t* dg, uint16_t* du,
                        hipStream_t s);
@@ -145,6 +147,16 @@ extern "C" int moe_grouped_gemm_down(int dtype, int E, int n, int d, int f, cons
   MOE_CHECK_ALIGN(ws);
   return gg_mx_down(E, n, d, f, offsets, a, static_cast<const uint8_t*>(w_down), w_down_scale, yexp,
                     static_cast<uint8_t*>(ws), s);
+}
+
+extern "C" int moe_grouped_gemm_down_mx(int E, int n, int d, int f, const int32_t* offsets, const uint8_t* a_q,
+                                        const uint8_t* a_scale, const uint8_t* w_down, const uint8_t* w_down_scale,
+                                        uint16_t* yexp, void* stream) {
+  if (int st = check_gg_shape(MOE_MXFP8, E, n, d, f)) return st;
+  MOE_CHECK_PTR(offsets); MOE_CHECK_PTR(a_q); MOE_CHECK_PTR(w_down); MOE_CHECK_PTR(yexp);
+  MOE_CHECK_ALIGN(a_q); MOE_CHECK_ALIGN(w_down); MOE_CHECK_ALIGN(yexp);
+  if (int st = check_scales(MOE_MXFP8, {a_scale, w_down_scale})) return st;
+  return gg_mx_down_q(E, n, d, f, offsets, a_q, a_scale, w_down, w_down_scale, yexp, as_stream(stream));
 }
 
 extern "C" int moe_grouped_gemm_swiglu(int dtype, int E, int n, int d, int f, const int32_t* offsets,

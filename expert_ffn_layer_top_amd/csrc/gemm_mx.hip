@@ -707,15 +707,20 @@ int gg_mx_gate_up(int E, int n, int d, int f, const int32_t* offsets, const uint
 }
 
 // Forward, second product: quantise A along f into ws, then FWD2 (Yexp).
+int gg_mx_down_q(int E, int n, int d, int f, const int32_t* offsets, const uint8_t* aq, const uint8_t* as,
+                 const uint8_t* wdq, const uint8_t* wds, uint16_t* yexp, hipStream_t s) {
+  gmx::Params q{};
+  q.offsets = offsets; q.E = E; q.n = n; q.d = d; q.f = f;
+  q.a0 = aq; q.a0s = as; q.b0 = wdq; q.b0s = wds; q.o0 = yexp;
+  return gmx::launch<gmx::FWD2>(q, s);
+}
+
 int gg_mx_down(int E, int n, int d, int f, const int32_t* offsets, const uint16_t* a, const uint8_t* wdq,
                const uint8_t* wds, uint16_t* yexp, uint8_t* ws, hipStream_t s) {
   uint8_t* aq = ws;
   uint8_t* as = ws + static_cast<size_t>(n) * f;
   if (int st = mxfp8_quantize_gemm(a, 1, n, f, aq, as, s)) return st;
-  gmx::Params q{};
-  q.offsets = offsets; q.E = E; q.n = n; q.d = d; q.f = f;
-  q.a0 = aq; q.a0s = as; q.b0 = wdq; q.b0s = wds; q.o0 = yexp;
-  return gmx::launch<gmx::FWD2>(q, s);
+  return gg_mx_down_q(E, n, d, f, offsets, aq, as, wdq, wds, yexp, s);
 }
 
 size_t gg_mx_forward_ws(int n, int f) { return static_cast<size_t>(n) * f + static_cast<size_t>(n) * f / 32; }

@@ -83,15 +83,16 @@ class _Span:
 
 
 # names of the calls `forward` and `backward` can bracket with events: each grouped-GEMM call is
-# one kernel ("down" under MXFP8 also quantises a along f first; "recompute" is the gate/up product
-# again, in the backward of a forward run with recompute=True); ROW_CALLS are the routing and
-# row-movement calls (route: its three kernels)
+# one kernel ("recompute" is the gate/up product again, in the backward of a forward run with
+# recompute=True); ROW_CALLS are the routing and row-movement calls (route: its three kernels)
 GEMM_CALLS = ("gate_up", "down", "dgrad_down", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up")
 RECOMPUTE_CALL = "recompute"
-# the router products (layers that own their router) and the MXFP8 quantiser calls (each one
-# kernel; under MXFP8 "quant_dyT" gathers dy with the combine backward's row gates)
+# the router products (layers that own their router) and the MXFP8 quantiser calls of the forward
+# and the backward (each one kernel; "quant_a" gives A's row blocks and grouped token blocks from
+# one read, "quant_dyT" gathers dy with the combine backward's row gates)
 ROUTER_CALLS = ("router", "router_bwd")
-QUANT_CALLS = ("quant_dg", "quant_du", "quant_dyT", "quant_aT", "quant_xT")
+QUANT_CALLS_FWD = ("quant_a",)
+QUANT_CALLS = ("quant_dg", "quant_du", "quant_dyT", "quant_xT")
 ROW_CALLS = ("route", "permute", "combine", "combine_bwd", "permute_bwd", "route_bwd")
 # MXFP8: each expert's rows start at a multiple of MX_PAD on the padded token axis of the
 # weight-gradient operands.  128 = one K step of those products: every step's 128-byte piece of an
@@ -146,8 +147,13 @@ def forward(x, weights, k, logits=None, mxfp8=False, want_probs=False, events=No
         with _Span(events, "gate_up"):
             g, u, a = ops.grouped_gemm_gate_up(xpq, r["offsets"], q["wg"], q["wu"],
                                                scales=(xps, q["wg_s"], q["wu_s"]))
+        # A read once for both its MXFP8 layouts: row blocks for the down product now, grouped
+        # token blocks for the down weight gradient (kept for the backward, recompute or not)
+        with _Span(events, "quant_a"):
+            aq, as_, aT, aTs = ops.mxfp8_quantize_rows_grouped(a, r["offsets"], r["offsets_pad"])
+        ctx["aT"], ctx["aTs"] = aT, aTs
         with _Span(events, "down"):
-            yexp = ops.grouped_gemm_down(a, r["offsets"], q["wd"], w_down_scale=q["wd_s"])
+            yexp = ops.grouped_gemm_down_mx(aq, as_, r["offsets"], q["wd"], q["wd_s"])
     if recompute:
         del g, u, a
         ctx.update(g=None, u=None, a=None, yexp=yexp)
@@ -225,8 +231,7 @@ def backward(ctx, weights, dy, events=None):
             dg, du = ops.grouped_gemm_dgrad_down(dyq, off, q["wd_t"], g, u, scales=(dys, q["wd_t_s"]))
         with _Span(events, "quant_dyT"):
             dyT, dyTs = ops.mxfp8_quantize_grouped(dy, off, pad, n, row_token=ctx["row_token"], row_gate=row_gate)
-        with _Span(events, "quant_aT"):
-            aT, aTs = ops.mxfp8_quantize_grouped(a, off, pad, n)
+        aT, aTs = ctx["aT"], ctx["aTs"]          # the forward's grouped token blocks of A
         with _Span(events, "wgrad_down"):
             dw_down = ops.grouped_gemm_wgrad_down(dyT, aT, off, n, offsets_pad=pad, scales=(dyTs, aTs))
         # dG and dU each read once for both layouts: row blocks for the gate/up dgrad, grouped

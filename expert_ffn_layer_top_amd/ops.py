@@ -514,6 +514,23 @@ def grouped_gemm_down(a, offsets, w_down, w_down_scale=None, ws=None):
     return yexp
 
 
+def grouped_gemm_down_mx(a_q, a_scale, offsets, w_down, w_down_scale):
+    """yexp [n,d] bf16 = a W_down[e]^T per expert from an MXFP8 a (a_q [n,f] E4M3, a_scale its row
+    blocks in the GEMM scale layout, as mxfp8_quantize_rows_grouped gives them)."""
+    _check(w_down, torch.uint8, "w_down", ndim=3)
+    E, d, f = w_down.shape
+    _check(offsets, torch.int32, "offsets", (E + 1,))
+    _check(a_q, torch.uint8, "a_q", (None, f))
+    n = a_q.shape[0]
+    _check(a_scale, torch.uint8, "a_scale", (n, f // 32))
+    _check(w_down_scale, torch.uint8, "w_down_scale", (E, d, f // 32))
+    _on_gpu(a_q, a_scale, offsets, w_down, w_down_scale)
+    yexp = _empty((n, d), torch.bfloat16, a_q)
+    call("moe_grouped_gemm_down_mx", E, n, d, f, _ptr(offsets), _ptr(a_q), _ptr(a_scale), _ptr(w_down),
+         _ptr(w_down_scale), _ptr(yexp), _stream(a_q))
+    return yexp
+
+
 def grouped_gemm_swiglu_bwd(x_rows, g, u, a, dyexp, offsets, w_gate, w_up, w_down, scales=None,
                             offsets_pad=None, row_token=None, ws=None):
     """dict(dg, du, dxp, dw_gate, dw_up, dw_down), all bf16.

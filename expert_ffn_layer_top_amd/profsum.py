@@ -61,8 +61,7 @@ def call_sources(call, dtype, router=False):
     """The csrc files whose code one call of the layer step runs (router: the layer owns its
     router, so the permute backward is the router file's fused kernel)."""
     if call in GEMM_CALLS or call == "recompute":
-        src = SOURCES[dtype]
-        return src + CALL_SOURCES["quant"] if (dtype == "mxfp8" and call == "down") else src
+        return SOURCES[dtype]
     if call in ("route", "route_bwd"):
         return CALL_SOURCES["route"]
     if call in ("router", "router_bwd") or (call == "permute_bwd" and router):
@@ -96,8 +95,8 @@ def step_sequence(mxfp8, router, forward_only=False):
         seq.append(("router", [("router_fwd_kernel", None)]))
     seq.append(("route", [("route_topk_local", None), ("route_scan", None), ("route_finalize", None)]))
     if mxfp8:
-        seq += [("permute", [("permute_mx_kernel", None)]),
-                ("gate_up", [g(0)]), ("down", [("quant_rows_kernel", None), g(1)])]
+        seq += [("permute", [("permute_mx_kernel", None)]), ("gate_up", [g(0)]),
+                ("quant_a", [("quant_rows_grouped_kernel", None)]), ("down", [g(1)])]
     else:
         seq += [("permute", [("permute_kernel", None)]), ("gate_up", [g(0)]), ("down", [g(1)])]
     seq.append(("combine", [("combine_kernel", None)]))
@@ -112,7 +111,7 @@ def step_sequence(mxfp8, router, forward_only=False):
           else [("permute_bwd_kernel", None)])
     if mxfp8:
         qg = ("quant_grouped_kernel", None)
-        seq += [("dgrad_down", [g(2)]), ("quant_dyT", [qg]), ("quant_aT", [qg]), ("wgrad_down", [g(4)]),
+        seq += [("dgrad_down", [g(2)]), ("quant_dyT", [qg]), ("wgrad_down", [g(4)]),
                 ("quant_dg", [("quant_rows_grouped_kernel", None)]), ("quant_du", [("quant_rows_grouped_kernel", None)]),
                 ("dgrad_gate_up", [g(3)]), pb, ("quant_xT", [qg]), ("wgrad_gate_up", [g(5)])]
     else:

@@ -366,6 +366,18 @@ int moe_grouped_gemm_down(int dtype, int E, int n, int d, int f, const int32_t* 
                           const uint16_t* a, const void* w_down, const uint8_t* w_down_scale,
                           uint16_t* yexp, void* ws, size_t ws_bytes, void* stream);
 
+/* The MXFP8 down product on an already quantised a ([news] "MXFP8 reduces compute and memory
+ * costs": the expert products run on 8-bit operands with a scale per block of 32): yexp [n,d] bf16
+ * = a W_down[e]^T per expert, with a_q [n,f] E4M3 and a_scale its row blocks in the GEMM scale
+ * layout (R = n, K = f) -- mxfp8_quantize_rows_grouped's q_rows / s_rows, which also give a's
+ * grouped token blocks for the down weight gradient from the same read -- and w_down [E,d,f]
+ * E4M3 + scale as for moe_grouped_gemm_down.  Equals moe_grouped_gemm_down(MOE_MXFP8) on the bf16
+ * a byte for byte; needs no workspace.  Shapes and errors as moe_grouped_gemm_down (MXFP8: d, f
+ * multiples of 128); a_q, w_down, yexp and both scales 16-byte aligned. */
+int moe_grouped_gemm_down_mx(int E, int n, int d, int f, const int32_t* offsets, const uint8_t* a_q,
+                             const uint8_t* a_scale, const uint8_t* w_down, const uint8_t* w_down_scale,
+                             uint16_t* yexp, void* stream);
+
 /* Backward of moe_grouped_gemm_swiglu: the dgrad and wgrad grouped GEMMs that training the
  * experts needs ([news] "Routing work stays on the GPU": grouped GEMM; [card] "Summary":
  * device-scheduled grouped GEMMs in the training stack; "MXFP8 reduces compute and memory

@@ -142,6 +142,14 @@ def test_argument_checks_return_status_without_launching():
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, fake, None, None, 0, None) == WORKSPACE
     # nothing requested: nothing to do
     assert L.moe_router_project_bwd(fake, fake, fake, 64, 128, 8, None, None, None, 0, None) == 0
+    # MXFP8 down product on quantised A: the MXFP8 shape rule, pointers, alignment, scales
+    gdm = L.moe_grouped_gemm_down_mx
+    assert gdm(4, 256, 192, 256, fake, fake, fake, fake, fake, fake, None) == UNSUPPORTED   # d % 128
+    assert gdm(0, 256, 256, 256, fake, fake, fake, fake, fake, fake, None) == UNSUPPORTED   # E = 0
+    assert gdm(4, 256, 256, 256, fake, None, fake, fake, fake, fake, None) == INVALID
+    assert gdm(4, 256, 256, 256, fake, fake, None, fake, fake, fake, None) == INVALID       # a scale
+    assert gdm(4, 256, 256, 256, fake, fake, fake, fake, ctypes.c_void_p(0x1008), fake, None) == INVALID
+    assert gdm(4, 256, 256, 256, fake, ctypes.c_void_p(0x1008), fake, fake, fake, fake, None) == INVALID
     # permute backward with the router's dx term: the rows' limits, the router's, the workspace
     pbr = L.moe_permute_bwd_router
     assert pbr(fake, fake, 64, 128, 0, fake, fake, 8, fake, fake, 1 << 30, None) == UNSUPPORTED    # k = 0

@@ -166,6 +166,10 @@ def test_grouped_gemm_mxfp8_forward_backward(case):
     aq, as_ = mxfp8.quantize_rows(bits(a))                     # the GPU quantises its own bf16 A
     Y = moe.expert_down(mxfp8.dequantize_blocks(aq, as_), p["off"], deq_w(*Q["wd"]))
     assert_close(codecs.bf16_to_f64(bits(yexp)), Y, MX_TOL, "Yexp (MX, chained)")
+    # the down product on A quantised by the one-read rows + grouped quantiser: the same bytes
+    aq_d, as_d, _, _ = ops.mxfp8_quantize_rows_grouped(a, off_d, i32_to_dev(p["offp"]))
+    y2 = ops.grouped_gemm_down_mx(aq_d, as_d, off_d, QG["wd"][0], QG["wd"][1])
+    assert np.array_equal(bits(y2), bits(yexp)), "down on pre-quantised A differs from the composite"
 
     note(f"gg mxfp8 bwd {case}")
     offp_d = i32_to_dev(p["offp"])
