@@ -213,7 +213,9 @@ __device__ __forceinline__ void epi_gate_up(f32x4 (&acc)[8][8], uint16_t* g, uin
   store_staged<4, 2 * JR>(aval, out_rsrc(a, n, f, row0, col0), rows_valid, cv, f, stg, lane);
 }
 
-template <int JR>
+// PF: load G and U of round q + 1 while round q is processed (two register buffers), so only the
+// first round waits a whole memory latency -- for kernels with the registers to spare.
+template <int JR, bool PF = false>
 __device__ __forceinline__ void epi_swiglu_bwd(f32x4 (&acc)[8][8], const uint16_t* g, const uint16_t* u,
                                                uint16_t* dg, uint16_t* du, long long n, int f, int row0,
                                                int rows_valid, int col0, uint32_t stg, int lane) {
@@ -222,13 +224,29 @@ __device__ __forceinline__ void epi_swiglu_bwd(f32x4 (&acc)[8][8], const uint16_
   const auto rui = out_rsrc(u, n, f, row0, col0);
   const auto rdg = out_rsrc(dg, n, f, row0, col0);
   const auto rdu = out_rsrc(du, n, f, row0, col0);
+  // (separate code for the two forms, so the kernels that do not prefetch keep their registers)
+  [[maybe_unused]] u32x4 pgl[PF ? 2 : 1][4 * JR], pul[PF ? 2 : 1][4 * JR];
+  if constexpr (PF) {
+    load_rows<JR>(rgi, 0, rows_valid, cv, f, lane, pgl[0]);
+    load_rows<JR>(rui, 0, rows_valid, cv, f, lane, pul[0]);
+  }
   sfor<0, 8 / JR>([&](auto q) {
-    u32x4 gl[4 * JR], ul[4 * JR];
-    load_rows<JR>(rgi, q, rows_valid, cv, f, lane, gl);
-    load_rows<JR>(rui, q, rows_valid, cv, f, lane, ul);
     u32x2 gm[JR][8], um[JR][8];
-    stage_in_round<JR>(gl, gm, stg, lane);
-    stage_in_round<JR>(ul, um, stg, lane);
+    if constexpr (PF) {
+      constexpr int b = q & 1;
+      if constexpr (q + 1 < 8 / JR) {
+        load_rows<JR>(rgi, q + 1, rows_valid, cv, f, lane, pgl[b ^ 1]);
+        load_rows<JR>(rui, q + 1, rows_valid, cv, f, lane, pul[b ^ 1]);
+      }
+      stage_in_round<JR>(pgl[b], gm, stg, lane);
+      stage_in_round<JR>(pul[b], um, stg, lane);
+    } else {
+      u32x4 gl[4 * JR], ul[4 * JR];
+      load_rows<JR>(rgi, q, rows_valid, cv, f, lane, gl);
+      load_rows<JR>(rui, q, rows_valid, cv, f, lane, ul);
+      stage_in_round<JR>(gl, gm, stg, lane);
+      stage_in_round<JR>(ul, um, stg, lane);
+    }
     sfor<0, JR>([&](auto jj) { pin_acc_col<JR * q + jj>(acc); });
     // dG, dU replace G, U in place (fewer live registers)
     sfor<0, JR>([&](auto jj) {

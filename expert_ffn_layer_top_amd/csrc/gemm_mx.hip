@@ -460,7 +460,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
   if constexpr (MODE == FWD1) {
     gep::epi_gate_up<1>(acc, p.o0, p.o1, p.o2, p.n, p.f, row0, rows_valid, t.n0 + 64 * wn, stg, lane);
   } else if constexpr (MODE == DGRAD1) {
-    gep::epi_swiglu_bwd<1>(acc, p.g, p.u, p.o0, p.o1, p.n, p.f, row0, rows_valid, t.n0 + 128 * wn, stg, lane);
+    gep::epi_swiglu_bwd<1, true>(acc, p.g, p.u, p.o0, p.o1, p.n, p.f, row0, rows_valid, t.n0 + 128 * wn, stg, lane);
   } else {
     const int Ntot = n_total<MODE>(p);
     uint16_t* out = p.o0;
