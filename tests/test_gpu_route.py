@@ -107,11 +107,13 @@ def test_router_project_and_bwd(T, d, E):
 
 
 @pytest.mark.parametrize("T,d,E,k", [(300, 192, 8, 2), (1000, 512, 64, 4), (257, 256, 5, 1), (100, 128, 16, 8),
-                                     (70, 64, 32, 16), (1, 64, 4, 3), (513, 7168, 64, 4)])
+                                     (70, 64, 32, 16), (1, 64, 4, 3), (513, 7168, 64, 4),
+                                     # more than 64 experts: several 64-expert chunks, a ragged last one
+                                     (130, 128, 256, 8), (64, 320, 96, 2)])
 def test_permute_bwd_with_router_term(T, d, E, k):
     """The permute backward with the router's dx term in one kernel: byte-identical to the router
     backward's fp32 dx followed by the permute backward with it as the addend, and within the bf16
-    bar of the oracle (ragged token tiles, d not a multiple of the 128-channel tile, k = 1..16)."""
+    bar of the oracle (ragged token tiles, partial 128-channel tiles, k = 1..16, E up to 256)."""
     from expert_ffn_layer_top_amd import ops
     rng = np.random.default_rng(T + d + E + k)
     logits = rng.standard_normal((T, E)).astype(np.float32)
