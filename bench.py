@@ -15,14 +15,14 @@ and the permute backward.  Inputs are resident in HBM before any timed region.
 
 Protocol (events are created before the first warm-up step):
   1. W warm-up steps.
-  2. Instrumented pass, K steps.  Before each, 1 GiB of scratch is written (cold L2 and
-     last-level cache; --no-flush skips it).  Every call of the step is bracketed with HIP events
+  2. Instrumented pass, K steps.  Before each, 1 GiB of scratch is read (cold L2 and last-level
+     cache, with no dirty lines left whose write-back would land on the step's first calls, as a
+     flush by writing leaves; --no-flush skips it).  Every call of the step is bracketed with HIP events
      on the stream it runs on, and so is the whole step.  Gives per-call medians: TFLOP/s of each
      grouped GEMM (`gemm_ms`, `gemm_tflops`), achieved HBM GB/s of the routing and row calls
      (`rows_*`) and of the router products and MXFP8 quantisers (`aux_*`) on their algorithmic
      bytes, and the cold step time (`step_ms_flushed`: median, p10, p90).  It also picks the
-     dominant kernel: the grouped GEMM with the largest median (under MXFP8 the forward down call,
-     which also quantises A, is not a candidate).
+     dominant kernel: the grouped GEMM with the largest median.
   3. Timed region, K steps back to back (warm: in training the layer's input was just written by
      the layer before it): an event at every step boundary and a pair around the dominant GEMM.
      `value` = T K / wall-clock seconds, `ms_per_step` = wall-clock / K, `step_ms` = median, p10,
@@ -238,7 +238,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=True):
     inst = [{c: (ev(), ev()) for c in names + ("step",)} for _ in range(steps)]
     bounds = [ev() for _ in range(steps + 1)]
     bounds_nq = [ev() for _ in range(steps + 1)]
-    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
 
     for _ in range(warmup):
         step()
@@ -247,7 +247,7 @@ def run_gpu(cfg, steps, warmup, probe_bytes=0, recompute=False, flush=True):
     # instrumented pass (cold caches unless --no-flush)
     for i in range(steps):
         if scratch is not None:
-            scratch.fill_(float(i))          # 1 GiB written: evicts the step's data from L2 and MALL
+            scratch.sum()                    # 1 GiB read: evicts the step's data from L2 and MALL
         inst[i]["step"][0].record()
         step(inst[i])
         inst[i]["step"][1].record()
