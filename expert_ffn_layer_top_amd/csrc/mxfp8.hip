@@ -3,7 +3,7 @@
 // E8M0 scale per 32 elements along a GEMM's contraction dimension:
 //   rows     blocks along the contiguous dim, output in the input's layout;
 //   cols     blocks along the strided dim, output transposed (each block contiguous again);
-//   grouped  token-axis blocks restarting at each expert group (padded to 32 rows), output
+//   grouped  token-axis blocks restarting at each expert group (padded to 32, 64 or 128 rows), output
 //            transposed to [C, padded tokens]: the weight-gradient operands.  Their scales are
 //            stored block-major, [padded tokens / 32, C], so the scales of one K step of the
 //            weight-gradient products (4 blocks) for consecutive channels are contiguous.
