@@ -322,9 +322,9 @@ def test_mxfp8_few_workgroups_bit_identical(case, monkeypatch):
 
 @pytest.mark.parametrize("case", [MX_CASES[0], MX_CASES[2], MX_CASES[8]], ids=case_id)
 def test_mxfp8_wgrad_pad_independent(case):
-    """The MXFP8 weight gradients with each expert padded to 32 and to 128 tokens on the token
+    """The MXFP8 weight gradients with each expert padded to 32, 64 and 128 tokens on the token
     axis: the 32-token scale blocks and the 128-token K steps start at the same rows of each
-    expert either way, so every weight gradient is bit-identical."""
+    expert every way, so every weight gradient is bit-identical."""
     from expert_ffn_layer_top_amd import ops
     p = problem(**{**case, "pad": 32})
     n = p["n"]
@@ -336,8 +336,8 @@ def test_mxfp8_wgrad_pad_independent(case):
     dg_d, du_d, a_d = (bf16_to_dev(to_bf16_bits(rng.standard_normal((n, p["f"])).astype(np.float32)))
                        for _ in range(3))
     outs = {}
-    for pad in (32, 128):
-        offp_d = i32_to_dev(p["offp"] if pad == 32 else problem(**{**case, "pad": 128})["offp"])
+    for pad in (32, 64, 128):
+        offp_d = i32_to_dev(p["offp"] if pad == 32 else problem(**{**case, "pad": pad})["offp"])
         note(f"gg mxfp8 wgrad pad {pad} {case}")
         dyT, dyTs = ops.mxfp8_quantize_grouped(dy_d, off_d, offp_d, n)
         aT, aTs = ops.mxfp8_quantize_grouped(a_d, off_d, offp_d, n)
@@ -348,5 +348,6 @@ def test_mxfp8_wgrad_pad_independent(case):
         dwg, dwu = ops.grouped_gemm_wgrad_gate_up(dgT, duT, xT, off_d, n, offsets_pad=offp_d,
                                                   scales=(dgTs, duTs, xTs))
         outs[pad] = [bits(t) for t in (dwd, dwg, dwu)]
-    for nm, r, o in zip(("dw_down", "dw_gate", "dw_up"), outs[32], outs[128]):
-        assert np.array_equal(r, o), f"{nm}: pad 128 differs from pad 32"
+    for pad in (64, 128):
+        for nm, r, o in zip(("dw_down", "dw_gate", "dw_up"), outs[32], outs[pad]):
+            assert np.array_equal(r, o), f"{nm}: pad {pad} differs from pad 32"

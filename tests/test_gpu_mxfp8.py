@@ -123,7 +123,7 @@ def test_gemm_scale_layout_producers(B, R, C):
 
 
 @pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
-@pytest.mark.parametrize("pad", [32, 128])
+@pytest.mark.parametrize("pad", [32, 64, 128])
 def test_rows_and_grouped_from_one_read(T, E, k, C, pad):
     """Both layouts of a grouped tensor from one read (the backward's dG, dU) against the oracle's
     row blocks and grouped token blocks, with an empty expert group and ragged group sizes."""
@@ -148,7 +148,7 @@ def test_rows_and_grouped_from_one_read(T, E, k, C, pad):
 
 @pytest.mark.parametrize("T,E,k,C", [(40, 5, 2, 64), (700, 6, 2, 256), (1000, 64, 4, 128), (300, 16, 8, 192)])
 @pytest.mark.parametrize("gather", [False, True])
-@pytest.mark.parametrize("pad", [32, 128])
+@pytest.mark.parametrize("pad", [32, 64, 128])
 def test_grouped_token_blocks(T, E, k, C, gather, pad):
     from expert_ffn_layer_top_amd import ops
     rng = np.random.default_rng(T + E + C)
