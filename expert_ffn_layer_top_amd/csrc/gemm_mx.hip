@@ -655,16 +655,15 @@ inline long long grid_upper(int mode, int E, int n, int d, int f) {
 // Tile cells per product, measured at the MXFP8 workload (2048 rows per expert, d 7168, f 2048;
 // time and FETCH_SIZE per product for several shapes): cells of 8 m-tiles x 2 n-tiles for the
 // gate/up product and the gate/up dgrad (fetch beyond L2 1.5-2.5x lower, 7-9% faster than
-// n-fastest), 2 x 16 for the down product, 8 x 4 for the down weight gradient (7% faster, same
-// fetch); n-fastest for the down dgrad, which was no faster in cells, and for the gate/up weight
-// gradient: its cells cut the fetch (16 x 2: 16 -> 8.9 GB per call) but ran 15% slower in the
-// layer step, from cold caches.
+// n-fastest), 8 x 4 for the down weight gradient (7% faster, same fetch; n-fastest, 4 x 8 and
+// 16 x 2 slower); n-fastest for the down dgrad, which was no faster in cells, for the down product
+// (5% faster than its 2 x 16 cells, 4 x 8 slower still) and for the gate/up weight gradient: its
+// cells cut the fetch (16 x 2: 16 -> 8.9 GB per call) but ran 10-15% slower in the layer step.
 template <int MODE>
 void tile_cells(Params& p) {
   p.cm = 1;
   p.cn = 1 << 20;
   if (MODE == FWD1 || MODE == DGRAD2) { p.cm = 8; p.cn = 2; }
-  if (MODE == FWD2) { p.cm = 2; p.cn = 16; }
   if (MODE == WGRAD_DOWN) { p.cm = 8; p.cn = 4; }
 }
 
