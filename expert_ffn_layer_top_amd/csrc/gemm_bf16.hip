@@ -99,6 +99,9 @@ struct Params {
   uint16_t* o0;
   uint16_t* o1;
   uint16_t* o2;
+  int cm, cn;           // tile cell shape (set by launch)
+  int cell_mt;          // cells apply to experts of at most this many m-tiles
+  int cell_deal;        // weight gradients: cells apply under the round-robin deal too
 };
 
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I = B .. E-1, so that indices into
@@ -460,18 +463,25 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
   }
 }
 
-// The tile with linear id `lid` (< the launch's tile count).  Linear ids run n-tile fastest, then
-// m-tile, then (weight gradients) expert.
+// The tile with linear id `lid` (< the launch's tile count).  Each expert owns a contiguous run
+// of ids (experts in order); inside it, tiles follow cell_order in cells of cm x cn (plain
+// n-fastest for experts of more than cell_mt m-tiles), so the tiles running at once on one XCD
+// share their operand slices in its L2.
 template <int MODE>
-__device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int ntiles_n, int lid) {
+__device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int ntiles_n, int cm, int cn, int lid) {
   Tile t;
   if constexpr (!Traits<MODE>::WGRAD) {
     const int mt_glob = lid / ntiles_n;
-    const int nt = lid - mt_glob * ntiles_n;
     int e, first;
     gsched::mtile_find(mts, mt_glob, e, first);
+    e = __builtin_amdgcn_readfirstlane(e);
+    first = __builtin_amdgcn_readfirstlane(first);
+    const int mt_e = (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
+    const bool cells = mt_e <= p.cell_mt;
+    int mi, nt;
+    gsched::cell_order(lid - first * ntiles_n, mt_e, ntiles_n, cells ? cm : 1, cells ? cn : 1 << 20, mi, nt);
     t.e = e;
-    t.m0 = p.offsets[e] + (mt_glob - first) * BM;
+    t.m0 = p.offsets[e] + mi * BM;
     t.m_end = p.offsets[e + 1];
     t.n0 = nt * n_tile_width<MODE>();
     t.half = 0;
@@ -483,8 +493,8 @@ __device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int 
     const int per_e = mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
     t.e = lid / per_e;
     const int rem = lid - t.e * per_e;
-    const int mi = rem / ntiles_n;
-    const int nt = rem - mi * ntiles_n;
+    int mi, nt;
+    gsched::cell_order(rem, mt * (MODE == WGRAD_GU ? 2 : 1), ntiles_n, cm, cn, mi, nt);
     t.half = mi >= mt ? 1 : 0;
     t.m0 = (mi - t.half * mt) * BM;
     t.m_end = Mtot;
@@ -657,6 +667,8 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     total = p.E * mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
     deal = gsched::wgrad_skewed(p.offsets, p.E, p.n);
   }
+  const int cm = deal && !p.cell_deal ? 1 : p.cm;
+  const int cn = deal && !p.cell_deal ? 1 << 20 : p.cn;
   const int G = gridDim.x;     // a multiple of 8
   const int bid = blockIdx.x;
   int lid, lstep, lend;
@@ -679,7 +691,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   const bool role_b = wave < 2;
   const int h = wave & 1;
   const OpLoad ld = op_load<MODE>(p, role_b, h);
-  Tile t = tile_at<MODE>(p, mts, ntiles_n, lid);
+  Tile t = tile_at<MODE>(p, mts, ntiles_n, cm, cn, lid);
   TileSrc cur = tile_src<MODE>(p, t, role_b, h);
   // round-robin deal in snake order: round r gives workgroup b tile r G + b (r even) or
   // r G + G - 1 - b (r odd), so the workgroups holding the first (hottest, lowest-id) experts'
@@ -690,7 +702,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   Tile tn = t;
   TileSrc nxt = empty_src(p);
   if (lid_n < lend) {
-    tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
+    tn = tile_at<MODE>(p, mts, ntiles_n, cm, cn, lid_n);
     nxt = tile_src<MODE>(p, tn, role_b, h);
   }
 
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     kt = 0;
     lid_n = deal ? deal_lid(++rn) : lid_n + lstep;
     if (lid_n < lend) {
-      tn = tile_at<MODE>(p, mts, ntiles_n, lid_n);
+      tn = tile_at<MODE>(p, mts, ntiles_n, cm, cn, lid_n);
       nxt = tile_src<MODE>(p, tn, role_b, h);
     } else {
       nxt = empty_src(p);
@@ -759,8 +771,32 @@ inline long long grid_upper(int mode, int E, int n, int d, int f) {
   }
 }
 
+// Tile cells per product, measured on the bf16 workloads (balanced E 64; sweep d 4096, f 1536 at
+// E 8, 32, 128; skewed zipf routing, E 128, top-8) against plain n-fastest order:
+//  - down product 4 x 4: 8-10% faster at E 8 and skewed, 2-3% elsewhere;
+//  - gate/up dgrad 4 x 4: 4-6% faster at E 128 and skewed, level elsewhere;
+//  - down weight gradient 4 x 8: 2-3% faster at E 128 and skewed;
+//  - gate/up product 8 x 2 on experts of at most 16 m-tiles: 4% faster at E 128 and 2% at E 32;
+//    on the skewed workload's hot experts (64 m-tiles) every cell shape ran 2-5% slower;
+//  - gate/up weight gradient 4 x 4 except under the round-robin deal: 2.5-6% faster at E 32 and
+//    128; the skewed workload (dealt) ran 3% slower in cells;
+//  - down dgrad: n-fastest (no shape was outside the run-to-run spread of about 1.5%).
 template <int MODE>
-int launch(const Params& p, hipStream_t s) {
+void tile_cells(Params& p) {
+  p.cm = 1;
+  p.cn = 1 << 20;
+  p.cell_mt = 1 << 20;
+  p.cell_deal = 1;
+  if (MODE == FWD1) { p.cm = 8; p.cn = 2; p.cell_mt = 16; }
+  if (MODE == FWD2 || MODE == DGRAD2) { p.cm = 4; p.cn = 4; }
+  if (MODE == WGRAD_DOWN) { p.cm = 4; p.cn = 8; }
+  if (MODE == WGRAD_GU) { p.cm = 4; p.cn = 4; p.cell_deal = 0; }
+}
+
+template <int MODE>
+int launch(const Params& p0, hipStream_t s) {
+  Params p = p0;
+  tile_cells<MODE>(p);
   const long long upper = grid_upper(MODE, p.E, p.n, p.d, p.f);
   MOE_REQUIRE(upper < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many tiles");
   const int g = gemm_workgroups(upper);

@@ -286,19 +286,6 @@ __device__ __forceinline__ int bfrag_base(int wn) {
   return MODE == FWD1 ? 4 * wn : 8 * wn;
 }
 
-// Local tile l of an expert's MT x NT tiles -> (m-tile, n-tile), in cells of CM m-tiles x CN
-// n-tiles taken m-fastest inside a cell, cells n-group by n-group within each group of CM
-// m-tiles (partial cells at the edges, no holes).  CM = 1, CN >= NT is plain n-fastest order.
-__device__ __forceinline__ void cell_order(int l, int MT, int NT, int CM, int CN, int& m, int& n) {
-  const int mg = l / (CM * NT);
-  const int r = l - mg * CM * NT;
-  const int cm = min(CM, MT - mg * CM);
-  const int ng = r / (cm * CN);
-  const int r2 = r - ng * cm * CN;
-  m = mg * CM + r2 % cm;
-  n = ng * CN + r2 / cm;
-}
-
 // The tile with linear id `lid` (< the launch's tile count).  Each expert owns a contiguous run
 // of ids (experts in order); inside it, tiles follow cell_order with the launch's cell shape, so
 // the tiles running at once on one XCD (consecutive ids) share their operand slices in its L2.
@@ -313,7 +300,7 @@ __device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int 
     first = __builtin_amdgcn_readfirstlane(first);
     const int mt_e = (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
     int mi, nt;
-    cell_order(lid - first * ntiles_n, mt_e, ntiles_n, p.cm, p.cn, mi, nt);
+    gsched::cell_order(lid - first * ntiles_n, mt_e, ntiles_n, p.cm, p.cn, mi, nt);
     t.e = e;
     t.m0 = p.offsets[e] + mi * BM;
     t.m_end = p.offsets[e + 1];
@@ -328,7 +315,7 @@ __device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int 
     t.e = lid / per_e;
     const int rem = lid - t.e * per_e;
     int mi, nt;
-    cell_order(rem, mt * (MODE == WGRAD_GU ? 2 : 1), ntiles_n, p.cm, p.cn, mi, nt);
+    gsched::cell_order(rem, mt * (MODE == WGRAD_GU ? 2 : 1), ntiles_n, p.cm, p.cn, mi, nt);
     t.half = mi >= mt ? 1 : 0;
     t.m0 = (mi - t.half * mt) * BM;
     t.m_end = Mtot;

@@ -1,6 +1,6 @@
 // Tile schedule of the persistent grouped GEMMs (bf16 and MXFP8): how many m-tiles each expert's
 // rows make and which expert owns a global m-tile, computed by every wave from one round of loads
-// (no LDS: the operand rings fill it).  Lane l of group r holds expert 64 r + l (at most 256).
+// (no LDS: the operand rings fill it), and the order of an expert's tiles.  Lane l of group r holds expert 64 r + l (at most 256).
 #pragma once
 
 #include "common.h"
@@ -70,6 +70,19 @@ __device__ __forceinline__ void mtile_find(const MTiles& m, int mt, int& e, int&
       first = __shfl(m.excl[r], src, 64);
     }
   }
+}
+
+// Local tile l of an expert's MT x NT tiles -> (m-tile, n-tile), in cells of CM m-tiles x CN
+// n-tiles taken m-fastest inside a cell, cells n-group by n-group within each group of CM
+// m-tiles (partial cells at the edges, no holes).  CM = 1, CN >= NT is plain n-fastest order.
+__device__ __forceinline__ void cell_order(int l, int MT, int NT, int CM, int CN, int& m, int& n) {
+  const int mg = l / (CM * NT);
+  const int r = l - mg * CM * NT;
+  const int cm = min(CM, MT - mg * CM);
+  const int ng = r / (cm * CN);
+  const int r2 = r - ng * cm * CN;
+  m = mg * CM + r2 % cm;
+  n = ng * CN + r2 / cm;
 }
 
 }  // namespace gsched
