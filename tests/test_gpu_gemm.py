@@ -46,6 +46,10 @@ BF16_CASES = [
     # one expert far above twice the mean rows (every token picks expert 0): the weight
     # gradients deal their tiles round-robin in snake order
     dict(T=700, d=256, E=8, k=2, f=256, seed=8, hot=0),
+    # expert 0 holds 4200 rows (17 m-tiles: the gate/up product takes its tiles n-fastest), the
+    # others about 1400 (6 m-tiles: in cells), within one launch; the weight gradients stay in
+    # contiguous runs (4200 is not above twice the mean)
+    dict(T=4200, d=128, E=4, k=2, f=256, seed=9, hot=0),
 ]
 
 
@@ -259,7 +263,8 @@ def test_backward_per_kernel_calls_match_composite(mx):
 
 # ------------------------------------------------ persistent launch: many tiles per workgroup
 
-@pytest.mark.parametrize("case", [BF16_CASES[0], BF16_CASES[2], BF16_CASES[4], BF16_CASES[7]], ids=case_id)
+@pytest.mark.parametrize("case", [BF16_CASES[0], BF16_CASES[2], BF16_CASES[4], BF16_CASES[7], BF16_CASES[8]],
+                         ids=case_id)
 def test_bf16_few_workgroups_bit_identical(case, monkeypatch):
     """With 8 workgroups each runs many tiles in a row (the next tile's first K steps stream in
     during the previous tile's epilogue); every output must match the default launch bit for bit,
