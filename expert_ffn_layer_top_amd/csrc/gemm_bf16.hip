@@ -162,6 +162,53 @@ struct Tile {
   int k_len;       // K extent (tokens for WGRAD)
 };
 
+// The experts with rows (empty = false) or without (empty = true), as four 64-bit ballots (bit l
+// of m[r]: expert 64 r + l), wave-uniform so that they stay in scalar registers.
+struct ExpertSet {
+  unsigned long long m[4];
+  int total;
+};
+
+__device__ __forceinline__ ExpertSet expert_set(const int32_t* __restrict__ offsets, int E, bool empty) {
+  const int lane = threadIdx.x & 63;
+  ExpertSet s;
+  s.total = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ex = 64 * r + lane;
+    const bool in = ex < E && ((offsets[ex + 1] - offsets[ex]) == 0) == empty;
+    s.m[r] = __ballot(in);
+    s.total += __popcll(s.m[r]);
+  }
+  return s;
+}
+
+// The j-th expert of the set (j < s.total).
+__device__ __forceinline__ int expert_set_nth(const ExpertSet& s, int j) {
+  int r = 0;
+  unsigned long long m = s.m[0];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int c = __popcll(m);
+    if (j >= c) {
+      j -= c;
+      m = s.m[q + 1];
+      r = q + 1;
+    }
+  }
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll(m & ((1ull << w) - 1));
+    if (j >= c) {
+      j -= c;
+      m >>= w;
+      pos += w;
+    }
+  }
+  return 64 * r + pos;
+}
+
 template <int MODE>
 __device__ __forceinline__ int n_total(const Params& p) {
   if (MODE == FWD1 || MODE == DGRAD1) return p.f;
@@ -468,7 +515,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, f32x4 (
 // n-fastest for experts of more than cell_mt m-tiles), so the tiles running at once on one XCD
 // share their operand slices in its L2.
 template <int MODE>
-__device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int ntiles_n, int cm, int cn, int lid) {
+__device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, const ExpertSet& nz, int ntiles_n, int cm,
+                                        int cn, int lid) {
   Tile t;
   if constexpr (!Traits<MODE>::WGRAD) {
     const int mt_glob = lid / ntiles_n;
@@ -491,8 +539,10 @@ __device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, int 
     const int Mtot = m_total_wgrad<MODE>(p);
     const int mt = (Mtot + BM - 1) / BM;
     const int per_e = mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
-    t.e = lid / per_e;
-    const int rem = lid - t.e * per_e;
+    // ids run over the experts with rows only (those without are zero_tiles' work)
+    const int j = lid / per_e;
+    t.e = expert_set_nth(nz, j);
+    const int rem = lid - j * per_e;
     int mi, nt;
     gsched::cell_order(rem, mt * (MODE == WGRAD_GU ? 2 : 1), ntiles_n, cm, cn, mi, nt);
     t.half = mi >= mt ? 1 : 0;
@@ -657,6 +707,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   const int NTW = n_tile_width<MODE>();
   const int ntiles_n = (n_total<MODE>(p) + NTW - 1) / NTW;
   MTiles mts{};
+  ExpertSet nz{};
   int total;
   bool deal = false;
   if constexpr (!Traits<MODE>::WGRAD) {
@@ -664,7 +715,8 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     total = mts.total * ntiles_n;
   } else {
     const int mt = (m_total_wgrad<MODE>(p) + BM - 1) / BM;
-    total = p.E * mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
+    nz = expert_set(p.offsets, p.E, false);
+    total = nz.total * mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
     deal = gsched::wgrad_skewed(p.offsets, p.E, p.n);
   }
   const int cm = deal && !p.cell_deal ? 1 : p.cm;
@@ -686,12 +738,45 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   lid = __builtin_amdgcn_readfirstlane(lid);
   lstep = __builtin_amdgcn_readfirstlane(lstep);
   lend = __builtin_amdgcn_readfirstlane(lend);
+
+  // Weight gradients of experts without rows are zero.  Their tiles stay out of the K-step
+  // stream (which runs at least two steps per tile): before its own tiles each workgroup writes
+  // its round-robin share of them with the epilogue on zeroed accumulators, staged in the first
+  // operand stage (the epilogue synchronises only within a wave; a barrier then hands the LDS to
+  // the stream).
+  if constexpr (Traits<MODE>::WGRAD) {
+    f32x4 acc[8][8];
+    const uint32_t stg = lds_addr(lds_ring) + B_RING + wave * STG_BYTES;
+    const int Mtot = m_total_wgrad<MODE>(p);
+    const int mt = (Mtot + BM - 1) / BM;
+    const int per_e = mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
+    const ExpertSet ez = expert_set(p.offsets, p.E, true);
+    const int total_z = ez.total * per_e;
+    for (int z = bid; z < total_z; z += G) {
+      const int j = z / per_e;
+      const int rem = z - j * per_e;
+      const int mi = rem / ntiles_n;
+      Tile tz;
+      tz.e = expert_set_nth(ez, j);
+      tz.half = mi >= mt ? 1 : 0;
+      tz.m0 = (mi - tz.half * mt) * BM;
+      tz.m_end = Mtot;
+      tz.n0 = (rem - mi * ntiles_n) * BN;
+      tz.k_begin = 0;
+      tz.k_len = 0;
+      zero_acc(acc);
+      epilogue<MODE>(p, tz, acc, wm, wn, lane, stg);
+    }
+    // the stores done (the prologue's vmcnt waits count only its own DMA) and every wave's
+    // staging reads done before the stream writes that stage
+    if (total_z > 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   if (lid >= lend) return;
 
   const bool role_b = wave < 2;
   const int h = wave & 1;
   const OpLoad ld = op_load<MODE>(p, role_b, h);
-  Tile t = tile_at<MODE>(p, mts, ntiles_n, cm, cn, lid);
+  Tile t = tile_at<MODE>(p, mts, nz, ntiles_n, cm, cn, lid);
   TileSrc cur = tile_src<MODE>(p, t, role_b, h);
   // round-robin deal in snake order: round r gives workgroup b tile r G + b (r even) or
   // r G + G - 1 - b (r odd), so the workgroups holding the first (hottest, lowest-id) experts'
@@ -702,7 +787,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
   Tile tn = t;
   TileSrc nxt = empty_src(p);
   if (lid_n < lend) {
-    tn = tile_at<MODE>(p, mts, ntiles_n, cm, cn, lid_n);
+    tn = tile_at<MODE>(p, mts, nz, ntiles_n, cm, cn, lid_n);
     nxt = tile_src<MODE>(p, tn, role_b, h);
   }
 
@@ -749,7 +834,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_kernel(Params p) {
     kt = 0;
     lid_n = deal ? deal_lid(++rn) : lid_n + lstep;
     if (lid_n < lend) {
-      tn = tile_at<MODE>(p, mts, ntiles_n, cm, cn, lid_n);
+      tn = tile_at<MODE>(p, mts, nz, ntiles_n, cm, cn, lid_n);
       nxt = tile_src<MODE>(p, tn, role_b, h);
     } else {
       nxt = empty_src(p);
