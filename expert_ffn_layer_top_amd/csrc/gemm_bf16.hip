@@ -539,7 +539,7 @@ __device__ __forceinline__ Tile tile_at(const Params& p, const MTiles& mts, cons
     const int Mtot = m_total_wgrad<MODE>(p);
     const int mt = (Mtot + BM - 1) / BM;
     const int per_e = mt * (MODE == WGRAD_GU ? 2 : 1) * ntiles_n;
-    // ids run over the experts with rows only (those without are zero_tiles' work)
+    // ids run over the experts with rows only (the kernel writes the others' zero tiles first)
     const int j = lid / per_e;
     t.e = expert_set_nth(nz, j);
     const int rem = lid - j * per_e;
