@@ -53,6 +53,8 @@ BF16_CASES = [
     # every token picks expert 0 alone: seven experts without rows, whose weight gradients are
     # written as zeros outside the K-step stream, beside the dealt tiles of the hot expert
     dict(T=700, d=256, E=8, k=1, f=256, seed=10, hot=0),
+    # 200 experts, top-1 of 300 tokens: empty experts in all four groups of 64
+    dict(T=300, d=128, E=200, k=1, f=128, seed=11),
 ]
 
 
@@ -266,7 +268,7 @@ def test_backward_per_kernel_calls_match_composite(mx):
 
 # ------------------------------------------------ persistent launch: many tiles per workgroup
 
-@pytest.mark.parametrize("case", [BF16_CASES[i] for i in (0, 2, 4, 7, 8, 9)], ids=case_id)
+@pytest.mark.parametrize("case", [BF16_CASES[i] for i in (0, 2, 4, 7, 8, 9, 10)], ids=case_id)
 def test_bf16_few_workgroups_bit_identical(case, monkeypatch):
     """With 8 workgroups each runs many tiles in a row (the next tile's first K steps stream in
     during the previous tile's epilogue); every output must match the default launch bit for bit,
